@@ -1,0 +1,351 @@
+/*
+ * fastvim_oracle.c -- plain, slow, fp64 CPU oracle of the pooled bidirectional
+ * selective-scan layer of FastVim (Fast Vision Mamba, arXiv 2502.00594).
+ *
+ * TEST INFRASTRUCTURE ONLY.  The library built from this file is loaded by the
+ * test-suite, by the smoke check and by the benchmark's CPU-baseline leg, and
+ * by nothing else.  The GPU product path never links, loads or calls it, and
+ * this file shares no code, header, table or constant with the GPU path.
+ *
+ * Every stage is written as its plain definition, in fp64, with sequential
+ * loops; the only parallelism is an OpenMP loop over independent images.
+ * Inputs arrive as fp32 (bf16 inputs are widened to fp32 by the caller, which
+ * is exact) and are widened to double before any arithmetic.
+ *
+ * Sources (cited by page and section; no line numbers):
+ *   [FastVim summary]  gptget.net page on arXiv 2502.00594 (Chinese summary),
+ *                      sections "方法详解" (method details, six bullets),
+ *                      "术语表" (glossary) and "技术贡献".
+ *   [Pith review]      pith.science verdict on 2502.00594, JSON fields
+ *                      "key_machinery", "core_discovery", "minor_comments".
+ *   [Vim article]      ijyty.com/news/106204, section 2.1, vim_block sketch.
+ *   [SF-Mamba article] glsqs.com/news/422358, section 二 (batch folding with
+ *                      periodic state reset).
+ *
+ * Readings of points the pages leave open (each is listed in the design doc):
+ *   - x_proj output is split [delta_lowrank (R) | B (N) | C (N)];
+ *   - s_delta(x) is the low-rank map W_dt * delta_lowrank plus a bias;
+ *   - A = -exp(A_log) (negative real, so the recurrence is stable);
+ *   - B enters as Delta * B_t * u_t (Euler), A as exp(Delta * A) (ZOH);
+ *   - the skip D*x is added after the repeat, on the full-resolution x, with
+ *     one D per direction (the layer adds (D_fwd + D_bwd) * x);
+ *   - the two directions are summed, then gated by silu(z);
+ *   - initial state is zero; no state is output.
+ *
+ * Layouts (all row-major, last index fastest):
+ *   dense x, z, out   (B, h, w, E)            masked x, z, out   (B, K, E)
+ *   u                 (B, T, E)               v (x_proj output)  (B, T, NX), NX = R + 2N
+ *   delta             (B, T, E)               s_fwd, s_bwd       (B, T, E)
+ *   x_proj_w (NX, E)  dt_proj_w (E, R)  dt_proj_b (E)  A_log (E, N)  D (E)
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Pooling axes.  COLS: mean over w, scan over the h rows.  ROWS: the
+ * transposed grid, mean over h, scan over the w columns.  NONE_*: no pooling,
+ * the scan runs over all h*w tokens in row-major (t = i*w + j) or column-major
+ * (t = j*h + i) order. */
+enum { FVO_COLS = 0, FVO_ROWS = 1, FVO_NONE_ROWMAJOR = 2, FVO_NONE_COLMAJOR = 3 };
+
+typedef struct {
+    const float *x_proj_w;  /* (R + 2N, E) */
+    const float *dt_proj_w; /* (E, R) */
+    const float *dt_proj_b; /* (E) */
+    const float *A_log;     /* (E, N) */
+    const float *D;         /* (E) */
+} fvo_dir;
+
+int fvo_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* Scan length T and pooled-axis length P for a dense grid. */
+static void seq_shape(int axis, int64_t h, int64_t w, int64_t *T, int64_t *P)
+{
+    switch (axis) {
+    case FVO_COLS: *T = h; *P = w; break;
+    case FVO_ROWS: *T = w; *P = h; break;
+    default: *T = h * w; *P = 1; break;
+    }
+}
+
+/* Position t along the scan of grid cell (i, j). */
+static int64_t seq_pos(int axis, int64_t h, int64_t w, int64_t i, int64_t j)
+{
+    switch (axis) {
+    case FVO_COLS: return i;
+    case FVO_ROWS: return j;
+    case FVO_NONE_ROWMAJOR: return i * w + j;
+    default: return j * h + i;
+    }
+}
+
+/*
+ * O1, dense pooling.  [FastVim summary, 方法详解 bullets 1-2; 术语表 "Mean
+ * Pooling"]: after the Conv1D the (B, h, w, D) grid is averaged, without
+ * parameters, along one spatial axis, giving (B, h, 1, D).  The transposed
+ * grid of the next block pools the other axis [FastVim summary, 方法详解
+ * bullet 5].  With no pooling u is x itself, read in scan order.
+ *   u[b, t, e] = (1/P) * sum_{cells (i,j) with seq_pos(i,j) = t} x[b, i, j, e]
+ */
+int fvo_pool_dense(const float *x, int64_t B, int64_t h, int64_t w, int64_t E, int axis, double *u)
+{
+    int64_t T, P;
+    if (axis < 0 || axis > 3) return -2;
+    seq_shape(axis, h, w, &T, &P);
+#pragma omp parallel for schedule(static)
+    for (int64_t b = 0; b < B; ++b) {
+        double *ub = u + b * T * E;
+        for (int64_t k = 0; k < T * E; ++k) ub[k] = 0.0;
+        for (int64_t i = 0; i < h; ++i)
+            for (int64_t j = 0; j < w; ++j) {
+                const int64_t t = seq_pos(axis, h, w, i, j);
+                const float *xv = x + ((b * h + i) * w + j) * E;
+                for (int64_t e = 0; e < E; ++e) ub[t * E + e] += (double)xv[e];
+            }
+        for (int64_t k = 0; k < T * E; ++k) ub[k] /= (double)P;
+    }
+    return 0;
+}
+
+/*
+ * Masked rows.  [FastVim summary, 方法详解 bullet 6; 技术贡献]: FastMaskVim
+ * works on the kept tokens' sparse indices into the h*w grid.  A kept token
+ * with flat index q = i*w + j belongs to scan row i (COLS) or to column j
+ * (ROWS).  Returns -3 for an index outside [0, h*w) or a repeated index.
+ */
+int fvo_mask_rows(const int32_t *idx, int64_t B, int64_t K, int64_t h, int64_t w, int axis, int32_t *rows)
+{
+    if (axis != FVO_COLS && axis != FVO_ROWS) return -2;
+    int bad = 0;
+    unsigned char *seen = (unsigned char *)malloc((size_t)(h * w));
+    if (!seen) return -9;
+    for (int64_t b = 0; b < B; ++b) {
+        memset(seen, 0, (size_t)(h * w));
+        for (int64_t k = 0; k < K; ++k) {
+            const int64_t q = idx[b * K + k];
+            if (q < 0 || q >= h * w || seen[q]) { bad = 1; rows[b * K + k] = -1; continue; }
+            seen[q] = 1;
+            rows[b * K + k] = (int32_t)(axis == FVO_COLS ? q / w : q % w);
+        }
+    }
+    free(seen);
+    return bad ? -3 : 0;
+}
+
+/*
+ * O1, masked pooling.  [FastVim summary, 方法详解 bullet 6]: the kept tokens
+ * of a row are summed and normalised by the fixed row length P (w for COLS,
+ * h for ROWS), not by how many tokens of that row were kept.  A row with no
+ * kept token pools to zero and is still scanned.
+ *   u[b, t, e] = (1/P) * sum_{k : rows[b,k] = t} x[b, k, e]
+ */
+int fvo_pool_masked(const float *x, const int32_t *rows, int64_t B, int64_t K, int64_t T, int64_t P,
+                    int64_t E, double *u)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t b = 0; b < B; ++b) {
+        double *ub = u + b * T * E;
+        for (int64_t k = 0; k < T * E; ++k) ub[k] = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            const int64_t t = rows[b * K + k];
+            if (t < 0 || t >= T) continue;
+            const float *xv = x + (b * K + k) * E;
+            for (int64_t e = 0; e < E; ++e) ub[t * E + e] += (double)xv[e];
+        }
+        for (int64_t k = 0; k < T * E; ++k) ub[k] /= (double)P;
+    }
+    return 0;
+}
+
+/*
+ * O2, input-dependent projection.  [FastVim summary, 方法详解 bullet 3]:
+ * Linear_N produces the input-dependent B and C (and the low-rank input of
+ * Delta) from each pooled token.
+ *   v[m, o] = sum_e x_proj_w[o, e] * u[m, e],   o in [0, R + 2N)
+ */
+void fvo_xproj(const double *u, int64_t M, int64_t E, const float *x_proj_w, int64_t NX, double *v)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t o = 0; o < NX; ++o) {
+            double acc = 0.0;
+            for (int64_t e = 0; e < E; ++e) acc += (double)x_proj_w[o * E + e] * u[m * E + e];
+            v[m * NX + o] = acc;
+        }
+}
+
+/* softplus(q) = log(1 + e^q), written in the overflow-free form. */
+static double softplus(double q) { return (q > 0.0 ? q : 0.0) + log1p(exp(-fabs(q))); }
+
+/*
+ * O3, step size.  [FastVim summary, 方法详解 bullet 3]: Delta =
+ * softplus(Parameter + s_Delta(x)); s_Delta is the low-rank map W_dt * v[0:R]
+ * and the Parameter is the bias dt_proj_b.
+ *   delta[m, e] = softplus(sum_r dt_proj_w[e, r] * v[m, r] + dt_proj_b[e])
+ */
+void fvo_delta(const double *v, int64_t M, int64_t NX, int64_t R, const float *dt_proj_w,
+               const float *dt_proj_b, int64_t E, double *delta)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t e = 0; e < E; ++e) {
+            double q = (double)dt_proj_b[e];
+            for (int64_t r = 0; r < R; ++r) q += (double)dt_proj_w[e * R + r] * v[m * NX + r];
+            delta[m * E + e] = softplus(q);
+        }
+}
+
+/*
+ * O4 + O5, discretisation and selective scan.  [FastVim summary, 术语表
+ * "State Space Model": h_t = A h_{t-1} + B x_t, y_t = C h_t (+ D x_t, added
+ * in the output stage); 方法详解 bullets 3-4: zero-order-hold discretisation,
+ * then the forward and the backward selective scans over the pooled
+ * sequence.]  Per image b and channel e, with A[e,n] = -exp(A_log[e,n]):
+ *   H_n <- exp(delta_t * A[e,n]) * H_n + delta_t * B_t[n] * u_t      (H_{-1} = 0)
+ *   s_t  = sum_n C_t[n] * H_n
+ * B_t = v[t, R + n], C_t = v[t, R + N + n].  The backward scan visits
+ * t = T-1 ... 0.  If reset is given, reset[t] != 0 drops the carried state at
+ * step t (the decay is set to zero there), as in [SF-Mamba article, 二,
+ * periodic state reset].
+ */
+void fvo_scan(const double *u, const double *delta, const double *v, int64_t B, int64_t T, int64_t E,
+              int64_t N, int64_t R, int64_t NX, const float *A_log, int reverse,
+              const unsigned char *reset, double *s)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t b = 0; b < B; ++b) {
+        double *H = (double *)malloc((size_t)N * sizeof(double));
+        for (int64_t e = 0; e < E; ++e) {
+            for (int64_t n = 0; n < N; ++n) H[n] = 0.0;
+            for (int64_t step = 0; step < T; ++step) {
+                const int64_t t = reverse ? T - 1 - step : step;
+                const int64_t m = b * T + t;
+                const double d = delta[m * E + e];
+                const double ut = u[m * E + e];
+                const double *vt = v + m * NX;
+                double acc = 0.0;
+                for (int64_t n = 0; n < N; ++n) {
+                    const double A = -exp((double)A_log[e * N + n]);
+                    const double a = (reset && reset[t]) ? 0.0 : exp(d * A);
+                    H[n] = a * H[n] + d * vt[R + n] * ut;
+                    acc += vt[R + N + n] * H[n];
+                }
+                s[m * E + e] = acc;
+            }
+        }
+        free(H);
+    }
+}
+
+/* silu(q) = q * sigmoid(q) */
+static double silu(double q) { return q / (1.0 + exp(-q)); }
+
+/* Stage outputs of one direction, all optional (NULL = not wanted). */
+typedef struct {
+    double *v;     /* (B, T, NX) */
+    double *delta; /* (B, T, E)  */
+    double *s;     /* (B, T, E)  */
+} fvo_dir_out;
+
+static int run_direction(const double *u, int64_t B, int64_t T, int64_t E, int64_t N, int64_t R,
+                         const fvo_dir *p, int reverse, fvo_dir_out *o, double *s_out)
+{
+    const int64_t NX = R + 2 * N, M = B * T;
+    double *v = o && o->v ? o->v : (double *)malloc((size_t)(M * NX) * sizeof(double));
+    double *dl = o && o->delta ? o->delta : (double *)malloc((size_t)(M * E) * sizeof(double));
+    if (!v || !dl) return -9;
+    fvo_xproj(u, M, E, p->x_proj_w, NX, v);
+    fvo_delta(v, M, NX, R, p->dt_proj_w, p->dt_proj_b, E, dl);
+    fvo_scan(u, dl, v, B, T, E, N, R, NX, p->A_log, reverse, NULL, s_out);
+    if (!(o && o->v)) free(v);
+    if (!(o && o->delta)) free(dl);
+    return 0;
+}
+
+/*
+ * The whole layer.  [FastVim summary, 方法详解 bullets 2-5; Pith review,
+ * "key_machinery": the pooled scan output is repeated back to the full token
+ * count before the D*x skip; Vim article 2.1: the two directions are summed
+ * and gated by z.]
+ *   out[b, cell, e] = (s_fwd[b, t(cell), e] + s_bwd[b, t(cell), e]
+ *                      + (D_fwd[e] + D_bwd[e]) * x[b, cell, e]) * silu(z[b, cell, e])
+ * cell is a grid cell (i, j) (dense) or a kept token k (masked, idx != NULL,
+ * axis COLS or ROWS only).  Returns 0, or -2 bad axis, -3 bad mask index,
+ * -9 out of memory.  Optional stage outputs: u_out (B,T,E), rows_out (B,K),
+ * fwd / bwd (v, delta, s).
+ */
+int fvo_layer(const float *x, const float *z, const fvo_dir *pf, const fvo_dir *pb, int64_t B, int64_t h,
+              int64_t w, int64_t E, int64_t N, int64_t R, int64_t K, int axis, const int32_t *idx,
+              double *out, double *u_out, int32_t *rows_out, fvo_dir_out *fwd, fvo_dir_out *bwd)
+{
+    int64_t T, P;
+    const int masked = idx != NULL;
+    if (axis < 0 || axis > 3 || (masked && axis > FVO_ROWS)) return -2;
+    seq_shape(axis, h, w, &T, &P);
+    const int64_t M = B * T;
+
+    double *u = u_out ? u_out : (double *)malloc((size_t)(M * E) * sizeof(double));
+    double *sf = fwd && fwd->s ? fwd->s : (double *)malloc((size_t)(M * E) * sizeof(double));
+    double *sb = bwd && bwd->s ? bwd->s : (double *)malloc((size_t)(M * E) * sizeof(double));
+    int32_t *rows = NULL;
+    int rc = 0;
+    if (!u || !sf || !sb) { rc = -9; goto done; }
+
+    if (masked) {
+        rows = rows_out ? rows_out : (int32_t *)malloc((size_t)(B * K) * sizeof(int32_t));
+        if (!rows) { rc = -9; goto done; }
+        rc = fvo_mask_rows(idx, B, K, h, w, axis, rows);
+        if (rc) goto done;
+        fvo_pool_masked(x, rows, B, K, T, P, E, u);
+    } else {
+        fvo_pool_dense(x, B, h, w, E, axis, u);
+    }
+
+    rc = run_direction(u, B, T, E, N, R, pf, 0, fwd, sf);
+    if (rc) goto done;
+    rc = run_direction(u, B, T, E, N, R, pb, 1, bwd, sb);
+    if (rc) goto done;
+
+    if (masked) {
+#pragma omp parallel for schedule(static)
+        for (int64_t b = 0; b < B; ++b)
+            for (int64_t k = 0; k < K; ++k) {
+                const int64_t t = rows[b * K + k];
+                for (int64_t e = 0; e < E; ++e) {
+                    const int64_t c = (b * K + k) * E + e;
+                    const double skip = ((double)pf->D[e] + (double)pb->D[e]) * (double)x[c];
+                    out[c] = (sf[(b * T + t) * E + e] + sb[(b * T + t) * E + e] + skip) * silu((double)z[c]);
+                }
+            }
+    } else {
+#pragma omp parallel for schedule(static)
+        for (int64_t b = 0; b < B; ++b)
+            for (int64_t i = 0; i < h; ++i)
+                for (int64_t j = 0; j < w; ++j) {
+                    const int64_t t = seq_pos(axis, h, w, i, j);
+                    for (int64_t e = 0; e < E; ++e) {
+                        const int64_t c = ((b * h + i) * w + j) * E + e;
+                        const double skip = ((double)pf->D[e] + (double)pb->D[e]) * (double)x[c];
+                        out[c] = (sf[(b * T + t) * E + e] + sb[(b * T + t) * E + e] + skip) * silu((double)z[c]);
+                    }
+                }
+    }
+
+done:
+    if (!u_out) free(u);
+    if (!(fwd && fwd->s)) free(sf);
+    if (!(bwd && bwd->s)) free(sb);
+    if (masked && !rows_out) free(rows);
+    return rc;
+}

@@ -1,0 +1,448 @@
+"""Checks that pin the fp64 oracle to facts other than itself.
+
+Each ``pin_*`` takes an ``oracle.Oracle`` and raises ``AssertionError`` when the
+oracle disagrees with a closed form, an invariant, a library routine, a
+brute-force evaluation on tiny inputs or the hand-worked golden example.  The
+same checks run against mutated builds of the oracle (``test_oracle_mutants``)
+to show that a plausible slip anywhere in it (a dropped term, a flipped sign,
+a wrong index or a transposed operand) fails at least one of them.
+
+Sources: the FastVim summary page (gptget.net, arXiv 2502.00594), sections
+方法详解 and 术语表; the Pith review of 2502.00594 ("key_machinery", the
+pooling-invariance falsifier); the SF-Mamba article (glsqs.com), section 二
+(periodic state reset).
+"""
+from __future__ import annotations
+
+import os
+
+import numpy as np
+from scipy.special import expit
+
+COLS, ROWS, NONE_ROWMAJOR, NONE_COLMAJOR = 0, 1, 2, 3
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+TIGHT = 1e-12
+
+
+def _close(a, b, tol=TIGHT, what=""):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    assert a.shape == b.shape, (what, a.shape, b.shape)
+    scale = max(np.max(np.abs(b)) if b.size else 0.0, 1e-300)
+    err = np.max(np.abs(a - b)) / scale if a.size else 0.0
+    assert err <= tol, "%s: rel err %.3e > %.1e" % (what, err, tol)
+
+
+def rand_dir(rng, E, N, R, scale=0.3):
+    """A parameter set with every entry distinct and O(1) effects."""
+    return {
+        "x_proj_w": (scale * rng.standard_normal((R + 2 * N, E))).astype(np.float32),
+        "dt_proj_w": (scale * rng.standard_normal((E, R))).astype(np.float32),
+        "dt_proj_b": rng.uniform(-3.0, -0.5, E).astype(np.float32),
+        "A_log": rng.uniform(-1.0, 1.5, (E, N)).astype(np.float32),
+        "D": rng.uniform(0.5, 1.5, E).astype(np.float32),
+    }
+
+
+def silu(z):
+    return np.asarray(z, np.float64) * expit(np.asarray(z, np.float64))
+
+
+def softplus(q):
+    return np.logaddexp(0.0, q)
+
+
+# ---------------------------------------------------------------- brute force
+def bf_direction(u, p, reverse):
+    """s of one direction by the matrix (convolution) form of the SSM:
+    s_t = sum_tau sum_n C_t[n] exp(A[e,n] * sum of delta strictly after tau up
+    to t) delta_tau B_tau[n] u_tau  (forward; mirrored for the backward scan).
+    Uses numpy for the contractions; no recurrence."""
+    B_, T, E = u.shape
+    Wx = p["x_proj_w"].astype(np.float64)
+    N = p["A_log"].shape[1]
+    R = Wx.shape[0] - 2 * N
+    v = u @ Wx.T
+    dl = softplus(v[..., :R] @ p["dt_proj_w"].astype(np.float64).T + p["dt_proj_b"].astype(np.float64))
+    Bm, Cm = v[..., R:R + N], v[..., R + N:]
+    A = -np.exp(p["A_log"].astype(np.float64))  # (E, N)
+    s = np.zeros((B_, T, E))
+    for b in range(B_):
+        cum = np.concatenate([np.zeros((1, E)), np.cumsum(dl[b], axis=0)])  # cum[k] = sum_{<k}
+        for t in range(T):
+            taus = range(0, t + 1) if not reverse else range(t, T)
+            for tau in taus:
+                if not reverse:
+                    span = cum[t + 1] - cum[tau + 1]  # sum_{k=tau+1..t}
+                else:
+                    span = cum[tau] - cum[t]  # sum_{k=t..tau-1}
+                decay = np.exp(A * span[:, None])  # (E, N)
+                s[b, t] += np.sum(Cm[b, t][None, :] * decay * (dl[b, tau] * u[b, tau])[:, None]
+                                  * Bm[b, tau][None, :], axis=1)
+    return s, v, dl
+
+
+def bf_layer(x, z, pf, pb, axis, idx=None, hw=None):
+    """Whole layer from scratch in numpy (means, permutations, matrix-form SSM)."""
+    x = np.asarray(x, np.float64)
+    z = np.asarray(z, np.float64)
+    if idx is None:
+        B_, h, w, E = x.shape
+        if axis == COLS:
+            u = x.mean(axis=2)
+        elif axis == ROWS:
+            u = x.mean(axis=1)
+        elif axis == NONE_ROWMAJOR:
+            u = x.reshape(B_, h * w, E)
+        else:
+            u = x.transpose(0, 2, 1, 3).reshape(B_, h * w, E)
+    else:
+        B_, K, E = x.shape
+        h, w = hw
+        T, P = (h, w) if axis == COLS else (w, h)
+        u = np.zeros((B_, T, E))
+        for b in range(B_):
+            for k in range(K):
+                i, j = divmod(int(idx[b, k]), w)
+                u[b, i if axis == COLS else j] += x[b, k]
+        u /= P
+    sf, _, _ = bf_direction(u, pf, False)
+    sb, _, _ = bf_direction(u, pb, True)
+    s = sf + sb
+    D = pf["D"].astype(np.float64) + pb["D"].astype(np.float64)
+    if idx is None:
+        if axis == COLS:
+            rep = np.repeat(s[:, :, None, :], w, axis=2)
+        elif axis == ROWS:
+            rep = np.repeat(s[:, None, :, :], h, axis=1)
+        elif axis == NONE_ROWMAJOR:
+            rep = s.reshape(B_, h, w, E)
+        else:
+            rep = s.reshape(B_, w, h, E).transpose(0, 2, 1, 3)
+    else:
+        rep = np.zeros_like(x)
+        for b in range(B_):
+            for k in range(K):
+                i, j = divmod(int(idx[b, k]), w)
+                rep[b, k] = s[b, i if axis == COLS else j]
+    return (rep + D * x) * silu(z), u, sf, sb
+
+
+# ----------------------------------------------------------------------- pins
+def pin_golden_worked_example(O):
+    """Hand-derived T=3 example (exact multiples of ln 2)."""
+    vals = {}
+    with open(os.path.join(GOLDEN, "worked_example_T3.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            k, v = line.split(":", 1)
+            vals[k.strip()] = np.array([float(t) for t in v.split()])
+    L = np.log(2.0)
+    x = vals["x"].astype(np.float32).reshape(1, 3, 2, 1)
+    z = vals["z"].astype(np.float32).reshape(1, 3, 2, 1)
+
+    def d(tag):
+        return {
+            "x_proj_w": vals[tag + ".x_proj_w"].astype(np.float32).reshape(5, 1),
+            "dt_proj_w": vals["dt_proj_w"].astype(np.float32).reshape(1, 1),
+            "dt_proj_b": vals["dt_proj_b"].astype(np.float32),
+            "A_log": np.log(vals[tag + ".A_log_exp"]).astype(np.float32).reshape(1, 2),
+            "D": vals[tag + ".D"].astype(np.float32),
+        }
+
+    r = O.layer(x, z, d("fwd"), d("bwd"), COLS, stages=True)
+    # A_log is stored in fp32, so exp(delta * A) is exact only to fp32 rounding of log 2.
+    _close(r["u"].ravel(), vals["u"], what="golden u")
+    _close(r["fwd"]["delta"].ravel(), vals["delta_over_ln2"] * L, what="golden delta")
+    _close(r["fwd"]["s"].ravel(), vals["s_fwd_over_ln2"] * L, tol=1e-7, what="golden s_fwd")
+    _close(r["bwd"]["s"].ravel(), vals["s_bwd_over_ln2"] * L, tol=1e-7, what="golden s_bwd")
+    _close(r["out"].ravel(), vals["out_ln2_coef"] * L + vals["out_const"], tol=1e-7, what="golden out")
+
+
+def pin_geometric_series(O):
+    """Inputs constant along every pooled and scanned position: the scan is a
+    geometric series, s_t = sum_n C_n delta B_n c (1 - a_n^(t+1)) / (1 - a_n)."""
+    rng = np.random.default_rng(11)
+    B_, h, w, E, N, R = 2, 5, 3, 6, 4, 3
+    c = rng.standard_normal((B_, E)).astype(np.float32)
+    x = np.broadcast_to(c[:, None, None, :], (B_, h, w, E)).copy()
+    z = rng.standard_normal((B_, h, w, E)).astype(np.float32)
+    pf, pb = rand_dir(rng, E, N, R), rand_dir(rng, E, N, R)
+    for axis, T in ((COLS, h), (ROWS, w), (NONE_ROWMAJOR, h * w)):
+        r = O.layer(x, z, pf, pb, axis, stages=True)
+        for name, p, rev in (("fwd", pf, False), ("bwd", pb, True)):
+            cc = c.astype(np.float64)
+            v = cc @ p["x_proj_w"].astype(np.float64).T  # (B, NX)
+            dl = softplus(v[:, :R] @ p["dt_proj_w"].astype(np.float64).T + p["dt_proj_b"])  # (B,E)
+            A = -np.exp(p["A_log"].astype(np.float64))
+            a = np.exp(dl[:, :, None] * A[None])  # (B,E,N)
+            Bn, Cn = v[:, R:R + N], v[:, R + N:]
+            t = np.arange(T)
+            k = (T - t) if rev else (t + 1)  # number of terms in the series
+            series = (1 - a[:, None, :, :] ** k[None, :, None, None]) / (1 - a[:, None, :, :])
+            coef = (Cn * Bn)[:, None, None, :] * (dl * cc)[:, None, :, None]
+            expect = np.sum(coef * series, axis=-1)
+            _close(r[name]["s"], expect, what="geometric series %s axis %d" % (name, axis))
+
+
+def pin_delta_to_zero(O):
+    """With the step size driven to ~1e-26 the scan contributes nothing and
+    out = (D_fwd + D_bwd) * x * silu(z)."""
+    rng = np.random.default_rng(12)
+    B_, h, w, E, N, R = 2, 4, 5, 8, 4, 2
+    x = rng.standard_normal((B_, h, w, E)).astype(np.float32)
+    z = rng.standard_normal((B_, h, w, E)).astype(np.float32)
+    pf, pb = rand_dir(rng, E, N, R), rand_dir(rng, E, N, R)
+    pf["dt_proj_b"][:] = -60.0
+    pb["dt_proj_b"][:] = -60.0
+    pf["dt_proj_w"][:] = 0.0
+    pb["dt_proj_w"][:] = 0.0
+    for axis in (COLS, ROWS, NONE_COLMAJOR):
+        out = O.layer(x, z, pf, pb, axis)
+        expect = (pf["D"].astype(np.float64) + pb["D"]) * x * silu(z)
+        _close(out, expect, tol=1e-20 * 1e6, what="delta->0 axis %d" % axis)
+
+
+def pin_flip(O):
+    """The backward scan is the forward scan of the time-reversed sequence."""
+    rng = np.random.default_rng(13)
+    B_, T, E, N, R = 2, 9, 5, 4, 3
+    u = rng.standard_normal((B_, T, E))
+    dl = rng.uniform(0.01, 0.5, (B_, T, E))
+    v = rng.standard_normal((B_, T, R + 2 * N))
+    A_log = rng.uniform(-1, 1, (E, N)).astype(np.float32)
+    sb = O.scan(u, dl, v, A_log, R, reverse=True)
+    sf_flipped = O.scan(u[:, ::-1], dl[:, ::-1], v[:, ::-1], A_log, R, reverse=False)
+    _close(sb, sf_flipped[:, ::-1], what="flip")
+    # and the two directions genuinely differ on this input
+    sf = O.scan(u, dl, v, A_log, R, reverse=False)
+    assert np.max(np.abs(sf - sb)) > 1e-3
+
+
+def pin_width_one_pooling(O):
+    """Pooling over an axis of length 1 is the identity, so the pooled layer
+    equals the unpooled layer (both raster orders) on that grid."""
+    rng = np.random.default_rng(14)
+    B_, h, E, N, R = 2, 7, 6, 4, 3
+    pf, pb = rand_dir(rng, E, N, R), rand_dir(rng, E, N, R)
+    x = rng.standard_normal((B_, h, 1, E)).astype(np.float32)
+    z = rng.standard_normal((B_, h, 1, E)).astype(np.float32)
+    ref = O.layer(x, z, pf, pb, NONE_ROWMAJOR)
+    _close(O.layer(x, z, pf, pb, COLS), ref, what="w=1 COLS")
+    _close(O.layer(x, z, pf, pb, NONE_COLMAJOR), ref, what="w=1 colmajor")
+    xt, zt = x.transpose(0, 2, 1, 3).copy(), z.transpose(0, 2, 1, 3).copy()  # (B,1,h,E)
+    _close(O.layer(xt, zt, pf, pb, ROWS), O.layer(xt, zt, pf, pb, NONE_ROWMAJOR), what="h=1 ROWS")
+
+
+def pin_reset_equals_independent(O):
+    """A scan over concatenated sequences with the decay forced to zero at each
+    sequence start equals independent scans of the pieces."""
+    rng = np.random.default_rng(15)
+    E, N, R = 4, 3, 2
+    lens = [3, 5, 1, 4]
+    A_log = rng.uniform(-1, 1, (E, N)).astype(np.float32)
+    pieces = [(rng.standard_normal((1, L, E)), rng.uniform(0.05, 0.6, (1, L, E)),
+               rng.standard_normal((1, L, R + 2 * N))) for L in lens]
+    u = np.concatenate([p[0] for p in pieces], axis=1)
+    dl = np.concatenate([p[1] for p in pieces], axis=1)
+    v = np.concatenate([p[2] for p in pieces], axis=1)
+    reset = np.zeros(sum(lens), np.uint8)
+    reset[np.cumsum([0] + lens[:-1])] = 1
+    s = O.scan(u, dl, v, A_log, R, reverse=False, reset=reset)
+    ind = np.concatenate([O.scan(p[0], p[1], p[2], A_log, R) for p in pieces], axis=1)
+    _close(s, ind, what="reset")
+    assert np.max(np.abs(O.scan(u, dl, v, A_log, R) - ind)) > 1e-4  # the reset matters
+
+
+def pin_brute_force_layer(O):
+    """Tiny layers against a from-scratch numpy evaluation (matrix-form SSM)."""
+    rng = np.random.default_rng(16)
+    B_, h, w, E, N, R = 2, 4, 3, 3, 4, 2
+    pf, pb = rand_dir(rng, E, N, R), rand_dir(rng, E, N, R)
+    x = rng.standard_normal((B_, h, w, E)).astype(np.float32)
+    z = rng.standard_normal((B_, h, w, E)).astype(np.float32)
+    for axis in (COLS, ROWS, NONE_ROWMAJOR, NONE_COLMAJOR):
+        r = O.layer(x, z, pf, pb, axis, stages=True)
+        out, u, sf, sb = bf_layer(x, z, pf, pb, axis)
+        _close(r["u"], u, what="bf u axis %d" % axis)
+        _close(r["fwd"]["s"], sf, tol=1e-11, what="bf s_fwd axis %d" % axis)
+        _close(r["bwd"]["s"], sb, tol=1e-11, what="bf s_bwd axis %d" % axis)
+        _close(r["out"], out, tol=1e-11, what="bf out axis %d" % axis)
+    K = 5
+    idx = np.stack([rng.permutation(h * w)[:K] for _ in range(B_)]).astype(np.int32)
+    xm = rng.standard_normal((B_, K, E)).astype(np.float32)
+    zm = rng.standard_normal((B_, K, E)).astype(np.float32)
+    for axis in (COLS, ROWS):
+        r = O.layer(xm, zm, pf, pb, axis, idx=idx, hw=(h, w), stages=True)
+        out, u, sf, sb = bf_layer(xm, zm, pf, pb, axis, idx=idx, hw=(h, w))
+        _close(r["u"], u, what="bf masked u axis %d" % axis)
+        _close(r["out"], out, tol=1e-11, what="bf masked out axis %d" % axis)
+
+
+def pin_pooling_invariance(O):
+    """Permuting the pooled positions within every scanned row (x and z alike)
+    leaves the scan unchanged and permutes out the same way (the Pith review's
+    falsifier: inputs equal after pooling give equal scan outputs)."""
+    rng = np.random.default_rng(17)
+    B_, h, w, E, N, R = 2, 4, 6, 5, 4, 2
+    pf, pb = rand_dir(rng, E, N, R), rand_dir(rng, E, N, R)
+    x = rng.standard_normal((B_, h, w, E)).astype(np.float32)
+    z = rng.standard_normal((B_, h, w, E)).astype(np.float32)
+    r = O.layer(x, z, pf, pb, COLS, stages=True)
+    perm = [rng.permutation(w) for _ in range(h)]
+    xp = np.stack([x[:, i, perm[i]] for i in range(h)], axis=1)
+    zp = np.stack([z[:, i, perm[i]] for i in range(h)], axis=1)
+    rp = O.layer(xp, zp, pf, pb, COLS, stages=True)
+    _close(rp["fwd"]["s"] + rp["bwd"]["s"], r["fwd"]["s"] + r["bwd"]["s"], tol=1e-13, what="perm s")
+    _close(rp["out"], np.stack([r["out"][:, i, perm[i]] for i in range(h)], axis=1), tol=1e-13,
+           what="perm out")
+
+
+def pin_transpose(O):
+    """ROWS pooling is COLS pooling on the transposed grid, and column-major
+    unpooled order is row-major order on the transposed grid."""
+    rng = np.random.default_rng(18)
+    B_, h, w, E, N, R = 2, 3, 5, 4, 4, 2
+    pf, pb = rand_dir(rng, E, N, R), rand_dir(rng, E, N, R)
+    x = rng.standard_normal((B_, h, w, E)).astype(np.float32)
+    z = rng.standard_normal((B_, h, w, E)).astype(np.float32)
+    xt, zt = x.transpose(0, 2, 1, 3).copy(), z.transpose(0, 2, 1, 3).copy()
+    for a, b in ((ROWS, COLS), (NONE_COLMAJOR, NONE_ROWMAJOR)):
+        _close(O.layer(x, z, pf, pb, a), O.layer(xt, zt, pf, pb, b).transpose(0, 2, 1, 3),
+               what="transpose %d/%d" % (a, b))
+
+
+def pin_masked_equals_zero_filled(O):
+    """Masked pooling (sum of kept tokens / fixed P) equals dense pooling of the
+    grid with the dropped tokens set to zero, at every kept position."""
+    rng = np.random.default_rng(19)
+    B_, h, w, E, N, R, K = 3, 5, 4, 6, 4, 3, 7
+    pf, pb = rand_dir(rng, E, N, R), rand_dir(rng, E, N, R)
+    idx = np.stack([rng.permutation(h * w)[:K] for _ in range(B_)]).astype(np.int32)
+    xm = rng.standard_normal((B_, K, E)).astype(np.float32)
+    zm = rng.standard_normal((B_, K, E)).astype(np.float32)
+    xf = np.zeros((B_, h * w, E), np.float32)
+    zf = np.zeros((B_, h * w, E), np.float32)
+    for b in range(B_):
+        xf[b, idx[b]] = xm[b]
+        zf[b, idx[b]] = zm[b]
+    xf, zf = xf.reshape(B_, h, w, E), zf.reshape(B_, h, w, E)
+    for axis in (COLS, ROWS):
+        dense = O.layer(xf, zf, pf, pb, axis).reshape(B_, h * w, E)
+        masked = O.layer(xm, zm, pf, pb, axis, idx=idx, hw=(h, w))
+        _close(masked, np.stack([dense[b, idx[b]] for b in range(B_)]), what="zero-fill axis %d" % axis)
+
+
+def pin_all_kept(O):
+    """With every token kept (any order) the masked layer is the dense layer."""
+    rng = np.random.default_rng(20)
+    B_, h, w, E, N, R = 2, 4, 3, 5, 4, 2
+    pf, pb = rand_dir(rng, E, N, R), rand_dir(rng, E, N, R)
+    x = rng.standard_normal((B_, h, w, E)).astype(np.float32)
+    z = rng.standard_normal((B_, h, w, E)).astype(np.float32)
+    idx = np.stack([rng.permutation(h * w) for _ in range(B_)]).astype(np.int32)
+    xf, zf = x.reshape(B_, h * w, E), z.reshape(B_, h * w, E)
+    xm = np.stack([xf[b, idx[b]] for b in range(B_)])
+    zm = np.stack([zf[b, idx[b]] for b in range(B_)])
+    for axis in (COLS, ROWS):
+        dense = O.layer(x, z, pf, pb, axis).reshape(B_, h * w, E)
+        masked = O.layer(xm, zm, pf, pb, axis, idx=idx, hw=(h, w))
+        _close(masked, np.stack([dense[b, idx[b]] for b in range(B_)]), what="all kept axis %d" % axis)
+
+
+def pin_zero_projection(O):
+    """x_proj_w = 0 gives B = C = 0, so the scan output is exactly zero."""
+    rng = np.random.default_rng(21)
+    B_, h, w, E, N, R = 2, 3, 4, 5, 4, 2
+    pf, pb = rand_dir(rng, E, N, R), rand_dir(rng, E, N, R)
+    pf["x_proj_w"][:] = 0
+    pb["x_proj_w"][:] = 0
+    x = rng.standard_normal((B_, h, w, E)).astype(np.float32)
+    z = rng.standard_normal((B_, h, w, E)).astype(np.float32)
+    r = O.layer(x, z, pf, pb, COLS, stages=True)
+    assert np.all(r["fwd"]["s"] == 0) and np.all(r["bwd"]["s"] == 0)
+    _close(r["out"], (pf["D"].astype(np.float64) + pb["D"]) * x * silu(z), what="W_x=0")
+
+
+def pin_linear_in_D(O):
+    """out(D) - out(D=0) = (D_fwd + D_bwd) * x * silu(z)."""
+    rng = np.random.default_rng(22)
+    B_, h, w, E, N, R = 2, 4, 4, 6, 4, 3
+    pf, pb = rand_dir(rng, E, N, R), rand_dir(rng, E, N, R)
+    x = rng.standard_normal((B_, h, w, E)).astype(np.float32)
+    z = rng.standard_normal((B_, h, w, E)).astype(np.float32)
+    f0, b0 = dict(pf), dict(pb)
+    f0["D"] = np.zeros(E, np.float32)
+    b0["D"] = np.zeros(E, np.float32)
+    for axis in (COLS, ROWS):
+        diff = O.layer(x, z, pf, pb, axis) - O.layer(x, z, f0, b0, axis)
+        _close(diff, (pf["D"].astype(np.float64) + pb["D"]) * x * silu(z), tol=1e-12,
+               what="linear in D axis %d" % axis)
+
+
+def pin_library_routines(O):
+    """Stages that are textbook operations equal numpy's: the mean over an
+    axis, the x_proj contraction (matmul), softplus (logaddexp)."""
+    rng = np.random.default_rng(23)
+    x = rng.standard_normal((2, 5, 7, 8)).astype(np.float32)
+    _close(O.pool_dense(x, COLS), x.astype(np.float64).mean(axis=2), tol=1e-15, what="mean cols")
+    _close(O.pool_dense(x, ROWS), x.astype(np.float64).mean(axis=1), tol=1e-15, what="mean rows")
+    u = rng.standard_normal((3, 4, 8))
+    W = rng.standard_normal((11, 8)).astype(np.float32)
+    _close(O.xproj(u, W), u @ W.astype(np.float64).T, tol=1e-14, what="xproj")
+    v = rng.standard_normal((3, 4, 11)) * 4
+    Wdt = rng.standard_normal((8, 3)).astype(np.float32)
+    bdt = rng.standard_normal(8).astype(np.float32) * 10
+    expect = softplus(v[..., :3] @ Wdt.astype(np.float64).T + bdt)
+    _close(O.delta(v, 3, Wdt, bdt), expect, tol=1e-14, what="softplus")
+    # softplus at large |q| (no overflow, no cancellation)
+    big = np.array([[[60.0] + [0.0] * 10]])
+    got = O.delta(big, 1, np.ones((1, 1), np.float32), np.zeros(1, np.float32))
+    assert abs(got.item() - 60.0) < 1e-12
+    got = O.delta(-big, 1, np.ones((1, 1), np.float32), np.zeros(1, np.float32))
+    assert abs(got.item() / np.exp(-60.0) - 1.0) < 1e-12
+
+
+def pin_mask_rows_exact(O):
+    """Kept-token rows are idx div w (COLS) or idx mod w (ROWS), exactly; masked
+    pooled sums of integer-valued tokens are exact integers."""
+    rng = np.random.default_rng(24)
+    B_, h, w, K, E = 4, 7, 5, 12, 3
+    idx = np.stack([rng.permutation(h * w)[:K] for _ in range(B_)]).astype(np.int32)
+    rc = O.mask_rows(idx, h, w, COLS)
+    rr = O.mask_rows(idx, h, w, ROWS)
+    assert np.array_equal(rc, idx // w) and np.array_equal(rr, idx % w)
+    x = np.broadcast_to((np.arange(K, dtype=np.float32) + 1)[None, :, None], (B_, K, E)).copy()
+    for rows, T, P in ((rc, h, w), (rr, w, h)):
+        sums = np.zeros((B_, T, E))
+        for b in range(B_):
+            np.add.at(sums[b], rows[b], x[b].astype(np.float64))
+        u = O.pool_masked(x, rows, T, P)
+        assert np.array_equal(u * P, sums)
+    for bad in ([0, h * w], [3, 3], [-1, 2]):
+        try:
+            O.mask_rows(np.array([bad], np.int32), h, w, COLS)
+        except ValueError:
+            continue
+        raise AssertionError("invalid mask index %s accepted" % (bad,))
+
+
+ALL_PINS = [
+    pin_golden_worked_example,
+    pin_geometric_series,
+    pin_delta_to_zero,
+    pin_flip,
+    pin_width_one_pooling,
+    pin_reset_equals_independent,
+    pin_brute_force_layer,
+    pin_pooling_invariance,
+    pin_transpose,
+    pin_masked_equals_zero_filled,
+    pin_all_kept,
+    pin_zero_projection,
+    pin_linear_in_D,
+    pin_library_routines,
+    pin_mask_rows_exact,
+]

@@ -1,0 +1,87 @@
+"""Plant plausible mistakes in copies of the oracle (CPU only) and check that
+the pin suite catches every one of them.
+
+Each mutant is the oracle's C source with one textual change, compiled into a
+temporary directory and exercised in a child process (a mutant that indexes
+out of bounds may crash; a crash counts as caught).  The real oracle is never
+modified.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+import pytest
+
+import oracle
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "fastvim_oracle.c")
+
+# (name, original text, replacement, occurrences)
+MUTANTS = [
+    ("A sign flipped", "const double A = -exp(", "const double A = exp(", 1),
+    ("output taken before the state update",
+     "H[n] = a * H[n] + d * vt[R + n] * ut;\n                    acc += vt[R + N + n] * H[n];",
+     "acc += vt[R + N + n] * H[n];\n                    H[n] = a * H[n] + d * vt[R + n] * ut;", 1),
+    ("delta dropped from the input term", "H[n] = a * H[n] + d * vt[R + n] * ut;",
+     "H[n] = a * H[n] + vt[R + n] * ut;", 1),
+    ("input term dropped u", "H[n] = a * H[n] + d * vt[R + n] * ut;", "H[n] = a * H[n] + d * vt[R + n];", 1),
+    ("B and C swapped", "H[n] = a * H[n] + d * vt[R + n] * ut;\n                    acc += vt[R + N + n] * H[n];",
+     "H[n] = a * H[n] + d * vt[R + N + n] * ut;\n                    acc += vt[R + n] * H[n];", 1),
+    ("delta not in the decay", "exp(d * A)", "exp(A)", 1),
+    ("backward scan not reversed", "reverse ? T - 1 - step : step", "step", 1),
+    ("dense pool not normalised", "        for (int64_t k = 0; k < T * E; ++k) ub[k] /= (double)P;\n    }\n    return 0;\n}\n\n/*\n * Masked rows.",
+     "    }\n    return 0;\n}\n\n/*\n * Masked rows.", 1),
+    ("masked pool normalised by E", "            for (int64_t e = 0; e < E; ++e) ub[t * E + e] += (double)xv[e];\n        }\n        for (int64_t k = 0; k < T * E; ++k) ub[k] /= (double)P;",
+     "            for (int64_t e = 0; e < E; ++e) ub[t * E + e] += (double)xv[e];\n        }\n        for (int64_t k = 0; k < T * E; ++k) ub[k] /= (double)K;", 1),
+    ("only the forward D in the skip", "((double)pf->D[e] + (double)pb->D[e])", "((double)pf->D[e])", 2),
+    ("gate uses sigmoid(-z)", "return q / (1.0 + exp(-q));", "return q / (1.0 + exp(q));", 1),
+    ("softplus without log", "log1p(exp(-fabs(q)))", "exp(-fabs(q))", 1),
+    ("dt_proj transposed", "dt_proj_w[e * R + r]", "dt_proj_w[r * E + e]", 1),
+    ("x_proj transposed", "x_proj_w[o * E + e]", "x_proj_w[e * NX + o]", 1),
+    ("ROWS pooling scans rows", "case FVO_ROWS: return j;", "case FVO_ROWS: return i;", 1),
+    ("column-major uses w", "default: return j * h + i;", "default: return j * w + i;", 1),
+    ("masked ROWS uses the row", "q / w : q % w", "q / w : q / w", 1),
+    ("bias dropped from delta", "double q = (double)dt_proj_b[e];", "double q = 0.0;", 1),
+    ("low-rank delta reads B", "dt_proj_w[e * R + r] * v[m * NX + r]", "dt_proj_w[e * R + r] * v[m * NX + R + r]", 1),
+    ("repeat uses the wrong direction sum", "out[c] = (sf[(b * T + t) * E + e] + sb[(b * T + t) * E + e] + skip)",
+     "out[c] = (sf[(b * T + t) * E + e] + sf[(b * T + t) * E + e] + skip)", 2),
+    ("reset ignored", "(reset && reset[t]) ? 0.0 : exp(d * A)", "exp(d * A)", 1),
+    ("duplicate mask index accepted", "if (q < 0 || q >= h * w || seen[q])", "if (q < 0 || q >= h * w)", 1),
+]
+
+
+@pytest.fixture(scope="module")
+def source():
+    with open(SRC) as f:
+        return f.read()
+
+
+@pytest.mark.parametrize("name,old,new,count", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(name, old, new, count, source, tmp_path):
+    assert source.count(old) == count, "mutation site for %r not found %d times" % (name, count)
+    mutated = source.replace(old, new)
+    src = tmp_path / "mutant.c"
+    src.write_text(mutated)
+    lib = oracle.build(force=True, src=str(src), out=str(tmp_path / "libmutant.so"))
+    proc = subprocess.run([sys.executable, "-c", _CHILD, lib], capture_output=True, text=True,
+                          timeout=300, cwd=os.path.dirname(os.path.dirname(SRC)))
+    if proc.returncode < 0:
+        return  # the mutant crashed: caught
+    assert proc.returncode == 0, proc.stderr[-2000:]
+    caught = [ln for ln in proc.stdout.splitlines() if ln.startswith("CAUGHT ")]
+    assert caught, "mutant %r passes every pin" % name
+
+
+_CHILD = """
+import sys
+sys.path[:0] = ['.', 'tests']
+import oracle, pins
+O = oracle.Oracle(sys.argv[1])
+for pin in pins.ALL_PINS:
+    try:
+        pin(O)
+    except (AssertionError, ValueError, FloatingPointError) as e:
+        print('CAUGHT', pin.__name__, str(e)[:200], flush=True)
+"""
