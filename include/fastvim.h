@@ -1,0 +1,185 @@
+/*
+ * fastvim.h -- C ABI of the MI355X (gfx950) pooled bidirectional
+ * selective-scan layer of FastVim (Fast Vision Mamba, arXiv 2502.00594).
+ *
+ * What one call computes (FastVim summary page, gptget.net, section 方法详解,
+ * bullets 1-6; Pith review of 2502.00594, field "key_machinery"; Vim article,
+ * ijyty.com, section 2.1):
+ *
+ *   1. mean-pool the post-Conv1D token grid x (B, h, w, E) along one spatial
+ *      axis: COLS averages over w and scans the h rows, ROWS (the transposed
+ *      grid of the next block) averages over h and scans the w columns:
+ *          u[b, t, e] = (1/P) * sum_p x[b, (t, p), e]
+ *   2. per direction d in {fwd, bwd}: v = x_proj_w^d u split as
+ *      [delta_lowrank (R) | B_t (N) | C_t (N)], and the step size
+ *          Delta[b, t, e] = softplus(dt_proj_w^d[e, :] . delta_lowrank + dt_proj_b^d[e])
+ *   3. zero-order-hold decay and selective scan, forward over t = 0..T-1 and
+ *      backward over t = T-1..0, with A^d = -exp(A_log^d) and H = 0 at start:
+ *          H[e, n] <- exp(Delta * A^d[e, n]) * H[e, n] + Delta * B_t[n] * u[b, t, e]
+ *          s^d[b, t, e] = sum_n C_t[n] * H[e, n]
+ *   4. repeat back over the pooled axis, add the skip, sum the directions and
+ *      gate:
+ *          out[b, i, j, e] = (s^fwd[b, t, e] + s^bwd[b, t, e]
+ *                             + (D^fwd[e] + D^bwd[e]) * x[b, i, j, e]) * silu(z[b, i, j, e])
+ *      with t = i (COLS) or t = j (ROWS).  Every output is written once.
+ *
+ * Masked (FastMaskVim, same page, bullet 6): x, z and out hold only the K kept
+ * tokens of each image, (B, K, E), and mask_idx (B, K) gives each kept
+ * token's flat index q = i*w + j into the h x w grid.  A row sums its kept
+ * tokens and divides by the fixed row length P (w for COLS, h for ROWS); an
+ * empty row pools to zero and is still scanned; out[b, k] uses the scan
+ * output of the token's own row.
+ *
+ * Unpooled (FASTVIM_POOL_NONE_*): the same layer with no pooling, the scan
+ * running over all T = h*w tokens in row-major (t = i*w + j) or column-major
+ * (t = j*h + i) order.  It exists to measure what pooling saves.
+ *
+ * Conventions for every entry point:
+ *   - device pointers (x, z, out, mask_idx, parameters, workspace) are HIP
+ *     device memory owned by the caller; the library keeps no pointer after a
+ *     call returns and allocates nothing;
+ *   - stream is a hipStream_t passed as void* (NULL = the legacy default
+ *     stream); work is only enqueued on it, nothing synchronises the host;
+ *   - the return value is FASTVIM_OK (0) or a negative fastvim_status; on an
+ *     argument error nothing has been launched.  No exception crosses the ABI;
+ *   - calls that share a workspace must not overlap in time (the workspace
+ *     holds the pooled tokens, projections and scan outputs of a call).
+ */
+#ifndef FASTVIM_H
+#define FASTVIM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FASTVIM_ABI_VERSION 1
+
+typedef enum fastvim_status {
+    FASTVIM_OK = 0,
+    FASTVIM_ERR_NULL = -1,        /* a required pointer is NULL */
+    FASTVIM_ERR_DIMS = -2,        /* a size is out of range or inconsistent */
+    FASTVIM_ERR_UNSUPPORTED = -3, /* valid shape this build does not run (N != 16, R > 64, E > 4096, E % vec) */
+    FASTVIM_ERR_ALIGN = -4,       /* x, z, out, x_proj_w not 16-byte aligned; workspace not 256-byte; others not 4-byte */
+    FASTVIM_ERR_OVERLAP = -5,     /* out overlaps x or z, or the workspace overlaps an input or output */
+    FASTVIM_ERR_WORKSPACE = -6,   /* workspace NULL or smaller than fastvim_ssm_workspace_bytes */
+    FASTVIM_ERR_HIP = -7,         /* a HIP launch or copy reported an error */
+    FASTVIM_ERR_ARG = -8          /* bad enum value, stage id or export id, or mask_idx given with K = 0 */
+} fastvim_status;
+
+/* Element type of x, z and out.  Parameters are always fp32; all arithmetic
+ * (pooled sums, projections, scan state, epilogue) is fp32.  bf16 outputs are
+ * rounded to nearest even. */
+typedef enum fastvim_dtype { FASTVIM_F32 = 0, FASTVIM_BF16 = 1 } fastvim_dtype;
+
+typedef enum fastvim_pool_axis {
+    FASTVIM_POOL_COLS = 0,          /* mean over w, scan over h (T = h, P = w) */
+    FASTVIM_POOL_ROWS = 1,          /* mean over h, scan over w (T = w, P = h): the transposed grid */
+    FASTVIM_POOL_NONE_ROWMAJOR = 2, /* no pooling, T = h*w, t = i*w + j */
+    FASTVIM_POOL_NONE_COLMAJOR = 3  /* no pooling, T = h*w, t = j*h + i */
+} fastvim_pool_axis;
+
+/* Problem sizes.  B images of an h x w token grid with E channels (d_inner),
+ * state size N, dt rank R.  K > 0 selects the masked layer with K kept tokens
+ * per image (then mask_idx is required and pool_axis must be COLS or ROWS);
+ * K = 0 is the dense layer.  B = 0 is a valid empty call (returns FASTVIM_OK,
+ * launches nothing).  Limits of this build: N = 16, 1 <= R <= 64,
+ * E <= 4096 and E % 4 == 0 (fp32) or E % 8 == 0 (bf16); masked grids
+ * h*w <= 16384; unpooled T = h*w <= 2^31 - 1. */
+typedef struct fastvim_dims {
+    int64_t B, h, w, E, N, R, K;
+    int32_t io_dtype; /* fastvim_dtype */
+    int32_t reserved; /* set to 0 */
+} fastvim_dims;
+
+/* One scan direction's parameters, all fp32, contiguous, row-major device
+ * memory, 4-byte aligned (x_proj_w 16-byte aligned):
+ *   x_proj_w (R + 2N, E): rows [0, R) give the low-rank step input, rows
+ *                         [R, R+N) give B_t, rows [R+N, R+2N) give C_t;
+ *   dt_proj_w (E, R), dt_proj_b (E), A_log (E, N) with A = -exp(A_log), D (E). */
+typedef struct fastvim_dir_params {
+    const float *x_proj_w;
+    const float *dt_proj_w;
+    const float *dt_proj_b;
+    const float *A_log;
+    const float *D;
+} fastvim_dir_params;
+
+typedef struct fastvim_params {
+    fastvim_dir_params fwd; /* forward scan (t ascending) */
+    fastvim_dir_params bwd; /* backward scan (t descending) */
+    void *workspace;        /* device scratch, >= fastvim_ssm_workspace_bytes, 256-byte aligned */
+    size_t workspace_bytes;
+    uint32_t flags;         /* reserved, set to 0 */
+    uint32_t reserved;
+} fastvim_params;
+
+/* Bytes of workspace a call with these sizes needs (0 if the sizes are
+ * invalid).  Dense pooled layers need 4 * B * T * (3E + 2(R + 2N)) bytes plus
+ * alignment; unpooled layers hold the per-token projections and scan outputs
+ * (at B = 128, h = w = 128, E = 384 about 7.2 GB). */
+size_t fastvim_ssm_workspace_bytes(const fastvim_dims *dims, int pool_axis);
+
+/* The layer.  x, z, out: (B, h, w, E) dense or (B, K, E) masked, contiguous,
+ * element type dims->io_dtype, 16-byte aligned; out must not overlap x or z.
+ * mask_idx: (B, K) int32 flat grid indices (masked only, else NULL).  Every
+ * index must lie in [0, h*w) and be unique within its image; a token whose
+ * index breaks this gets NaN in every output channel (and is counted, see
+ * FASTVIM_EXPORT_BAD_TOKENS), the other tokens of that image pool as if it
+ * were absent.  Enqueues its kernels on stream and returns. */
+int fastvim_ssm_fwd(const void *x, const void *z, const fastvim_params *params, const fastvim_dims *dims,
+                    int pool_axis, const int32_t *mask_idx, void *out, void *stream);
+
+/* The layer's stages, for timing and inspection.  fastvim_ssm_fwd runs
+ * ROWS (masked only), POOL (pooled only), PROJ, SCAN and EPILOGUE in that
+ * order; fastvim_ssm_stage runs one of them with the same arguments, reading
+ * what earlier stages left in the workspace.  Running a stage before the
+ * stages it depends on gives unspecified (but in-bounds) results. */
+typedef enum fastvim_stage {
+    FASTVIM_STAGE_ROWS = 0,     /* masked: validate mask_idx, row of every kept token */
+    FASTVIM_STAGE_POOL = 1,     /* u = pooled tokens */
+    FASTVIM_STAGE_PROJ = 2,     /* v = x_proj of u (both directions) */
+    FASTVIM_STAGE_SCAN = 3,     /* step sizes, decays and both scans -> s_fwd, s_bwd */
+    FASTVIM_STAGE_EPILOGUE = 4  /* repeat + skip + gate -> out */
+} fastvim_stage;
+
+int fastvim_ssm_stage(int stage, const void *x, const void *z, const fastvim_params *params,
+                      const fastvim_dims *dims, int pool_axis, const int32_t *mask_idx, void *out,
+                      void *stream);
+
+/* Copy one intermediate result of the last call that used this workspace into
+ * dst (device memory, dst_bytes large enough), enqueued on stream:
+ *   U           (B, T, E)        fp32 pooled tokens (pooled layers only)
+ *   XDBL        (B, T, 2, R+2N)  fp32 x_proj outputs, [.., 0, :] fwd, [.., 1, :] bwd
+ *   S_FWD/S_BWD (B, T, E)        fp32 scan outputs of each direction
+ *   ROWS        (B, K)           int32 row (COLS) or column (ROWS) of each kept token, -1 if invalid
+ *   BAD_TOKENS  (B)              int32 number of invalid mask entries per image
+ * Returns FASTVIM_ERR_ARG for an export the layer does not have. */
+typedef enum fastvim_export {
+    FASTVIM_EXPORT_U = 0,
+    FASTVIM_EXPORT_XDBL = 1,
+    FASTVIM_EXPORT_S_FWD = 2,
+    FASTVIM_EXPORT_S_BWD = 3,
+    FASTVIM_EXPORT_ROWS = 4,
+    FASTVIM_EXPORT_BAD_TOKENS = 5
+} fastvim_export;
+
+int fastvim_ssm_export(const fastvim_params *params, const fastvim_dims *dims, int pool_axis, int what,
+                       void *dst, size_t dst_bytes, void *stream);
+
+/* Size in bytes of an export (0 if the layer does not have it). */
+size_t fastvim_ssm_export_bytes(const fastvim_dims *dims, int pool_axis, int what);
+
+/* Static text for a status code. */
+const char *fastvim_status_string(int status);
+
+/* FASTVIM_ABI_VERSION of the built library. */
+int fastvim_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FASTVIM_H */

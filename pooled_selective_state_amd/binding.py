@@ -1,0 +1,211 @@
+"""ctypes binding of ``libfastvim.so`` (declared in ``include/fastvim.h``).
+
+Argument marshalling only: torch provides device memory and the current HIP
+stream, every step of the layer runs in the library's HIP kernels.  There is
+no fallback: if the library is not built, loading it raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Dict, Optional, Tuple
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libfastvim.so")
+
+# fastvim_pool_axis
+POOL_COLS, POOL_ROWS, POOL_NONE_ROWMAJOR, POOL_NONE_COLMAJOR = 0, 1, 2, 3
+# fastvim_dtype
+F32, BF16 = 0, 1
+# fastvim_stage
+STAGE_ROWS, STAGE_POOL, STAGE_PROJ, STAGE_SCAN, STAGE_EPILOGUE = 0, 1, 2, 3, 4
+# fastvim_export
+EXPORT_U, EXPORT_XDBL, EXPORT_S_FWD, EXPORT_S_BWD, EXPORT_ROWS, EXPORT_BAD_TOKENS = 0, 1, 2, 3, 4, 5
+
+STATUS = {
+    0: "FASTVIM_OK", -1: "FASTVIM_ERR_NULL", -2: "FASTVIM_ERR_DIMS", -3: "FASTVIM_ERR_UNSUPPORTED",
+    -4: "FASTVIM_ERR_ALIGN", -5: "FASTVIM_ERR_OVERLAP", -6: "FASTVIM_ERR_WORKSPACE", -7: "FASTVIM_ERR_HIP",
+    -8: "FASTVIM_ERR_ARG",
+}
+
+DIR_FIELDS = ("x_proj_w", "dt_proj_w", "dt_proj_b", "A_log", "D")
+
+
+class FastVimError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = lib().fastvim_status_string(status).decode()
+        super().__init__("%s: %s (%d, %s)" % (where, msg, status, STATUS.get(status, "?")))
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int64), ("h", ctypes.c_int64), ("w", ctypes.c_int64), ("E", ctypes.c_int64),
+                ("N", ctypes.c_int64), ("R", ctypes.c_int64), ("K", ctypes.c_int64),
+                ("io_dtype", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+class DirParams(ctypes.Structure):
+    _fields_ = [(f, ctypes.c_void_p) for f in DIR_FIELDS]
+
+
+class Params(ctypes.Structure):
+    _fields_ = [("fwd", DirParams), ("bwd", DirParams), ("workspace", ctypes.c_void_p),
+                ("workspace_bytes", ctypes.c_size_t), ("flags", ctypes.c_uint32), ("reserved", ctypes.c_uint32)]
+
+
+EXPORTED_SYMBOLS = (
+    "fastvim_ssm_workspace_bytes", "fastvim_ssm_fwd", "fastvim_ssm_stage", "fastvim_ssm_export",
+    "fastvim_ssm_export_bytes", "fastvim_status_string", "fastvim_abi_version",
+)
+
+_lock = threading.Lock()
+_lib = None
+
+
+def lib():
+    """Load ``libfastvim.so`` (raises if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError("libfastvim.so is not built; run `python -m pooled_selective_state_amd.build`")
+            L = ctypes.CDLL(LIB_PATH)
+            vp, ci, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+            PD, PP = ctypes.POINTER(Dims), ctypes.POINTER(Params)
+            L.fastvim_ssm_workspace_bytes.argtypes = [PD, ci]
+            L.fastvim_ssm_workspace_bytes.restype = sz
+            L.fastvim_ssm_fwd.argtypes = [vp, vp, PP, PD, ci, vp, vp, vp]
+            L.fastvim_ssm_fwd.restype = ci
+            L.fastvim_ssm_stage.argtypes = [ci, vp, vp, PP, PD, ci, vp, vp, vp]
+            L.fastvim_ssm_stage.restype = ci
+            L.fastvim_ssm_export.argtypes = [PP, PD, ci, ci, vp, sz, vp]
+            L.fastvim_ssm_export.restype = ci
+            L.fastvim_ssm_export_bytes.argtypes = [PD, ci, ci]
+            L.fastvim_ssm_export_bytes.restype = sz
+            L.fastvim_status_string.argtypes = [ci]
+            L.fastvim_status_string.restype = ctypes.c_char_p
+            L.fastvim_abi_version.argtypes = []
+            L.fastvim_abi_version.restype = ci
+            _lib = L
+    return _lib
+
+
+def make_dims(B, h, w, E, N=16, R=12, K=0, io_dtype=F32) -> Dims:
+    return Dims(B, h, w, E, N, R, K, io_dtype, 0)
+
+
+def workspace_bytes(dims: Dims, pool_axis: int) -> int:
+    return int(lib().fastvim_ssm_workspace_bytes(ctypes.byref(dims), pool_axis))
+
+
+def _io_dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError("x, z must be float32 or bfloat16, got %s" % t.dtype)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+class SSMCall:
+    """One prepared layer call: sizes, parameter pointers, workspace and out.
+
+    Dense: x, z (B, h, w, E).  Masked: x, z (B, K, E), mask_idx (B, K) int32
+    and hw = (h, w).  params = {"fwd": {...}, "bwd": {...}} holding fp32
+    device tensors x_proj_w (R+2N, E), dt_proj_w (E, R), dt_proj_b (E),
+    A_log (E, N), D (E)."""
+
+    def __init__(self, x: torch.Tensor, z: torch.Tensor, params: Dict[str, Dict[str, torch.Tensor]],
+                 pool_axis: int, mask_idx: Optional[torch.Tensor] = None, hw: Optional[Tuple[int, int]] = None,
+                 out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+        io = _io_dtype(x)
+        if z.dtype != x.dtype or z.shape != x.shape:
+            raise ValueError("z must match x in shape and dtype")
+        E = x.shape[-1]
+        pf = params["fwd"]
+        NX = pf["x_proj_w"].shape[0]
+        N = pf["A_log"].shape[1]
+        R = NX - 2 * N
+        if mask_idx is None:
+            if x.dim() != 4:
+                raise ValueError("dense x must be (B, h, w, E)")
+            B, h, w, _ = x.shape
+            K = 0
+        else:
+            if x.dim() != 3 or hw is None:
+                raise ValueError("masked x must be (B, K, E) with hw=(h, w)")
+            B, K, _ = x.shape
+            h, w = hw
+            if mask_idx.dtype != torch.int32 or tuple(mask_idx.shape) != (B, K):
+                raise ValueError("mask_idx must be int32 (B, K)")
+        self.dims = make_dims(B, h, w, E, N, R, K, io)
+        self.pool_axis = pool_axis
+        self.x, self.z, self.mask_idx = x, z, mask_idx
+        self.out = torch.empty_like(x) if out is None else out
+        self._keep = []
+        dirs = []
+        for name in ("fwd", "bwd"):
+            p = params[name]
+            ts = []
+            for f in DIR_FIELDS:
+                t = p[f]
+                if t.dtype != torch.float32 or not t.is_contiguous():
+                    raise ValueError("parameter %s.%s must be contiguous float32" % (name, f))
+                ts.append(t)
+            self._keep.extend(ts)
+            dirs.append(DirParams(*[t.data_ptr() for t in ts]))
+        nbytes = workspace_bytes(self.dims, pool_axis)
+        if workspace is None:
+            workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=x.device)
+        self.workspace = workspace
+        self.params = Params(dirs[0], dirs[1], workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                             0, 0)
+
+    def _args(self):
+        return (_ptr(self.x), _ptr(self.z), ctypes.byref(self.params), ctypes.byref(self.dims), self.pool_axis,
+                _ptr(self.mask_idx), _ptr(self.out))
+
+    def run(self, stream=None) -> torch.Tensor:
+        st = lib().fastvim_ssm_fwd(*self._args(), _stream(stream))
+        if st:
+            raise FastVimError(st, "fastvim_ssm_fwd")
+        return self.out
+
+    def stage(self, stage: int, stream=None) -> None:
+        st = lib().fastvim_ssm_stage(stage, *self._args(), _stream(stream))
+        if st:
+            raise FastVimError(st, "fastvim_ssm_stage(%d)" % stage)
+
+    def export(self, what: int, stream=None) -> torch.Tensor:
+        """Copy of an intermediate of the last run (U, XDBL, S_FWD, S_BWD: fp32; ROWS, BAD_TOKENS: int32)."""
+        n = int(lib().fastvim_ssm_export_bytes(ctypes.byref(self.dims), self.pool_axis, what))
+        d = self.dims
+        T = {POOL_COLS: d.h, POOL_ROWS: d.w}.get(self.pool_axis, d.h * d.w)
+        shapes = {
+            EXPORT_U: (d.B, T, d.E), EXPORT_XDBL: (d.B, T, 2, d.R + 2 * d.N), EXPORT_S_FWD: (d.B, T, d.E),
+            EXPORT_S_BWD: (d.B, T, d.E), EXPORT_ROWS: (d.B, d.K), EXPORT_BAD_TOKENS: (d.B,),
+        }
+        dtype = torch.int32 if what in (EXPORT_ROWS, EXPORT_BAD_TOKENS) else torch.float32
+        dst = torch.empty(shapes[what], dtype=dtype, device=self.x.device)
+        st = lib().fastvim_ssm_export(ctypes.byref(self.params), ctypes.byref(self.dims), self.pool_axis, what,
+                                      _ptr(dst), max(n, dst.numel() * dst.element_size()), _stream(stream))
+        if st:
+            raise FastVimError(st, "fastvim_ssm_export(%d)" % what)
+        return dst
+
+
+def ssm_fwd(x, z, params, pool_axis=POOL_COLS, mask_idx=None, hw=None, out=None, workspace=None, stream=None):
+    """The pooled bidirectional selective-scan layer; returns out."""
+    return SSMCall(x, z, params, pool_axis, mask_idx=mask_idx, hw=hw, out=out, workspace=workspace).run(stream)

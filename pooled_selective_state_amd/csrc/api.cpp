@@ -1,0 +1,245 @@
+// Host side of the C ABI: argument validation, workspace layout, stage
+// dispatch and intermediate-result export.  Every check runs on the host
+// before anything is enqueued, so an argument error launches nothing.
+#include <cstdint>
+#include <cstring>
+
+#include "fastvim_internal.h"
+
+namespace fastvim {
+namespace {
+
+constexpr int64_t kMaxE = 4096;
+constexpr int64_t kMaxR = 64;
+constexpr int64_t kMaskedMaxCells = 16384;  // per-image occurrence counters live in 64 KB of LDS
+constexpr int64_t kMaxElems = int64_t(1) << 60;
+
+size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+bool mul_ok(int64_t a, int64_t b, int64_t* r) {
+    if (a != 0 && b > kMaxElems / a) return false;
+    *r = a * b;
+    return true;
+}
+
+// Sizes only (no pointers): fills g.  Returns FASTVIM_OK or a status.
+int resolve_geom(const fastvim_dims* d, int axis, Geom* g) {
+    if (!d) return FASTVIM_ERR_NULL;
+    if (axis < FASTVIM_POOL_COLS || axis > FASTVIM_POOL_NONE_COLMAJOR) return FASTVIM_ERR_ARG;
+    if (d->io_dtype != FASTVIM_F32 && d->io_dtype != FASTVIM_BF16) return FASTVIM_ERR_ARG;
+    if (d->B < 0 || d->h <= 0 || d->w <= 0 || d->E <= 0 || d->N <= 0 || d->R <= 0 || d->K < 0)
+        return FASTVIM_ERR_DIMS;
+    const bool masked = d->K > 0;
+    const bool pooled = axis == FASTVIM_POOL_COLS || axis == FASTVIM_POOL_ROWS;
+    int64_t hw, tmp;
+    if (!mul_ok(d->h, d->w, &hw)) return FASTVIM_ERR_DIMS;
+    if (masked && (!pooled || d->K > hw)) return FASTVIM_ERR_DIMS;
+    if (d->N != 16 || d->R > kMaxR || d->E > kMaxE) return FASTVIM_ERR_UNSUPPORTED;
+    if (d->E % (d->io_dtype == FASTVIM_F32 ? 4 : 8) != 0) return FASTVIM_ERR_UNSUPPORTED;
+    if (masked && hw > kMaskedMaxCells) return FASTVIM_ERR_UNSUPPORTED;
+    if (!pooled && hw > INT32_MAX) return FASTVIM_ERR_UNSUPPORTED;
+    const int64_t tokens = masked ? d->K : hw;
+    if (!mul_ok(d->B, tokens, &tmp) || !mul_ok(tmp, d->E, &tmp)) return FASTVIM_ERR_DIMS;
+    g->B = d->B; g->h = d->h; g->w = d->w; g->E = d->E; g->N = d->N; g->R = d->R; g->K = d->K;
+    g->axis = axis;
+    g->masked = masked;
+    g->pooled = pooled;
+    g->io = d->io_dtype;
+    g->NX = d->R + 2 * d->N;
+    if (axis == FASTVIM_POOL_COLS) { g->T = d->h; g->P = d->w; }
+    else if (axis == FASTVIM_POOL_ROWS) { g->T = d->w; g->P = d->h; }
+    else { g->T = hw; g->P = 1; }
+    return FASTVIM_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+    const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
+    return na && nb && pa < pb + nb && pb < pa + na;
+}
+
+// x_proj_w is read with 16-byte vector loads, the others with scalar loads.
+int check_dir(const fastvim_dir_params& d) {
+    const float* ps[5] = {d.x_proj_w, d.dt_proj_w, d.dt_proj_b, d.A_log, d.D};
+    for (const float* p : ps)
+        if (!p) return FASTVIM_ERR_NULL;
+    for (const float* p : ps)
+        if (!aligned(p, p == d.x_proj_w ? 16 : 4)) return FASTVIM_ERR_ALIGN;
+    return FASTVIM_OK;
+}
+
+// Full validation of a layer call.  *empty is set for B == 0.
+int validate(const void* x, const void* z, const fastvim_params* prm, const fastvim_dims* d, int axis,
+             const int32_t* idx, const void* out, Geom* g, Workspace* ws, bool* empty) {
+    if (!prm) return FASTVIM_ERR_NULL;
+    int st = resolve_geom(d, axis, g);
+    if (st) return st;
+    if (!g->masked && idx) return FASTVIM_ERR_ARG;
+    *empty = g->B == 0;
+    if (*empty) return FASTVIM_OK;
+    if (!x || !z || !out || (g->masked && !idx)) return FASTVIM_ERR_NULL;
+    if ((st = check_dir(prm->fwd)) || (st = check_dir(prm->bwd))) return st;
+    if (!prm->workspace) return FASTVIM_ERR_WORKSPACE;
+    if (!aligned(x, 16) || !aligned(z, 16) || !aligned(out, 16) || !aligned(prm->workspace, 256) ||
+        (idx && !aligned(idx, 4)))
+        return FASTVIM_ERR_ALIGN;
+    const size_t need = workspace_layout(*g, nullptr, nullptr);
+    if (prm->workspace_bytes < need) return FASTVIM_ERR_WORKSPACE;
+    const size_t io_bytes =
+        (size_t)(g->B * (g->masked ? g->K : g->h * g->w) * g->E) * (g->io == FASTVIM_F32 ? 4 : 2);
+    if (overlap(out, io_bytes, x, io_bytes) || overlap(out, io_bytes, z, io_bytes)) return FASTVIM_ERR_OVERLAP;
+    const void* w = prm->workspace;
+    if (overlap(w, need, x, io_bytes) || overlap(w, need, z, io_bytes) || overlap(w, need, out, io_bytes))
+        return FASTVIM_ERR_OVERLAP;
+    workspace_layout(*g, prm->workspace, ws);
+    return FASTVIM_OK;
+}
+
+int run_stage(int stage, const Geom& g, const void* x, const void* z, const fastvim_params& p,
+              const int32_t* idx, void* out, const Workspace& ws, hipStream_t st) {
+    hipError_t e = hipSuccess;
+    switch (stage) {
+        case FASTVIM_STAGE_ROWS:
+            if (g.masked) e = launch_mask_rows(g, idx, ws, st);
+            break;
+        case FASTVIM_STAGE_POOL:
+            if (g.pooled) e = launch_pool(g, x, ws, st);
+            break;
+        case FASTVIM_STAGE_PROJ: e = launch_proj(g, x, p, ws, st); break;
+        case FASTVIM_STAGE_SCAN: e = launch_scan(g, x, p, ws, st); break;
+        case FASTVIM_STAGE_EPILOGUE: e = launch_epilogue(g, x, z, p, ws, out, st); break;
+        default: return FASTVIM_ERR_ARG;
+    }
+    return e == hipSuccess ? FASTVIM_OK : FASTVIM_ERR_HIP;
+}
+
+size_t export_bytes(const Geom& g, int what) {
+    switch (what) {
+        case FASTVIM_EXPORT_U: return g.pooled ? (size_t)(g.B * g.T * g.E) * 4 : 0;
+        case FASTVIM_EXPORT_XDBL: return (size_t)(g.B * g.T * 2 * g.NX) * 4;
+        case FASTVIM_EXPORT_S_FWD:
+        case FASTVIM_EXPORT_S_BWD: return (size_t)(g.B * g.T * g.E) * 4;
+        case FASTVIM_EXPORT_ROWS: return g.masked ? (size_t)(g.B * g.K) * 4 : 0;
+        case FASTVIM_EXPORT_BAD_TOKENS: return g.masked ? (size_t)g.B * 4 : 0;
+        default: return 0;
+    }
+}
+
+}  // namespace
+
+size_t workspace_layout(const Geom& g, void* base, Workspace* ws) {
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off = align256(off + bytes);
+        return o;
+    };
+    const size_t bte = (size_t)(g.B * g.T * g.E) * sizeof(float);
+    const size_t o_u = g.pooled ? take(bte) : 0;
+    const size_t o_x = take((size_t)(g.B * g.T * 2 * g.NX) * sizeof(float));
+    const size_t o_sf = take(bte);
+    const size_t o_sb = take(bte);
+    const size_t o_rows = g.masked ? take((size_t)(g.B * g.K) * sizeof(int32_t)) : 0;
+    const size_t o_bad = g.masked ? take((size_t)g.B * sizeof(int32_t)) : 0;
+    if (base && ws) {
+        char* c = static_cast<char*>(base);
+        ws->u = g.pooled ? reinterpret_cast<float*>(c + o_u) : nullptr;
+        ws->xdbl = reinterpret_cast<float*>(c + o_x);
+        ws->s_f = reinterpret_cast<float*>(c + o_sf);
+        ws->s_b = reinterpret_cast<float*>(c + o_sb);
+        ws->rows = g.masked ? reinterpret_cast<int32_t*>(c + o_rows) : nullptr;
+        ws->bad = g.masked ? reinterpret_cast<int32_t*>(c + o_bad) : nullptr;
+    }
+    return off;
+}
+
+}  // namespace fastvim
+
+using namespace fastvim;
+
+extern "C" {
+
+size_t fastvim_ssm_workspace_bytes(const fastvim_dims* dims, int pool_axis) {
+    Geom g;
+    if (resolve_geom(dims, pool_axis, &g) != FASTVIM_OK) return 0;
+    return workspace_layout(g, nullptr, nullptr);
+}
+
+int fastvim_ssm_fwd(const void* x, const void* z, const fastvim_params* params, const fastvim_dims* dims,
+                    int pool_axis, const int32_t* mask_idx, void* out, void* stream) {
+    Geom g;
+    Workspace ws;
+    bool empty = false;
+    int st = validate(x, z, params, dims, pool_axis, mask_idx, out, &g, &ws, &empty);
+    if (st || empty) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    for (int stage = FASTVIM_STAGE_ROWS; stage <= FASTVIM_STAGE_EPILOGUE; ++stage) {
+        st = run_stage(stage, g, x, z, *params, mask_idx, out, ws, s);
+        if (st) return st;
+    }
+    return FASTVIM_OK;
+}
+
+int fastvim_ssm_stage(int stage, const void* x, const void* z, const fastvim_params* params,
+                      const fastvim_dims* dims, int pool_axis, const int32_t* mask_idx, void* out, void* stream) {
+    if (stage < FASTVIM_STAGE_ROWS || stage > FASTVIM_STAGE_EPILOGUE) return FASTVIM_ERR_ARG;
+    Geom g;
+    Workspace ws;
+    bool empty = false;
+    int st = validate(x, z, params, dims, pool_axis, mask_idx, out, &g, &ws, &empty);
+    if (st || empty) return st;
+    return run_stage(stage, g, x, z, *params, mask_idx, out, ws, static_cast<hipStream_t>(stream));
+}
+
+size_t fastvim_ssm_export_bytes(const fastvim_dims* dims, int pool_axis, int what) {
+    Geom g;
+    if (resolve_geom(dims, pool_axis, &g) != FASTVIM_OK) return 0;
+    return export_bytes(g, what);
+}
+
+int fastvim_ssm_export(const fastvim_params* params, const fastvim_dims* dims, int pool_axis, int what, void* dst,
+                       size_t dst_bytes, void* stream) {
+    if (!params || !dims) return FASTVIM_ERR_NULL;
+    Geom g;
+    int st = resolve_geom(dims, pool_axis, &g);
+    if (st) return st;
+    const size_t n = export_bytes(g, what);
+    if (n == 0) return g.B == 0 && what >= FASTVIM_EXPORT_U && what <= FASTVIM_EXPORT_BAD_TOKENS ? FASTVIM_OK
+                                                                                                 : FASTVIM_ERR_ARG;
+    if (!dst || !params->workspace) return FASTVIM_ERR_NULL;
+    if (dst_bytes < n) return FASTVIM_ERR_DIMS;
+    if (params->workspace_bytes < workspace_layout(g, nullptr, nullptr)) return FASTVIM_ERR_WORKSPACE;
+    Workspace ws;
+    workspace_layout(g, params->workspace, &ws);
+    const void* src = nullptr;
+    switch (what) {
+        case FASTVIM_EXPORT_U: src = ws.u; break;
+        case FASTVIM_EXPORT_XDBL: src = ws.xdbl; break;
+        case FASTVIM_EXPORT_S_FWD: src = ws.s_f; break;
+        case FASTVIM_EXPORT_S_BWD: src = ws.s_b; break;
+        case FASTVIM_EXPORT_ROWS: src = ws.rows; break;
+        default: src = ws.bad; break;
+    }
+    hipError_t e = hipMemcpyAsync(dst, src, n, hipMemcpyDeviceToDevice, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? FASTVIM_OK : FASTVIM_ERR_HIP;
+}
+
+const char* fastvim_status_string(int status) {
+    switch (status) {
+        case FASTVIM_OK: return "ok";
+        case FASTVIM_ERR_NULL: return "a required pointer is NULL";
+        case FASTVIM_ERR_DIMS: return "a size is out of range or inconsistent";
+        case FASTVIM_ERR_UNSUPPORTED: return "shape not supported by this build (N != 16, R > 64, E > 4096 or E not a multiple of the vector width, masked grid > 16384 cells)";
+        case FASTVIM_ERR_ALIGN: return "misaligned pointer (x, z, out, x_proj_w need 16 bytes, workspace 256, others 4)";
+        case FASTVIM_ERR_OVERLAP: return "out overlaps x or z, or the workspace overlaps an input or output";
+        case FASTVIM_ERR_WORKSPACE: return "workspace missing or smaller than fastvim_ssm_workspace_bytes";
+        case FASTVIM_ERR_HIP: return "HIP reported an error while enqueuing work";
+        case FASTVIM_ERR_ARG: return "bad enum, stage or export id, or mask_idx given for a dense layer";
+        default: return "unknown status";
+    }
+}
+
+int fastvim_abi_version(void) { return FASTVIM_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,116 @@
+// Internal declarations shared by the HIP kernels and the host API of the
+// gfx950 pooled selective-scan layer.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+#include "fastvim.h"
+
+namespace fastvim {
+
+// ------------------------------------------------------------------ geometry
+// Resolved sizes of one call.  T is the scan length, P the pooled-axis length
+// (1 when unpooled), NX = R + 2N the width of one direction's x_proj output.
+struct Geom {
+    int64_t B, h, w, E, N, R, K, T, P, NX;
+    int axis;     // fastvim_pool_axis
+    bool masked;  // K > 0
+    bool pooled;  // axis is COLS or ROWS
+    int io;       // fastvim_dtype
+};
+
+// Workspace carve-up (every region 256-byte aligned).
+struct Workspace {
+    float* u;         // (B, T, E) pooled tokens; unused when unpooled
+    float* xdbl;      // (B, T, 2, NX) x_proj outputs of both directions
+    float* s_f;       // (B, T, E) forward scan output
+    float* s_b;       // (B, T, E) backward scan output
+    int32_t* rows;    // (B, K) masked: scan row of each kept token, -1 if invalid
+    int32_t* bad;     // (B) masked: invalid mask entries per image
+};
+
+// Bytes needed; when base != nullptr also fills *ws.
+size_t workspace_layout(const Geom& g, void* base, Workspace* ws);
+
+// Stage launchers (enqueue only; return the launch's hipError_t).
+hipError_t launch_mask_rows(const Geom& g, const int32_t* idx, const Workspace& ws, hipStream_t st);
+hipError_t launch_pool(const Geom& g, const void* x, const Workspace& ws, hipStream_t st);
+hipError_t launch_proj(const Geom& g, const void* x, const fastvim_params& p, const Workspace& ws,
+                       hipStream_t st);
+hipError_t launch_scan(const Geom& g, const void* x, const fastvim_params& p, const Workspace& ws,
+                       hipStream_t st);
+hipError_t launch_epilogue(const Geom& g, const void* x, const void* z, const fastvim_params& p,
+                           const Workspace& ws, void* out, hipStream_t st);
+
+// ------------------------------------------------------------ device helpers
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// I/O element traits: one 16-byte vector holds V elements.
+struct IoF32 {
+    using elem = float;
+    static constexpr int V = 4;
+};
+struct IoBf16 {
+    using elem = uint16_t;
+    static constexpr int V = 8;
+};
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+// fp32 -> bf16 bits, round to nearest even; NaN stays NaN (quiet).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) | 0x40u) & 0xffffu;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+// 16-byte vector load / store of V I/O elements widened to fp32.
+template <bool NT>
+__device__ __forceinline__ void load_vec(const float* p, float (&v)[4]) {
+    f32x4 t = NT ? __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p))
+                 : *reinterpret_cast<const f32x4*>(p);
+    v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
+}
+template <bool NT>
+__device__ __forceinline__ void load_vec(const uint16_t* p, float (&v)[8]) {
+    u32x4 t = NT ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p))
+                 : *reinterpret_cast<const u32x4*>(p);
+    v[0] = __uint_as_float(t.x << 16); v[1] = __uint_as_float(t.x & 0xffff0000u);
+    v[2] = __uint_as_float(t.y << 16); v[3] = __uint_as_float(t.y & 0xffff0000u);
+    v[4] = __uint_as_float(t.z << 16); v[5] = __uint_as_float(t.z & 0xffff0000u);
+    v[6] = __uint_as_float(t.w << 16); v[7] = __uint_as_float(t.w & 0xffff0000u);
+}
+template <bool NT>
+__device__ __forceinline__ void store_vec(float* p, const float (&v)[4]) {
+    f32x4 t = {v[0], v[1], v[2], v[3]};
+    if (NT) __builtin_nontemporal_store(t, reinterpret_cast<f32x4*>(p));
+    else *reinterpret_cast<f32x4*>(p) = t;
+}
+template <bool NT>
+__device__ __forceinline__ void store_vec(uint16_t* p, const float (&v)[8]) {
+    u32x4 t;
+    t.x = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
+    t.y = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
+    t.z = f32_to_bf16_bits(v[4]) | (f32_to_bf16_bits(v[5]) << 16);
+    t.w = f32_to_bf16_bits(v[6]) | (f32_to_bf16_bits(v[7]) << 16);
+    if (NT) __builtin_nontemporal_store(t, reinterpret_cast<u32x4*>(p));
+    else *reinterpret_cast<u32x4*>(p) = t;
+}
+
+// Scalar element load widened to fp32.
+__device__ __forceinline__ float load_elem(const float* p) { return *p; }
+__device__ __forceinline__ float load_elem(const uint16_t* p) { return bf16_bits_to_f32(*p); }
+
+// Offset (in tokens) of scan position t of image b's grid in unpooled order.
+__device__ __forceinline__ int64_t unpooled_token(int axis, int64_t t, int64_t h, int64_t w) {
+    if (axis == FASTVIM_POOL_NONE_ROWMAJOR) return t;
+    const int64_t j = t / h, i = t - j * h;  // t = j*h + i
+    return i * w + j;
+}
+
+}  // namespace fastvim
