@@ -112,13 +112,20 @@ typedef struct fastvim_params {
     fastvim_dir_params bwd; /* backward scan (t descending) */
     void *workspace;        /* device scratch, >= fastvim_ssm_workspace_bytes, 256-byte aligned */
     size_t workspace_bytes;
-    uint32_t flags;         /* reserved, set to 0 */
+    uint32_t flags;         /* FASTVIM_FLAG_* bits, else 0 */
     uint32_t reserved;
 } fastvim_params;
 
+/* params.flags bits.  By default a layer runs as its stage kernels (the ones
+ * fastvim_ssm_stage runs).  FASTVIM_FLAG_FUSED runs a dense pooled layer as
+ * one pipelined launch (plus a one-block launch that resets its counters)
+ * instead; other layers ignore it.  Both give the same results within
+ * rounding. */
+#define FASTVIM_FLAG_FUSED 1u
+
 /* Bytes of workspace a call with these sizes needs (0 if the sizes are
  * invalid).  Dense pooled layers need 4 * B * T * (3E + 2(R + 2N)) bytes plus
- * alignment; unpooled layers hold the per-token projections and scan outputs
+ * 4 * (2 + 2B) bytes of counters and alignment; unpooled layers hold the per-token projections and scan outputs
  * (at B = 128, h = w = 128, E = 384 about 7.2 GB). */
 size_t fastvim_ssm_workspace_bytes(const fastvim_dims *dims, int pool_axis);
 
@@ -156,6 +163,8 @@ int fastvim_ssm_stage(int stage, const void *x, const void *z, const fastvim_par
  *   S_FWD/S_BWD (B, T, E)        fp32 scan outputs of each direction
  *   ROWS        (B, K)           int32 row (COLS) or column (ROWS) of each kept token, -1 if invalid
  *   BAD_TOKENS  (B)              int32 number of invalid mask entries per image
+ *   STATUS      (1)              uint32, 0 normally; bit 0 set if a wait inside the single-launch
+ *                                kernel gave up after its bounded polling (results then invalid)
  * Returns FASTVIM_ERR_ARG for an export the layer does not have. */
 typedef enum fastvim_export {
     FASTVIM_EXPORT_U = 0,
@@ -163,7 +172,8 @@ typedef enum fastvim_export {
     FASTVIM_EXPORT_S_FWD = 2,
     FASTVIM_EXPORT_S_BWD = 3,
     FASTVIM_EXPORT_ROWS = 4,
-    FASTVIM_EXPORT_BAD_TOKENS = 5
+    FASTVIM_EXPORT_BAD_TOKENS = 5,
+    FASTVIM_EXPORT_STATUS = 6
 } fastvim_export;
 
 int fastvim_ssm_export(const fastvim_params *params, const fastvim_dims *dims, int pool_axis, int what,

@@ -23,7 +23,9 @@ F32, BF16 = 0, 1
 # fastvim_stage
 STAGE_ROWS, STAGE_POOL, STAGE_PROJ, STAGE_SCAN, STAGE_EPILOGUE = 0, 1, 2, 3, 4
 # fastvim_export
-EXPORT_U, EXPORT_XDBL, EXPORT_S_FWD, EXPORT_S_BWD, EXPORT_ROWS, EXPORT_BAD_TOKENS = 0, 1, 2, 3, 4, 5
+EXPORT_U, EXPORT_XDBL, EXPORT_S_FWD, EXPORT_S_BWD, EXPORT_ROWS, EXPORT_BAD_TOKENS, EXPORT_STATUS = 0, 1, 2, 3, 4, 5, 6
+# params.flags
+FLAG_FUSED = 1
 
 STATUS = {
     0: "FASTVIM_OK", -1: "FASTVIM_ERR_NULL", -2: "FASTVIM_ERR_DIMS", -3: "FASTVIM_ERR_UNSUPPORTED",
@@ -129,7 +131,8 @@ class SSMCall:
 
     def __init__(self, x: torch.Tensor, z: torch.Tensor, params: Dict[str, Dict[str, torch.Tensor]],
                  pool_axis: int, mask_idx: Optional[torch.Tensor] = None, hw: Optional[Tuple[int, int]] = None,
-                 out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+                 out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                 flags: int = 0):
         io = _io_dtype(x)
         if z.dtype != x.dtype or z.shape != x.shape:
             raise ValueError("z must match x in shape and dtype")
@@ -171,7 +174,7 @@ class SSMCall:
             workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=x.device)
         self.workspace = workspace
         self.params = Params(dirs[0], dirs[1], workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-                             0, 0)
+                             flags, 0)
 
     def _args(self):
         return (_ptr(self.x), _ptr(self.z), ctypes.byref(self.params), ctypes.byref(self.dims), self.pool_axis,
@@ -195,9 +198,9 @@ class SSMCall:
         T = {POOL_COLS: d.h, POOL_ROWS: d.w}.get(self.pool_axis, d.h * d.w)
         shapes = {
             EXPORT_U: (d.B, T, d.E), EXPORT_XDBL: (d.B, T, 2, d.R + 2 * d.N), EXPORT_S_FWD: (d.B, T, d.E),
-            EXPORT_S_BWD: (d.B, T, d.E), EXPORT_ROWS: (d.B, d.K), EXPORT_BAD_TOKENS: (d.B,),
+            EXPORT_S_BWD: (d.B, T, d.E), EXPORT_ROWS: (d.B, d.K), EXPORT_BAD_TOKENS: (d.B,), EXPORT_STATUS: (1,),
         }
-        dtype = torch.int32 if what in (EXPORT_ROWS, EXPORT_BAD_TOKENS) else torch.float32
+        dtype = torch.int32 if what in (EXPORT_ROWS, EXPORT_BAD_TOKENS, EXPORT_STATUS) else torch.float32
         dst = torch.empty(shapes[what], dtype=dtype, device=self.x.device)
         st = lib().fastvim_ssm_export(ctypes.byref(self.params), ctypes.byref(self.dims), self.pool_axis, what,
                                       _ptr(dst), max(n, dst.numel() * dst.element_size()), _stream(stream))
@@ -206,6 +209,8 @@ class SSMCall:
         return dst
 
 
-def ssm_fwd(x, z, params, pool_axis=POOL_COLS, mask_idx=None, hw=None, out=None, workspace=None, stream=None):
+def ssm_fwd(x, z, params, pool_axis=POOL_COLS, mask_idx=None, hw=None, out=None, workspace=None, stream=None,
+            flags=0):
     """The pooled bidirectional selective-scan layer; returns out."""
-    return SSMCall(x, z, params, pool_axis, mask_idx=mask_idx, hw=hw, out=out, workspace=workspace).run(stream)
+    return SSMCall(x, z, params, pool_axis, mask_idx=mask_idx, hw=hw, out=out, workspace=workspace,
+                   flags=flags).run(stream)

@@ -122,6 +122,7 @@ size_t export_bytes(const Geom& g, int what) {
         case FASTVIM_EXPORT_S_BWD: return (size_t)(g.B * g.T * g.E) * 4;
         case FASTVIM_EXPORT_ROWS: return g.masked ? (size_t)(g.B * g.K) * 4 : 0;
         case FASTVIM_EXPORT_BAD_TOKENS: return g.masked ? (size_t)g.B * 4 : 0;
+        case FASTVIM_EXPORT_STATUS: return 4;
         default: return 0;
     }
 }
@@ -142,6 +143,7 @@ size_t workspace_layout(const Geom& g, void* base, Workspace* ws) {
     const size_t o_sb = take(bte);
     const size_t o_rows = g.masked ? take((size_t)(g.B * g.K) * sizeof(int32_t)) : 0;
     const size_t o_bad = g.masked ? take((size_t)g.B * sizeof(int32_t)) : 0;
+    const size_t o_sync = take((size_t)sync_words(g) * sizeof(unsigned));
     if (base && ws) {
         char* c = static_cast<char*>(base);
         ws->u = g.pooled ? reinterpret_cast<float*>(c + o_u) : nullptr;
@@ -150,6 +152,7 @@ size_t workspace_layout(const Geom& g, void* base, Workspace* ws) {
         ws->s_b = reinterpret_cast<float*>(c + o_sb);
         ws->rows = g.masked ? reinterpret_cast<int32_t*>(c + o_rows) : nullptr;
         ws->bad = g.masked ? reinterpret_cast<int32_t*>(c + o_bad) : nullptr;
+        ws->sync = reinterpret_cast<unsigned*>(c + o_sync);
     }
     return off;
 }
@@ -174,6 +177,9 @@ int fastvim_ssm_fwd(const void* x, const void* z, const fastvim_params* params, 
     int st = validate(x, z, params, dims, pool_axis, mask_idx, out, &g, &ws, &empty);
     if (st || empty) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (launch_zero_sync(ws, sync_words(g), s) != hipSuccess) return FASTVIM_ERR_HIP;
+    if ((params->flags & FASTVIM_FLAG_FUSED) && fused_supported(g))
+        return launch_fused(g, x, z, *params, ws, out, s) == hipSuccess ? FASTVIM_OK : FASTVIM_ERR_HIP;
     for (int stage = FASTVIM_STAGE_ROWS; stage <= FASTVIM_STAGE_EPILOGUE; ++stage) {
         st = run_stage(stage, g, x, z, *params, mask_idx, out, ws, s);
         if (st) return st;
@@ -205,8 +211,8 @@ int fastvim_ssm_export(const fastvim_params* params, const fastvim_dims* dims, i
     int st = resolve_geom(dims, pool_axis, &g);
     if (st) return st;
     const size_t n = export_bytes(g, what);
-    if (n == 0) return g.B == 0 && what >= FASTVIM_EXPORT_U && what <= FASTVIM_EXPORT_BAD_TOKENS ? FASTVIM_OK
-                                                                                                 : FASTVIM_ERR_ARG;
+    if (n == 0) return g.B == 0 && what >= FASTVIM_EXPORT_U && what <= FASTVIM_EXPORT_STATUS ? FASTVIM_OK
+                                                                                             : FASTVIM_ERR_ARG;
     if (!dst || !params->workspace) return FASTVIM_ERR_NULL;
     if (dst_bytes < n) return FASTVIM_ERR_DIMS;
     if (params->workspace_bytes < workspace_layout(g, nullptr, nullptr)) return FASTVIM_ERR_WORKSPACE;
@@ -219,7 +225,8 @@ int fastvim_ssm_export(const fastvim_params* params, const fastvim_dims* dims, i
         case FASTVIM_EXPORT_S_FWD: src = ws.s_f; break;
         case FASTVIM_EXPORT_S_BWD: src = ws.s_b; break;
         case FASTVIM_EXPORT_ROWS: src = ws.rows; break;
-        default: src = ws.bad; break;
+        case FASTVIM_EXPORT_BAD_TOKENS: src = ws.bad; break;
+        default: src = ws.sync + 1; break;
     }
     hipError_t e = hipMemcpyAsync(dst, src, n, hipMemcpyDeviceToDevice, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? FASTVIM_OK : FASTVIM_ERR_HIP;

@@ -30,7 +30,11 @@ struct Workspace {
     float* s_b;       // (B, T, E) backward scan output
     int32_t* rows;    // (B, K) masked: scan row of each kept token, -1 if invalid
     int32_t* bad;     // (B) masked: invalid mask entries per image
+    unsigned* sync;   // (2 + 2B) ticket, status word, per-image progress counters
 };
+
+// Words of the sync region: ticket, status, and two counters per image.
+inline int64_t sync_words(const Geom& g) { return 2 + 2 * g.B; }
 
 // Bytes needed; when base != nullptr also fills *ws.
 size_t workspace_layout(const Geom& g, void* base, Workspace* ws);
@@ -44,18 +48,25 @@ hipError_t launch_scan(const Geom& g, const void* x, const fastvim_params& p, co
                        hipStream_t st);
 hipError_t launch_epilogue(const Geom& g, const void* x, const void* z, const fastvim_params& p,
                            const Workspace& ws, void* out, hipStream_t st);
+// Single-launch dense pooled layer (fused.hip).
+bool fused_supported(const Geom& g);
+hipError_t launch_fused(const Geom& g, const void* x, const void* z, const fastvim_params& p, const Workspace& ws,
+                        void* out, hipStream_t st);
+hipError_t launch_zero_sync(const Workspace& ws, int64_t n, hipStream_t st);
 
 // ------------------------------------------------------------ device helpers
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// I/O element traits: one 16-byte vector holds V elements.
+// I/O element traits: one 16-byte vector (raw) holds V elements.
 struct IoF32 {
     using elem = float;
+    using raw = f32x4;
     static constexpr int V = 4;
 };
 struct IoBf16 {
     using elem = uint16_t;
+    using raw = u32x4;
     static constexpr int V = 8;
 };
 
@@ -100,6 +111,22 @@ __device__ __forceinline__ void store_vec(uint16_t* p, const float (&v)[8]) {
     t.w = f32_to_bf16_bits(v[6]) | (f32_to_bf16_bits(v[7]) << 16);
     if (NT) __builtin_nontemporal_store(t, reinterpret_cast<u32x4*>(p));
     else *reinterpret_cast<u32x4*>(p) = t;
+}
+
+// Raw 16-byte loads (kept narrow until used) and their widening.
+template <bool NT>
+__device__ __forceinline__ f32x4 load_raw(const float* p) {
+    return NT ? __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p)) : *reinterpret_cast<const f32x4*>(p);
+}
+template <bool NT>
+__device__ __forceinline__ u32x4 load_raw(const uint16_t* p) {
+    return NT ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)) : *reinterpret_cast<const u32x4*>(p);
+}
+// Element k (0 <= k < V) of a raw vector, as fp32.
+__device__ __forceinline__ float raw_at(const f32x4& r, int k) { return r[k]; }
+__device__ __forceinline__ float raw_at(const u32x4& r, int k) {
+    const uint32_t wd = r[k >> 1];
+    return __uint_as_float((k & 1) ? (wd & 0xffff0000u) : (wd << 16));
 }
 
 // Scalar element load widened to fp32.

@@ -29,25 +29,26 @@ pool_dense_kernel(const typename IO::elem* __restrict__ x, float* __restrict__ u
     const int tid = threadIdx.x;
     const int c = tid % VE, g = tid / VE;
     if (g < G) {
+        using raw = typename IO::raw;
         float acc[V];
 #pragma unroll
         for (int k = 0; k < V; ++k) acc[k] = 0.f;
         const typename IO::elem* base = x + b * img_stride + t * t_stride + (int64_t)c * V;
         int64_t p = g;
-        for (; p + 3 * G < P; p += 4 * G) {
-            float a0[V], a1[V], a2[V], a3[V];
-            load_vec<false>(base + p * p_stride, a0);
-            load_vec<false>(base + (p + G) * p_stride, a1);
-            load_vec<false>(base + (p + 2 * G) * p_stride, a2);
-            load_vec<false>(base + (p + 3 * G) * p_stride, a3);
+        // 8 loads in flight per lane, summed in a fixed pairwise order
+        for (; p + 7 * G < P; p += 8 * G) {
+            raw r[8];
 #pragma unroll
-            for (int k = 0; k < V; ++k) acc[k] += (a0[k] + a1[k]) + (a2[k] + a3[k]);
+            for (int u = 0; u < 8; ++u) r[u] = load_raw<true>(base + (p + u * G) * p_stride);
+#pragma unroll
+            for (int k = 0; k < V; ++k)
+                acc[k] += ((raw_at(r[0], k) + raw_at(r[1], k)) + (raw_at(r[2], k) + raw_at(r[3], k))) +
+                          ((raw_at(r[4], k) + raw_at(r[5], k)) + (raw_at(r[6], k) + raw_at(r[7], k)));
         }
         for (; p < P; p += G) {
-            float a0[V];
-            load_vec<false>(base + p * p_stride, a0);
+            const raw r0 = load_raw<true>(base + p * p_stride);
 #pragma unroll
-            for (int k = 0; k < V; ++k) acc[k] += a0[k];
+            for (int k = 0; k < V; ++k) acc[k] += raw_at(r0, k);
         }
 #pragma unroll
         for (int k = 0; k < V; ++k) red[((int64_t)g * VE + c) * V + k] = acc[k];

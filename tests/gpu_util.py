@@ -46,11 +46,17 @@ def io_dtype(cfg_or_name):
     return torch.bfloat16 if cfg_or_name == "bf16" else torch.float32
 
 
-def gpu_call(x, z, params, axis, idx=None, hw=None, dtype=torch.float32):
+def gpu_call(x, z, params, axis, idx=None, hw=None, dtype=torch.float32, flags=0):
     """Prepared call on device copies of numpy inputs; returns the SSMCall."""
     xd, zd = dev(x, dtype), dev(z, dtype)
     idd = None if idx is None else dev(idx, torch.int32)
-    return P.SSMCall(xd, zd, dev_params(params), axis, mask_idx=idd, hw=hw)
+    return P.SSMCall(xd, zd, dev_params(params), axis, mask_idx=idd, hw=hw, flags=flags)
+
+
+def status_ok(call):
+    """The single-launch kernel's status word is 0 (no wait gave up)."""
+    st = int(call.export(P.EXPORT_STATUS).cpu().item())
+    assert st == 0, "fused-kernel status %#x" % st
 
 
 def stage_exports(call):

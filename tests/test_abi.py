@@ -56,15 +56,18 @@ def _ws(dims, axis):
 def test_workspace_bytes():
     def al(n):
         return (n + 255) // 256 * 256
+    def sync(B):
+        return al(4 * (2 + 2 * B))
     d = P.make_dims(128, 128, 128, 384, 16, 12)
     B, T, E, NX = 128, 128, 384, 44
-    assert _ws(d, P.POOL_COLS) == 3 * al(B * T * E * 4) + al(B * T * 2 * NX * 4)
+    assert _ws(d, P.POOL_COLS) == 3 * al(B * T * E * 4) + al(B * T * 2 * NX * 4) + sync(B)
     d2 = P.make_dims(128, 128, 64, 384, 16, 12)
-    assert _ws(d2, P.POOL_ROWS) == 3 * al(128 * 64 * E * 4) + al(128 * 64 * 2 * NX * 4)
+    assert _ws(d2, P.POOL_ROWS) == 3 * al(128 * 64 * E * 4) + al(128 * 64 * 2 * NX * 4) + sync(B)
     T2 = 128 * 128
-    assert _ws(d, P.POOL_NONE_ROWMAJOR) == 2 * al(B * T2 * E * 4) + al(B * T2 * 2 * NX * 4)
+    assert _ws(d, P.POOL_NONE_ROWMAJOR) == 2 * al(B * T2 * E * 4) + al(B * T2 * 2 * NX * 4) + sync(B)
     dm = P.make_dims(256, 14, 14, 1536, 16, 48, 49, P.BF16)
-    expect = 3 * al(256 * 14 * 1536 * 4) + al(256 * 14 * 2 * 80 * 4) + al(256 * 49 * 4) + al(256 * 4)
+    expect = (3 * al(256 * 14 * 1536 * 4) + al(256 * 14 * 2 * 80 * 4) + al(256 * 49 * 4) + al(256 * 4)
+              + sync(256))
     assert _ws(dm, P.POOL_COLS) == expect
     # invalid sizes report 0
     assert _ws(P.make_dims(1, 2, 2, 8, 15, 4), P.POOL_COLS) == 0
@@ -201,6 +204,7 @@ def test_export_arguments():
     lib = P.lib()
     c = FakeCall()
     assert lib.fastvim_ssm_export(ctypes.byref(c.params), ctypes.byref(c.dims), 0, 9, c.out, 1 << 20, None) == EARG
+    assert lib.fastvim_ssm_export(ctypes.byref(c.params), ctypes.byref(c.dims), 0, -1, c.out, 1 << 20, None) == EARG
     assert lib.fastvim_ssm_export(ctypes.byref(c.params), ctypes.byref(c.dims), 0, P.EXPORT_ROWS, c.out, 1 << 20,
                                   None) == EARG  # dense layer has no rows
     assert lib.fastvim_ssm_export(ctypes.byref(c.params), ctypes.byref(c.dims), 0, P.EXPORT_U, c.out, 16,
@@ -209,11 +213,12 @@ def test_export_arguments():
     assert lib.fastvim_ssm_export_bytes(ctypes.byref(c.dims), P.POOL_NONE_ROWMAJOR, P.EXPORT_U) == 0
 
 
-@pytest.mark.parametrize("what", range(6))
+@pytest.mark.parametrize("what", range(7))
 def test_export_bytes_masked(what):
     lib = P.lib()
     d = P.make_dims(3, 4, 5, 16, 16, 4, 7, P.BF16)
     n = lib.fastvim_ssm_export_bytes(ctypes.byref(d), P.POOL_ROWS, what)
     T = 5
-    expect_n = {0: 3 * T * 16 * 4, 1: 3 * T * 2 * 36 * 4, 2: 3 * T * 16 * 4, 3: 3 * T * 16 * 4, 4: 3 * 7 * 4, 5: 12}
+    expect_n = {0: 3 * T * 16 * 4, 1: 3 * T * 2 * 36 * 4, 2: 3 * T * 16 * 4, 3: 3 * T * 16 * 4, 4: 3 * 7 * 4, 5: 12,
+                6: 4}
     assert n == expect_n[what]

@@ -21,7 +21,7 @@ import torch
 import oracle
 import pooled_selective_state_amd as P
 from gpu_util import (BF16_TOL, FP32_TOL, check, compare_stages, dev, dev_params, gpu_call, host, rel_inf,
-                      stage_exports)
+                      stage_exports, status_ok)
 from pins import rand_dir
 from pooled_selective_state_amd import configs as C
 from pooled_selective_state_amd.inputs import draw_workload, random_mask, round_to_bf16, zero_D
@@ -29,6 +29,8 @@ from pooled_selective_state_amd.inputs import draw_workload, random_mask, round_
 pytestmark = pytest.mark.gpu
 
 AXES = (P.POOL_COLS, P.POOL_ROWS, P.POOL_NONE_ROWMAJOR, P.POOL_NONE_COLMAJOR)
+# dense pooled layers run as stage kernels by default; FLAG_FUSED runs them as one pipelined launch
+PATHS = {"staged": 0, "fused": P.FLAG_FUSED}
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -39,16 +41,19 @@ def _gpu():
     torch.cuda.synchronize()
 
 
-def _layer_check(x, z, prm, axis, tol, dtype, tag, idx=None, hw=None, sel=None):
+def _layer_check(x, z, prm, axis, tol, dtype, tag, idx=None, hw=None, sel=None, flags=0):
     """Run GPU layer + D=0 twin, compare out / twin / stages with the oracle
     on images ``sel`` (all if None)."""
-    call = gpu_call(x, z, prm, axis, idx=idx, hw=hw, dtype=dtype)
+    call = gpu_call(x, z, prm, axis, idx=idx, hw=hw, dtype=dtype, flags=flags)
     out = call.run()
     torch.cuda.synchronize()
+    status_ok(call)
     st = stage_exports(call)
     rows = host(call.export(P.EXPORT_ROWS)).astype(np.int64) if idx is not None else None
-    twin = gpu_call(x, z, zero_D(prm), axis, idx=idx, hw=hw, dtype=dtype).run()
+    tcall = gpu_call(x, z, zero_D(prm), axis, idx=idx, hw=hw, dtype=dtype, flags=flags)
+    twin = tcall.run()
     torch.cuda.synchronize()
+    status_ok(tcall)
     s = slice(None) if sel is None else sel
     ref = oracle.layer(x[s], z[s], prm["fwd"], prm["bwd"], axis, idx=None if idx is None else idx[s], hw=hw,
                        stages=True)
@@ -64,15 +69,17 @@ def _layer_check(x, z, prm, axis, tol, dtype, tag, idx=None, hw=None, sel=None):
 
 
 # ------------------------------------------------------------------ small / ragged
+@pytest.mark.parametrize("path", list(PATHS))
 @pytest.mark.parametrize("axis", AXES)
 @pytest.mark.parametrize("io", ["f32", "bf16"])
-def test_tiny_fastvim_t_layer(axis, io):
+def test_tiny_fastvim_t_layer(axis, io, path):
     wl = draw_workload(C.TINY)
     x, z = wl["x"], wl["z"][0]
     if io == "bf16":
         x, z = round_to_bf16(x), round_to_bf16(z)
     _layer_check(x, z, wl["params"][0], axis, FP32_TOL if io == "f32" else BF16_TOL,
-                 torch.float32 if io == "f32" else torch.bfloat16, "tiny %s axis %d" % (io, axis))
+                 torch.float32 if io == "f32" else torch.bfloat16, "tiny %s axis %d %s" % (io, axis, path),
+                 flags=PATHS[path])
 
 
 RAGGED = [
@@ -85,10 +92,11 @@ RAGGED = [
 ]
 
 
+@pytest.mark.parametrize("path", list(PATHS))
 @pytest.mark.parametrize("shape", RAGGED, ids=["x".join(map(str, s)) for s in RAGGED])
 @pytest.mark.parametrize("axis", AXES)
 @pytest.mark.parametrize("io", ["f32", "bf16"])
-def test_ragged_shapes(shape, axis, io):
+def test_ragged_shapes(shape, axis, io, path):
     B, h, w, E, R = shape
     rng = np.random.default_rng(zlib.crc32(repr((shape, axis, io)).encode()))
     x = rng.standard_normal((B, h, w, E)).astype(np.float32)
@@ -97,7 +105,8 @@ def test_ragged_shapes(shape, axis, io):
         x, z = round_to_bf16(x), round_to_bf16(z)
     prm = {"fwd": rand_dir(rng, E, 16, R, 0.1), "bwd": rand_dir(rng, E, 16, R, 0.1)}
     _layer_check(x, z, prm, axis, FP32_TOL if io == "f32" else BF16_TOL,
-                 torch.float32 if io == "f32" else torch.bfloat16, "ragged %s %s axis %d" % (shape, io, axis))
+                 torch.float32 if io == "f32" else torch.bfloat16, "ragged %s %s axis %d %s" % (shape, io, axis, path),
+                 flags=PATHS[path])
 
 
 @pytest.mark.parametrize("axis", (P.POOL_COLS, P.POOL_ROWS))
@@ -199,13 +208,31 @@ def test_rows_is_cols_on_transposed_grid():
         assert rel_inf(ra, rb) <= 1e-6
 
 
-def test_deterministic():
+@pytest.mark.parametrize("path", list(PATHS))
+def test_deterministic(path):
+    """Bit-identical results on repeated calls (no reduction depends on timing)."""
     wl = draw_workload(C.SHORT_224_S, batch=16)
-    call = gpu_call(wl["x"], wl["z"][0], wl["params"][0], P.POOL_COLS)
+    call = gpu_call(wl["x"], wl["z"][0], wl["params"][0], P.POOL_COLS, flags=PATHS[path])
     a = call.run().clone()
     b = call.run().clone()
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("axis", (P.POOL_COLS, P.POOL_ROWS))
+def test_fused_matches_staged(axis):
+    """The single-launch kernel and the stage kernels agree to rounding on
+    every stage output."""
+    wl = draw_workload(C.CHAIN_1024, batch=6)
+    x, z, prm = wl["x"], wl["z"][0], wl["params"][0]
+    f = gpu_call(x, z, prm, axis, flags=P.FLAG_FUSED)
+    s = gpu_call(x, z, prm, axis)
+    of, os_ = host(f.run()), host(s.run())
+    torch.cuda.synchronize()
+    status_ok(f)
+    assert rel_inf(of, os_) <= 1e-5
+    for what in (P.EXPORT_U, P.EXPORT_XDBL, P.EXPORT_S_FWD, P.EXPORT_S_BWD):
+        assert rel_inf(host(f.export(what)), host(s.export(what))) <= 1e-5, what
 
 
 # --------------------------------------------------------------- full-size workloads
@@ -223,8 +250,9 @@ def _sample(B):
     return np.unique(np.array([0, B // 2, B - 1]))
 
 
+@pytest.mark.parametrize("path", list(PATHS))
 @pytest.mark.parametrize("cfg", [C.SHORT_224_S, C.HIRES_2048, C.MASKED_B], ids=lambda c: c.name)
-def test_full_size_pooled(cfg):
+def test_full_size_pooled(cfg, path):
     wl = _workload(cfg)
     x, z, prm = wl["x"], wl["z"][0], wl["params"][0]
     tol = BF16_TOL if cfg.io_dtype == "bf16" else FP32_TOL
@@ -232,7 +260,8 @@ def test_full_size_pooled(cfg):
     idx = wl["idx"]
     hw = (cfg.h, cfg.w) if cfg.masked else None
     print("\n[%s] B=%d grid=%dx%d E=%d" % (cfg.name, cfg.B, cfg.h, cfg.w, cfg.E), flush=True)
-    _layer_check(x, z, prm, P.POOL_COLS, tol, dtype, cfg.name, idx=idx, hw=hw, sel=_sample(cfg.B))
+    _layer_check(x, z, prm, P.POOL_COLS, tol, dtype, cfg.name + " " + path, idx=idx, hw=hw, sel=_sample(cfg.B),
+                 flags=PATHS[path])
 
 
 def test_full_size_chain_1024():
@@ -246,6 +275,8 @@ def test_full_size_chain_1024():
     c2 = P.SSMCall(out1, dev(z2), dev_params(p2), P.POOL_ROWS)
     out2 = c2.run()
     torch.cuda.synchronize()
+    status_ok(c1)
+    status_ok(c2)
     sel = _sample(cfg.B)
     r1 = oracle.layer(x[sel], z1[sel], p1["fwd"], p1["bwd"], P.POOL_COLS)
     r2 = oracle.layer(r1.astype(np.float32), z2[sel], p2["fwd"], p2["bwd"], P.POOL_ROWS, stages=True)
