@@ -1,34 +1,41 @@
-// The whole dense pooled layer in one launch.
+// The whole dense pooled layer in one pipelined launch.
 //
 // FastVim summary page (gptget.net, arXiv 2502.00594), section 方法详解,
 // bullets 2-5 (pool one axis, input-dependent projections and step size,
 // forward and backward scans, repeat + skip); Pith review, "key_machinery"
 // (repeat before the D x skip); Vim article (ijyty.com) 2.1 (sum of both
-// directions gated by z).  Each stage computes exactly what the staged
-// kernels compute (pool.hip, proj.hip, scan_core.h, epilogue.hip).
+// directions gated by z).  Each stage computes what the staged kernels
+// compute (pool.hip, proj.hip, scan_core.h, epilogue.hip).
 //
 // Why one launch: the output needs x twice (its own skip term) and the scan
 // needs every token of the image, so the layer reads x, then z and x again.
-// Run image by image in a software pipeline, the second read of x comes a
-// couple of images after the first, while the image is still in the 256 MB
-// Infinity Cache (the first read uses ordinary, allocating loads), so HBM sees
-// close to one read of x, one of z and one write of out.  The small
-// projection and scan work of one image overlaps the streaming of others.
+// Run image by image as a software pipeline, the second read of x comes a few
+// images after the first, while the image is still in the 256 MB Infinity
+// Cache (the first read uses ordinary, allocating loads; z and out use
+// non-allocating ones), so HBM sees close to one read of x, one of z and one
+// write of out.  The projection and scan work of one image overlaps the
+// streaming of others.
 //
-// Work items, each run by one 512-thread workgroup:
-//   A(b, k)  pool scan positions [k*RG, k*RG + RG) of image b, then x_proj of
-//            those pooled tokens (both directions); count it in rowsDone[b];
-//   S(b, k)  wait until rowsDone[b] == nA, then scan channels [64k, 64k + 64)
-//            of image b in both directions (scan_core.h); count it in scanDone[b];
-//   E(b, k)  wait until scanDone[b] == nS, then repeat + skip + gate grid rows
+// Work items, one per 512-thread workgroup:
+//   A(b, k)  pool scan positions [k*RG, k*RG + RG) of image b and project the
+//            pooled tokens (both directions); count it in rowsDone[b];
+//   S(b, k)  once rowsDone[b] == nA, scan channels [64k, 64k + 64) of image b
+//            in both directions (scan_core.h); count it in scanDone[b];
+//   E(b, k)  once scanDone[b] == nS, repeat + skip + gate grid rows
 //            [k*RE, k*RE + RE) of image b.
-// Items are handed out through one atomic ticket counter, in slots:
-//   slot s = [A(s, *)] [S(s - LS, *)] [E(s - LE, *)],  1 <= LS <= LE.
-// A workgroup takes its ticket when it starts and only ever waits for items
-// with smaller tickets, which were taken by workgroups that had already
-// started; so every wait ends, whatever the grid size or residency.  As a
-// guard against a broken invariant, a wait also gives up after a bounded
-// number of polls and raises a status bit instead of hanging.
+// Items are numbered slot by slot, slot s = [A(s, *)] [S(s - LS, *)]
+// [E(s - LE, *)] with 1 <= LS <= LE (items outside [0, B) are left out), and
+// handed out through one atomic ticket counter.  A workgroup takes its ticket
+// when it starts and waits only for items with smaller tickets, which were
+// taken by workgroups that had already started, so every wait ends whatever
+// the grid size or residency.  As a guard against a broken invariant a wait
+// also gives up after a bounded number of polls and raises a status bit.
+//
+// Publication without L2 write-backs: a producer stores its results with
+// agent-scope atomic stores (written through to the device-coherent level),
+// waits for them to complete, then bumps the counter; a consumer polls the
+// counter, then executes an agent-scope acquire (invalidating its CU's L1 and
+// its XCD's L2) before reading with ordinary loads.
 #include <cstdlib>
 
 #include "scan_core.h"
@@ -36,9 +43,11 @@
 namespace fastvim {
 namespace {
 
-constexpr int kFusedThreads = 512;
+constexpr int kFT = 512;                                     // threads per workgroup
 constexpr int kLdsFloats = (int)(sizeof(ScanSmem) / sizeof(float));
-constexpr unsigned kSpinLimit = 1u << 20;  // about a second of polling; normal waits are microseconds
+constexpr unsigned kSpinLimit = 1u << 20;                   // about a second of polling
+constexpr int kEU = 4;                                       // tokens per lane per batch (E items)
+constexpr int kMaxIv = 6;
 
 struct FusedArgs {
     const void* x;
@@ -54,7 +63,11 @@ struct FusedArgs {
     int R, NX, axis;
     int nA, nS, nE, RG, RE, G, VE, KS;
     int LS, LE;
-    int64_t per_slot, total;
+    int niv;                  // slot intervals with a constant number of items per slot
+    int64_t iv_s0[kMaxIv];    // first slot of the interval
+    int64_t iv_t0[kMaxIv];    // first ticket of the interval
+    int64_t iv_sz[kMaxIv];    // items per slot in the interval
+    int64_t total;
 };
 
 union alignas(16) FusedSmem {
@@ -75,9 +88,16 @@ __device__ __forceinline__ void wait_at_least(unsigned* cnt, unsigned target, un
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 }
 
-// Thread 0 only, after a workgroup barrier: publish the workgroup's stores.
-__device__ __forceinline__ void count_done(unsigned* cnt) {
-    __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+// All threads: wait for this thread's write-through stores to complete, then
+// (after the barrier) thread 0 counts the item done.
+__device__ __forceinline__ void publish(unsigned* cnt) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0) __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void store_through(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __device__ __forceinline__ float silu(float q) { return q * __builtin_amdgcn_rcpf(1.f + __expf(-q)); }
@@ -99,93 +119,80 @@ __device__ void item_pool_proj(const FusedArgs& a, int64_t b, int k, float* lds)
     const int64_t p_stride = cols ? E : a.w * E;
     const float inv_p = 1.0f / (float)P;
     const int NO = 2 * a.NX;
-    float* red = lds;                       // [G][E]
-    float* urow = lds + (int64_t)G * E;     // [RG][E]
-    float* part = urow + (int64_t)a.RG * E; // [RG][NO][KS]
+    float* red = lds;                        // [G][E]
+    float* urow = lds + (int64_t)G * E;      // [RG][E]
+    float* part = urow + (int64_t)a.RG * E;  // [RG][NO][KS]
 
+    const int pstr = (int)p_stride;
     for (int pos = 0; pos < npos; ++pos) {
         const int64_t t = t0 + pos;
         if (g < G) {
-            const elem* base = x + b * a.h * a.w * E + (cols ? t * a.w * E : t * E) + (int64_t)c * V;
+            // wave-uniform base, 32-bit lane offsets (an image holds < 2^31 elements)
+            const elem* base = x + b * a.h * a.w * E + (cols ? t * a.w * E : t * E);
+            const int coff = c * V;
             float acc[V];
 #pragma unroll
             for (int v = 0; v < V; ++v) acc[v] = 0.f;
-            int64_t p = g;
-            for (; p + 3 * G < P; p += 4 * G) {
-                const raw r0 = load_raw<false>(base + p * p_stride);
-                const raw r1 = load_raw<false>(base + (p + G) * p_stride);
-                const raw r2 = load_raw<false>(base + (p + 2 * G) * p_stride);
-                const raw r3 = load_raw<false>(base + (p + 3 * G) * p_stride);
+            int p = g;
+            // 8 allocating loads in flight per lane (x is read again by E items)
+            for (; p + 7 * G < P; p += 8 * G) {
+                raw r[8];
+#pragma unroll
+                for (int q = 0; q < 8; ++q) r[q] = load_raw<false>(base + (coff + (p + q * G) * pstr));
 #pragma unroll
                 for (int v = 0; v < V; ++v)
-                    acc[v] += (raw_at(r0, v) + raw_at(r1, v)) + (raw_at(r2, v) + raw_at(r3, v));
+                    acc[v] += ((raw_at(r[0], v) + raw_at(r[1], v)) + (raw_at(r[2], v) + raw_at(r[3], v))) +
+                              ((raw_at(r[4], v) + raw_at(r[5], v)) + (raw_at(r[6], v) + raw_at(r[7], v)));
             }
             for (; p < P; p += G) {
-                const raw r0 = load_raw<false>(base + p * p_stride);
+                const raw r0 = load_raw<false>(base + (coff + p * pstr));
 #pragma unroll
                 for (int v = 0; v < V; ++v) acc[v] += raw_at(r0, v);
             }
 #pragma unroll
-            for (int v = 0; v < V; ++v) red[(int64_t)g * E + (int64_t)c * V + v] = acc[v];
+            for (int v = 0; v < V; ++v) red[g * (int)E + coff + v] = acc[v];
         }
         __syncthreads();
-        for (int q = tid; q < E; q += kFusedThreads) {
+        for (int q = tid; q < E; q += kFT) {
             float s = red[q];
             for (int gg = 1; gg < G; ++gg) s += red[(int64_t)gg * E + q];
             s *= inv_p;
             urow[(int64_t)pos * E + q] = s;
-            a.u[(b * T + t) * E + q] = s;
+            store_through(a.u + (b * T + t) * E + q, s);
         }
         __syncthreads();
     }
 
-    // x_proj of the npos pooled tokens: pair (o, kk) dots the kk-th interleaved
-    // quarter of E with weight row o, for every position.
+    // x_proj of the pooled tokens: pair (o, kk) dots the kk-th interleaved
+    // part of E with weight row o, for every position (weights through the cache).
     const int npairs = NO * a.KS;
-    for (int pr = tid; pr < npairs; pr += kFusedThreads) {
+    const int E4 = (int)(E / 4);
+    for (int pr = tid; pr < npairs; pr += kFT) {
         const int o = pr / a.KS, kk = pr - o * a.KS;
         const float* W = o < a.NX ? a.pf.x_proj_w + (int64_t)o * E : a.pb.x_proj_w + (int64_t)(o - a.NX) * E;
-        float accp[8];
-#pragma unroll
-        for (int q = 0; q < 8; ++q) accp[q] = 0.f;
-        for (int64_t c4 = kk; c4 < E / 4; c4 += a.KS) {
-            const f32x4 wv = *reinterpret_cast<const f32x4*>(W + 4 * c4);
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                if (q < npos) {
-                    const f32x4 uv = *reinterpret_cast<const f32x4*>(urow + (int64_t)q * E + 4 * c4);
-                    accp[q] = fmaf(wv.x, uv.x, fmaf(wv.y, uv.y, fmaf(wv.z, uv.z, fmaf(wv.w, uv.w, accp[q]))));
-                }
+        for (int q = 0; q < npos; ++q) {  // the weight row is re-read from the cache per position
+            const float* ur = urow + q * (int)E;
+            float acc = 0.f;
+#pragma unroll 4
+            for (int c4 = kk; c4 < E4; c4 += a.KS) {
+                const f32x4 wv = *reinterpret_cast<const f32x4*>(W + 4 * c4);
+                const f32x4 uv = *reinterpret_cast<const f32x4*>(ur + 4 * c4);
+                acc = fmaf(wv.x, uv.x, fmaf(wv.y, uv.y, fmaf(wv.z, uv.z, fmaf(wv.w, uv.w, acc))));
             }
+            part[(q * NO + o) * a.KS + kk] = acc;
         }
-#pragma unroll
-        for (int q = 0; q < 8; ++q)
-            if (q < npos) part[((int64_t)q * NO + o) * a.KS + kk] = accp[q];
     }
     __syncthreads();
-    for (int idx = tid; idx < npos * NO; idx += kFusedThreads) {
+    for (int idx = tid; idx < npos * NO; idx += kFT) {
         const int q = idx / NO, o = idx - q * NO;
         float v = 0.f;
         for (int kk = 0; kk < a.KS; ++kk) v += part[((int64_t)q * NO + o) * a.KS + kk];
-        a.xdbl[(b * T + t0 + q) * NO + o] = v;
+        store_through(a.xdbl + (b * T + t0 + q) * NO + o, v);
     }
-    __syncthreads();
-    if (tid == 0) count_done(&a.sync[2 + b]);
+    publish(&a.sync[2 + b]);
 }
 
 // ---------------------------------------------------------------- E items
-// out of one token from its raw x and z vectors and its scan sum sv.
-template <class IO>
-__device__ __forceinline__ void emit_token(typename IO::elem* dst, const typename IO::raw& xr,
-                                           const typename IO::raw& zr, const float* sv, const float* dsum) {
-    constexpr int V = IO::V;
-    float o[V];
-#pragma unroll
-    for (int v = 0; v < V; ++v) o[v] = (sv[v] + dsum[v] * raw_at(xr, v)) * silu(raw_at(zr, v));
-    store_vec<true>(dst, o);
-}
-
-// s_fwd + s_bwd of scan position t for the lane's V channels.
 template <int V>
 __device__ __forceinline__ void scan_sum(const FusedArgs& a, int64_t b, int64_t t, int64_t col, float (&sv)[V]) {
     const float* s1 = a.s_f + (b * a.T + t) * a.E + col;
@@ -201,8 +208,8 @@ __device__ __forceinline__ void scan_sum(const FusedArgs& a, int64_t b, int64_t 
 }
 
 // Grid rows [k*RE, k*RE + RE) of image b.  x and z are read for the last time
-// (non-temporal), out is written once (non-temporal).  COLS: every token of
-// row i uses scan position i; ROWS: token (i, j) uses scan position j.
+// (non-temporal), out is written once (non-temporal).  Lane (c, g) handles the
+// row's tokens g + G*m in batches of kEU, all loads of a batch issued first.
 template <class IO, bool COLS>
 __device__ void item_epilogue(const FusedArgs& a, int64_t b, int k) {
     constexpr int V = IO::V;
@@ -213,7 +220,7 @@ __device__ void item_epilogue(const FusedArgs& a, int64_t b, int k) {
     __syncthreads();
     const int VE = a.VE, G = a.G;
     const int c = tid % VE, g = tid / VE;
-    if (g >= G) return;  // no barrier follows
+    if (g >= G) return;
     const int64_t E = a.E, w = a.w;
     const int64_t col = (int64_t)c * V;
     float dsum[V];
@@ -222,77 +229,83 @@ __device__ void item_epilogue(const FusedArgs& a, int64_t b, int k) {
 
     const int64_t i0 = (int64_t)k * a.RE;
     const int64_t i1 = i0 + a.RE < a.h ? i0 + a.RE : a.h;
+    const int iw = (int)w, iE = (int)E, coff = (int)col;
     for (int64_t i = i0; i < i1; ++i) {
-        const int64_t rowoff = (b * a.h + i) * w * E + col;
+        // wave-uniform row bases, 32-bit lane offsets
+        const int64_t rowoff = (b * a.h + i) * w * E;
         const elem* xr = static_cast<const elem*>(a.x) + rowoff;
         const elem* zr = static_cast<const elem*>(a.z) + rowoff;
         elem* orow = static_cast<elem*>(a.out) + rowoff;
-        if (COLS) {
-            float sv[V];
-            scan_sum<V>(a, b, i, col, sv);
-            int64_t j = g;
-            for (; j + G < w; j += 2 * G) {
-                const raw x0 = load_raw<true>(xr + j * E), z0 = load_raw<true>(zr + j * E);
-                const raw x1 = load_raw<true>(xr + (j + G) * E), z1 = load_raw<true>(zr + (j + G) * E);
-                emit_token<IO>(orow + j * E, x0, z0, sv, dsum);
-                emit_token<IO>(orow + (j + G) * E, x1, z1, sv, dsum);
+        float srow[V];
+        if (COLS) scan_sum<V>(a, b, i, col, srow);
+        for (int j0 = g; j0 < iw; j0 += G * kEU) {
+            raw xv[kEU], zv[kEU];
+#pragma unroll
+            for (int m = 0; m < kEU; ++m) {
+                const int j = j0 + G * m;
+                if (j < iw) {
+                    xv[m] = load_raw<true>(xr + (coff + j * iE));
+                    zv[m] = load_raw<true>(zr + (coff + j * iE));
+                }
             }
-            if (j < w) emit_token<IO>(orow + j * E, load_raw<true>(xr + j * E), load_raw<true>(zr + j * E), sv, dsum);
-        } else {
-            for (int64_t j = g; j < w; j += G) {
-                const raw x0 = load_raw<true>(xr + j * E), z0 = load_raw<true>(zr + j * E);
+#pragma unroll
+            for (int m = 0; m < kEU; ++m) {
+                const int j = j0 + G * m;
+                if (j >= iw) continue;
                 float sv[V];
-                scan_sum<V>(a, b, j, col, sv);
-                emit_token<IO>(orow + j * E, x0, z0, sv, dsum);
+                if (COLS) {
+#pragma unroll
+                    for (int v = 0; v < V; ++v) sv[v] = srow[v];
+                } else {
+                    scan_sum<V>(a, b, j, col, sv);
+                }
+                float o[V];
+#pragma unroll
+                for (int v = 0; v < V; ++v) o[v] = (sv[v] + dsum[v] * raw_at(xv[m], v)) * silu(raw_at(zv[m], v));
+                store_vec<true>(orow + (coff + j * iE), o);
             }
         }
     }
 }
 
 // ---------------------------------------------------------------- kernel
-template <class IO>
-__device__ __forceinline__ void run_item(const FusedArgs& a, int64_t ticket, FusedSmem& sm);
-
-// Persistent workgroups: each takes tickets in increasing order until they run
-// out, so every item waits only for items taken earlier by running workgroups.
-template <class IO>
-__global__ void __launch_bounds__(kFusedThreads) __attribute__((amdgpu_waves_per_eu(8))) fused_layer_kernel(FusedArgs a) {
+template <class IO, bool COLS, int RMAX>
+__global__ void __launch_bounds__(kFT) fused_layer_kernel(FusedArgs a) {
     __shared__ FusedSmem sm;
     __shared__ unsigned s_ticket;
-    for (;;) {
-        __syncthreads();  // the previous item is finished by every thread before s_ticket changes
-        if (threadIdx.x == 0)
-            s_ticket = __hip_atomic_fetch_add(&a.sync[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __syncthreads();
-        const int64_t ticket = s_ticket;
-        if (ticket >= a.total) return;
-        run_item<IO>(a, ticket, sm);
+    if (threadIdx.x == 0)
+        s_ticket = __hip_atomic_fetch_add(&a.sync[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const int64_t ticket = s_ticket;
+    if (ticket >= a.total) return;
+    // ticket -> (slot, index within the slot)
+    int iv = 0;
+    while (iv + 1 < a.niv && ticket >= a.iv_t0[iv + 1]) ++iv;
+    const int64_t off = ticket - a.iv_t0[iv];
+    const int64_t slot = a.iv_s0[iv] + off / a.iv_sz[iv];
+    int64_t r = off % a.iv_sz[iv];
+    if (slot < a.B) {
+        if (r < a.nA) {
+            item_pool_proj<IO>(a, slot, (int)r, sm.buf);
+            return;
+        }
+        r -= a.nA;
     }
-}
-
-template <class IO>
-__device__ __forceinline__ void run_item(const FusedArgs& a, int64_t ticket, FusedSmem& sm) {
-    const int64_t slot = ticket / a.per_slot;
-    const int r = (int)(ticket - slot * a.per_slot);
-    if (r < a.nA) {
-        if (slot < a.B) item_pool_proj<IO>(a, slot, r, sm.buf);
-    } else if (r < a.nA + a.nS) {
-        const int64_t b = slot - a.LS;
-        if (b >= 0 && b < a.B) {
-            if (threadIdx.x == 0) wait_at_least(&a.sync[2 + b], (unsigned)a.nA, &a.sync[1]);
+    const int64_t bs = slot - a.LS;
+    if (bs >= 0 && bs < a.B) {
+        if (r < a.nS) {
+            if (threadIdx.x == 0) wait_at_least(&a.sync[2 + bs], (unsigned)a.nA, &a.sync[1]);
             __syncthreads();
+            __builtin_amdgcn_s_setprio(2);  // the scan is on the critical path of its image
             ScanArgs sa{a.xdbl, a.pf, a.pb, a.s_f, a.s_b, a.T, a.E, a.R, a.NX};
-            scan_tile(sa, USrcPooled{a.u, a.T, a.E}, b, (int64_t)(r - a.nA) * kScanCh, sm.scan);
-            __syncthreads();
-            if (threadIdx.x == 0) count_done(&a.sync[2 + a.B + b]);
+            scan_tile<RMAX, true>(sa, USrcPooled{a.u, a.T, a.E}, bs, (int64_t)r * kScanCh, sm.scan);
+            __builtin_amdgcn_s_setprio(0);
+            publish(&a.sync[2 + a.B + bs]);
+            return;
         }
-    } else {
-        const int64_t b = slot - a.LE;
-        if (b >= 0 && b < a.B) {
-            if (a.axis == FASTVIM_POOL_COLS) item_epilogue<IO, true>(a, b, r - a.nA - a.nS);
-            else item_epilogue<IO, false>(a, b, r - a.nA - a.nS);
-        }
+        r -= a.nS;
     }
+    item_epilogue<IO, COLS>(a, slot - a.LE, (int)r);
 }
 
 __global__ void zero_sync_kernel(unsigned* sync, int64_t n) {
@@ -305,27 +318,28 @@ int env_int(const char* name, int dflt) {
     return s ? atoi(s) : dflt;
 }
 
-// Item sizes for a geometry; false if the fused kernel does not cover it.
+// Item sizes and ticket layout for a geometry; false if not covered.
 bool plan(const Geom& g, FusedArgs* a) {
-    if (!g.pooled || g.masked) return false;
+    if (!g.pooled || g.masked || g.B < 1) return false;
+    if (g.h * g.w * g.E >= ((int64_t)1 << 31)) return false;  // 32-bit offsets within an image
     const int V = g.io == FASTVIM_BF16 ? 8 : 4;
     const int64_t esz = g.io == FASTVIM_BF16 ? 2 : 4;
     const int64_t VE = g.E / V;
-    if (VE > kFusedThreads) return false;
-    const int G = (int)(kFusedThreads / VE);
+    if (VE > kFT) return false;
+    const int G = (int)(kFT / VE);
     const int64_t NO = 2 * g.NX;
-    int KS = (int)(kFusedThreads / NO);
+    int KS = (int)(kFT / NO);
     KS = KS < 1 ? 1 : (KS > 4 ? 4 : KS);
-    // A items: about 384 KB of x each, at most 8 positions, within the LDS budget.
+    // A items: about 200 KB of x each, at most 8 positions, within the LDS budget.
     const int64_t pos_bytes = g.P * g.E * esz;
-    int64_t RG = (384 * 1024) / (pos_bytes > 0 ? pos_bytes : 1);
+    int64_t RG = (200 * 1024) / (pos_bytes > 0 ? pos_bytes : 1);
     RG = RG < 1 ? 1 : (RG > 8 ? 8 : RG);
     if (RG > g.T) RG = g.T;
     while (RG > 1 && G * g.E + RG * g.E + RG * NO * KS > kLdsFloats) --RG;
     if (G * g.E + RG * g.E + RG * NO * KS > kLdsFloats) return false;
-    // E items: about 256 KB of each stream.
+    // E items: about 200 KB of each stream.
     const int64_t row_bytes = g.w * g.E * esz;
-    int64_t RE = (256 * 1024) / (row_bytes > 0 ? row_bytes : 1);
+    int64_t RE = (200 * 1024) / (row_bytes > 0 ? row_bytes : 1);
     RE = RE < 1 ? 1 : RE;
     if (RE > g.h) RE = g.h;
     a->B = g.B; a->h = g.h; a->w = g.w; a->E = g.E; a->T = g.T; a->P = g.P;
@@ -334,29 +348,50 @@ bool plan(const Geom& g, FusedArgs* a) {
     a->nA = (int)((g.T + RG - 1) / RG);
     a->nS = (int)((g.E + kScanCh - 1) / kScanCh);
     a->nE = (int)((g.h + RE - 1) / RE);
-    a->LS = env_int("FASTVIM_FUSED_LS", 1);
-    a->LE = env_int("FASTVIM_FUSED_LE", 2);
+    a->LS = env_int("FASTVIM_FUSED_LS", 3);
+    a->LE = env_int("FASTVIM_FUSED_LE", 8);
     if (a->LS < 1) a->LS = 1;
     if (a->LE < a->LS) a->LE = a->LS;
-    a->per_slot = a->nA + a->nS + a->nE;
-    a->total = (g.B + a->LE) * a->per_slot;
-    return a->total < (int64_t)UINT32_MAX;
+    // slots [0, B + LE): piecewise-constant item counts between the breakpoints
+    int64_t pts[6] = {0, a->LS, a->LE, g.B, g.B + a->LS, g.B + a->LE};
+    for (int i = 1; i < 6; ++i)  // insertion sort
+        for (int j = i; j > 0 && pts[j] < pts[j - 1]; --j) {
+            const int64_t tmp = pts[j];
+            pts[j] = pts[j - 1];
+            pts[j - 1] = tmp;
+        }
+    int64_t tick = 0;
+    a->niv = 0;
+    for (int i = 0; i + 1 < 6; ++i) {
+        const int64_t s0 = pts[i], s1 = pts[i + 1];
+        if (s1 <= s0) continue;
+        const int64_t sz = (s0 < g.B ? a->nA : 0) + (s0 >= a->LS && s0 < g.B + a->LS ? a->nS : 0) +
+                           (s0 >= a->LE && s0 < g.B + a->LE ? a->nE : 0);
+        if (sz == 0) continue;
+        a->iv_s0[a->niv] = s0;
+        a->iv_t0[a->niv] = tick;
+        a->iv_sz[a->niv] = sz;
+        ++a->niv;
+        tick += (s1 - s0) * sz;
+    }
+    a->total = tick;
+    return a->niv > 0 && a->total < (int64_t)UINT32_MAX;
 }
 
-// Persistent grid: as many workgroups as can be resident at once (never more
-// than there are tickets).
+template <class IO, int RMAX>
+hipError_t fused_launch_r(const FusedArgs& a, hipStream_t st) {
+    if (a.axis == FASTVIM_POOL_COLS)
+        hipLaunchKernelGGL((fused_layer_kernel<IO, true, RMAX>), dim3((unsigned)a.total), dim3(kFT), 0, st, a);
+    else
+        hipLaunchKernelGGL((fused_layer_kernel<IO, false, RMAX>), dim3((unsigned)a.total), dim3(kFT), 0, st, a);
+    return hipGetLastError();
+}
+
 template <class IO>
 hipError_t fused_launch_io(const FusedArgs& a, hipStream_t st) {
-    int dev = 0, cus = 0, per_cu = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e == hipSuccess)
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fused_layer_kernel<IO>, kFusedThreads, 0);
-    if (e != hipSuccess) return e;
-    int64_t grid = (int64_t)(cus > 0 ? cus : 1) * (per_cu > 0 ? per_cu : 1);
-    if (grid > a.total) grid = a.total;
-    hipLaunchKernelGGL((fused_layer_kernel<IO>), dim3((unsigned)grid), dim3(kFusedThreads), 0, st, a);
-    return hipGetLastError();
+    if (a.R <= 16) return fused_launch_r<IO, 16>(a, st);
+    if (a.R <= 32) return fused_launch_r<IO, 32>(a, st);
+    return fused_launch_r<IO, 64>(a, st);
 }
 
 }  // namespace

@@ -8,21 +8,30 @@
 namespace fastvim {
 namespace {
 
-template <class USrc>
+template <int RMAX, class USrc>
 __global__ void __launch_bounds__(kScanThreads) scan_kernel(ScanArgs a, USrc usrc, int nEg) {
     __shared__ ScanSmem sm;
     const int64_t b = blockIdx.x / nEg;
     const int64_t e0 = (int64_t)(blockIdx.x % nEg) * kScanCh;
-    scan_tile(a, usrc, b, e0, sm);
+    scan_tile<RMAX, false>(a, usrc, b, e0, sm);
+}
+
+template <int RMAX, class USrc>
+hipError_t scan_launch(const USrc& usrc, const Geom& g, const fastvim_params& p, const Workspace& ws,
+                       hipStream_t st) {
+    const int nEg = (int)((g.E + kScanCh - 1) / kScanCh);
+    ScanArgs a{ws.xdbl, p.fwd, p.bwd, ws.s_f, ws.s_b, g.T, g.E, (int)g.R, (int)g.NX};
+    hipLaunchKernelGGL((scan_kernel<RMAX, USrc>), dim3((unsigned)(g.B * nEg)), dim3(kScanThreads), 0, st, a, usrc,
+                       nEg);
+    return hipGetLastError();
 }
 
 template <class USrc>
 hipError_t scan_dispatch(const USrc& usrc, const Geom& g, const fastvim_params& p, const Workspace& ws,
                          hipStream_t st) {
-    const int nEg = (int)((g.E + kScanCh - 1) / kScanCh);
-    ScanArgs a{ws.xdbl, p.fwd, p.bwd, ws.s_f, ws.s_b, g.T, g.E, (int)g.R, (int)g.NX};
-    hipLaunchKernelGGL((scan_kernel<USrc>), dim3((unsigned)(g.B * nEg)), dim3(kScanThreads), 0, st, a, usrc, nEg);
-    return hipGetLastError();
+    if (g.R <= 16) return scan_launch<16>(usrc, g, p, ws, st);
+    if (g.R <= 32) return scan_launch<32>(usrc, g, p, ws, st);
+    return scan_launch<64>(usrc, g, p, ws, st);
 }
 
 }  // namespace
