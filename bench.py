@@ -1,31 +1,52 @@
 #!/usr/bin/env python3
 """Benchmark of the pooled bidirectional selective-scan layer on one MI355X.
 
-One step = one call of the whole layer (pool, x_proj, step size + both scans,
-repeat + skip + gate) on the 2048^2 FastVim-T workload: B = 128 images of a
-128 x 128 token grid, E = 384, N = 16, R = 12, fp32, pooled over columns,
-inputs resident in HBM.  Prints one JSON line.
+One step = one call of the whole layer -- pool, x_proj, step sizes and both
+scans, repeat + skip + gate -- on the 2048^2 FastVim-T workload: B = 128
+images of a 128 x 128 token grid, E = 384, N = 16, R = 12, fp32, pooled over
+columns, inputs already resident in HBM.  The layer runs as the library's
+default path, one pipelined kernel launch (plus a one-block launch that resets
+its counters).  Prints one JSON line on stdout.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--no-extras]
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-extras] [--no-cpu-baseline]
+                    [--cpu-seconds S] [--profile-run]
 
-Besides the headline images/s it reports the per-stage kernel times, the
-roofline of the dominant kernel (the streaming epilogue: x and z read once,
-out written once), a plain device-copy ceiling, the unpooled layer on the same
-inputs (scan over all h*w tokens) for the pooling speedup, and the fp64 CPU
-oracle's throughput on a bounded sample of the same workload.
+Reported besides images/s:
+  roofline      the single-launch kernel against the 8 TB/s HBM peak, with
+                algorithmic bytes (x and z read once, out written once:
+                12 B per grid element) over the measured step time, and the
+                HBM traffic the hardware counters recorded for it, when the
+                recorded counter summary belongs to the current kernel source;
+  cpu_baseline  the fp64 CPU oracle on the same host arrays, cycled over the
+                batch for at least --cpu-seconds;
+  extras        the stage-kernel path and its per-stage times, the other
+                pooling axis, the calibration-copy ceiling, the unpooled layer
+                (scan over all h*w tokens) with the pooled / unpooled ratios,
+                and the 1024^2 two-block chain.
+--profile-run times a few steps and the calibration copy only (for profiler
+runs).
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
 import numpy as np
 
+ROOT = os.path.dirname(os.path.abspath(__file__))
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 METRIC = "pooled SSM layer images/s + % HBM peak at 2048² (h=w=128) fp32, B=128"
+COUNTERS = os.path.join(ROOT, "profiles", "fused_layer_pooled_2048_T_b128_counters.md")
+# the sources the single-launch kernel is compiled from (the counter summary is
+# only valid for the exact text it was recorded with)
+KERNEL_SOURCES = ("pooled_selective_state_amd/csrc/fused.hip", "pooled_selective_state_amd/csrc/scan_core.h",
+                  "pooled_selective_state_amd/csrc/fastvim_internal.h", "include/fastvim.h",
+                  "pooled_selective_state_amd/build.py")
 
 
 def parse():
@@ -34,44 +55,96 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-extras", action="store_true", help="skip the unpooled / copy-ceiling measurements")
-    ap.add_argument("--cpu-images", type=int, default=64, help="images in the oracle's timed sample")
+    ap.add_argument("--no-extras", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum CPU time of the oracle sample")
+    ap.add_argument("--profile-run", action="store_true", help="layer steps and calibration copy only")
     return ap.parse_args()
 
 
-def timed(fn, n, stream):
-    """Average ms of fn() over n calls, HIP events on ``stream``."""
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def kernel_sources_sha256():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        h.update(rel.encode())
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic():
+    """HBM bytes per launch of the single-launch kernel from the committed
+    counter summary, or None if absent or recorded for other kernel sources."""
+    if not os.path.exists(COUNTERS):
+        return None, "no counter summary"
+    text = open(COUNTERS).read()
+    m_t = re.search(r"^traffic_bytes_per_launch:\s*([0-9.eE+]+)\s*$", text, re.M)
+    m_h = re.search(r"^kernel_sources_sha256:\s*([0-9a-f]{64})\s*$", text, re.M)
+    if not (m_t and m_h):
+        return None, "counter summary incomplete"
+    if m_h.group(1) != kernel_sources_sha256():
+        return None, "counter summary recorded for other kernel sources"
+    return float(m_t.group(1)), os.path.relpath(COUNTERS, ROOT)
+
+
+def time_steps(fn, k, stream):
+    """Run fn() k times on ``stream`` with a HIP event between calls; returns
+    (mean ms over the whole region, list of per-call ms)."""
     import torch
-    a = torch.cuda.Event(enable_timing=True)
-    b = torch.cuda.Event(enable_timing=True)
-    a.record(stream)
-    for _ in range(n):
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(k + 1)]
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for i in range(k):
         fn()
-    b.record(stream)
-    b.synchronize()
-    return a.elapsed_time(b) / n
+        ev[i + 1].record(stream)
+    ev[k].synchronize()
+    torch.cuda.synchronize()
+    return ev[0].elapsed_time(ev[k]) / k, [ev[i].elapsed_time(ev[i + 1]) for i in range(k)]
 
 
-def cpu_baseline(wl, n_img):
-    """fp64 oracle (as it stands) on the first n_img images of the workload."""
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(x, z, prm, axis, seconds):
+    """The fp64 oracle as it stands, cycled over the batch in chunks of
+    images until at least ``seconds`` have passed."""
     import oracle
-    x, z, prm = wl["x"], wl["z"][0], wl["params"][0]
-    n_img = min(n_img, x.shape[0])
-    xs, zs = x[:n_img], z[:n_img]
+    B = x.shape[0]
+    threads = oracle.max_threads()
+    chunk = min(B, max(8, threads))
+    done, b = 0, 0
     t0 = time.perf_counter()
-    oracle.layer(xs, zs, prm["fwd"], prm["bwd"], oracle.COLS)
-    dt = time.perf_counter() - t0
-    return {"value": n_img / dt, "unit": "images/s", "cores": oracle.max_threads(), "kind": "oracle",
-            "sample": "first %d of %d images of the same seeded workload, full layer in fp64 (%.2f s wall)"
-                      % (n_img, x.shape[0], dt)}
+    while True:
+        e = min(B, b + chunk)
+        oracle.layer(x[b:e], z[b:e], prm["fwd"], prm["bwd"], axis)
+        done += e - b
+        b = 0 if e == B else e
+        dt = time.perf_counter() - t0
+        if dt >= seconds:
+            break
+    return {"value": done / dt, "unit": "images/s", "cores": min(threads, chunk), "kind": "oracle",
+            "sample": "%d images (the batch of %d cycled in chunks of %d) of the same seeded host arrays, whole "
+                      "layer in fp64, %.1f s wall; CPU %s" % (done, B, chunk, dt, cpu_model())}
 
 
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (batch sharding across GPUs is "
-              "described in the design notes); run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU: the layer has no multi-GPU path in this library (images are "
+              "independent, so a batch shards across GPUs with no exchange); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
+    if args.profile_run:
+        args.no_extras = args.no_cpu_baseline = True
 
     import torch
     import pooled_selective_state_amd as P
@@ -79,11 +152,11 @@ def main():
     from pooled_selective_state_amd.inputs import draw_workload
 
     assert torch.cuda.is_available(), "bench.py needs a ROCm GPU"
-    P.lib()
+    P.lib()  # raises if the HIP library is not built
     cfg = C.HIRES_2048
     t0 = time.perf_counter()
     wl = draw_workload(cfg)
-    print("[bench] inputs drawn in %.1f s" % (time.perf_counter() - t0), file=sys.stderr, flush=True)
+    log("inputs drawn in %.1f s" % (time.perf_counter() - t0))
     dev = torch.device("cuda:0")
     x = torch.from_numpy(wl["x"]).to(dev)
     z = torch.from_numpy(wl["z"][0]).to(dev)
@@ -95,19 +168,16 @@ def main():
     for _ in range(args.warmup):
         call.run(stream)
     torch.cuda.synchronize()
-    ms = timed(lambda: call.run(stream), args.steps, stream)
-    torch.cuda.synchronize()
-    print("[bench] layer %.3f ms/step" % ms, file=sys.stderr, flush=True)
+    ms, per = time_steps(lambda: call.run(stream), args.steps, stream)
+    status = int(call.export(P.EXPORT_STATUS, stream).item())
+    if status:
+        raise RuntimeError("single-launch kernel reported status %#x (a bounded wait gave up)" % status)
+    log("layer %.4f ms/step (median %.4f, min %.4f)" % (ms, float(np.median(per)), min(per)))
 
     elems = cfg.B * cfg.h * cfg.w * cfg.E
-    alg_bytes = 3 * 4 * elems  # x read once, z read once, out written once
-    stages = {}
-    for name, sid in (("pool", P.STAGE_POOL), ("proj", P.STAGE_PROJ), ("scan", P.STAGE_SCAN),
-                      ("epilogue", P.STAGE_EPILOGUE)):
-        stages[name] = timed(lambda: call.stage(sid, stream), max(3, args.steps // 2), stream)
-    torch.cuda.synchronize()
-    epi_ms = stages["epilogue"]
-    epi_gbs = alg_bytes / (epi_ms * 1e-3) / 1e9
+    alg_bytes = 3 * 4 * elems  # x read once, z read once, out written once (fp32)
+    achieved = alg_bytes / (ms * 1e-3) / 1e9
+    traffic, traffic_src = recorded_traffic()
 
     result = {
         "metric": METRIC,
@@ -121,37 +191,94 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
-        "data": "synthetic",
+        "data": "synthetic (seeded N(0,1) activations, pages' parameter recipe)",
         "config": {"workload": cfg.name, "B": cfg.B, "h": cfg.h, "w": cfg.w, "E": cfg.E, "N": cfg.N, "R": cfg.R,
-                   "pool_axis": "cols", "seed": 0},
+                   "pool_axis": "cols", "path": "single launch", "seed": 0},
+        "ms_median": float(np.median(per)),
+        "ms_min": float(min(per)),
         "tokens_per_s": cfg.B * cfg.h * cfg.w / (ms * 1e-3),
-        "layer_hbm_frac": alg_bytes / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9),
-        "stage_ms": stages,
-        "roofline": {"bound": "hbm", "kernel": "epilogue (repeat + skip + gate)", "achieved": epi_gbs,
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": epi_gbs / HBM_PEAK_GBS, "traffic": None},
+        "hbm_frac": achieved / HBM_PEAK_GBS,
+        "roofline": {"bound": "hbm", "kernel": "fused_layer_kernel (whole layer, one launch per step)",
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": traffic, "traffic_unit": "HBM bytes per launch", "traffic_source": traffic_src,
+                     "alg_bytes_per_launch": alg_bytes},
     }
 
+    # calibration copy of one input-sized buffer (also the counter scale run)
+    dst = torch.empty_like(x)
+    for _ in range(2):
+        P.calib_copy(dst, x, stream)
+    cp_ms, _ = time_steps(lambda: P.calib_copy(dst, x, stream), 3 if args.profile_run else 5, stream)
+    result["copy_ceiling"] = {"GBps": 2 * 4 * elems / (cp_ms * 1e-3) / 1e9, "bytes_read": 4 * elems,
+                              "bytes_written": 4 * elems, "ms": cp_ms, "kernel": "calib_copy_kernel"}
+    del dst
+    log("calibration copy %.4f ms (%.0f GB/s)" % (cp_ms, result["copy_ceiling"]["GBps"]))
+
     if not args.no_extras:
-        # Plain device copy of one input-sized buffer: a practical streaming ceiling.
+        extras = {}
+        n = max(3, args.steps // 2)
+        # the same layer as stage kernels
+        scall = P.SSMCall(x, z, prm, P.POOL_COLS, workspace=call.workspace, flags=P.FLAG_STAGED)
+        scall.run(stream)
+        st_ms, _ = time_steps(lambda: scall.run(stream), n, stream)
+        stages = {}
+        for name, sid in (("pool", P.STAGE_POOL), ("proj", P.STAGE_PROJ), ("scan", P.STAGE_SCAN),
+                          ("epilogue", P.STAGE_EPILOGUE)):
+            stages[name], _ = time_steps(lambda: scall.stage(sid, stream), n, stream)
+        extras["staged"] = {"layer_ms": st_ms, "stage_ms": stages}
+        # the other pooling axis (the next block's orientation)
+        rcall = P.SSMCall(x, z, prm, P.POOL_ROWS, workspace=call.workspace, out=call.out)
+        rcall.run(stream)
+        extras["rows_layer_ms"], _ = time_steps(lambda: rcall.run(stream), n, stream)
+        # torch's device copy, for comparison with the calibration copy
         dst = torch.empty_like(x)
-        cp_ms = timed(lambda: dst.copy_(x), 5, stream)
-        result["copy_ceiling_GBps"] = 2 * 4 * elems / (cp_ms * 1e-3) / 1e9
-        del dst
-        # Unpooled layer on the same inputs: scan over all h*w tokens.
-        ucall = P.SSMCall(x, z, prm, P.POOL_NONE_ROWMAJOR)
+        tc_ms, _ = time_steps(lambda: dst.copy_(x), 3, stream)
+        extras["torch_copy_GBps"] = 2 * 4 * elems / (tc_ms * 1e-3) / 1e9
+        del dst, scall, rcall
+        # unpooled layer on the same inputs: a scan over all h*w tokens
+        ucall = P.SSMCall(x, z, prm, P.POOL_NONE_ROWMAJOR, out=call.out)
         ucall.run(stream)
-        torch.cuda.synchronize()
-        u_ms = timed(lambda: ucall.run(stream), 3, stream)
-        u_scan = timed(lambda: ucall.stage(P.STAGE_SCAN, stream), 3, stream)
-        u_proj = timed(lambda: ucall.stage(P.STAGE_PROJ, stream), 3, stream)
-        torch.cuda.synchronize()
-        result["unpooled"] = {"layer_ms": u_ms, "scan_ms": u_scan, "proj_ms": u_proj, "T": cfg.h * cfg.w,
-                              "layer_speedup": u_ms / ms, "scan_speedup": u_scan / stages["scan"]}
+        u_ms, _ = time_steps(lambda: ucall.run(stream), 3, stream)
+        u_scan, _ = time_steps(lambda: ucall.stage(P.STAGE_SCAN, stream), 3, stream)
+        u_proj, _ = time_steps(lambda: ucall.stage(P.STAGE_PROJ, stream), 3, stream)
+        extras["unpooled_2048"] = {"T": cfg.h * cfg.w, "layer_ms": u_ms, "scan_ms": u_scan, "proj_ms": u_proj,
+                                   "layer_speedup_pooled": u_ms / ms, "scan_speedup_pooled": u_scan / stages["scan"]}
         del ucall
         torch.cuda.empty_cache()
+        log("unpooled layer %.3f ms, scan %.3f ms" % (u_ms, u_scan))
+        # 1024^2 two-block chain on a quarter of the same buffers (same E and R)
+        c2 = C.CHAIN_1024
+        n2 = c2.B * c2.h * c2.w * c2.E
+        x2 = x.view(-1)[:n2].view(c2.B, c2.h, c2.w, c2.E)
+        z2 = z.view(-1)[:n2].view(c2.B, c2.h, c2.w, c2.E)
+        z2b = z.view(-1)[n2:2 * n2].view(c2.B, c2.h, c2.w, c2.E)
+        b1 = P.SSMCall(x2, z2, prm, P.POOL_COLS)
+        b2 = P.SSMCall(b1.out, z2b, prm, P.POOL_ROWS, workspace=b1.workspace)
+
+        def chain():
+            b1.run(stream)
+            b2.run(stream)
+        chain()
+        ch_ms, _ = time_steps(chain, n, stream)
+        s1 = P.SSMCall(x2, z2, prm, P.POOL_COLS, workspace=b1.workspace, out=b2.out, flags=P.FLAG_STAGED)
+        s1.run(stream)
+        p_scan, _ = time_steps(lambda: s1.stage(P.STAGE_SCAN, stream), n, stream)
+        u2 = P.SSMCall(x2, z2, prm, P.POOL_NONE_ROWMAJOR, out=b2.out)
+        u2.run(stream)
+        u2_ms, _ = time_steps(lambda: u2.run(stream), 3, stream)
+        u2_scan, _ = time_steps(lambda: u2.stage(P.STAGE_SCAN, stream), 3, stream)
+        extras["chain_1024"] = {"workload": c2.name, "two_block_ms": ch_ms, "images_per_s": c2.B / (ch_ms * 1e-3),
+                                "hbm_frac": 2 * 12 * n2 / (ch_ms * 1e-3) / (HBM_PEAK_GBS * 1e9),
+                                "pooled_scan_ms": p_scan, "unpooled_layer_ms": u2_ms, "unpooled_scan_ms": u2_scan,
+                                "scan_speedup_pooled": u2_scan / p_scan,
+                                "layer_speedup_pooled": u2_ms / (ch_ms / 2)}
+        del b1, b2, s1, u2
+        torch.cuda.empty_cache()
+        result["extras"] = extras
 
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_images)
+        log("timing the CPU oracle (>= %.0f s)" % args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(wl["x"], wl["z"][0], wl["params"][0], 0, args.cpu_seconds)
 
     print(json.dumps(result), flush=True)
 

@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define FASTVIM_ABI_VERSION 1
+#define FASTVIM_ABI_VERSION 2
 
 typedef enum fastvim_status {
     FASTVIM_OK = 0,
@@ -116,12 +116,16 @@ typedef struct fastvim_params {
     uint32_t reserved;
 } fastvim_params;
 
-/* params.flags bits.  By default a layer runs as its stage kernels (the ones
- * fastvim_ssm_stage runs).  FASTVIM_FLAG_FUSED runs a dense pooled layer as
- * one pipelined launch (plus a one-block launch that resets its counters)
- * instead; other layers ignore it.  Both give the same results within
- * rounding. */
-#define FASTVIM_FLAG_FUSED 1u
+/* params.flags bits.  By default a dense pooled layer (COLS or ROWS, no mask)
+ * whose images hold at least 8 MiB of x each runs as one pipelined launch,
+ * preceded by a one-block launch that resets its counters in the workspace;
+ * every other layer runs as its stage kernels (the ones fastvim_ssm_stage
+ * runs).  FASTVIM_FLAG_STAGED runs every layer as its stage kernels;
+ * FASTVIM_FLAG_FUSED runs every dense pooled layer as the single launch,
+ * whatever its size.  Both paths give the same results within rounding.
+ * Setting both bits is FASTVIM_ERR_ARG. */
+#define FASTVIM_FLAG_STAGED 1u
+#define FASTVIM_FLAG_FUSED 2u
 
 /* Bytes of workspace a call with these sizes needs (0 if the sizes are
  * invalid).  Dense pooled layers need 4 * B * T * (3E + 2(R + 2N)) bytes plus
@@ -181,6 +185,16 @@ int fastvim_ssm_export(const fastvim_params *params, const fastvim_dims *dims, i
 
 /* Size in bytes of an export (0 if the layer does not have it). */
 size_t fastvim_ssm_export_bytes(const fastvim_dims *dims, int pool_axis, int what);
+
+/* Measurement aid, not part of the layer: copy `bytes` bytes from src to dst
+ * (device memory, both 16-byte aligned, bytes a multiple of 16, no overlap)
+ * with a plain streaming kernel -- 16-byte nontemporal loads and stores, every
+ * byte read once and written once.  Its rate is the device's practical
+ * streaming ceiling, and its hardware byte counters (read bytes == written
+ * bytes == `bytes`) calibrate those of the layer's kernels.  Enqueued on
+ * stream; bytes == 0 launches nothing.  Errors: FASTVIM_ERR_NULL,
+ * FASTVIM_ERR_ALIGN, FASTVIM_ERR_OVERLAP, FASTVIM_ERR_HIP. */
+int fastvim_calib_copy(void *dst, const void *src, size_t bytes, void *stream);
 
 /* Static text for a status code. */
 const char *fastvim_status_string(int status);

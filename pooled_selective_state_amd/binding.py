@@ -24,8 +24,10 @@ F32, BF16 = 0, 1
 STAGE_ROWS, STAGE_POOL, STAGE_PROJ, STAGE_SCAN, STAGE_EPILOGUE = 0, 1, 2, 3, 4
 # fastvim_export
 EXPORT_U, EXPORT_XDBL, EXPORT_S_FWD, EXPORT_S_BWD, EXPORT_ROWS, EXPORT_BAD_TOKENS, EXPORT_STATUS = 0, 1, 2, 3, 4, 5, 6
-# params.flags
-FLAG_FUSED = 1
+# params.flags: FLAG_STAGED runs every layer as its stage kernels, FLAG_FUSED
+# every dense pooled layer as the single pipelined launch; by default the
+# library picks by size
+FLAG_STAGED, FLAG_FUSED = 1, 2
 
 STATUS = {
     0: "FASTVIM_OK", -1: "FASTVIM_ERR_NULL", -2: "FASTVIM_ERR_DIMS", -3: "FASTVIM_ERR_UNSUPPORTED",
@@ -60,7 +62,7 @@ class Params(ctypes.Structure):
 
 EXPORTED_SYMBOLS = (
     "fastvim_ssm_workspace_bytes", "fastvim_ssm_fwd", "fastvim_ssm_stage", "fastvim_ssm_export",
-    "fastvim_ssm_export_bytes", "fastvim_status_string", "fastvim_abi_version",
+    "fastvim_ssm_export_bytes", "fastvim_calib_copy", "fastvim_status_string", "fastvim_abi_version",
 )
 
 _lock = threading.Lock()
@@ -87,6 +89,8 @@ def lib():
             L.fastvim_ssm_export.restype = ci
             L.fastvim_ssm_export_bytes.argtypes = [PD, ci, ci]
             L.fastvim_ssm_export_bytes.restype = sz
+            L.fastvim_calib_copy.argtypes = [vp, vp, sz, vp]
+            L.fastvim_calib_copy.restype = ci
             L.fastvim_status_string.argtypes = [ci]
             L.fastvim_status_string.restype = ctypes.c_char_p
             L.fastvim_abi_version.argtypes = []
@@ -214,3 +218,14 @@ def ssm_fwd(x, z, params, pool_axis=POOL_COLS, mask_idx=None, hw=None, out=None,
     """The pooled bidirectional selective-scan layer; returns out."""
     return SSMCall(x, z, params, pool_axis, mask_idx=mask_idx, hw=hw, out=out, workspace=workspace,
                    flags=flags).run(stream)
+
+
+def calib_copy(dst: torch.Tensor, src: torch.Tensor, stream=None) -> None:
+    """Streaming copy of src into dst (same byte size) by the library's
+    calibration kernel; a measurement aid, not part of the layer."""
+    n = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != n or not (dst.is_contiguous() and src.is_contiguous()):
+        raise ValueError("calib_copy needs contiguous tensors of equal byte size")
+    st = lib().fastvim_calib_copy(_ptr(dst), _ptr(src), n, _stream(stream))
+    if st:
+        raise FastVimError(st, "fastvim_calib_copy")

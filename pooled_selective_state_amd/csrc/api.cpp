@@ -73,6 +73,8 @@ int check_dir(const fastvim_dir_params& d) {
 int validate(const void* x, const void* z, const fastvim_params* prm, const fastvim_dims* d, int axis,
              const int32_t* idx, const void* out, Geom* g, Workspace* ws, bool* empty) {
     if (!prm) return FASTVIM_ERR_NULL;
+    const uint32_t known = FASTVIM_FLAG_STAGED | FASTVIM_FLAG_FUSED;
+    if ((prm->flags & ~known) || (prm->flags & known) == known) return FASTVIM_ERR_ARG;
     int st = resolve_geom(d, axis, g);
     if (st) return st;
     if (!g->masked && idx) return FASTVIM_ERR_ARG;
@@ -178,7 +180,9 @@ int fastvim_ssm_fwd(const void* x, const void* z, const fastvim_params* params, 
     if (st || empty) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (launch_zero_sync(ws, sync_words(g), s) != hipSuccess) return FASTVIM_ERR_HIP;
-    if ((params->flags & FASTVIM_FLAG_FUSED) && fused_supported(g))
+    const bool single = (params->flags & FASTVIM_FLAG_FUSED) ? fused_supported(g)
+                        : !(params->flags & FASTVIM_FLAG_STAGED) && fused_preferred(g);
+    if (single)
         return launch_fused(g, x, z, *params, ws, out, s) == hipSuccess ? FASTVIM_OK : FASTVIM_ERR_HIP;
     for (int stage = FASTVIM_STAGE_ROWS; stage <= FASTVIM_STAGE_EPILOGUE; ++stage) {
         st = run_stage(stage, g, x, z, *params, mask_idx, out, ws, s);
@@ -232,6 +236,16 @@ int fastvim_ssm_export(const fastvim_params* params, const fastvim_dims* dims, i
     return e == hipSuccess ? FASTVIM_OK : FASTVIM_ERR_HIP;
 }
 
+int fastvim_calib_copy(void* dst, const void* src, size_t bytes, void* stream) {
+    if (bytes == 0) return FASTVIM_OK;
+    if (!dst || !src) return FASTVIM_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(dst) | reinterpret_cast<uintptr_t>(src) | bytes) & 15) return FASTVIM_ERR_ALIGN;
+    const uintptr_t d0 = reinterpret_cast<uintptr_t>(dst), s0 = reinterpret_cast<uintptr_t>(src);
+    if (d0 < s0 + bytes && s0 < d0 + bytes) return FASTVIM_ERR_OVERLAP;
+    return launch_calib_copy(dst, src, bytes, static_cast<hipStream_t>(stream)) == hipSuccess ? FASTVIM_OK
+                                                                                               : FASTVIM_ERR_HIP;
+}
+
 const char* fastvim_status_string(int status) {
     switch (status) {
         case FASTVIM_OK: return "ok";
@@ -242,7 +256,7 @@ const char* fastvim_status_string(int status) {
         case FASTVIM_ERR_OVERLAP: return "out overlaps x or z, or the workspace overlaps an input or output";
         case FASTVIM_ERR_WORKSPACE: return "workspace missing or smaller than fastvim_ssm_workspace_bytes";
         case FASTVIM_ERR_HIP: return "HIP reported an error while enqueuing work";
-        case FASTVIM_ERR_ARG: return "bad enum, stage or export id, or mask_idx given for a dense layer";
+        case FASTVIM_ERR_ARG: return "bad enum, stage or export id, unknown or conflicting flags, or mask_idx given for a dense layer";
         default: return "unknown status";
     }
 }

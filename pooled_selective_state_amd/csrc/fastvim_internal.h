@@ -50,9 +50,11 @@ hipError_t launch_epilogue(const Geom& g, const void* x, const void* z, const fa
                            const Workspace& ws, void* out, hipStream_t st);
 // Single-launch dense pooled layer (fused.hip).
 bool fused_supported(const Geom& g);
+bool fused_preferred(const Geom& g);  // the default path for this geometry is the single launch
 hipError_t launch_fused(const Geom& g, const void* x, const void* z, const fastvim_params& p, const Workspace& ws,
                         void* out, hipStream_t st);
 hipError_t launch_zero_sync(const Workspace& ws, int64_t n, hipStream_t st);
+hipError_t launch_calib_copy(void* dst, const void* src, size_t bytes, hipStream_t st);
 
 // ------------------------------------------------------------ device helpers
 typedef float f32x4 __attribute__((ext_vector_type(4)));

@@ -44,7 +44,12 @@ namespace fastvim {
 namespace {
 
 constexpr int kFT = 512;                                     // threads per workgroup
-constexpr int kLdsFloats = (int)(sizeof(ScanSmem) / sizeof(float));
+// LDS of one workgroup: the larger of the scan's chunk buffer and the pooling
+// item's [G][E] partial sums + [RG][E] pooled tokens + [RG][KS][2 NX] partial
+// projections.  Two workgroups per CU (the register budget's limit) leave
+// room to spare at 40 KB.
+constexpr int kLdsFloats = 10240;
+static_assert(sizeof(ScanSmem) <= kLdsFloats * sizeof(float), "scan buffer fits");
 constexpr unsigned kSpinLimit = 1u << 20;                   // about a second of polling
 constexpr int kEU = 4;                                       // tokens per lane per batch (E items)
 constexpr int kMaxIv = 6;
@@ -348,8 +353,20 @@ bool plan(const Geom& g, FusedArgs* a) {
     a->nA = (int)((g.T + RG - 1) / RG);
     a->nS = (int)((g.E + kScanCh - 1) / kScanCh);
     a->nE = (int)((g.h + RE - 1) / RE);
-    a->LS = env_int("FASTVIM_FUSED_LS", 3);
-    a->LE = env_int("FASTVIM_FUSED_LE", 8);
+    // Lags.  Between the A items of image b (slot b) and its E items (slot
+    // b + LE) the pipeline reads LE other images' x with allocating loads;
+    // E items find x in the 256 MB Infinity Cache only while that stays
+    // within about 200 MB, so LE = 200 MB / x bytes per image (8 images at
+    // 2048^2 fp32, 16 in bf16: both measured best).  The scans start LS
+    // slots after pooling, enough for the image's A items to drain.  The
+    // environment variables override both (for lag sweeps).
+    const int64_t x_img = g.h * g.w * g.E * esz;
+    int64_t le = (200ll << 20) / x_img;
+    le = le < 1 ? 1 : (le > g.B ? g.B : le);
+    int64_t ls = le / 4 < 3 ? 3 : le / 4;
+    if (ls > le) ls = le;
+    a->LS = env_int("FASTVIM_FUSED_LS", (int)ls);
+    a->LE = env_int("FASTVIM_FUSED_LE", (int)le);
     if (a->LS < 1) a->LS = 1;
     if (a->LE < a->LS) a->LE = a->LS;
     // slots [0, B + LE): piecewise-constant item counts between the breakpoints
@@ -399,6 +416,15 @@ hipError_t fused_launch_io(const FusedArgs& a, hipStream_t st) {
 bool fused_supported(const Geom& g) {
     FusedArgs a;
     return plan(g, &a);
+}
+
+bool fused_preferred(const Geom& g) {
+    // The pipeline's fixed costs (scan latency per image, fill and drain)
+    // pay off once an image's x is several MB: measured faster than the stage
+    // kernels at 2048^2 (25 MB fp32, 12.6 MB bf16), slower at 1024^2 (6.3 MB)
+    // and below.
+    const int64_t esz = g.io == FASTVIM_BF16 ? 2 : 4;
+    return g.h * g.w * g.E * esz >= (8ll << 20) && fused_supported(g);
 }
 
 hipError_t launch_zero_sync(const Workspace& ws, int64_t n, hipStream_t st) {

@@ -32,7 +32,7 @@ def test_library_exports_every_declared_function():
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(Bd.EXPORTED_SYMBOLS)
-    assert lib.fastvim_abi_version() == 1
+    assert lib.fastvim_abi_version() == 2
 
 
 def test_status_strings():
@@ -148,6 +148,10 @@ def test_bad_enums():
     c = FakeCall()
     assert lib.fastvim_ssm_stage(5, c.x, c.z, ctypes.byref(c.params), ctypes.byref(c.dims), 0, None, c.out,
                                  None) == EARG
+    for flags in (P.FLAG_STAGED | P.FLAG_FUSED, 4, 1 << 31):  # conflicting or unknown flags
+        c = FakeCall()
+        c.params.flags = flags
+        expect(c, EARG)
 
 
 def test_alignment():
@@ -222,3 +226,17 @@ def test_export_bytes_masked(what):
     expect_n = {0: 3 * T * 16 * 4, 1: 3 * T * 2 * 36 * 4, 2: 3 * T * 16 * 4, 3: 3 * T * 16 * 4, 4: 3 * 7 * 4, 5: 12,
                 6: 4}
     assert n == expect_n[what]
+
+
+def test_calib_copy_validation():
+    """The calibration copy rejects bad arguments before launching anything."""
+    lib = P.lib()
+    a, b = 0x10000, 0x20000
+    assert lib.fastvim_calib_copy(None, None, 0, None) == OK  # nothing to do
+    assert lib.fastvim_calib_copy(None, b, 64, None) == ENULL
+    assert lib.fastvim_calib_copy(a, None, 64, None) == ENULL
+    assert lib.fastvim_calib_copy(a + 4, b, 64, None) == EALIGN
+    assert lib.fastvim_calib_copy(a, b + 8, 64, None) == EALIGN
+    assert lib.fastvim_calib_copy(a, b, 60, None) == EALIGN
+    assert lib.fastvim_calib_copy(a, a + 32, 64, None) == EOVERLAP
+    assert lib.fastvim_calib_copy(a + 32, a, 64, None) == EOVERLAP

@@ -29,8 +29,8 @@ from pooled_selective_state_amd.inputs import draw_workload, random_mask, round_
 pytestmark = pytest.mark.gpu
 
 AXES = (P.POOL_COLS, P.POOL_ROWS, P.POOL_NONE_ROWMAJOR, P.POOL_NONE_COLMAJOR)
-# dense pooled layers run as stage kernels by default; FLAG_FUSED runs them as one pipelined launch
-PATHS = {"staged": 0, "fused": P.FLAG_FUSED}
+# the two paths of a dense pooled layer, forced (by default the library picks by size)
+PATHS = {"staged": P.FLAG_STAGED, "fused": P.FLAG_FUSED}
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -226,7 +226,7 @@ def test_fused_matches_staged(axis):
     wl = draw_workload(C.CHAIN_1024, batch=6)
     x, z, prm = wl["x"], wl["z"][0], wl["params"][0]
     f = gpu_call(x, z, prm, axis, flags=P.FLAG_FUSED)
-    s = gpu_call(x, z, prm, axis)
+    s = gpu_call(x, z, prm, axis, flags=P.FLAG_STAGED)
     of, os_ = host(f.run()), host(s.run())
     torch.cuda.synchronize()
     status_ok(f)
@@ -302,3 +302,17 @@ def test_full_size_unpooled(cfg, axis):
     xd = host(call.export(P.EXPORT_XDBL)[sel])
     NX = ref["fwd"]["v"].shape[-1]
     check(xd[..., 0, :NX], ref["fwd"]["v"], FP32_TOL, "unpooled x_proj fwd")
+
+
+def test_default_path_selection():
+    """Without flags the library runs small dense layers as stage kernels and
+    layers with large images (>= 8 MiB of x each) as the single launch; both
+    paths are deterministic, so the default matches the chosen one bit for bit."""
+    small = draw_workload(C.SHORT_224_S, batch=8)
+    big = draw_workload(C.HIRES_2048, batch=2)
+    for wl, chosen in ((small, P.FLAG_STAGED), (big, P.FLAG_FUSED)):
+        x, z, prm = wl["x"], wl["z"][0], wl["params"][0]
+        d = gpu_call(x, z, prm, P.POOL_COLS).run().clone()
+        c = gpu_call(x, z, prm, P.POOL_COLS, flags=chosen).run().clone()
+        torch.cuda.synchronize()
+        assert torch.equal(d, c), chosen
