@@ -44,12 +44,11 @@ namespace fastvim {
 namespace {
 
 constexpr int kFT = 512;                                     // threads per workgroup
-// LDS of one workgroup: the larger of the scan's chunk buffer and the pooling
+// LDS of one workgroup: the scan's rows of a whole sequence, or the pooling
 // item's [G][E] partial sums + [RG][E] pooled tokens + [RG][KS][2 NX] partial
-// projections.  Two workgroups per CU (the register budget's limit) leave
-// room to spare at 40 KB.
-constexpr int kLdsFloats = 10240;
-static_assert(sizeof(ScanSmem) <= kLdsFloats * sizeof(float), "scan buffer fits");
+// projections.  48 KB lets three workgroups share a CU.
+constexpr int kLdsFloats = kScanLdsFloats;
+static_assert(sizeof(ScanSmem) == kLdsFloats * sizeof(float), "one buffer");
 constexpr unsigned kSpinLimit = 1u << 20;                   // about a second of polling
 constexpr int kEU = 4;                                       // tokens per lane per batch (E items)
 constexpr int kMaxIv = 6;
@@ -303,7 +302,7 @@ __global__ void __launch_bounds__(kFT) fused_layer_kernel(FusedArgs a) {
             __syncthreads();
             __builtin_amdgcn_s_setprio(2);  // the scan is on the critical path of its image
             ScanArgs sa{a.xdbl, a.pf, a.pb, a.s_f, a.s_b, a.T, a.E, a.R, a.NX};
-            scan_tile<RMAX, true>(sa, USrcPooled{a.u, a.T, a.E}, bs, (int64_t)r * kScanCh, sm.scan);
+            scan_tile_resident<RMAX, true>(sa, USrcPooled{a.u, a.T, a.E}, bs, (int64_t)r * kScanCh, sm.scan);
             __builtin_amdgcn_s_setprio(0);
             publish(&a.sync[2 + a.B + bs]);
             return;
@@ -326,6 +325,9 @@ int env_int(const char* name, int dflt) {
 // Item sizes and ticket layout for a geometry; false if not covered.
 bool plan(const Geom& g, FusedArgs* a) {
     if (!g.pooled || g.masked || g.B < 1) return false;
+    // the scan items hold a whole sequence's x_proj rows in LDS
+    const int64_t tmax = g.R <= 16 ? resident_tmax<16>() : g.R <= 32 ? resident_tmax<32>() : resident_tmax<64>();
+    if (g.T > tmax) return false;
     if (g.h * g.w * g.E >= ((int64_t)1 << 31)) return false;  // 32-bit offsets within an image
     const int V = g.io == FASTVIM_BF16 ? 8 : 4;
     const int64_t esz = g.io == FASTVIM_BF16 ? 2 : 4;

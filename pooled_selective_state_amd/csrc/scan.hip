@@ -10,10 +10,10 @@ namespace {
 
 template <int RMAX, class USrc>
 __global__ void __launch_bounds__(kScanThreads) scan_kernel(ScanArgs a, USrc usrc, int nEg) {
-    __shared__ ScanSmem sm;
+    __shared__ float xs[chunk_lds_floats<RMAX>()];
     const int64_t b = blockIdx.x / nEg;
     const int64_t e0 = (int64_t)(blockIdx.x % nEg) * kScanCh;
-    scan_tile<RMAX, false>(a, usrc, b, e0, sm);
+    scan_tile<RMAX, false>(a, usrc, b, e0, xs);
 }
 
 template <int RMAX, class USrc>

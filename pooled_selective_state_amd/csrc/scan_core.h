@@ -14,12 +14,16 @@
 // keeps the sequential critical path of a step to 4 exp2 and a two-step quad
 // reduction.  (Eight lanes per sequence, with a half-row mirror added to the
 // reduction, also works but measured slower: twice the workgroups, each with
-// the same chunk staging and step-size work.)  Time is walked in chunks of kChunk steps in traversal order
-// (ascending t forward, descending t backward).  For each chunk:
-//   1. its 2 * kChunk x_proj rows (low-rank step input, B_t, C_t of both
-//      directions), loaded into registers while the previous chunk was
-//      computing (16 lanes per row), go to LDS as they are;
-//   2. the loads of the next chunk are issued;
+// the same row staging and step-size work.)
+//
+// Time is walked in chunks of kChunk steps in traversal order (ascending t
+// forward, descending t backward).  The x_proj rows of the steps (low-rank
+// step input, B_t, C_t of both directions) sit in LDS, row stride RMAX + 32:
+// positions [0, RMAX) hold the low-rank input permuted so that the quarter
+// r = q + 4i of quad lane q is contiguous (position q * RMAX/4 + i, zero past
+// R), then B_t at [RMAX, RMAX + 16) and C_t at [RMAX + 16, RMAX + 32), so
+// every lane reads its operands as 16-byte vectors.  Every chunk runs two
+// phases:
 //   3. each quad computes every step's dt_proj dot product, each lane over
 //      its quarter of the (register-resident) dt_proj row, summed across the
 //      quad; the lane q of the quad that owns step s (s = q + 4j) keeps its
@@ -29,6 +33,18 @@
 //      from lane s mod 4 of the quad by a quad broadcast, B_t and C_t from LDS,
 //      and lane 0 of the sequence stores s_t.  Broadcasts and the reduction
 //      over the sequence's lanes are DPP lane moves, with no LDS round trip.
+// Two ways to fill the LDS rows:
+//   scan_tile           any length: one chunk of rows at a time, the next
+//                       chunk's rows loaded into registers while the current
+//                       one computes (one memory round trip per chunk);
+//   scan_tile_resident  T <= resident_tmax<RMAX>(): all rows and all token
+//                       values of the sequence loaded at once, before the
+//                       first chunk, so a sequence waits for memory once and
+//                       its chunk loop holds no loads (a load there would
+//                       also wait for the outputs stored so far, which share
+//                       its counter); the fused kernel's scans sit on the
+//                       critical path of their image while the memory system
+//                       is saturated by other work.
 #pragma once
 
 #include "fastvim_internal.h"
@@ -40,12 +56,32 @@ constexpr int kLps = 4;                            // lanes per (channel, direct
 constexpr int kNs = 16 / kLps;                     // states per lane
 constexpr int kScanCh = kScanThreads / 2 / kLps;   // channels per workgroup (64)
 static_assert(kLps == 4 || kLps == 8, "a sequence spans one quad or one half row");
+static_assert(kLps == 4, "the LDS row layout gives each lane 4 states as one vector");
 constexpr int kChunk = 16;      // steps per chunk
 constexpr int kJ = kChunk / 4;  // steps per lane in the step-size phase
 constexpr int kRMax = 64;       // largest dt rank
-constexpr int kNXMax = kRMax + 32;
-constexpr int kRowLanes = kScanThreads / (2 * kChunk);      // lanes per staged x_proj row (16)
-constexpr int kPre = (kNXMax + kRowLanes - 1) / kRowLanes;  // x_proj values prefetched per lane (6)
+constexpr int kRowLanes = kScanThreads / (2 * kChunk);  // lanes per staged x_proj row (16)
+constexpr int kScanLdsFloats = 12288;                   // 48 KB of rows
+
+// LDS row stride and the longest sequence whose rows fit at once.
+template <int RMAX>
+constexpr int row_stride_lds() { return RMAX + 32; }
+template <int RMAX>
+constexpr int resident_tmax() { return kScanLdsFloats / (2 * row_stride_lds<RMAX>()); }  // 128, 96, 64
+template <int RMAX>
+constexpr int row_loads() { return (row_stride_lds<RMAX>() + kRowLanes - 1) / kRowLanes; }  // per lane per row
+
+// Column of an x_proj row that feeds LDS position p of a staged row, or -1
+// for the zero padding of the low-rank part (see the layout above).
+template <int RMAX>
+__device__ __forceinline__ int lds_source_col(int p, int R) {
+    constexpr int kWQ = RMAX / 4;
+    if (p < RMAX) {
+        const int r = 4 * (p % kWQ) + p / kWQ;
+        return r < R ? r : -1;
+    }
+    return R + (p - RMAX);
+}
 
 // DPP quad permute: lane i of every quad of 4 takes the value of lane
 // ((CTRL >> 2*(i)) & 3) of its quad.
@@ -71,7 +107,7 @@ __device__ __forceinline__ float seq_sum(float v) {
 }
 
 struct alignas(16) ScanSmem {
-    float xs[2 * kChunk * kNXMax];  // the chunk's x_proj rows [dir][s][0, NX), row stride kNXMax
+    float xs[kScanLdsFloats];  // x_proj rows [dir][step][0, RMAX + 32), laid out as described above
 };
 
 // Source of the scanned token value u[b, t, e] (fp32 pooled tokens, or grid
@@ -102,65 +138,184 @@ struct ScanArgs {
     int R, NX;
 };
 
-// Scan channels [e0, e0 + kScanCh) of image b in both directions.  All 512 threads
-// of the workgroup must call it (it synchronises the workgroup).  With
-// WRITE_THROUGH the outputs are stored with agent-scope atomic stores (written
-// through to the device-coherent level), for consumers on other XCDs that
-// synchronise without an L2 write-back.  RMAX bounds the dt rank R.
-template <int RMAX, bool WRITE_THROUGH, class USrc>
-__device__ __forceinline__ void scan_tile(const ScanArgs& a, const USrc& usrc, int64_t b, int64_t e0,
-                                          ScanSmem& sm) {
-    const int tid = threadIdx.x;
-    const int dir = tid >> 8;
-    const int ch = (tid & 255) / kLps;
-    const int l = tid & (kLps - 1);  // lane within the sequence
-    const int q = tid & 3;           // lane within its quad
-    const int64_t e = e0 + ch;
-    const bool valid = e < a.E;
-    const int64_t ec = valid ? e : a.E - 1;
-    const fastvim_dir_params p = dir ? a.pb : a.pf;
-    const int R = a.R, NX = a.NX;
-    const int64_t T = a.T;
-    const int64_t row_stride = 2 * (int64_t)NX;
-    const float kLog2e = 1.4426950408889634f;
+// Per-lane state of one sequence: decay rates, the lane's states, its quarter
+// of the dt_proj row, the bias, and where its outputs go: quad lane q stores
+// the outputs of the steps q + 4j, at sq + (traversal step) * sstep.
+template <int RMAX>
+struct ScanLane {
+    static constexpr int kWQ = RMAX / 4;
+    int dir, l, q;
+    bool valid;
+    float A2[kNs], hs[kNs], wq[kWQ], bias;
+    float* sq;
+    int64_t sstep;
+};
 
-    float A2[kNs], hs[kNs];
+template <int RMAX>
+__device__ __forceinline__ void scan_lane_setup(const ScanArgs& a, int64_t b, int64_t e0, ScanLane<RMAX>& L,
+                                                int64_t& ec) {
+    static_assert(RMAX % 4 == 0 && RMAX <= kRMax, "dt rank bound");
+    const int tid = threadIdx.x;
+    L.dir = tid >> 8;
+    const int ch = (tid & 255) / kLps;
+    L.l = tid & (kLps - 1);
+    L.q = tid & 3;
+    const int64_t e = e0 + ch;
+    L.valid = e < a.E;
+    ec = L.valid ? e : a.E - 1;
+    const fastvim_dir_params p = L.dir ? a.pb : a.pf;
+    const int R = a.R;
+    const float kLog2e = 1.4426950408889634f;
 #pragma unroll
     for (int n = 0; n < kNs; ++n) {
-        A2[n] = -expf(p.A_log[ec * 16 + kNs * l + n]) * kLog2e;
-        hs[n] = 0.f;
+        L.A2[n] = -expf(p.A_log[ec * 16 + kNs * L.l + n]) * kLog2e;
+        L.hs[n] = 0.f;
     }
-    // this lane's quarter of the dt_proj row: r = q + 4i
-    static_assert(RMAX % 4 == 0 && RMAX <= kRMax, "dt rank bound");
-    constexpr int kWQ = RMAX / 4;
-    float wq[kWQ];
+    // this lane's quarter of the dt_proj row: r = q + 4i, zero past R (the
+    // step-size phase then reads every r < RMAX of a row unconditionally:
+    // still inside the row, whose stride is RMAX + 32)
 #pragma unroll
-    for (int i = 0; i < kWQ; ++i) {
-        const int r = q + 4 * i;
-        wq[i] = r < R ? p.dt_proj_w[ec * R + r] : 0.f;
+    for (int i = 0; i < ScanLane<RMAX>::kWQ; ++i) {
+        const int r = L.q + 4 * i;
+        L.wq[i] = r < R ? p.dt_proj_w[ec * R + r] : 0.f;
     }
-    const int nwq = (R + 3) / 4;
-    const float bias = p.dt_proj_b[ec];
-    const float* xb = a.xdbl + b * T * row_stride;
-    float* sdst = (dir ? a.s_b : a.s_f) + b * T * a.E + ec;
+    L.bias = p.dt_proj_b[ec];
+    // traversal step ti is t = ti forward, t = T - 1 - ti backward
+    L.sstep = L.dir ? -a.E : a.E;
+    L.sq = (L.dir ? a.s_b + (a.T - 1) * a.E : a.s_f) + b * a.T * a.E + ec + L.q * L.sstep;
+}
 
-    // Prefetch of one chunk into registers: lane tid loads columns
-    // o = tid % 16 + 16 i of x_proj row (d, s) = (tid / 256, tid / 16 % 16),
-    // and its own u values for the steps q + 4j.
+// Phases 3 and 4 of one chunk.  dr: this direction's LDS row of the chunk's
+// local step 0; ucur: token values of the lane's steps q + 4j; base:
+// traversal index of local step 0.
+template <int RMAX, bool WRITE_THROUGH>
+__device__ __forceinline__ void scan_chunk(const ScanArgs& a, ScanLane<RMAX>& L, const float* dr,
+                                           const float (&ucur)[kJ], int64_t base) {
+    constexpr int S = row_stride_lds<RMAX>();
+    const int64_t T = a.T;
+    float dl[kJ], du[kJ];
+    {
+        float qv[kJ];
+        const float* dq = dr + L.q * ScanLane<RMAX>::kWQ;
+        // one group of 4 steps per iteration; qv rotates so its indices stay constant
+#pragma unroll 1
+        for (int j = 0; j < kJ; ++j) {
+            float own = 0.f;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const float* row = dq + (4 * j + m) * S;
+                float pq = 0.f;
+#pragma unroll
+                for (int i = 0; i < ScanLane<RMAX>::kWQ; i += 4) {  // weights and inputs past R are zero
+                    const f32x4 d4 = *reinterpret_cast<const f32x4*>(row + i);
+                    pq = fmaf(L.wq[i], d4.x, pq);
+                    pq = fmaf(L.wq[i + 1], d4.y, pq);
+                    pq = fmaf(L.wq[i + 2], d4.z, pq);
+                    pq = fmaf(L.wq[i + 3], d4.w, pq);
+                }
+                pq = quad_sum(pq);
+                own = (m == L.q) ? pq : own;
+            }
+#pragma unroll
+            for (int t = 0; t + 1 < kJ; ++t) qv[t] = qv[t + 1];
+            qv[kJ - 1] = own + L.bias;
+        }
+#pragma unroll
+        for (int j = 0; j < kJ; ++j) {
+            const bool in = base + L.q + 4 * j < T;
+            const float d = qv[j] > 20.f ? qv[j] : log1pf(__expf(qv[j]));
+            dl[j] = in ? d : 0.f;
+            du[j] = in ? d * ucur[j] : 0.f;
+        }
+    }
+    // the recurrence, four steps (one per quad lane's step size) at a time;
+    // dl / du rotate so every register index stays constant
+    // B_t and C_t of the next step are read while the current one computes;
+    // the outputs of each group of 4 steps are stored one per quad lane
+    static_assert(kNs == 4, "one 16-byte vector of B_t and of C_t per lane");
+    const float* rows = dr + RMAX + kNs * L.l;
+    f32x4 bn = *reinterpret_cast<const f32x4*>(rows), cn = *reinterpret_cast<const f32x4*>(rows + 16);
+    float* sp = L.sq + base * L.sstep;
+#pragma unroll
+    for (int k = 0; k < kJ; ++k) {
+        float keep = 0.f;
+        const float dk = dl[0], uk = du[0];
+#pragma unroll
+        for (int j = 0; j + 1 < kJ; ++j) {
+            dl[j] = dl[j + 1];
+            du[j] = du[j + 1];
+        }
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int s = 4 * k + m;
+            const float dlt = m == 0 ? quad_bcast<0>(dk) : m == 1 ? quad_bcast<1>(dk)
+                            : m == 2 ? quad_bcast<2>(dk) : quad_bcast<3>(dk);
+            const float dus = m == 0 ? quad_bcast<0>(uk) : m == 1 ? quad_bcast<1>(uk)
+                            : m == 2 ? quad_bcast<2>(uk) : quad_bcast<3>(uk);
+            const f32x4 b4 = bn, c4 = cn;
+            if (s + 1 < kChunk) {
+                bn = *reinterpret_cast<const f32x4*>(rows + (s + 1) * S);
+                cn = *reinterpret_cast<const f32x4*>(rows + (s + 1) * S + 16);
+            }
+            const float bt[kNs] = {b4.x, b4.y, b4.z, b4.w}, ct[kNs] = {c4.x, c4.y, c4.z, c4.w};
+            float part = 0.f;
+#pragma unroll
+            for (int n = 0; n < kNs; ++n) {
+                const float dA = __builtin_amdgcn_exp2f(dlt * L.A2[n]);
+                L.hs[n] = fmaf(dA, L.hs[n], dus * bt[n]);
+                part = fmaf(ct[n], L.hs[n], part);
+            }
+            part = seq_sum(part);
+            keep = (m == L.q) ? part : keep;
+        }
+        if (L.valid && base + 4 * k + L.q < T) {
+            if (WRITE_THROUGH) __hip_atomic_store(sp, keep, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            else *sp = keep;
+        }
+        sp += 4 * L.sstep;
+    }
+}
+
+// Scan channels [e0, e0 + kScanCh) of image b in both directions, any T, with
+// chunk_lds_floats<RMAX>() floats of LDS at xs.  All 512 threads of the
+// workgroup must call it (it synchronises the workgroup).
+// With WRITE_THROUGH the outputs are stored with agent-scope atomic stores
+// (written through to the device-coherent level), for consumers on other XCDs
+// that synchronise without an L2 write-back.  RMAX bounds the dt rank R.
+template <int RMAX>
+constexpr int chunk_lds_floats() { return 2 * kChunk * row_stride_lds<RMAX>(); }
+
+template <int RMAX, bool WRITE_THROUGH, class USrc>
+__device__ __forceinline__ void scan_tile(const ScanArgs& a, const USrc& usrc, int64_t b, int64_t e0,
+                                          float* xs /* chunk_lds_floats<RMAX>() */) {
+    constexpr int S = row_stride_lds<RMAX>();
+    constexpr int kPre = row_loads<RMAX>();
+    ScanLane<RMAX> L;
+    int64_t ec;
+    scan_lane_setup<RMAX>(a, b, e0, L, ec);
+    const int tid = threadIdx.x;
+    const int NX = a.NX;
+    const int64_t T = a.T;
+    const int64_t row_stride = 2 * (int64_t)NX;
+    const float* xb = a.xdbl + b * T * row_stride;
+
+    // Prefetch of one chunk into registers: lane tid fills LDS positions
+    // p = tid % 16 + 16 i of x_proj row (d, s) = (tid / 256, tid / 16 % 16),
+    // and loads its own u values for the steps q + 4j.
     const int prow = tid / kRowLanes, pd = prow / kChunk, ps = prow % kChunk, po = tid % kRowLanes;
+    int scol[kPre];
+#pragma unroll
+    for (int i = 0; i < kPre; ++i) scol[i] = lds_source_col<RMAX>(po + kRowLanes * i, a.R);
     float pre_x[kPre], pre_u[kJ];
     auto prefetch = [&](int64_t base) {
         const int64_t ti = base + ps;
         const float* src = xb + (pd ? T - 1 - ti : ti) * row_stride + (int64_t)pd * NX;
 #pragma unroll
-        for (int i = 0; i < kPre; ++i) {
-            const int o = po + kRowLanes * i;
-            pre_x[i] = (ti < T && o < NX) ? src[o] : 0.f;
-        }
+        for (int i = 0; i < kPre; ++i) pre_x[i] = (ti < T && scol[i] >= 0) ? src[scol[i]] : 0.f;
 #pragma unroll
         for (int j = 0; j < kJ; ++j) {
-            const int64_t tj = base + q + 4 * j;
-            pre_u[j] = tj < T ? usrc(b, dir ? T - 1 - tj : tj, ec) : 0.f;
+            const int64_t tj = base + L.q + 4 * j;
+            pre_u[j] = tj < T ? usrc(b, L.dir ? T - 1 - tj : tj, ec) : 0.f;
         }
     };
 
@@ -168,84 +323,88 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, const USrc& usrc, i
     prefetch(0);
     for (int64_t c = 0; c < nchunks; ++c) {
         const int64_t base = c * kChunk;  // traversal index of local step 0
-        // 1. stage this chunk's x_proj rows
         __syncthreads();  // every lane is done reading the previous chunk's rows
 #pragma unroll
-        for (int i = 0; i < kPre; ++i) {
-            const int o = po + kRowLanes * i;
-            if (o < NX) sm.xs[prow * kNXMax + o] = pre_x[i];
-        }
+        for (int i = 0; i < kPre; ++i) xs[prow * S + po + kRowLanes * i] = pre_x[i];
         float ucur[kJ];
 #pragma unroll
         for (int j = 0; j < kJ; ++j) ucur[j] = pre_u[j];
         __syncthreads();
-        // 2. loads of the next chunk
         if (c + 1 < nchunks) prefetch(base + kChunk);
-        // 3. step sizes: quad-wide dot products, kept by the owning lane
-        float dl[kJ], du[kJ];
-        {
-            float qv[kJ];
-            const float* dr = sm.xs + dir * kChunk * kNXMax + q;
-            // one group of 4 steps per iteration; qv rotates so its indices stay constant
+        scan_chunk<RMAX, WRITE_THROUGH>(a, L, xs + L.dir * kChunk * S, ucur, base);
+    }
+}
+
+// The same for T <= resident_tmax<RMAX>(), with every x_proj row and every
+// token value of the sequence loaded at once.  Rows (t, d) are contiguous in
+// xdbl; lane tid fills LDS positions tid % 16 + 16 i of rows
+// r = tid / 16 + 32 p (r = 2t + d), stored at traversal step t (forward) or
+// T - 1 - t (backward).  Each lane holds the token values of its steps
+// q + 4j for the whole sequence (resident_tmax / 4 registers), rotated one
+// chunk at a time so register indices stay constant.  One barrier in all.
+template <int RMAX, bool WRITE_THROUGH, class USrc>
+__device__ __forceinline__ void scan_tile_resident(const ScanArgs& a, const USrc& usrc, int64_t b, int64_t e0,
+                                                   ScanSmem& sm) {
+    constexpr int S = row_stride_lds<RMAX>();
+    constexpr int TM = resident_tmax<RMAX>();
+    constexpr int kCM = TM / kChunk;                         // chunks at most: 8, 6, 4
+    constexpr int kPre = row_loads<RMAX>();
+    constexpr int kRowsPerPass = kScanThreads / kRowLanes;  // 32
+    constexpr int kPasses = 2 * TM / kRowsPerPass;          // 8, 6, 4
+    static_assert(2 * TM % kRowsPerPass == 0 && TM % kChunk == 0, "whole passes and chunks");
+    ScanLane<RMAX> L;
+    int64_t ec;
+    scan_lane_setup<RMAX>(a, b, e0, L, ec);
+    const int tid = threadIdx.x;
+    const int NX = a.NX;
+    const int64_t T = a.T;
+    const float* xb = a.xdbl + b * T * 2 * (int64_t)NX;
+    const int nrows = 2 * (int)T;
+    const int prow = tid / kRowLanes, po = tid % kRowLanes;
+    int scol[kPre];
+#pragma unroll
+    for (int i = 0; i < kPre; ++i) scol[i] = lds_source_col<RMAX>(po + kRowLanes * i, a.R);
+
+    float stage[kPasses][kPre];
+#pragma unroll
+    for (int p = 0; p < kPasses; ++p) {
+        const int r = prow + kRowsPerPass * p;
+#pragma unroll
+        for (int i = 0; i < kPre; ++i) stage[p][i] = (r < nrows && scol[i] >= 0) ? xb[r * NX + scol[i]] : 0.f;
+    }
+    float uall[kCM][kJ];
+#pragma unroll
+    for (int c = 0; c < kCM; ++c)
+#pragma unroll
+        for (int j = 0; j < kJ; ++j) {
+            const int64_t tj = (int64_t)c * kChunk + L.q + 4 * j;
+            uall[c][j] = tj < T ? usrc(b, L.dir ? T - 1 - tj : tj, ec) : 0.f;
+        }
+#pragma unroll
+    for (int p = 0; p < kPasses; ++p) {
+        const int r = prow + kRowsPerPass * p;
+        const int t = r >> 1, d = r & 1;
+        const int ti = d ? (int)T - 1 - t : t;
+        if (r < nrows) {
+            float* dst = sm.xs + (d * TM + ti) * S + po;
+#pragma unroll
+            for (int i = 0; i < kPre; ++i) dst[kRowLanes * i] = stage[p][i];
+        }
+    }
+    __syncthreads();
+
+    const int nchunks = (int)((T + kChunk - 1) / kChunk);
+    const float* dr = sm.xs + L.dir * TM * S;
 #pragma unroll 1
-            for (int j = 0; j < kJ; ++j) {
-                float own = 0.f;
+    for (int c = 0; c < nchunks; ++c) {
+        float ucur[kJ];
 #pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    const float* row = dr + (4 * j + m) * kNXMax;
-                    float pq = 0.f;
+        for (int j = 0; j < kJ; ++j) ucur[j] = uall[0][j];
 #pragma unroll
-                    for (int i = 0; i < kWQ; ++i)
-                        if (i < nwq) pq = fmaf(wq[i], row[4 * i], pq);
-                    pq = quad_sum(pq);
-                    own = (m == q) ? pq : own;
-                }
+        for (int k = 0; k + 1 < kCM; ++k)
 #pragma unroll
-                for (int t = 0; t + 1 < kJ; ++t) qv[t] = qv[t + 1];
-                qv[kJ - 1] = own + bias;
-            }
-#pragma unroll
-            for (int j = 0; j < kJ; ++j) {
-                const bool in = base + q + 4 * j < T;
-                const float d = qv[j] > 20.f ? qv[j] : log1pf(__expf(qv[j]));
-                dl[j] = in ? d : 0.f;
-                du[j] = in ? d * ucur[j] : 0.f;
-            }
-        }
-        // 4. the recurrence, four steps (one per quad lane's step size) at a
-        //    time; dl / du rotate so every register index stays constant
-        const float* rows = sm.xs + dir * kChunk * kNXMax + R + kNs * l;
-        for (int k = 0; k < kJ; ++k) {
-            const float dk = dl[0], uk = du[0];
-#pragma unroll
-            for (int j = 0; j + 1 < kJ; ++j) {
-                dl[j] = dl[j + 1];
-                du[j] = du[j + 1];
-            }
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const int s = 4 * k + m;
-                const float dlt = m == 0 ? quad_bcast<0>(dk) : m == 1 ? quad_bcast<1>(dk)
-                                : m == 2 ? quad_bcast<2>(dk) : quad_bcast<3>(dk);
-                const float dus = m == 0 ? quad_bcast<0>(uk) : m == 1 ? quad_bcast<1>(uk)
-                                : m == 2 ? quad_bcast<2>(uk) : quad_bcast<3>(uk);
-                const float* row = rows + s * kNXMax;
-                float part = 0.f;
-#pragma unroll
-                for (int n = 0; n < kNs; ++n) {
-                    const float dA = __builtin_amdgcn_exp2f(dlt * A2[n]);
-                    hs[n] = fmaf(dA, hs[n], dus * row[n]);
-                    part = fmaf(row[16 + n], hs[n], part);
-                }
-                part = seq_sum(part);
-                const int64_t ti = base + s;
-                if (l == 0 && valid && ti < T) {
-                    float* dst = sdst + (dir ? T - 1 - ti : ti) * a.E;
-                    if (WRITE_THROUGH) __hip_atomic_store(dst, part, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    else *dst = part;
-                }
-            }
-        }
+            for (int j = 0; j < kJ; ++j) uall[k][j] = uall[k + 1][j];
+        scan_chunk<RMAX, WRITE_THROUGH>(a, L, dr + c * kChunk * S, ucur, (int64_t)c * kChunk);
     }
 }
 
