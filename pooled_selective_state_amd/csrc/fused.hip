@@ -21,8 +21,9 @@
 //            pooled tokens (both directions); count it in rowsDone[b];
 //   S(b, k)  once rowsDone[b] == nA, scan channels [64k, 64k + 64) of image b
 //            in both directions (scan_core.h); count it in scanDone[b];
-//   E(b, k)  once scanDone[b] == nS, repeat + skip + gate grid rows
-//            [k*RE, k*RE + RE) of image b.
+//   E(b, k)  once scanDone[b] == nS, repeat + skip + gate a block of image
+//            b: grid rows [k*RE, k*RE + RE) (COLS), or RE rows x CJ columns
+//            with the block's scan rows staged in LDS (ROWS).
 // Items are numbered slot by slot, slot s = [A(s, *)] [S(s - LS, *)]
 // [E(s - LE, *)] with 1 <= LS <= LE (items outside [0, B) are left out), and
 // handed out through one atomic ticket counter.  A workgroup takes its ticket
@@ -65,7 +66,7 @@ struct FusedArgs {
     unsigned* sync;  // [0] ticket, [1] status, [2, 2+B) rowsDone, [2+B, 2+2B) scanDone
     int64_t B, h, w, E, T, P;
     int R, NX, axis;
-    int nA, nS, nE, RG, RE, G, VE, KS;
+    int nA, nS, nE, RG, RE, CJ, G, VE, KS;
     int LS, LE;
     int niv;                  // slot intervals with a constant number of items per slot
     int64_t iv_s0[kMaxIv];    // first slot of the interval
@@ -272,6 +273,101 @@ __device__ void item_epilogue(const FusedArgs& a, int64_t b, int k) {
     }
 }
 
+// ROWS: token (i, j) belongs to scan position j, so neighbouring tokens of a
+// grid row need different scan rows.  An item covers grid rows
+// [i0, i0 + RE) x columns [j0, j0 + CJ) of image b: it stages
+// s_fwd + s_bwd of its CJ columns in LDS once (CJ * E floats), then streams
+// the block's tokens (each row segment of the block is contiguous in memory)
+// in batches of kEU per lane, all loads of a batch issued first, walking the
+// block row by row without divisions.
+template <class IO>
+__device__ void item_epilogue_rows(const FusedArgs& a, int64_t b, int k, float* lds) {
+    constexpr int V = IO::V;
+    using elem = typename IO::elem;
+    using raw = typename IO::raw;
+    const int tid = threadIdx.x;
+    if (tid == 0) wait_at_least(&a.sync[2 + a.B + b], (unsigned)a.nS, &a.sync[1]);
+    __syncthreads();
+    const int64_t E = a.E, w = a.w;
+    const int nJB = (int)((w + a.CJ - 1) / a.CJ);
+    const int ib = k / nJB, jb = k - ib * nJB;
+    const int64_t i0 = (int64_t)ib * a.RE, j0 = (int64_t)jb * a.CJ;
+    const int ni = (int)(i0 + a.RE < a.h ? a.RE : a.h - i0);
+    const int nj = (int)(j0 + a.CJ < w ? a.CJ : w - j0);
+    const int iE = (int)E, iw = (int)w;
+    {
+        // all loads in flight at once: the rows come from beyond this XCD's L2
+        constexpr int kIt = kLdsFloats / (4 * kFT);
+        const float* s1 = a.s_f + (b * a.T + j0) * E;  // columns j0 .. are consecutive scan rows
+        const float* s2 = a.s_b + (b * a.T + j0) * E;
+        const int n = nj * iE;
+        f32x4 p1[kIt], p2[kIt];
+#pragma unroll
+        for (int it = 0; it < kIt; ++it) {
+            const int q = 4 * tid + 4 * kFT * it;
+            if (q < n) {
+                p1[it] = load_raw<false>(s1 + q);
+                p2[it] = load_raw<false>(s2 + q);
+            }
+        }
+#pragma unroll
+        for (int it = 0; it < kIt; ++it) {
+            const int q = 4 * tid + 4 * kFT * it;
+            if (q < n) *reinterpret_cast<f32x4*>(lds + q) = p1[it] + p2[it];
+        }
+    }
+    __syncthreads();
+    const int VE = a.VE, G = a.G;
+    const int c = tid % VE, g = tid / VE;
+    if (g >= G) return;
+    const int coff = c * V;
+    float dsum[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) dsum[v] = a.pf.D[coff + v] + a.pb.D[coff + v];
+    // wave-uniform block base, 32-bit token offsets (an image holds < 2^31 elements)
+    const int64_t base = (b * a.h + i0) * w * E + j0 * E;
+    const elem* xb = static_cast<const elem*>(a.x) + base;
+    const elem* zb = static_cast<const elem*>(a.z) + base;
+    elem* ob = static_cast<elem*>(a.out) + base;
+    int ii = g / nj, jj = g - (g / nj) * nj;  // this lane's next token of the block
+    while (ii < ni) {
+        int off[kEU], sj[kEU];
+        bool ok[kEU];
+        raw xv[kEU], zv[kEU];
+#pragma unroll
+        for (int m = 0; m < kEU; ++m) {
+            ok[m] = ii < ni;
+            off[m] = (ii * iw + jj) * iE + coff;
+            sj[m] = jj * iE + coff;
+            jj += G;
+            while (jj >= nj) {
+                jj -= nj;
+                ++ii;
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < kEU; ++m)
+            if (ok[m]) {
+                xv[m] = load_raw<true>(xb + off[m]);
+                zv[m] = load_raw<true>(zb + off[m]);
+            }
+#pragma unroll
+        for (int m = 0; m < kEU; ++m) {
+            if (!ok[m]) continue;
+            float o[V];
+#pragma unroll
+            for (int v = 0; v < V; v += 4) {
+                const f32x4 sv = *reinterpret_cast<const f32x4*>(lds + sj[m] + v);
+                o[v] = (sv.x + dsum[v] * raw_at(xv[m], v)) * silu(raw_at(zv[m], v));
+                o[v + 1] = (sv.y + dsum[v + 1] * raw_at(xv[m], v + 1)) * silu(raw_at(zv[m], v + 1));
+                o[v + 2] = (sv.z + dsum[v + 2] * raw_at(xv[m], v + 2)) * silu(raw_at(zv[m], v + 2));
+                o[v + 3] = (sv.w + dsum[v + 3] * raw_at(xv[m], v + 3)) * silu(raw_at(zv[m], v + 3));
+            }
+            store_vec<true>(ob + off[m], o);
+        }
+    }
+}
+
 // ---------------------------------------------------------------- kernel
 template <class IO, bool COLS, int RMAX>
 __global__ void __launch_bounds__(kFT) fused_layer_kernel(FusedArgs a) {
@@ -309,7 +405,8 @@ __global__ void __launch_bounds__(kFT) fused_layer_kernel(FusedArgs a) {
         }
         r -= a.nS;
     }
-    item_epilogue<IO, COLS>(a, slot - a.LE, (int)r);
+    if (COLS) item_epilogue<IO, true>(a, slot - a.LE, (int)r);
+    else item_epilogue_rows<IO>(a, slot - a.LE, (int)r, sm.buf);
 }
 
 __global__ void zero_sync_kernel(unsigned* sync, int64_t n) {
@@ -344,26 +441,36 @@ bool plan(const Geom& g, FusedArgs* a) {
     if (RG > g.T) RG = g.T;
     while (RG > 1 && G * g.E + RG * g.E + RG * NO * KS > kLdsFloats) --RG;
     if (G * g.E + RG * g.E + RG * NO * KS > kLdsFloats) return false;
-    // E items: about 200 KB of each stream.
-    const int64_t row_bytes = g.w * g.E * esz;
-    int64_t RE = (200 * 1024) / (row_bytes > 0 ? row_bytes : 1);
-    RE = RE < 1 ? 1 : RE;
-    if (RE > g.h) RE = g.h;
+    // E items: about 200 KB of each stream.  COLS: RE whole grid rows.  ROWS:
+    // RE rows x CJ columns, CJ as many columns as the LDS holds scan rows of.
+    int64_t RE, CJ;
+    if (g.axis == FASTVIM_POOL_COLS) {
+        const int64_t row_bytes = g.w * g.E * esz;
+        RE = (200 * 1024) / row_bytes;
+        CJ = g.w;
+    } else {
+        CJ = kLdsFloats / g.E;
+        if (CJ > 32) CJ = 32;
+        if (CJ > g.w) CJ = g.w;
+        if (CJ < 1) return false;
+        RE = (200 * 1024) / (CJ * g.E * esz);
+    }
+    RE = RE < 1 ? 1 : (RE > g.h ? g.h : RE);
     a->B = g.B; a->h = g.h; a->w = g.w; a->E = g.E; a->T = g.T; a->P = g.P;
     a->R = (int)g.R; a->NX = (int)g.NX; a->axis = g.axis;
-    a->VE = (int)VE; a->G = G; a->KS = KS; a->RG = (int)RG; a->RE = (int)RE;
+    a->VE = (int)VE; a->G = G; a->KS = KS; a->RG = (int)RG; a->RE = (int)RE; a->CJ = (int)CJ;
     a->nA = (int)((g.T + RG - 1) / RG);
     a->nS = (int)((g.E + kScanCh - 1) / kScanCh);
-    a->nE = (int)((g.h + RE - 1) / RE);
+    a->nE = (int)(((g.h + RE - 1) / RE) * ((g.w + CJ - 1) / CJ));
     // Lags.  Between the A items of image b (slot b) and its E items (slot
     // b + LE) the pipeline reads LE other images' x with allocating loads;
     // E items find x in the 256 MB Infinity Cache only while that stays
-    // within about 200 MB, so LE = 200 MB / x bytes per image (8 images at
-    // 2048^2 fp32, 16 in bf16: both measured best).  The scans start LS
-    // slots after pooling, enough for the image's A items to drain.  The
-    // environment variables override both (for lag sweeps).
+    // within about 180 MB, so LE = 180 MB / x bytes per image (7 images at
+    // 2048^2 fp32, 14 in bf16: measured best, 7-8 and 12-16).  The scans
+    // start LS slots after pooling, enough for the image's A items to drain.
+    // The environment variables override both (for lag sweeps).
     const int64_t x_img = g.h * g.w * g.E * esz;
-    int64_t le = (200ll << 20) / x_img;
+    int64_t le = (180ll << 20) / x_img;
     le = le < 1 ? 1 : (le > g.B ? g.B : le);
     int64_t ls = le / 4 < 3 ? 3 : le / 4;
     if (ls > le) ls = le;

@@ -126,6 +126,21 @@ def test_masked_small(axis, io, K):
                  idx=idx, hw=(h, w))
 
 
+@pytest.mark.parametrize("R", [1, 16, 17, 33, 64])
+@pytest.mark.parametrize("axis", (P.POOL_COLS, P.POOL_NONE_COLMAJOR))
+def test_projection_every_tile_count(R, axis):
+    """The matrix-core projection covers 2(R + 32) output columns in tiles of
+    16 (5 to 12 tiles for R = 1..64): every tile count's edge, a token count
+    that is not a multiple of 16 (3 x 5 x 7 grid) and an E whose tail is not a
+    multiple of the 16-wide k-step (E = 100)."""
+    rng = np.random.default_rng(40 + R)
+    B, h, w, E, N = 3, 5, 7, 100, 16
+    x = rng.standard_normal((B, h, w, E), dtype=np.float32)
+    z = rng.standard_normal((B, h, w, E), dtype=np.float32)
+    prm = {d: rand_dir(rng, E, N, R, scale=0.1) for d in ("fwd", "bwd")}
+    _layer_check(x, z, prm, axis, FP32_TOL, torch.float32, "proj R=%d" % R, flags=P.FLAG_STAGED)
+
+
 def test_masked_integer_sums_exact():
     """x[b, k, :] = k + 1: the pooled sums are small integers, exact in fp32,
     so u * P must equal them bit for bit."""
