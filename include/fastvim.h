@@ -61,7 +61,8 @@ typedef enum fastvim_status {
     FASTVIM_OK = 0,
     FASTVIM_ERR_NULL = -1,        /* a required pointer is NULL */
     FASTVIM_ERR_DIMS = -2,        /* a size is out of range or inconsistent */
-    FASTVIM_ERR_UNSUPPORTED = -3, /* valid shape this build does not run (N != 16, R > 64, E > 4096, E % vec) */
+    FASTVIM_ERR_UNSUPPORTED = -3, /* valid shape this build does not run (N != 16, R > 64, E > 4096, E % vec,
+                                     an image of 2^31 elements or more) */
     FASTVIM_ERR_ALIGN = -4,       /* x, z, out, x_proj_w not 16-byte aligned; workspace not 256-byte; others not 4-byte */
     FASTVIM_ERR_OVERLAP = -5,     /* out overlaps x or z, or the workspace overlaps an input or output */
     FASTVIM_ERR_WORKSPACE = -6,   /* workspace NULL or smaller than fastvim_ssm_workspace_bytes */

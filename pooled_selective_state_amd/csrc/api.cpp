@@ -37,7 +37,8 @@ int resolve_geom(const fastvim_dims* d, int axis, Geom* g) {
     if (d->N != 16 || d->R > kMaxR || d->E > kMaxE) return FASTVIM_ERR_UNSUPPORTED;
     if (d->E % (d->io_dtype == FASTVIM_F32 ? 4 : 8) != 0) return FASTVIM_ERR_UNSUPPORTED;
     if (masked && hw > kMaskedMaxCells) return FASTVIM_ERR_UNSUPPORTED;
-    if (!pooled && hw > INT32_MAX) return FASTVIM_ERR_UNSUPPORTED;
+    // kernels address within an image with 32-bit offsets
+    if (!mul_ok(hw, d->E, &tmp) || tmp > INT32_MAX) return FASTVIM_ERR_UNSUPPORTED;
     const int64_t tokens = masked ? d->K : hw;
     if (!mul_ok(d->B, tokens, &tmp) || !mul_ok(tmp, d->E, &tmp)) return FASTVIM_ERR_DIMS;
     g->B = d->B; g->h = d->h; g->w = d->w; g->E = d->E; g->N = d->N; g->R = d->R; g->K = d->K;
@@ -251,7 +252,7 @@ const char* fastvim_status_string(int status) {
         case FASTVIM_OK: return "ok";
         case FASTVIM_ERR_NULL: return "a required pointer is NULL";
         case FASTVIM_ERR_DIMS: return "a size is out of range or inconsistent";
-        case FASTVIM_ERR_UNSUPPORTED: return "shape not supported by this build (N != 16, R > 64, E > 4096 or E not a multiple of the vector width, masked grid > 16384 cells)";
+        case FASTVIM_ERR_UNSUPPORTED: return "shape not supported by this build (N != 16, R > 64, E > 4096 or E not a multiple of the vector width, h*w*E >= 2^31, masked grid > 16384 cells)";
         case FASTVIM_ERR_ALIGN: return "misaligned pointer (x, z, out, x_proj_w need 16 bytes, workspace 256, others 4)";
         case FASTVIM_ERR_OVERLAP: return "out overlaps x or z, or the workspace overlaps an input or output";
         case FASTVIM_ERR_WORKSPACE: return "workspace missing or smaller than fastvim_ssm_workspace_bytes";

@@ -39,9 +39,15 @@ hipError_t scan_dispatch(const USrc& usrc, const Geom& g, const fastvim_params& 
 hipError_t launch_scan(const Geom& g, const void* x, const fastvim_params& p, const Workspace& ws,
                        hipStream_t st) {
     if (g.pooled) return scan_dispatch(USrcPooled{ws.u, g.T, g.E}, g, p, ws, st);
-    if (g.io == FASTVIM_BF16)
-        return scan_dispatch(USrcGrid<uint16_t>{static_cast<const uint16_t*>(x), g.axis, g.h, g.w, g.E}, g, p, ws, st);
-    return scan_dispatch(USrcGrid<float>{static_cast<const float*>(x), g.axis, g.h, g.w, g.E}, g, p, ws, st);
+    const bool colmajor = g.axis == FASTVIM_POOL_NONE_COLMAJOR;
+    if (g.io == FASTVIM_BF16) {
+        const uint16_t* xb = static_cast<const uint16_t*>(x);
+        return colmajor ? scan_dispatch(USrcGrid<uint16_t, true>{xb, g.h, g.w, g.E}, g, p, ws, st)
+                        : scan_dispatch(USrcGrid<uint16_t, false>{xb, g.h, g.w, g.E}, g, p, ws, st);
+    }
+    const float* xf = static_cast<const float*>(x);
+    return colmajor ? scan_dispatch(USrcGrid<float, true>{xf, g.h, g.w, g.E}, g, p, ws, st)
+                    : scan_dispatch(USrcGrid<float, false>{xf, g.h, g.w, g.E}, g, p, ws, st);
 }
 
 }  // namespace fastvim

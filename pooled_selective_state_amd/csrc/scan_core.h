@@ -110,24 +110,50 @@ struct alignas(16) ScanSmem {
     float xs[kScanLdsFloats];  // x_proj rows [dir][step][0, RMAX + 32), laid out as described above
 };
 
-// Source of the scanned token value u[b, t, e] (fp32 pooled tokens, or grid
-// tokens of x in unpooled scan order).
+// Source of the scanned token values: image(b) gives an accessor of u[b, t, e]
+// with 32-bit offsets from the image's base (an image holds fewer than 2^31
+// elements): fp32 pooled tokens, or the grid tokens of x in unpooled scan
+// order (row-major t = i w + j, or column-major t = j h + i).
 struct USrcPooled {
     const float* u;
     int64_t T, E;
-    __device__ __forceinline__ float operator()(int64_t b, int64_t t, int64_t e) const {
-        return u[(b * T + t) * E + e];
-    }
+    struct Image {
+        const float* p;
+        int E;
+        __device__ __forceinline__ float operator()(int t, int e) const { return p[t * E + e]; }
+    };
+    __device__ __forceinline__ Image image(int64_t b) const { return Image{u + b * T * E, (int)E}; }
 };
-template <class Elem>
+template <class Elem, bool COLMAJOR>
 struct USrcGrid {
     const Elem* x;
-    int axis;
     int64_t h, w, E;
-    __device__ __forceinline__ float operator()(int64_t b, int64_t t, int64_t e) const {
-        return load_elem(x + (b * h * w + unpooled_token(axis, t, h, w)) * E + e);
+    struct Image {
+        const Elem* p;
+        int h, w, E;
+        __device__ __forceinline__ float operator()(int t, int e) const {
+            const int tok = COLMAJOR ? (t % h) * w + t / h : t;
+            return load_elem(p + (tok * E + e));
+        }
+    };
+    __device__ __forceinline__ Image image(int64_t b) const {
+        return Image{x + b * h * w * E, (int)h, (int)w, (int)E};
     }
 };
+
+// Step size softplus(q) = ln(1 + e^q) in fp32.  Above q = 20 it is q (the log
+// term is below half an ulp of q).  Below, log1p(y) with y = e^q by Kahan's
+// identity log1p(y) = ln(u) * y / (u - 1), u = 1 + y rounded (y itself when
+// u == 1), which keeps the relative error within a few ulp using the
+// hardware base-2 exp and log (D. Goldberg, "What every computer scientist
+// should know about floating-point arithmetic", 1991, Theorem 4).
+__device__ __forceinline__ float softplus_f(float q) {
+    const float kLog2e = 1.4426950408889634f, kLn2 = 0.6931471805599453f;
+    const float y = __builtin_amdgcn_exp2f(q * kLog2e);
+    const float u = 1.f + y;
+    const float l = u == 1.f ? y : __builtin_amdgcn_logf(u) * kLn2 * (y * __builtin_amdgcn_rcpf(u - 1.f));
+    return q > 20.f ? q : l;
+}
 
 struct ScanArgs {
     const float* xdbl;  // (B, T, 2, NX)
@@ -223,7 +249,7 @@ __device__ __forceinline__ void scan_chunk(const ScanArgs& a, ScanLane<RMAX>& L,
 #pragma unroll
         for (int j = 0; j < kJ; ++j) {
             const bool in = base + L.q + 4 * j < T;
-            const float d = qv[j] > 20.f ? qv[j] : log1pf(__expf(qv[j]));
+            const float d = softplus_f(qv[j]);
             dl[j] = in ? d : 0.f;
             du[j] = in ? d * ucur[j] : 0.f;
         }
@@ -296,8 +322,10 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, const USrc& usrc, i
     const int tid = threadIdx.x;
     const int NX = a.NX;
     const int64_t T = a.T;
-    const int64_t row_stride = 2 * (int64_t)NX;
-    const float* xb = a.xdbl + b * T * row_stride;
+    const int row_stride = 2 * NX;
+    const float* xb = a.xdbl + b * T * row_stride;  // this image's rows: 32-bit offsets below
+    const auto ui = usrc.image(b);
+    const int iT = (int)T, iec = (int)ec;
 
     // Prefetch of one chunk into registers: lane tid fills LDS positions
     // p = tid % 16 + 16 i of x_proj row (d, s) = (tid / 256, tid / 16 % 16),
@@ -307,22 +335,22 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, const USrc& usrc, i
 #pragma unroll
     for (int i = 0; i < kPre; ++i) scol[i] = lds_source_col<RMAX>(po + kRowLanes * i, a.R);
     float pre_x[kPre], pre_u[kJ];
-    auto prefetch = [&](int64_t base) {
-        const int64_t ti = base + ps;
-        const float* src = xb + (pd ? T - 1 - ti : ti) * row_stride + (int64_t)pd * NX;
+    auto prefetch = [&](int base) {
+        const int ti = base + ps;
+        const float* src = xb + ((pd ? iT - 1 - ti : ti) * row_stride + pd * NX);
 #pragma unroll
-        for (int i = 0; i < kPre; ++i) pre_x[i] = (ti < T && scol[i] >= 0) ? src[scol[i]] : 0.f;
+        for (int i = 0; i < kPre; ++i) pre_x[i] = (ti < iT && scol[i] >= 0) ? src[scol[i]] : 0.f;
 #pragma unroll
         for (int j = 0; j < kJ; ++j) {
-            const int64_t tj = base + L.q + 4 * j;
-            pre_u[j] = tj < T ? usrc(b, L.dir ? T - 1 - tj : tj, ec) : 0.f;
+            const int tj = base + L.q + 4 * j;
+            pre_u[j] = tj < iT ? ui(L.dir ? iT - 1 - tj : tj, iec) : 0.f;
         }
     };
 
-    const int64_t nchunks = (T + kChunk - 1) / kChunk;
+    const int nchunks = (iT + kChunk - 1) / kChunk;
     prefetch(0);
-    for (int64_t c = 0; c < nchunks; ++c) {
-        const int64_t base = c * kChunk;  // traversal index of local step 0
+    for (int c = 0; c < nchunks; ++c) {
+        const int base = c * kChunk;  // traversal index of local step 0
         __syncthreads();  // every lane is done reading the previous chunk's rows
 #pragma unroll
         for (int i = 0; i < kPre; ++i) xs[prow * S + po + kRowLanes * i] = pre_x[i];
@@ -373,12 +401,13 @@ __device__ __forceinline__ void scan_tile_resident(const ScanArgs& a, const USrc
         for (int i = 0; i < kPre; ++i) stage[p][i] = (r < nrows && scol[i] >= 0) ? xb[r * NX + scol[i]] : 0.f;
     }
     float uall[kCM][kJ];
+    const auto ui = usrc.image(b);
 #pragma unroll
     for (int c = 0; c < kCM; ++c)
 #pragma unroll
         for (int j = 0; j < kJ; ++j) {
-            const int64_t tj = (int64_t)c * kChunk + L.q + 4 * j;
-            uall[c][j] = tj < T ? usrc(b, L.dir ? T - 1 - tj : tj, ec) : 0.f;
+            const int tj = c * kChunk + L.q + 4 * j;
+            uall[c][j] = tj < T ? ui(L.dir ? (int)T - 1 - tj : tj, (int)ec) : 0.f;
         }
 #pragma unroll
     for (int p = 0; p < kPasses; ++p) {
