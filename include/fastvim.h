@@ -124,7 +124,11 @@ typedef struct fastvim_params {
  * runs).  FASTVIM_FLAG_STAGED runs every layer as its stage kernels;
  * FASTVIM_FLAG_FUSED runs every dense pooled layer as the single launch,
  * whatever its size.  Both paths give the same results within rounding.
- * Setting both bits is FASTVIM_ERR_ARG. */
+ * Setting both bits is FASTVIM_ERR_ARG.  The single launch pipelines images:
+ * an image's scans start LS images after its pooling and its outputs LE
+ * images after; both follow the image size, and the environment variables
+ * FASTVIM_FUSED_LS and FASTVIM_FUSED_LE (read at each call) override them,
+ * for measurement. */
 #define FASTVIM_FLAG_STAGED 1u
 #define FASTVIM_FLAG_FUSED 2u
 

@@ -44,53 +44,64 @@ proj_kernel(const Elem* __restrict__ src, int map_axis, int64_t M, int64_t T, in
     const int NO = 2 * NX;
     const int64_t m0 = (int64_t)blockIdx.x * 16;
 
-    const int64_t m = m0 + ri;
-    const Elem* rowp = nullptr;
-    if (m < M) {
-        int64_t tok = m;  // pooled tokens and row-major order: row m is token m
-        if (map_axis == FASTVIM_POOL_NONE_COLMAJOR) {
-            const int64_t b = m / T, t = m - b * T;
-            tok = b * h * w + unpooled_token(map_axis, t, h, w);
-        }
-        rowp = src + tok * E;
+    // Rows past M and columns past 2NX read a valid row instead (the last
+    // token, weight row 0): their outputs are never stored, so the loads need
+    // no per-lane guards.
+    const int64_t m = m0 + ri < M ? m0 + ri : M - 1;
+    int64_t tok = m;  // pooled tokens and row-major order: row m is token m
+    if (map_axis == FASTVIM_POOL_NONE_COLMAJOR) {
+        const int64_t b = m / T, t = m - b * T;
+        tok = b * h * w + unpooled_token(map_axis, t, h, w);
     }
+    const Elem* rowp = src + tok * E + 4 * kk;
     const float* wrow[CT];
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
         const int o = ct * 16 + ri;
-        wrow[ct] = o < NX ? Wf + (int64_t)o * E : (o < NO ? Wb + (int64_t)(o - NX) * E : nullptr);
+        wrow[ct] = (o < NX ? Wf + (int64_t)o * E : (o < NO ? Wb + (int64_t)(o - NX) * E : Wf)) + 4 * kk;
     }
 
     f32x4 acc[CT];
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // operands of the next step are loaded while the current step's MFMAs run
-    float a4[4], b4[CT][4];
-    auto load_step = [&](int64_t k0) {
-        const int64_t k = k0 + 4 * kk;  // E is a multiple of 4: a run is all in or all out
-        a4[0] = a4[1] = a4[2] = a4[3] = 0.f;
-        if (rowp && k < E) load4(rowp + k, a4);
+    auto load_step = [&](int k0, float (&av)[4], float (&bv)[CT][4]) {
+        load4(rowp + k0, av);
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) load4(wrow[ct] + k0, bv[ct]);
+    };
+    auto mfma_step = [&](const float (&av)[4], const float (&bv)[CT][4]) {
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[i], bv[ct][i], acc[ct], 0, 0, 0);
+    };
+    // Full 16-wide steps of this wave (k0 = 16 wv + 64 i, k0 + 16 <= E),
+    // double-buffered in two register sets: the next step's operands load
+    // while the current step's MFMAs run.
+    const int step = 16 * kPW;
+    const int Ef = (int)(E / 16) * 16;  // end of the full steps
+    float a0[4], b0[CT][4], a1[4], b1[CT][4];
+    int k0 = 16 * wv;
+    if (k0 < Ef) load_step(k0, a0, b0);
+    for (; k0 < Ef; k0 += 2 * step) {
+        const bool has1 = k0 + step < Ef;
+        if (has1) load_step(k0 + step, a1, b1);
+        mfma_step(a0, b0);
+        if (k0 + 2 * step < Ef) load_step(k0 + 2 * step, a0, b0);
+        if (has1) mfma_step(a1, b1);
+    }
+    // The tail of E (E % 16 != 0, a multiple of 4): one step with guarded
+    // loads, taken by the wave whose turn it is.
+    if (Ef < E && wv == (Ef / 16) % kPW) {
+        const bool in = Ef + 4 * kk < E;
+        a0[0] = a0[1] = a0[2] = a0[3] = 0.f;
+        if (in) load4(rowp + Ef, a0);
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
-            b4[ct][0] = b4[ct][1] = b4[ct][2] = b4[ct][3] = 0.f;
-            if (wrow[ct] && k < E) load4(wrow[ct] + k, b4[ct]);
+            b0[ct][0] = b0[ct][1] = b0[ct][2] = b0[ct][3] = 0.f;
+            if (in) load4(wrow[ct] + Ef, b0[ct]);
         }
-    };
-    int64_t k0 = 16 * wv;
-    load_step(k0);
-    for (; k0 < E; k0 += 16 * kPW) {
-        float a[4], b[CT][4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) a[i] = a4[i];
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) b[ct][i] = b4[ct][i];
-        if (k0 + 16 * kPW < E) load_step(k0 + 16 * kPW);
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) acc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], b[ct][i], acc[ct], 0, 0, 0);
+        mfma_step(a0, b0);
     }
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct)
@@ -110,13 +121,110 @@ proj_kernel(const Elem* __restrict__ src, int map_axis, int64_t M, int64_t T, in
     }
 }
 
+// Many tokens (unpooled layers): each wave owns RT 16-row tiles over all of
+// E, so every weight fragment it loads feeds RT tiles' MFMAs (the weights are
+// re-read from L2 once per 16 RT rows instead of once per 16) and no
+// cross-wave reduction is needed; a workgroup's kPW waves cover 16 RT kPW rows.
+// Same operand layout and out-of-range handling as proj_kernel.
+template <class Elem, int CT, int RT>
+__global__ void __launch_bounds__(64 * kPW)
+proj_rows_kernel(const Elem* __restrict__ src, int map_axis, int64_t M, int64_t T, int64_t h, int64_t w, int64_t E,
+                 const float* __restrict__ Wf, const float* __restrict__ Wb, int NX, float* __restrict__ xdbl) {
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int ri = lane & 15, kk = lane >> 4;
+    const int NO = 2 * NX;
+    const int64_t m0 = ((int64_t)blockIdx.x * kPW + wv) * 16 * RT;
+    if (m0 >= M) return;
+    const Elem* rowp[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        const int64_t m = m0 + rt * 16 + ri < M ? m0 + rt * 16 + ri : M - 1;
+        int64_t tok = m;
+        if (map_axis == FASTVIM_POOL_NONE_COLMAJOR) {
+            const int64_t b = m / T, t = m - b * T;
+            tok = b * h * w + unpooled_token(map_axis, t, h, w);
+        }
+        rowp[rt] = src + tok * E + 4 * kk;
+    }
+    const float* wrow[CT];
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+        const int o = ct * 16 + ri;
+        wrow[ct] = (o < NX ? Wf + (int64_t)o * E : (o < NO ? Wb + (int64_t)(o - NX) * E : Wf)) + 4 * kk;
+    }
+    f32x4 acc[RT][CT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) acc[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto load_step = [&](int k0, float (&av)[RT][4], float (&bv)[CT][4]) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) load4(rowp[rt] + k0, av[rt]);
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) load4(wrow[ct] + k0, bv[ct]);
+    };
+    auto mfma_step = [&](const float (&av)[RT][4], const float (&bv)[CT][4]) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[rt][i], bv[ct][i], acc[rt][ct], 0, 0, 0);
+    };
+    const int Ef = (int)(E / 16) * 16;
+    float a0[RT][4], b0[CT][4], a1[RT][4], b1[CT][4];
+    int k0 = 0;
+    if (k0 < Ef) load_step(k0, a0, b0);
+    for (; k0 < Ef; k0 += 32) {
+        const bool has1 = k0 + 16 < Ef;
+        if (has1) load_step(k0 + 16, a1, b1);
+        mfma_step(a0, b0);
+        if (k0 + 32 < Ef) load_step(k0 + 32, a0, b0);
+        if (has1) mfma_step(a1, b1);
+    }
+    if (Ef < E) {  // tail of E (a multiple of 4)
+        const bool in = Ef + 4 * kk < E;
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            a0[rt][0] = a0[rt][1] = a0[rt][2] = a0[rt][3] = 0.f;
+            if (in) load4(rowp[rt] + Ef, a0[rt]);
+        }
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+            b0[ct][0] = b0[ct][1] = b0[ct][2] = b0[ct][3] = 0.f;
+            if (in) load4(wrow[ct] + Ef, b0[ct]);
+        }
+        mfma_step(a0, b0);
+    }
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int64_t mm = m0 + rt * 16 + 4 * kk + r;
+                const int o = ct * 16 + ri;
+                if (mm < M && o < NO) xdbl[mm * NO + o] = acc[rt][ct][r];
+            }
+}
+
+constexpr int kRowsRT = 2;                       // row tiles per wave in proj_rows_kernel
+constexpr int64_t kRowsMinTokens = 64 * 1024;    // token count from which it is used
+
 template <class Elem, int CT>
 hipError_t proj_launch(const Elem* src, int map_axis, const Geom& g, const fastvim_params& p, const Workspace& ws,
                        hipStream_t st) {
     const int64_t M = g.B * g.T;
-    const unsigned blocks = (unsigned)((M + 15) / 16);
-    hipLaunchKernelGGL((proj_kernel<Elem, CT>), dim3(blocks), dim3(64 * kPW), 0, st, src, map_axis, M, g.T, g.h,
-                       g.w, g.E, p.fwd.x_proj_w, p.bwd.x_proj_w, (int)g.NX, ws.xdbl);
+    if (M >= kRowsMinTokens) {
+        const int64_t rows = 16 * kRowsRT * kPW;
+        hipLaunchKernelGGL((proj_rows_kernel<Elem, CT, kRowsRT>), dim3((unsigned)((M + rows - 1) / rows)),
+                           dim3(64 * kPW), 0, st, src, map_axis, M, g.T, g.h, g.w, g.E, p.fwd.x_proj_w,
+                           p.bwd.x_proj_w, (int)g.NX, ws.xdbl);
+    } else {
+        hipLaunchKernelGGL((proj_kernel<Elem, CT>), dim3((unsigned)((M + 15) / 16)), dim3(64 * kPW), 0, st, src,
+                           map_axis, M, g.T, g.h, g.w, g.E, p.fwd.x_proj_w, p.bwd.x_proj_w, (int)g.NX, ws.xdbl);
+    }
     return hipGetLastError();
 }
 

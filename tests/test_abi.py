@@ -135,6 +135,7 @@ def test_unsupported():
     expect(FakeCall(E=18), EUNSUP)  # fp32 needs E % 4 == 0
     expect(FakeCall(E=20, io=P.BF16), EUNSUP)  # bf16 needs E % 8 == 0
     expect(FakeCall(h=200, w=100, K=5), EUNSUP)  # masked grid > 16384 cells
+    expect(FakeCall(B=1, h=1 << 14, w=1 << 14, E=8), EUNSUP)  # an image of 2^31 elements
 
 
 def test_bad_enums():

@@ -141,6 +141,46 @@ def test_projection_every_tile_count(R, axis):
     _layer_check(x, z, prm, axis, FP32_TOL, torch.float32, "proj R=%d" % R, flags=P.FLAG_STAGED)
 
 
+@pytest.mark.parametrize("path", list(PATHS))
+def test_step_size_extremes(path):
+    """Step-size biases spread over [-25, 25] with tiny dt_proj weights drive
+    softplus through all of its regimes: the identity above 20, e^q itself
+    where 1 + e^q rounds to 1, and the log1p range between."""
+    rng = np.random.default_rng(50)
+    B, h, w, E, N, R = 2, 9, 6, 96, 16, 8
+    x = rng.standard_normal((B, h, w, E), dtype=np.float32)
+    z = rng.standard_normal((B, h, w, E), dtype=np.float32)
+    prm = {}
+    for d in ("fwd", "bwd"):
+        p = rand_dir(rng, E, N, R, scale=0.05)
+        p["dt_proj_w"] = (1e-3 * rng.standard_normal((E, R))).astype(np.float32)
+        p["dt_proj_b"] = np.linspace(-25.0, 25.0, E).astype(np.float32)
+        prm[d] = p
+    _layer_check(x, z, prm, P.POOL_COLS, FP32_TOL, torch.float32, "softplus extremes", flags=PATHS[path])
+
+
+@pytest.mark.parametrize("R", [1, 33, 64])
+@pytest.mark.parametrize("axis", (P.POOL_NONE_ROWMAJOR, P.POOL_NONE_COLMAJOR))
+def test_projection_many_tokens(R, axis):
+    """From 64 k tokens the projection switches to row-tiled waves over the
+    whole of E: 256 x 257 tokens (not a multiple of the 128-row workgroup)
+    with E = 100 (an E tail), compared with the oracle's x_proj of the
+    tokens in scan order."""
+    rng = np.random.default_rng(60 + R)
+    B, h, w, E, N = 1, 256, 257, 100, 16
+    x = rng.standard_normal((B, h, w, E), dtype=np.float32)
+    z = rng.standard_normal((B, h, w, E), dtype=np.float32)
+    prm = {d: rand_dir(rng, E, N, R, scale=0.1) for d in ("fwd", "bwd")}
+    call = gpu_call(x, z, prm, axis, flags=P.FLAG_STAGED)
+    call.stage(P.STAGE_PROJ)
+    got = host(call.export(P.EXPORT_XDBL))
+    torch.cuda.synchronize()
+    seq = x if axis == P.POOL_NONE_ROWMAJOR else x.transpose(0, 2, 1, 3)
+    seq = np.ascontiguousarray(seq).reshape(B, h * w, E)
+    for d, name in enumerate(("fwd", "bwd")):
+        check(got[:, :, d, :], oracle.xproj(seq, prm[name]["x_proj_w"]), FP32_TOL, "x_proj %s R=%d" % (name, R))
+
+
 def test_masked_integer_sums_exact():
     """x[b, k, :] = k + 1: the pooled sums are small integers, exact in fp32,
     so u * P must equal them bit for bit."""
