@@ -84,6 +84,7 @@ class Oracle:
             vp, vp, ctypes.POINTER(_Dir), ctypes.POINTER(_Dir),
             i64, i64, i64, i64, i64, i64, i64, ci, vp,
             vp, vp, vp, ctypes.POINTER(_DirOut), ctypes.POINTER(_DirOut),
+            vp, vp, ctypes.c_double,
         ]
         lib.fvo_layer.restype = ci
         self._lib = lib
@@ -159,12 +160,18 @@ class Oracle:
                            1 if reverse else 0, _ptr(rs), _ptr(s))
         return s
 
-    def layer(self, x, z, fwd, bwd, axis, idx=None, hw=None, stages=False):
+    def layer(self, x, z, fwd, bwd, axis, idx=None, hw=None, stages=False, ln=None):
         """Full layer.  Dense: x, z (B,h,w,E).  Masked: x, z (B,K,E), idx (B,K),
         hw=(h, w).  fwd / bwd: dicts with x_proj_w, dt_proj_w, dt_proj_b, A_log, D.
+        ln: None, or {"weight": (E,), "bias": (E,), "eps": float} for the
+        post-SSM LayerNorm before the gate.
         Returns out (fp64), or with stages=True a dict of out, u, rows and the
         per-direction v, delta, s."""
         x, z = _f32(x), _f32(z)
+        ln_w = ln_b = None
+        ln_eps = 0.0
+        if ln is not None:
+            ln_w, ln_b, ln_eps = _f32(ln["weight"]), _f32(ln["bias"]), float(ln["eps"])
         keep = []
         pf, pb = _dir_struct(fwd, keep), _dir_struct(bwd, keep)
         NX, E = keep[0].shape
@@ -201,6 +208,7 @@ class Oracle:
             _ptr(out), _ptr(u), _ptr(rows),
             ctypes.byref(fo) if fo is not None else None,
             ctypes.byref(bo) if bo is not None else None,
+            _ptr(ln_w), _ptr(ln_b), ln_eps,
         )
         if rc:
             raise ValueError("fvo_layer failed: %d" % rc)
@@ -258,5 +266,5 @@ def scan(u, dlt, v, A_log, R, reverse=False, reset=None):
     return get().scan(u, dlt, v, A_log, R, reverse=reverse, reset=reset)
 
 
-def layer(x, z, fwd, bwd, axis, idx=None, hw=None, stages=False):
-    return get().layer(x, z, fwd, bwd, axis, idx=idx, hw=hw, stages=stages)
+def layer(x, z, fwd, bwd, axis, idx=None, hw=None, stages=False, ln=None):
+    return get().layer(x, z, fwd, bwd, axis, idx=idx, hw=hw, stages=stages, ln=ln)

@@ -30,6 +30,9 @@
  *   - the skip D*x is added after the repeat, on the full-resolution x, with
  *     one D per direction (the layer adds (D_fwd + D_bwd) * x);
  *   - the two directions are summed, then gated by silu(z);
+ *   - optionally a post-SSM LayerNorm over the channels of each token sits
+ *     between the skip and the gate (population variance, eps inside the
+ *     root, per-channel scale and shift);
  *   - initial state is zero; no state is output.
  *
  * Layouts (all row-major, last index fastest):
@@ -285,9 +288,47 @@ static int run_direction(const double *u, int64_t B, int64_t T, int64_t E, int64
  * -9 out of memory.  Optional stage outputs: u_out (B,T,E), rows_out (B,K),
  * fwd / bwd (v, delta, s).
  */
+/*
+ * Output of one token (channels e < E): the repeated scan outputs of its scan
+ * position plus the skip,
+ *   y[e] = s_fwd[e] + s_bwd[e] + (D_fwd[e] + D_bwd[e]) x[e]
+ * (FastVim summary, 方法详解 bullet 5: repeat, then the skip connection; Vim
+ * article 2.1: the two directions summed), optionally the post-SSM LayerNorm
+ * over the channels (FastVim summary, 方法详解 bullet 5, which puts a
+ * LayerNorm after the skip connection; Pith review: the post-SSM LayerNorm
+ * taken from VMamba, applied to the SSM output before the gate),
+ *   y[e] <- (y[e] - mean) / sqrt(var + eps) * ln_w[e] + ln_b[e],
+ *   mean = sum_e y[e] / E,  var = sum_e (y[e] - mean)^2 / E,
+ * and finally the gate, out[e] = y[e] * silu(z[e]).  y is caller scratch.
+ */
+static void output_token(const double *sf, const double *sb, const float *x, const float *z, const fvo_dir *pf,
+                         const fvo_dir *pb, int64_t E, const float *ln_w, const float *ln_b, double ln_eps,
+                         double *y, double *out)
+{
+    for (int64_t e = 0; e < E; ++e) {
+        const double skip = ((double)pf->D[e] + (double)pb->D[e]) * (double)x[e];
+        y[e] = sf[e] + sb[e] + skip;
+    }
+    if (ln_w) {
+        double mean = 0.0, var = 0.0;
+        for (int64_t e = 0; e < E; ++e) mean += y[e];
+        mean /= (double)E;
+        for (int64_t e = 0; e < E; ++e) {
+            const double d = y[e] - mean;
+            var += d * d;
+        }
+        var /= (double)E;
+        const double r = 1.0 / sqrt(var + ln_eps);
+        for (int64_t e = 0; e < E; ++e) y[e] = (y[e] - mean) * r * (double)ln_w[e] + (double)ln_b[e];
+    }
+    for (int64_t e = 0; e < E; ++e) out[e] = y[e] * silu((double)z[e]);
+}
+
+/* ln_w == NULL: no post-SSM LayerNorm. */
 int fvo_layer(const float *x, const float *z, const fvo_dir *pf, const fvo_dir *pb, int64_t B, int64_t h,
               int64_t w, int64_t E, int64_t N, int64_t R, int64_t K, int axis, const int32_t *idx,
-              double *out, double *u_out, int32_t *rows_out, fvo_dir_out *fwd, fvo_dir_out *bwd)
+              double *out, double *u_out, int32_t *rows_out, fvo_dir_out *fwd, fvo_dir_out *bwd,
+              const float *ln_w, const float *ln_b, double ln_eps)
 {
     int64_t T, P;
     const int masked = idx != NULL;
@@ -319,27 +360,27 @@ int fvo_layer(const float *x, const float *z, const fvo_dir *pf, const fvo_dir *
 
     if (masked) {
 #pragma omp parallel for schedule(static)
-        for (int64_t b = 0; b < B; ++b)
-            for (int64_t k = 0; k < K; ++k) {
-                const int64_t t = rows[b * K + k];
-                for (int64_t e = 0; e < E; ++e) {
-                    const int64_t c = (b * K + k) * E + e;
-                    const double skip = ((double)pf->D[e] + (double)pb->D[e]) * (double)x[c];
-                    out[c] = (sf[(b * T + t) * E + e] + sb[(b * T + t) * E + e] + skip) * silu((double)z[c]);
-                }
+        for (int64_t b = 0; b < B; ++b) {
+            double *y = (double *)malloc((size_t)E * sizeof(double));
+            for (int64_t k = 0; y && k < K; ++k) {
+                const int64_t t = rows[b * K + k], c = (b * K + k) * E;
+                output_token(sf + (b * T + t) * E, sb + (b * T + t) * E, x + c, z + c, pf, pb, E, ln_w, ln_b,
+                             ln_eps, y, out + c);
             }
+            free(y);
+        }
     } else {
 #pragma omp parallel for schedule(static)
-        for (int64_t b = 0; b < B; ++b)
-            for (int64_t i = 0; i < h; ++i)
+        for (int64_t b = 0; b < B; ++b) {
+            double *y = (double *)malloc((size_t)E * sizeof(double));
+            for (int64_t i = 0; y && i < h; ++i)
                 for (int64_t j = 0; j < w; ++j) {
-                    const int64_t t = seq_pos(axis, h, w, i, j);
-                    for (int64_t e = 0; e < E; ++e) {
-                        const int64_t c = ((b * h + i) * w + j) * E + e;
-                        const double skip = ((double)pf->D[e] + (double)pb->D[e]) * (double)x[c];
-                        out[c] = (sf[(b * T + t) * E + e] + sb[(b * T + t) * E + e] + skip) * silu((double)z[c]);
-                    }
+                    const int64_t t = seq_pos(axis, h, w, i, j), c = ((b * h + i) * w + j) * E;
+                    output_token(sf + (b * T + t) * E, sb + (b * T + t) * E, x + c, z + c, pf, pb, E, ln_w, ln_b,
+                                 ln_eps, y, out + c);
                 }
+            free(y);
+        }
     }
 
 done:

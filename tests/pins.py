@@ -346,10 +346,13 @@ def pin_all_kept(O):
     xf, zf = x.reshape(B_, h * w, E), z.reshape(B_, h * w, E)
     xm = np.stack([xf[b, idx[b]] for b in range(B_)])
     zm = np.stack([zf[b, idx[b]] for b in range(B_)])
+    ln = rand_ln(rng, E)
     for axis in (COLS, ROWS):
-        dense = O.layer(x, z, pf, pb, axis).reshape(B_, h * w, E)
-        masked = O.layer(xm, zm, pf, pb, axis, idx=idx, hw=(h, w))
-        _close(masked, np.stack([dense[b, idx[b]] for b in range(B_)]), what="all kept axis %d" % axis)
+        for norm in (None, ln):
+            dense = O.layer(x, z, pf, pb, axis, ln=norm).reshape(B_, h * w, E)
+            masked = O.layer(xm, zm, pf, pb, axis, idx=idx, hw=(h, w), ln=norm)
+            _close(masked, np.stack([dense[b, idx[b]] for b in range(B_)]),
+                   what="all kept axis %d%s" % (axis, " with LayerNorm" if norm else ""))
 
 
 def pin_zero_projection(O):
@@ -429,6 +432,70 @@ def pin_mask_rows_exact(O):
         raise AssertionError("invalid mask index %s accepted" % (bad,))
 
 
+def rand_ln(rng, E, eps=1e-5):
+    """Post-SSM LayerNorm parameters with every entry distinct."""
+    return {"weight": rng.uniform(0.5, 1.5, E).astype(np.float32),
+            "bias": rng.uniform(-0.5, 0.5, E).astype(np.float32), "eps": eps}
+
+
+def _ln_case(rng, B_=2, h=5, w=4, E=7, N=4, R=3):
+    pf, pb = rand_dir(rng, E, N, R), rand_dir(rng, E, N, R)
+    x = rng.standard_normal((B_, h, w, E)).astype(np.float32)
+    # the gate bounded away from zero, so the pre-gate value can be recovered
+    z = (1.0 + np.abs(rng.standard_normal((B_, h, w, E)))).astype(np.float32)
+    return pf, pb, x, z
+
+
+def pin_layernorm_moments(O):
+    """With unit scale and zero shift, every token's normalised output (the
+    output divided by the gate) has mean 0 and mean square var / (var + eps),
+    var being the variance of the same token's output without the norm."""
+    rng = np.random.default_rng(25)
+    pf, pb, x, z = _ln_case(rng)
+    E = x.shape[-1]
+    eps = 0.25  # large enough that a misplaced eps shows
+    ln = {"weight": np.ones(E, np.float32), "bias": np.zeros(E, np.float32), "eps": eps}
+    for axis in (COLS, ROWS, NONE_ROWMAJOR):
+        g = silu(z)
+        y = O.layer(x, z, pf, pb, axis) / g
+        yn = O.layer(x, z, pf, pb, axis, ln=ln) / g
+        var = y.var(axis=-1)
+        assert float(np.abs(yn.mean(axis=-1)).max()) <= 1e-12, "LayerNorm mean not zero"
+        _close((yn ** 2).mean(axis=-1), var / (var + eps), what="LayerNorm mean square")
+
+
+def pin_layernorm_affine(O):
+    """The norm's shift enters linearly and only through the gate:
+    out(w, b) - out(w, 0) = b * silu(z); its scale multiplies the output."""
+    rng = np.random.default_rng(26)
+    pf, pb, x, z = _ln_case(rng)
+    E = x.shape[-1]
+    ln = rand_ln(rng, E)
+    ln0 = dict(ln, bias=np.zeros(E, np.float32))
+    ln2 = dict(ln0, weight=(2.0 * ln["weight"]).astype(np.float32))
+    for axis in (COLS, ROWS):
+        o1 = O.layer(x, z, pf, pb, axis, ln=ln)
+        o0 = O.layer(x, z, pf, pb, axis, ln=ln0)
+        o2 = O.layer(x, z, pf, pb, axis, ln=ln2)
+        _close(o1 - o0, np.broadcast_to(ln["bias"].astype(np.float64), x.shape) * silu(z), what="LayerNorm shift")
+        _close(o2, 2.0 * o0, what="LayerNorm scale")
+
+
+def pin_layernorm_library(O):
+    """The normalised output equals numpy's mean / var normalisation of the
+    un-normalised output, scaled and shifted, then gated."""
+    rng = np.random.default_rng(27)
+    pf, pb, x, z = _ln_case(rng, E=9)
+    E = x.shape[-1]
+    ln = rand_ln(rng, E, eps=0.1)
+    for axis in (COLS, NONE_COLMAJOR):
+        g = silu(z)
+        y = O.layer(x, z, pf, pb, axis) / g
+        ref = ((y - y.mean(-1, keepdims=True)) / np.sqrt(y.var(-1, keepdims=True) + ln["eps"])
+               * ln["weight"].astype(np.float64) + ln["bias"].astype(np.float64)) * g
+        _close(O.layer(x, z, pf, pb, axis, ln=ln), ref, tol=1e-11, what="LayerNorm vs numpy")
+
+
 ALL_PINS = [
     pin_golden_worked_example,
     pin_geometric_series,
@@ -445,4 +512,7 @@ ALL_PINS = [
     pin_linear_in_D,
     pin_library_routines,
     pin_mask_rows_exact,
+    pin_layernorm_moments,
+    pin_layernorm_affine,
+    pin_layernorm_library,
 ]

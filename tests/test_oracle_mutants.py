@@ -35,7 +35,7 @@ MUTANTS = [
      "    }\n    return 0;\n}\n\n/*\n * Masked rows.", 1),
     ("masked pool normalised by E", "            for (int64_t e = 0; e < E; ++e) ub[t * E + e] += (double)xv[e];\n        }\n        for (int64_t k = 0; k < T * E; ++k) ub[k] /= (double)P;",
      "            for (int64_t e = 0; e < E; ++e) ub[t * E + e] += (double)xv[e];\n        }\n        for (int64_t k = 0; k < T * E; ++k) ub[k] /= (double)K;", 1),
-    ("only the forward D in the skip", "((double)pf->D[e] + (double)pb->D[e])", "((double)pf->D[e])", 2),
+    ("only the forward D in the skip", "((double)pf->D[e] + (double)pb->D[e])", "((double)pf->D[e])", 1),
     ("gate uses sigmoid(-z)", "return q / (1.0 + exp(-q));", "return q / (1.0 + exp(q));", 1),
     ("softplus without log", "log1p(exp(-fabs(q)))", "exp(-fabs(q))", 1),
     ("dt_proj transposed", "dt_proj_w[e * R + r]", "dt_proj_w[r * E + e]", 1),
@@ -45,8 +45,13 @@ MUTANTS = [
     ("masked ROWS uses the row", "q / w : q % w", "q / w : q / w", 1),
     ("bias dropped from delta", "double q = (double)dt_proj_b[e];", "double q = 0.0;", 1),
     ("low-rank delta reads B", "dt_proj_w[e * R + r] * v[m * NX + r]", "dt_proj_w[e * R + r] * v[m * NX + R + r]", 1),
-    ("repeat uses the wrong direction sum", "out[c] = (sf[(b * T + t) * E + e] + sb[(b * T + t) * E + e] + skip)",
-     "out[c] = (sf[(b * T + t) * E + e] + sf[(b * T + t) * E + e] + skip)", 2),
+    ("repeat uses the wrong direction sum", "y[e] = sf[e] + sb[e] + skip;", "y[e] = sf[e] + sf[e] + skip;", 1),
+    ("repeat reads the wrong scan row", "output_token(sf + (b * T + t) * E, sb + (b * T + t) * E, x + c",
+     "output_token(sf + (b * T + t / 2) * E, sb + (b * T + t / 2) * E, x + c", 2),
+    ("LayerNorm with the unbiased variance", "var /= (double)E;", "var /= (double)(E - 1);", 1),
+    ("LayerNorm eps outside the root", "1.0 / sqrt(var + ln_eps)", "1.0 / (sqrt(var) + ln_eps)", 1),
+    ("LayerNorm without centring", "y[e] = (y[e] - mean) * r", "y[e] = y[e] * r", 1),
+    ("LayerNorm scale and shift swapped", "* (double)ln_w[e] + (double)ln_b[e]", "* (double)ln_b[e] + (double)ln_w[e]", 1),
     ("reset ignored", "(reset && reset[t]) ? 0.0 : exp(d * A)", "exp(d * A)", 1),
     ("duplicate mask index accepted", "if (q < 0 || q >= h * w || seen[q])", "if (q < 0 || q >= h * w)", 1),
 ]
