@@ -267,6 +267,17 @@ def main():
         rcall = P.SSMCall(x, z, prm, P.POOL_ROWS, workspace=call.workspace, out=call.out)
         rcall.run(stream)
         extras["rows_layer_ms"], _ = time_steps(lambda: rcall.run(stream), n, stream)
+        # the layer with the post-SSM LayerNorm before the gate (stage kernels)
+        g_ln = torch.Generator(device="cuda").manual_seed(1)
+        ln = {"weight": 1.0 + 0.1 * torch.randn(cfg.E, device=dev, generator=g_ln),
+              "bias": 0.1 * torch.randn(cfg.E, device=dev, generator=g_ln), "eps": 1e-5}
+        ncall = P.SSMCall(x, z, prm, P.POOL_COLS, workspace=call.workspace, out=call.out, ln=ln)
+        ncall.run(stream)
+        ln_ms, _ = time_steps(lambda: ncall.run(stream), n, stream)
+        ln_epi, _ = time_steps(lambda: ncall.stage(P.STAGE_EPILOGUE, stream), n, stream)
+        extras["post_norm_2048"] = {"layer_ms": ln_ms, "epilogue_ms": ln_epi, "path": "stage kernels",
+                                    "epilogue_GBps": alg_bytes / (ln_epi * 1e-3) / 1e9}
+        del ncall
         # torch's device copy, for comparison with the calibration copy
         dst = torch.empty_like(x)
         tc_ms, _ = time_steps(lambda: dst.copy_(x), 3, stream)

@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define FASTVIM_ABI_VERSION 2
+#define FASTVIM_ABI_VERSION 3
 
 typedef enum fastvim_status {
     FASTVIM_OK = 0,
@@ -115,6 +115,12 @@ typedef struct fastvim_params {
     size_t workspace_bytes;
     uint32_t flags;         /* FASTVIM_FLAG_* bits, else 0 */
     uint32_t reserved;
+    /* Post-SSM LayerNorm, used with FASTVIM_FLAG_POST_NORM only: per-channel
+     * scale and shift (E) fp32, 16-byte aligned, and eps > 0. */
+    const float *ln_weight;
+    const float *ln_bias;
+    float ln_eps;
+    uint32_t reserved2;
 } fastvim_params;
 
 /* params.flags bits.  By default a dense pooled layer (COLS or ROWS, no mask)
@@ -131,6 +137,18 @@ typedef struct fastvim_params {
  * for measurement. */
 #define FASTVIM_FLAG_STAGED 1u
 #define FASTVIM_FLAG_FUSED 2u
+
+/* FASTVIM_FLAG_POST_NORM adds the post-SSM LayerNorm between the skip and the
+ * gate (FastVim summary page, section 方法详解, bullet 5: LayerNorm after the
+ * repeat and the skip connection; the Pith review on 2502.00594: the
+ * post-SSM LayerNorm of VMamba, on the SSM output).  Per token, over its E
+ * channels: y = s_fwd + s_bwd + (D_fwd + D_bwd) x,
+ *   out = ((y - mean(y)) / sqrt(var(y) + ln_eps) * ln_weight + ln_bias) * silu(z)
+ * with the population variance.  Layers with the norm run as stage kernels
+ * (the single launch does not take it; FASTVIM_FLAG_FUSED is then ignored).
+ * Errors: FASTVIM_ERR_NULL (ln_weight or ln_bias NULL), FASTVIM_ERR_ALIGN (not
+ * 16-byte aligned), FASTVIM_ERR_ARG (ln_eps not > 0 or not finite). */
+#define FASTVIM_FLAG_POST_NORM 4u
 
 /* Bytes of workspace a call with these sizes needs (0 if the sizes are
  * invalid).  Dense pooled layers need 4 * B * T * (3E + 2(R + 2N)) bytes plus

@@ -28,6 +28,8 @@ EXPORT_U, EXPORT_XDBL, EXPORT_S_FWD, EXPORT_S_BWD, EXPORT_ROWS, EXPORT_BAD_TOKEN
 # every dense pooled layer as the single pipelined launch; by default the
 # library picks by size
 FLAG_STAGED, FLAG_FUSED = 1, 2
+# FLAG_POST_NORM: post-SSM LayerNorm between the skip and the gate
+FLAG_POST_NORM = 4
 
 STATUS = {
     0: "FASTVIM_OK", -1: "FASTVIM_ERR_NULL", -2: "FASTVIM_ERR_DIMS", -3: "FASTVIM_ERR_UNSUPPORTED",
@@ -57,7 +59,9 @@ class DirParams(ctypes.Structure):
 
 class Params(ctypes.Structure):
     _fields_ = [("fwd", DirParams), ("bwd", DirParams), ("workspace", ctypes.c_void_p),
-                ("workspace_bytes", ctypes.c_size_t), ("flags", ctypes.c_uint32), ("reserved", ctypes.c_uint32)]
+                ("workspace_bytes", ctypes.c_size_t), ("flags", ctypes.c_uint32), ("reserved", ctypes.c_uint32),
+                ("ln_weight", ctypes.c_void_p), ("ln_bias", ctypes.c_void_p), ("ln_eps", ctypes.c_float),
+                ("reserved2", ctypes.c_uint32)]
 
 
 EXPORTED_SYMBOLS = (
@@ -131,12 +135,13 @@ class SSMCall:
     Dense: x, z (B, h, w, E).  Masked: x, z (B, K, E), mask_idx (B, K) int32
     and hw = (h, w).  params = {"fwd": {...}, "bwd": {...}} holding fp32
     device tensors x_proj_w (R+2N, E), dt_proj_w (E, R), dt_proj_b (E),
-    A_log (E, N), D (E)."""
+    A_log (E, N), D (E).  ln = {"weight": (E,), "bias": (E,), "eps": float}
+    (fp32 device tensors) adds the post-SSM LayerNorm before the gate."""
 
     def __init__(self, x: torch.Tensor, z: torch.Tensor, params: Dict[str, Dict[str, torch.Tensor]],
                  pool_axis: int, mask_idx: Optional[torch.Tensor] = None, hw: Optional[Tuple[int, int]] = None,
                  out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-                 flags: int = 0):
+                 flags: int = 0, ln: Optional[Dict[str, object]] = None):
         io = _io_dtype(x)
         if z.dtype != x.dtype or z.shape != x.shape:
             raise ValueError("z must match x in shape and dtype")
@@ -177,8 +182,17 @@ class SSMCall:
         if workspace is None:
             workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=x.device)
         self.workspace = workspace
+        ln_w = ln_b = None
+        ln_eps = 0.0
+        if ln is not None:
+            ln_w, ln_b, ln_eps = ln["weight"], ln["bias"], float(ln["eps"])
+            for t in (ln_w, ln_b):
+                if t.dtype != torch.float32 or not t.is_contiguous():
+                    raise ValueError("LayerNorm weight and bias must be contiguous float32")
+            self._keep.extend([ln_w, ln_b])
+            flags |= FLAG_POST_NORM
         self.params = Params(dirs[0], dirs[1], workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-                             flags, 0)
+                             flags, 0, _ptr(ln_w), _ptr(ln_b), ln_eps, 0)
 
     def _args(self):
         return (_ptr(self.x), _ptr(self.z), ctypes.byref(self.params), ctypes.byref(self.dims), self.pool_axis,
@@ -214,10 +228,10 @@ class SSMCall:
 
 
 def ssm_fwd(x, z, params, pool_axis=POOL_COLS, mask_idx=None, hw=None, out=None, workspace=None, stream=None,
-            flags=0):
+            flags=0, ln=None):
     """The pooled bidirectional selective-scan layer; returns out."""
     return SSMCall(x, z, params, pool_axis, mask_idx=mask_idx, hw=hw, out=out, workspace=workspace,
-                   flags=flags).run(stream)
+                   flags=flags, ln=ln).run(stream)
 
 
 def calib_copy(dst: torch.Tensor, src: torch.Tensor, stream=None) -> None:

@@ -74,8 +74,8 @@ int check_dir(const fastvim_dir_params& d) {
 int validate(const void* x, const void* z, const fastvim_params* prm, const fastvim_dims* d, int axis,
              const int32_t* idx, const void* out, Geom* g, Workspace* ws, bool* empty) {
     if (!prm) return FASTVIM_ERR_NULL;
-    const uint32_t known = FASTVIM_FLAG_STAGED | FASTVIM_FLAG_FUSED;
-    if ((prm->flags & ~known) || (prm->flags & known) == known) return FASTVIM_ERR_ARG;
+    const uint32_t paths = FASTVIM_FLAG_STAGED | FASTVIM_FLAG_FUSED;
+    if ((prm->flags & ~(paths | FASTVIM_FLAG_POST_NORM)) || (prm->flags & paths) == paths) return FASTVIM_ERR_ARG;
     int st = resolve_geom(d, axis, g);
     if (st) return st;
     if (!g->masked && idx) return FASTVIM_ERR_ARG;
@@ -83,6 +83,11 @@ int validate(const void* x, const void* z, const fastvim_params* prm, const fast
     if (*empty) return FASTVIM_OK;
     if (!x || !z || !out || (g->masked && !idx)) return FASTVIM_ERR_NULL;
     if ((st = check_dir(prm->fwd)) || (st = check_dir(prm->bwd))) return st;
+    if (prm->flags & FASTVIM_FLAG_POST_NORM) {
+        if (!prm->ln_weight || !prm->ln_bias) return FASTVIM_ERR_NULL;
+        if (!aligned(prm->ln_weight, 16) || !aligned(prm->ln_bias, 16)) return FASTVIM_ERR_ALIGN;
+        if (!(prm->ln_eps > 0.f) || !(prm->ln_eps < 3.4e38f)) return FASTVIM_ERR_ARG;
+    }
     if (!prm->workspace) return FASTVIM_ERR_WORKSPACE;
     if (!aligned(x, 16) || !aligned(z, 16) || !aligned(out, 16) || !aligned(prm->workspace, 256) ||
         (idx && !aligned(idx, 4)))
@@ -111,7 +116,10 @@ int run_stage(int stage, const Geom& g, const void* x, const void* z, const fast
             break;
         case FASTVIM_STAGE_PROJ: e = launch_proj(g, x, p, ws, st); break;
         case FASTVIM_STAGE_SCAN: e = launch_scan(g, x, p, ws, st); break;
-        case FASTVIM_STAGE_EPILOGUE: e = launch_epilogue(g, x, z, p, ws, out, st); break;
+        case FASTVIM_STAGE_EPILOGUE:
+            e = (p.flags & FASTVIM_FLAG_POST_NORM) ? launch_epilogue_norm(g, x, z, p, ws, out, st)
+                                                  : launch_epilogue(g, x, z, p, ws, out, st);
+            break;
         default: return FASTVIM_ERR_ARG;
     }
     return e == hipSuccess ? FASTVIM_OK : FASTVIM_ERR_HIP;
@@ -181,8 +189,9 @@ int fastvim_ssm_fwd(const void* x, const void* z, const fastvim_params* params, 
     if (st || empty) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (launch_zero_sync(ws, sync_words(g), s) != hipSuccess) return FASTVIM_ERR_HIP;
-    const bool single = (params->flags & FASTVIM_FLAG_FUSED) ? fused_supported(g)
-                        : !(params->flags & FASTVIM_FLAG_STAGED) && fused_preferred(g);
+    const bool single = !(params->flags & FASTVIM_FLAG_POST_NORM) &&
+                        ((params->flags & FASTVIM_FLAG_FUSED) ? fused_supported(g)
+                                                              : !(params->flags & FASTVIM_FLAG_STAGED) && fused_preferred(g));
     if (single)
         return launch_fused(g, x, z, *params, ws, out, s) == hipSuccess ? FASTVIM_OK : FASTVIM_ERR_HIP;
     for (int stage = FASTVIM_STAGE_ROWS; stage <= FASTVIM_STAGE_EPILOGUE; ++stage) {

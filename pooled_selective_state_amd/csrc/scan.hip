@@ -31,6 +31,7 @@ hipError_t scan_dispatch(const USrc& usrc, const Geom& g, const fastvim_params& 
                          hipStream_t st) {
     if (g.R <= 16) return scan_launch<16>(usrc, g, p, ws, st);
     if (g.R <= 32) return scan_launch<32>(usrc, g, p, ws, st);
+    if (g.R <= 48) return scan_launch<48>(usrc, g, p, ws, st);
     return scan_launch<64>(usrc, g, p, ws, st);
 }
 

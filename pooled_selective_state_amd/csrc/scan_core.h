@@ -180,7 +180,7 @@ struct ScanLane {
 template <int RMAX>
 __device__ __forceinline__ void scan_lane_setup(const ScanArgs& a, int64_t b, int64_t e0, ScanLane<RMAX>& L,
                                                 int64_t& ec) {
-    static_assert(RMAX % 4 == 0 && RMAX <= kRMax, "dt rank bound");
+    static_assert(RMAX % 16 == 0 && RMAX <= kRMax, "dt rank bound: 16-byte aligned rows and lane quarters");
     const int tid = threadIdx.x;
     L.dir = tid >> 8;
     const int ch = (tid & 255) / kLps;

@@ -32,7 +32,7 @@ def test_library_exports_every_declared_function():
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(Bd.EXPORTED_SYMBOLS)
-    assert lib.fastvim_abi_version() == 2
+    assert lib.fastvim_abi_version() == 3
 
 
 def test_status_strings():
@@ -43,10 +43,10 @@ def test_status_strings():
 
 
 def test_struct_layout_matches_header():
-    # int64 x 7 + int32 x 2; five pointers; two dir structs + ptr + size_t + 2 x u32
+    # int64 x 7 + int32 x 2; five pointers; two dir structs + ptr + size_t + 2 x u32 + 2 ptrs + f32 + u32
     assert ctypes.sizeof(Bd.Dims) == 64
     assert ctypes.sizeof(Bd.DirParams) == 40
-    assert ctypes.sizeof(Bd.Params) == 2 * 40 + 8 + 8 + 8
+    assert ctypes.sizeof(Bd.Params) == 2 * 40 + 8 + 8 + 8 + 8 + 8 + 4 + 4
 
 
 def _ws(dims, axis):
@@ -149,7 +149,7 @@ def test_bad_enums():
     c = FakeCall()
     assert lib.fastvim_ssm_stage(5, c.x, c.z, ctypes.byref(c.params), ctypes.byref(c.dims), 0, None, c.out,
                                  None) == EARG
-    for flags in (P.FLAG_STAGED | P.FLAG_FUSED, 4, 1 << 31):  # conflicting or unknown flags
+    for flags in (P.FLAG_STAGED | P.FLAG_FUSED, 8, 1 << 31):  # conflicting or unknown flags
         c = FakeCall()
         c.params.flags = flags
         expect(c, EARG)
@@ -241,3 +241,15 @@ def test_calib_copy_validation():
     assert lib.fastvim_calib_copy(a, b, 60, None) == EALIGN
     assert lib.fastvim_calib_copy(a, a + 32, 64, None) == EOVERLAP
     assert lib.fastvim_calib_copy(a + 32, a, 64, None) == EOVERLAP
+
+
+def test_post_norm_validation():
+    """The post-SSM LayerNorm's parameters are checked before any launch."""
+    base = 0x40000
+    for (w, b, eps, code) in ((None, base, 1e-5, ENULL), (base, None, 1e-5, ENULL), (base + 4, base, 1e-5, EALIGN),
+                              (base, base + 8, 1e-5, EALIGN), (base, base, 0.0, EARG), (base, base, -1.0, EARG),
+                              (base, base, float("nan"), EARG), (base, base, float("inf"), EARG)):
+        c = FakeCall()
+        c.params.flags = P.FLAG_POST_NORM
+        c.params.ln_weight, c.params.ln_bias, c.params.ln_eps = w, b, eps
+        expect(c, code)

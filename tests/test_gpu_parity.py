@@ -22,7 +22,7 @@ import oracle
 import pooled_selective_state_amd as P
 from gpu_util import (BF16_TOL, FP32_TOL, check, compare_stages, dev, dev_params, gpu_call, host, rel_inf,
                       stage_exports, status_ok)
-from pins import rand_dir
+from pins import rand_dir, rand_ln
 from pooled_selective_state_amd import configs as C
 from pooled_selective_state_amd.inputs import draw_workload, random_mask, round_to_bf16, zero_D
 
@@ -41,24 +41,24 @@ def _gpu():
     torch.cuda.synchronize()
 
 
-def _layer_check(x, z, prm, axis, tol, dtype, tag, idx=None, hw=None, sel=None, flags=0):
+def _layer_check(x, z, prm, axis, tol, dtype, tag, idx=None, hw=None, sel=None, flags=0, ln=None):
     """Run GPU layer + D=0 twin, compare out / twin / stages with the oracle
     on images ``sel`` (all if None)."""
-    call = gpu_call(x, z, prm, axis, idx=idx, hw=hw, dtype=dtype, flags=flags)
+    call = gpu_call(x, z, prm, axis, idx=idx, hw=hw, dtype=dtype, flags=flags, ln=ln)
     out = call.run()
     torch.cuda.synchronize()
     status_ok(call)
     st = stage_exports(call)
     rows = host(call.export(P.EXPORT_ROWS)).astype(np.int64) if idx is not None else None
-    tcall = gpu_call(x, z, zero_D(prm), axis, idx=idx, hw=hw, dtype=dtype, flags=flags)
+    tcall = gpu_call(x, z, zero_D(prm), axis, idx=idx, hw=hw, dtype=dtype, flags=flags, ln=ln)
     twin = tcall.run()
     torch.cuda.synchronize()
     status_ok(tcall)
     s = slice(None) if sel is None else sel
     ref = oracle.layer(x[s], z[s], prm["fwd"], prm["bwd"], axis, idx=None if idx is None else idx[s], hw=hw,
-                       stages=True)
+                       stages=True, ln=ln)
     ref0 = oracle.layer(x[s], z[s], zero_D(prm)["fwd"], zero_D(prm)["bwd"], axis,
-                        idx=None if idx is None else idx[s], hw=hw)
+                        idx=None if idx is None else idx[s], hw=hw, ln=ln)
     check(host(out[s]), ref["out"], tol, tag + " out")
     check(host(twin[s]), ref0, tol, tag + " out(D=0)")
     compare_stages({k: v[s] for k, v in st.items()}, ref, tol, tag)
@@ -179,6 +179,69 @@ def test_projection_many_tokens(R, axis):
     seq = np.ascontiguousarray(seq).reshape(B, h * w, E)
     for d, name in enumerate(("fwd", "bwd")):
         check(got[:, :, d, :], oracle.xproj(seq, prm[name]["x_proj_w"]), FP32_TOL, "x_proj %s R=%d" % (name, R))
+
+
+# ------------------------------------------------------------ post-SSM LayerNorm
+@pytest.mark.parametrize("axis", AXES)
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_post_norm_tiny(axis, io):
+    """The post-SSM LayerNorm before the gate, every pooling axis."""
+    wl = draw_workload(C.TINY)
+    x, z = wl["x"], wl["z"][0]
+    if io == "bf16":
+        x, z = round_to_bf16(x), round_to_bf16(z)
+    ln = rand_ln(np.random.default_rng(70 + axis), C.TINY.E)
+    _layer_check(x, z, wl["params"][0], axis, FP32_TOL if io == "f32" else BF16_TOL,
+                 torch.float32 if io == "f32" else torch.bfloat16, "norm tiny %d %s" % (axis, io), ln=ln)
+
+
+@pytest.mark.parametrize("E", [8, 72, 520, 1032, 2056, 4096])
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_post_norm_widths(E, io):
+    """Every lane-team size of the normalising epilogue (16, 32 or 64 lanes per
+    token, up to 16 vectors per lane) and widths that leave part of the team
+    idle, on a ragged grid."""
+    if io == "bf16" and E % 8:
+        pytest.skip("bf16 needs E % 8 == 0")
+    rng = np.random.default_rng(80 + E)
+    B, h, w, N, R = 2, 3, 5, 16, 5
+    x = rng.standard_normal((B, h, w, E), dtype=np.float32)
+    z = rng.standard_normal((B, h, w, E), dtype=np.float32)
+    if io == "bf16":
+        x, z = round_to_bf16(x), round_to_bf16(z)
+    prm = {d: rand_dir(rng, E, N, R, scale=0.05) for d in ("fwd", "bwd")}
+    ln = rand_ln(rng, E, eps=1e-5)
+    _layer_check(x, z, prm, P.POOL_ROWS, FP32_TOL if io == "f32" else BF16_TOL,
+                 torch.float32 if io == "f32" else torch.bfloat16, "norm E=%d %s" % (E, io), ln=ln)
+
+
+def test_post_norm_masked_with_invalid_index():
+    """Masked layer with the norm; a duplicated index gives NaN for exactly
+    the tokens that carry it, the others match the oracle on the valid set."""
+    rng = np.random.default_rng(90)
+    B, h, w, K, E, N, R = 2, 6, 7, 11, 96, 16, 6
+    x = rng.standard_normal((B, K, E), dtype=np.float32)
+    z = rng.standard_normal((B, K, E), dtype=np.float32)
+    prm = {d: rand_dir(rng, E, N, R, scale=0.05) for d in ("fwd", "bwd")}
+    ln = rand_ln(rng, E)
+    idx = random_mask(rng, B, h, w, K)
+    _layer_check(x, z, prm, P.POOL_COLS, FP32_TOL, torch.float32, "norm masked", idx=idx, hw=(h, w), ln=ln)
+    bad = idx.copy()
+    bad[1, 3] = bad[1, 5]  # a duplicate in image 1
+    call = gpu_call(x, z, prm, P.POOL_COLS, idx=bad, hw=(h, w), ln=ln)
+    out = host(call.run())
+    torch.cuda.synchronize()
+    nan_tok = np.isnan(out).all(axis=-1)
+    assert nan_tok[1, 3] and nan_tok[1, 5] and nan_tok.sum() == 2
+    assert np.isfinite(out[~nan_tok]).all()
+
+
+def test_post_norm_full_size_2048():
+    """The 2048^2 layer with the norm (stage kernels), sampled images."""
+    wl = _workload(C.HIRES_2048)
+    ln = rand_ln(np.random.default_rng(95), C.HIRES_2048.E)
+    _layer_check(wl["x"], wl["z"][0], wl["params"][0], P.POOL_COLS, FP32_TOL, torch.float32, "norm 2048",
+                 sel=_sample(C.HIRES_2048.B), ln=ln)
 
 
 def test_masked_integer_sums_exact():
