@@ -38,6 +38,16 @@ class _DirOut(ctypes.Structure):
     _fields_ = [("v", ctypes.c_void_p), ("delta", ctypes.c_void_p), ("s", ctypes.c_void_p)]
 
 
+class _DirGrad(ctypes.Structure):
+    _fields_ = [(k, ctypes.c_void_p) for k in ("x_proj_w", "dt_proj_w", "dt_proj_b", "A_log", "D")]
+
+
+class _BwdStages(ctypes.Structure):
+    _fields_ = [(k, ctypes.c_void_p) for k in ("gs", "du", "dv_f", "dv_b")]
+
+PARAM_NAMES = ("x_proj_w", "dt_proj_w", "dt_proj_b", "A_log", "D")
+
+
 def build(force: bool = True, src: str = _SRC, out: str = _LIB) -> str:
     """Compile the oracle C source with gcc into a shared library."""
     if force or not os.path.exists(out):
@@ -87,6 +97,12 @@ class Oracle:
             vp, vp, ctypes.c_double,
         ]
         lib.fvo_layer.restype = ci
+        lib.fvo_layer_bwd.argtypes = [
+            vp, vp, vp, ctypes.POINTER(_Dir), ctypes.POINTER(_Dir),
+            i64, i64, i64, i64, i64, i64, i64, ci, vp,
+            vp, vp, ctypes.POINTER(_DirGrad), ctypes.POINTER(_DirGrad), ctypes.POINTER(_BwdStages),
+        ]
+        lib.fvo_layer_bwd.restype = ci
         self._lib = lib
         self.path = path
 
@@ -216,6 +232,54 @@ class Oracle:
             return out
         return {"out": out, "u": u, "rows": rows, "fwd": st["fwd"], "bwd": st["bwd"]}
 
+    def layer_bwd(self, x, z, dout, fwd, bwd, axis, idx=None, hw=None, stages=False):
+        """Gradients of sum(dout * layer(x, z, ...)) (no LayerNorm).  Arguments as
+        layer(); dout is shaped like x.  Returns a dict with dx, dz (fp64, shaped
+        like x) and "fwd" / "bwd" dicts of parameter gradients keyed like the
+        parameters; with stages=True also gs, du (B,T,E) and dv_fwd, dv_bwd
+        (B,T,NX)."""
+        x, z, dout = _f32(x), _f32(z), _f32(dout)
+        assert dout.shape == x.shape
+        keep = []
+        pf, pb = _dir_struct(fwd, keep), _dir_struct(bwd, keep)
+        NX, E = keep[0].shape
+        N = keep[3].shape[1]
+        R = NX - 2 * N
+        if idx is None:
+            B, h, w, _ = x.shape
+            K = 0
+            idx_a = None
+        else:
+            B, K, _ = x.shape
+            h, w = hw
+            idx_a = np.ascontiguousarray(idx, dtype=np.int32)
+            assert idx_a.shape == (B, K)
+        T = {COLS: h, ROWS: w}.get(axis, h * w)
+        dx = np.empty(x.shape, np.float64)
+        dz = np.empty(x.shape, np.float64)
+        grads = {}
+        structs = []
+        for name, p in (("fwd", fwd), ("bwd", bwd)):
+            grads[name] = {k: np.empty(np.shape(p[k]), np.float64) for k in PARAM_NAMES}
+            structs.append(_DirGrad(*[grads[name][k].ctypes.data for k in PARAM_NAMES]))
+        st = None
+        res = {"dx": dx, "dz": dz, "fwd": grads["fwd"], "bwd": grads["bwd"]}
+        if stages:
+            res["gs"] = np.empty((B, T, E), np.float64)
+            res["du"] = np.empty((B, T, E), np.float64)
+            res["dv_fwd"] = np.empty((B, T, NX), np.float64)
+            res["dv_bwd"] = np.empty((B, T, NX), np.float64)
+            st = _BwdStages(*[res[k].ctypes.data for k in ("gs", "du", "dv_fwd", "dv_bwd")])
+        rc = self._lib.fvo_layer_bwd(
+            _ptr(x), _ptr(z), _ptr(dout), ctypes.byref(pf), ctypes.byref(pb),
+            B, h, w, E, N, R, K, axis, _ptr(idx_a), _ptr(dx), _ptr(dz),
+            ctypes.byref(structs[0]), ctypes.byref(structs[1]),
+            ctypes.byref(st) if st is not None else None,
+        )
+        if rc:
+            raise ValueError("fvo_layer_bwd failed: %d" % rc)
+        return res
+
 
 def _dir_struct(p, keep):
     arrs = [_f32(p[k]) for k in ("x_proj_w", "dt_proj_w", "dt_proj_b", "A_log", "D")]
@@ -268,3 +332,7 @@ def scan(u, dlt, v, A_log, R, reverse=False, reset=None):
 
 def layer(x, z, fwd, bwd, axis, idx=None, hw=None, stages=False, ln=None):
     return get().layer(x, z, fwd, bwd, axis, idx=idx, hw=hw, stages=stages, ln=ln)
+
+
+def layer_bwd(x, z, dout, fwd, bwd, axis, idx=None, hw=None, stages=False):
+    return get().layer_bwd(x, z, dout, fwd, bwd, axis, idx=idx, hw=hw, stages=stages)

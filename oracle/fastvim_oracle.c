@@ -390,3 +390,267 @@ done:
     if (masked && !rows_out) free(rows);
     return rc;
 }
+
+/* ------------------------------------------------------------------------
+ * Backward pass: the gradient of a scalar loss L = sum(dout * out) with
+ * respect to x, z and every parameter of both directions, written as the
+ * chain rule taken through the forward steps in reverse order, one step at a
+ * time.  Each function below is the adjoint of one forward step above; the
+ * training workload the gradients serve is the one the FastVim summary page
+ * (实验结果: ImageNet training and MAE pre-training) trains.
+ * ------------------------------------------------------------------------ */
+
+/* Gradients of one direction's parameters (all shaped like the parameters). */
+typedef struct {
+    double *x_proj_w;  /* (NX, E) */
+    double *dt_proj_w; /* (E, R)  */
+    double *dt_proj_b; /* (E)     */
+    double *A_log;     /* (E, N)  */
+    double *D;         /* (E)     */
+} fvo_dir_grad;
+
+/* Optional intermediate adjoints (NULL = not wanted). */
+typedef struct {
+    double *gs;    /* (B, T, E)  dL/ds, the same for both directions      */
+    double *du;    /* (B, T, E)  dL/du, both directions, scan and x_proj  */
+    double *dv_f;  /* (B, T, NX) dL/dv of the forward direction           */
+    double *dv_b;  /* (B, T, NX) dL/dv of the backward direction          */
+} fvo_bwd_stages;
+
+static double sigmoid(double q) { return 1.0 / (1.0 + exp(-q)); }
+
+/* Pre-activation of the step size, q[m, e] = sum_r dt_proj_w[e, r] v[m, r] + dt_proj_b[e]. */
+static void dt_preact(const double *v, int64_t M, int64_t NX, int64_t R, const float *dt_proj_w,
+                      const float *dt_proj_b, int64_t E, double *q)
+{
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t e = 0; e < E; ++e) {
+            double acc = (double)dt_proj_b[e];
+            for (int64_t r = 0; r < R; ++r) acc += (double)dt_proj_w[e * R + r] * v[m * NX + r];
+            q[m * E + e] = acc;
+        }
+}
+
+/*
+ * Adjoint of the output of one token (no LayerNorm).  With
+ * y = s_fwd + s_bwd + (D_fwd + D_bwd) x and out = y silu(z):
+ *   g       = dL/dy = dout silu(z)                  (also dL/ds of both scans)
+ *   dz      = dout y silu'(z),  silu'(q) = sigmoid(q) (1 + q (1 - sigmoid(q)))
+ *   dx_skip = g (D_fwd + D_bwd)
+ *   dD     += g x          (the same for D_fwd and D_bwd)
+ */
+static void output_token_adjoint(const double *sf, const double *sb, const float *x, const float *z,
+                                 const float *dout, const fvo_dir *pf, const fvo_dir *pb, int64_t E, double *g,
+                                 double *dz, double *dx_skip, double *dD)
+{
+    for (int64_t e = 0; e < E; ++e) {
+        const double Ds = (double)pf->D[e] + (double)pb->D[e];
+        const double xe = (double)x[e], ze = (double)z[e], de = (double)dout[e];
+        const double y = sf[e] + sb[e] + Ds * xe;
+        const double sg = sigmoid(ze);
+        g[e] = de * silu(ze);
+        dz[e] = de * y * sg * (1.0 + ze * (1.0 - sg));
+        dx_skip[e] = g[e] * Ds;
+        dD[e] += g[e] * xe;
+    }
+}
+
+/*
+ * Adjoint of one selective scan (the recurrence of fvo_scan).  With k the
+ * scan step (t = k forward, t = T-1-k backward), a_k[n] = exp(delta_k A[n]),
+ * H_k = a_k H_{k-1} + delta_k B_k u_k and s_k = sum_n C_k[n] H_k[n], the state
+ * adjoint lambda_k = dL/dH_k runs backwards in k:
+ *   lambda_k[n] = C_k[n] gs_k + a_{k+1}[n] lambda_{k+1}[n]      (lambda_T = 0)
+ * and gives
+ *   ddelta_k   = sum_n lambda_k[n] (A[n] a_k[n] H_{k-1}[n] + B_k[n] u_k)
+ *   du_k      += sum_n lambda_k[n] delta_k B_k[n]
+ *   dB_k[n]   += lambda_k[n] delta_k u_k         (summed over channels e)
+ *   dC_k[n]   += gs_k H_k[n]                     (summed over channels e)
+ *   dA[e, n]  += lambda_k[n] a_k[n] delta_k H_{k-1}[n]
+ * dB and dC land in dv[m, R + n] and dv[m, R + N + n].  The states of the
+ * forward sweep are kept whole (T*N doubles per channel).
+ */
+static int scan_adjoint(const double *u, const double *delta, const double *v, const double *gs, int64_t B,
+                        int64_t T, int64_t E, int64_t N, int64_t R, int64_t NX, const float *A_log, int reverse,
+                        double *du, double *ddelta, double *dv, double *dA)
+{
+    double *Hs = (double *)malloc((size_t)(T * N) * sizeof(double));
+    double *lam = (double *)malloc((size_t)N * sizeof(double));
+    double *carry = (double *)malloc((size_t)N * sizeof(double));
+    if (!Hs || !lam || !carry) { free(Hs); free(lam); free(carry); return -9; }
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t e = 0; e < E; ++e) {
+            /* forward sweep, keeping every state */
+            for (int64_t k = 0; k < T; ++k) {
+                const int64_t m = b * T + (reverse ? T - 1 - k : k);
+                for (int64_t n = 0; n < N; ++n) {
+                    const double A = -exp((double)A_log[e * N + n]);
+                    const double prev = k > 0 ? Hs[(k - 1) * N + n] : 0.0;
+                    Hs[k * N + n] = exp(delta[m * E + e] * A) * prev + delta[m * E + e] * v[m * NX + R + n] * u[m * E + e];
+                }
+            }
+            /* reverse sweep */
+            for (int64_t n = 0; n < N; ++n) carry[n] = 0.0;
+            for (int64_t k = T - 1; k >= 0; --k) {
+                const int64_t m = b * T + (reverse ? T - 1 - k : k);
+                const double d = delta[m * E + e], ut = u[m * E + e], g = gs[m * E + e];
+                double dd = 0.0, duk = 0.0;
+                for (int64_t n = 0; n < N; ++n) {
+                    const double A = -exp((double)A_log[e * N + n]);
+                    const double a = exp(d * A);
+                    const double Bn = v[m * NX + R + n], Cn = v[m * NX + R + N + n];
+                    const double prev = k > 0 ? Hs[(k - 1) * N + n] : 0.0;
+                    lam[n] = Cn * g + carry[n];
+                    dd += lam[n] * (A * a * prev + Bn * ut);
+                    duk += lam[n] * d * Bn;
+                    dv[m * NX + R + n] += lam[n] * d * ut;
+                    dv[m * NX + R + N + n] += g * Hs[k * N + n];
+                    dA[e * N + n] += lam[n] * a * d * prev;
+                    carry[n] = a * lam[n];
+                }
+                ddelta[m * E + e] = dd;
+                du[m * E + e] += duk;
+            }
+        }
+    free(Hs); free(lam); free(carry);
+    return 0;
+}
+
+/*
+ * Adjoint of the step size, delta = softplus(q) with q = W_dt v[0:R] + b_dt:
+ *   dq = ddelta sigmoid(q);  db_dt[e] += dq;  dW_dt[e, r] += dq v[m, r];
+ *   dv[m, r] += sum_e W_dt[e, r] dq.
+ */
+static void step_size_adjoint(const double *q, const double *ddelta, const double *v, int64_t M, int64_t NX,
+                              int64_t R, int64_t E, const float *dt_proj_w, double *dWdt, double *dbdt, double *dv)
+{
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t e = 0; e < E; ++e) {
+            const double dq = ddelta[m * E + e] * sigmoid(q[m * E + e]);
+            dbdt[e] += dq;
+            for (int64_t r = 0; r < R; ++r) {
+                dWdt[e * R + r] += dq * v[m * NX + r];
+                dv[m * NX + r] += (double)dt_proj_w[e * R + r] * dq;
+            }
+        }
+}
+
+/* Adjoint of v = W_x u:  dW_x[o, e] += dv[m, o] u[m, e];  du[m, e] += sum_o W_x[o, e] dv[m, o]. */
+static void xproj_adjoint(const double *u, const double *dv, int64_t M, int64_t NX, int64_t E,
+                          const float *x_proj_w, double *dWx, double *du)
+{
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t o = 0; o < NX; ++o)
+            for (int64_t e = 0; e < E; ++e) {
+                dWx[o * E + e] += dv[m * NX + o] * u[m * E + e];
+                du[m * E + e] += (double)x_proj_w[o * E + e] * dv[m * NX + o];
+            }
+}
+
+/*
+ * The whole backward pass (no LayerNorm).  Inputs as fvo_layer plus dout
+ * (shaped like x).  Outputs dx, dz (shaped like x) and the gradients of both
+ * directions' parameters (overwritten).  The pool's adjoint spreads du of a
+ * scan position over its cells: dx[b, cell, e] = dx_skip + du[b, t(cell), e] / P
+ * (P = 1 unpooled; the fixed row length for masked tokens).  Returns 0, -2,
+ * -3 or -9 as fvo_layer.
+ */
+int fvo_layer_bwd(const float *x, const float *z, const float *dout, const fvo_dir *pf, const fvo_dir *pb,
+                  int64_t B, int64_t h, int64_t w, int64_t E, int64_t N, int64_t R, int64_t K, int axis,
+                  const int32_t *idx, double *dx, double *dz, fvo_dir_grad *gf, fvo_dir_grad *gb,
+                  fvo_bwd_stages *st)
+{
+    int64_t T, P;
+    const int masked = idx != NULL;
+    if (axis < 0 || axis > 3 || (masked && axis > FVO_ROWS)) return -2;
+    seq_shape(axis, h, w, &T, &P);
+    const int64_t NX = R + 2 * N, M = B * T, ntok = masked ? B * K : B * h * w;
+    const size_t me = (size_t)(M * E) * sizeof(double), mx = (size_t)(M * NX) * sizeof(double);
+    const fvo_dir *pd[2] = {pf, pb};
+    fvo_dir_grad *gd[2] = {gf, gb};
+    int rc = 0;
+
+    double *u = (double *)malloc(me), *gs = (double *)calloc((size_t)(M * E), sizeof(double));
+    double *du = (double *)calloc((size_t)(M * E), sizeof(double)), *dd = (double *)malloc(me);
+    double *g = (double *)malloc((size_t)E * sizeof(double));
+    double *dxs = (double *)malloc((size_t)(ntok * E) * sizeof(double));
+    double *dD = (double *)calloc((size_t)E, sizeof(double));
+    double *v[2], *q[2], *dl[2], *s[2], *dv[2];
+    int32_t *rows = masked ? (int32_t *)malloc((size_t)(B * K) * sizeof(int32_t)) : NULL;
+    for (int d = 0; d < 2; ++d) {
+        v[d] = (double *)malloc(mx); q[d] = (double *)malloc(me); dl[d] = (double *)malloc(me);
+        s[d] = (double *)malloc(me); dv[d] = (double *)calloc((size_t)(M * NX), sizeof(double));
+    }
+    if (!u || !gs || !du || !dd || !g || !dxs || !dD || (masked && !rows)) { rc = -9; goto done; }
+    for (int d = 0; d < 2; ++d)
+        if (!v[d] || !q[d] || !dl[d] || !s[d] || !dv[d]) { rc = -9; goto done; }
+
+    /* forward recomputation: pooled input, per-direction v, q, delta, s */
+    if (masked) {
+        rc = fvo_mask_rows(idx, B, K, h, w, axis, rows);
+        if (rc) goto done;
+        fvo_pool_masked(x, rows, B, K, T, P, E, u);
+    } else {
+        fvo_pool_dense(x, B, h, w, E, axis, u);
+    }
+    for (int d = 0; d < 2; ++d) {
+        fvo_xproj(u, M, E, pd[d]->x_proj_w, NX, v[d]);
+        dt_preact(v[d], M, NX, R, pd[d]->dt_proj_w, pd[d]->dt_proj_b, E, q[d]);
+        for (int64_t i = 0; i < M * E; ++i) dl[d][i] = softplus(q[d][i]);
+        fvo_scan(u, dl[d], v[d], B, T, E, N, R, NX, pd[d]->A_log, d, NULL, s[d]);
+    }
+
+    /* adjoint of the output (gate, skip, repeat): dz, the skip part of dx, dD and gs */
+    for (int64_t b = 0; b < B; ++b) {
+        const int64_t ncell = masked ? K : h * w;
+        for (int64_t c = 0; c < ncell; ++c) {
+            int64_t t;
+            if (masked) t = rows[b * K + c];
+            else t = seq_pos(axis, h, w, c / w, c % w);
+            const int64_t off = (b * ncell + c) * E, mt = (b * T + t) * E;
+            output_token_adjoint(s[0] + mt, s[1] + mt, x + off, z + off, dout + off, pf, pb, E, g, dz + off,
+                                 dxs + off, dD);
+            for (int64_t e = 0; e < E; ++e) gs[mt + e] += g[e];
+        }
+    }
+
+    /* adjoints of both directions: scan, step size, x_proj */
+    for (int d = 0; d < 2; ++d) {
+        fvo_dir_grad *o = gd[d];
+        for (int64_t i = 0; i < NX * E; ++i) o->x_proj_w[i] = 0.0;
+        for (int64_t i = 0; i < E * R; ++i) o->dt_proj_w[i] = 0.0;
+        for (int64_t i = 0; i < E * N; ++i) o->A_log[i] = 0.0;
+        for (int64_t e = 0; e < E; ++e) o->dt_proj_b[e] = 0.0;
+        rc = scan_adjoint(u, dl[d], v[d], gs, B, T, E, N, R, NX, pd[d]->A_log, d, du, dd, dv[d], o->A_log);
+        if (rc) goto done;
+        /* dA -> dA_log: A = -exp(A_log), so dA/dA_log = A */
+        for (int64_t i = 0; i < E * N; ++i) o->A_log[i] *= -exp((double)pd[d]->A_log[i]);
+        step_size_adjoint(q[d], dd, v[d], M, NX, R, E, pd[d]->dt_proj_w, o->dt_proj_w, o->dt_proj_b, dv[d]);
+        xproj_adjoint(u, dv[d], M, NX, E, pd[d]->x_proj_w, o->x_proj_w, du);
+        for (int64_t e = 0; e < E; ++e) o->D[e] = dD[e];
+    }
+
+    /* adjoint of the pool */
+    for (int64_t b = 0; b < B; ++b) {
+        const int64_t ncell = masked ? K : h * w;
+        for (int64_t c = 0; c < ncell; ++c) {
+            int64_t t;
+            if (masked) t = rows[b * K + c];
+            else t = seq_pos(axis, h, w, c / w, c % w);
+            const int64_t off = (b * ncell + c) * E, mt = (b * T + t) * E;
+            for (int64_t e = 0; e < E; ++e) dx[off + e] = dxs[off + e] + du[mt + e] / (double)P;
+        }
+    }
+
+    if (st) {
+        if (st->gs) memcpy(st->gs, gs, me);
+        if (st->du) memcpy(st->du, du, me);
+        if (st->dv_f) memcpy(st->dv_f, dv[0], mx);
+        if (st->dv_b) memcpy(st->dv_b, dv[1], mx);
+    }
+
+done:
+    free(u); free(gs); free(du); free(dd); free(g); free(dxs); free(dD); free(rows);
+    for (int d = 0; d < 2; ++d) { free(v[d]); free(q[d]); free(dl[d]); free(s[d]); free(dv[d]); }
+    return rc;
+}

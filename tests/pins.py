@@ -496,6 +496,102 @@ def pin_layernorm_library(O):
         _close(O.layer(x, z, pf, pb, axis, ln=ln), ref, tol=1e-11, what="LayerNorm vs numpy")
 
 
+# ---------------------------------------------------------------- backward pass
+def _dyadic(a, step=2.0 ** -10, lim=3.9):
+    """Values on a grid of 2^-10 inside (-4, 4): a perturbation by a multiple of
+    2^-14 stays exactly representable in fp32, so finite differences of the
+    oracle see exactly the perturbation they ask for."""
+    return (np.round(np.clip(np.asarray(a, np.float64), -lim, lim) / step) * step).astype(np.float32)
+
+
+def _bwd_case(rng, axis, masked, B_=2, h=4, w=3, E=5, N=3, R=2):
+    pf = {k: _dyadic(v) for k, v in rand_dir(rng, E, N, R).items()}
+    pb = {k: _dyadic(v) for k, v in rand_dir(rng, E, N, R).items()}
+    if masked:
+        K = 7
+        idx = np.stack([rng.permutation(h * w)[:K] for _ in range(B_)]).astype(np.int32)
+        shape = (B_, K, E)
+    else:
+        idx = None
+        shape = (B_, h, w, E)
+    x = _dyadic(rng.standard_normal(shape))
+    z = _dyadic(rng.standard_normal(shape))
+    dout = rng.standard_normal(shape).astype(np.float32)
+    return pf, pb, x, z, dout, idx, (h, w)
+
+
+def _loss(O, x, z, dout, pf, pb, axis, idx, hw):
+    return float(np.sum(dout.astype(np.float64) * O.layer(x, z, pf, pb, axis, idx=idx, hw=hw)))
+
+
+def _perturbed(a, V, eps):
+    out = (a.astype(np.float64) + eps * V).astype(np.float32)
+    assert np.array_equal(out.astype(np.float64), a.astype(np.float64) + eps * V), "perturbation not exact"
+    return out
+
+
+def pin_bwd_finite_differences(O):
+    """Every gradient of L = sum(dout * out) (x, z, and the five parameters of
+    each direction) matches the central difference of the pinned forward
+    oracle along a random +-1 direction.  Inputs sit on a dyadic grid, so the
+    perturbed inputs are exact and the difference quotient carries only its
+    O(eps^2) truncation error (~1e-9 relative at eps = 2^-14)."""
+    eps = 2.0 ** -14
+    rng = np.random.default_rng(40)
+    cases = ((COLS, False), (ROWS, False), (NONE_ROWMAJOR, False), (NONE_COLMAJOR, False), (COLS, True), (ROWS, True))
+    for axis, masked in cases:
+        pf, pb, x, z, dout, idx, hw = _bwd_case(rng, axis, masked)
+        g = O.layer_bwd(x, z, dout, pf, pb, axis, idx=idx, hw=hw)
+        targets = [("x", None), ("z", None)] + [(d, k) for d in ("fwd", "bwd") for k in
+                                                 ("x_proj_w", "dt_proj_w", "dt_proj_b", "A_log", "D")]
+        for d, k in targets:
+            if k is None:
+                base = x if d == "x" else z
+                grad = g["dx"] if d == "x" else g["dz"]
+            else:
+                base = (pf if d == "fwd" else pb)[k]
+                grad = g[d][k]
+            V = rng.choice([-1.0, 1.0], size=base.shape)
+            L = []
+            for sgn in (1.0, -1.0):
+                arg = {"x": x, "z": z, "pf": dict(pf), "pb": dict(pb)}
+                pert = _perturbed(base, sgn * V, eps)
+                if k is None:
+                    arg[d] = pert
+                else:
+                    arg["pf" if d == "fwd" else "pb"][k] = pert
+                L.append(_loss(O, arg["x"], arg["z"], dout, arg["pf"], arg["pb"], axis, idx, hw))
+            fd = (L[0] - L[1]) / (2.0 * eps)
+            an = float(np.sum(grad * V))
+            scale = max(float(np.linalg.norm(grad)), 1e-30)
+            assert abs(fd - an) <= 1e-6 * scale, "axis %d masked %s: d/d%s %s: analytic %.12g, finite " \
+                "difference %.12g" % (axis, masked, d, k or "", an, fd)
+
+
+def pin_bwd_masked_equals_zero_filled(O):
+    """The masked backward pass equals the dense one on the zero-filled grid
+    (x, z and dout scattered into zeros): every parameter gradient agrees, and
+    dx, dz agree at the kept cells (an unkept cell has z = 0, so silu(0) = 0
+    removes it from the pooled adjoint and from dD)."""
+    rng = np.random.default_rng(41)
+    for axis in (COLS, ROWS):
+        pf, pb, x, z, dout, idx, (h, w) = _bwd_case(rng, axis, True)
+        B_, K, E = x.shape
+        dense = [np.zeros((B_, h * w, E), np.float32) for _ in range(3)]
+        for b in range(B_):
+            for arr, src in zip(dense, (x, z, dout)):
+                arr[b, idx[b]] = src[b]
+        xd, zd, dd = (a.reshape(B_, h, w, E) for a in dense)
+        gm = O.layer_bwd(x, z, dout, pf, pb, axis, idx=idx, hw=(h, w))
+        gd = O.layer_bwd(xd, zd, dd, pf, pb, axis)
+        for d in ("fwd", "bwd"):
+            for k in gm[d]:
+                _close(gm[d][k], gd[d][k], tol=1e-12, what="masked %s %s" % (d, k))
+        for name in ("dx", "dz"):
+            flat = gd[name].reshape(B_, h * w, E)
+            _close(gm[name], np.stack([flat[b, idx[b]] for b in range(B_)]), tol=1e-12, what="masked " + name)
+
+
 ALL_PINS = [
     pin_golden_worked_example,
     pin_geometric_series,
@@ -515,4 +611,6 @@ ALL_PINS = [
     pin_layernorm_moments,
     pin_layernorm_affine,
     pin_layernorm_library,
+    pin_bwd_finite_differences,
+    pin_bwd_masked_equals_zero_filled,
 ]

@@ -20,7 +20,8 @@ SRC = os.path.join(os.path.dirname(oracle.__file__), "fastvim_oracle.c")
 
 # (name, original text, replacement, occurrences)
 MUTANTS = [
-    ("A sign flipped", "const double A = -exp(", "const double A = exp(", 1),
+    ("A sign flipped", "const double A = -exp((double)A_log[e * N + n]);\n                    const double a = (reset",
+     "const double A = exp((double)A_log[e * N + n]);\n                    const double a = (reset", 1),
     ("output taken before the state update",
      "H[n] = a * H[n] + d * vt[R + n] * ut;\n                    acc += vt[R + N + n] * H[n];",
      "acc += vt[R + N + n] * H[n];\n                    H[n] = a * H[n] + d * vt[R + n] * ut;", 1),
@@ -29,7 +30,7 @@ MUTANTS = [
     ("input term dropped u", "H[n] = a * H[n] + d * vt[R + n] * ut;", "H[n] = a * H[n] + d * vt[R + n];", 1),
     ("B and C swapped", "H[n] = a * H[n] + d * vt[R + n] * ut;\n                    acc += vt[R + N + n] * H[n];",
      "H[n] = a * H[n] + d * vt[R + N + n] * ut;\n                    acc += vt[R + n] * H[n];", 1),
-    ("delta not in the decay", "exp(d * A)", "exp(A)", 1),
+    ("delta not in the decay", "? 0.0 : exp(d * A)", "? 0.0 : exp(A)", 1),
     ("backward scan not reversed", "reverse ? T - 1 - step : step", "step", 1),
     ("dense pool not normalised", "        for (int64_t k = 0; k < T * E; ++k) ub[k] /= (double)P;\n    }\n    return 0;\n}\n\n/*\n * Masked rows.",
      "    }\n    return 0;\n}\n\n/*\n * Masked rows.", 1),
@@ -38,13 +39,14 @@ MUTANTS = [
     ("only the forward D in the skip", "((double)pf->D[e] + (double)pb->D[e])", "((double)pf->D[e])", 1),
     ("gate uses sigmoid(-z)", "return q / (1.0 + exp(-q));", "return q / (1.0 + exp(q));", 1),
     ("softplus without log", "log1p(exp(-fabs(q)))", "exp(-fabs(q))", 1),
-    ("dt_proj transposed", "dt_proj_w[e * R + r]", "dt_proj_w[r * E + e]", 1),
-    ("x_proj transposed", "x_proj_w[o * E + e]", "x_proj_w[e * NX + o]", 1),
+    ("dt_proj transposed", "q += (double)dt_proj_w[e * R + r]", "q += (double)dt_proj_w[r * E + e]", 1),
+    ("x_proj transposed", "acc += (double)x_proj_w[o * E + e]", "acc += (double)x_proj_w[e * NX + o]", 1),
     ("ROWS pooling scans rows", "case FVO_ROWS: return j;", "case FVO_ROWS: return i;", 1),
     ("column-major uses w", "default: return j * h + i;", "default: return j * w + i;", 1),
     ("masked ROWS uses the row", "q / w : q % w", "q / w : q / w", 1),
     ("bias dropped from delta", "double q = (double)dt_proj_b[e];", "double q = 0.0;", 1),
-    ("low-rank delta reads B", "dt_proj_w[e * R + r] * v[m * NX + r]", "dt_proj_w[e * R + r] * v[m * NX + R + r]", 1),
+    ("low-rank delta reads B", "q += (double)dt_proj_w[e * R + r] * v[m * NX + r]",
+     "q += (double)dt_proj_w[e * R + r] * v[m * NX + R + r]", 1),
     ("repeat uses the wrong direction sum", "y[e] = sf[e] + sb[e] + skip;", "y[e] = sf[e] + sf[e] + skip;", 1),
     ("repeat reads the wrong scan row", "output_token(sf + (b * T + t) * E, sb + (b * T + t) * E, x + c",
      "output_token(sf + (b * T + t / 2) * E, sb + (b * T + t / 2) * E, x + c", 2),
@@ -54,6 +56,34 @@ MUTANTS = [
     ("LayerNorm scale and shift swapped", "* (double)ln_w[e] + (double)ln_b[e]", "* (double)ln_b[e] + (double)ln_w[e]", 1),
     ("reset ignored", "(reset && reset[t]) ? 0.0 : exp(d * A)", "exp(d * A)", 1),
     ("duplicate mask index accepted", "if (q < 0 || q >= h * w || seen[q])", "if (q < 0 || q >= h * w)", 1),
+    # backward pass
+    ("adjoint carried without the decay", "carry[n] = a * lam[n];", "carry[n] = lam[n];", 1),
+    ("adjoint decay term with the wrong sign", "dd += lam[n] * (A * a * prev + Bn * ut);",
+     "dd += lam[n] * (-A * a * prev + Bn * ut);", 1),
+    ("step-size adjoint without the decay term", "dd += lam[n] * (A * a * prev + Bn * ut);",
+     "dd += lam[n] * (Bn * ut);", 1),
+    ("dC from the previous state", "dv[m * NX + R + N + n] += g * Hs[k * N + n];",
+     "dv[m * NX + R + N + n] += g * prev;", 1),
+    ("dB without u", "dv[m * NX + R + n] += lam[n] * d * ut;", "dv[m * NX + R + n] += lam[n] * d;", 1),
+    ("dA without delta", "dA[e * N + n] += lam[n] * a * d * prev;", "dA[e * N + n] += lam[n] * a * prev;", 1),
+    ("dA_log chain factor dropped", "o->A_log[i] *= -exp((double)pd[d]->A_log[i]);", "o->A_log[i] *= -1.0;", 1),
+    ("softplus derivative taken as exp", "ddelta[m * E + e] * sigmoid(q[m * E + e])",
+     "ddelta[m * E + e] * exp(q[m * E + e])", 1),
+    ("dW_dt reads B", "dWdt[e * R + r] += dq * v[m * NX + r];", "dWdt[e * R + r] += dq * v[m * NX + R + r];", 1),
+    ("dt_proj adjoint does not reach dv", "dv[m * NX + r] += (double)dt_proj_w[e * R + r] * dq;", "(void)dv;", 1),
+    ("x_proj adjoint does not reach du", "du[m * E + e] += (double)x_proj_w[o * E + e] * dv[m * NX + o];",
+     "(void)du;", 1),
+    ("pool adjoint not normalised", "du[mt + e] / (double)P", "du[mt + e]", 1),
+    ("silu derivative without its second term", "sg * (1.0 + ze * (1.0 - sg))", "sg", 1),
+    ("dz without the skip", "const double y = sf[e] + sb[e] + Ds * xe;", "const double y = sf[e] + sb[e];", 1),
+    ("dD of the backward direction zero", "o->D[e] = dD[e];", "o->D[e] = d == 0 ? dD[e] : 0.0;", 1),
+    ("scan adjoint fed dout without the gate", "g[e] = de * silu(ze);", "g[e] = de;", 1),
+    ("backward direction's adjoint not reversed", "pd[d]->A_log, d, du, dd", "pd[d]->A_log, 0, du, dd", 1),
+    ("dx without the skip", "dx[off + e] = dxs[off + e] + du[mt + e] / (double)P;",
+     "dx[off + e] = du[mt + e] / (double)P;", 1),
+    ("du of the scan without B", "duk += lam[n] * d * Bn;", "duk += lam[n] * d;", 1),
+    ("adjoint uses the current state for the decay", "dd += lam[n] * (A * a * prev + Bn * ut);",
+     "dd += lam[n] * (A * a * Hs[k * N + n] + Bn * ut);", 1),
 ]
 
 
@@ -70,8 +100,11 @@ def test_mutant_is_caught(name, old, new, count, source, tmp_path):
     src = tmp_path / "mutant.c"
     src.write_text(mutated)
     lib = oracle.build(force=True, src=str(src), out=str(tmp_path / "libmutant.so"))
+    # one OpenMP thread per child: the pins are small, and parallel test workers
+    # each running a full team of spinning threads oversubscribe the cores
+    env = dict(os.environ, OMP_NUM_THREADS="1")
     proc = subprocess.run([sys.executable, "-c", _CHILD, lib], capture_output=True, text=True,
-                          timeout=300, cwd=os.path.dirname(os.path.dirname(SRC)))
+                          timeout=300, cwd=os.path.dirname(os.path.dirname(SRC)), env=env)
     if proc.returncode < 0:
         return  # the mutant crashed: caught
     assert proc.returncode == 0, proc.stderr[-2000:]
