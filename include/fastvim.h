@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define FASTVIM_ABI_VERSION 3
+#define FASTVIM_ABI_VERSION 4
 
 typedef enum fastvim_status {
     FASTVIM_OK = 0,
@@ -208,6 +208,64 @@ int fastvim_ssm_export(const fastvim_params *params, const fastvim_dims *dims, i
 
 /* Size in bytes of an export (0 if the layer does not have it). */
 size_t fastvim_ssm_export_bytes(const fastvim_dims *dims, int pool_axis, int what);
+
+/* ------------------------------------------------------------------ backward
+ * Gradients of the layer, for training (FastVim summary page, section 实验结果:
+ * the pooled layer is trained from scratch and in MAE pre-training).  For a
+ * scalar loss L whose gradient with respect to out is dout, fastvim_ssm_bwd
+ * computes dx = dL/dx, dz = dL/dz and dL/dparameter for both directions, by
+ * the chain rule through the forward steps in reverse:
+ *   g     = dout * silu(z)                          (dL/dy, y the pre-gate value)
+ *   dz    = dout * y * sigmoid(z) * (1 + z * (1 - sigmoid(z)))
+ *   gs    = g summed over the cells repeated from each scan position (the
+ *           repeat's adjoint), the adjoint input of both scans
+ *   each scan's adjoint, run backwards in time from the recomputed forward
+ *           states, gives du and dL/d(delta_lowrank, B_t, C_t), d dt_proj_w,
+ *           d dt_proj_b (through softplus) and d A_log (A = -exp(A_log))
+ *   d x_proj_w = sum over pooled tokens of dL/dv u^T, du += x_proj_w^T dL/dv
+ *   dD_fwd = dD_bwd = sum over all cells of g * x
+ *   dx    = g * (D_fwd + D_bwd) + du[b, t(cell), :] / P   (the pool's adjoint)
+ * The forward pass is recomputed inside the call (pooled tokens, projections,
+ * states), so only x, z and dout are needed.  Arithmetic is fp32; every sum
+ * has a fixed order (no atomics), so results are run-to-run identical.
+ *
+ * Supported: pooled layers (COLS or ROWS, dense or masked) with T <= 128 scan
+ * steps and the limits of the forward call; FASTVIM_ERR_UNSUPPORTED for
+ * unpooled layers, longer scans, and the flags FASTVIM_FLAG_FUSED and
+ * FASTVIM_FLAG_POST_NORM (0 and FASTVIM_FLAG_STAGED run the same kernels). */
+
+/* Gradients of one direction's parameters: fp32 device buffers shaped like
+ * the parameters, 4-byte aligned, overwritten by the call. */
+typedef struct fastvim_dir_grads {
+    float *x_proj_w;  /* (R + 2N, E) */
+    float *dt_proj_w; /* (E, R) */
+    float *dt_proj_b; /* (E) */
+    float *A_log;     /* (E, N) */
+    float *D;         /* (E) */
+} fastvim_dir_grads;
+
+typedef struct fastvim_grads {
+    fastvim_dir_grads fwd, bwd;
+} fastvim_grads;
+
+/* Bytes of workspace fastvim_ssm_bwd needs (0 if the sizes are invalid or
+ * the backward pass does not support them): about 4 * B * T * (8E + 4(R + 2N))
+ * plus per-image and per-chunk partial sums (at B = 128, h = w = 128, E = 384,
+ * R = 12: about 270 MB). */
+size_t fastvim_ssm_bwd_workspace_bytes(const fastvim_dims *dims, int pool_axis);
+
+/* The backward pass.  x, z, dout, dx, dz: like x of fastvim_ssm_fwd (same
+ * shape, element type and 16-byte alignment); params as for the forward call,
+ * its workspace at least fastvim_ssm_bwd_workspace_bytes (256-byte aligned);
+ * mask_idx as for the forward call (a token with an invalid index gets NaN in
+ * dx and dz and takes no part in the pooled sums).  dx, dz, the workspace and
+ * the ten gradient buffers must overlap neither each other nor any input or
+ * parameter (FASTVIM_ERR_OVERLAP).  B == 0 writes zero gradients.  Errors as
+ * fastvim_ssm_fwd, plus FASTVIM_ERR_NULL for a NULL grads or gradient buffer.
+ * Enqueues its kernels on stream and returns. */
+int fastvim_ssm_bwd(const void *x, const void *z, const void *dout, const fastvim_params *params,
+                    const fastvim_dims *dims, int pool_axis, const int32_t *mask_idx, void *dx, void *dz,
+                    const fastvim_grads *grads, void *stream);
 
 /* Measurement aid, not part of the layer: copy `bytes` bytes from src to dst
  * (device memory, both 16-byte aligned, bytes a multiple of 16, no overlap)

@@ -64,9 +64,18 @@ class Params(ctypes.Structure):
                 ("reserved2", ctypes.c_uint32)]
 
 
+class DirGrads(ctypes.Structure):
+    _fields_ = [(f, ctypes.c_void_p) for f in DIR_FIELDS]
+
+
+class Grads(ctypes.Structure):
+    _fields_ = [("fwd", DirGrads), ("bwd", DirGrads)]
+
+
 EXPORTED_SYMBOLS = (
     "fastvim_ssm_workspace_bytes", "fastvim_ssm_fwd", "fastvim_ssm_stage", "fastvim_ssm_export",
-    "fastvim_ssm_export_bytes", "fastvim_calib_copy", "fastvim_status_string", "fastvim_abi_version",
+    "fastvim_ssm_export_bytes", "fastvim_ssm_bwd_workspace_bytes", "fastvim_ssm_bwd", "fastvim_calib_copy",
+    "fastvim_status_string", "fastvim_abi_version",
 )
 
 _lock = threading.Lock()
@@ -93,6 +102,10 @@ def lib():
             L.fastvim_ssm_export.restype = ci
             L.fastvim_ssm_export_bytes.argtypes = [PD, ci, ci]
             L.fastvim_ssm_export_bytes.restype = sz
+            L.fastvim_ssm_bwd_workspace_bytes.argtypes = [PD, ci]
+            L.fastvim_ssm_bwd_workspace_bytes.restype = sz
+            L.fastvim_ssm_bwd.argtypes = [vp, vp, vp, PP, PD, ci, vp, vp, vp, ctypes.POINTER(Grads), vp]
+            L.fastvim_ssm_bwd.restype = ci
             L.fastvim_calib_copy.argtypes = [vp, vp, sz, vp]
             L.fastvim_calib_copy.restype = ci
             L.fastvim_status_string.argtypes = [ci]
@@ -109,6 +122,10 @@ def make_dims(B, h, w, E, N=16, R=12, K=0, io_dtype=F32) -> Dims:
 
 def workspace_bytes(dims: Dims, pool_axis: int) -> int:
     return int(lib().fastvim_ssm_workspace_bytes(ctypes.byref(dims), pool_axis))
+
+
+def bwd_workspace_bytes(dims: Dims, pool_axis: int) -> int:
+    return int(lib().fastvim_ssm_bwd_workspace_bytes(ctypes.byref(dims), pool_axis))
 
 
 def _io_dtype(t: torch.Tensor) -> int:
@@ -129,6 +146,45 @@ def _stream(stream) -> int:
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
+def _layer_dims(x, z, params, mask_idx, hw) -> Dims:
+    io = _io_dtype(x)
+    if z.dtype != x.dtype or z.shape != x.shape:
+        raise ValueError("z must match x in shape and dtype")
+    E = x.shape[-1]
+    pf = params["fwd"]
+    NX = pf["x_proj_w"].shape[0]
+    N = pf["A_log"].shape[1]
+    R = NX - 2 * N
+    if mask_idx is None:
+        if x.dim() != 4:
+            raise ValueError("dense x must be (B, h, w, E)")
+        B, h, w, _ = x.shape
+        K = 0
+    else:
+        if x.dim() != 3 or hw is None:
+            raise ValueError("masked x must be (B, K, E) with hw=(h, w)")
+        B, K, _ = x.shape
+        h, w = hw
+        if mask_idx.dtype != torch.int32 or tuple(mask_idx.shape) != (B, K):
+            raise ValueError("mask_idx must be int32 (B, K)")
+    return make_dims(B, h, w, E, N, R, K, io)
+
+
+def _dir_params(params, keep):
+    dirs = []
+    for name in ("fwd", "bwd"):
+        p = params[name]
+        ts = []
+        for f in DIR_FIELDS:
+            t = p[f]
+            if t.dtype != torch.float32 or not t.is_contiguous():
+                raise ValueError("parameter %s.%s must be contiguous float32" % (name, f))
+            ts.append(t)
+        keep.extend(ts)
+        dirs.append(DirParams(*[t.data_ptr() for t in ts]))
+    return dirs
+
+
 class SSMCall:
     """One prepared layer call: sizes, parameter pointers, workspace and out.
 
@@ -142,42 +198,12 @@ class SSMCall:
                  pool_axis: int, mask_idx: Optional[torch.Tensor] = None, hw: Optional[Tuple[int, int]] = None,
                  out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
                  flags: int = 0, ln: Optional[Dict[str, object]] = None):
-        io = _io_dtype(x)
-        if z.dtype != x.dtype or z.shape != x.shape:
-            raise ValueError("z must match x in shape and dtype")
-        E = x.shape[-1]
-        pf = params["fwd"]
-        NX = pf["x_proj_w"].shape[0]
-        N = pf["A_log"].shape[1]
-        R = NX - 2 * N
-        if mask_idx is None:
-            if x.dim() != 4:
-                raise ValueError("dense x must be (B, h, w, E)")
-            B, h, w, _ = x.shape
-            K = 0
-        else:
-            if x.dim() != 3 or hw is None:
-                raise ValueError("masked x must be (B, K, E) with hw=(h, w)")
-            B, K, _ = x.shape
-            h, w = hw
-            if mask_idx.dtype != torch.int32 or tuple(mask_idx.shape) != (B, K):
-                raise ValueError("mask_idx must be int32 (B, K)")
-        self.dims = make_dims(B, h, w, E, N, R, K, io)
+        self.dims = _layer_dims(x, z, params, mask_idx, hw)
         self.pool_axis = pool_axis
         self.x, self.z, self.mask_idx = x, z, mask_idx
         self.out = torch.empty_like(x) if out is None else out
         self._keep = []
-        dirs = []
-        for name in ("fwd", "bwd"):
-            p = params[name]
-            ts = []
-            for f in DIR_FIELDS:
-                t = p[f]
-                if t.dtype != torch.float32 or not t.is_contiguous():
-                    raise ValueError("parameter %s.%s must be contiguous float32" % (name, f))
-                ts.append(t)
-            self._keep.extend(ts)
-            dirs.append(DirParams(*[t.data_ptr() for t in ts]))
+        dirs = _dir_params(params, self._keep)
         nbytes = workspace_bytes(self.dims, pool_axis)
         if workspace is None:
             workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=x.device)
@@ -232,6 +258,63 @@ def ssm_fwd(x, z, params, pool_axis=POOL_COLS, mask_idx=None, hw=None, out=None,
     """The pooled bidirectional selective-scan layer; returns out."""
     return SSMCall(x, z, params, pool_axis, mask_idx=mask_idx, hw=hw, out=out, workspace=workspace,
                    flags=flags, ln=ln).run(stream)
+
+
+class BwdCall:
+    """One prepared backward call (gradients of sum(dout * out)).
+
+    Arguments as SSMCall, plus dout shaped like x.  dx, dz (like x) and the
+    gradients grads = {"fwd": {...}, "bwd": {...}} (fp32, shaped like the
+    parameters) are allocated unless given.  run() returns
+    {"dx": dx, "dz": dz, "fwd": {...}, "bwd": {...}}."""
+
+    def __init__(self, x: torch.Tensor, z: torch.Tensor, dout: torch.Tensor,
+                 params: Dict[str, Dict[str, torch.Tensor]], pool_axis: int,
+                 mask_idx: Optional[torch.Tensor] = None, hw: Optional[Tuple[int, int]] = None,
+                 dx: Optional[torch.Tensor] = None, dz: Optional[torch.Tensor] = None,
+                 grads: Optional[Dict[str, Dict[str, torch.Tensor]]] = None,
+                 workspace: Optional[torch.Tensor] = None, flags: int = 0):
+        self.dims = _layer_dims(x, z, params, mask_idx, hw)
+        if dout.dtype != x.dtype or dout.shape != x.shape:
+            raise ValueError("dout must match x in shape and dtype")
+        self.pool_axis = pool_axis
+        self.x, self.z, self.dout, self.mask_idx = x, z, dout, mask_idx
+        self.dx = torch.empty_like(x) if dx is None else dx
+        self.dz = torch.empty_like(x) if dz is None else dz
+        self._keep = []
+        dirs = _dir_params(params, self._keep)
+        if grads is None:
+            grads = {d: {f: torch.empty_like(params[d][f]) for f in DIR_FIELDS} for d in ("fwd", "bwd")}
+        self.grads = grads
+        gd = []
+        for d in ("fwd", "bwd"):
+            for f in DIR_FIELDS:
+                t = grads[d][f]
+                if t.dtype != torch.float32 or not t.is_contiguous() or t.shape != params[d][f].shape:
+                    raise ValueError("gradient %s.%s must be contiguous float32 shaped like the parameter" % (d, f))
+            gd.append(DirGrads(*[grads[d][f].data_ptr() for f in DIR_FIELDS]))
+        self.cgrads = Grads(gd[0], gd[1])
+        nbytes = bwd_workspace_bytes(self.dims, pool_axis)
+        if workspace is None:
+            workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=x.device)
+        self.workspace = workspace
+        self.params = Params(dirs[0], dirs[1], workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                             flags, 0, None, None, 0.0, 0)
+
+    def run(self, stream=None) -> Dict[str, object]:
+        st = lib().fastvim_ssm_bwd(_ptr(self.x), _ptr(self.z), _ptr(self.dout), ctypes.byref(self.params),
+                                   ctypes.byref(self.dims), self.pool_axis, _ptr(self.mask_idx), _ptr(self.dx),
+                                   _ptr(self.dz), ctypes.byref(self.cgrads), _stream(stream))
+        if st:
+            raise FastVimError(st, "fastvim_ssm_bwd")
+        return {"dx": self.dx, "dz": self.dz, "fwd": self.grads["fwd"], "bwd": self.grads["bwd"]}
+
+
+def ssm_bwd(x, z, dout, params, pool_axis=POOL_COLS, mask_idx=None, hw=None, workspace=None, stream=None,
+            flags=0):
+    """Gradients of the layer; returns {"dx", "dz", "fwd": {...}, "bwd": {...}}."""
+    return BwdCall(x, z, dout, params, pool_axis, mask_idx=mask_idx, hw=hw, workspace=workspace,
+                   flags=flags).run(stream)
 
 
 def calib_copy(dst: torch.Tensor, src: torch.Tensor, stream=None) -> None:

@@ -16,7 +16,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfastvim.so")
-SOURCES = ["api.cpp", "pool.hip", "proj.hip", "scan.hip", "epilogue.hip", "fused.hip", "calib.hip", "epilogue_norm.hip"]
+SOURCES = ["api.cpp", "pool.hip", "proj.hip", "scan.hip", "epilogue.hip", "fused.hip", "calib.hip", "epilogue_norm.hip",
+           "scan_bwd.hip", "bwd.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

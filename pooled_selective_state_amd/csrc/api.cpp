@@ -4,7 +4,7 @@
 #include <cstdint>
 #include <cstring>
 
-#include "fastvim_internal.h"
+#include "bwd_internal.h"
 
 namespace fastvim {
 namespace {
@@ -138,6 +138,103 @@ size_t export_bytes(const Geom& g, int what) {
     }
 }
 
+// The backward pass covers the pooled layer (dense or masked) without the
+// post-SSM norm, with scans of at most kBwdTMax steps.
+bool bwd_supported(const Geom& g) { return g.pooled && g.T <= kBwdTMax; }
+
+struct Span {
+    const void* p;
+    size_t n;
+};
+
+// Full validation of a backward call.  *empty is set for B == 0.
+int validate_bwd(const void* x, const void* z, const void* dout, const fastvim_params* prm, const fastvim_dims* d,
+                 int axis, const int32_t* idx, const void* dx, const void* dz, const fastvim_grads* gr, Geom* g,
+                 BwdWorkspace* ws, bool* empty) {
+    if (!prm) return FASTVIM_ERR_NULL;
+    const uint32_t known = FASTVIM_FLAG_STAGED | FASTVIM_FLAG_FUSED | FASTVIM_FLAG_POST_NORM;
+    if (prm->flags & ~known) return FASTVIM_ERR_ARG;
+    if (prm->flags & (FASTVIM_FLAG_FUSED | FASTVIM_FLAG_POST_NORM)) return FASTVIM_ERR_UNSUPPORTED;
+    int st = resolve_geom(d, axis, g);
+    if (st) return st;
+    if (!bwd_supported(*g)) return FASTVIM_ERR_UNSUPPORTED;
+    if (!g->masked && idx) return FASTVIM_ERR_ARG;
+    if (!gr) return FASTVIM_ERR_NULL;
+    const fastvim_dir_grads* gd[2] = {&gr->fwd, &gr->bwd};
+    const size_t gsz[5] = {(size_t)(g->NX * g->E), (size_t)(g->E * g->R), (size_t)g->E, (size_t)(g->E * g->N),
+                           (size_t)g->E};
+    Span gs[10];
+    for (int k = 0; k < 2; ++k) {
+        const float* ps[5] = {gd[k]->x_proj_w, gd[k]->dt_proj_w, gd[k]->dt_proj_b, gd[k]->A_log, gd[k]->D};
+        for (int i = 0; i < 5; ++i) {
+            if (!ps[i]) return FASTVIM_ERR_NULL;
+            if (!aligned(ps[i], 4)) return FASTVIM_ERR_ALIGN;
+            gs[5 * k + i] = Span{ps[i], gsz[i] * sizeof(float)};
+        }
+    }
+    for (int i = 0; i < 10; ++i)
+        for (int j = i + 1; j < 10; ++j)
+            if (overlap(gs[i].p, gs[i].n, gs[j].p, gs[j].n)) return FASTVIM_ERR_OVERLAP;
+    *empty = g->B == 0;
+    if (*empty) return FASTVIM_OK;
+    if (!x || !z || !dout || !dx || !dz || (g->masked && !idx)) return FASTVIM_ERR_NULL;
+    if ((st = check_dir(prm->fwd)) || (st = check_dir(prm->bwd))) return st;
+    if (!prm->workspace) return FASTVIM_ERR_WORKSPACE;
+    if (!aligned(x, 16) || !aligned(z, 16) || !aligned(dout, 16) || !aligned(dx, 16) || !aligned(dz, 16) ||
+        !aligned(prm->workspace, 256) || (idx && !aligned(idx, 4)))
+        return FASTVIM_ERR_ALIGN;
+    const size_t need = bwd_workspace_layout(*g, nullptr, nullptr);
+    if (prm->workspace_bytes < need) return FASTVIM_ERR_WORKSPACE;
+    const size_t io = (size_t)(g->B * (g->masked ? g->K : g->h * g->w) * g->E) * (g->io == FASTVIM_F32 ? 4 : 2);
+    // outputs (dx, dz, the workspace and every gradient) overlap neither each
+    // other nor an input; parameters count as inputs
+    Span ins[13] = {{x, io}, {z, io}, {dout, io}};
+    int nin = 3;
+    for (const fastvim_dir_params* pd : {&prm->fwd, &prm->bwd}) {
+        const float* ps[5] = {pd->x_proj_w, pd->dt_proj_w, pd->dt_proj_b, pd->A_log, pd->D};
+        for (int i = 0; i < 5; ++i) ins[nin++] = Span{ps[i], gsz[i] * sizeof(float)};
+    }
+    Span outs[13] = {{dx, io}, {dz, io}, {prm->workspace, need}};
+    for (int i = 0; i < 10; ++i) outs[3 + i] = gs[i];
+    for (int i = 0; i < 13; ++i) {
+        for (int j = 0; j < 13; ++j)
+            if (overlap(outs[i].p, outs[i].n, ins[j].p, ins[j].n)) return FASTVIM_ERR_OVERLAP;
+        for (int j = i + 1; j < 13; ++j)
+            if (overlap(outs[i].p, outs[i].n, outs[j].p, outs[j].n)) return FASTVIM_ERR_OVERLAP;
+    }
+    bwd_workspace_layout(*g, prm->workspace, ws);
+    return FASTVIM_OK;
+}
+
+int run_bwd(const Geom& g, const void* x, const void* z, const void* dout, const fastvim_params& p,
+            const int32_t* idx, void* dx, void* dz, const fastvim_grads& gr, const BwdWorkspace& ws, hipStream_t s) {
+    hipError_t e = hipSuccess;
+    auto ok = [&](hipError_t r) {
+        if (e == hipSuccess) e = r;
+        return e == hipSuccess;
+    };
+    if (g.masked && !ok(launch_mask_rows(g, idx, ws.fwd, s))) return FASTVIM_ERR_HIP;
+    if (!ok(launch_bwd_pool(g, x, z, dout, ws, s))) return FASTVIM_ERR_HIP;
+    if (!ok(launch_proj(g, x, p, ws.fwd, s))) return FASTVIM_ERR_HIP;
+    BwdScanArgs a{ws.fwd.xdbl, ws.fwd.u, ws.gs, p.fwd, p.bwd, ws.fwd.s_f, ws.fwd.s_b, ws.du_f, ws.du_b, ws.dvp,
+                  ws.dAp, ws.dWdtp, ws.dbp, g.B, g.T, g.E, (int)g.R, (int)g.NX, (int)ws.G};
+    if (!ok(launch_scan_bwd(a, s)) || !ok(launch_bwd_dv(g, ws, s)) || !ok(launch_bwd_du(g, p, ws, s)) ||
+        !ok(launch_bwd_dwx(g, ws, s)))
+        return FASTVIM_ERR_HIP;
+    const fastvim_dir_grads* gd[2] = {&gr.fwd, &gr.bwd};
+    const int64_t E = g.E, NX = g.NX, R = g.R, B = g.B;
+    for (int d = 0; d < 2; ++d) {
+        if (!ok(launch_colsum(ws.dWxp + d * NX * E, ws.MC, NX * E, 2 * NX * E, gd[d]->x_proj_w, nullptr, ws.tmp, s)) ||
+            !ok(launch_colsum(ws.dAp + d * B * E * 16, B, E * 16, E * 16, gd[d]->A_log, nullptr, ws.tmp, s)) ||
+            !ok(launch_colsum(ws.dWdtp + d * B * E * R, B, E * R, E * R, gd[d]->dt_proj_w, nullptr, ws.tmp, s)) ||
+            !ok(launch_colsum(ws.dbp + d * B * E, B, E, E, gd[d]->dt_proj_b, nullptr, ws.tmp, s)))
+            return FASTVIM_ERR_HIP;
+    }
+    if (!ok(launch_colsum(ws.dDp, B * g.T, E, E, gr.fwd.D, gr.bwd.D, ws.tmp, s))) return FASTVIM_ERR_HIP;
+    if (!ok(launch_bwd_epilogue(g, x, z, dout, p, ws, dx, dz, s))) return FASTVIM_ERR_HIP;
+    return FASTVIM_OK;
+}
+
 }  // namespace
 
 size_t workspace_layout(const Geom& g, void* base, Workspace* ws) {
@@ -164,6 +261,66 @@ size_t workspace_layout(const Geom& g, void* base, Workspace* ws) {
         ws->rows = g.masked ? reinterpret_cast<int32_t*>(c + o_rows) : nullptr;
         ws->bad = g.masked ? reinterpret_cast<int32_t*>(c + o_bad) : nullptr;
         ws->sync = reinterpret_cast<unsigned*>(c + o_sync);
+    }
+    return off;
+}
+
+size_t bwd_workspace_layout(const Geom& g, void* base, BwdWorkspace* ws) {
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off = align256(off + bytes);
+        return o;
+    };
+    const int64_t B = g.B, T = g.T, E = g.E, NX = g.NX, R = g.R, M = g.B * g.T;
+    const int64_t G = (E + kBwdCh - 1) / kBwdCh, S = bwd_rmax(R) + 32;
+    const int64_t MC = (M + kBwdTokChunk - 1) / kBwdTokChunk;
+    const size_t bte = (size_t)(M * E) * sizeof(float);
+    const size_t o_u = take(bte);
+    const size_t o_x = take((size_t)(M * 2 * NX) * sizeof(float));
+    const size_t o_sf = take(bte), o_sb = take(bte);
+    const size_t o_rows = g.masked ? take((size_t)(B * g.K) * sizeof(int32_t)) : 0;
+    const size_t o_bad = g.masked ? take((size_t)B * sizeof(int32_t)) : 0;
+    const size_t o_gs = take(bte), o_dDp = take(bte), o_duf = take(bte), o_dub = take(bte), o_du = take(bte);
+    const size_t o_dvp = take((size_t)(2 * B * G * T * S) * sizeof(float));
+    const size_t o_dv = take((size_t)(M * 2 * NX) * sizeof(float));
+    const size_t o_dAp = take((size_t)(2 * B * E * 16) * sizeof(float));
+    const size_t o_dWdtp = take((size_t)(2 * B * E * R) * sizeof(float));
+    const size_t o_dbp = take((size_t)(2 * B * E) * sizeof(float));
+    const size_t o_dWxp = take((size_t)(MC * 2 * NX * E) * sizeof(float));
+    auto stage1 = [](int64_t rows, int64_t cols) {
+        return rows > kColRowsPerBlock ? (rows + kColRowsPerBlock - 1) / kColRowsPerBlock * cols : int64_t(0);
+    };
+    int64_t tmpf = 1;
+    for (int64_t v : {stage1(M, E), stage1(B, E * 16), stage1(B, E * R), stage1(B, E), stage1(MC, NX * E)})
+        tmpf = v > tmpf ? v : tmpf;
+    const size_t o_tmp = take((size_t)tmpf * sizeof(float));
+    if (base && ws) {
+        char* c = static_cast<char*>(base);
+        auto f = [&](size_t o) { return reinterpret_cast<float*>(c + o); };
+        ws->fwd.u = f(o_u);
+        ws->fwd.xdbl = f(o_x);
+        ws->fwd.s_f = f(o_sf);
+        ws->fwd.s_b = f(o_sb);
+        ws->fwd.rows = g.masked ? reinterpret_cast<int32_t*>(c + o_rows) : nullptr;
+        ws->fwd.bad = g.masked ? reinterpret_cast<int32_t*>(c + o_bad) : nullptr;
+        ws->fwd.sync = nullptr;
+        ws->gs = f(o_gs);
+        ws->dDp = f(o_dDp);
+        ws->du_f = f(o_duf);
+        ws->du_b = f(o_dub);
+        ws->du = f(o_du);
+        ws->dvp = f(o_dvp);
+        ws->dv = f(o_dv);
+        ws->dAp = f(o_dAp);
+        ws->dWdtp = f(o_dWdtp);
+        ws->dbp = f(o_dbp);
+        ws->dWxp = f(o_dWxp);
+        ws->tmp = f(o_tmp);
+        ws->G = G;
+        ws->S = S;
+        ws->MC = MC;
+        ws->tmp_floats = tmpf;
     }
     return off;
 }
@@ -244,6 +401,33 @@ int fastvim_ssm_export(const fastvim_params* params, const fastvim_dims* dims, i
     }
     hipError_t e = hipMemcpyAsync(dst, src, n, hipMemcpyDeviceToDevice, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? FASTVIM_OK : FASTVIM_ERR_HIP;
+}
+
+size_t fastvim_ssm_bwd_workspace_bytes(const fastvim_dims* dims, int pool_axis) {
+    Geom g;
+    if (resolve_geom(dims, pool_axis, &g) != FASTVIM_OK || !bwd_supported(g)) return 0;
+    return bwd_workspace_layout(g, nullptr, nullptr);
+}
+
+int fastvim_ssm_bwd(const void* x, const void* z, const void* dout, const fastvim_params* params,
+                    const fastvim_dims* dims, int pool_axis, const int32_t* mask_idx, void* dx, void* dz,
+                    const fastvim_grads* grads, void* stream) {
+    Geom g;
+    BwdWorkspace ws;
+    bool empty = false;
+    const int st = validate_bwd(x, z, dout, params, dims, pool_axis, mask_idx, dx, dz, grads, &g, &ws, &empty);
+    if (st) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (empty) {  // no tokens: every gradient is zero
+        const int64_t n[5] = {g.NX * g.E, g.E * g.R, g.E, g.E * g.N, g.E};
+        for (const fastvim_dir_grads* gd : {&grads->fwd, &grads->bwd}) {
+            float* ps[5] = {gd->x_proj_w, gd->dt_proj_w, gd->dt_proj_b, gd->A_log, gd->D};
+            for (int i = 0; i < 5; ++i)
+                if (launch_fill_zero(ps[i], n[i], s) != hipSuccess) return FASTVIM_ERR_HIP;
+        }
+        return FASTVIM_OK;
+    }
+    return run_bwd(g, x, z, dout, *params, mask_idx, dx, dz, *grads, ws, s);
 }
 
 int fastvim_calib_copy(void* dst, const void* src, size_t bytes, void* stream) {

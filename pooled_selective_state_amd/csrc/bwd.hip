@@ -1,0 +1,505 @@
+// Backward pass of the pooled layer, apart from the scan adjoint
+// (scan_bwd.hip): the gradient of L = sum(dout * out) with respect to x, z
+// and both directions' parameters, taken through the forward steps in reverse
+// (FastVim summary page, gptget.net, arXiv 2502.00594, section 方法详解
+// bullets 2-5 for the forward steps; the page's 实验结果 section for the
+// training runs the gradient serves).  With y = s_fwd + s_bwd + (D_fwd + D_bwd) x
+// and out = y silu(z):
+//   g   = dL/dy = dout silu(z)
+//   dz  = dout y silu'(z),   silu'(q) = sigmoid(q) (1 + q (1 - sigmoid(q)))
+//   gs[b, t, e] = sum of g over the cells repeated from scan position t (the
+//               repeat's adjoint), the same for both scan directions
+//   dD_fwd = dD_bwd = sum over all cells of g x
+//   dx  = g (D_fwd + D_bwd) + du[b, t(cell), e] / P   (the pool's adjoint)
+// and du, the gradient of the pooled tokens, collects the scan adjoint of
+// both directions and the x_proj adjoint du += x_proj_w^T dv.
+//
+// Kernels here, in launch order:
+//   pass 1   (x, z, dout read once)  pooled tokens u (the scan input, which
+//            the backward recomputes), gs and per-row partials of dD;
+//   dv       dL/dv from the scan adjoint's channel-group partials;
+//   du       du = du_fwd + du_bwd + x_proj_w^T dv for both directions;
+//   dwx      per-chunk partials of d x_proj_w = sum_m dv[m] u[m]^T;
+//   colsum   fixed-order column sums: parameter gradients from per-image or
+//            per-chunk partials;
+//   pass 2   (x, z, dout read again, dx and dz written once).
+// Passes 1 and 2 move the full-resolution tensors and bound the pass; both
+// stream 16-byte vectors with every load issued before any arithmetic, like
+// the forward pool and epilogue kernels.
+#include "bwd_internal.h"
+
+namespace fastvim {
+namespace {
+
+__device__ __forceinline__ float sigmoid_f(float q) { return __builtin_amdgcn_rcpf(1.f + __expf(-q)); }
+
+// ------------------------------------------------------------------ pass 1
+// One workgroup per pooled token (b, t): G groups of VE vector lanes, lane c
+// owning the 16-byte column [c V, c V + V) of E, group g taking the pooled
+// positions p = g, g + G, ...; the G partial sums are added through LDS in a
+// fixed order.
+template <class IO>
+__global__ void __launch_bounds__(1024)
+bwd_pool_dense_kernel(const typename IO::elem* __restrict__ x, const typename IO::elem* __restrict__ z,
+                      const typename IO::elem* __restrict__ dout, float* __restrict__ u, float* __restrict__ gs,
+                      float* __restrict__ dDp, int64_t T, int64_t P, int VE, int G, int64_t E, int64_t img_stride,
+                      int64_t t_stride, int64_t p_stride, float inv_p) {
+    constexpr int V = IO::V;
+    constexpr int kD = 4;  // pooled positions in flight per lane
+    using raw = typename IO::raw;
+    extern __shared__ float red[];  // [3][G][VE * V]
+    const int64_t bt = blockIdx.x;
+    const int64_t b = bt / T, t = bt - b * T;
+    const int tid = threadIdx.x;
+    const int c = tid % VE, g = tid / VE;
+    const int width = VE * V;
+    if (g < G) {
+        float au[V], ag[V], ad[V];
+#pragma unroll
+        for (int k = 0; k < V; ++k) au[k] = ag[k] = ad[k] = 0.f;
+        const int64_t off = b * img_stride + t * t_stride + (int64_t)c * V;
+        for (int64_t p0 = g; p0 < P; p0 += kD * G) {
+            raw xr[kD], zr[kD], dr[kD];
+#pragma unroll
+            for (int i = 0; i < kD; ++i) {
+                const int64_t p = p0 + (int64_t)i * G;
+                if (p < P) {
+                    const int64_t o = off + p * p_stride;
+                    xr[i] = load_raw<false>(x + o);
+                    zr[i] = load_raw<false>(z + o);
+                    dr[i] = load_raw<false>(dout + o);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < kD; ++i) {
+                if (p0 + (int64_t)i * G < P) {
+#pragma unroll
+                    for (int k = 0; k < V; ++k) {
+                        const float xv = raw_at(xr[i], k), zv = raw_at(zr[i], k);
+                        const float gv = raw_at(dr[i], k) * zv * sigmoid_f(zv);
+                        au[k] += xv;
+                        ag[k] += gv;
+                        ad[k] = fmaf(gv, xv, ad[k]);
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < V; ++k) {
+            const int64_t o = ((int64_t)g * VE + c) * V + k;
+            red[o] = au[k];
+            red[(int64_t)G * width + o] = ag[k];
+            red[2 * (int64_t)G * width + o] = ad[k];
+        }
+    }
+    __syncthreads();
+    for (int q = tid; q < width; q += blockDim.x) {
+        float su = red[q], sg = red[G * width + q], sd = red[2 * G * width + q];
+        for (int gg = 1; gg < G; ++gg) {
+            su += red[gg * width + q];
+            sg += red[(G + gg) * width + q];
+            sd += red[(2 * G + gg) * width + q];
+        }
+        u[bt * E + q] = su * inv_p;
+        gs[bt * E + q] = sg;
+        dDp[bt * E + q] = sd;
+    }
+}
+
+// Masked pass 1: workgroup (b, t) takes the kept tokens whose row is t; the
+// pooled sum is divided by the fixed row length P.  Tokens with an invalid
+// mask entry (row -1) belong to no row.
+template <class IO>
+__global__ void __launch_bounds__(1024)
+bwd_pool_masked_kernel(const typename IO::elem* __restrict__ x, const typename IO::elem* __restrict__ z,
+                       const typename IO::elem* __restrict__ dout, const int32_t* __restrict__ rows,
+                       float* __restrict__ u, float* __restrict__ gs, float* __restrict__ dDp, int64_t T, int64_t K,
+                       int VE, int G, int64_t E, float inv_p) {
+    constexpr int V = IO::V;
+    extern __shared__ float red[];  // [3][G][VE * V]
+    const int64_t bt = blockIdx.x;
+    const int64_t b = bt / T, t = bt - b * T;
+    const int tid = threadIdx.x;
+    const int c = tid % VE, g = tid / VE;
+    const int width = VE * V;
+    if (g < G) {
+        float au[V], ag[V], ad[V];
+#pragma unroll
+        for (int k = 0; k < V; ++k) au[k] = ag[k] = ad[k] = 0.f;
+        for (int64_t k = g; k < K; k += G) {
+            if (rows[b * K + k] != t) continue;
+            const int64_t o = (b * K + k) * E + (int64_t)c * V;
+            float xv[V], zv[V], dv[V];
+            load_vec<false>(x + o, xv);
+            load_vec<false>(z + o, zv);
+            load_vec<false>(dout + o, dv);
+#pragma unroll
+            for (int q = 0; q < V; ++q) {
+                const float gv = dv[q] * zv[q] * sigmoid_f(zv[q]);
+                au[q] += xv[q];
+                ag[q] += gv;
+                ad[q] = fmaf(gv, xv[q], ad[q]);
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < V; ++k) {
+            const int64_t o = ((int64_t)g * VE + c) * V + k;
+            red[o] = au[k];
+            red[(int64_t)G * width + o] = ag[k];
+            red[2 * (int64_t)G * width + o] = ad[k];
+        }
+    }
+    __syncthreads();
+    for (int q = tid; q < width; q += blockDim.x) {
+        float su = red[q], sg = red[G * width + q], sd = red[2 * G * width + q];
+        for (int gg = 1; gg < G; ++gg) {
+            su += red[gg * width + q];
+            sg += red[(G + gg) * width + q];
+            sd += red[(2 * G + gg) * width + q];
+        }
+        u[bt * E + q] = su * inv_p;
+        gs[bt * E + q] = sg;
+        dDp[bt * E + q] = sd;
+    }
+}
+
+// G groups of VE lanes, G <= n, about 512 threads.
+void pick_groups_bwd(int64_t VE, int64_t n, int* G, int* threads) {
+    int64_t g = 512 / VE;
+    if (g > n) g = n;
+    if (g < 1) g = 1;
+    *G = (int)g;
+    *threads = (int)((VE * g + 63) / 64 * 64);
+}
+
+template <class IO>
+hipError_t bwd_pool_t(const Geom& g, const void* x, const void* z, const void* dout, const BwdWorkspace& ws,
+                      hipStream_t st) {
+    using elem = typename IO::elem;
+    const int64_t VE = g.E / IO::V;
+    int G, threads;
+    pick_groups_bwd(VE, g.masked ? g.K : g.P, &G, &threads);
+    const size_t lds = 3 * (size_t)G * VE * IO::V * sizeof(float);
+    const elem *xe = static_cast<const elem*>(x), *ze = static_cast<const elem*>(z),
+               *de = static_cast<const elem*>(dout);
+    if (g.masked) {
+        hipLaunchKernelGGL(bwd_pool_masked_kernel<IO>, dim3((unsigned)(g.B * g.T)), dim3(threads), lds, st, xe, ze,
+                           de, ws.fwd.rows, ws.fwd.u, ws.gs, ws.dDp, g.T, g.K, (int)VE, G, g.E, 1.0f / (float)g.P);
+    } else {
+        const int64_t t_stride = g.axis == FASTVIM_POOL_COLS ? g.w * g.E : g.E;
+        const int64_t p_stride = g.axis == FASTVIM_POOL_COLS ? g.E : g.w * g.E;
+        hipLaunchKernelGGL(bwd_pool_dense_kernel<IO>, dim3((unsigned)(g.B * g.T)), dim3(threads), lds, st, xe, ze,
+                           de, ws.fwd.u, ws.gs, ws.dDp, g.T, g.P, (int)VE, G, g.E, g.h * g.w * g.E, t_stride,
+                           p_stride, 1.0f / (float)g.P);
+    }
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------- dv
+// dv[b, t, d, o] = sum over channel groups of the scan adjoint's partials,
+// taken from the LDS row layout: o < R is the low-rank input r = o at
+// position (r mod 4) RMAX/4 + r div 4, o >= R is B / C at RMAX + o - R.
+__global__ void __launch_bounds__(256)
+bwd_dv_kernel(const float* __restrict__ dvp, float* __restrict__ dv, int64_t B, int64_t T, int64_t G, int S, int R,
+              int NX, int RMAX) {
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t total = B * T * 2 * NX;
+    if (idx >= total) return;
+    const int o = (int)(idx % NX);
+    const int64_t rest = idx / NX;
+    const int d = (int)(rest % 2);
+    const int64_t bt = rest / 2, b = bt / T, t = bt - b * T;
+    const int pos = o < R ? (o % 4) * (RMAX / 4) + o / 4 : RMAX + (o - R);
+    const float* src = dvp + ((d * B + b) * G) * T * S + t * S + pos;
+    float s = 0.f;
+    for (int64_t gg = 0; gg < G; ++gg) s += src[gg * T * S];
+    dv[idx] = s;
+}
+
+// ---------------------------------------------------------------------- du
+// du[m, e] = du_f[m, e] + du_b[m, e] + sum_o (W_f[o, e] dv[m, 0, o] + W_b[o, e] dv[m, 1, o]).
+// Lane = channel, each wave 16 tokens: the weight column entry is loaded once
+// per (o, 16 tokens) and the dv entries are wave-uniform (scalar) loads.
+constexpr int kDuTok = 16;
+__global__ void __launch_bounds__(256)
+bwd_du_kernel(const float* __restrict__ du_f, const float* __restrict__ du_b, const float* __restrict__ dv,
+              const float* __restrict__ Wf, const float* __restrict__ Wb, float* __restrict__ du, int64_t M, int64_t E,
+              int NX) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t e = (int64_t)blockIdx.y * 64 + lane;
+    const int64_t ec = e < E ? e : E - 1;
+    const int64_t m0 = ((int64_t)blockIdx.x * 4 + wave) * kDuTok;
+    if (m0 >= M) return;
+    float acc[kDuTok];
+#pragma unroll
+    for (int k = 0; k < kDuTok; ++k) {
+        const int64_t m = m0 + k < M ? m0 + k : M - 1;
+        acc[k] = du_f[m * E + ec] + du_b[m * E + ec];
+    }
+    for (int d = 0; d < 2; ++d) {
+        const float* W = d ? Wb : Wf;
+        for (int o = 0; o < NX; ++o) {
+            const float wv = W[(int64_t)o * E + ec];
+#pragma unroll
+            for (int k = 0; k < kDuTok; ++k) {
+                const int64_t m = m0 + k < M ? m0 + k : M - 1;
+                acc[k] = fmaf(wv, dv[(m * 2 + d) * NX + o], acc[k]);
+            }
+        }
+    }
+    if (e < E) {
+#pragma unroll
+        for (int k = 0; k < kDuTok; ++k)
+            if (m0 + k < M) du[(m0 + k) * E + e] = acc[k];
+    }
+}
+
+// --------------------------------------------------------------------- dwx
+// Partial of d x_proj_w over one chunk of kBwdTokChunk pooled tokens:
+//   dWxp[chunk, d, o, e] = sum_{m in chunk} dv[m, d, o] u[m, e]
+// Lane = channel, wave w takes the outputs o = w * kOG ... (wave-uniform dv
+// loads).
+constexpr int kOG = 24;  // outputs per wave: NX <= 96
+__global__ void __launch_bounds__(256)
+bwd_dwx_kernel(const float* __restrict__ dv, const float* __restrict__ u, float* __restrict__ dWxp, int64_t M,
+               int64_t E, int NX) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t chunk = blockIdx.x;
+    const int64_t e = (int64_t)blockIdx.y * 64 + lane;
+    const int64_t ec = e < E ? e : E - 1;
+    const int d = blockIdx.z;
+    const int og = (NX + 3) / 4;
+    const int o0 = wave * og;
+    const int64_t m0 = chunk * kBwdTokChunk;
+    const int64_t m1 = m0 + kBwdTokChunk < M ? m0 + kBwdTokChunk : M;
+    float acc[kOG];
+#pragma unroll
+    for (int i = 0; i < kOG; ++i) acc[i] = 0.f;
+    for (int64_t m = m0; m < m1; ++m) {
+        const float uv = u[m * E + ec];
+        const float* dvr = dv + (m * 2 + d) * NX;
+#pragma unroll
+        for (int i = 0; i < kOG; ++i)
+            if (i < og && o0 + i < NX) acc[i] = fmaf(dvr[o0 + i], uv, acc[i]);
+    }
+    if (e < E) {
+#pragma unroll
+        for (int i = 0; i < kOG; ++i)
+            if (i < og && o0 + i < NX) dWxp[((chunk * 2 + d) * NX + o0 + i) * E + e] = acc[i];
+    }
+}
+
+// ------------------------------------------------------------------ colsum
+// out[c, j] = sum_{i in rows [c rpb, (c + 1) rpb)} in[i ld + j]
+__global__ void __launch_bounds__(256)
+colsum_kernel(const float* __restrict__ in, int64_t rows, int64_t cols, int64_t ld, int64_t rpb,
+              float* __restrict__ out, float* __restrict__ out2) {
+    const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (j >= cols) return;
+    const int64_t c = blockIdx.y;
+    const int64_t r0 = c * rpb, r1 = r0 + rpb < rows ? r0 + rpb : rows;
+    float s = 0.f;
+    for (int64_t i = r0; i < r1; ++i) s += in[i * ld + j];
+    out[c * cols + j] = s;
+    if (out2) out2[c * cols + j] = s;
+}
+
+__global__ void __launch_bounds__(256) fill_zero_kernel(float* __restrict__ p, int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0.f;
+}
+
+// ------------------------------------------------------------------ pass 2
+enum { kModeCols = 0, kModeRows = 1, kModeMasked = 4 };
+constexpr int kU = 4;  // tokens per thread
+
+template <int V>
+__device__ __forceinline__ void row_vec(const float* a, const float* b, int64_t off, float (&r)[V]) {
+#pragma unroll
+    for (int v = 0; v < V; v += 4) {
+        const f32x4 p1 = load_raw<false>(a + off + v), p2 = load_raw<false>(b + off + v);
+        r[v] = p1.x + p2.x;
+        r[v + 1] = p1.y + p2.y;
+        r[v + 2] = p1.z + p2.z;
+        r[v + 3] = p1.w + p2.w;
+    }
+}
+template <int V>
+__device__ __forceinline__ void row_vec1(const float* a, int64_t off, float (&r)[V]) {
+#pragma unroll
+    for (int v = 0; v < V; v += 4) {
+        const f32x4 p1 = load_raw<false>(a + off + v);
+        r[v] = p1.x;
+        r[v + 1] = p1.y;
+        r[v + 2] = p1.z;
+        r[v + 3] = p1.w;
+    }
+}
+
+// A workgroup takes a run of G * kU memory-contiguous tokens (part of a grid
+// row, or of one image's kept tokens), as the forward epilogue does.
+template <class IO, int MODE>
+__global__ void __launch_bounds__(1024)
+bwd_epilogue_kernel(const typename IO::elem* __restrict__ x, const typename IO::elem* __restrict__ z,
+                    const typename IO::elem* __restrict__ dout, const float* __restrict__ sf,
+                    const float* __restrict__ sb, const float* __restrict__ du, const float* __restrict__ Df,
+                    const float* __restrict__ Db, typename IO::elem* __restrict__ dx,
+                    typename IO::elem* __restrict__ dz, const int32_t* __restrict__ rows, int64_t T, int64_t h,
+                    int64_t w, int64_t K, int64_t E, int VE, int G, int64_t seg_len, int64_t blocks_per_seg,
+                    int64_t segs_per_img, float inv_p) {
+    constexpr int V = IO::V;
+    using raw = typename IO::raw;
+    const int tid = threadIdx.x, c = tid % VE, g = tid / VE;
+    if (g >= G) return;
+    const int64_t blk = blockIdx.x;
+    const int64_t seg = blk / blocks_per_seg;
+    const int64_t p0 = (blk - seg * blocks_per_seg) * (int64_t)G * kU;
+    const int64_t b = seg / segs_per_img, sgi = seg - b * segs_per_img;
+    const int64_t col = (int64_t)c * V;
+    int64_t tok[kU];
+    bool ok[kU];
+#pragma unroll
+    for (int k = 0; k < kU; ++k) {
+        const int64_t p = p0 + g + (int64_t)G * k;
+        ok[k] = p < seg_len;
+        tok[k] = MODE == kModeMasked ? b * K + p : (b * h + sgi) * w + p;
+    }
+    raw xr[kU], zr[kU], dr[kU];
+#pragma unroll
+    for (int k = 0; k < kU; ++k) {
+        if (ok[k]) {
+            xr[k] = load_raw<true>(x + tok[k] * E + col);
+            zr[k] = load_raw<true>(z + tok[k] * E + col);
+            dr[k] = load_raw<true>(dout + tok[k] * E + col);
+        }
+    }
+    float dsum[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) dsum[v] = Df[col + v] + Db[col + v];
+    float srow[V], urow[V];
+    if (MODE == kModeCols) {
+        row_vec<V>(sf, sb, (b * T + sgi) * E + col, srow);
+        row_vec1<V>(du, (b * T + sgi) * E + col, urow);
+    }
+#pragma unroll
+    for (int k = 0; k < kU; ++k) {
+        if (!ok[k]) continue;
+        float sv[V], uv[V];
+        bool valid = true;
+        if (MODE == kModeCols) {
+#pragma unroll
+            for (int v = 0; v < V; ++v) {
+                sv[v] = srow[v];
+                uv[v] = urow[v];
+            }
+        } else {
+            const int64_t t = MODE == kModeRows ? p0 + g + (int64_t)G * k : rows[tok[k]];
+            valid = t >= 0;
+            if (valid) {
+                row_vec<V>(sf, sb, (b * T + t) * E + col, sv);
+                row_vec1<V>(du, (b * T + t) * E + col, uv);
+            }
+        }
+        float ox[V], oz[V];
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+            const float xv = raw_at(xr[k], v), zv = raw_at(zr[k], v), dv = raw_at(dr[k], v);
+            const float sg = sigmoid_f(zv);
+            const float y = fmaf(dsum[v], xv, sv[v]);
+            ox[v] = valid ? fmaf(dv * zv * sg, dsum[v], uv[v] * inv_p) : __builtin_nanf("");
+            oz[v] = valid ? dv * y * sg * fmaf(zv, 1.f - sg, 1.f) : __builtin_nanf("");
+        }
+        store_vec<true>(dx + tok[k] * E + col, ox);
+        store_vec<true>(dz + tok[k] * E + col, oz);
+    }
+}
+
+template <class IO, int MODE>
+hipError_t bwd_epi_launch(const Geom& g, const void* x, const void* z, const void* dout, const fastvim_params& p,
+                          const BwdWorkspace& ws, void* dx, void* dz, hipStream_t st) {
+    const int64_t VE = g.E / IO::V;
+    int64_t G = 512 / VE;
+    if (G < 1) G = 1;
+    const int64_t seg_len = MODE == kModeMasked ? g.K : g.w;
+    const int64_t segs_per_img = MODE == kModeMasked ? 1 : g.h;
+    if (G * kU > seg_len) G = (seg_len + kU - 1) / kU;
+    if (G < 1) G = 1;
+    const int64_t blocks_per_seg = (seg_len + G * kU - 1) / (G * kU);
+    const int threads = (int)((VE * G + 63) / 64 * 64);
+    using elem = typename IO::elem;
+    const int64_t blocks = g.B * segs_per_img * blocks_per_seg;
+    hipLaunchKernelGGL((bwd_epilogue_kernel<IO, MODE>), dim3((unsigned)blocks), dim3(threads), 0, st,
+                       static_cast<const elem*>(x), static_cast<const elem*>(z), static_cast<const elem*>(dout),
+                       ws.fwd.s_f, ws.fwd.s_b, ws.du, p.fwd.D, p.bwd.D, static_cast<elem*>(dx),
+                       static_cast<elem*>(dz), ws.fwd.rows, g.T, g.h, g.w, g.K, g.E, (int)VE, (int)G, seg_len,
+                       blocks_per_seg, segs_per_img, 1.0f / (float)g.P);
+    return hipGetLastError();
+}
+
+template <class IO>
+hipError_t bwd_epi_dispatch(const Geom& g, const void* x, const void* z, const void* dout, const fastvim_params& p,
+                            const BwdWorkspace& ws, void* dx, void* dz, hipStream_t st) {
+    if (g.masked) return bwd_epi_launch<IO, kModeMasked>(g, x, z, dout, p, ws, dx, dz, st);
+    if (g.axis == FASTVIM_POOL_COLS) return bwd_epi_launch<IO, kModeCols>(g, x, z, dout, p, ws, dx, dz, st);
+    return bwd_epi_launch<IO, kModeRows>(g, x, z, dout, p, ws, dx, dz, st);
+}
+
+}  // namespace
+
+hipError_t launch_bwd_pool(const Geom& g, const void* x, const void* z, const void* dout, const BwdWorkspace& ws,
+                           hipStream_t st) {
+    return g.io == FASTVIM_BF16 ? bwd_pool_t<IoBf16>(g, x, z, dout, ws, st) : bwd_pool_t<IoF32>(g, x, z, dout, ws, st);
+}
+
+hipError_t launch_bwd_dv(const Geom& g, const BwdWorkspace& ws, hipStream_t st) {
+    const int64_t total = g.B * g.T * 2 * g.NX;
+    hipLaunchKernelGGL(bwd_dv_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, ws.dvp, ws.dv, g.B,
+                       g.T, ws.G, (int)ws.S, (int)g.R, (int)g.NX, bwd_rmax(g.R));
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_du(const Geom& g, const fastvim_params& p, const BwdWorkspace& ws, hipStream_t st) {
+    const int64_t M = g.B * g.T;
+    const dim3 grid((unsigned)((M + 4 * kDuTok - 1) / (4 * kDuTok)), (unsigned)((g.E + 63) / 64));
+    hipLaunchKernelGGL(bwd_du_kernel, grid, dim3(256), 0, st, ws.du_f, ws.du_b, ws.dv, p.fwd.x_proj_w,
+                       p.bwd.x_proj_w, ws.du, M, g.E, (int)g.NX);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_dwx(const Geom& g, const BwdWorkspace& ws, hipStream_t st) {
+    const int64_t M = g.B * g.T;
+    const dim3 grid((unsigned)ws.MC, (unsigned)((g.E + 63) / 64), 2);
+    hipLaunchKernelGGL(bwd_dwx_kernel, grid, dim3(256), 0, st, ws.dv, ws.fwd.u, ws.dWxp, M, g.E, (int)g.NX);
+    return hipGetLastError();
+}
+
+hipError_t launch_colsum(const float* in, int64_t rows, int64_t cols, int64_t ld, float* out, float* out2,
+                         float* tmp, hipStream_t st) {
+    const unsigned cb = (unsigned)((cols + 255) / 256);
+    if (rows <= kColRowsPerBlock) {
+        hipLaunchKernelGGL(colsum_kernel, dim3(cb, 1), dim3(256), 0, st, in, rows, cols, ld, rows, out, out2);
+        return hipGetLastError();
+    }
+    const int64_t nc = (rows + kColRowsPerBlock - 1) / kColRowsPerBlock;
+    hipLaunchKernelGGL(colsum_kernel, dim3(cb, (unsigned)nc), dim3(256), 0, st, in, rows, cols, ld,
+                       (int64_t)kColRowsPerBlock, tmp, (float*)nullptr);
+    hipLaunchKernelGGL(colsum_kernel, dim3(cb, 1), dim3(256), 0, st, (const float*)tmp, nc, cols, cols, nc, out,
+                       out2);
+    return hipGetLastError();
+}
+
+hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st) {
+    if (n <= 0) return hipSuccess;
+    const int64_t blocks = (n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096;
+    hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, st, p, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_epilogue(const Geom& g, const void* x, const void* z, const void* dout,
+                               const fastvim_params& p, const BwdWorkspace& ws, void* dx, void* dz, hipStream_t st) {
+    return g.io == FASTVIM_BF16 ? bwd_epi_dispatch<IoBf16>(g, x, z, dout, p, ws, dx, dz, st)
+                                : bwd_epi_dispatch<IoF32>(g, x, z, dout, p, ws, dx, dz, st);
+}
+
+}  // namespace fastvim

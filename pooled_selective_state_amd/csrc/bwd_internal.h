@@ -1,0 +1,64 @@
+// Internal declarations of the backward pass (gradients of the pooled layer).
+// Not part of the public ABI.
+#pragma once
+
+#include "fastvim_internal.h"
+
+namespace fastvim {
+
+constexpr int kBwdTMax = 128;        // longest scan the backward kernels take (sequence rows held in LDS)
+constexpr int kBwdCh = 64;           // channels per scan-adjoint workgroup (one channel group)
+constexpr int kBwdTokChunk = 256;    // pooled tokens per partial of d x_proj_w
+constexpr int kColRowsPerBlock = 128;  // rows per first-stage block of a column sum
+
+// Workspace of one backward call (every region 256-byte aligned).  fwd views
+// the part shared with the forward stages (u, xdbl, s_f, s_b, rows, bad).
+struct BwdWorkspace {
+    Workspace fwd;
+    float* gs;     // (B, T, E) dL/ds: the gated upstream gradient summed over the pooled axis
+    float* dDp;    // (B, T, E) per pooled row: sum over its cells of dL/dy * x
+    float* du_f;   // (B, T, E) scan part of dL/du, forward direction
+    float* du_b;   // (B, T, E) the same, backward direction
+    float* du;     // (B, T, E) dL/du, both directions, scan and x_proj
+    float* dvp;    // (2, B, G, T, S) channel-group partials of dL/dv, in the scan's LDS row layout
+    float* dv;     // (B, T, 2, NX) dL/dv of both directions
+    float* dAp;    // (2, B, E, 16) per-image d A_log
+    float* dWdtp;  // (2, B, E, R) per-image d dt_proj_w
+    float* dbp;    // (2, B, E) per-image d dt_proj_b
+    float* dWxp;   // (MC, 2, NX, E) per token chunk d x_proj_w
+    float* tmp;    // first-stage sums of the column reductions
+    int64_t G, S, MC, tmp_floats;
+};
+
+struct BwdScanArgs {
+    const float* xdbl;  // (B, T, 2, NX)
+    const float* u;     // (B, T, E)
+    const float* gs;    // (B, T, E)
+    fastvim_dir_params pf, pb;
+    float *s_f, *s_b;     // (B, T, E) recomputed scan outputs
+    float *du_f, *du_b;   // (B, T, E)
+    float* dvp;           // (2, B, G, T, S)
+    float *dAp, *dWdtp, *dbp;
+    int64_t B, T, E;
+    int R, NX, G;
+};
+
+int bwd_rmax(int64_t R);  // the dt-rank bound (16, 32, 48, 64) whose kernel instance serves R
+size_t bwd_workspace_layout(const Geom& g, void* base, BwdWorkspace* ws);
+
+hipError_t launch_bwd_pool(const Geom& g, const void* x, const void* z, const void* dout, const BwdWorkspace& ws,
+                           hipStream_t st);
+hipError_t launch_scan_bwd(const BwdScanArgs& a, hipStream_t st);
+hipError_t launch_bwd_dv(const Geom& g, const BwdWorkspace& ws, hipStream_t st);
+hipError_t launch_bwd_du(const Geom& g, const fastvim_params& p, const BwdWorkspace& ws, hipStream_t st);
+hipError_t launch_bwd_dwx(const Geom& g, const BwdWorkspace& ws, hipStream_t st);
+// out[j] = sum_i in[i * ld + j] for j < cols (and the same into out2 when
+// given), in a fixed order; more than kColRowsPerBlock rows go through tmp
+// (ceil(rows / kColRowsPerBlock) * cols floats).
+hipError_t launch_colsum(const float* in, int64_t rows, int64_t cols, int64_t ld, float* out, float* out2,
+                         float* tmp, hipStream_t st);
+hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st);
+hipError_t launch_bwd_epilogue(const Geom& g, const void* x, const void* z, const void* dout,
+                               const fastvim_params& p, const BwdWorkspace& ws, void* dx, void* dz, hipStream_t st);
+
+}  // namespace fastvim

@@ -1,0 +1,382 @@
+// Adjoint of the selective scan (backward pass of the layer): for one image,
+// one direction and 64 channels, the gradients of L with respect to the
+// scanned tokens u, the x_proj outputs (low-rank step input, B_t, C_t) and the
+// direction's dt_proj_w, dt_proj_b and A_log, given gs = dL/ds.
+//
+// The forward recurrence is the one of scan_core.h (FastVim summary page,
+// gptget.net, arXiv 2502.00594, section 方法详解 bullets 3-4; section 术语表,
+// "State Space Model").  With k the traversal step, a_k[n] = exp(Delta_k A[n])
+// and H_k = a_k H_{k-1} + Delta_k B_k[n] u_k, its adjoint runs backwards in k:
+//   lambda_k[n] = C_k[n] gs_k + a_{k+1}[n] lambda_{k+1}[n]
+//   dDelta_k    = sum_n lambda_k[n] (A[n] a_k[n] H_{k-1}[n] + B_k[n] u_k)
+//   du_k        = Delta_k sum_n lambda_k[n] B_k[n]
+//   dB_k[n]     = sum_e lambda_k[e, n] Delta_k[e] u_k[e]
+//   dC_k[n]     = sum_e gs_k[e] H_k[e, n]
+//   dA_log[n]  += lambda_k[n] a_k[n] Delta_k H_{k-1}[n] A[n]
+// and through Delta = softplus(q), q = dt_proj_w delta_lowrank + dt_proj_b,
+//   dq_k = dDelta_k sigmoid(q_k),  d dt_proj_b += dq_k,
+//   d dt_proj_w[e, r] += dq_k delta_k[r],  ddelta_k[r] = sum_e dt_proj_w[e, r] dq_k[e].
+//
+// One 256-thread workgroup takes (image b, channel group g, direction d),
+// with the lane layout of the forward scan: 4 lanes per channel, lane q
+// holding the states n = 4q .. 4q + 3.  All x_proj rows of the sequence are
+// staged in LDS once (the forward scan's row layout, zero-filled past T), and
+// each lane keeps the token values u and adjoint inputs gs of its own steps
+// q + 4j in registers.  Then:
+//   1. a forward sweep (the forward scan's own chunk code) recomputes the
+//      states, writes s^d (needed by the output adjoint) and keeps the state
+//      entering every chunk of kChunk steps as a register checkpoint;
+//   2. a reverse sweep over the chunks, last first, recomputes the chunk's
+//      step sizes and its kChunk states from the checkpoint, then walks the
+//      chunk's steps backwards carrying lambda.
+// Sums over n stay inside a quad (DPP).  Sums over channels e (dB, dC and
+// ddelta, needed per step) are taken over the 4 channels of each DPP row of
+// 16 lanes with two row rotations, written by the row's first quad into an
+// LDS buffer of kBwdFlush steps x 16 rows, and every kBwdFlush steps the
+// workgroup adds the 16 row partials and stores one partial per channel
+// group (B, G, T, S) for a later kernel to add over the groups.  Per-image
+// partials of the parameter gradients (summed over t) go to (B, E, ...)
+// buffers, summed over images by a later kernel.  No atomics: every sum has
+// a fixed order.
+#include "scan_core.h"
+#include "bwd_internal.h"
+
+namespace fastvim {
+namespace {
+
+constexpr int kBwdThreads = 256;                   // one direction: 64 channels x 4 lanes
+constexpr int kBwdFlush = 8;                       // steps per flush of the channel sums
+constexpr int kBwdRows = kBwdThreads / 16;         // DPP rows of 16 lanes per workgroup
+constexpr int kBwdCM = kBwdTMax / kChunk;          // chunks at most (8)
+static_assert(kBwdThreads / kLps == kScanCh && kScanCh == kBwdCh, "a workgroup covers one channel group");
+static_assert(kChunk % kBwdFlush == 0, "whole flushes per chunk");
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_row(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+// Sum over the 4 quads of a DPP row of 16 lanes (lanes i, i+4, i+8, i+12).
+__device__ __forceinline__ float row_quads_sum(float v) {
+    v += dpp_row<0x124>(v);  // row_ror:4
+    v += dpp_row<0x128>(v);  // row_ror:8
+    return v;
+}
+__device__ __forceinline__ float sigmoid_f(float q) { return __builtin_amdgcn_rcpf(1.f + __expf(-q)); }
+
+template <int M>
+__device__ __forceinline__ float bcast(float v) {
+    return quad_bcast<M>(v);
+}
+
+template <int RMAX>
+__global__ void __launch_bounds__(kBwdThreads) scan_bwd_kernel(BwdScanArgs a) {
+    constexpr int S = row_stride_lds<RMAX>();
+    constexpr int kWQ = RMAX / 4;
+    constexpr int kPre = (S + 15) / 16;          // row positions per lane (16 lanes per row)
+    constexpr int kPasses = kBwdTMax / 16;       // 16 rows per pass
+    __shared__ __attribute__((aligned(16))) float rows[kBwdTMax * S];
+    __shared__ __attribute__((aligned(16))) float red[kBwdFlush * kBwdRows * S];
+
+    const int tid = threadIdx.x;
+    const int dir = blockIdx.y;
+    const int64_t b = blockIdx.x / a.G;
+    const int gi = (int)(blockIdx.x % a.G);
+    const int ch = tid / kLps, q = tid & 3;
+    const int64_t e = (int64_t)gi * kScanCh + ch;
+    const bool valid = e < a.E;
+    const int64_t ec = valid ? e : a.E - 1;
+    const int T = (int)a.T, R = a.R, NX = a.NX, E = (int)a.E;
+    const fastvim_dir_params p = dir ? a.pb : a.pf;
+    const float kLog2e = 1.4426950408889634f;
+
+    ScanLane<RMAX> L;
+    L.dir = dir;
+    L.l = q;
+    L.q = q;
+    L.valid = valid;
+    float An[kNs];
+#pragma unroll
+    for (int n = 0; n < kNs; ++n) {
+        An[n] = -expf(p.A_log[ec * 16 + kNs * q + n]);
+        L.A2[n] = An[n] * kLog2e;
+        L.hs[n] = 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < kWQ; ++i) {
+        const int r = q + 4 * i;
+        L.wq[i] = r < R ? p.dt_proj_w[ec * R + r] : 0.f;
+    }
+    L.bias = p.dt_proj_b[ec];
+    L.sstep = dir ? -(int64_t)E : (int64_t)E;
+    L.sq = (dir ? a.s_b + (int64_t)(T - 1) * E : a.s_f) + b * T * E + ec + q * L.sstep;
+
+    // stage this direction's x_proj rows at their traversal steps, zeros past T
+    const int nch = (T + kChunk - 1) / kChunk;
+    const int nrow = nch * kChunk;
+    {
+        const float* xb = a.xdbl + (b * T * 2 + dir) * (int64_t)NX;  // row t at xb + 2 t NX
+        const int prow = tid / 16, po = tid % 16;
+        int scol[kPre];
+#pragma unroll
+        for (int i = 0; i < kPre; ++i) scol[i] = po + 16 * i < S ? lds_source_col<RMAX>(po + 16 * i, R) : -1;
+        float stage[kPasses][kPre];
+#pragma unroll
+        for (int ps = 0; ps < kPasses; ++ps) {
+            const int ti = prow + 16 * ps;
+            const int t = dir ? T - 1 - ti : ti;
+#pragma unroll
+            for (int i = 0; i < kPre; ++i) stage[ps][i] = (ti < T && scol[i] >= 0) ? xb[2 * t * NX + scol[i]] : 0.f;
+        }
+#pragma unroll
+        for (int ps = 0; ps < kPasses; ++ps) {
+            const int ti = prow + 16 * ps;
+            if (ti < nrow) {
+#pragma unroll
+                for (int i = 0; i < kPre; ++i)
+                    if (po + 16 * i < S) rows[ti * S + po + 16 * i] = stage[ps][i];
+            }
+        }
+    }
+    // token values and adjoint inputs of the lane's own steps (zero past T and
+    // for channels past E, which then contribute nothing to the channel sums)
+    float uall[kBwdCM][kJ], gall[kBwdCM][kJ];
+    {
+        const float* ub = a.u + b * T * E + ec;
+        const float* gb = a.gs + b * T * E + ec;
+#pragma unroll
+        for (int c = 0; c < kBwdCM; ++c)
+#pragma unroll
+            for (int j = 0; j < kJ; ++j) {
+                const int tj = c * kChunk + q + 4 * j;
+                const int t = dir ? T - 1 - tj : tj;
+                const bool in = valid && tj < T;
+                uall[c][j] = in ? ub[(int64_t)t * E] : 0.f;
+                gall[c][j] = in ? gb[(int64_t)t * E] : 0.f;
+            }
+    }
+    __syncthreads();
+
+    // 1. forward sweep: outputs s^d and the state entering every chunk.
+    // uall / gall rotate left one chunk per step and hck is a shift register,
+    // so every register index is a constant.
+    ScanArgs sa{};
+    sa.T = T;
+    float hck[kBwdCM][kNs];
+#pragma unroll 1
+    for (int c = 0; c < nch; ++c) {
+#pragma unroll
+        for (int k = 0; k + 1 < kBwdCM; ++k)
+#pragma unroll
+            for (int n = 0; n < kNs; ++n) hck[k][n] = hck[k + 1][n];
+#pragma unroll
+        for (int n = 0; n < kNs; ++n) hck[kBwdCM - 1][n] = L.hs[n];
+        float ucur[kJ], u0[kJ], g0[kJ];
+#pragma unroll
+        for (int j = 0; j < kJ; ++j) {
+            ucur[j] = u0[j] = uall[0][j];
+            g0[j] = gall[0][j];
+        }
+#pragma unroll
+        for (int k = 0; k + 1 < kBwdCM; ++k)
+#pragma unroll
+            for (int j = 0; j < kJ; ++j) {
+                uall[k][j] = uall[k + 1][j];
+                gall[k][j] = gall[k + 1][j];
+            }
+#pragma unroll
+        for (int j = 0; j < kJ; ++j) {
+            uall[kBwdCM - 1][j] = u0[j];
+            gall[kBwdCM - 1][j] = g0[j];
+        }
+        scan_chunk<RMAX, false>(sa, L, rows + c * kChunk * S, ucur, (int64_t)c * kChunk);
+    }
+    // After nch left rotations, chunk c sits at index c - nch + kBwdCM, so the
+    // last chunk is at kBwdCM - 1; the reverse sweep rotates right.
+
+    // 2. reverse sweep
+    float carry[kNs], dA[kNs], dW[kWQ], db = 0.f;
+#pragma unroll
+    for (int n = 0; n < kNs; ++n) carry[n] = dA[n] = 0.f;
+#pragma unroll
+    for (int i = 0; i < kWQ; ++i) dW[i] = 0.f;
+    float* du_dir = (dir ? a.du_b : a.du_f) + b * T * E + ec;
+    float* dvp = a.dvp + (((int64_t)dir * a.B + b) * a.G + gi) * T * S;
+    const bool row_writer = (tid & 15) < 4;  // first quad of each DPP row
+    float* red_row = red + (tid / 16) * S;
+
+#pragma unroll 1
+    for (int c = nch - 1; c >= 0; --c) {
+        const float* dr = rows + c * kChunk * S;
+        const int base = c * kChunk;
+        float uc[kJ], gc[kJ], h0[kNs];
+#pragma unroll
+        for (int j = 0; j < kJ; ++j) {
+            uc[j] = uall[kBwdCM - 1][j];
+            gc[j] = gall[kBwdCM - 1][j];
+        }
+#pragma unroll
+        for (int n = 0; n < kNs; ++n) h0[n] = hck[kBwdCM - 1][n];
+#pragma unroll
+        for (int k = kBwdCM - 1; k > 0; --k) {
+#pragma unroll
+            for (int j = 0; j < kJ; ++j) {
+                uall[k][j] = uall[k - 1][j];
+                gall[k][j] = gall[k - 1][j];
+            }
+#pragma unroll
+            for (int n = 0; n < kNs; ++n) hck[k][n] = hck[k - 1][n];
+        }
+#pragma unroll
+        for (int j = 0; j < kJ; ++j) {
+            uall[0][j] = uc[j];
+            gall[0][j] = gc[j];
+        }
+        // step sizes (and sigmoid of their pre-activation) of the own steps
+        float qv[kJ], dl[kJ], sg[kJ];
+        scan_step_preact<RMAX>(L, dr, qv);
+#pragma unroll
+        for (int j = 0; j < kJ; ++j) {
+            const bool in = base + q + 4 * j < T;
+            dl[j] = in ? softplus_f(qv[j]) : 0.f;
+            sg[j] = in ? sigmoid_f(qv[j]) : 0.f;
+        }
+        // states of the chunk's steps, recomputed from the checkpoint
+        float Hc[kChunk][kNs];
+        {
+            float hs[kNs];
+#pragma unroll
+            for (int n = 0; n < kNs; ++n) hs[n] = h0[n];
+#pragma unroll
+            for (int s = 0; s < kChunk; ++s) {
+                const int m = s & 3, j = s >> 2;
+                const float dlt = m == 0 ? bcast<0>(dl[j]) : m == 1 ? bcast<1>(dl[j]) : m == 2 ? bcast<2>(dl[j]) : bcast<3>(dl[j]);
+                const float us = m == 0 ? bcast<0>(uc[j]) : m == 1 ? bcast<1>(uc[j]) : m == 2 ? bcast<2>(uc[j]) : bcast<3>(uc[j]);
+                const f32x4 b4 = *reinterpret_cast<const f32x4*>(dr + s * S + RMAX + kNs * q);
+                const float bt[kNs] = {b4.x, b4.y, b4.z, b4.w};
+                const float du_ = dlt * us;
+#pragma unroll
+                for (int n = 0; n < kNs; ++n) {
+                    hs[n] = fmaf(__builtin_amdgcn_exp2f(dlt * L.A2[n]), hs[n], du_ * bt[n]);
+                    Hc[s][n] = hs[n];
+                }
+            }
+        }
+        float duo[kJ];
+#pragma unroll
+        for (int j = 0; j < kJ; ++j) duo[j] = 0.f;
+#pragma unroll
+        for (int half = kChunk / kBwdFlush - 1; half >= 0; --half) {
+#pragma unroll
+            for (int s = half * kBwdFlush + kBwdFlush - 1; s >= half * kBwdFlush; --s) {
+                const int m = s & 3, j = s >> 2;
+                const float dlt = m == 0 ? bcast<0>(dl[j]) : m == 1 ? bcast<1>(dl[j]) : m == 2 ? bcast<2>(dl[j]) : bcast<3>(dl[j]);
+                const float ut = m == 0 ? bcast<0>(uc[j]) : m == 1 ? bcast<1>(uc[j]) : m == 2 ? bcast<2>(uc[j]) : bcast<3>(uc[j]);
+                const float g = m == 0 ? bcast<0>(gc[j]) : m == 1 ? bcast<1>(gc[j]) : m == 2 ? bcast<2>(gc[j]) : bcast<3>(gc[j]);
+                const float sgs = m == 0 ? bcast<0>(sg[j]) : m == 1 ? bcast<1>(sg[j]) : m == 2 ? bcast<2>(sg[j]) : bcast<3>(sg[j]);
+                const float* row = dr + s * S;
+                const f32x4 b4 = *reinterpret_cast<const f32x4*>(row + RMAX + kNs * q);
+                const f32x4 c4 = *reinterpret_cast<const f32x4*>(row + RMAX + 16 + kNs * q);
+                const float bt[kNs] = {b4.x, b4.y, b4.z, b4.w}, ct[kNs] = {c4.x, c4.y, c4.z, c4.w};
+                float ddl = 0.f, dup = 0.f, cb[kNs], cc[kNs];
+                const float dut = dlt * ut;
+#pragma unroll
+                for (int n = 0; n < kNs; ++n) {
+                    const float av = __builtin_amdgcn_exp2f(dlt * L.A2[n]);
+                    const float hp = s > 0 ? Hc[s > 0 ? s - 1 : 0][n] : h0[n];
+                    const float lam = fmaf(ct[n], g, carry[n]);
+                    ddl = fmaf(lam, fmaf(An[n] * av, hp, bt[n] * ut), ddl);
+                    dup = fmaf(lam, bt[n], dup);
+                    cb[n] = lam * dut;
+                    cc[n] = g * Hc[s][n];
+                    dA[n] = fmaf(lam * av, dlt * hp, dA[n]);
+                    carry[n] = av * lam;
+                }
+                ddl = quad_sum(ddl);
+                dup = quad_sum(dup);
+                duo[j] = (m == q) ? dlt * dup : duo[j];
+                const float dq = ddl * sgs;
+                db += dq;
+                // d dt_proj_w over the lane's quarter r = q + 4i, and that
+                // quarter's terms of ddelta
+                float cd[kWQ];
+                const float* dq_row = row + q * kWQ;
+#pragma unroll
+                for (int i = 0; i < kWQ; i += 4) {
+                    const f32x4 d4 = *reinterpret_cast<const f32x4*>(dq_row + i);
+                    dW[i] = fmaf(dq, d4.x, dW[i]);
+                    dW[i + 1] = fmaf(dq, d4.y, dW[i + 1]);
+                    dW[i + 2] = fmaf(dq, d4.z, dW[i + 2]);
+                    dW[i + 3] = fmaf(dq, d4.w, dW[i + 3]);
+                }
+#pragma unroll
+                for (int i = 0; i < kWQ; ++i) cd[i] = row_quads_sum(L.wq[i] * dq);
+#pragma unroll
+                for (int n = 0; n < kNs; ++n) {
+                    cb[n] = row_quads_sum(cb[n]);
+                    cc[n] = row_quads_sum(cc[n]);
+                }
+                if (row_writer) {
+                    float* rr = red_row + (s - half * kBwdFlush) * kBwdRows * S;
+#pragma unroll
+                    for (int i = 0; i < kWQ; i += 4)
+                        *reinterpret_cast<f32x4*>(rr + q * kWQ + i) = f32x4{cd[i], cd[i + 1], cd[i + 2], cd[i + 3]};
+                    *reinterpret_cast<f32x4*>(rr + RMAX + kNs * q) = f32x4{cb[0], cb[1], cb[2], cb[3]};
+                    *reinterpret_cast<f32x4*>(rr + RMAX + 16 + kNs * q) = f32x4{cc[0], cc[1], cc[2], cc[3]};
+                }
+            }
+            // add the 16 row partials of these steps; one partial per channel group
+            __syncthreads();
+            for (int o = tid; o < kBwdFlush * S; o += kBwdThreads) {
+                const int st = o / S, pos = o - st * S;
+                const int ti = base + half * kBwdFlush + st;
+                const float* src = red + st * kBwdRows * S + pos;
+                float sum = 0.f;
+#pragma unroll
+                for (int r = 0; r < kBwdRows; ++r) sum += src[r * S];
+                if (ti < T) dvp[(int64_t)(dir ? T - 1 - ti : ti) * S + pos] = sum;
+            }
+            __syncthreads();
+        }
+        if (valid) {
+#pragma unroll
+            for (int j = 0; j < kJ; ++j) {
+                const int ti = base + q + 4 * j;
+                if (ti < T) du_dir[(int64_t)(dir ? T - 1 - ti : ti) * E] = duo[j];
+            }
+        }
+    }
+
+    // per-image partials of the parameter gradients
+    if (valid) {
+        const int64_t pe = ((int64_t)dir * a.B + b) * E + ec;
+#pragma unroll
+        for (int n = 0; n < kNs; ++n) a.dAp[pe * 16 + kNs * q + n] = dA[n] * An[n];
+#pragma unroll
+        for (int i = 0; i < kWQ; ++i) {
+            const int r = q + 4 * i;
+            if (r < R) a.dWdtp[pe * R + r] = dW[i];
+        }
+        if (q == 0) a.dbp[pe] = db;
+    }
+}
+
+template <int RMAX>
+hipError_t scan_bwd_launch(const BwdScanArgs& a, hipStream_t st) {
+    hipLaunchKernelGGL((scan_bwd_kernel<RMAX>), dim3((unsigned)(a.B * a.G), 2), dim3(kBwdThreads), 0, st, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+int bwd_rmax(int64_t R) { return R <= 16 ? 16 : R <= 32 ? 32 : R <= 48 ? 48 : 64; }
+
+hipError_t launch_scan_bwd(const BwdScanArgs& a, hipStream_t st) {
+    switch (bwd_rmax(a.R)) {
+        case 16: return scan_bwd_launch<16>(a, st);
+        case 32: return scan_bwd_launch<32>(a, st);
+        case 48: return scan_bwd_launch<48>(a, st);
+        default: return scan_bwd_launch<64>(a, st);
+    }
+}
+
+}  // namespace fastvim

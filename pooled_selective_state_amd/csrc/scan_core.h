@@ -211,6 +211,38 @@ __device__ __forceinline__ void scan_lane_setup(const ScanArgs& a, int64_t b, in
     L.sq = (L.dir ? a.s_b + (a.T - 1) * a.E : a.s_f) + b * a.T * a.E + ec + L.q * L.sstep;
 }
 
+// Phase 3 for the kChunk steps of LDS rows dr: qv[j] is the step-size
+// pre-activation dt_proj_w[e] . delta_lowrank + dt_proj_b[e] of the lane's
+// own step q + 4j.
+template <int RMAX>
+__device__ __forceinline__ void scan_step_preact(const ScanLane<RMAX>& L, const float* dr, float (&qv)[kJ]) {
+    constexpr int S = row_stride_lds<RMAX>();
+    const float* dq = dr + L.q * ScanLane<RMAX>::kWQ;
+    // one group of 4 steps per iteration; qv rotates so its indices stay constant
+#pragma unroll 1
+    for (int j = 0; j < kJ; ++j) {
+        float own = 0.f;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const float* row = dq + (4 * j + m) * S;
+            float pq = 0.f;
+#pragma unroll
+            for (int i = 0; i < ScanLane<RMAX>::kWQ; i += 4) {  // weights and inputs past R are zero
+                const f32x4 d4 = *reinterpret_cast<const f32x4*>(row + i);
+                pq = fmaf(L.wq[i], d4.x, pq);
+                pq = fmaf(L.wq[i + 1], d4.y, pq);
+                pq = fmaf(L.wq[i + 2], d4.z, pq);
+                pq = fmaf(L.wq[i + 3], d4.w, pq);
+            }
+            pq = quad_sum(pq);
+            own = (m == L.q) ? pq : own;
+        }
+#pragma unroll
+        for (int t = 0; t + 1 < kJ; ++t) qv[t] = qv[t + 1];
+        qv[kJ - 1] = own + L.bias;
+    }
+}
+
 // Phases 3 and 4 of one chunk.  dr: this direction's LDS row of the chunk's
 // local step 0; ucur: token values of the lane's steps q + 4j; base:
 // traversal index of local step 0.
@@ -222,30 +254,7 @@ __device__ __forceinline__ void scan_chunk(const ScanArgs& a, ScanLane<RMAX>& L,
     float dl[kJ], du[kJ];
     {
         float qv[kJ];
-        const float* dq = dr + L.q * ScanLane<RMAX>::kWQ;
-        // one group of 4 steps per iteration; qv rotates so its indices stay constant
-#pragma unroll 1
-        for (int j = 0; j < kJ; ++j) {
-            float own = 0.f;
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const float* row = dq + (4 * j + m) * S;
-                float pq = 0.f;
-#pragma unroll
-                for (int i = 0; i < ScanLane<RMAX>::kWQ; i += 4) {  // weights and inputs past R are zero
-                    const f32x4 d4 = *reinterpret_cast<const f32x4*>(row + i);
-                    pq = fmaf(L.wq[i], d4.x, pq);
-                    pq = fmaf(L.wq[i + 1], d4.y, pq);
-                    pq = fmaf(L.wq[i + 2], d4.z, pq);
-                    pq = fmaf(L.wq[i + 3], d4.w, pq);
-                }
-                pq = quad_sum(pq);
-                own = (m == L.q) ? pq : own;
-            }
-#pragma unroll
-            for (int t = 0; t + 1 < kJ; ++t) qv[t] = qv[t + 1];
-            qv[kJ - 1] = own + L.bias;
-        }
+        scan_step_preact<RMAX>(L, dr, qv);
 #pragma unroll
         for (int j = 0; j < kJ; ++j) {
             const bool in = base + L.q + 4 * j < T;

@@ -32,7 +32,7 @@ def test_library_exports_every_declared_function():
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(Bd.EXPORTED_SYMBOLS)
-    assert lib.fastvim_abi_version() == 3
+    assert lib.fastvim_abi_version() == 4
 
 
 def test_status_strings():
@@ -47,6 +47,7 @@ def test_struct_layout_matches_header():
     assert ctypes.sizeof(Bd.Dims) == 64
     assert ctypes.sizeof(Bd.DirParams) == 40
     assert ctypes.sizeof(Bd.Params) == 2 * 40 + 8 + 8 + 8 + 8 + 8 + 4 + 4
+    assert ctypes.sizeof(Bd.DirGrads) == 40 and ctypes.sizeof(Bd.Grads) == 80
 
 
 def _ws(dims, axis):
@@ -253,3 +254,122 @@ def test_post_norm_validation():
         c.params.flags = P.FLAG_POST_NORM
         c.params.ln_weight, c.params.ln_bias, c.params.ln_eps = w, b, eps
         expect(c, code)
+
+
+# ------------------------------------------------------------------ backward
+class FakeBwd:
+    """Backward-call arguments with fake (never dereferenced) device addresses."""
+
+    def __init__(self, B=2, h=4, w=5, E=16, N=16, R=4, K=0, io=P.F32, axis=P.POOL_COLS):
+        self.dims = P.make_dims(B, h, w, E, N, R, K, io)
+        self.axis = axis
+        base = 1 << 41
+        esz = 4 if io == P.F32 else 2
+        n = B * (K if K else h * w) * E * esz
+        span = (n + 4096) // 4096 * 4096
+        self.x, self.z, self.dout, self.dx, self.dz = (base + i * span for i in range(5))
+        self.idx = base + 5 * span if K else None
+        pbase = base + 6 * span
+        dirs = [Bd.DirParams(*[pbase + (5 * i + j) * 65536 for j in range(5)]) for i in range(2)]
+        gbase = pbase + 10 * 65536
+        self.grads = Bd.Grads(*[Bd.DirGrads(*[gbase + (5 * i + j) * 65536 for j in range(5)]) for i in range(2)])
+        wsb = max(P.bwd_workspace_bytes(self.dims, axis), 256)
+        self.params = Bd.Params(dirs[0], dirs[1], gbase + 10 * 65536, wsb, 0, 0)
+
+    def bwd(self):
+        return P.lib().fastvim_ssm_bwd(self.x, self.z, self.dout, ctypes.byref(self.params), ctypes.byref(self.dims),
+                                       self.axis, self.idx, self.dx, self.dz, ctypes.byref(self.grads), None)
+
+
+def test_bwd_workspace_bytes():
+    d = P.make_dims(2, 4, 5, 16, 16, 4)
+    assert P.bwd_workspace_bytes(d, P.POOL_COLS) > P.workspace_bytes(d, P.POOL_COLS) > 0
+    assert P.bwd_workspace_bytes(d, P.POOL_NONE_ROWMAJOR) == 0  # unpooled: no backward pass
+    assert P.bwd_workspace_bytes(P.make_dims(2, 129, 4, 16), P.POOL_COLS) == 0  # scan of 129 steps
+    assert P.bwd_workspace_bytes(P.make_dims(2, 129, 4, 16), P.POOL_ROWS) > 0   # ... but 4 steps over columns
+    assert P.bwd_workspace_bytes(P.make_dims(2, 4, 5, 16, 8), P.POOL_COLS) == 0  # N != 16
+
+
+def test_bwd_null_pointers():
+    lib = P.lib()
+    c = FakeBwd()
+    assert lib.fastvim_ssm_bwd(c.x, c.z, c.dout, None, ctypes.byref(c.dims), 0, None, c.dx, c.dz,
+                               ctypes.byref(c.grads), None) == ENULL
+    assert lib.fastvim_ssm_bwd(c.x, c.z, c.dout, ctypes.byref(c.params), None, 0, None, c.dx, c.dz,
+                               ctypes.byref(c.grads), None) == ENULL
+    assert lib.fastvim_ssm_bwd(c.x, c.z, c.dout, ctypes.byref(c.params), ctypes.byref(c.dims), 0, None, c.dx, c.dz,
+                               None, None) == ENULL
+    for attr in ("x", "z", "dout", "dx", "dz"):
+        c = FakeBwd()
+        setattr(c, attr, None)
+        assert c.bwd() == ENULL, attr
+    for d in ("fwd", "bwd"):
+        for f in Bd.DIR_FIELDS:
+            c = FakeBwd()
+            setattr(getattr(c.params, d), f, None)
+            assert c.bwd() == ENULL
+            c = FakeBwd()
+            setattr(getattr(c.grads, d), f, None)
+            assert c.bwd() == ENULL
+    c = FakeBwd(K=3)
+    c.idx = None
+    assert c.bwd() == ENULL
+
+
+def test_bwd_unsupported_and_bad_flags():
+    for axis in (P.POOL_NONE_ROWMAJOR, P.POOL_NONE_COLMAJOR):
+        assert FakeBwd(axis=axis).bwd() == EUNSUP
+    assert FakeBwd(h=129).bwd() == EUNSUP
+    assert FakeBwd(N=8).bwd() == EUNSUP
+    for flags, code in ((P.FLAG_FUSED, EUNSUP), (P.FLAG_POST_NORM, EUNSUP), (8, EARG), (P.FLAG_STAGED, OK)):
+        c = FakeBwd()
+        c.params.flags = flags
+        if code != OK:
+            assert c.bwd() == code, flags
+    c = FakeBwd()
+    c.idx = c.dx + (1 << 30)
+    assert c.bwd() == EARG  # mask_idx with a dense layer
+
+
+def test_bwd_alignment():
+    for attr, off in (("dx", 4), ("dz", 8), ("dout", 4), ("x", 2)):
+        c = FakeBwd()
+        setattr(c, attr, getattr(c, attr) + off)
+        assert c.bwd() == EALIGN, attr
+    c = FakeBwd()
+    c.grads.fwd.A_log += 2
+    assert c.bwd() == EALIGN
+    c = FakeBwd()
+    c.params.workspace += 64
+    c.params.workspace_bytes += 256
+    assert c.bwd() == EALIGN
+
+
+def test_bwd_overlap():
+    c = FakeBwd()
+    c.dx = c.x
+    assert c.bwd() == EOVERLAP
+    c = FakeBwd()
+    c.dz = c.dx + 64
+    assert c.bwd() == EOVERLAP
+    c = FakeBwd()
+    c.params.workspace = c.dout
+    assert c.bwd() == EOVERLAP
+    c = FakeBwd()
+    c.grads.bwd.D = c.grads.fwd.D
+    assert c.bwd() == EOVERLAP
+    c = FakeBwd()
+    c.grads.fwd.x_proj_w = c.params.fwd.x_proj_w
+    assert c.bwd() == EOVERLAP
+    c = FakeBwd()
+    c.grads.fwd.D = c.params.workspace + 512
+    assert c.bwd() == EOVERLAP
+
+
+def test_bwd_workspace_checks():
+    c = FakeBwd()
+    c.params.workspace_bytes -= 1
+    assert c.bwd() == EWS
+    c = FakeBwd()
+    c.params.workspace = None
+    assert c.bwd() == EWS

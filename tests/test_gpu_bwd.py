@@ -1,0 +1,249 @@
+"""GPU parity of the backward pass: fastvim_ssm_bwd (through the C ABI)
+against the fp64 oracle's chain rule, which is pinned to central differences
+of the forward oracle.
+
+Every tensor is compared on its own scale, max|gpu - oracle| / max|oracle|:
+dx, dz, and the five parameter gradients of each direction.  A D = 0 twin
+repeats dx and dz with the skip removed, so the skip's share of them (which
+dominates at the workloads' parameter scales) cannot hide the scan adjoint.
+Bar: 1e-4 for fp32 I/O, 2e-2 for bf16 I/O (oracle on the bf16-rounded
+inputs and upstream gradient).  Full-size workloads run on the GPU at their
+real shape with the upstream gradient nonzero on a sample of images only:
+every gradient then comes from those images alone, so the oracle on the
+sample gives every parameter gradient, and the other images' dx and dz must
+be exactly zero.
+"""
+from __future__ import annotations
+
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import pooled_selective_state_amd as P
+from gpu_util import BF16_TOL, FP32_TOL, check, dev, dev_params, host
+from pins import rand_dir
+from pooled_selective_state_amd import configs as C
+from pooled_selective_state_amd.inputs import DIRECTIONS, draw_workload, random_mask, round_to_bf16, zero_D
+
+pytestmark = pytest.mark.gpu
+
+FIELDS = ("x_proj_w", "dt_proj_w", "dt_proj_b", "A_log", "D")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm GPU"
+    P.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def gpu_bwd(x, z, dout, prm, axis, idx=None, hw=None, dtype=torch.float32, flags=0):
+    idd = None if idx is None else dev(idx, torch.int32)
+    call = P.BwdCall(dev(x, dtype), dev(z, dtype), dev(dout, dtype), dev_params(prm), axis, mask_idx=idd, hw=hw,
+                     flags=flags)
+    res = call.run()
+    torch.cuda.synchronize()
+    return {"dx": host(res["dx"]), "dz": host(res["dz"]),
+            **{d: {f: host(res[d][f]) for f in FIELDS} for d in DIRECTIONS}}
+
+
+def compare(got, ref, tol, tag, sel=None, params=True):
+    s = slice(None) if sel is None else sel
+    check(got["dx"][s], ref["dx"], tol, tag + " dx")
+    check(got["dz"][s], ref["dz"], tol, tag + " dz")
+    if params:
+        for d in DIRECTIONS:
+            for f in FIELDS:
+                check(got[d][f], ref[d][f], tol, "%s d%s.%s" % (tag, d, f))
+
+
+def bwd_check(x, z, dout, prm, axis, tol, dtype, tag, idx=None, hw=None, twin=True):
+    """GPU gradients and those of the D = 0 twin against the oracle."""
+    got = gpu_bwd(x, z, dout, prm, axis, idx=idx, hw=hw, dtype=dtype)
+    ref = oracle.layer_bwd(x, z, dout, prm["fwd"], prm["bwd"], axis, idx=idx, hw=hw)
+    compare(got, ref, tol, tag)
+    if twin:
+        p0 = zero_D(prm)
+        got0 = gpu_bwd(x, z, dout, p0, axis, idx=idx, hw=hw, dtype=dtype)
+        ref0 = oracle.layer_bwd(x, z, dout, p0["fwd"], p0["bwd"], axis, idx=idx, hw=hw)
+        compare(got0, ref0, tol, tag + " (D=0)", params=False)
+    return got
+
+
+def _io(io, *arrays):
+    if io == "bf16":
+        return [round_to_bf16(a) for a in arrays]
+    return list(arrays)
+
+
+def _tol(io):
+    return (FP32_TOL, torch.float32) if io == "f32" else (BF16_TOL, torch.bfloat16)
+
+
+# ------------------------------------------------------------------ small / ragged
+@pytest.mark.parametrize("axis", (P.POOL_COLS, P.POOL_ROWS))
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_bwd_tiny_fastvim_t(axis, io):
+    wl = draw_workload(C.TINY)
+    rng = np.random.default_rng(11 + axis)
+    dout = rng.standard_normal(wl["x"].shape).astype(np.float32)
+    x, z, dout = _io(io, wl["x"], wl["z"][0], dout)
+    tol, dt = _tol(io)
+    bwd_check(x, z, dout, wl["params"][0], axis, tol, dt, "tiny %s axis %d" % (io, axis))
+
+
+RAGGED = [
+    # B, h, w, E, R   (E not a multiple of 64, scan lengths not multiples of 16, every dt-rank bound)
+    (3, 13, 7, 72, 5),
+    (1, 1, 1, 8, 1),
+    (2, 5, 9, 200, 20),
+    (2, 3, 33, 136, 64),
+    (1, 37, 2, 1032, 33),
+    (2, 128, 3, 40, 12),
+    (2, 17, 100, 64, 40),
+]
+
+
+@pytest.mark.parametrize("shape", RAGGED, ids=["x".join(map(str, s)) for s in RAGGED])
+@pytest.mark.parametrize("axis", (P.POOL_COLS, P.POOL_ROWS))
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_bwd_ragged_shapes(shape, axis, io):
+    B, h, w, E, R = shape
+    if (h if axis == P.POOL_COLS else w) > 128:
+        pytest.skip("scan longer than the backward pass supports")
+    rng = np.random.default_rng(zlib.crc32(repr(("bwd", shape, axis, io)).encode()))
+    x = rng.standard_normal((B, h, w, E)).astype(np.float32)
+    z = rng.standard_normal((B, h, w, E)).astype(np.float32)
+    dout = rng.standard_normal((B, h, w, E)).astype(np.float32)
+    x, z, dout = _io(io, x, z, dout)
+    prm = {"fwd": rand_dir(rng, E, 16, R, 0.1), "bwd": rand_dir(rng, E, 16, R, 0.1)}
+    tol, dt = _tol(io)
+    bwd_check(x, z, dout, prm, axis, tol, dt, "ragged %s %s axis %d" % (shape, io, axis))
+
+
+@pytest.mark.parametrize("axis", (P.POOL_COLS, P.POOL_ROWS))
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("K", [1, 17, 42])
+def test_bwd_masked_small(axis, io, K):
+    B, h, w, E, R = 5, 6, 7, 64, 6
+    rng = np.random.default_rng(200 + K + 7 * axis)
+    x = rng.standard_normal((B, K, E)).astype(np.float32)
+    z = rng.standard_normal((B, K, E)).astype(np.float32)
+    dout = rng.standard_normal((B, K, E)).astype(np.float32)
+    x, z, dout = _io(io, x, z, dout)
+    idx = random_mask(rng, B, h, w, K)
+    prm = {"fwd": rand_dir(rng, E, 16, R, 0.1), "bwd": rand_dir(rng, E, 16, R, 0.1)}
+    tol, dt = _tol(io)
+    bwd_check(x, z, dout, prm, axis, tol, dt, "masked K=%d %s axis %d" % (K, io, axis), idx=idx, hw=(h, w))
+
+
+def test_bwd_masked_invalid_indices():
+    """Tokens with an out-of-range or repeated index get NaN in dx and dz and
+    take no part in any sum: the rest equals the oracle on the valid tokens."""
+    B, h, w, E, R, K = 3, 5, 6, 48, 4, 9
+    rng = np.random.default_rng(19)
+    idx = random_mask(rng, B, h, w, K)
+    idx[0, 2] = h * w
+    idx[1, 4] = idx[1, 7]
+    idx[2, 0] = -5
+    x, z, dout = (rng.standard_normal((B, K, E)).astype(np.float32) for _ in range(3))
+    prm = {"fwd": rand_dir(rng, E, 16, R, 0.1), "bwd": rand_dir(rng, E, 16, R, 0.1)}
+    got = gpu_bwd(x, z, dout, prm, P.POOL_COLS, idx=idx, hw=(h, w))
+    invalid = {(0, 2), (1, 4), (1, 7), (2, 0)}
+    sums = {d: {f: 0.0 for f in FIELDS} for d in DIRECTIONS}
+    for b in range(B):
+        keep = [k for k in range(K) if (b, k) not in invalid]
+        bad = [k for k in range(K) if (b, k) in invalid]
+        for name in ("dx", "dz"):
+            assert np.all(np.isnan(got[name][b, bad])), "invalid token of image %d not NaN in %s" % (b, name)
+        ref = oracle.layer_bwd(x[b:b + 1, keep], z[b:b + 1, keep], dout[b:b + 1, keep], prm["fwd"], prm["bwd"],
+                               P.POOL_COLS, idx=idx[b:b + 1, keep], hw=(h, w))
+        check(got["dx"][b:b + 1, keep], ref["dx"], FP32_TOL, "invalid-index image %d dx" % b)
+        check(got["dz"][b:b + 1, keep], ref["dz"], FP32_TOL, "invalid-index image %d dz" % b)
+        for d in DIRECTIONS:
+            for f in FIELDS:
+                sums[d][f] = sums[d][f] + ref[d][f]
+    for d in DIRECTIONS:
+        for f in FIELDS:
+            check(got[d][f], sums[d][f], FP32_TOL, "invalid-index d%s.%s" % (d, f))
+
+
+def test_bwd_empty_batch_zero_gradients():
+    E, R = 16, 3
+    rng = np.random.default_rng(3)
+    prm = dev_params({d: rand_dir(rng, E, 16, R) for d in DIRECTIONS})
+    x = torch.empty((0, 3, 4, E), device="cuda")
+    grads = {d: {f: torch.full_like(prm[d][f], 7.0) for f in FIELDS} for d in DIRECTIONS}
+    call = P.BwdCall(x, x.clone(), x.clone(), prm, P.POOL_COLS, grads=grads)
+    res = call.run()
+    torch.cuda.synchronize()
+    for d in DIRECTIONS:
+        for f in FIELDS:
+            assert torch.count_nonzero(res[d][f]).item() == 0
+
+
+def test_bwd_deterministic():
+    """Fixed-order sums: two calls give bitwise identical gradients."""
+    B, h, w, E, R = 4, 24, 20, 136, 12
+    rng = np.random.default_rng(5)
+    x, z, dout = (rng.standard_normal((B, h, w, E)).astype(np.float32) for _ in range(3))
+    prm = {"fwd": rand_dir(rng, E, 16, R, 0.1), "bwd": rand_dir(rng, E, 16, R, 0.1)}
+    a = gpu_bwd(x, z, dout, prm, P.POOL_ROWS)
+    b = gpu_bwd(x, z, dout, prm, P.POOL_ROWS)
+    for k in ("dx", "dz"):
+        assert np.array_equal(a[k], b[k])
+    for d in DIRECTIONS:
+        for f in FIELDS:
+            assert np.array_equal(a[d][f], b[d][f])
+
+
+def test_bwd_rows_is_cols_on_transposed_grid():
+    """ROWS gradients are the COLS gradients of the transposed grid."""
+    B, h, w, E, R = 2, 9, 14, 64, 8
+    rng = np.random.default_rng(6)
+    x, z, dout = (rng.standard_normal((B, h, w, E)).astype(np.float32) for _ in range(3))
+    prm = {"fwd": rand_dir(rng, E, 16, R, 0.1), "bwd": rand_dir(rng, E, 16, R, 0.1)}
+    r = gpu_bwd(x, z, dout, prm, P.POOL_ROWS)
+    t = gpu_bwd(*(np.ascontiguousarray(a.transpose(0, 2, 1, 3)) for a in (x, z, dout)), prm, P.POOL_COLS)
+    check(r["dx"], t["dx"].transpose(0, 2, 1, 3), FP32_TOL, "transpose dx")
+    check(r["dz"], t["dz"].transpose(0, 2, 1, 3), FP32_TOL, "transpose dz")
+    for d in DIRECTIONS:
+        for f in FIELDS:
+            check(r[d][f], t[d][f], FP32_TOL, "transpose d%s.%s" % (d, f))
+
+
+# ------------------------------------------------------------------ full size
+def _sampled_full_size(cfg, axis=P.POOL_COLS):
+    wl = draw_workload(cfg)
+    x, z, prm, idx = wl["x"], wl["z"][0], wl["params"][0], wl["idx"]
+    sel = np.array([0, cfg.B - 1])
+    rng = np.random.default_rng(77)
+    dout = np.zeros_like(x)
+    dout[sel] = rng.standard_normal(dout[sel].shape).astype(np.float32)
+    if cfg.io_dtype == "bf16":
+        dout = round_to_bf16(dout)
+    tol, dt = _tol(cfg.io_dtype)
+    hw = (cfg.h, cfg.w) if cfg.masked else None
+    print("\n[%s bwd] B=%d grid=%dx%d E=%d, upstream gradient on images %s" % (cfg.name, cfg.B, cfg.h, cfg.w, cfg.E,
+                                                                           list(sel)), flush=True)
+    got = gpu_bwd(x, z, dout, prm, axis, idx=idx, hw=hw, dtype=dt)
+    rest = np.setdiff1d(np.arange(cfg.B), sel)
+    for name in ("dx", "dz"):
+        assert np.count_nonzero(got[name][rest]) == 0, name + " nonzero on images without upstream gradient"
+    ref = oracle.layer_bwd(x[sel], z[sel], dout[sel], prm["fwd"], prm["bwd"], axis,
+                           idx=None if idx is None else idx[sel], hw=hw)
+    compare(got, ref, tol, cfg.name, sel=sel)
+
+
+@pytest.mark.parametrize("axis", (P.POOL_COLS, P.POOL_ROWS))
+def test_bwd_full_size_2048(axis):
+    _sampled_full_size(C.HIRES_2048, axis)
+
+
+@pytest.mark.parametrize("cfg", [C.SHORT_224_S, C.MASKED_B], ids=lambda c: c.name)
+def test_bwd_full_size_other(cfg):
+    _sampled_full_size(cfg)
