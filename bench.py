@@ -278,6 +278,21 @@ def main():
         extras["post_norm_2048"] = {"layer_ms": ln_ms, "epilogue_ms": ln_epi, "path": "stage kernels",
                                     "epilogue_GBps": alg_bytes / (ln_epi * 1e-3) / 1e9}
         del ncall
+        # the backward pass (gradients of sum(dout * out)) on the same inputs
+        g_b = torch.Generator(device="cuda").manual_seed(2)
+        dout = torch.randn(x.shape, device=dev, generator=g_b)
+        bwd_bytes = 5 * 4 * elems  # x, z, dout read once, dx, dz written once (fp32)
+        extras["backward_2048"] = {"alg_bytes": bwd_bytes, "path": "stage kernels, two full-resolution passes"}
+        for name, axis in (("cols", P.POOL_COLS), ("rows", P.POOL_ROWS)):
+            bcall = P.BwdCall(x, z, dout, prm, axis)
+            bcall.run(stream)
+            b_ms, _ = time_steps(lambda: bcall.run(stream), n, stream)
+            extras["backward_2048"][name] = {"ms": b_ms, "images_per_s": cfg.B / (b_ms * 1e-3),
+                                             "GBps": bwd_bytes / (b_ms * 1e-3) / 1e9,
+                                             "hbm_frac": bwd_bytes / (b_ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+            del bcall
+        del dout
+        log("backward %.3f ms (cols)" % extras["backward_2048"]["cols"]["ms"])
         # torch's device copy, for comparison with the calibration copy
         dst = torch.empty_like(x)
         tc_ms, _ = time_steps(lambda: dst.copy_(x), 3, stream)

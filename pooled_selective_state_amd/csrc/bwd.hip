@@ -258,9 +258,10 @@ bwd_du_kernel(const float* __restrict__ du_f, const float* __restrict__ du_b, co
 // --------------------------------------------------------------------- dwx
 // Partial of d x_proj_w over one chunk of kBwdTokChunk pooled tokens:
 //   dWxp[chunk, d, o, e] = sum_{m in chunk} dv[m, d, o] u[m, e]
-// Lane = channel, wave w takes the outputs o = w * kOG ... (wave-uniform dv
-// loads).
+// Lane = channel, wave w takes the outputs o = w * og ... (wave-uniform dv
+// loads); the token values of 8 tokens are loaded before their products.
 constexpr int kOG = 24;  // outputs per wave: NX <= 96
+constexpr int kDwxU = 8;  // tokens in flight per lane
 __global__ void __launch_bounds__(256)
 bwd_dwx_kernel(const float* __restrict__ dv, const float* __restrict__ u, float* __restrict__ dWxp, int64_t M,
                int64_t E, int NX) {
@@ -277,12 +278,18 @@ bwd_dwx_kernel(const float* __restrict__ dv, const float* __restrict__ u, float*
     float acc[kOG];
 #pragma unroll
     for (int i = 0; i < kOG; ++i) acc[i] = 0.f;
-    for (int64_t m = m0; m < m1; ++m) {
-        const float uv = u[m * E + ec];
-        const float* dvr = dv + (m * 2 + d) * NX;
+    for (int64_t mb = m0; mb < m1; mb += kDwxU) {
+        float uv[kDwxU];
 #pragma unroll
-        for (int i = 0; i < kOG; ++i)
-            if (i < og && o0 + i < NX) acc[i] = fmaf(dvr[o0 + i], uv, acc[i]);
+        for (int k = 0; k < kDwxU; ++k) uv[k] = mb + k < m1 ? u[(mb + k) * E + ec] : 0.f;
+#pragma unroll
+        for (int k = 0; k < kDwxU; ++k) {
+            const int64_t m = mb + k < m1 ? mb + k : m1 - 1;  // past the chunk: a zero token value
+            const float* dvr = dv + (m * 2 + d) * NX;
+#pragma unroll
+            for (int i = 0; i < kOG; ++i)
+                if (i < og && o0 + i < NX) acc[i] = fmaf(dvr[o0 + i], uv[k], acc[i]);
+        }
     }
     if (e < E) {
 #pragma unroll
@@ -292,18 +299,30 @@ bwd_dwx_kernel(const float* __restrict__ dv, const float* __restrict__ u, float*
 }
 
 // ------------------------------------------------------------------ colsum
-// out[c, j] = sum_{i in rows [c rpb, (c + 1) rpb)} in[i ld + j]
+// out[c, j] = sum_{i in rows [c rpb, (c + 1) rpb)} in[i ld + j].  A workgroup
+// takes 32 columns and one row chunk: 8 row groups of 32 lanes, group g
+// summing rows g, g + 8, ...; the 8 group sums are added in a fixed order.
+constexpr int kColTile = 32;
+constexpr int kColGroups = 8;
 __global__ void __launch_bounds__(256)
 colsum_kernel(const float* __restrict__ in, int64_t rows, int64_t cols, int64_t ld, int64_t rpb,
               float* __restrict__ out, float* __restrict__ out2) {
-    const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (j >= cols) return;
+    __shared__ float part[kColGroups][kColTile];
+    const int cl = threadIdx.x % kColTile, g = threadIdx.x / kColTile;
+    const int64_t j = (int64_t)blockIdx.x * kColTile + cl;
     const int64_t c = blockIdx.y;
     const int64_t r0 = c * rpb, r1 = r0 + rpb < rows ? r0 + rpb : rows;
     float s = 0.f;
-    for (int64_t i = r0; i < r1; ++i) s += in[i * ld + j];
-    out[c * cols + j] = s;
-    if (out2) out2[c * cols + j] = s;
+    if (j < cols)
+        for (int64_t i = r0 + g; i < r1; i += kColGroups) s += in[i * ld + j];
+    part[g][cl] = s;
+    __syncthreads();
+    if (g == 0 && j < cols) {
+#pragma unroll
+        for (int k = 1; k < kColGroups; ++k) s += part[k][cl];
+        out[c * cols + j] = s;
+        if (out2) out2[c * cols + j] = s;
+    }
 }
 
 __global__ void __launch_bounds__(256) fill_zero_kernel(float* __restrict__ p, int64_t n) {
@@ -476,7 +495,7 @@ hipError_t launch_bwd_dwx(const Geom& g, const BwdWorkspace& ws, hipStream_t st)
 
 hipError_t launch_colsum(const float* in, int64_t rows, int64_t cols, int64_t ld, float* out, float* out2,
                          float* tmp, hipStream_t st) {
-    const unsigned cb = (unsigned)((cols + 255) / 256);
+    const unsigned cb = (unsigned)((cols + kColTile - 1) / kColTile);
     if (rows <= kColRowsPerBlock) {
         hipLaunchKernelGGL(colsum_kernel, dim3(cb, 1), dim3(256), 0, st, in, rows, cols, ld, rows, out, out2);
         return hipGetLastError();

@@ -8,8 +8,8 @@ namespace fastvim {
 
 constexpr int kBwdTMax = 128;        // longest scan the backward kernels take (sequence rows held in LDS)
 constexpr int kBwdCh = 64;           // channels per scan-adjoint workgroup (one channel group)
-constexpr int kBwdTokChunk = 256;    // pooled tokens per partial of d x_proj_w
-constexpr int kColRowsPerBlock = 128;  // rows per first-stage block of a column sum
+constexpr int kBwdTokChunk = 64;     // pooled tokens per partial of d x_proj_w
+constexpr int kColRowsPerBlock = 256;  // rows per first-stage block of a column sum
 
 // Workspace of one backward call (every region 256-byte aligned).  fwd views
 // the part shared with the forward stages (u, xdbl, s_f, s_b, rows, bad).
