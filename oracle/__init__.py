@@ -94,9 +94,11 @@ class Oracle:
             vp, vp, ctypes.POINTER(_Dir), ctypes.POINTER(_Dir),
             i64, i64, i64, i64, i64, i64, i64, ci, vp,
             vp, vp, vp, ctypes.POINTER(_DirOut), ctypes.POINTER(_DirOut),
-            vp, vp, ctypes.c_double,
+            vp, vp, ctypes.c_double, vp, vp, i64,
         ]
         lib.fvo_layer.restype = ci
+        lib.fvo_conv_silu.argtypes = [vp, i64, i64, i64, i64, ci, vp, vp, i64, vp]
+        lib.fvo_conv_silu.restype = ci
         lib.fvo_layer_bwd.argtypes = [
             vp, vp, vp, ctypes.POINTER(_Dir), ctypes.POINTER(_Dir),
             i64, i64, i64, i64, i64, i64, i64, ci, vp,
@@ -176,14 +178,34 @@ class Oracle:
                            1 if reverse else 0, _ptr(rs), _ptr(s))
         return s
 
-    def layer(self, x, z, fwd, bwd, axis, idx=None, hw=None, stages=False, ln=None):
+    def conv_silu(self, x, axis, conv):
+        """x_conv (B,h,w,E) fp64: the depthwise causal Conv1D (conv["weight"]
+        (E, KC), oldest tap first; conv["bias"] (E,)) along the oriented grid's
+        sequence, then SiLU."""
+        x = _f32(x)
+        Wc, bc = _f32(conv["weight"]), _f32(conv["bias"])
+        B, h, w, E = x.shape
+        xc = np.empty(x.shape, np.float64)
+        rc = self._lib.fvo_conv_silu(_ptr(x), B, h, w, E, axis, _ptr(Wc), _ptr(bc), Wc.shape[1], _ptr(xc))
+        if rc:
+            raise ValueError("fvo_conv_silu failed: %d" % rc)
+        return xc
+
+    def layer(self, x, z, fwd, bwd, axis, idx=None, hw=None, stages=False, ln=None, conv=None):
         """Full layer.  Dense: x, z (B,h,w,E).  Masked: x, z (B,K,E), idx (B,K),
         hw=(h, w).  fwd / bwd: dicts with x_proj_w, dt_proj_w, dt_proj_b, A_log, D.
         ln: None, or {"weight": (E,), "bias": (E,), "eps": float} for the
-        post-SSM LayerNorm before the gate.
+        post-SSM LayerNorm before the gate.  conv: None, or {"weight": (E, KC),
+        "bias": (E,)}: x is then the Conv1D's input and the layer runs on
+        conv_silu(x) (dense layers only).
         Returns out (fp64), or with stages=True a dict of out, u, rows and the
         per-direction v, delta, s."""
         x, z = _f32(x), _f32(z)
+        conv_w = conv_b = None
+        conv_k = 0
+        if conv is not None:
+            conv_w, conv_b = _f32(conv["weight"]), _f32(conv["bias"])
+            conv_k = conv_w.shape[1]
         ln_w = ln_b = None
         ln_eps = 0.0
         if ln is not None:
@@ -224,7 +246,7 @@ class Oracle:
             _ptr(out), _ptr(u), _ptr(rows),
             ctypes.byref(fo) if fo is not None else None,
             ctypes.byref(bo) if bo is not None else None,
-            _ptr(ln_w), _ptr(ln_b), ln_eps,
+            _ptr(ln_w), _ptr(ln_b), ln_eps, _ptr(conv_w), _ptr(conv_b), conv_k,
         )
         if rc:
             raise ValueError("fvo_layer failed: %d" % rc)
@@ -330,8 +352,12 @@ def scan(u, dlt, v, A_log, R, reverse=False, reset=None):
     return get().scan(u, dlt, v, A_log, R, reverse=reverse, reset=reset)
 
 
-def layer(x, z, fwd, bwd, axis, idx=None, hw=None, stages=False, ln=None):
-    return get().layer(x, z, fwd, bwd, axis, idx=idx, hw=hw, stages=stages, ln=ln)
+def layer(x, z, fwd, bwd, axis, idx=None, hw=None, stages=False, ln=None, conv=None):
+    return get().layer(x, z, fwd, bwd, axis, idx=idx, hw=hw, stages=stages, ln=ln, conv=conv)
+
+
+def conv_silu(x, axis, conv):
+    return get().conv_silu(x, axis, conv)
 
 
 def layer_bwd(x, z, dout, fwd, bwd, axis, idx=None, hw=None, stages=False):

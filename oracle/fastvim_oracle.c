@@ -101,10 +101,21 @@ static int64_t seq_pos(int axis, int64_t h, int64_t w, int64_t i, int64_t j)
  * bullet 5].  With no pooling u is x itself, read in scan order.
  *   u[b, t, e] = (1/P) * sum_{cells (i,j) with seq_pos(i,j) = t} x[b, i, j, e]
  */
+static void pool_dense_any(const float *x, const double *xd, int64_t B, int64_t h, int64_t w, int64_t E,
+                           int axis, double *u);
+
 int fvo_pool_dense(const float *x, int64_t B, int64_t h, int64_t w, int64_t E, int axis, double *u)
 {
-    int64_t T, P;
     if (axis < 0 || axis > 3) return -2;
+    pool_dense_any(x, NULL, B, h, w, E, axis, u);
+    return 0;
+}
+
+/* The same, reading x from xd (double) when xd is given. */
+static void pool_dense_any(const float *x, const double *xd, int64_t B, int64_t h, int64_t w, int64_t E,
+                           int axis, double *u)
+{
+    int64_t T, P;
     seq_shape(axis, h, w, &T, &P);
 #pragma omp parallel for schedule(static)
     for (int64_t b = 0; b < B; ++b) {
@@ -113,11 +124,46 @@ int fvo_pool_dense(const float *x, int64_t B, int64_t h, int64_t w, int64_t E, i
         for (int64_t i = 0; i < h; ++i)
             for (int64_t j = 0; j < w; ++j) {
                 const int64_t t = seq_pos(axis, h, w, i, j);
-                const float *xv = x + ((b * h + i) * w + j) * E;
-                for (int64_t e = 0; e < E; ++e) ub[t * E + e] += (double)xv[e];
+                const int64_t c = ((b * h + i) * w + j) * E;
+                for (int64_t e = 0; e < E; ++e) ub[t * E + e] += xd ? xd[c + e] : (double)x[c + e];
             }
         for (int64_t k = 0; k < T * E; ++k) ub[k] /= (double)P;
     }
+}
+
+/*
+ * Producer side: depthwise causal Conv1D and SiLU on the token sequence of
+ * the oriented grid.  [FastVim summary, 方法详解 bullets 1-2: the grid is
+ * pooled after the Conv1D; Vim article 2.1: conv1d then the SSM, per
+ * direction in Vim, one shared x here.]  The sequence is the flattened
+ * oriented grid, the scan order of the unpooled layer: row-major
+ * (r = i*w + j) for COLS and NONE_ROWMAJOR, column-major (r = j*h + i) for ROWS
+ * and NONE_COLMAJOR.  With KC taps per channel (the oldest first):
+ *   xc[b, cell(r), e] = silu(conv_b[e] + sum_{k<KC} conv_w[e, k] x[b, cell(r - KC + 1 + k), e])
+ * where positions before the start of the sequence contribute zero.
+ * xc has x's (B, h, w, E) layout.
+ */
+int fvo_conv_silu(const float *x, int64_t B, int64_t h, int64_t w, int64_t E, int axis, const float *conv_w,
+                  const float *conv_b, int64_t KC, double *xc)
+{
+    if (axis < 0 || axis > 3) return -2;
+    const int colmajor = axis == FVO_ROWS || axis == FVO_NONE_COLMAJOR;
+    const int64_t n = h * w;
+#pragma omp parallel for schedule(static)
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t r = 0; r < n; ++r) {
+            const int64_t cell = colmajor ? (r % h) * w + r / h : r;
+            for (int64_t e = 0; e < E; ++e) {
+                double acc = (double)conv_b[e];
+                for (int64_t k = 0; k < KC; ++k) {
+                    const int64_t rr = r - KC + 1 + k;
+                    if (rr < 0) continue;
+                    const int64_t cc = colmajor ? (rr % h) * w + rr / h : rr;
+                    acc += (double)conv_w[e * KC + k] * (double)x[(b * n + cc) * E + e];
+                }
+                xc[(b * n + cell) * E + e] = acc / (1.0 + exp(-acc));
+            }
+        }
     return 0;
 }
 
@@ -301,12 +347,12 @@ static int run_direction(const double *u, int64_t B, int64_t T, int64_t E, int64
  *   mean = sum_e y[e] / E,  var = sum_e (y[e] - mean)^2 / E,
  * and finally the gate, out[e] = y[e] * silu(z[e]).  y is caller scratch.
  */
-static void output_token(const double *sf, const double *sb, const float *x, const float *z, const fvo_dir *pf,
-                         const fvo_dir *pb, int64_t E, const float *ln_w, const float *ln_b, double ln_eps,
-                         double *y, double *out)
+static void output_token(const double *sf, const double *sb, const float *x, const double *xd, const float *z,
+                         const fvo_dir *pf, const fvo_dir *pb, int64_t E, const float *ln_w, const float *ln_b,
+                         double ln_eps, double *y, double *out)
 {
     for (int64_t e = 0; e < E; ++e) {
-        const double skip = ((double)pf->D[e] + (double)pb->D[e]) * (double)x[e];
+        const double skip = ((double)pf->D[e] + (double)pb->D[e]) * (xd ? xd[e] : (double)x[e]);
         y[e] = sf[e] + sb[e] + skip;
     }
     if (ln_w) {
@@ -324,24 +370,29 @@ static void output_token(const double *sf, const double *sb, const float *x, con
     for (int64_t e = 0; e < E; ++e) out[e] = y[e] * silu((double)z[e]);
 }
 
-/* ln_w == NULL: no post-SSM LayerNorm. */
+/* ln_w == NULL: no post-SSM LayerNorm.  conv_w == NULL: x is the layer's
+ * input itself; else x is the Conv1D's input and the layer runs on
+ * fvo_conv_silu(x) (dense layers only). */
 int fvo_layer(const float *x, const float *z, const fvo_dir *pf, const fvo_dir *pb, int64_t B, int64_t h,
               int64_t w, int64_t E, int64_t N, int64_t R, int64_t K, int axis, const int32_t *idx,
               double *out, double *u_out, int32_t *rows_out, fvo_dir_out *fwd, fvo_dir_out *bwd,
-              const float *ln_w, const float *ln_b, double ln_eps)
+              const float *ln_w, const float *ln_b, double ln_eps, const float *conv_w, const float *conv_b,
+              int64_t conv_k)
 {
     int64_t T, P;
     const int masked = idx != NULL;
-    if (axis < 0 || axis > 3 || (masked && axis > FVO_ROWS)) return -2;
+    if (axis < 0 || axis > 3 || (masked && axis > FVO_ROWS) || (masked && conv_w)) return -2;
     seq_shape(axis, h, w, &T, &P);
     const int64_t M = B * T;
 
     double *u = u_out ? u_out : (double *)malloc((size_t)(M * E) * sizeof(double));
     double *sf = fwd && fwd->s ? fwd->s : (double *)malloc((size_t)(M * E) * sizeof(double));
     double *sb = bwd && bwd->s ? bwd->s : (double *)malloc((size_t)(M * E) * sizeof(double));
+    double *xc = conv_w ? (double *)malloc((size_t)(B * h * w * E) * sizeof(double)) : NULL;
     int32_t *rows = NULL;
     int rc = 0;
-    if (!u || !sf || !sb) { rc = -9; goto done; }
+    if (!u || !sf || !sb || (conv_w && !xc)) { rc = -9; goto done; }
+    if (conv_w) fvo_conv_silu(x, B, h, w, E, axis, conv_w, conv_b, conv_k, xc);
 
     if (masked) {
         rows = rows_out ? rows_out : (int32_t *)malloc((size_t)(B * K) * sizeof(int32_t));
@@ -350,7 +401,7 @@ int fvo_layer(const float *x, const float *z, const fvo_dir *pf, const fvo_dir *
         if (rc) goto done;
         fvo_pool_masked(x, rows, B, K, T, P, E, u);
     } else {
-        fvo_pool_dense(x, B, h, w, E, axis, u);
+        pool_dense_any(x, xc, B, h, w, E, axis, u);
     }
 
     rc = run_direction(u, B, T, E, N, R, pf, 0, fwd, sf);
@@ -364,8 +415,8 @@ int fvo_layer(const float *x, const float *z, const fvo_dir *pf, const fvo_dir *
             double *y = (double *)malloc((size_t)E * sizeof(double));
             for (int64_t k = 0; y && k < K; ++k) {
                 const int64_t t = rows[b * K + k], c = (b * K + k) * E;
-                output_token(sf + (b * T + t) * E, sb + (b * T + t) * E, x + c, z + c, pf, pb, E, ln_w, ln_b,
-                             ln_eps, y, out + c);
+                output_token(sf + (b * T + t) * E, sb + (b * T + t) * E, x + c, NULL, z + c, pf, pb, E, ln_w,
+                             ln_b, ln_eps, y, out + c);
             }
             free(y);
         }
@@ -376,14 +427,15 @@ int fvo_layer(const float *x, const float *z, const fvo_dir *pf, const fvo_dir *
             for (int64_t i = 0; y && i < h; ++i)
                 for (int64_t j = 0; j < w; ++j) {
                     const int64_t t = seq_pos(axis, h, w, i, j), c = ((b * h + i) * w + j) * E;
-                    output_token(sf + (b * T + t) * E, sb + (b * T + t) * E, x + c, z + c, pf, pb, E, ln_w, ln_b,
-                                 ln_eps, y, out + c);
+                    output_token(sf + (b * T + t) * E, sb + (b * T + t) * E, x + c, xc ? xc + c : NULL, z + c, pf,
+                                 pb, E, ln_w, ln_b, ln_eps, y, out + c);
                 }
             free(y);
         }
     }
 
 done:
+    free(xc);
     if (!u_out) free(u);
     if (!(fwd && fwd->s)) free(sf);
     if (!(bwd && bwd->s)) free(sb);

@@ -592,6 +592,101 @@ def pin_bwd_masked_equals_zero_filled(O):
             _close(gm[name], np.stack([flat[b, idx[b]] for b in range(B_)]), tol=1e-12, what="masked " + name)
 
 
+# ---------------------------------------------------------------- producer Conv1D
+def rand_conv(rng, E, KC=4):
+    return {"weight": rng.uniform(-0.8, 0.8, (E, KC)).astype(np.float32),
+            "bias": rng.uniform(-0.3, 0.3, E).astype(np.float32)}
+
+
+def _oriented_seq(x, axis):
+    """(B, h*w, E) view of x in the oriented grid's sequence order."""
+    B, h, w, E = x.shape
+    if axis in (ROWS, NONE_COLMAJOR):
+        return np.ascontiguousarray(x.transpose(0, 2, 1, 3)).reshape(B, h * w, E)
+    return x.reshape(B, h * w, E)
+
+
+def pin_conv_library(O):
+    """The producer's causal depthwise Conv1D + SiLU equals numpy's full
+    convolution truncated to the sequence (taps reversed, oldest first), then
+    x * sigmoid(x), along the oriented grid's sequence (both orders)."""
+    rng = np.random.default_rng(50)
+    B_, h, w, E = 2, 5, 3, 6
+    x = rng.standard_normal((B_, h, w, E)).astype(np.float32)
+    for KC in (4, 2):
+        conv = rand_conv(rng, E, KC)
+        for axis in (COLS, ROWS, NONE_ROWMAJOR, NONE_COLMAJOR):
+            xc = O.conv_silu(x, axis, conv)
+            seq = _oriented_seq(x.astype(np.float64), axis)
+            got = _oriented_seq(xc, axis)
+            for b in range(B_):
+                for e in range(E):
+                    a = np.convolve(seq[b, :, e], conv["weight"][e, ::-1].astype(np.float64))[: h * w]
+                    a = a + float(conv["bias"][e])
+                    _close(got[b, :, e], a * expit(a), what="conv KC=%d axis %d" % (KC, axis))
+
+
+def pin_conv_closed_forms(O):
+    """Identity taps (only the newest, weight 1, bias 0) pool silu(x); with
+    x_proj_w = 0 the scan is zero and out = (D_fwd + D_bwd) silu(x) silu(z)
+    exactly, for any taps."""
+    rng = np.random.default_rng(51)
+    B_, h, w, E, N, R = 2, 4, 5, 7, 4, 3
+    x = rng.standard_normal((B_, h, w, E)).astype(np.float32)
+    z = rng.standard_normal((B_, h, w, E)).astype(np.float32)
+    pf, pb = rand_dir(rng, E, N, R), rand_dir(rng, E, N, R)
+    ident = {"weight": np.zeros((E, 4), np.float32), "bias": np.zeros(E, np.float32)}
+    ident["weight"][:, 3] = 1.0
+    for axis in (COLS, ROWS):
+        st = O.layer(x, z, pf, pb, axis, stages=True, conv=ident)
+        sx = silu(x)
+        ref_u = sx.mean(axis=2) if axis == COLS else sx.mean(axis=1)
+        _close(st["u"], ref_u, what="identity-tap pooled tokens")
+        conv = rand_conv(rng, E)
+        pf0, pb0 = dict(pf), dict(pb)
+        pf0["x_proj_w"] = np.zeros_like(pf["x_proj_w"])
+        pb0["x_proj_w"] = np.zeros_like(pb["x_proj_w"])
+        out = O.layer(x, z, pf0, pb0, axis, conv=conv)
+        Ds = pf["D"].astype(np.float64) + pb["D"].astype(np.float64)
+        _close(out, Ds * O.conv_silu(x, axis, conv) * silu(z), what="conv with zero projection")
+
+
+def pin_conv_transpose(O):
+    """With the Conv1D, ROWS is COLS on the transposed grid (the conv follows
+    the orientation, as the scan does)."""
+    rng = np.random.default_rng(52)
+    B_, h, w, E, N, R = 2, 4, 6, 5, 4, 2
+    x = rng.standard_normal((B_, h, w, E)).astype(np.float32)
+    z = rng.standard_normal((B_, h, w, E)).astype(np.float32)
+    pf, pb = rand_dir(rng, E, N, R), rand_dir(rng, E, N, R)
+    conv = rand_conv(rng, E)
+    r = O.layer(x, z, pf, pb, ROWS, conv=conv)
+    xt, zt = (np.ascontiguousarray(a.transpose(0, 2, 1, 3)) for a in (x, z))
+    c = O.layer(xt, zt, pf, pb, COLS, conv=conv)
+    _close(r, c.transpose(0, 2, 1, 3), what="conv ROWS = COLS transposed")
+
+
+def pin_conv_causal(O):
+    """Changing x at one position of the sequence changes the conv output at
+    that position and the next KC - 1 only, in every channel."""
+    rng = np.random.default_rng(53)
+    B_, h, w, E, KC = 1, 4, 5, 3, 4
+    x = rng.standard_normal((B_, h, w, E)).astype(np.float32)
+    conv = rand_conv(rng, E, KC)
+    for axis in (COLS, ROWS):
+        base = _oriented_seq(O.conv_silu(x, axis, conv), axis)
+        for r0 in (0, 6, h * w - 2):
+            seq = _oriented_seq(x, axis).copy()
+            seq[:, r0] += 1.0
+            if axis == ROWS:
+                x2 = np.ascontiguousarray(seq.reshape(B_, w, h, E).transpose(0, 2, 1, 3))
+            else:
+                x2 = seq.reshape(B_, h, w, E)
+            diff = np.abs(_oriented_seq(O.conv_silu(x2, axis, conv), axis) - base).max(axis=(0, 2))
+            changed = set(np.nonzero(diff > 0)[0].tolist())
+            assert changed == set(range(r0, min(r0 + KC, h * w))), (axis, r0, sorted(changed))
+
+
 ALL_PINS = [
     pin_golden_worked_example,
     pin_geometric_series,
@@ -613,4 +708,8 @@ ALL_PINS = [
     pin_layernorm_library,
     pin_bwd_finite_differences,
     pin_bwd_masked_equals_zero_filled,
+    pin_conv_library,
+    pin_conv_closed_forms,
+    pin_conv_transpose,
+    pin_conv_causal,
 ]

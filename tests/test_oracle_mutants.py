@@ -32,8 +32,8 @@ MUTANTS = [
      "H[n] = a * H[n] + d * vt[R + N + n] * ut;\n                    acc += vt[R + n] * H[n];", 1),
     ("delta not in the decay", "? 0.0 : exp(d * A)", "? 0.0 : exp(A)", 1),
     ("backward scan not reversed", "reverse ? T - 1 - step : step", "step", 1),
-    ("dense pool not normalised", "        for (int64_t k = 0; k < T * E; ++k) ub[k] /= (double)P;\n    }\n    return 0;\n}\n\n/*\n * Masked rows.",
-     "    }\n    return 0;\n}\n\n/*\n * Masked rows.", 1),
+    ("dense pool not normalised", "        for (int64_t k = 0; k < T * E; ++k) ub[k] /= (double)P;\n    }\n}\n\n/*\n * Producer side",
+     "    }\n}\n\n/*\n * Producer side", 1),
     ("masked pool normalised by E", "            for (int64_t e = 0; e < E; ++e) ub[t * E + e] += (double)xv[e];\n        }\n        for (int64_t k = 0; k < T * E; ++k) ub[k] /= (double)P;",
      "            for (int64_t e = 0; e < E; ++e) ub[t * E + e] += (double)xv[e];\n        }\n        for (int64_t k = 0; k < T * E; ++k) ub[k] /= (double)K;", 1),
     ("only the forward D in the skip", "((double)pf->D[e] + (double)pb->D[e])", "((double)pf->D[e])", 1),
@@ -56,6 +56,16 @@ MUTANTS = [
     ("LayerNorm scale and shift swapped", "* (double)ln_w[e] + (double)ln_b[e]", "* (double)ln_b[e] + (double)ln_w[e]", 1),
     ("reset ignored", "(reset && reset[t]) ? 0.0 : exp(d * A)", "exp(d * A)", 1),
     ("duplicate mask index accepted", "if (q < 0 || q >= h * w || seen[q])", "if (q < 0 || q >= h * w)", 1),
+    # producer Conv1D
+    ("conv taps reversed", "acc += (double)conv_w[e * KC + k] *", "acc += (double)conv_w[e * KC + (KC - 1 - k)] *", 1),
+    ("conv centred instead of causal", "const int64_t rr = r - KC + 1 + k;\n                    if (rr < 0) continue;",
+     "const int64_t rr = r - KC / 2 + k;\n                    if (rr < 0 || rr >= n) continue;", 1),
+    ("conv without its bias", "double acc = (double)conv_b[e];", "double acc = 0.0;", 1),
+    ("conv without SiLU", "xc[(b * n + cell) * E + e] = acc / (1.0 + exp(-acc));", "xc[(b * n + cell) * E + e] = acc;", 1),
+    ("conv row-major on the transposed grid", "const int colmajor = axis == FVO_ROWS || axis == FVO_NONE_COLMAJOR;",
+     "const int colmajor = axis == FVO_NONE_COLMAJOR;", 1),
+    ("skip reads the conv's input", "(xd ? xd[e] : (double)x[e])", "((double)x[e])", 1),
+    ("pool reads the conv's input", "xd ? xd[c + e] : (double)x[c + e]", "(double)x[c + e]", 1),
     # backward pass
     ("adjoint carried without the decay", "carry[n] = a * lam[n];", "carry[n] = lam[n];", 1),
     ("adjoint decay term with the wrong sign", "dd += lam[n] * (A * a * prev + Bn * ut);",
