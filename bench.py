@@ -278,6 +278,21 @@ def main():
         extras["post_norm_2048"] = {"layer_ms": ln_ms, "epilogue_ms": ln_epi, "path": "stage kernels",
                                     "epilogue_GBps": alg_bytes / (ln_epi * 1e-3) / 1e9}
         del ncall
+        # the producer Conv1D + SiLU fused into the layer (x is the conv's input; stage kernels)
+        conv = {"weight": 0.5 * torch.randn(cfg.E, P.CONV_TAPS, device=dev, generator=g_ln),
+                "bias": 0.1 * torch.randn(cfg.E, device=dev, generator=g_ln)}
+        ccall = P.SSMCall(x, z, prm, P.POOL_COLS, workspace=call.workspace, out=call.out, conv=conv)
+        ccall.run(stream)
+        cv_ms, _ = time_steps(lambda: ccall.run(stream), n, stream)
+        cv_pool, _ = time_steps(lambda: ccall.stage(P.STAGE_POOL, stream), n, stream)
+        cv_epi, _ = time_steps(lambda: ccall.stage(P.STAGE_EPILOGUE, stream), n, stream)
+        extras["conv_producer_2048"] = {"layer_ms": cv_ms, "pool_ms": cv_pool, "epilogue_ms": cv_epi,
+                                        "path": "stage kernels, x_conv computed on load",
+                                        "layer_GBps": alg_bytes / (cv_ms * 1e-3) / 1e9,
+                                        "pool_GBps": 4 * elems / (cv_pool * 1e-3) / 1e9,
+                                        "epilogue_GBps": alg_bytes / (cv_epi * 1e-3) / 1e9}
+        del ccall
+        log("conv-fused layer %.3f ms" % cv_ms)
         # the backward pass (gradients of sum(dout * out)) on the same inputs
         g_b = torch.Generator(device="cuda").manual_seed(2)
         dout = torch.randn(x.shape, device=dev, generator=g_b)

@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define FASTVIM_ABI_VERSION 4
+#define FASTVIM_ABI_VERSION 5
 
 typedef enum fastvim_status {
     FASTVIM_OK = 0,
@@ -121,6 +121,11 @@ typedef struct fastvim_params {
     const float *ln_bias;
     float ln_eps;
     uint32_t reserved2;
+    /* Producer Conv1D, used with FASTVIM_FLAG_CONV only: depthwise taps
+     * (E, FASTVIM_CONV_TAPS) fp32, oldest tap first, 16-byte aligned, and bias
+     * (E) fp32. */
+    const float *conv_w;
+    const float *conv_b;
 } fastvim_params;
 
 /* params.flags bits.  By default a dense pooled layer (COLS or ROWS, no mask)
@@ -149,6 +154,22 @@ typedef struct fastvim_params {
  * Errors: FASTVIM_ERR_NULL (ln_weight or ln_bias NULL), FASTVIM_ERR_ALIGN (not
  * 16-byte aligned), FASTVIM_ERR_ARG (ln_eps not > 0 or not finite). */
 #define FASTVIM_FLAG_POST_NORM 4u
+
+/* FASTVIM_FLAG_CONV fuses the producer side into the layer: x is the input of
+ * the depthwise causal Conv1D + SiLU that makes the layer's x (FastVim summary
+ * page, section 方法详解, bullets 1-2: the grid is pooled after the Conv1D;
+ * Vim article, section 2.1: conv1d, then the SSM).  Along the oriented grid's
+ * sequence r -- row-major r = i*w + j for COLS, column-major r = j*h + i for
+ * ROWS (the transposed grid) -- with zeros before its start,
+ *   x_conv[r, e] = silu(conv_b[e] + sum_{k<4} conv_w[e, k] * x[r - 3 + k, e])
+ * and the layer runs on x_conv: the pool and the skip term compute it where
+ * they read x, so it is never written.  Dense pooled layers only, as stage
+ * kernels (FASTVIM_FLAG_FUSED is ignored); FASTVIM_ERR_UNSUPPORTED for masked
+ * or unpooled layers and with FASTVIM_FLAG_POST_NORM.  Errors:
+ * FASTVIM_ERR_NULL (conv_w or conv_b NULL), FASTVIM_ERR_ALIGN (conv_w not
+ * 16-byte aligned, conv_b not 4-byte aligned). */
+#define FASTVIM_FLAG_CONV 8u
+#define FASTVIM_CONV_TAPS 4
 
 /* Bytes of workspace a call with these sizes needs (0 if the sizes are
  * invalid).  Dense pooled layers need 4 * B * T * (3E + 2(R + 2N)) bytes plus
@@ -231,8 +252,9 @@ size_t fastvim_ssm_export_bytes(const fastvim_dims *dims, int pool_axis, int wha
  *
  * Supported: pooled layers (COLS or ROWS, dense or masked) with T <= 128 scan
  * steps and the limits of the forward call; FASTVIM_ERR_UNSUPPORTED for
- * unpooled layers, longer scans, and the flags FASTVIM_FLAG_FUSED and
- * FASTVIM_FLAG_POST_NORM (0 and FASTVIM_FLAG_STAGED run the same kernels). */
+ * unpooled layers, longer scans, and the flags FASTVIM_FLAG_FUSED,
+ * FASTVIM_FLAG_POST_NORM and FASTVIM_FLAG_CONV (0 and FASTVIM_FLAG_STAGED run
+ * the same kernels). */
 
 /* Gradients of one direction's parameters: fp32 device buffers shaped like
  * the parameters, 4-byte aligned, overwritten by the call. */

@@ -30,6 +30,8 @@ EXPORT_U, EXPORT_XDBL, EXPORT_S_FWD, EXPORT_S_BWD, EXPORT_ROWS, EXPORT_BAD_TOKEN
 FLAG_STAGED, FLAG_FUSED = 1, 2
 # FLAG_POST_NORM: post-SSM LayerNorm between the skip and the gate
 FLAG_POST_NORM = 4
+FLAG_CONV = 8
+CONV_TAPS = 4
 
 STATUS = {
     0: "FASTVIM_OK", -1: "FASTVIM_ERR_NULL", -2: "FASTVIM_ERR_DIMS", -3: "FASTVIM_ERR_UNSUPPORTED",
@@ -61,7 +63,7 @@ class Params(ctypes.Structure):
     _fields_ = [("fwd", DirParams), ("bwd", DirParams), ("workspace", ctypes.c_void_p),
                 ("workspace_bytes", ctypes.c_size_t), ("flags", ctypes.c_uint32), ("reserved", ctypes.c_uint32),
                 ("ln_weight", ctypes.c_void_p), ("ln_bias", ctypes.c_void_p), ("ln_eps", ctypes.c_float),
-                ("reserved2", ctypes.c_uint32)]
+                ("reserved2", ctypes.c_uint32), ("conv_w", ctypes.c_void_p), ("conv_b", ctypes.c_void_p)]
 
 
 class DirGrads(ctypes.Structure):
@@ -192,12 +194,15 @@ class SSMCall:
     and hw = (h, w).  params = {"fwd": {...}, "bwd": {...}} holding fp32
     device tensors x_proj_w (R+2N, E), dt_proj_w (E, R), dt_proj_b (E),
     A_log (E, N), D (E).  ln = {"weight": (E,), "bias": (E,), "eps": float}
-    (fp32 device tensors) adds the post-SSM LayerNorm before the gate."""
+    (fp32 device tensors) adds the post-SSM LayerNorm before the gate.
+    conv = {"weight": (E, 4), "bias": (E,)} (fp32 device tensors) makes x the
+    input of the producer Conv1D + SiLU, computed inside the layer."""
 
     def __init__(self, x: torch.Tensor, z: torch.Tensor, params: Dict[str, Dict[str, torch.Tensor]],
                  pool_axis: int, mask_idx: Optional[torch.Tensor] = None, hw: Optional[Tuple[int, int]] = None,
                  out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-                 flags: int = 0, ln: Optional[Dict[str, object]] = None):
+                 flags: int = 0, ln: Optional[Dict[str, object]] = None,
+                 conv: Optional[Dict[str, torch.Tensor]] = None):
         self.dims = _layer_dims(x, z, params, mask_idx, hw)
         self.pool_axis = pool_axis
         self.x, self.z, self.mask_idx = x, z, mask_idx
@@ -217,8 +222,16 @@ class SSMCall:
                     raise ValueError("LayerNorm weight and bias must be contiguous float32")
             self._keep.extend([ln_w, ln_b])
             flags |= FLAG_POST_NORM
+        conv_w = conv_b = None
+        if conv is not None:
+            conv_w, conv_b = conv["weight"], conv["bias"]
+            for t in (conv_w, conv_b):
+                if t.dtype != torch.float32 or not t.is_contiguous():
+                    raise ValueError("Conv1D weight and bias must be contiguous float32")
+            self._keep.extend([conv_w, conv_b])
+            flags |= FLAG_CONV
         self.params = Params(dirs[0], dirs[1], workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-                             flags, 0, _ptr(ln_w), _ptr(ln_b), ln_eps, 0)
+                             flags, 0, _ptr(ln_w), _ptr(ln_b), ln_eps, 0, _ptr(conv_w), _ptr(conv_b))
 
     def _args(self):
         return (_ptr(self.x), _ptr(self.z), ctypes.byref(self.params), ctypes.byref(self.dims), self.pool_axis,
@@ -254,10 +267,10 @@ class SSMCall:
 
 
 def ssm_fwd(x, z, params, pool_axis=POOL_COLS, mask_idx=None, hw=None, out=None, workspace=None, stream=None,
-            flags=0, ln=None):
+            flags=0, ln=None, conv=None):
     """The pooled bidirectional selective-scan layer; returns out."""
     return SSMCall(x, z, params, pool_axis, mask_idx=mask_idx, hw=hw, out=out, workspace=workspace,
-                   flags=flags, ln=ln).run(stream)
+                   flags=flags, ln=ln, conv=conv).run(stream)
 
 
 class BwdCall:

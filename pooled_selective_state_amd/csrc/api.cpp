@@ -75,9 +75,13 @@ int validate(const void* x, const void* z, const fastvim_params* prm, const fast
              const int32_t* idx, const void* out, Geom* g, Workspace* ws, bool* empty) {
     if (!prm) return FASTVIM_ERR_NULL;
     const uint32_t paths = FASTVIM_FLAG_STAGED | FASTVIM_FLAG_FUSED;
-    if ((prm->flags & ~(paths | FASTVIM_FLAG_POST_NORM)) || (prm->flags & paths) == paths) return FASTVIM_ERR_ARG;
+    if ((prm->flags & ~(paths | FASTVIM_FLAG_POST_NORM | FASTVIM_FLAG_CONV)) || (prm->flags & paths) == paths)
+        return FASTVIM_ERR_ARG;
     int st = resolve_geom(d, axis, g);
     if (st) return st;
+    if ((prm->flags & FASTVIM_FLAG_CONV) &&
+        (!g->pooled || g->masked || (prm->flags & FASTVIM_FLAG_POST_NORM)))
+        return FASTVIM_ERR_UNSUPPORTED;
     if (!g->masked && idx) return FASTVIM_ERR_ARG;
     *empty = g->B == 0;
     if (*empty) return FASTVIM_OK;
@@ -87,6 +91,10 @@ int validate(const void* x, const void* z, const fastvim_params* prm, const fast
         if (!prm->ln_weight || !prm->ln_bias) return FASTVIM_ERR_NULL;
         if (!aligned(prm->ln_weight, 16) || !aligned(prm->ln_bias, 16)) return FASTVIM_ERR_ALIGN;
         if (!(prm->ln_eps > 0.f) || !(prm->ln_eps < 3.4e38f)) return FASTVIM_ERR_ARG;
+    }
+    if (prm->flags & FASTVIM_FLAG_CONV) {
+        if (!prm->conv_w || !prm->conv_b) return FASTVIM_ERR_NULL;
+        if (!aligned(prm->conv_w, 16) || !aligned(prm->conv_b, 4)) return FASTVIM_ERR_ALIGN;
     }
     if (!prm->workspace) return FASTVIM_ERR_WORKSPACE;
     if (!aligned(x, 16) || !aligned(z, 16) || !aligned(out, 16) || !aligned(prm->workspace, 256) ||
@@ -112,13 +120,15 @@ int run_stage(int stage, const Geom& g, const void* x, const void* z, const fast
             if (g.masked) e = launch_mask_rows(g, idx, ws, st);
             break;
         case FASTVIM_STAGE_POOL:
-            if (g.pooled) e = launch_pool(g, x, ws, st);
+            if (g.pooled)
+                e = (p.flags & FASTVIM_FLAG_CONV) ? launch_conv_pool(g, x, p, ws, st) : launch_pool(g, x, ws, st);
             break;
         case FASTVIM_STAGE_PROJ: e = launch_proj(g, x, p, ws, st); break;
         case FASTVIM_STAGE_SCAN: e = launch_scan(g, x, p, ws, st); break;
         case FASTVIM_STAGE_EPILOGUE:
             e = (p.flags & FASTVIM_FLAG_POST_NORM) ? launch_epilogue_norm(g, x, z, p, ws, out, st)
-                                                  : launch_epilogue(g, x, z, p, ws, out, st);
+                : (p.flags & FASTVIM_FLAG_CONV)    ? launch_conv_epilogue(g, x, z, p, ws, out, st)
+                                                   : launch_epilogue(g, x, z, p, ws, out, st);
             break;
         default: return FASTVIM_ERR_ARG;
     }
@@ -152,9 +162,10 @@ int validate_bwd(const void* x, const void* z, const void* dout, const fastvim_p
                  int axis, const int32_t* idx, const void* dx, const void* dz, const fastvim_grads* gr, Geom* g,
                  BwdWorkspace* ws, bool* empty) {
     if (!prm) return FASTVIM_ERR_NULL;
-    const uint32_t known = FASTVIM_FLAG_STAGED | FASTVIM_FLAG_FUSED | FASTVIM_FLAG_POST_NORM;
+    const uint32_t known = FASTVIM_FLAG_STAGED | FASTVIM_FLAG_FUSED | FASTVIM_FLAG_POST_NORM | FASTVIM_FLAG_CONV;
     if (prm->flags & ~known) return FASTVIM_ERR_ARG;
-    if (prm->flags & (FASTVIM_FLAG_FUSED | FASTVIM_FLAG_POST_NORM)) return FASTVIM_ERR_UNSUPPORTED;
+    if (prm->flags & (FASTVIM_FLAG_FUSED | FASTVIM_FLAG_POST_NORM | FASTVIM_FLAG_CONV))
+        return FASTVIM_ERR_UNSUPPORTED;
     int st = resolve_geom(d, axis, g);
     if (st) return st;
     if (!bwd_supported(*g)) return FASTVIM_ERR_UNSUPPORTED;
@@ -346,7 +357,7 @@ int fastvim_ssm_fwd(const void* x, const void* z, const fastvim_params* params, 
     if (st || empty) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (launch_zero_sync(ws, sync_words(g), s) != hipSuccess) return FASTVIM_ERR_HIP;
-    const bool single = !(params->flags & FASTVIM_FLAG_POST_NORM) &&
+    const bool single = !(params->flags & (FASTVIM_FLAG_POST_NORM | FASTVIM_FLAG_CONV)) &&
                         ((params->flags & FASTVIM_FLAG_FUSED) ? fused_supported(g)
                                                               : !(params->flags & FASTVIM_FLAG_STAGED) && fused_preferred(g));
     if (single)

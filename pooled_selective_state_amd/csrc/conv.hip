@@ -1,0 +1,302 @@
+// Producer side fused into the layer: the depthwise causal Conv1D + SiLU that
+// makes the layer's x is computed where x is read -- in the pool and again in
+// the epilogue's skip term -- so x_conv never goes to memory.
+//
+// FastVim summary page (gptget.net, arXiv 2502.00594), section 方法详解,
+// bullets 1-2: the token grid is pooled after the Conv1D; Vim article
+// (ijyty.com) 2.1: conv1d, then the SSM.  With x the conv's input (B, h, w, E)
+// and the oriented grid's sequence r (row-major r = i*w + j for COLS,
+// column-major r = j*h + i for ROWS, the transposed grid),
+//   x_conv[r, e] = silu(conv_b[e] + sum_{k<4} conv_w[e, k] x[r - 3 + k, e])
+// with zeros before the start of the sequence (oldest tap first).
+//
+// Each token's value needs its three predecessors in the sequence: for COLS
+// they are the three previous tokens in memory (crossing into the previous
+// grid row at its start); for ROWS the same column of the three previous grid
+// rows (crossing into earlier columns at the top).  Lanes walk runs of cells
+// that follow one another in the sequence and slide a window of three raw
+// vectors, so each cell is loaded once plus a halo of three per run; the halo
+// is the neighbouring lane's cells, loaded at about the same time, and comes
+// from the caches.  The kernels follow the pool and epilogue kernels
+// (pool.hip, epilogue.hip) otherwise.
+#include "fastvim_internal.h"
+
+namespace fastvim {
+namespace {
+
+constexpr int kTaps = FASTVIM_CONV_TAPS;
+
+__device__ __forceinline__ float silu(float q) { return q * __builtin_amdgcn_rcpf(1.f + __expf(-q)); }
+
+// Token index within the image of the k-th predecessor (k >= 1) of grid cell
+// (i, j) in the oriented sequence, or -1 before the start of the sequence.
+template <bool COLS>
+__device__ __forceinline__ int pred_token(int i, int j, int k, int h, int w) {
+    if (COLS) {
+        const int r = i * w + j - k;
+        return r;  // row-major: memory order; negative before the start
+    }
+    if (i >= k) return (i - k) * w + j;
+    const int r = j * h + i - k;  // column-major position; may lie several columns back when h < k
+    return r < 0 ? -1 : (r % h) * w + r / h;
+}
+
+// Channel weights of the lane's V channels: taps (oldest first) and bias.
+template <int V>
+struct ConvW {
+    float w[V][kTaps], b[V];
+};
+template <int V>
+__device__ __forceinline__ void load_conv_w(const float* cw, const float* cb, int64_t col, ConvW<V>& W) {
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+        const f32x4 t = *reinterpret_cast<const f32x4*>(cw + (col + v) * kTaps);
+        W.w[v][0] = t.x;
+        W.w[v][1] = t.y;
+        W.w[v][2] = t.z;
+        W.w[v][3] = t.w;
+        W.b[v] = cb[col + v];
+    }
+}
+
+// x_conv for the lane's V channels from a window of raw vectors: the cell
+// (cur) and its three predecessors (p1 the newest); a predecessor before the
+// start of the sequence is a zero vector.
+template <class IO>
+__device__ __forceinline__ void conv_window(const typename IO::raw& p3, const typename IO::raw& p2,
+                                            const typename IO::raw& p1, const typename IO::raw& cur,
+                                            const ConvW<IO::V>& W, float (&xc)[IO::V]) {
+    static_assert(kTaps == 4, "window of three predecessors");
+#pragma unroll
+    for (int v = 0; v < IO::V; ++v) {
+        float a = fmaf(W.w[v][3], raw_at(cur, v), W.b[v]);
+        a = fmaf(W.w[v][2], raw_at(p1, v), a);
+        a = fmaf(W.w[v][1], raw_at(p2, v), a);
+        a = fmaf(W.w[v][0], raw_at(p3, v), a);
+        xc[v] = silu(a);
+    }
+}
+
+// The three predecessors of cell (i, j) (p1 the newest), zero before the start.
+template <class IO, bool COLS>
+__device__ __forceinline__ void load_halo(const typename IO::elem* xb, int coff, int E, int i, int j, int h, int w,
+                                          typename IO::raw& p3, typename IO::raw& p2, typename IO::raw& p1) {
+    typename IO::raw r[3];
+#pragma unroll
+    for (int k = 1; k <= 3; ++k) {
+        const int tok = pred_token<COLS>(i, j, k, h, w);
+        r[k - 1] = typename IO::raw{};
+        if (tok >= 0) r[k - 1] = load_raw<false>(xb + (coff + tok * E));
+    }
+    p1 = r[0];
+    p2 = r[1];
+    p3 = r[2];
+}
+
+// ------------------------------------------------------------------ pool
+// One workgroup per pooled token (b, t), G groups of VE vector lanes.  Group g
+// takes a run of consecutive pooled positions [g L, g L + L): along the pooled
+// axis each cell's predecessor in the sequence is the previous cell of the
+// run (COLS: (t, j - 1); ROWS: (i - 1, t)), so a lane slides a window of
+// three raw vectors and loads the run's cells once, plus a halo of three at
+// its start.  Fixed-order LDS reduction of the G partial sums.
+constexpr int kPU = 4;  // cells loaded at once per lane
+template <class IO, bool COLS>
+__global__ void __launch_bounds__(1024)
+conv_pool_kernel(const typename IO::elem* __restrict__ x, const float* __restrict__ cw, const float* __restrict__ cb,
+                 float* __restrict__ u, int T, int P, int h, int w, int VE, int G, int E, float inv_p) {
+    constexpr int V = IO::V;
+    using raw = typename IO::raw;
+    extern __shared__ float red[];  // [G][VE * V]
+    const int64_t bt = blockIdx.x;
+    const int64_t b = bt / T;
+    const int t = (int)(bt - b * T);
+    const int tid = threadIdx.x;
+    const int c = tid % VE, g = tid / VE;
+    const int coff = c * V;
+    if (g < G) {
+        ConvW<V> W;
+        load_conv_w<V>(cw, cb, coff, W);
+        const typename IO::elem* xb = x + b * (int64_t)h * w * E;
+        const int pstr = (COLS ? 1 : w) * E;  // tokens along the pooled axis
+        const int L = (P + G - 1) / G;
+        const int p0 = g * L, p1 = p0 + L < P ? p0 + L : P;
+        float acc[V];
+#pragma unroll
+        for (int v = 0; v < V; ++v) acc[v] = 0.f;
+        if (p0 < p1) {
+            const int i0 = COLS ? t : p0, j0 = COLS ? p0 : t;
+            raw w3, w2, w1;
+            load_halo<IO, COLS>(xb, coff, E, i0, j0, h, w, w3, w2, w1);
+            const typename IO::elem* cell = xb + (coff + (i0 * w + j0) * E);
+            for (int p = p0; p < p1; p += kPU) {
+                raw cur[kPU];
+#pragma unroll
+                for (int q = 0; q < kPU; ++q)
+                    if (p + q < p1) cur[q] = load_raw<false>(cell + (p - p0 + q) * pstr);
+#pragma unroll
+                for (int q = 0; q < kPU; ++q) {
+                    if (p + q < p1) {
+                        float xc[V];
+                        conv_window<IO>(w3, w2, w1, cur[q], W, xc);
+#pragma unroll
+                        for (int v = 0; v < V; ++v) acc[v] += xc[v];
+                        w3 = w2;
+                        w2 = w1;
+                        w1 = cur[q];
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int v = 0; v < V; ++v) red[(g * VE + c) * V + v] = acc[v];
+    }
+    __syncthreads();
+    const int width = VE * V;
+    for (int q = tid; q < width; q += blockDim.x) {
+        float s = red[q];
+        for (int gg = 1; gg < G; ++gg) s += red[gg * width + q];
+        u[bt * E + q] = s * inv_p;
+    }
+}
+
+// -------------------------------------------------------------- epilogue
+// out = (s_fwd + s_bwd + (D_fwd + D_bwd) x_conv) silu(z), each output written
+// once.  Lane (c, g) takes kU cells that follow one another in the sequence
+// and slides the conv window over them, with a halo of three at their start:
+//   COLS: a workgroup covers G * kU consecutive cells of grid row i, lane
+//         group g the cells j0 + g kU + m (the scan row i is shared);
+//   ROWS: a workgroup covers kU grid rows x G columns, lane group g walks
+//         column j0 + g down the rows i0 + m (its scan row j is fixed).
+// All x and z loads of a lane are issued before its arithmetic.
+constexpr int kU = 4;
+
+template <class IO, bool COLS>
+__global__ void __launch_bounds__(1024)
+conv_epilogue_kernel(const typename IO::elem* __restrict__ x, const typename IO::elem* __restrict__ z,
+                     const float* __restrict__ cw, const float* __restrict__ cb, const float* __restrict__ sf,
+                     const float* __restrict__ sb, const float* __restrict__ Df, const float* __restrict__ Db,
+                     typename IO::elem* __restrict__ out, int T, int h, int w, int E, int VE, int G, int nbi,
+                     int nbj) {
+    constexpr int V = IO::V;
+    using raw = typename IO::raw;
+    const int tid = threadIdx.x, c = tid % VE, g = tid / VE;
+    if (g >= G) return;
+    // block (b, bi, bj): COLS bi = grid row, bj = run of G kU cells; ROWS bi =
+    // run of kU rows, bj = run of G columns
+    const int64_t blk = blockIdx.x;
+    const int64_t b = blk / ((int64_t)nbi * nbj);
+    const int rem = (int)(blk - b * nbi * nbj);
+    const int bi = rem / nbj, bj = rem - (rem / nbj) * nbj;
+    const int i0 = COLS ? bi : bi * kU;
+    const int j0 = COLS ? bj * G * kU + g * kU : bj * G + g;
+    const int n = COLS ? (w - j0 < kU ? w - j0 : kU) : (h - i0 < kU ? h - i0 : kU);  // cells of this lane
+    if (n <= 0 || j0 >= w) return;
+    const int coff = c * V;
+    const int cstr = (COLS ? 1 : w) * E;  // token stride between the lane's cells
+    const int64_t img = b * (int64_t)h * w * E;
+    const typename IO::elem* xb = x + img;
+    const int off0 = coff + (i0 * w + j0) * E;
+    raw xr[kU], zr[kU];
+#pragma unroll
+    for (int m = 0; m < kU; ++m) {
+        if (m < n) {
+            xr[m] = load_raw<false>(xb + (off0 + m * cstr));
+            zr[m] = load_raw<true>(z + img + (off0 + m * cstr));
+        }
+    }
+    raw w3, w2, w1;
+    load_halo<IO, COLS>(xb, coff, E, i0, j0, h, w, w3, w2, w1);
+    ConvW<V> W;
+    load_conv_w<V>(cw, cb, coff, W);
+    float dsum[V], sv[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) dsum[v] = Df[coff + v] + Db[coff + v];
+    const int64_t srow = (b * T + (COLS ? i0 : j0)) * E + coff;
+#pragma unroll
+    for (int v = 0; v < V; v += 4) {
+        const f32x4 q1 = load_raw<false>(sf + srow + v), q2 = load_raw<false>(sb + srow + v);
+        sv[v] = q1.x + q2.x;
+        sv[v + 1] = q1.y + q2.y;
+        sv[v + 2] = q1.z + q2.z;
+        sv[v + 3] = q1.w + q2.w;
+    }
+    typename IO::elem* ob = out + img;
+#pragma unroll
+    for (int m = 0; m < kU; ++m) {
+        if (m < n) {
+            float xc[V], o[V];
+            conv_window<IO>(w3, w2, w1, xr[m], W, xc);
+            w3 = w2;
+            w2 = w1;
+            w1 = xr[m];
+#pragma unroll
+            for (int v = 0; v < V; ++v) o[v] = (sv[v] + dsum[v] * xc[v]) * silu(raw_at(zr[m], v));
+            store_vec<true>(ob + (off0 + m * cstr), o);
+        }
+    }
+}
+
+template <class IO>
+hipError_t conv_pool_t(const Geom& g, const void* x, const fastvim_params& p, const Workspace& ws, hipStream_t st) {
+    const int64_t VE = g.E / IO::V;
+    int64_t G = 512 / VE;
+    if (G > g.P) G = g.P;
+    if (G < 1) G = 1;
+    const int threads = (int)((VE * G + 63) / 64 * 64);
+    const size_t lds = (size_t)G * VE * IO::V * sizeof(float);
+    const auto* xe = static_cast<const typename IO::elem*>(x);
+    if (g.axis == FASTVIM_POOL_COLS)
+        hipLaunchKernelGGL((conv_pool_kernel<IO, true>), dim3((unsigned)(g.B * g.T)), dim3(threads), lds, st, xe,
+                           p.conv_w, p.conv_b, ws.u, (int)g.T, (int)g.P, (int)g.h, (int)g.w, (int)VE, (int)G,
+                           (int)g.E, 1.0f / (float)g.P);
+    else
+        hipLaunchKernelGGL((conv_pool_kernel<IO, false>), dim3((unsigned)(g.B * g.T)), dim3(threads), lds, st, xe,
+                           p.conv_w, p.conv_b, ws.u, (int)g.T, (int)g.P, (int)g.h, (int)g.w, (int)VE, (int)G,
+                           (int)g.E, 1.0f / (float)g.P);
+    return hipGetLastError();
+}
+
+template <class IO>
+hipError_t conv_epi_t(const Geom& g, const void* x, const void* z, const fastvim_params& p, const Workspace& ws,
+                      void* out, hipStream_t st) {
+    using elem = typename IO::elem;
+    const int64_t VE = g.E / IO::V;
+    int64_t G = 512 / VE;
+    if (G < 1) G = 1;
+    const bool cols = g.axis == FASTVIM_POOL_COLS;
+    if (cols && G * kU > g.w) G = (g.w + kU - 1) / kU;
+    if (!cols && G > g.w) G = g.w;
+    if (G < 1) G = 1;
+    const int64_t nbi = cols ? g.h : (g.h + kU - 1) / kU;
+    const int64_t nbj = cols ? (g.w + G * kU - 1) / (G * kU) : (g.w + G - 1) / G;
+    const int threads = (int)((VE * G + 63) / 64 * 64);
+    const dim3 grid((unsigned)(g.B * nbi * nbj));
+    const auto* xe = static_cast<const elem*>(x);
+    const auto* ze = static_cast<const elem*>(z);
+    auto* oe = static_cast<elem*>(out);
+    if (cols)
+        hipLaunchKernelGGL((conv_epilogue_kernel<IO, true>), grid, dim3(threads), 0, st, xe, ze, p.conv_w, p.conv_b,
+                           ws.s_f, ws.s_b, p.fwd.D, p.bwd.D, oe, (int)g.T, (int)g.h, (int)g.w, (int)g.E, (int)VE,
+                           (int)G, (int)nbi, (int)nbj);
+    else
+        hipLaunchKernelGGL((conv_epilogue_kernel<IO, false>), grid, dim3(threads), 0, st, xe, ze, p.conv_w, p.conv_b,
+                           ws.s_f, ws.s_b, p.fwd.D, p.bwd.D, oe, (int)g.T, (int)g.h, (int)g.w, (int)g.E, (int)VE,
+                           (int)G, (int)nbi, (int)nbj);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_conv_pool(const Geom& g, const void* x, const fastvim_params& p, const Workspace& ws,
+                            hipStream_t st) {
+    return g.io == FASTVIM_BF16 ? conv_pool_t<IoBf16>(g, x, p, ws, st) : conv_pool_t<IoF32>(g, x, p, ws, st);
+}
+
+hipError_t launch_conv_epilogue(const Geom& g, const void* x, const void* z, const fastvim_params& p,
+                                const Workspace& ws, void* out, hipStream_t st) {
+    return g.io == FASTVIM_BF16 ? conv_epi_t<IoBf16>(g, x, z, p, ws, out, st)
+                                : conv_epi_t<IoF32>(g, x, z, p, ws, out, st);
+}
+
+}  // namespace fastvim

@@ -48,6 +48,10 @@ hipError_t launch_scan(const Geom& g, const void* x, const fastvim_params& p, co
                        hipStream_t st);
 hipError_t launch_epilogue(const Geom& g, const void* x, const void* z, const fastvim_params& p,
                            const Workspace& ws, void* out, hipStream_t st);
+hipError_t launch_conv_pool(const Geom& g, const void* x, const fastvim_params& p, const Workspace& ws,
+                            hipStream_t st);
+hipError_t launch_conv_epilogue(const Geom& g, const void* x, const void* z, const fastvim_params& p,
+                                const Workspace& ws, void* out, hipStream_t st);
 hipError_t launch_epilogue_norm(const Geom& g, const void* x, const void* z, const fastvim_params& p,
                                 const Workspace& ws, void* out, hipStream_t st);
 // Single-launch dense pooled layer (fused.hip).

@@ -32,7 +32,7 @@ def test_library_exports_every_declared_function():
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(Bd.EXPORTED_SYMBOLS)
-    assert lib.fastvim_abi_version() == 4
+    assert lib.fastvim_abi_version() == 5
 
 
 def test_status_strings():
@@ -46,7 +46,7 @@ def test_struct_layout_matches_header():
     # int64 x 7 + int32 x 2; five pointers; two dir structs + ptr + size_t + 2 x u32 + 2 ptrs + f32 + u32
     assert ctypes.sizeof(Bd.Dims) == 64
     assert ctypes.sizeof(Bd.DirParams) == 40
-    assert ctypes.sizeof(Bd.Params) == 2 * 40 + 8 + 8 + 8 + 8 + 8 + 4 + 4
+    assert ctypes.sizeof(Bd.Params) == 2 * 40 + 8 + 8 + 8 + 8 + 8 + 4 + 4 + 8 + 8
     assert ctypes.sizeof(Bd.DirGrads) == 40 and ctypes.sizeof(Bd.Grads) == 80
 
 
@@ -150,7 +150,7 @@ def test_bad_enums():
     c = FakeCall()
     assert lib.fastvim_ssm_stage(5, c.x, c.z, ctypes.byref(c.params), ctypes.byref(c.dims), 0, None, c.out,
                                  None) == EARG
-    for flags in (P.FLAG_STAGED | P.FLAG_FUSED, 8, 1 << 31):  # conflicting or unknown flags
+    for flags in (P.FLAG_STAGED | P.FLAG_FUSED, 16, 1 << 31):  # conflicting or unknown flags
         c = FakeCall()
         c.params.flags = flags
         expect(c, EARG)
@@ -321,7 +321,8 @@ def test_bwd_unsupported_and_bad_flags():
         assert FakeBwd(axis=axis).bwd() == EUNSUP
     assert FakeBwd(h=129).bwd() == EUNSUP
     assert FakeBwd(N=8).bwd() == EUNSUP
-    for flags, code in ((P.FLAG_FUSED, EUNSUP), (P.FLAG_POST_NORM, EUNSUP), (8, EARG), (P.FLAG_STAGED, OK)):
+    for flags, code in ((P.FLAG_FUSED, EUNSUP), (P.FLAG_POST_NORM, EUNSUP), (P.FLAG_CONV, EUNSUP), (16, EARG),
+                        (P.FLAG_STAGED, OK)):
         c = FakeBwd()
         c.params.flags = flags
         if code != OK:
@@ -373,3 +374,30 @@ def test_bwd_workspace_checks():
     c = FakeBwd()
     c.params.workspace = None
     assert c.bwd() == EWS
+
+
+def test_conv_validation():
+    """The producer Conv1D's arguments and scope are checked before any launch."""
+    base = 0x80000
+    for (cw, cb, code) in ((None, base, ENULL), (base, None, ENULL), (base + 4, base, EALIGN),
+                           (base, base + 2, EALIGN)):
+        c = FakeCall()
+        c.params.flags = P.FLAG_CONV
+        c.params.conv_w, c.params.conv_b = cw, cb
+        expect(c, code)
+    for kw, axis in ((dict(K=3), P.POOL_COLS), (dict(), P.POOL_NONE_ROWMAJOR), (dict(), P.POOL_NONE_COLMAJOR)):
+        c = FakeCall(axis=axis, **kw)
+        c.params.flags = P.FLAG_CONV
+        c.params.conv_w, c.params.conv_b = base, base
+        expect(c, EUNSUP)
+    c = FakeCall()
+    c.params.flags = P.FLAG_CONV | P.FLAG_POST_NORM
+    c.params.conv_w = c.params.conv_b = c.params.ln_weight = c.params.ln_bias = base
+    c.params.ln_eps = 1e-5
+    expect(c, EUNSUP)
+    c = FakeBwd()
+    c.params.flags = P.FLAG_CONV
+    assert c.bwd() == EUNSUP
+    c = FakeCall()
+    c.params.flags = 16
+    expect(c, EARG)
