@@ -94,7 +94,7 @@ class Oracle:
             vp, vp, ctypes.POINTER(_Dir), ctypes.POINTER(_Dir),
             i64, i64, i64, i64, i64, i64, i64, ci, vp,
             vp, vp, vp, ctypes.POINTER(_DirOut), ctypes.POINTER(_DirOut),
-            vp, vp, ctypes.c_double, vp, vp, i64,
+            vp, vp, ctypes.c_double, vp, vp, i64, i64,
         ]
         lib.fvo_layer.restype = ci
         lib.fvo_conv_silu.argtypes = [vp, i64, i64, i64, i64, ci, vp, vp, i64, vp]
@@ -191,13 +191,16 @@ class Oracle:
             raise ValueError("fvo_conv_silu failed: %d" % rc)
         return xc
 
-    def layer(self, x, z, fwd, bwd, axis, idx=None, hw=None, stages=False, ln=None, conv=None):
+    def layer(self, x, z, fwd, bwd, axis, idx=None, hw=None, stages=False, ln=None, conv=None, local_window=0):
         """Full layer.  Dense: x, z (B,h,w,E).  Masked: x, z (B,K,E), idx (B,K),
         hw=(h, w).  fwd / bwd: dicts with x_proj_w, dt_proj_w, dt_proj_b, A_log, D.
         ln: None, or {"weight": (E,), "bias": (E,), "eps": float} for the
         post-SSM LayerNorm before the gate.  conv: None, or {"weight": (E, KC),
         "bias": (E,)}: x is then the Conv1D's input and the layer runs on
-        conv_silu(x) (dense layers only).
+        conv_silu(x) (dense layers only).  local_window = L > 0: LBMamba's
+        local backward scan (forward parameters, state reset at the top of
+        every window of L steps) replaces the global backward scan; of bwd only
+        D is used.
         Returns out (fp64), or with stages=True a dict of out, u, rows and the
         per-direction v, delta, s."""
         x, z = _f32(x), _f32(z)
@@ -246,7 +249,7 @@ class Oracle:
             _ptr(out), _ptr(u), _ptr(rows),
             ctypes.byref(fo) if fo is not None else None,
             ctypes.byref(bo) if bo is not None else None,
-            _ptr(ln_w), _ptr(ln_b), ln_eps, _ptr(conv_w), _ptr(conv_b), conv_k,
+            _ptr(ln_w), _ptr(ln_b), ln_eps, _ptr(conv_w), _ptr(conv_b), conv_k, int(local_window),
         )
         if rc:
             raise ValueError("fvo_layer failed: %d" % rc)
@@ -352,8 +355,9 @@ def scan(u, dlt, v, A_log, R, reverse=False, reset=None):
     return get().scan(u, dlt, v, A_log, R, reverse=reverse, reset=reset)
 
 
-def layer(x, z, fwd, bwd, axis, idx=None, hw=None, stages=False, ln=None, conv=None):
-    return get().layer(x, z, fwd, bwd, axis, idx=idx, hw=hw, stages=stages, ln=ln, conv=conv)
+def layer(x, z, fwd, bwd, axis, idx=None, hw=None, stages=False, ln=None, conv=None, local_window=0):
+    return get().layer(x, z, fwd, bwd, axis, idx=idx, hw=hw, stages=stages, ln=ln, conv=conv,
+                       local_window=local_window)
 
 
 def conv_silu(x, axis, conv):

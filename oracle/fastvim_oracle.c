@@ -308,7 +308,7 @@ typedef struct {
 } fvo_dir_out;
 
 static int run_direction(const double *u, int64_t B, int64_t T, int64_t E, int64_t N, int64_t R,
-                         const fvo_dir *p, int reverse, fvo_dir_out *o, double *s_out)
+                         const fvo_dir *p, int reverse, const unsigned char *reset, fvo_dir_out *o, double *s_out)
 {
     const int64_t NX = R + 2 * N, M = B * T;
     double *v = o && o->v ? o->v : (double *)malloc((size_t)(M * NX) * sizeof(double));
@@ -316,7 +316,7 @@ static int run_direction(const double *u, int64_t B, int64_t T, int64_t E, int64
     if (!v || !dl) return -9;
     fvo_xproj(u, M, E, p->x_proj_w, NX, v);
     fvo_delta(v, M, NX, R, p->dt_proj_w, p->dt_proj_b, E, dl);
-    fvo_scan(u, dl, v, B, T, E, N, R, NX, p->A_log, reverse, NULL, s_out);
+    fvo_scan(u, dl, v, B, T, E, N, R, NX, p->A_log, reverse, reset, s_out);
     if (!(o && o->v)) free(v);
     if (!(o && o->delta)) free(dl);
     return 0;
@@ -372,12 +372,21 @@ static void output_token(const double *sf, const double *sb, const float *x, con
 
 /* ln_w == NULL: no post-SSM LayerNorm.  conv_w == NULL: x is the layer's
  * input itself; else x is the Conv1D's input and the layer runs on
- * fvo_conv_silu(x) (dense layers only). */
+ * fvo_conv_silu(x) (dense layers only).
+ *
+ * local_window = L > 0: the local backward scan of LBMamba [LBMamba article,
+ * 论文创新点 1-2: a light backward scan inside the forward selective scan, run
+ * within subsequences, in place of the global backward scan].  The backward
+ * output s_bwd is then the scan over t descending with the forward
+ * direction's projection, step size and decay (the same inputs the forward
+ * scan holds), whose state starts from zero at the top of every window of L
+ * steps, windows aligned at t = 0: a reset at every t with t mod L = L - 1.
+ * Of the backward parameters only D is used, in the skip. */
 int fvo_layer(const float *x, const float *z, const fvo_dir *pf, const fvo_dir *pb, int64_t B, int64_t h,
               int64_t w, int64_t E, int64_t N, int64_t R, int64_t K, int axis, const int32_t *idx,
               double *out, double *u_out, int32_t *rows_out, fvo_dir_out *fwd, fvo_dir_out *bwd,
               const float *ln_w, const float *ln_b, double ln_eps, const float *conv_w, const float *conv_b,
-              int64_t conv_k)
+              int64_t conv_k, int64_t local_window)
 {
     int64_t T, P;
     const int masked = idx != NULL;
@@ -389,6 +398,7 @@ int fvo_layer(const float *x, const float *z, const fvo_dir *pf, const fvo_dir *
     double *sf = fwd && fwd->s ? fwd->s : (double *)malloc((size_t)(M * E) * sizeof(double));
     double *sb = bwd && bwd->s ? bwd->s : (double *)malloc((size_t)(M * E) * sizeof(double));
     double *xc = conv_w ? (double *)malloc((size_t)(B * h * w * E) * sizeof(double)) : NULL;
+    unsigned char *reset = NULL;
     int32_t *rows = NULL;
     int rc = 0;
     if (!u || !sf || !sb || (conv_w && !xc)) { rc = -9; goto done; }
@@ -404,9 +414,17 @@ int fvo_layer(const float *x, const float *z, const fvo_dir *pf, const fvo_dir *
         pool_dense_any(x, xc, B, h, w, E, axis, u);
     }
 
-    rc = run_direction(u, B, T, E, N, R, pf, 0, fwd, sf);
+    rc = run_direction(u, B, T, E, N, R, pf, 0, NULL, fwd, sf);
     if (rc) goto done;
-    rc = run_direction(u, B, T, E, N, R, pb, 1, bwd, sb);
+    if (local_window > 0) {
+        const fvo_dir pl = {pf->x_proj_w, pf->dt_proj_w, pf->dt_proj_b, pf->A_log, pb->D};
+        reset = (unsigned char *)malloc((size_t)T);
+        if (!reset) { rc = -9; goto done; }
+        for (int64_t t = 0; t < T; ++t) reset[t] = (unsigned char)(t % local_window == local_window - 1);
+        rc = run_direction(u, B, T, E, N, R, &pl, 1, reset, bwd, sb);
+    } else {
+        rc = run_direction(u, B, T, E, N, R, pb, 1, NULL, bwd, sb);
+    }
     if (rc) goto done;
 
     if (masked) {
@@ -436,6 +454,7 @@ int fvo_layer(const float *x, const float *z, const fvo_dir *pf, const fvo_dir *
 
 done:
     free(xc);
+    free(reset);
     if (!u_out) free(u);
     if (!(fwd && fwd->s)) free(sf);
     if (!(bwd && bwd->s)) free(sb);

@@ -687,6 +687,55 @@ def pin_conv_causal(O):
             assert changed == set(range(r0, min(r0 + KC, h * w))), (axis, r0, sorted(changed))
 
 
+# ---------------------------------------------------------------- LBMamba local backward scan
+def _local_case(rng, B_=2, h=10, w=3, E=5, N=4, R=3):
+    pf, pb = rand_dir(rng, E, N, R), rand_dir(rng, E, N, R)
+    x = rng.standard_normal((B_, h, w, E)).astype(np.float32)
+    z = rng.standard_normal((B_, h, w, E)).astype(np.float32)
+    return pf, pb, x, z
+
+
+def pin_local_window_covers_sequence(O):
+    """A window as long as the sequence is the global backward scan run with
+    the forward direction's projection, step size and decay."""
+    rng = np.random.default_rng(60)
+    pf, pb, x, z = _local_case(rng)
+    shared = dict(pf, D=pb["D"])
+    for axis, L in ((COLS, 10), (COLS, 64), (ROWS, 3), (NONE_ROWMAJOR, 30)):
+        _close(O.layer(x, z, pf, pb, axis, local_window=L), O.layer(x, z, pf, shared, axis),
+               what="local window %d axis %d" % (L, axis))
+
+
+def pin_local_window_one(O):
+    """Windows of one step: s_bwd[t] = sum_n C_t[n] Delta_t B_t[n] u_t."""
+    rng = np.random.default_rng(61)
+    pf, pb, x, z = _local_case(rng)
+    N = pf["A_log"].shape[1]
+    R = pf["x_proj_w"].shape[0] - 2 * N
+    st = O.layer(x, z, pf, pb, COLS, stages=True, local_window=1)
+    v, dl, u = st["fwd"]["v"], st["fwd"]["delta"], st["u"]
+    Bt, Ct = v[..., R:R + N], v[..., R + N:]
+    ref = dl * u * np.sum(Bt * Ct, axis=-1, keepdims=True)
+    _close(st["bwd"]["s"], ref, what="local window 1")
+
+
+def pin_local_windows_independent(O):
+    """Each window [a, a + L) (aligned at t = 0, the last one partial) is the
+    reverse scan of that window's inputs alone."""
+    rng = np.random.default_rng(62)
+    pf, pb, x, z = _local_case(rng)
+    N = pf["A_log"].shape[1]
+    R = pf["x_proj_w"].shape[0] - 2 * N
+    for axis, L in ((COLS, 4), (ROWS, 2), (COLS, 3)):
+        st = O.layer(x, z, pf, pb, axis, stages=True, local_window=L)
+        T = st["u"].shape[1]
+        v, dl, u = st["fwd"]["v"], st["fwd"]["delta"], st["u"]
+        for a in range(0, T, L):
+            sl = slice(a, min(a + L, T))
+            ref = O.scan(u[:, sl], dl[:, sl], v[:, sl], pf["A_log"], R, reverse=True)
+            _close(st["bwd"]["s"][:, sl], ref, what="local window [%d, %d) axis %d" % (a, sl.stop, axis))
+
+
 ALL_PINS = [
     pin_golden_worked_example,
     pin_geometric_series,
@@ -712,4 +761,7 @@ ALL_PINS = [
     pin_conv_closed_forms,
     pin_conv_transpose,
     pin_conv_causal,
+    pin_local_window_covers_sequence,
+    pin_local_window_one,
+    pin_local_windows_independent,
 ]

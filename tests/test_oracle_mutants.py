@@ -66,6 +66,15 @@ MUTANTS = [
      "const int colmajor = axis == FVO_NONE_COLMAJOR;", 1),
     ("skip reads the conv's input", "(xd ? xd[e] : (double)x[e])", "((double)x[e])", 1),
     ("pool reads the conv's input", "xd ? xd[c + e] : (double)x[c + e]", "(double)x[c + e]", 1),
+    # LBMamba local backward scan
+    ("local windows aligned one step late", "reset[t] = (unsigned char)(t % local_window == local_window - 1);",
+     "reset[t] = (unsigned char)(t % local_window == 0);", 1),
+    ("local windows never reset", "rc = run_direction(u, B, T, E, N, R, &pl, 1, reset, bwd, sb);",
+     "rc = run_direction(u, B, T, E, N, R, &pl, 1, NULL, bwd, sb);", 1),
+    ("local scan reads the backward projection", "const fvo_dir pl = {pf->x_proj_w, pf->dt_proj_w,",
+     "const fvo_dir pl = {pb->x_proj_w, pf->dt_proj_w,", 1),
+    ("local scan runs forward", "rc = run_direction(u, B, T, E, N, R, &pl, 1, reset, bwd, sb);",
+     "rc = run_direction(u, B, T, E, N, R, &pl, 0, reset, bwd, sb);", 1),
     # backward pass
     ("adjoint carried without the decay", "carry[n] = a * lam[n];", "carry[n] = lam[n];", 1),
     ("adjoint decay term with the wrong sign", "dd += lam[n] * (A * a * prev + Bn * ut);",
