@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define FASTVIM_ABI_VERSION 5
+#define FASTVIM_ABI_VERSION 6
 
 typedef enum fastvim_status {
     FASTVIM_OK = 0,
@@ -171,6 +171,22 @@ typedef struct fastvim_params {
 #define FASTVIM_FLAG_CONV 8u
 #define FASTVIM_CONV_TAPS 4
 
+/* FASTVIM_FLAG_LOCAL_BWD replaces the global backward scan by LBMamba's local
+ * backward scan (LBMamba article, pswp.cn, 论文创新点 1-2: a light backward
+ * scan run within subsequences inside the forward selective scan, on the
+ * same inputs, instead of a second global scan).  s_bwd is then the scan
+ * over t descending with the forward direction's projection, step size and
+ * decay, its state starting from zero at the top of every window of
+ * FASTVIM_LOCAL_WINDOW steps aligned at t = 0 (at every t with
+ * t mod FASTVIM_LOCAL_WINDOW = FASTVIM_LOCAL_WINDOW - 1); the layer is
+ *   out = (s_fwd + s_bwd + (D_fwd + D_bwd) x) silu(z)
+ * as before.  Of params.bwd only D is read (the other four may be NULL); pass
+ * D_bwd = 0 for a single skip.  Any pooled, masked or unpooled layer, as
+ * stage kernels (FASTVIM_FLAG_FUSED is ignored); combines with the other
+ * options.  The backward pass returns FASTVIM_ERR_UNSUPPORTED for it. */
+#define FASTVIM_FLAG_LOCAL_BWD 16u
+#define FASTVIM_LOCAL_WINDOW 16
+
 /* Bytes of workspace a call with these sizes needs (0 if the sizes are
  * invalid).  Dense pooled layers need 4 * B * T * (3E + 2(R + 2N)) bytes plus
  * 4 * (2 + 2B) bytes of counters and alignment; unpooled layers hold the per-token projections and scan outputs
@@ -253,8 +269,8 @@ size_t fastvim_ssm_export_bytes(const fastvim_dims *dims, int pool_axis, int wha
  * Supported: pooled layers (COLS or ROWS, dense or masked) with T <= 128 scan
  * steps and the limits of the forward call; FASTVIM_ERR_UNSUPPORTED for
  * unpooled layers, longer scans, and the flags FASTVIM_FLAG_FUSED,
- * FASTVIM_FLAG_POST_NORM and FASTVIM_FLAG_CONV (0 and FASTVIM_FLAG_STAGED run
- * the same kernels). */
+ * FASTVIM_FLAG_POST_NORM, FASTVIM_FLAG_CONV and FASTVIM_FLAG_LOCAL_BWD (0 and
+ * FASTVIM_FLAG_STAGED run the same kernels). */
 
 /* Gradients of one direction's parameters: fp32 device buffers shaped like
  * the parameters, 4-byte aligned, overwritten by the call. */

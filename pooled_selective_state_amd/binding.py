@@ -32,6 +32,8 @@ FLAG_STAGED, FLAG_FUSED = 1, 2
 FLAG_POST_NORM = 4
 FLAG_CONV = 8
 CONV_TAPS = 4
+FLAG_LOCAL_BWD = 16
+LOCAL_WINDOW = 16
 
 STATUS = {
     0: "FASTVIM_OK", -1: "FASTVIM_ERR_NULL", -2: "FASTVIM_ERR_DIMS", -3: "FASTVIM_ERR_UNSUPPORTED",
@@ -173,17 +175,22 @@ def _layer_dims(x, z, params, mask_idx, hw) -> Dims:
 
 
 def _dir_params(params, keep):
+    """DirParams of both directions; a parameter that is absent or None is
+    passed as NULL (FASTVIM_FLAG_LOCAL_BWD reads only D of the backward set)."""
     dirs = []
     for name in ("fwd", "bwd"):
         p = params[name]
-        ts = []
+        ptrs = []
         for f in DIR_FIELDS:
-            t = p[f]
+            t = p.get(f)
+            if t is None:
+                ptrs.append(None)
+                continue
             if t.dtype != torch.float32 or not t.is_contiguous():
                 raise ValueError("parameter %s.%s must be contiguous float32" % (name, f))
-            ts.append(t)
-        keep.extend(ts)
-        dirs.append(DirParams(*[t.data_ptr() for t in ts]))
+            keep.append(t)
+            ptrs.append(t.data_ptr())
+        dirs.append(DirParams(*ptrs))
     return dirs
 
 

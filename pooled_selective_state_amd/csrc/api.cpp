@@ -70,13 +70,27 @@ int check_dir(const fastvim_dir_params& d) {
     return FASTVIM_OK;
 }
 
+// The parameters the kernels see.  With FASTVIM_FLAG_LOCAL_BWD the backward
+// slot carries the forward direction's projection, step size and decay (the
+// local backward scan shares them) and the caller's backward D.
+fastvim_params effective_params(const fastvim_params& p) {
+    fastvim_params q = p;
+    if (p.flags & FASTVIM_FLAG_LOCAL_BWD) {
+        q.bwd.x_proj_w = p.fwd.x_proj_w;
+        q.bwd.dt_proj_w = p.fwd.dt_proj_w;
+        q.bwd.dt_proj_b = p.fwd.dt_proj_b;
+        q.bwd.A_log = p.fwd.A_log;
+    }
+    return q;
+}
+
 // Full validation of a layer call.  *empty is set for B == 0.
 int validate(const void* x, const void* z, const fastvim_params* prm, const fastvim_dims* d, int axis,
              const int32_t* idx, const void* out, Geom* g, Workspace* ws, bool* empty) {
     if (!prm) return FASTVIM_ERR_NULL;
     const uint32_t paths = FASTVIM_FLAG_STAGED | FASTVIM_FLAG_FUSED;
-    if ((prm->flags & ~(paths | FASTVIM_FLAG_POST_NORM | FASTVIM_FLAG_CONV)) || (prm->flags & paths) == paths)
-        return FASTVIM_ERR_ARG;
+    const uint32_t options = FASTVIM_FLAG_POST_NORM | FASTVIM_FLAG_CONV | FASTVIM_FLAG_LOCAL_BWD;
+    if ((prm->flags & ~(paths | options)) || (prm->flags & paths) == paths) return FASTVIM_ERR_ARG;
     int st = resolve_geom(d, axis, g);
     if (st) return st;
     if ((prm->flags & FASTVIM_FLAG_CONV) &&
@@ -86,7 +100,8 @@ int validate(const void* x, const void* z, const fastvim_params* prm, const fast
     *empty = g->B == 0;
     if (*empty) return FASTVIM_OK;
     if (!x || !z || !out || (g->masked && !idx)) return FASTVIM_ERR_NULL;
-    if ((st = check_dir(prm->fwd)) || (st = check_dir(prm->bwd))) return st;
+    const fastvim_params eff = effective_params(*prm);
+    if ((st = check_dir(eff.fwd)) || (st = check_dir(eff.bwd))) return st;
     if (prm->flags & FASTVIM_FLAG_POST_NORM) {
         if (!prm->ln_weight || !prm->ln_bias) return FASTVIM_ERR_NULL;
         if (!aligned(prm->ln_weight, 16) || !aligned(prm->ln_bias, 16)) return FASTVIM_ERR_ALIGN;
@@ -162,10 +177,10 @@ int validate_bwd(const void* x, const void* z, const void* dout, const fastvim_p
                  int axis, const int32_t* idx, const void* dx, const void* dz, const fastvim_grads* gr, Geom* g,
                  BwdWorkspace* ws, bool* empty) {
     if (!prm) return FASTVIM_ERR_NULL;
-    const uint32_t known = FASTVIM_FLAG_STAGED | FASTVIM_FLAG_FUSED | FASTVIM_FLAG_POST_NORM | FASTVIM_FLAG_CONV;
-    if (prm->flags & ~known) return FASTVIM_ERR_ARG;
-    if (prm->flags & (FASTVIM_FLAG_FUSED | FASTVIM_FLAG_POST_NORM | FASTVIM_FLAG_CONV))
-        return FASTVIM_ERR_UNSUPPORTED;
+    const uint32_t unsupported =
+        FASTVIM_FLAG_FUSED | FASTVIM_FLAG_POST_NORM | FASTVIM_FLAG_CONV | FASTVIM_FLAG_LOCAL_BWD;
+    if (prm->flags & ~(FASTVIM_FLAG_STAGED | unsupported)) return FASTVIM_ERR_ARG;
+    if (prm->flags & unsupported) return FASTVIM_ERR_UNSUPPORTED;
     int st = resolve_geom(d, axis, g);
     if (st) return st;
     if (!bwd_supported(*g)) return FASTVIM_ERR_UNSUPPORTED;
@@ -357,13 +372,14 @@ int fastvim_ssm_fwd(const void* x, const void* z, const fastvim_params* params, 
     if (st || empty) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (launch_zero_sync(ws, sync_words(g), s) != hipSuccess) return FASTVIM_ERR_HIP;
-    const bool single = !(params->flags & (FASTVIM_FLAG_POST_NORM | FASTVIM_FLAG_CONV)) &&
+    const fastvim_params q = effective_params(*params);
+    const bool single = !(params->flags & (FASTVIM_FLAG_POST_NORM | FASTVIM_FLAG_CONV | FASTVIM_FLAG_LOCAL_BWD)) &&
                         ((params->flags & FASTVIM_FLAG_FUSED) ? fused_supported(g)
                                                               : !(params->flags & FASTVIM_FLAG_STAGED) && fused_preferred(g));
     if (single)
         return launch_fused(g, x, z, *params, ws, out, s) == hipSuccess ? FASTVIM_OK : FASTVIM_ERR_HIP;
     for (int stage = FASTVIM_STAGE_ROWS; stage <= FASTVIM_STAGE_EPILOGUE; ++stage) {
-        st = run_stage(stage, g, x, z, *params, mask_idx, out, ws, s);
+        st = run_stage(stage, g, x, z, q, mask_idx, out, ws, s);
         if (st) return st;
     }
     return FASTVIM_OK;
@@ -377,7 +393,7 @@ int fastvim_ssm_stage(int stage, const void* x, const void* z, const fastvim_par
     bool empty = false;
     int st = validate(x, z, params, dims, pool_axis, mask_idx, out, &g, &ws, &empty);
     if (st || empty) return st;
-    return run_stage(stage, g, x, z, *params, mask_idx, out, ws, static_cast<hipStream_t>(stream));
+    return run_stage(stage, g, x, z, effective_params(*params), mask_idx, out, ws, static_cast<hipStream_t>(stream));
 }
 
 size_t fastvim_ssm_export_bytes(const fastvim_dims* dims, int pool_axis, int what) {

@@ -175,6 +175,7 @@ struct ScanLane {
     float A2[kNs], hs[kNs], wq[kWQ], bias;
     float* sq;
     int64_t sstep;
+    int reset_s;  // local backward scan: the chunk step whose state starts from zero (T mod kChunk)
 };
 
 template <int RMAX>
@@ -206,6 +207,7 @@ __device__ __forceinline__ void scan_lane_setup(const ScanArgs& a, int64_t b, in
         L.wq[i] = r < R ? p.dt_proj_w[ec * R + r] : 0.f;
     }
     L.bias = p.dt_proj_b[ec];
+    L.reset_s = (int)(a.T % kChunk);
     // traversal step ti is t = ti forward, t = T - 1 - ti backward
     L.sstep = L.dir ? -a.E : a.E;
     L.sq = (L.dir ? a.s_b + (a.T - 1) * a.E : a.s_f) + b * a.T * a.E + ec + L.q * L.sstep;
@@ -246,7 +248,12 @@ __device__ __forceinline__ void scan_step_preact(const ScanLane<RMAX>& L, const 
 // Phases 3 and 4 of one chunk.  dr: this direction's LDS row of the chunk's
 // local step 0; ucur: token values of the lane's steps q + 4j; base:
 // traversal index of local step 0.
-template <int RMAX, bool WRITE_THROUGH>
+// LOCAL: the backward-direction lanes run LBMamba's local backward scan,
+// whose state starts from zero at the top of every window of kChunk steps
+// aligned at t = 0 (t mod kChunk = kChunk - 1).  In the backward traversal
+// (t = T - 1 - ti, ti = base + s with base a multiple of kChunk) that is the
+// chunk step s = T mod kChunk of every chunk.
+template <int RMAX, bool WRITE_THROUGH, bool LOCAL = false>
 __device__ __forceinline__ void scan_chunk(const ScanArgs& a, ScanLane<RMAX>& L, const float* dr,
                                            const float (&ucur)[kJ], int64_t base) {
     constexpr int S = row_stride_lds<RMAX>();
@@ -294,6 +301,10 @@ __device__ __forceinline__ void scan_chunk(const ScanArgs& a, ScanLane<RMAX>& L,
             }
             const float bt[kNs] = {b4.x, b4.y, b4.z, b4.w}, ct[kNs] = {c4.x, c4.y, c4.z, c4.w};
             float part = 0.f;
+            if (LOCAL && L.dir && s == L.reset_s) {
+#pragma unroll
+                for (int n = 0; n < kNs; ++n) L.hs[n] = 0.f;
+            }
 #pragma unroll
             for (int n = 0; n < kNs; ++n) {
                 const float dA = __builtin_amdgcn_exp2f(dlt * L.A2[n]);
@@ -320,7 +331,7 @@ __device__ __forceinline__ void scan_chunk(const ScanArgs& a, ScanLane<RMAX>& L,
 template <int RMAX>
 constexpr int chunk_lds_floats() { return 2 * kChunk * row_stride_lds<RMAX>(); }
 
-template <int RMAX, bool WRITE_THROUGH, class USrc>
+template <int RMAX, bool WRITE_THROUGH, class USrc, bool LOCAL = false>
 __device__ __forceinline__ void scan_tile(const ScanArgs& a, const USrc& usrc, int64_t b, int64_t e0,
                                           float* xs /* chunk_lds_floats<RMAX>() */) {
     constexpr int S = row_stride_lds<RMAX>();
@@ -368,7 +379,7 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, const USrc& usrc, i
         for (int j = 0; j < kJ; ++j) ucur[j] = pre_u[j];
         __syncthreads();
         if (c + 1 < nchunks) prefetch(base + kChunk);
-        scan_chunk<RMAX, WRITE_THROUGH>(a, L, xs + L.dir * kChunk * S, ucur, base);
+        scan_chunk<RMAX, WRITE_THROUGH, LOCAL>(a, L, xs + L.dir * kChunk * S, ucur, base);
     }
 }
 

@@ -32,7 +32,7 @@ def test_library_exports_every_declared_function():
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(Bd.EXPORTED_SYMBOLS)
-    assert lib.fastvim_abi_version() == 5
+    assert lib.fastvim_abi_version() == 6
 
 
 def test_status_strings():
@@ -150,7 +150,7 @@ def test_bad_enums():
     c = FakeCall()
     assert lib.fastvim_ssm_stage(5, c.x, c.z, ctypes.byref(c.params), ctypes.byref(c.dims), 0, None, c.out,
                                  None) == EARG
-    for flags in (P.FLAG_STAGED | P.FLAG_FUSED, 16, 1 << 31):  # conflicting or unknown flags
+    for flags in (P.FLAG_STAGED | P.FLAG_FUSED, 32, 1 << 31):  # conflicting or unknown flags
         c = FakeCall()
         c.params.flags = flags
         expect(c, EARG)
@@ -321,7 +321,7 @@ def test_bwd_unsupported_and_bad_flags():
         assert FakeBwd(axis=axis).bwd() == EUNSUP
     assert FakeBwd(h=129).bwd() == EUNSUP
     assert FakeBwd(N=8).bwd() == EUNSUP
-    for flags, code in ((P.FLAG_FUSED, EUNSUP), (P.FLAG_POST_NORM, EUNSUP), (P.FLAG_CONV, EUNSUP), (16, EARG),
+    for flags, code in ((P.FLAG_FUSED, EUNSUP), (P.FLAG_POST_NORM, EUNSUP), (P.FLAG_CONV, EUNSUP), (P.FLAG_LOCAL_BWD, EUNSUP), (32, EARG),
                         (P.FLAG_STAGED, OK)):
         c = FakeBwd()
         c.params.flags = flags
@@ -399,5 +399,26 @@ def test_conv_validation():
     c.params.flags = P.FLAG_CONV
     assert c.bwd() == EUNSUP
     c = FakeCall()
-    c.params.flags = 16
+    c.params.flags = 32
     expect(c, EARG)
+
+
+def test_local_bwd_validation():
+    """LBMamba's local backward scan reads only D of the backward parameters:
+    a NULL backward D is an error, misaligned D too; the backward pass does
+    not take the option."""
+    c = FakeCall()
+    c.params.flags = P.FLAG_LOCAL_BWD
+    c.params.bwd.D = None
+    expect(c, ENULL)
+    c = FakeCall()
+    c.params.flags = P.FLAG_LOCAL_BWD
+    c.params.bwd.D += 2
+    expect(c, EALIGN)
+    c = FakeCall()
+    c.params.flags = P.FLAG_LOCAL_BWD
+    c.params.fwd.A_log = None  # the forward set is still read
+    expect(c, ENULL)
+    c = FakeBwd()
+    c.params.flags = P.FLAG_LOCAL_BWD
+    assert c.bwd() == EUNSUP
