@@ -322,6 +322,21 @@ def main():
         extras["unpooled_2048"] = {"T": cfg.h * cfg.w, "layer_ms": u_ms, "scan_ms": u_scan, "proj_ms": u_proj,
                                    "layer_speedup_pooled": u_ms / ms, "scan_speedup_pooled": u_scan / stages["scan"]}
         del ucall
+        # LBMamba's local backward scan in place of the global one: unpooled (T = h w) and pooled
+        lb = {}
+        for name, axis, reps in (("unpooled", P.POOL_NONE_ROWMAJOR, 3), ("pooled", P.POOL_COLS, n)):
+            lcall = P.SSMCall(x, z, prm, axis, out=call.out, flags=P.FLAG_LOCAL_BWD)
+            lcall.run(stream)
+            l_ms, _ = time_steps(lambda: lcall.run(stream), reps, stream)
+            l_scan, _ = time_steps(lambda: lcall.stage(P.STAGE_SCAN, stream), reps, stream)
+            l_proj, _ = time_steps(lambda: lcall.stage(P.STAGE_PROJ, stream), reps, stream)
+            lb[name] = {"layer_ms": l_ms, "scan_ms": l_scan, "proj_ms": l_proj}
+            del lcall
+        lb["unpooled"]["scan_vs_bidirectional"] = lb["unpooled"]["scan_ms"] / u_scan
+        lb["unpooled"]["layer_vs_bidirectional"] = lb["unpooled"]["layer_ms"] / u_ms
+        lb["window"] = P.LOCAL_WINDOW
+        extras["local_bwd_2048"] = lb
+        torch.cuda.empty_cache()
         torch.cuda.empty_cache()
         log("unpooled layer %.3f ms, scan %.3f ms" % (u_ms, u_scan))
         # 1024^2 two-block chain on a quarter of the same buffers (same E and R)

@@ -37,16 +37,16 @@ __device__ __forceinline__ void load4(const uint16_t* p, float (&v)[4]) {
 template <class Elem, int CT>
 __global__ void __launch_bounds__(64 * kPW)
 proj_kernel(const Elem* __restrict__ src, int map_axis, int64_t M, int64_t T, int64_t h, int64_t w, int64_t E,
-            const float* __restrict__ Wf, const float* __restrict__ Wb, int NX, float* __restrict__ xdbl) {
+            const float* __restrict__ Wf, const float* __restrict__ Wb, int NX, int nout, float* __restrict__ xdbl) {
     __shared__ float red[kPW][CT][256];  // each wave's partial tiles, [lane * 4 + r]
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int ri = lane & 15, kk = lane >> 4;
     const int NO = 2 * NX;
     const int64_t m0 = (int64_t)blockIdx.x * 16;
 
-    // Rows past M and columns past 2NX read a valid row instead (the last
-    // token, weight row 0): their outputs are never stored, so the loads need
-    // no per-lane guards.
+    // Rows past M and columns past the computed ones read a valid row instead
+    // (the last token, a weight row in range): their outputs are never stored,
+    // so the loads need no per-lane guards.
     const int64_t m = m0 + ri < M ? m0 + ri : M - 1;
     int64_t tok = m;  // pooled tokens and row-major order: row m is token m
     if (map_axis == FASTVIM_POOL_NONE_COLMAJOR) {
@@ -117,7 +117,7 @@ proj_kernel(const Elem* __restrict__ src, int map_axis, int64_t M, int64_t T, in
         for (int q = 1; q < kPW; ++q) v += red[q][ct][src_idx];
         const int64_t mm = m0 + i;
         const int o = ct * 16 + j;
-        if (mm < M && o < NO) xdbl[mm * NO + o] = v;
+        if (mm < M && o < nout) xdbl[mm * NO + o] = v;
     }
 }
 
@@ -129,7 +129,8 @@ proj_kernel(const Elem* __restrict__ src, int map_axis, int64_t M, int64_t T, in
 template <class Elem, int CT, int RT>
 __global__ void __launch_bounds__(64 * kPW)
 proj_rows_kernel(const Elem* __restrict__ src, int map_axis, int64_t M, int64_t T, int64_t h, int64_t w, int64_t E,
-                 const float* __restrict__ Wf, const float* __restrict__ Wb, int NX, float* __restrict__ xdbl) {
+                 const float* __restrict__ Wf, const float* __restrict__ Wb, int NX, int nout,
+                 float* __restrict__ xdbl) {
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int ri = lane & 15, kk = lane >> 4;
     const int NO = 2 * NX;
@@ -205,7 +206,7 @@ proj_rows_kernel(const Elem* __restrict__ src, int map_axis, int64_t M, int64_t 
             for (int r = 0; r < 4; ++r) {
                 const int64_t mm = m0 + rt * 16 + 4 * kk + r;
                 const int o = ct * 16 + ri;
-                if (mm < M && o < NO) xdbl[mm * NO + o] = acc[rt][ct][r];
+                if (mm < M && o < nout) xdbl[mm * NO + o] = acc[rt][ct][r];
             }
 }
 
@@ -214,29 +215,33 @@ constexpr int64_t kRowsMinTokens = 64 * 1024;    // token count from which it is
 
 template <class Elem, int CT>
 hipError_t proj_launch(const Elem* src, int map_axis, const Geom& g, const fastvim_params& p, const Workspace& ws,
-                       hipStream_t st) {
+                       int nout, hipStream_t st) {
     const int64_t M = g.B * g.T;
     if (M >= kRowsMinTokens) {
         const int64_t rows = 16 * kRowsRT * kPW;
         hipLaunchKernelGGL((proj_rows_kernel<Elem, CT, kRowsRT>), dim3((unsigned)((M + rows - 1) / rows)),
                            dim3(64 * kPW), 0, st, src, map_axis, M, g.T, g.h, g.w, g.E, p.fwd.x_proj_w,
-                           p.bwd.x_proj_w, (int)g.NX, ws.xdbl);
+                           p.bwd.x_proj_w, (int)g.NX, nout, ws.xdbl);
     } else {
         hipLaunchKernelGGL((proj_kernel<Elem, CT>), dim3((unsigned)((M + 15) / 16)), dim3(64 * kPW), 0, st, src,
-                           map_axis, M, g.T, g.h, g.w, g.E, p.fwd.x_proj_w, p.bwd.x_proj_w, (int)g.NX, ws.xdbl);
+                           map_axis, M, g.T, g.h, g.w, g.E, p.fwd.x_proj_w, p.bwd.x_proj_w, (int)g.NX, nout,
+                           ws.xdbl);
     }
     return hipGetLastError();
 }
 
+// Both directions' columns (2 NX), or only the forward direction's (NX) when
+// LBMamba's local backward scan shares the forward projection.
 template <class Elem>
 hipError_t proj_dispatch(const Elem* src, int map_axis, const Geom& g, const fastvim_params& p,
                          const Workspace& ws, hipStream_t st) {
-    const int ct = (int)((2 * g.NX + 15) / 16);  // 2NX in [66, 192]
+    const int nout = (int)((p.flags & FASTVIM_FLAG_LOCAL_BWD) ? g.NX : 2 * g.NX);  // in [33, 192]
+    const int ct = (nout + 15) / 16;
     switch (ct) {
 #define FASTVIM_CPT(n) \
-    case n: return proj_launch<Elem, n>(src, map_axis, g, p, ws, st);
-        FASTVIM_CPT(5) FASTVIM_CPT(6) FASTVIM_CPT(7) FASTVIM_CPT(8) FASTVIM_CPT(9) FASTVIM_CPT(10)
-        FASTVIM_CPT(11) FASTVIM_CPT(12)
+    case n: return proj_launch<Elem, n>(src, map_axis, g, p, ws, nout, st);
+        FASTVIM_CPT(3) FASTVIM_CPT(4) FASTVIM_CPT(5) FASTVIM_CPT(6) FASTVIM_CPT(7) FASTVIM_CPT(8)
+        FASTVIM_CPT(9) FASTVIM_CPT(10) FASTVIM_CPT(11) FASTVIM_CPT(12)
 #undef FASTVIM_CPT
         default: return hipErrorInvalidValue;
     }

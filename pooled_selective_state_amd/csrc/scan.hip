@@ -1,9 +1,10 @@
 // Standalone scan stage: one 512-thread workgroup per (image, 64-channel
 // group) runs both scan directions over the whole sequence (see scan_core.h
 // for the recurrence, its sources and the lane layout).  With LBMamba's
-// local backward scan (LBMamba article, 论文创新点 1-2) the backward lanes
-// scan windows of kChunk steps with the forward direction's inputs, at the
-// same time as the forward lanes run the global scan.  Used by the staged
+// local backward scan (LBMamba article, 论文创新点 1-2: run inside the forward
+// scan, in the thread's registers, on its own chunk) every lane scans
+// forward and follows each chunk with the chunk's local backward scan, so a
+// workgroup needs half the lanes.  Used by the staged
 // path (masked and unpooled layers, stage-by-stage calls); the fused layer
 // kernel runs the same core as one of its work items.
 #include "scan_core.h"
@@ -11,6 +12,11 @@
 namespace fastvim {
 namespace {
 
+// A workgroup scans kScanCh channels: in both directions (kScanThreads
+// lanes), or (LOCAL, kScanThreads / 2 lanes) forward, each lane adding the
+// local backward scan of its chunks.  Half-size workgroups keep the grid as
+// large as in the bidirectional case (long unpooled scans balance over the
+// CUs only with several workgroups per CU).
 template <int RMAX, class USrc, bool LOCAL>
 __global__ void __launch_bounds__(kScanThreads) scan_kernel(ScanArgs a, USrc usrc, int nEg) {
     __shared__ float xs[chunk_lds_floats<RMAX>()];
@@ -19,16 +25,14 @@ __global__ void __launch_bounds__(kScanThreads) scan_kernel(ScanArgs a, USrc usr
     scan_tile<RMAX, false, USrc, LOCAL>(a, usrc, b, e0, xs);
 }
 
-// With FASTVIM_FLAG_LOCAL_BWD the caller's parameters already carry the
-// forward direction's projection, step size and decay in p.bwd.
 template <int RMAX, class USrc>
 hipError_t scan_launch(const USrc& usrc, const Geom& g, const fastvim_params& p, const Workspace& ws,
                        hipStream_t st) {
-    const int nEg = (int)((g.E + kScanCh - 1) / kScanCh);
     ScanArgs a{ws.xdbl, p.fwd, p.bwd, ws.s_f, ws.s_b, g.T, g.E, (int)g.R, (int)g.NX};
+    const int nEg = (int)((g.E + kScanCh - 1) / kScanCh);
     if (p.flags & FASTVIM_FLAG_LOCAL_BWD)
-        hipLaunchKernelGGL((scan_kernel<RMAX, USrc, true>), dim3((unsigned)(g.B * nEg)), dim3(kScanThreads), 0, st,
-                           a, usrc, nEg);
+        hipLaunchKernelGGL((scan_kernel<RMAX, USrc, true>), dim3((unsigned)(g.B * nEg)), dim3(kScanThreads / 2), 0,
+                           st, a, usrc, nEg);
     else
         hipLaunchKernelGGL((scan_kernel<RMAX, USrc, false>), dim3((unsigned)(g.B * nEg)), dim3(kScanThreads), 0, st,
                            a, usrc, nEg);

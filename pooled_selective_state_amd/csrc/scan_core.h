@@ -175,16 +175,18 @@ struct ScanLane {
     float A2[kNs], hs[kNs], wq[kWQ], bias;
     float* sq;
     int64_t sstep;
-    int reset_s;  // local backward scan: the chunk step whose state starts from zero (T mod kChunk)
+    float* sqb;  // local backward scan: the lane's first output in s_bwd (its step q)
 };
 
-template <int RMAX>
+// LOCAL: every lane scans forward (with kScanThreads / 2 lanes a workgroup
+// covers the kScanCh channels [e0, e0 + 64); with more, the next 64).
+template <int RMAX, bool LOCAL = false>
 __device__ __forceinline__ void scan_lane_setup(const ScanArgs& a, int64_t b, int64_t e0, ScanLane<RMAX>& L,
                                                 int64_t& ec) {
     static_assert(RMAX % 16 == 0 && RMAX <= kRMax, "dt rank bound: 16-byte aligned rows and lane quarters");
     const int tid = threadIdx.x;
-    L.dir = tid >> 8;
-    const int ch = (tid & 255) / kLps;
+    L.dir = LOCAL ? 0 : tid >> 8;
+    const int ch = (tid & 255) / kLps + (LOCAL ? kScanCh * (tid >> 8) : 0);
     L.l = tid & (kLps - 1);
     L.q = tid & 3;
     const int64_t e = e0 + ch;
@@ -207,10 +209,10 @@ __device__ __forceinline__ void scan_lane_setup(const ScanArgs& a, int64_t b, in
         L.wq[i] = r < R ? p.dt_proj_w[ec * R + r] : 0.f;
     }
     L.bias = p.dt_proj_b[ec];
-    L.reset_s = (int)(a.T % kChunk);
     // traversal step ti is t = ti forward, t = T - 1 - ti backward
     L.sstep = L.dir ? -a.E : a.E;
     L.sq = (L.dir ? a.s_b + (a.T - 1) * a.E : a.s_f) + b * a.T * a.E + ec + L.q * L.sstep;
+    L.sqb = a.s_b + b * a.T * a.E + ec + L.q * a.E;
 }
 
 // Phase 3 for the kChunk steps of LDS rows dr: qv[j] is the step-size
@@ -248,17 +250,19 @@ __device__ __forceinline__ void scan_step_preact(const ScanLane<RMAX>& L, const 
 // Phases 3 and 4 of one chunk.  dr: this direction's LDS row of the chunk's
 // local step 0; ucur: token values of the lane's steps q + 4j; base:
 // traversal index of local step 0.
-// LOCAL: the backward-direction lanes run LBMamba's local backward scan,
-// whose state starts from zero at the top of every window of kChunk steps
-// aligned at t = 0 (t mod kChunk = kChunk - 1).  In the backward traversal
-// (t = T - 1 - ti, ti = base + s with base a multiple of kChunk) that is the
-// chunk step s = T mod kChunk of every chunk.
+// LOCAL (forward lanes only): after the chunk's forward steps the lane runs
+// LBMamba's local backward scan over the same kChunk steps, last first, from
+// a zero state -- the window of kChunk steps aligned at t = 0 -- and stores
+// it to s_bwd.  Step t of that scan decays by the same exp(Delta_t A) as step
+// t of the forward scan, so the chunk's decays are kept in registers and the
+// local scan needs no exponential and no second step-size pass.
 template <int RMAX, bool WRITE_THROUGH, bool LOCAL = false>
 __device__ __forceinline__ void scan_chunk(const ScanArgs& a, ScanLane<RMAX>& L, const float* dr,
                                            const float (&ucur)[kJ], int64_t base) {
     constexpr int S = row_stride_lds<RMAX>();
     const int64_t T = a.T;
-    float dl[kJ], du[kJ];
+    float dl[kJ], du[kJ], du0[kJ];
+    float aS[LOCAL ? kChunk : 1][kNs];  // decays of the chunk's steps (LOCAL)
     {
         float qv[kJ];
         scan_step_preact<RMAX>(L, dr, qv);
@@ -268,6 +272,7 @@ __device__ __forceinline__ void scan_chunk(const ScanArgs& a, ScanLane<RMAX>& L,
             const float d = softplus_f(qv[j]);
             dl[j] = in ? d : 0.f;
             du[j] = in ? d * ucur[j] : 0.f;
+            du0[j] = du[j];
         }
     }
     // the recurrence, four steps (one per quad lane's step size) at a time;
@@ -301,13 +306,10 @@ __device__ __forceinline__ void scan_chunk(const ScanArgs& a, ScanLane<RMAX>& L,
             }
             const float bt[kNs] = {b4.x, b4.y, b4.z, b4.w}, ct[kNs] = {c4.x, c4.y, c4.z, c4.w};
             float part = 0.f;
-            if (LOCAL && L.dir && s == L.reset_s) {
-#pragma unroll
-                for (int n = 0; n < kNs; ++n) L.hs[n] = 0.f;
-            }
 #pragma unroll
             for (int n = 0; n < kNs; ++n) {
                 const float dA = __builtin_amdgcn_exp2f(dlt * L.A2[n]);
+                if (LOCAL) aS[LOCAL ? s : 0][n] = dA;
                 L.hs[n] = fmaf(dA, L.hs[n], dus * bt[n]);
                 part = fmaf(ct[n], L.hs[n], part);
             }
@@ -319,6 +321,39 @@ __device__ __forceinline__ void scan_chunk(const ScanArgs& a, ScanLane<RMAX>& L,
             else *sp = keep;
         }
         sp += 4 * L.sstep;
+    }
+    if (LOCAL) {
+        // the local backward scan over the chunk (steps past T have zero input
+        // and decay 1, so the state stays zero through them)
+        float hl[kNs] = {0.f, 0.f, 0.f, 0.f};
+        // B_t and C_t are read from LDS again: an offset the compiler cannot
+        // see through keeps it from holding the forward pass's 16 steps of
+        // them in registers instead (about 128 more per lane)
+        int zero = 0;
+        __asm__ volatile("" : "+v"(zero));
+        const float* lrows = dr + RMAX + kNs * L.l + zero;
+#pragma unroll
+        for (int k = kJ - 1; k >= 0; --k) {
+            float keep = 0.f;
+#pragma unroll
+            for (int m = 3; m >= 0; --m) {
+                const int s = 4 * k + m;
+                const float dus = m == 0 ? quad_bcast<0>(du0[k]) : m == 1 ? quad_bcast<1>(du0[k])
+                                : m == 2 ? quad_bcast<2>(du0[k]) : quad_bcast<3>(du0[k]);
+                const f32x4 b4 = *reinterpret_cast<const f32x4*>(lrows + s * S);
+                const f32x4 c4 = *reinterpret_cast<const f32x4*>(lrows + s * S + 16);
+                const float bt[kNs] = {b4.x, b4.y, b4.z, b4.w}, ct[kNs] = {c4.x, c4.y, c4.z, c4.w};
+                float part = 0.f;
+#pragma unroll
+                for (int n = 0; n < kNs; ++n) {
+                    hl[n] = fmaf(aS[LOCAL ? s : 0][n], hl[n], dus * bt[n]);
+                    part = fmaf(ct[n], hl[n], part);
+                }
+                part = seq_sum(part);
+                keep = (m == L.q) ? part : keep;
+            }
+            if (L.valid && base + 4 * k + L.q < T) L.sqb[(base + 4 * k) * a.E] = keep;
+        }
     }
 }
 
@@ -338,7 +373,7 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, const USrc& usrc, i
     constexpr int kPre = row_loads<RMAX>();
     ScanLane<RMAX> L;
     int64_t ec;
-    scan_lane_setup<RMAX>(a, b, e0, L, ec);
+    scan_lane_setup<RMAX, LOCAL>(a, b, e0, L, ec);
     const int tid = threadIdx.x;
     const int NX = a.NX;
     const int64_t T = a.T;
@@ -355,9 +390,10 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, const USrc& usrc, i
 #pragma unroll
     for (int i = 0; i < kPre; ++i) scol[i] = lds_source_col<RMAX>(po + kRowLanes * i, a.R);
     float pre_x[kPre], pre_u[kJ];
+    const int pdr = LOCAL ? 0 : pd;  // LOCAL: both halves hold the forward rows (only the first is read)
     auto prefetch = [&](int base) {
         const int ti = base + ps;
-        const float* src = xb + ((pd ? iT - 1 - ti : ti) * row_stride + pd * NX);
+        const float* src = xb + ((pdr ? iT - 1 - ti : ti) * row_stride + pdr * NX);
 #pragma unroll
         for (int i = 0; i < kPre; ++i) pre_x[i] = (ti < iT && scol[i] >= 0) ? src[scol[i]] : 0.f;
 #pragma unroll
