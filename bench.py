@@ -20,9 +20,12 @@ Reported besides images/s:
   cpu_baseline  the fp64 CPU oracle on the same host arrays, cycled over the
                 batch for at least --cpu-seconds;
   extras        the stage-kernel path and its per-stage times, the other
-                pooling axis, the calibration-copy ceiling, the unpooled layer
-                (scan over all h*w tokens) with the pooled / unpooled ratios,
-                and the 1024^2 two-block chain.
+                pooling axis, the layer with the post-SSM LayerNorm, the layer
+                with the producer Conv1D fused, the backward pass, the
+                unpooled layer (scan over all h*w tokens) with the pooled /
+                unpooled ratios, LBMamba's local backward scan against the
+                bidirectional one, the 1024^2 two-block chain, and the small
+                workloads over rotating input sets.
 --profile-run times a few steps and the calibration copy only (for profiler
 runs).
 """
