@@ -9,7 +9,7 @@ default path, one pipelined kernel launch (plus a one-block launch that resets
 its counters).  Prints one JSON line on stdout.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-extras] [--no-cpu-baseline]
-                    [--cpu-seconds S] [--profile-run]
+                    [--cpu-seconds S] [--profile-run] [--profile-bwd]
 
 Reported besides images/s:
   roofline      the single-launch kernel against the 8 TB/s HBM peak, with
@@ -27,7 +27,7 @@ Reported besides images/s:
                 bidirectional one, the 1024^2 two-block chain, and the small
                 workloads over rotating input sets.
 --profile-run times a few steps and the calibration copy only (for profiler
-runs).
+runs); --profile-bwd adds three backward calls of the same workload.
 """
 from __future__ import annotations
 
@@ -61,6 +61,7 @@ def parse():
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum CPU time of the oracle sample")
     ap.add_argument("--profile-run", action="store_true", help="layer steps and calibration copy only")
+    ap.add_argument("--profile-bwd", action="store_true", help="with --profile-run: also three backward calls")
     return ap.parse_args()
 
 
@@ -253,6 +254,13 @@ def main():
                               "bytes_written": 4 * elems, "ms": cp_ms, "kernel": "calib_copy_kernel"}
     del dst
     log("calibration copy %.4f ms (%.0f GB/s)" % (cp_ms, result["copy_ceiling"]["GBps"]))
+    if args.profile_bwd:
+        dout = torch.randn(x.shape, device=dev, generator=torch.Generator(device="cuda").manual_seed(2))
+        bcall = P.BwdCall(x, z, dout, prm, P.POOL_COLS)
+        for _ in range(3):
+            bcall.run(stream)
+        torch.cuda.synchronize()
+        del bcall, dout
 
     if not args.no_extras:
         extras = {}
