@@ -63,9 +63,21 @@ __device__ __forceinline__ float row_quads_sum(float v) {
 }
 __device__ __forceinline__ float sigmoid_f(float q) { return __builtin_amdgcn_rcpf(1.f + __expf(-q)); }
 
-template <int M>
-__device__ __forceinline__ float bcast(float v) {
-    return quad_bcast<M>(v);
+// Lane m of the quad's value (m a compile-time constant after unrolling).
+__device__ __forceinline__ float qpick(int m, float v) {
+    return m == 0 ? quad_bcast<0>(v) : m == 1 ? quad_bcast<1>(v) : m == 2 ? quad_bcast<2>(v) : quad_bcast<3>(v);
+}
+
+// One step of the forward recurrence on the lane's 4 states, from the LDS
+// row of the step (B_t at RMAX + 4q).
+template <int RMAX>
+__device__ __forceinline__ void recompute_step(float (&hs)[kNs], const float* row, float dlt, float us,
+                                               const float (&A2)[kNs], int q) {
+    const f32x4 b4 = *reinterpret_cast<const f32x4*>(row + RMAX + kNs * q);
+    const float bt[kNs] = {b4.x, b4.y, b4.z, b4.w};
+    const float du = dlt * us;
+#pragma unroll
+    for (int n = 0; n < kNs; ++n) hs[n] = fmaf(__builtin_amdgcn_exp2f(dlt * A2[n]), hs[n], du * bt[n]);
 }
 
 template <int RMAX>
@@ -240,40 +252,54 @@ __global__ void __launch_bounds__(kBwdThreads) scan_bwd_kernel(BwdScanArgs a) {
             dl[j] = in ? softplus_f(qv[j]) : 0.f;
             sg[j] = in ? sigmoid_f(qv[j]) : 0.f;
         }
-        // states of the chunk's steps, recomputed from the checkpoint
-        float Hc[kChunk][kNs];
+        // the states entering each group of 4 steps: hb[j] for steps 4j .. 4j + 3
+        float hb[kJ][kNs];
         {
             float hs[kNs];
 #pragma unroll
-            for (int n = 0; n < kNs; ++n) hs[n] = h0[n];
+            for (int n = 0; n < kNs; ++n) hs[n] = hb[0][n] = h0[n];
 #pragma unroll
-            for (int s = 0; s < kChunk; ++s) {
+            for (int s = 0; s + 4 < kChunk; ++s) {
                 const int m = s & 3, j = s >> 2;
-                const float dlt = m == 0 ? bcast<0>(dl[j]) : m == 1 ? bcast<1>(dl[j]) : m == 2 ? bcast<2>(dl[j]) : bcast<3>(dl[j]);
-                const float us = m == 0 ? bcast<0>(uc[j]) : m == 1 ? bcast<1>(uc[j]) : m == 2 ? bcast<2>(uc[j]) : bcast<3>(uc[j]);
-                const f32x4 b4 = *reinterpret_cast<const f32x4*>(dr + s * S + RMAX + kNs * q);
-                const float bt[kNs] = {b4.x, b4.y, b4.z, b4.w};
-                const float du_ = dlt * us;
+                recompute_step<RMAX>(hs, dr + s * S, qpick(m, dl[j]), qpick(m, uc[j]), L.A2, q);
+                if (m == 3) {
 #pragma unroll
-                for (int n = 0; n < kNs; ++n) {
-                    hs[n] = fmaf(__builtin_amdgcn_exp2f(dlt * L.A2[n]), hs[n], du_ * bt[n]);
-                    Hc[s][n] = hs[n];
+                    for (int n = 0; n < kNs; ++n) hb[j + 1][n] = hs[n];
                 }
             }
         }
-        float duo[kJ];
+        // Groups of 4 steps, last first, one group per iteration of a rolled
+        // loop (so one group's values are live at a time): the group's inputs
+        // sit at index kJ - 1 of arrays rotated right after each group.
+#pragma unroll 1
+        for (int j = kJ - 1; j >= 0; --j) {
+            const float* gr = dr + 4 * j * S;  // LDS row of the group's first step
+            float Hs[4][kNs], Av[4][kNs];
+            {
+                float hs[kNs];
 #pragma unroll
-        for (int j = 0; j < kJ; ++j) duo[j] = 0.f;
+                for (int n = 0; n < kNs; ++n) hs[n] = hb[kJ - 1][n];
 #pragma unroll
-        for (int half = kChunk / kBwdFlush - 1; half >= 0; --half) {
+                for (int m = 0; m < 4; ++m) {
+                    const float dlt = qpick(m, dl[kJ - 1]), us = qpick(m, uc[kJ - 1]);
+                    const f32x4 b4 = *reinterpret_cast<const f32x4*>(gr + m * S + RMAX + kNs * q);
+                    const float bt[kNs] = {b4.x, b4.y, b4.z, b4.w};
+                    const float du = dlt * us;
 #pragma unroll
-            for (int s = half * kBwdFlush + kBwdFlush - 1; s >= half * kBwdFlush; --s) {
-                const int m = s & 3, j = s >> 2;
-                const float dlt = m == 0 ? bcast<0>(dl[j]) : m == 1 ? bcast<1>(dl[j]) : m == 2 ? bcast<2>(dl[j]) : bcast<3>(dl[j]);
-                const float ut = m == 0 ? bcast<0>(uc[j]) : m == 1 ? bcast<1>(uc[j]) : m == 2 ? bcast<2>(uc[j]) : bcast<3>(uc[j]);
-                const float g = m == 0 ? bcast<0>(gc[j]) : m == 1 ? bcast<1>(gc[j]) : m == 2 ? bcast<2>(gc[j]) : bcast<3>(gc[j]);
-                const float sgs = m == 0 ? bcast<0>(sg[j]) : m == 1 ? bcast<1>(sg[j]) : m == 2 ? bcast<2>(sg[j]) : bcast<3>(sg[j]);
-                const float* row = dr + s * S;
+                    for (int n = 0; n < kNs; ++n) {
+                        Av[m][n] = __builtin_amdgcn_exp2f(dlt * L.A2[n]);
+                        hs[n] = fmaf(Av[m][n], hs[n], du * bt[n]);
+                        Hs[m][n] = hs[n];
+                    }
+                }
+            }
+            const int half = (4 * j) / kBwdFlush;
+            float duo = 0.f;
+#pragma unroll
+            for (int m = 3; m >= 0; --m) {
+                const float dlt = qpick(m, dl[kJ - 1]), ut = qpick(m, uc[kJ - 1]);
+                const float g = qpick(m, gc[kJ - 1]), sgs = qpick(m, sg[kJ - 1]);
+                const float* row = gr + m * S;
                 const f32x4 b4 = *reinterpret_cast<const f32x4*>(row + RMAX + kNs * q);
                 const f32x4 c4 = *reinterpret_cast<const f32x4*>(row + RMAX + 16 + kNs * q);
                 const float bt[kNs] = {b4.x, b4.y, b4.z, b4.w}, ct[kNs] = {c4.x, c4.y, c4.z, c4.w};
@@ -281,19 +307,19 @@ __global__ void __launch_bounds__(kBwdThreads) scan_bwd_kernel(BwdScanArgs a) {
                 const float dut = dlt * ut;
 #pragma unroll
                 for (int n = 0; n < kNs; ++n) {
-                    const float av = __builtin_amdgcn_exp2f(dlt * L.A2[n]);
-                    const float hp = s > 0 ? Hc[s > 0 ? s - 1 : 0][n] : h0[n];
+                    const float av = Av[m][n];
+                    const float hp = m > 0 ? Hs[m > 0 ? m - 1 : 0][n] : hb[kJ - 1][n];
                     const float lam = fmaf(ct[n], g, carry[n]);
                     ddl = fmaf(lam, fmaf(An[n] * av, hp, bt[n] * ut), ddl);
                     dup = fmaf(lam, bt[n], dup);
                     cb[n] = lam * dut;
-                    cc[n] = g * Hc[s][n];
+                    cc[n] = g * Hs[m][n];
                     dA[n] = fmaf(lam * av, dlt * hp, dA[n]);
                     carry[n] = av * lam;
                 }
                 ddl = quad_sum(ddl);
                 dup = quad_sum(dup);
-                duo[j] = (m == q) ? dlt * dup : duo[j];
+                duo = (m == q) ? dlt * dup : duo;
                 const float dq = ddl * sgs;
                 db += dq;
                 // d dt_proj_w over the lane's quarter r = q + 4i, and that
@@ -316,7 +342,7 @@ __global__ void __launch_bounds__(kBwdThreads) scan_bwd_kernel(BwdScanArgs a) {
                     cc[n] = row_quads_sum(cc[n]);
                 }
                 if (row_writer) {
-                    float* rr = red_row + (s - half * kBwdFlush) * kBwdRows * S;
+                    float* rr = red_row + (4 * j + m - half * kBwdFlush) * kBwdRows * S;
 #pragma unroll
                     for (int i = 0; i < kWQ; i += 4)
                         *reinterpret_cast<f32x4*>(rr + q * kWQ + i) = f32x4{cd[i], cd[i + 1], cd[i + 2], cd[i + 3]};
@@ -324,24 +350,33 @@ __global__ void __launch_bounds__(kBwdThreads) scan_bwd_kernel(BwdScanArgs a) {
                     *reinterpret_cast<f32x4*>(rr + RMAX + 16 + kNs * q) = f32x4{cc[0], cc[1], cc[2], cc[3]};
                 }
             }
-            // add the 16 row partials of these steps; one partial per channel group
-            __syncthreads();
-            for (int o = tid; o < kBwdFlush * S; o += kBwdThreads) {
-                const int st = o / S, pos = o - st * S;
-                const int ti = base + half * kBwdFlush + st;
-                const float* src = red + st * kBwdRows * S + pos;
-                float sum = 0.f;
-#pragma unroll
-                for (int r = 0; r < kBwdRows; ++r) sum += src[r * S];
-                if (ti < T) dvp[(int64_t)(dir ? T - 1 - ti : ti) * S + pos] = sum;
+            {
+                const int ti = base + 4 * j + q;
+                if (valid && ti < T) du_dir[(int64_t)(dir ? T - 1 - ti : ti) * E] = duo;
             }
-            __syncthreads();
-        }
-        if (valid) {
+            if ((4 * j) % kBwdFlush == 0) {
+                // add the 16 row partials of these kBwdFlush steps; one partial per channel group
+                __syncthreads();
+                for (int o = tid; o < kBwdFlush * S; o += kBwdThreads) {
+                    const int st = o / S, pos = o - st * S;
+                    const int ti = base + half * kBwdFlush + st;
+                    const float* src = red + st * kBwdRows * S + pos;
+                    float sum = 0.f;
 #pragma unroll
-            for (int j = 0; j < kJ; ++j) {
-                const int ti = base + q + 4 * j;
-                if (ti < T) du_dir[(int64_t)(dir ? T - 1 - ti : ti) * E] = duo[j];
+                    for (int r = 0; r < kBwdRows; ++r) sum += src[r * S];
+                    if (ti < T) dvp[(int64_t)(dir ? T - 1 - ti : ti) * S + pos] = sum;
+                }
+                __syncthreads();
+            }
+            // next group's inputs to index kJ - 1
+#pragma unroll
+            for (int k = kJ - 1; k > 0; --k) {
+                dl[k] = dl[k - 1];
+                uc[k] = uc[k - 1];
+                gc[k] = gc[k - 1];
+                sg[k] = sg[k - 1];
+#pragma unroll
+                for (int n = 0; n < kNs; ++n) hb[k][n] = hb[k - 1][n];
             }
         }
     }
