@@ -218,23 +218,30 @@ bwd_dv_kernel(const float* __restrict__ dvp, float* __restrict__ dv, int64_t B, 
 
 // ---------------------------------------------------------------------- du
 // du[m, e] = du_f[m, e] + du_b[m, e] + sum_o (W_f[o, e] dv[m, 0, o] + W_b[o, e] dv[m, 1, o]).
-// Lane = channel, each wave 16 tokens: the weight column entry is loaded once
-// per (o, 16 tokens) and the dv entries are wave-uniform (scalar) loads.
+// A workgroup takes 64 channels (lane = channel) and 4 kDuTok tokens (wave w
+// the tokens w kDuTok ...); the tokens' dv rows of both directions are staged
+// in LDS and read as broadcasts, each weight entry is loaded once per wave.
 constexpr int kDuTok = 16;
 __global__ void __launch_bounds__(256)
 bwd_du_kernel(const float* __restrict__ du_f, const float* __restrict__ du_b, const float* __restrict__ dv,
               const float* __restrict__ Wf, const float* __restrict__ Wb, float* __restrict__ du, int64_t M, int64_t E,
               int NX) {
+    __shared__ float dvs[4 * kDuTok * 2 * 96];  // [token][d][o]
     const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wave = threadIdx.x >> 6;
     const int64_t e = (int64_t)blockIdx.y * 64 + lane;
     const int64_t ec = e < E ? e : E - 1;
-    const int64_t m0 = ((int64_t)blockIdx.x * 4 + wave) * kDuTok;
-    if (m0 >= M) return;
+    const int64_t mblk = (int64_t)blockIdx.x * 4 * kDuTok;
+    const int nm = (int)(mblk + 4 * kDuTok < M ? 4 * kDuTok : M - mblk);
+    const int row = 2 * NX;
+    for (int idx = threadIdx.x; idx < nm * row; idx += 256) dvs[idx] = dv[mblk * row + idx];
+    __syncthreads();
+    const int t0 = wave * kDuTok;
+    if (t0 >= nm) return;
     float acc[kDuTok];
 #pragma unroll
     for (int k = 0; k < kDuTok; ++k) {
-        const int64_t m = m0 + k < M ? m0 + k : M - 1;
+        const int64_t m = mblk + (t0 + k < nm ? t0 + k : nm - 1);
         acc[k] = du_f[m * E + ec] + du_b[m * E + ec];
     }
     for (int d = 0; d < 2; ++d) {
@@ -243,30 +250,33 @@ bwd_du_kernel(const float* __restrict__ du_f, const float* __restrict__ du_b, co
             const float wv = W[(int64_t)o * E + ec];
 #pragma unroll
             for (int k = 0; k < kDuTok; ++k) {
-                const int64_t m = m0 + k < M ? m0 + k : M - 1;
-                acc[k] = fmaf(wv, dv[(m * 2 + d) * NX + o], acc[k]);
+                const int mm = t0 + k < nm ? t0 + k : nm - 1;
+                acc[k] = fmaf(wv, dvs[mm * row + d * NX + o], acc[k]);
             }
         }
     }
     if (e < E) {
 #pragma unroll
         for (int k = 0; k < kDuTok; ++k)
-            if (m0 + k < M) du[(m0 + k) * E + e] = acc[k];
+            if (t0 + k < nm) du[(mblk + t0 + k) * E + e] = acc[k];
     }
 }
 
 // --------------------------------------------------------------------- dwx
 // Partial of d x_proj_w over one chunk of kBwdTokChunk pooled tokens:
 //   dWxp[chunk, d, o, e] = sum_{m in chunk} dv[m, d, o] u[m, e]
-// Lane = channel, wave w takes the outputs o = w * og ... (wave-uniform dv
-// loads); the token values of 8 tokens are loaded before their products.
-constexpr int kOG = 24;  // outputs per wave: NX <= 96
+// The chunk's dv rows of direction d are staged in LDS with vector loads;
+// lane = channel, wave w takes the outputs o = w * og ... and reads them as
+// LDS broadcasts; the token values of 8 tokens are loaded before their
+// products.
+constexpr int kOG = 24;   // outputs per wave: NX <= 96
 constexpr int kDwxU = 8;  // tokens in flight per lane
 __global__ void __launch_bounds__(256)
 bwd_dwx_kernel(const float* __restrict__ dv, const float* __restrict__ u, float* __restrict__ dWxp, int64_t M,
                int64_t E, int NX) {
+    __shared__ float dvs[kBwdTokChunk * 96];  // [token][o], o < NX <= 96
     const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wave = threadIdx.x >> 6;
     const int64_t chunk = blockIdx.x;
     const int64_t e = (int64_t)blockIdx.y * 64 + lane;
     const int64_t ec = e < E ? e : E - 1;
@@ -274,21 +284,25 @@ bwd_dwx_kernel(const float* __restrict__ dv, const float* __restrict__ u, float*
     const int og = (NX + 3) / 4;
     const int o0 = wave * og;
     const int64_t m0 = chunk * kBwdTokChunk;
-    const int64_t m1 = m0 + kBwdTokChunk < M ? m0 + kBwdTokChunk : M;
+    const int nm = (int)(m0 + kBwdTokChunk < M ? kBwdTokChunk : M - m0);
+    for (int idx = threadIdx.x; idx < nm * NX; idx += 256) {
+        const int mm = idx / NX, o = idx - mm * NX;
+        dvs[mm * NX + o] = dv[((m0 + mm) * 2 + d) * NX + o];
+    }
+    __syncthreads();
     float acc[kOG];
 #pragma unroll
     for (int i = 0; i < kOG; ++i) acc[i] = 0.f;
-    for (int64_t mb = m0; mb < m1; mb += kDwxU) {
+    for (int mb = 0; mb < nm; mb += kDwxU) {
         float uv[kDwxU];
 #pragma unroll
-        for (int k = 0; k < kDwxU; ++k) uv[k] = mb + k < m1 ? u[(mb + k) * E + ec] : 0.f;
+        for (int k = 0; k < kDwxU; ++k) uv[k] = mb + k < nm ? u[(m0 + mb + k) * E + ec] : 0.f;
 #pragma unroll
         for (int k = 0; k < kDwxU; ++k) {
-            const int64_t m = mb + k < m1 ? mb + k : m1 - 1;  // past the chunk: a zero token value
-            const float* dvr = dv + (m * 2 + d) * NX;
+            const float* dvr = dvs + (mb + k < nm ? mb + k : nm - 1) * NX + o0;  // past the chunk: a zero token value
 #pragma unroll
             for (int i = 0; i < kOG; ++i)
-                if (i < og && o0 + i < NX) acc[i] = fmaf(dvr[o0 + i], uv[k], acc[i]);
+                if (i < og && o0 + i < NX) acc[i] = fmaf(dvr[i], uv[k], acc[i]);
         }
     }
     if (e < E) {
