@@ -282,13 +282,17 @@ def main():
         g_ln = torch.Generator(device="cuda").manual_seed(1)
         ln = {"weight": 1.0 + 0.1 * torch.randn(cfg.E, device=dev, generator=g_ln),
               "bias": 0.1 * torch.randn(cfg.E, device=dev, generator=g_ln), "eps": 1e-5}
-        ncall = P.SSMCall(x, z, prm, P.POOL_COLS, workspace=call.workspace, out=call.out, ln=ln)
-        ncall.run(stream)
-        ln_ms, _ = time_steps(lambda: ncall.run(stream), n, stream)
-        ln_epi, _ = time_steps(lambda: ncall.stage(P.STAGE_EPILOGUE, stream), n, stream)
-        extras["post_norm_2048"] = {"layer_ms": ln_ms, "epilogue_ms": ln_epi, "path": "stage kernels",
-                                    "epilogue_GBps": alg_bytes / (ln_epi * 1e-3) / 1e9}
-        del ncall
+        norm = {}
+        for name, fl in (("single_launch", P.FLAG_FUSED), ("stage_kernels", P.FLAG_STAGED)):
+            ncall = P.SSMCall(x, z, prm, P.POOL_COLS, workspace=call.workspace, out=call.out, ln=ln, flags=fl)
+            ncall.run(stream)
+            norm[name + "_ms"], _ = time_steps(lambda: ncall.run(stream), n, stream)
+            if fl == P.FLAG_STAGED:
+                norm["epilogue_ms"], _ = time_steps(lambda: ncall.stage(P.STAGE_EPILOGUE, stream), n, stream)
+                norm["epilogue_GBps"] = alg_bytes / (norm["epilogue_ms"] * 1e-3) / 1e9
+            del ncall
+        norm["single_launch_hbm_frac"] = alg_bytes / (norm["single_launch_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS
+        extras["post_norm_2048"] = norm
         # the producer Conv1D + SiLU fused into the layer (x is the conv's input; stage kernels)
         conv = {"weight": 0.5 * torch.randn(cfg.E, P.CONV_TAPS, device=dev, generator=g_ln),
                 "bias": 0.1 * torch.randn(cfg.E, device=dev, generator=g_ln)}

@@ -149,8 +149,11 @@ typedef struct fastvim_params {
  * post-SSM LayerNorm of VMamba, on the SSM output).  Per token, over its E
  * channels: y = s_fwd + s_bwd + (D_fwd + D_bwd) x,
  *   out = ((y - mean(y)) / sqrt(var(y) + ln_eps) * ln_weight + ln_bias) * silu(z)
- * with the population variance.  Layers with the norm run as stage kernels
- * (the single launch does not take it; FASTVIM_FLAG_FUSED is then ignored).
+ * with the population variance.  The single launch takes the norm for dense
+ * pooled layers with E / V <= 128 (V = 4 for fp32, 8 for bf16 elements per 16
+ * bytes): by default for COLS layers (the size rule above), with
+ * FASTVIM_FLAG_FUSED for ROWS too; other layers run the norm in their stage
+ * epilogue (FASTVIM_FLAG_FUSED then falls back to the stage kernels).
  * Errors: FASTVIM_ERR_NULL (ln_weight or ln_bias NULL), FASTVIM_ERR_ALIGN (not
  * 16-byte aligned), FASTVIM_ERR_ARG (ln_eps not > 0 or not finite). */
 #define FASTVIM_FLAG_POST_NORM 4u

@@ -373,9 +373,11 @@ int fastvim_ssm_fwd(const void* x, const void* z, const fastvim_params* params, 
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (launch_zero_sync(ws, sync_words(g), s) != hipSuccess) return FASTVIM_ERR_HIP;
     const fastvim_params q = effective_params(*params);
-    const bool single = !(params->flags & (FASTVIM_FLAG_POST_NORM | FASTVIM_FLAG_CONV | FASTVIM_FLAG_LOCAL_BWD)) &&
-                        ((params->flags & FASTVIM_FLAG_FUSED) ? fused_supported(g)
-                                                              : !(params->flags & FASTVIM_FLAG_STAGED) && fused_preferred(g));
+    const bool norm = (params->flags & FASTVIM_FLAG_POST_NORM) != 0;
+    const bool single = !(params->flags & (FASTVIM_FLAG_CONV | FASTVIM_FLAG_LOCAL_BWD)) &&
+                        ((params->flags & FASTVIM_FLAG_FUSED)
+                             ? fused_supported(g, norm)
+                             : !(params->flags & FASTVIM_FLAG_STAGED) && fused_preferred(g, norm));
     if (single)
         return launch_fused(g, x, z, *params, ws, out, s) == hipSuccess ? FASTVIM_OK : FASTVIM_ERR_HIP;
     for (int stage = FASTVIM_STAGE_ROWS; stage <= FASTVIM_STAGE_EPILOGUE; ++stage) {

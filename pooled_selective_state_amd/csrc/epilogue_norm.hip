@@ -1,68 +1,14 @@
-// Repeat + skip + post-SSM LayerNorm + gate: every output token written once,
-//   y   = s_fwd[b, t] + s_bwd[b, t] + (D_fwd + D_bwd) x[b, cell]
-//   out = ((y - mean(y)) / sqrt(var(y) + eps) * ln_weight + ln_bias) * silu(z[b, cell])
-// with mean and (population) variance over the token's E channels and t the
-// scan position of the cell (its row, its column, its raster position, or a
-// kept token's row).
-//
-// FastVim summary page (gptget.net, arXiv 2502.00594), section 方法详解,
-// bullet 5: the scan output is repeated, the skip connection added, then a
-// LayerNorm; Pith review of 2502.00594: the post-SSM LayerNorm taken from
-// VMamba, on the SSM output before the gate; Vim article (ijyty.com) 2.1:
-// the two directions summed and gated by z.
-//
-// The norm needs all E channels of a token at once, so a team of TL lanes
-// (16, 32 or 64; a DPP row, half a wave or a wave) owns one token: lane l of
-// the team holds the 16-byte vectors v = 0 .. nv-1 at channel (v TL + l) V,
-// so every vector step of the team reads TL consecutive vectors.  The team
-// sums over its lanes with DPP inside a row of 16 and shuffles across rows;
-// mean and variance take two passes over the registers (no cancellation).
-// x and z are read for the last time (non-temporal), out written once
-// (non-temporal); the scan rows and the per-channel vectors come through the
-// caches.
-#include "fastvim_internal.h"
+// Stage kernel of the epilogue with the post-SSM LayerNorm (the per-token
+// arithmetic, its sources and the team layout are in epilogue_norm.h): one
+// team of TL lanes per output token, t the scan position of the cell (its
+// row, its column, its raster position, or a kept token's row).
+#include "epilogue_norm.h"
 
 namespace fastvim {
 namespace {
 
 enum { kModeCols = 0, kModeRows = 1, kModeNoneRow = 2, kModeNoneCol = 3, kModeMasked = 4 };
 constexpr int kNormThreads = 256;
-
-__device__ __forceinline__ float silu(float q) { return q * __builtin_amdgcn_rcpf(1.f + __expf(-q)); }
-
-template <int CTRL>
-__device__ __forceinline__ float dpp(float v) {
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
-}
-
-// Sum over the TL lanes of a team; every lane of the team gets the total.
-template <int TL>
-__device__ __forceinline__ float team_sum(float v) {
-    v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]
-    v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]
-    v += dpp<0x124>(v);  // row_ror:4
-    v += dpp<0x128>(v);  // row_ror:8  -> sum over the row of 16
-    if (TL >= 32) v += __shfl_xor(v, 16);
-    if (TL >= 64) v += __shfl_xor(v, 32);
-    return v;
-}
-
-// V floats: 16-byte vector loads (16-byte aligned data: scan rows, norm
-// parameters) or plain loads (D, 4-byte aligned).
-template <class IO>
-__device__ __forceinline__ void load_f(const float* p, float (&v)[IO::V]) {
-#pragma unroll
-    for (int k = 0; k < IO::V; k += 4) {
-        const f32x4 t = *reinterpret_cast<const f32x4*>(p + k);
-        v[k] = t.x; v[k + 1] = t.y; v[k + 2] = t.z; v[k + 3] = t.w;
-    }
-}
-
-template <class IO>
-__device__ __forceinline__ void load_f_scalar(const float* p, float (&v)[IO::V]) {
-#pragma unroll
-    for (int k = 0; k < IO::V; ++k) v[k] = p[k];
-}
 
 template <class IO, int TL, int NV>
 __global__ void __launch_bounds__(kNormThreads)
@@ -71,7 +17,6 @@ epilogue_norm_kernel(const typename IO::elem* __restrict__ x, const typename IO:
                      const float* __restrict__ Db, const float* __restrict__ lnw, const float* __restrict__ lnb,
                      float eps, typename IO::elem* __restrict__ out, const int32_t* __restrict__ rows, int mode,
                      int64_t ntok, int64_t T, int64_t h, int64_t w, int64_t K, int E) {
-    constexpr int V = IO::V;
     using raw = typename IO::raw;
     constexpr int kTeams = kNormThreads / TL;
     const int lane = threadIdx.x % TL;
@@ -88,82 +33,14 @@ epilogue_norm_kernel(const typename IO::elem* __restrict__ x, const typename IO:
         const int64_t cell = tok - b * hw, i = cell / w, j = cell - i * w;
         t = mode == kModeCols ? i : mode == kModeRows ? j : mode == kModeNoneRow ? cell : j * h + i;
     }
-    const int nv = (E / V + TL - 1) / TL;  // vectors of this lane's team per token (<= NV)
     typename IO::elem* ob = out + tok * E;
     if (t < 0) {  // masked token with an invalid index
-#pragma unroll
-        for (int v = 0; v < NV; ++v) {
-            const int c = (v * TL + lane) * V;
-            if (v < nv && c < E) {
-                float o[V];
-#pragma unroll
-                for (int k = 0; k < V; ++k) o[k] = __builtin_nanf("");
-                store_vec<true>(ob + c, o);
-            }
-        }
+        norm_nan<IO, TL, NV>(ob, E, lane);
         return;
     }
-    const typename IO::elem* xb = x + tok * E;
-    const typename IO::elem* zb = z + tok * E;
-    const float* s1 = sf + (b * T + t) * E;
-    const float* s2 = sb + (b * T + t) * E;
     raw xr[NV], zr[NV];
-#pragma unroll
-    for (int v = 0; v < NV; ++v) {
-        const int c = (v * TL + lane) * V;
-        if (v < nv && c < E) {
-            xr[v] = load_raw<true>(xb + c);
-            zr[v] = load_raw<true>(zb + c);
-        }
-    }
-    float y[NV][V];
-    float sum = 0.f;
-#pragma unroll
-    for (int v = 0; v < NV; ++v) {
-        const int c = (v * TL + lane) * V;
-        if (v < nv && c < E) {
-            float a1[V], a2[V], d1[V], d2[V];
-            load_f<IO>(s1 + c, a1);
-            load_f<IO>(s2 + c, a2);
-            load_f_scalar<IO>(Df + c, d1);
-            load_f_scalar<IO>(Db + c, d2);
-#pragma unroll
-            for (int k = 0; k < V; ++k) {
-                y[v][k] = a1[k] + a2[k] + (d1[k] + d2[k]) * raw_at(xr[v], k);
-                sum += y[v][k];
-            }
-        } else {
-#pragma unroll
-            for (int k = 0; k < V; ++k) y[v][k] = 0.f;
-        }
-    }
-    const float inv_e = 1.f / (float)E;
-    const float mean = team_sum<TL>(sum) * inv_e;
-    float sq = 0.f;
-#pragma unroll
-    for (int v = 0; v < NV; ++v) {
-        const int c = (v * TL + lane) * V;
-        if (v < nv && c < E) {
-#pragma unroll
-            for (int k = 0; k < V; ++k) {
-                const float d = y[v][k] - mean;
-                sq = fmaf(d, d, sq);
-            }
-        }
-    }
-    const float r = __builtin_amdgcn_rsqf(team_sum<TL>(sq) * inv_e + eps);
-#pragma unroll
-    for (int v = 0; v < NV; ++v) {
-        const int c = (v * TL + lane) * V;
-        if (v < nv && c < E) {
-            float g[V], be[V], o[V];
-            load_f<IO>(lnw + c, g);
-            load_f<IO>(lnb + c, be);
-#pragma unroll
-            for (int k = 0; k < V; ++k) o[k] = ((y[v][k] - mean) * r * g[k] + be[k]) * silu(raw_at(zr[v], k));
-            store_vec<true>(ob + c, o);
-        }
-    }
+    norm_load<IO, TL, NV>(x + tok * E, z + tok * E, E, lane, xr, zr);
+    norm_finish<IO, TL, NV>(xr, zr, sf + (b * T + t) * E, sb + (b * T + t) * E, Df, Db, lnw, lnb, eps, ob, E, lane);
 }
 
 template <class IO, int TL, int NV>

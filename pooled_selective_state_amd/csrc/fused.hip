@@ -23,7 +23,9 @@
 //            in both directions (scan_core.h); count it in scanDone[b];
 //   E(b, k)  once scanDone[b] == nS, repeat + skip + gate a block of image
 //            b: grid rows [k*RE, k*RE + RE) (COLS), or RE rows x CJ columns
-//            with the block's scan rows staged in LDS (ROWS).
+//            with the block's scan rows staged in LDS (ROWS); with the
+//            post-SSM LayerNorm, grid rows [k*RE, k*RE + RE) in teams of
+//            lanes per token (epilogue_norm.h), both orientations.
 // Items are numbered slot by slot, slot s = [A(s, *)] [S(s - LS, *)]
 // [E(s - LE, *)] with 1 <= LS <= LE (items outside [0, B) are left out), and
 // handed out through one atomic ticket counter.  A workgroup takes its ticket
@@ -39,6 +41,7 @@
 // its XCD's L2) before reading with ordinary loads.
 #include <cstdlib>
 
+#include "epilogue_norm.h"
 #include "scan_core.h"
 
 namespace fastvim {
@@ -53,6 +56,8 @@ static_assert(sizeof(ScanSmem) == kLdsFloats * sizeof(float), "one buffer");
 constexpr unsigned kSpinLimit = 1u << 20;                   // about a second of polling
 constexpr int kEU = 4;                                       // tokens per lane per batch (E items)
 constexpr int kMaxIv = 6;
+constexpr int kNormTL = 64;  // norm E items: lanes per token (a wave) ...
+constexpr int kNormNV = 2;   // ... and vectors per lane: E / V <= 128
 
 struct FusedArgs {
     const void* x;
@@ -63,6 +68,9 @@ struct FusedArgs {
     float* xdbl;
     float* s_f;
     float* s_b;
+    const float* ln_w;  // post-SSM LayerNorm (NORM instances)
+    const float* ln_b;
+    float ln_eps;
     unsigned* sync;  // [0] ticket, [1] status, [2, 2+B) rowsDone, [2+B, 2+2B) scanDone
     int64_t B, h, w, E, T, P;
     int R, NX, axis;
@@ -368,8 +376,88 @@ __device__ void item_epilogue_rows(const FusedArgs& a, int64_t b, int k, float* 
     }
 }
 
+// Norm E items: grid rows [k*RE, k*RE + RE) of image b.  The per-channel
+// vectors (D_fwd + D_bwd, the norm's weight and bias) are staged in LDS once
+// per item and, for COLS, the summed scan row once per grid row; each team of
+// kNormTL lanes (a wave) then takes two tokens at a time and runs the
+// per-token norm epilogue, the next two tokens' x and z loads issued before
+// the current two are computed.  ROWS tokens read their scan rows through
+// the caches.
+template <class IO, bool COLS>
+__device__ void item_epilogue_norm(const FusedArgs& a, int64_t b, int k, float* lds) {
+    using raw = typename IO::raw;
+    using elem = typename IO::elem;
+    constexpr int kTeams = kFT / kNormTL;
+    const int tid = threadIdx.x;
+    if (tid == 0) wait_at_least(&a.sync[2 + a.B + b], (unsigned)a.nS, &a.sync[1]);
+    const int w = (int)a.w, E = (int)a.E;
+    float* ds = lds;              // [E] D_fwd + D_bwd
+    float* gw = lds + E;          // [E] norm weight
+    float* gb = lds + 2 * E;      // [E] norm bias
+    float* srow = lds + 3 * E;    // [E] COLS: s_fwd + s_bwd of the current grid row
+    for (int e = tid; e < E; e += kFT) {
+        ds[e] = a.pf.D[e] + a.pb.D[e];
+        gw[e] = a.ln_w[e];
+        gb[e] = a.ln_b[e];
+    }
+    __syncthreads();
+    const int lane = tid % kNormTL, team = tid / kNormTL;
+    const int64_t i0 = (int64_t)k * a.RE;
+    const int64_t i1 = i0 + a.RE < a.h ? i0 + a.RE : a.h;
+    const int64_t img = b * a.h * a.w;
+    const elem* x = static_cast<const elem*>(a.x);
+    const elem* z = static_cast<const elem*>(a.z);
+    elem* out = static_cast<elem*>(a.out);
+    for (int64_t i = i0; i < i1; ++i) {
+        if (COLS) {
+            __syncthreads();  // the previous row's tokens are done with srow
+            const float* s1 = a.s_f + (b * a.T + i) * E;
+            const float* s2 = a.s_b + (b * a.T + i) * E;
+            for (int e = tid; e < E; e += kFT) srow[e] = s1[e] + s2[e];
+            __syncthreads();
+        }
+        // the next pair's x and z are loaded before the current pair is computed
+        raw nx1[kNormNV], nz1[kNormNV], nx2[kNormNV], nz2[kNormNV];
+        auto load_pair = [&](int j) {
+            const int j2 = j + kTeams;
+            const int64_t c1 = img + i * w + j, c2 = img + i * w + (j2 < w ? j2 : j);
+            norm_load<IO, kNormTL, kNormNV>(x + c1 * E, z + c1 * E, E, lane, nx1, nz1);
+            if (j2 < w) norm_load<IO, kNormTL, kNormNV>(x + c2 * E, z + c2 * E, E, lane, nx2, nz2);
+        };
+        if (team < w) load_pair(team);
+        for (int j = team; j < w; j += 2 * kTeams) {
+            const int j2 = j + kTeams;
+            const bool two = j2 < w;
+            const int64_t c1 = img + i * w + j, c2 = img + i * w + (two ? j2 : j);
+            raw x1[kNormNV], z1[kNormNV], x2[kNormNV], z2[kNormNV];
+#pragma unroll
+            for (int v = 0; v < kNormNV; ++v) {
+                x1[v] = nx1[v];
+                z1[v] = nz1[v];
+                x2[v] = nx2[v];
+                z2[v] = nz2[v];
+            }
+            if (j + 2 * kTeams < w) load_pair(j + 2 * kTeams);
+            if (COLS) {
+                norm_finish<IO, kNormTL, kNormNV, true>(x1, z1, srow, nullptr, ds, nullptr, gw, gb, a.ln_eps,
+                                                        out + c1 * E, E, lane);
+                if (two)
+                    norm_finish<IO, kNormTL, kNormNV, true>(x2, z2, srow, nullptr, ds, nullptr, gw, gb, a.ln_eps,
+                                                            out + c2 * E, E, lane);
+            } else {
+                norm_finish<IO, kNormTL, kNormNV>(x1, z1, a.s_f + (b * a.T + j) * E, a.s_b + (b * a.T + j) * E,
+                                                  a.pf.D, a.pb.D, gw, gb, a.ln_eps, out + c1 * E, E, lane);
+                if (two)
+                    norm_finish<IO, kNormTL, kNormNV>(x2, z2, a.s_f + (b * a.T + j2) * E,
+                                                      a.s_b + (b * a.T + j2) * E, a.pf.D, a.pb.D, gw, gb, a.ln_eps,
+                                                      out + c2 * E, E, lane);
+            }
+        }
+    }
+}
+
 // ---------------------------------------------------------------- kernel
-template <class IO, bool COLS, int RMAX>
+template <class IO, bool COLS, int RMAX, bool NORM>
 __global__ void __launch_bounds__(kFT) fused_layer_kernel(FusedArgs a) {
     __shared__ FusedSmem sm;
     __shared__ unsigned s_ticket;
@@ -405,7 +493,8 @@ __global__ void __launch_bounds__(kFT) fused_layer_kernel(FusedArgs a) {
         }
         r -= a.nS;
     }
-    if (COLS) item_epilogue<IO, true>(a, slot - a.LE, (int)r);
+    if (NORM) item_epilogue_norm<IO, COLS>(a, slot - a.LE, (int)r, sm.buf);
+    else if (COLS) item_epilogue<IO, true>(a, slot - a.LE, (int)r);
     else item_epilogue_rows<IO>(a, slot - a.LE, (int)r, sm.buf);
 }
 
@@ -419,8 +508,9 @@ int env_int(const char* name, int dflt) {
     return s ? atoi(s) : dflt;
 }
 
-// Item sizes and ticket layout for a geometry; false if not covered.
-bool plan(const Geom& g, FusedArgs* a) {
+// Item sizes and ticket layout for a geometry; false if not covered.  norm:
+// with the post-SSM LayerNorm (E items of whole grid rows, E / V <= 128).
+bool plan(const Geom& g, FusedArgs* a, bool norm) {
     if (!g.pooled || g.masked || g.B < 1) return false;
     // the scan items hold a whole sequence's x_proj rows in LDS
     const int64_t tmax = g.R <= 16 ? resident_tmax<16>() : g.R <= 32 ? resident_tmax<32>() : resident_tmax<64>();
@@ -430,6 +520,7 @@ bool plan(const Geom& g, FusedArgs* a) {
     const int64_t esz = g.io == FASTVIM_BF16 ? 2 : 4;
     const int64_t VE = g.E / V;
     if (VE > kFT) return false;
+    if (norm && VE > kNormTL * kNormNV) return false;
     const int G = (int)(kFT / VE);
     const int64_t NO = 2 * g.NX;
     int KS = (int)(kFT / NO);
@@ -444,7 +535,7 @@ bool plan(const Geom& g, FusedArgs* a) {
     // E items: about 200 KB of each stream.  COLS: RE whole grid rows.  ROWS:
     // RE rows x CJ columns, CJ as many columns as the LDS holds scan rows of.
     int64_t RE, CJ;
-    if (g.axis == FASTVIM_POOL_COLS) {
+    if (g.axis == FASTVIM_POOL_COLS || norm) {
         const int64_t row_bytes = g.w * g.E * esz;
         RE = (200 * 1024) / row_bytes;
         CJ = g.w;
@@ -504,13 +595,19 @@ bool plan(const Geom& g, FusedArgs* a) {
     return a->niv > 0 && a->total < (int64_t)UINT32_MAX;
 }
 
+template <class IO, int RMAX, bool NORM>
+hipError_t fused_launch_n(const FusedArgs& a, hipStream_t st) {
+    if (a.axis == FASTVIM_POOL_COLS)
+        hipLaunchKernelGGL((fused_layer_kernel<IO, true, RMAX, NORM>), dim3((unsigned)a.total), dim3(kFT), 0, st, a);
+    else
+        hipLaunchKernelGGL((fused_layer_kernel<IO, false, RMAX, NORM>), dim3((unsigned)a.total), dim3(kFT), 0, st,
+                           a);
+    return hipGetLastError();
+}
+
 template <class IO, int RMAX>
 hipError_t fused_launch_r(const FusedArgs& a, hipStream_t st) {
-    if (a.axis == FASTVIM_POOL_COLS)
-        hipLaunchKernelGGL((fused_layer_kernel<IO, true, RMAX>), dim3((unsigned)a.total), dim3(kFT), 0, st, a);
-    else
-        hipLaunchKernelGGL((fused_layer_kernel<IO, false, RMAX>), dim3((unsigned)a.total), dim3(kFT), 0, st, a);
-    return hipGetLastError();
+    return a.ln_w ? fused_launch_n<IO, RMAX, true>(a, st) : fused_launch_n<IO, RMAX, false>(a, st);
 }
 
 template <class IO>
@@ -522,18 +619,22 @@ hipError_t fused_launch_io(const FusedArgs& a, hipStream_t st) {
 
 }  // namespace
 
-bool fused_supported(const Geom& g) {
+bool fused_supported(const Geom& g, bool norm) {
     FusedArgs a;
-    return plan(g, &a);
+    return plan(g, &a, norm);
 }
 
-bool fused_preferred(const Geom& g) {
+bool fused_preferred(const Geom& g, bool norm) {
     // The pipeline's fixed costs (scan latency per image, fill and drain)
     // pay off once an image's x is several MB: measured faster than the stage
     // kernels at 2048^2 (25 MB fp32, 12.6 MB bf16), slower at 1024^2 (6.3 MB)
     // and below.
+    // With the norm, ROWS reads each token's scan rows through the caches and
+    // measured slower than its stage kernels; COLS (a scan row per grid row,
+    // staged in LDS) is faster.
     const int64_t esz = g.io == FASTVIM_BF16 ? 2 : 4;
-    return g.h * g.w * g.E * esz >= (8ll << 20) && fused_supported(g);
+    if (norm && g.axis != FASTVIM_POOL_COLS) return false;
+    return g.h * g.w * g.E * esz >= (8ll << 20) && fused_supported(g, norm);
 }
 
 hipError_t launch_zero_sync(const Workspace& ws, int64_t n, hipStream_t st) {
@@ -544,9 +645,13 @@ hipError_t launch_zero_sync(const Workspace& ws, int64_t n, hipStream_t st) {
 hipError_t launch_fused(const Geom& g, const void* x, const void* z, const fastvim_params& p, const Workspace& ws,
                         void* out, hipStream_t st) {
     FusedArgs a;
-    if (!plan(g, &a)) return hipErrorInvalidValue;
+    const bool norm = (p.flags & FASTVIM_FLAG_POST_NORM) != 0;
+    if (!plan(g, &a, norm)) return hipErrorInvalidValue;
     a.x = x; a.z = z; a.out = out;
     a.pf = p.fwd; a.pb = p.bwd;
+    a.ln_w = norm ? p.ln_weight : nullptr;
+    a.ln_b = norm ? p.ln_bias : nullptr;
+    a.ln_eps = norm ? p.ln_eps : 0.f;
     a.u = ws.u; a.xdbl = ws.xdbl; a.s_f = ws.s_f; a.s_b = ws.s_b;
     a.sync = ws.sync;
     return g.io == FASTVIM_BF16 ? fused_launch_io<IoBf16>(a, st) : fused_launch_io<IoF32>(a, st);

@@ -182,22 +182,26 @@ def test_projection_many_tokens(R, axis):
 
 
 # ------------------------------------------------------------ post-SSM LayerNorm
+@pytest.mark.parametrize("path", list(PATHS))
 @pytest.mark.parametrize("axis", AXES)
 @pytest.mark.parametrize("io", ["f32", "bf16"])
-def test_post_norm_tiny(axis, io):
-    """The post-SSM LayerNorm before the gate, every pooling axis."""
+def test_post_norm_tiny(axis, io, path):
+    """The post-SSM LayerNorm before the gate, every pooling axis, both paths
+    of a dense pooled layer (the single launch takes the norm for E / V <= 128)."""
     wl = draw_workload(C.TINY)
     x, z = wl["x"], wl["z"][0]
     if io == "bf16":
         x, z = round_to_bf16(x), round_to_bf16(z)
     ln = rand_ln(np.random.default_rng(70 + axis), C.TINY.E)
     _layer_check(x, z, wl["params"][0], axis, FP32_TOL if io == "f32" else BF16_TOL,
-                 torch.float32 if io == "f32" else torch.bfloat16, "norm tiny %d %s" % (axis, io), ln=ln)
+                 torch.float32 if io == "f32" else torch.bfloat16, "norm tiny %d %s %s" % (axis, io, path), ln=ln,
+                 flags=PATHS[path])
 
 
+@pytest.mark.parametrize("path", list(PATHS))
 @pytest.mark.parametrize("E", [8, 72, 520, 1032, 2056, 4096])
 @pytest.mark.parametrize("io", ["f32", "bf16"])
-def test_post_norm_widths(E, io):
+def test_post_norm_widths(E, io, path):
     """Every lane-team size of the normalising epilogue (16, 32 or 64 lanes per
     token, up to 16 vectors per lane) and widths that leave part of the team
     idle, on a ragged grid."""
@@ -212,7 +216,8 @@ def test_post_norm_widths(E, io):
     prm = {d: rand_dir(rng, E, N, R, scale=0.05) for d in ("fwd", "bwd")}
     ln = rand_ln(rng, E, eps=1e-5)
     _layer_check(x, z, prm, P.POOL_ROWS, FP32_TOL if io == "f32" else BF16_TOL,
-                 torch.float32 if io == "f32" else torch.bfloat16, "norm E=%d %s" % (E, io), ln=ln)
+                 torch.float32 if io == "f32" else torch.bfloat16, "norm E=%d %s %s" % (E, io, path), ln=ln,
+                 flags=PATHS[path])
 
 
 def test_post_norm_masked_with_invalid_index():
@@ -236,12 +241,14 @@ def test_post_norm_masked_with_invalid_index():
     assert np.isfinite(out[~nan_tok]).all()
 
 
-def test_post_norm_full_size_2048():
-    """The 2048^2 layer with the norm (stage kernels), sampled images."""
+@pytest.mark.parametrize("axis", (P.POOL_COLS, P.POOL_ROWS))
+@pytest.mark.parametrize("path", list(PATHS))
+def test_post_norm_full_size_2048(path, axis):
+    """The 2048^2 layer with the norm, both paths and axes, sampled images."""
     wl = _workload(C.HIRES_2048)
     ln = rand_ln(np.random.default_rng(95), C.HIRES_2048.E)
-    _layer_check(wl["x"], wl["z"][0], wl["params"][0], P.POOL_COLS, FP32_TOL, torch.float32, "norm 2048",
-                 sel=_sample(C.HIRES_2048.B), ln=ln)
+    _layer_check(wl["x"], wl["z"][0], wl["params"][0], axis, FP32_TOL, torch.float32,
+                 "norm 2048 %s axis %d" % (path, axis), sel=_sample(C.HIRES_2048.B), ln=ln, flags=PATHS[path])
 
 
 def test_masked_integer_sums_exact():
