@@ -27,7 +27,8 @@ Reported besides images/s:
                 bidirectional one, the 1024^2 two-block chain, and the small
                 workloads over rotating input sets.
 --profile-run times a few steps and the calibration copy only (for profiler
-runs); --profile-bwd adds three backward calls of the same workload.
+runs); --profile-bwd adds three backward calls of the same workload, then
+three more given the pooled tokens a forward call saved.
 """
 from __future__ import annotations
 
@@ -256,11 +257,15 @@ def main():
     log("calibration copy %.4f ms (%.0f GB/s)" % (cp_ms, result["copy_ceiling"]["GBps"]))
     if args.profile_bwd:
         dout = torch.randn(x.shape, device=dev, generator=torch.Generator(device="cuda").manual_seed(2))
-        bcall = P.BwdCall(x, z, dout, prm, P.POOL_COLS)
-        for _ in range(3):
-            bcall.run(stream)
-        torch.cuda.synchronize()
-        del bcall, dout
+        su = torch.empty((cfg.B, cfg.h, cfg.E), device=dev)
+        P.SSMCall(x, z, prm, P.POOL_COLS, workspace=call.workspace, out=call.out, saved_u=su).run(stream)
+        for kept in (None, su):
+            bcall = P.BwdCall(x, z, dout, prm, P.POOL_COLS, saved_u=kept)
+            for _ in range(3):
+                bcall.run(stream)
+            torch.cuda.synchronize()
+            del bcall
+        del dout, su
 
     if not args.no_extras:
         extras = {}
@@ -312,17 +317,25 @@ def main():
         g_b = torch.Generator(device="cuda").manual_seed(2)
         dout = torch.randn(x.shape, device=dev, generator=g_b)
         bwd_bytes = 5 * 4 * elems  # x, z, dout read once, dx, dz written once (fp32)
-        extras["backward_2048"] = {"alg_bytes": bwd_bytes, "path": "stage kernels, two full-resolution passes"}
+        extras["backward_2048"] = {"alg_bytes": bwd_bytes, "path": "stage kernels, two full-resolution passes",
+                                   "saved_u": "pooled tokens kept from the forward call (pass 1 reads z and dout "
+                                              "only); pools_x: the backward pools x again"}
         for name, axis in (("cols", P.POOL_COLS), ("rows", P.POOL_ROWS)):
-            bcall = P.BwdCall(x, z, dout, prm, axis)
-            bcall.run(stream)
-            b_ms, _ = time_steps(lambda: bcall.run(stream), n, stream)
-            extras["backward_2048"][name] = {"ms": b_ms, "images_per_s": cfg.B / (b_ms * 1e-3),
-                                             "GBps": bwd_bytes / (b_ms * 1e-3) / 1e9,
-                                             "hbm_frac": bwd_bytes / (b_ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
-            del bcall
+            su = torch.empty((cfg.B, cfg.h if axis == P.POOL_COLS else cfg.w, cfg.E), device=dev)
+            P.SSMCall(x, z, prm, axis, workspace=call.workspace, out=call.out, saved_u=su).run(stream)
+            res = {}
+            for kind, kept in (("pools_x", None), ("saved_u", su)):
+                bcall = P.BwdCall(x, z, dout, prm, axis, saved_u=kept)
+                bcall.run(stream)
+                b_ms, _ = time_steps(lambda: bcall.run(stream), n, stream)
+                res[kind] = {"ms": b_ms, "images_per_s": cfg.B / (b_ms * 1e-3),
+                             "GBps": bwd_bytes / (b_ms * 1e-3) / 1e9,
+                             "hbm_frac": bwd_bytes / (b_ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+                del bcall
+            extras["backward_2048"][name] = res
+            del su
         del dout
-        log("backward %.3f ms (cols)" % extras["backward_2048"]["cols"]["ms"])
+        log("backward %.3f ms (cols, saved u)" % extras["backward_2048"]["cols"]["saved_u"]["ms"])
         # torch's device copy, for comparison with the calibration copy
         dst = torch.empty_like(x)
         tc_ms, _ = time_steps(lambda: dst.copy_(x), 3, stream)

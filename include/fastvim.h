@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define FASTVIM_ABI_VERSION 6
+#define FASTVIM_ABI_VERSION 7
 
 typedef enum fastvim_status {
     FASTVIM_OK = 0,
@@ -126,6 +126,17 @@ typedef struct fastvim_params {
      * (E) fp32. */
     const float *conv_w;
     const float *conv_b;
+    /* Pooled tokens kept from the forward call for the backward call (as
+     * training keeps a layer's activations), or NULL: pooled layers only,
+     * (B, T, E) fp32, 16-byte aligned.  fastvim_ssm_fwd (and its stages) then
+     * writes the pooled tokens u here instead of into the workspace, and
+     * fastvim_ssm_bwd reads them from here instead of pooling x again, so its
+     * first pass reads z and dout only.  The caller keeps the buffer between
+     * the two calls and passes the same x, mask and pool axis to both; the
+     * library does not check that the contents match.  Errors: FASTVIM_ERR_ARG
+     * (unpooled layer), FASTVIM_ERR_ALIGN, FASTVIM_ERR_OVERLAP (it overlaps
+     * an input, an output or the workspace). */
+    float *saved_u;
 } fastvim_params;
 
 /* params.flags bits.  By default a dense pooled layer (COLS or ROWS, no mask)
@@ -225,7 +236,7 @@ int fastvim_ssm_stage(int stage, const void *x, const void *z, const fastvim_par
 
 /* Copy one intermediate result of the last call that used this workspace into
  * dst (device memory, dst_bytes large enough), enqueued on stream:
- *   U           (B, T, E)        fp32 pooled tokens (pooled layers only)
+ *   U           (B, T, E)        fp32 pooled tokens (pooled layers only; from saved_u when given)
  *   XDBL        (B, T, 2, R+2N)  fp32 x_proj outputs, [.., 0, :] fwd, [.., 1, :] bwd
  *   S_FWD/S_BWD (B, T, E)        fp32 scan outputs of each direction
  *   ROWS        (B, K)           int32 row (COLS) or column (ROWS) of each kept token, -1 if invalid
@@ -266,8 +277,12 @@ size_t fastvim_ssm_export_bytes(const fastvim_dims *dims, int pool_axis, int wha
  *   dD_fwd = dD_bwd = sum over all cells of g * x
  *   dx    = g * (D_fwd + D_bwd) + du[b, t(cell), :] / P   (the pool's adjoint)
  * The forward pass is recomputed inside the call (pooled tokens, projections,
- * states), so only x, z and dout are needed.  Arithmetic is fp32; every sum
- * has a fixed order (no atomics), so results are run-to-run identical.
+ * states), so only x, z and dout are needed; with params->saved_u the pooled
+ * tokens come from the forward call instead.  Two passes stream the grid: the
+ * first reads x (unless saved_u is given), z and dout and pools u and gs; the
+ * second reads x, z and dout again, writes dx and dz and sums dD.  Arithmetic
+ * is fp32; every sum has a fixed order (no atomics), so results are
+ * run-to-run identical.
  *
  * Supported: pooled layers (COLS or ROWS, dense or masked) with T <= 128 scan
  * steps and the limits of the forward call; FASTVIM_ERR_UNSUPPORTED for

@@ -65,7 +65,8 @@ class Params(ctypes.Structure):
     _fields_ = [("fwd", DirParams), ("bwd", DirParams), ("workspace", ctypes.c_void_p),
                 ("workspace_bytes", ctypes.c_size_t), ("flags", ctypes.c_uint32), ("reserved", ctypes.c_uint32),
                 ("ln_weight", ctypes.c_void_p), ("ln_bias", ctypes.c_void_p), ("ln_eps", ctypes.c_float),
-                ("reserved2", ctypes.c_uint32), ("conv_w", ctypes.c_void_p), ("conv_b", ctypes.c_void_p)]
+                ("reserved2", ctypes.c_uint32), ("conv_w", ctypes.c_void_p), ("conv_b", ctypes.c_void_p),
+                ("saved_u", ctypes.c_void_p)]
 
 
 class DirGrads(ctypes.Structure):
@@ -194,6 +195,11 @@ def _dir_params(params, keep):
     return dirs
 
 
+def _check_saved_u(t: Optional[torch.Tensor]) -> None:
+    if t is not None and (t.dtype != torch.float32 or not t.is_contiguous()):
+        raise ValueError("saved_u must be a contiguous float32 tensor (B, T, E)")
+
+
 class SSMCall:
     """One prepared layer call: sizes, parameter pointers, workspace and out.
 
@@ -203,13 +209,15 @@ class SSMCall:
     A_log (E, N), D (E).  ln = {"weight": (E,), "bias": (E,), "eps": float}
     (fp32 device tensors) adds the post-SSM LayerNorm before the gate.
     conv = {"weight": (E, 4), "bias": (E,)} (fp32 device tensors) makes x the
-    input of the producer Conv1D + SiLU, computed inside the layer."""
+    input of the producer Conv1D + SiLU, computed inside the layer.
+    saved_u (B, T, E) fp32 (pooled layers) receives the pooled tokens, for a
+    later backward call given the same tensor."""
 
     def __init__(self, x: torch.Tensor, z: torch.Tensor, params: Dict[str, Dict[str, torch.Tensor]],
                  pool_axis: int, mask_idx: Optional[torch.Tensor] = None, hw: Optional[Tuple[int, int]] = None,
                  out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
                  flags: int = 0, ln: Optional[Dict[str, object]] = None,
-                 conv: Optional[Dict[str, torch.Tensor]] = None):
+                 conv: Optional[Dict[str, torch.Tensor]] = None, saved_u: Optional[torch.Tensor] = None):
         self.dims = _layer_dims(x, z, params, mask_idx, hw)
         self.pool_axis = pool_axis
         self.x, self.z, self.mask_idx = x, z, mask_idx
@@ -237,8 +245,11 @@ class SSMCall:
                     raise ValueError("Conv1D weight and bias must be contiguous float32")
             self._keep.extend([conv_w, conv_b])
             flags |= FLAG_CONV
+        _check_saved_u(saved_u)
+        self.saved_u = saved_u
         self.params = Params(dirs[0], dirs[1], workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-                             flags, 0, _ptr(ln_w), _ptr(ln_b), ln_eps, 0, _ptr(conv_w), _ptr(conv_b))
+                             flags, 0, _ptr(ln_w), _ptr(ln_b), ln_eps, 0, _ptr(conv_w), _ptr(conv_b),
+                             _ptr(saved_u))
 
     def _args(self):
         return (_ptr(self.x), _ptr(self.z), ctypes.byref(self.params), ctypes.byref(self.dims), self.pool_axis,
@@ -274,10 +285,10 @@ class SSMCall:
 
 
 def ssm_fwd(x, z, params, pool_axis=POOL_COLS, mask_idx=None, hw=None, out=None, workspace=None, stream=None,
-            flags=0, ln=None, conv=None):
+            flags=0, ln=None, conv=None, saved_u=None):
     """The pooled bidirectional selective-scan layer; returns out."""
     return SSMCall(x, z, params, pool_axis, mask_idx=mask_idx, hw=hw, out=out, workspace=workspace,
-                   flags=flags, ln=ln, conv=conv).run(stream)
+                   flags=flags, ln=ln, conv=conv, saved_u=saved_u).run(stream)
 
 
 class BwdCall:
@@ -285,15 +296,17 @@ class BwdCall:
 
     Arguments as SSMCall, plus dout shaped like x.  dx, dz (like x) and the
     gradients grads = {"fwd": {...}, "bwd": {...}} (fp32, shaped like the
-    parameters) are allocated unless given.  run() returns
-    {"dx": dx, "dz": dz, "fwd": {...}, "bwd": {...}}."""
+    parameters) are allocated unless given.  saved_u: the pooled tokens a
+    forward call with the same x wrote (then x is read once, not twice).
+    run() returns {"dx": dx, "dz": dz, "fwd": {...}, "bwd": {...}}."""
 
     def __init__(self, x: torch.Tensor, z: torch.Tensor, dout: torch.Tensor,
                  params: Dict[str, Dict[str, torch.Tensor]], pool_axis: int,
                  mask_idx: Optional[torch.Tensor] = None, hw: Optional[Tuple[int, int]] = None,
                  dx: Optional[torch.Tensor] = None, dz: Optional[torch.Tensor] = None,
                  grads: Optional[Dict[str, Dict[str, torch.Tensor]]] = None,
-                 workspace: Optional[torch.Tensor] = None, flags: int = 0):
+                 workspace: Optional[torch.Tensor] = None, flags: int = 0,
+                 saved_u: Optional[torch.Tensor] = None):
         self.dims = _layer_dims(x, z, params, mask_idx, hw)
         if dout.dtype != x.dtype or dout.shape != x.shape:
             raise ValueError("dout must match x in shape and dtype")
@@ -318,8 +331,10 @@ class BwdCall:
         if workspace is None:
             workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=x.device)
         self.workspace = workspace
+        _check_saved_u(saved_u)
+        self.saved_u = saved_u
         self.params = Params(dirs[0], dirs[1], workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-                             flags, 0, None, None, 0.0, 0)
+                             flags, 0, None, None, 0.0, 0, None, None, _ptr(saved_u))
 
     def run(self, stream=None) -> Dict[str, object]:
         st = lib().fastvim_ssm_bwd(_ptr(self.x), _ptr(self.z), _ptr(self.dout), ctypes.byref(self.params),
@@ -331,10 +346,10 @@ class BwdCall:
 
 
 def ssm_bwd(x, z, dout, params, pool_axis=POOL_COLS, mask_idx=None, hw=None, workspace=None, stream=None,
-            flags=0):
+            flags=0, saved_u=None):
     """Gradients of the layer; returns {"dx", "dz", "fwd": {...}, "bwd": {...}}."""
     return BwdCall(x, z, dout, params, pool_axis, mask_idx=mask_idx, hw=hw, workspace=workspace,
-                   flags=flags).run(stream)
+                   flags=flags, saved_u=saved_u).run(stream)
 
 
 def calib_copy(dst: torch.Tensor, src: torch.Tensor, stream=None) -> None:

@@ -97,6 +97,7 @@ int validate(const void* x, const void* z, const fastvim_params* prm, const fast
         (!g->pooled || g->masked || (prm->flags & FASTVIM_FLAG_POST_NORM)))
         return FASTVIM_ERR_UNSUPPORTED;
     if (!g->masked && idx) return FASTVIM_ERR_ARG;
+    if (prm->saved_u && !g->pooled) return FASTVIM_ERR_ARG;
     *empty = g->B == 0;
     if (*empty) return FASTVIM_OK;
     if (!x || !z || !out || (g->masked && !idx)) return FASTVIM_ERR_NULL;
@@ -123,7 +124,16 @@ int validate(const void* x, const void* z, const fastvim_params* prm, const fast
     const void* w = prm->workspace;
     if (overlap(w, need, x, io_bytes) || overlap(w, need, z, io_bytes) || overlap(w, need, out, io_bytes))
         return FASTVIM_ERR_OVERLAP;
+    if (prm->saved_u) {
+        const void* su = prm->saved_u;
+        const size_t ub = (size_t)(g->B * g->T * g->E) * sizeof(float);
+        if (!aligned(su, 16)) return FASTVIM_ERR_ALIGN;
+        if (overlap(su, ub, x, io_bytes) || overlap(su, ub, z, io_bytes) || overlap(su, ub, out, io_bytes) ||
+            overlap(su, ub, w, need))
+            return FASTVIM_ERR_OVERLAP;
+    }
     workspace_layout(*g, prm->workspace, ws);
+    if (prm->saved_u) ws->u = prm->saved_u;
     return FASTVIM_OK;
 }
 
@@ -214,21 +224,27 @@ int validate_bwd(const void* x, const void* z, const void* dout, const fastvim_p
     const size_t io = (size_t)(g->B * (g->masked ? g->K : g->h * g->w) * g->E) * (g->io == FASTVIM_F32 ? 4 : 2);
     // outputs (dx, dz, the workspace and every gradient) overlap neither each
     // other nor an input; parameters count as inputs
-    Span ins[13] = {{x, io}, {z, io}, {dout, io}};
+    Span ins[14] = {{x, io}, {z, io}, {dout, io}};
     int nin = 3;
     for (const fastvim_dir_params* pd : {&prm->fwd, &prm->bwd}) {
         const float* ps[5] = {pd->x_proj_w, pd->dt_proj_w, pd->dt_proj_b, pd->A_log, pd->D};
         for (int i = 0; i < 5; ++i) ins[nin++] = Span{ps[i], gsz[i] * sizeof(float)};
     }
+    if (prm->saved_u && !aligned(prm->saved_u, 16)) return FASTVIM_ERR_ALIGN;
+    ins[nin++] = Span{prm->saved_u, prm->saved_u ? (size_t)(g->B * g->T * g->E) * sizeof(float) : 0};
     Span outs[13] = {{dx, io}, {dz, io}, {prm->workspace, need}};
     for (int i = 0; i < 10; ++i) outs[3 + i] = gs[i];
     for (int i = 0; i < 13; ++i) {
-        for (int j = 0; j < 13; ++j)
+        for (int j = 0; j < nin; ++j)
             if (overlap(outs[i].p, outs[i].n, ins[j].p, ins[j].n)) return FASTVIM_ERR_OVERLAP;
         for (int j = i + 1; j < 13; ++j)
             if (overlap(outs[i].p, outs[i].n, outs[j].p, outs[j].n)) return FASTVIM_ERR_OVERLAP;
     }
     bwd_workspace_layout(*g, prm->workspace, ws);
+    if (prm->saved_u) {
+        ws->fwd.u = prm->saved_u;
+        ws->u_saved = true;
+    }
     return FASTVIM_OK;
 }
 
@@ -256,8 +272,8 @@ int run_bwd(const Geom& g, const void* x, const void* z, const void* dout, const
             !ok(launch_colsum(ws.dbp + d * B * E, B, E, E, gd[d]->dt_proj_b, nullptr, ws.tmp, s)))
             return FASTVIM_ERR_HIP;
     }
-    if (!ok(launch_colsum(ws.dDp, B * g.T, E, E, gr.fwd.D, gr.bwd.D, ws.tmp, s))) return FASTVIM_ERR_HIP;
     if (!ok(launch_bwd_epilogue(g, x, z, dout, p, ws, dx, dz, s))) return FASTVIM_ERR_HIP;
+    if (!ok(launch_colsum(ws.dDp, bwd_dd_parts(g), E, E, gr.fwd.D, gr.bwd.D, ws.tmp, s))) return FASTVIM_ERR_HIP;
     return FASTVIM_OK;
 }
 
@@ -307,7 +323,9 @@ size_t bwd_workspace_layout(const Geom& g, void* base, BwdWorkspace* ws) {
     const size_t o_sf = take(bte), o_sb = take(bte);
     const size_t o_rows = g.masked ? take((size_t)(B * g.K) * sizeof(int32_t)) : 0;
     const size_t o_bad = g.masked ? take((size_t)B * sizeof(int32_t)) : 0;
-    const size_t o_gs = take(bte), o_dDp = take(bte), o_duf = take(bte), o_dub = take(bte), o_du = take(bte);
+    const int64_t ND = bwd_dd_parts(g);
+    const size_t o_gs = take(bte), o_dDp = take((size_t)(ND * E) * sizeof(float));
+    const size_t o_duf = take(bte), o_dub = take(bte), o_du = take(bte);
     const size_t o_dvp = take((size_t)(2 * B * G * T * S) * sizeof(float));
     const size_t o_dv = take((size_t)(M * 2 * NX) * sizeof(float));
     const size_t o_dAp = take((size_t)(2 * B * E * 16) * sizeof(float));
@@ -318,7 +336,7 @@ size_t bwd_workspace_layout(const Geom& g, void* base, BwdWorkspace* ws) {
         return rows > kColRowsPerBlock ? (rows + kColRowsPerBlock - 1) / kColRowsPerBlock * cols : int64_t(0);
     };
     int64_t tmpf = 1;
-    for (int64_t v : {stage1(M, E), stage1(B, E * 16), stage1(B, E * R), stage1(B, E), stage1(MC, NX * E)})
+    for (int64_t v : {stage1(ND, E), stage1(B, E * 16), stage1(B, E * R), stage1(B, E), stage1(MC, NX * E)})
         tmpf = v > tmpf ? v : tmpf;
     const size_t o_tmp = take((size_t)tmpf * sizeof(float));
     if (base && ws) {
@@ -347,6 +365,7 @@ size_t bwd_workspace_layout(const Geom& g, void* base, BwdWorkspace* ws) {
         ws->S = S;
         ws->MC = MC;
         ws->tmp_floats = tmpf;
+        ws->u_saved = false;
     }
     return off;
 }
@@ -420,7 +439,7 @@ int fastvim_ssm_export(const fastvim_params* params, const fastvim_dims* dims, i
     workspace_layout(g, params->workspace, &ws);
     const void* src = nullptr;
     switch (what) {
-        case FASTVIM_EXPORT_U: src = ws.u; break;
+        case FASTVIM_EXPORT_U: src = params->saved_u ? params->saved_u : ws.u; break;
         case FASTVIM_EXPORT_XDBL: src = ws.xdbl; break;
         case FASTVIM_EXPORT_S_FWD: src = ws.s_f; break;
         case FASTVIM_EXPORT_S_BWD: src = ws.s_b; break;

@@ -15,17 +15,19 @@
 // both directions and the x_proj adjoint du += x_proj_w^T dv.
 //
 // Kernels here, in launch order:
-//   pass 1   (x, z, dout read once)  pooled tokens u (the scan input, which
-//            the backward recomputes), gs and per-row partials of dD;
+//   pass 1   (z and dout read once, and x unless the caller saved the pooled
+//            tokens u from the forward call) gs, and u (the scan input,
+//            which the backward otherwise recomputes);
 //   dv       dL/dv from the scan adjoint's channel-group partials;
 //   du       du = du_fwd + du_bwd + x_proj_w^T dv for both directions;
 //   dwx      per-chunk partials of d x_proj_w = sum_m dv[m] u[m]^T;
-//   colsum   fixed-order column sums: parameter gradients from per-image or
-//            per-chunk partials;
-//   pass 2   (x, z, dout read again, dx and dz written once).
+//   pass 2   (x, z, dout read again) dx and dz written once, and per-workgroup
+//            partials of dD;
+//   colsum   fixed-order column sums: parameter gradients from per-image,
+//            per-chunk or per-workgroup partials.
 // Passes 1 and 2 move the full-resolution tensors and bound the pass; both
-// stream 16-byte vectors with every load issued before any arithmetic, like
-// the forward pool and epilogue kernels.
+// stream 16-byte vectors with every load of a batch issued before any
+// arithmetic, like the forward pool and epilogue kernels.
 #include "bwd_internal.h"
 
 namespace fastvim {
@@ -37,26 +39,27 @@ __device__ __forceinline__ float sigmoid_f(float q) { return __builtin_amdgcn_rc
 // One workgroup per pooled token (b, t): G groups of VE vector lanes, lane c
 // owning the 16-byte column [c V, c V + V) of E, group g taking the pooled
 // positions p = g, g + G, ...; the G partial sums are added through LDS in a
-// fixed order.
-template <class IO>
+// fixed order.  POOL: also pool x into u (else u is the caller's saved copy
+// and x is not read here).
+template <class IO, bool POOL>
 __global__ void __launch_bounds__(1024)
 bwd_pool_dense_kernel(const typename IO::elem* __restrict__ x, const typename IO::elem* __restrict__ z,
                       const typename IO::elem* __restrict__ dout, float* __restrict__ u, float* __restrict__ gs,
-                      float* __restrict__ dDp, int64_t T, int64_t P, int VE, int G, int64_t E, int64_t img_stride,
-                      int64_t t_stride, int64_t p_stride, float inv_p) {
+                      int64_t T, int64_t P, int VE, int G, int64_t E, int64_t img_stride, int64_t t_stride,
+                      int64_t p_stride, float inv_p) {
     constexpr int V = IO::V;
-    constexpr int kD = 4;  // pooled positions in flight per lane
+    constexpr int kD = POOL ? 4 : 6;  // pooled positions in flight per lane (12 loads either way)
     using raw = typename IO::raw;
-    extern __shared__ float red[];  // [3][G][VE * V]
+    extern __shared__ float red[];  // [POOL ? 2 : 1][G][VE * V]
     const int64_t bt = blockIdx.x;
     const int64_t b = bt / T, t = bt - b * T;
     const int tid = threadIdx.x;
     const int c = tid % VE, g = tid / VE;
     const int width = VE * V;
     if (g < G) {
-        float au[V], ag[V], ad[V];
+        float au[V], ag[V];
 #pragma unroll
-        for (int k = 0; k < V; ++k) au[k] = ag[k] = ad[k] = 0.f;
+        for (int k = 0; k < V; ++k) au[k] = ag[k] = 0.f;
         const int64_t off = b * img_stride + t * t_stride + (int64_t)c * V;
         for (int64_t p0 = g; p0 < P; p0 += kD * G) {
             raw xr[kD], zr[kD], dr[kD];
@@ -65,7 +68,7 @@ bwd_pool_dense_kernel(const typename IO::elem* __restrict__ x, const typename IO
                 const int64_t p = p0 + (int64_t)i * G;
                 if (p < P) {
                     const int64_t o = off + p * p_stride;
-                    xr[i] = load_raw<false>(x + o);
+                    if (POOL) xr[i] = load_raw<false>(x + o);
                     zr[i] = load_raw<false>(z + o);
                     dr[i] = load_raw<false>(dout + o);
                 }
@@ -75,11 +78,9 @@ bwd_pool_dense_kernel(const typename IO::elem* __restrict__ x, const typename IO
                 if (p0 + (int64_t)i * G < P) {
 #pragma unroll
                     for (int k = 0; k < V; ++k) {
-                        const float xv = raw_at(xr[i], k), zv = raw_at(zr[i], k);
-                        const float gv = raw_at(dr[i], k) * zv * sigmoid_f(zv);
-                        au[k] += xv;
-                        ag[k] += gv;
-                        ad[k] = fmaf(gv, xv, ad[k]);
+                        const float zv = raw_at(zr[i], k);
+                        ag[k] += raw_at(dr[i], k) * zv * sigmoid_f(zv);
+                        if (POOL) au[k] += raw_at(xr[i], k);
                     }
                 }
             }
@@ -87,79 +88,73 @@ bwd_pool_dense_kernel(const typename IO::elem* __restrict__ x, const typename IO
 #pragma unroll
         for (int k = 0; k < V; ++k) {
             const int64_t o = ((int64_t)g * VE + c) * V + k;
-            red[o] = au[k];
-            red[(int64_t)G * width + o] = ag[k];
-            red[2 * (int64_t)G * width + o] = ad[k];
+            red[o] = ag[k];
+            if (POOL) red[(int64_t)G * width + o] = au[k];
         }
     }
     __syncthreads();
     for (int q = tid; q < width; q += blockDim.x) {
-        float su = red[q], sg = red[G * width + q], sd = red[2 * G * width + q];
-        for (int gg = 1; gg < G; ++gg) {
-            su += red[gg * width + q];
-            sg += red[(G + gg) * width + q];
-            sd += red[(2 * G + gg) * width + q];
-        }
-        u[bt * E + q] = su * inv_p;
+        float sg = red[q];
+        for (int gg = 1; gg < G; ++gg) sg += red[gg * width + q];
         gs[bt * E + q] = sg;
-        dDp[bt * E + q] = sd;
+        if (POOL) {
+            float su = red[G * width + q];
+            for (int gg = 1; gg < G; ++gg) su += red[(G + gg) * width + q];
+            u[bt * E + q] = su * inv_p;
+        }
     }
 }
 
 // Masked pass 1: workgroup (b, t) takes the kept tokens whose row is t; the
 // pooled sum is divided by the fixed row length P.  Tokens with an invalid
 // mask entry (row -1) belong to no row.
-template <class IO>
+template <class IO, bool POOL>
 __global__ void __launch_bounds__(1024)
 bwd_pool_masked_kernel(const typename IO::elem* __restrict__ x, const typename IO::elem* __restrict__ z,
                        const typename IO::elem* __restrict__ dout, const int32_t* __restrict__ rows,
-                       float* __restrict__ u, float* __restrict__ gs, float* __restrict__ dDp, int64_t T, int64_t K,
-                       int VE, int G, int64_t E, float inv_p) {
+                       float* __restrict__ u, float* __restrict__ gs, int64_t T, int64_t K, int VE, int G,
+                       int64_t E, float inv_p) {
     constexpr int V = IO::V;
-    extern __shared__ float red[];  // [3][G][VE * V]
+    extern __shared__ float red[];  // [POOL ? 2 : 1][G][VE * V]
     const int64_t bt = blockIdx.x;
     const int64_t b = bt / T, t = bt - b * T;
     const int tid = threadIdx.x;
     const int c = tid % VE, g = tid / VE;
     const int width = VE * V;
     if (g < G) {
-        float au[V], ag[V], ad[V];
+        float au[V], ag[V];
 #pragma unroll
-        for (int k = 0; k < V; ++k) au[k] = ag[k] = ad[k] = 0.f;
+        for (int k = 0; k < V; ++k) au[k] = ag[k] = 0.f;
         for (int64_t k = g; k < K; k += G) {
             if (rows[b * K + k] != t) continue;
             const int64_t o = (b * K + k) * E + (int64_t)c * V;
             float xv[V], zv[V], dv[V];
-            load_vec<false>(x + o, xv);
+            if (POOL) load_vec<false>(x + o, xv);
             load_vec<false>(z + o, zv);
             load_vec<false>(dout + o, dv);
 #pragma unroll
             for (int q = 0; q < V; ++q) {
-                const float gv = dv[q] * zv[q] * sigmoid_f(zv[q]);
-                au[q] += xv[q];
-                ag[q] += gv;
-                ad[q] = fmaf(gv, xv[q], ad[q]);
+                ag[q] += dv[q] * zv[q] * sigmoid_f(zv[q]);
+                if (POOL) au[q] += xv[q];
             }
         }
 #pragma unroll
         for (int k = 0; k < V; ++k) {
             const int64_t o = ((int64_t)g * VE + c) * V + k;
-            red[o] = au[k];
-            red[(int64_t)G * width + o] = ag[k];
-            red[2 * (int64_t)G * width + o] = ad[k];
+            red[o] = ag[k];
+            if (POOL) red[(int64_t)G * width + o] = au[k];
         }
     }
     __syncthreads();
     for (int q = tid; q < width; q += blockDim.x) {
-        float su = red[q], sg = red[G * width + q], sd = red[2 * G * width + q];
-        for (int gg = 1; gg < G; ++gg) {
-            su += red[gg * width + q];
-            sg += red[(G + gg) * width + q];
-            sd += red[(2 * G + gg) * width + q];
-        }
-        u[bt * E + q] = su * inv_p;
+        float sg = red[q];
+        for (int gg = 1; gg < G; ++gg) sg += red[gg * width + q];
         gs[bt * E + q] = sg;
-        dDp[bt * E + q] = sd;
+        if (POOL) {
+            float su = red[G * width + q];
+            for (int gg = 1; gg < G; ++gg) su += red[(G + gg) * width + q];
+            u[bt * E + q] = su * inv_p;
+        }
     }
 }
 
@@ -172,27 +167,34 @@ void pick_groups_bwd(int64_t VE, int64_t n, int* G, int* threads) {
     *threads = (int)((VE * g + 63) / 64 * 64);
 }
 
-template <class IO>
+template <class IO, bool POOL>
 hipError_t bwd_pool_t(const Geom& g, const void* x, const void* z, const void* dout, const BwdWorkspace& ws,
                       hipStream_t st) {
     using elem = typename IO::elem;
     const int64_t VE = g.E / IO::V;
     int G, threads;
     pick_groups_bwd(VE, g.masked ? g.K : g.P, &G, &threads);
-    const size_t lds = 3 * (size_t)G * VE * IO::V * sizeof(float);
+    const size_t lds = (POOL ? 2 : 1) * (size_t)G * VE * IO::V * sizeof(float);
     const elem *xe = static_cast<const elem*>(x), *ze = static_cast<const elem*>(z),
                *de = static_cast<const elem*>(dout);
     if (g.masked) {
-        hipLaunchKernelGGL(bwd_pool_masked_kernel<IO>, dim3((unsigned)(g.B * g.T)), dim3(threads), lds, st, xe, ze,
-                           de, ws.fwd.rows, ws.fwd.u, ws.gs, ws.dDp, g.T, g.K, (int)VE, G, g.E, 1.0f / (float)g.P);
+        hipLaunchKernelGGL((bwd_pool_masked_kernel<IO, POOL>), dim3((unsigned)(g.B * g.T)), dim3(threads), lds, st,
+                           xe, ze, de, ws.fwd.rows, ws.fwd.u, ws.gs, g.T, g.K, (int)VE, G, g.E,
+                           1.0f / (float)g.P);
     } else {
         const int64_t t_stride = g.axis == FASTVIM_POOL_COLS ? g.w * g.E : g.E;
         const int64_t p_stride = g.axis == FASTVIM_POOL_COLS ? g.E : g.w * g.E;
-        hipLaunchKernelGGL(bwd_pool_dense_kernel<IO>, dim3((unsigned)(g.B * g.T)), dim3(threads), lds, st, xe, ze,
-                           de, ws.fwd.u, ws.gs, ws.dDp, g.T, g.P, (int)VE, G, g.E, g.h * g.w * g.E, t_stride,
+        hipLaunchKernelGGL((bwd_pool_dense_kernel<IO, POOL>), dim3((unsigned)(g.B * g.T)), dim3(threads), lds, st,
+                           xe, ze, de, ws.fwd.u, ws.gs, g.T, g.P, (int)VE, G, g.E, g.h * g.w * g.E, t_stride,
                            p_stride, 1.0f / (float)g.P);
     }
     return hipGetLastError();
+}
+
+template <class IO>
+hipError_t bwd_pool_io(const Geom& g, const void* x, const void* z, const void* dout, const BwdWorkspace& ws,
+                       hipStream_t st) {
+    return ws.u_saved ? bwd_pool_t<IO, false>(g, x, z, dout, ws, st) : bwd_pool_t<IO, true>(g, x, z, dout, ws, st);
 }
 
 // ---------------------------------------------------------------------- dv
@@ -370,103 +372,135 @@ __device__ __forceinline__ void row_vec1(const float* a, int64_t off, float (&r)
     }
 }
 
-// A workgroup takes a run of G * kU memory-contiguous tokens (part of a grid
-// row, or of one image's kept tokens), as the forward epilogue does.
+// A workgroup takes a run of G * kU consecutive tokens of one segment: a grid
+// row (dense; its tokens are contiguous in memory) or one image's kept tokens
+// (masked).  Lane (c, g) handles the tokens p0 + g + G k, k < kU, all loads
+// issued first, and sums dL/dy * x over them; the G group sums are added
+// through LDS in a fixed order into the workgroup's row of dDp.
 template <class IO, int MODE>
 __global__ void __launch_bounds__(1024)
 bwd_epilogue_kernel(const typename IO::elem* __restrict__ x, const typename IO::elem* __restrict__ z,
                     const typename IO::elem* __restrict__ dout, const float* __restrict__ sf,
                     const float* __restrict__ sb, const float* __restrict__ du, const float* __restrict__ Df,
                     const float* __restrict__ Db, typename IO::elem* __restrict__ dx,
-                    typename IO::elem* __restrict__ dz, const int32_t* __restrict__ rows, int64_t T, int64_t h,
-                    int64_t w, int64_t K, int64_t E, int VE, int G, int64_t seg_len, int64_t blocks_per_seg,
-                    int64_t segs_per_img, float inv_p) {
+                    typename IO::elem* __restrict__ dz, const int32_t* __restrict__ rows, float* __restrict__ dDp,
+                    int64_t T, int64_t h, int64_t w, int64_t K, int64_t E, int VE, int G, int64_t seg_len,
+                    int64_t blocks_per_seg, int64_t segs_per_img, float inv_p) {
     constexpr int V = IO::V;
     using raw = typename IO::raw;
+    extern __shared__ float red[];  // [G][VE * V]
     const int tid = threadIdx.x, c = tid % VE, g = tid / VE;
-    if (g >= G) return;
+    const int width = VE * V;
     const int64_t blk = blockIdx.x;
     const int64_t seg = blk / blocks_per_seg;
     const int64_t p0 = (blk - seg * blocks_per_seg) * (int64_t)G * kU;
     const int64_t b = seg / segs_per_img, sgi = seg - b * segs_per_img;
     const int64_t col = (int64_t)c * V;
-    int64_t tok[kU];
-    bool ok[kU];
+    if (g < G) {
+        int64_t tok[kU];
+        bool ok[kU];
 #pragma unroll
-    for (int k = 0; k < kU; ++k) {
-        const int64_t p = p0 + g + (int64_t)G * k;
-        ok[k] = p < seg_len;
-        tok[k] = MODE == kModeMasked ? b * K + p : (b * h + sgi) * w + p;
-    }
-    raw xr[kU], zr[kU], dr[kU];
-#pragma unroll
-    for (int k = 0; k < kU; ++k) {
-        if (ok[k]) {
-            xr[k] = load_raw<true>(x + tok[k] * E + col);
-            zr[k] = load_raw<true>(z + tok[k] * E + col);
-            dr[k] = load_raw<true>(dout + tok[k] * E + col);
+        for (int k = 0; k < kU; ++k) {
+            const int64_t p = p0 + g + (int64_t)G * k;
+            ok[k] = p < seg_len;
+            tok[k] = MODE == kModeMasked ? b * K + p : (b * h + sgi) * w + p;
         }
-    }
-    float dsum[V];
+        raw xr[kU], zr[kU], dr[kU];
 #pragma unroll
-    for (int v = 0; v < V; ++v) dsum[v] = Df[col + v] + Db[col + v];
-    float srow[V], urow[V];
-    if (MODE == kModeCols) {
-        row_vec<V>(sf, sb, (b * T + sgi) * E + col, srow);
-        row_vec1<V>(du, (b * T + sgi) * E + col, urow);
-    }
-#pragma unroll
-    for (int k = 0; k < kU; ++k) {
-        if (!ok[k]) continue;
-        float sv[V], uv[V];
-        bool valid = true;
-        if (MODE == kModeCols) {
-#pragma unroll
-            for (int v = 0; v < V; ++v) {
-                sv[v] = srow[v];
-                uv[v] = urow[v];
-            }
-        } else {
-            const int64_t t = MODE == kModeRows ? p0 + g + (int64_t)G * k : rows[tok[k]];
-            valid = t >= 0;
-            if (valid) {
-                row_vec<V>(sf, sb, (b * T + t) * E + col, sv);
-                row_vec1<V>(du, (b * T + t) * E + col, uv);
+        for (int k = 0; k < kU; ++k) {
+            if (ok[k]) {
+                xr[k] = load_raw<true>(x + tok[k] * E + col);
+                zr[k] = load_raw<true>(z + tok[k] * E + col);
+                dr[k] = load_raw<true>(dout + tok[k] * E + col);
             }
         }
-        float ox[V], oz[V];
+        float dsum[V], ad[V];
 #pragma unroll
         for (int v = 0; v < V; ++v) {
-            const float xv = raw_at(xr[k], v), zv = raw_at(zr[k], v), dv = raw_at(dr[k], v);
-            const float sg = sigmoid_f(zv);
-            const float y = fmaf(dsum[v], xv, sv[v]);
-            ox[v] = valid ? fmaf(dv * zv * sg, dsum[v], uv[v] * inv_p) : __builtin_nanf("");
-            oz[v] = valid ? dv * y * sg * fmaf(zv, 1.f - sg, 1.f) : __builtin_nanf("");
+            dsum[v] = Df[col + v] + Db[col + v];
+            ad[v] = 0.f;
         }
-        store_vec<true>(dx + tok[k] * E + col, ox);
-        store_vec<true>(dz + tok[k] * E + col, oz);
+        float srow[V], urow[V];
+        if (MODE == kModeCols) {
+            row_vec<V>(sf, sb, (b * T + sgi) * E + col, srow);
+            row_vec1<V>(du, (b * T + sgi) * E + col, urow);
+        }
+#pragma unroll
+        for (int k = 0; k < kU; ++k) {
+            if (!ok[k]) continue;
+            float sv[V], uv[V];
+            bool valid = true;
+            if (MODE == kModeCols) {
+#pragma unroll
+                for (int v = 0; v < V; ++v) {
+                    sv[v] = srow[v];
+                    uv[v] = urow[v];
+                }
+            } else {
+                const int64_t t = MODE == kModeRows ? p0 + g + (int64_t)G * k : rows[tok[k]];
+                valid = t >= 0;
+                if (valid) {
+                    row_vec<V>(sf, sb, (b * T + t) * E + col, sv);
+                    row_vec1<V>(du, (b * T + t) * E + col, uv);
+                }
+            }
+            float ox[V], oz[V];
+#pragma unroll
+            for (int v = 0; v < V; ++v) {
+                const float xv = raw_at(xr[k], v), zv = raw_at(zr[k], v), dv = raw_at(dr[k], v);
+                const float sg = sigmoid_f(zv);
+                const float gv = dv * zv * sg;
+                const float y = fmaf(dsum[v], xv, sv[v]);
+                if (valid) ad[v] = fmaf(gv, xv, ad[v]);
+                ox[v] = valid ? fmaf(gv, dsum[v], uv[v] * inv_p) : __builtin_nanf("");
+                oz[v] = valid ? dv * y * sg * fmaf(zv, 1.f - sg, 1.f) : __builtin_nanf("");
+            }
+            store_vec<true>(dx + tok[k] * E + col, ox);
+            store_vec<true>(dz + tok[k] * E + col, oz);
+        }
+#pragma unroll
+        for (int v = 0; v < V; ++v) red[g * width + col + v] = ad[v];
     }
+    __syncthreads();
+    for (int q = tid; q < width; q += blockDim.x) {
+        float sd = red[q];
+        for (int gg = 1; gg < G; ++gg) sd += red[gg * width + q];
+        dDp[blk * E + q] = sd;
+    }
+}
+
+// Launch shape of pass 2: G groups of VE lanes per workgroup, kU tokens per
+// lane, runs of G * kU tokens within a segment.
+struct BwdEpiShape {
+    int64_t VE, G, seg_len, segs_per_img, blocks_per_seg, blocks;
+    int threads;
+};
+
+BwdEpiShape bwd_epi_shape(const Geom& g) {
+    BwdEpiShape s;
+    s.VE = g.E / (g.io == FASTVIM_BF16 ? IoBf16::V : IoF32::V);
+    s.seg_len = g.masked ? g.K : g.w;
+    s.segs_per_img = g.masked ? 1 : g.h;
+    s.G = 512 / s.VE;
+    if (s.G * kU > s.seg_len) s.G = (s.seg_len + kU - 1) / kU;
+    if (s.G < 1) s.G = 1;
+    s.blocks_per_seg = (s.seg_len + s.G * kU - 1) / (s.G * kU);
+    s.blocks = g.B * s.segs_per_img * s.blocks_per_seg;
+    s.threads = (int)((s.VE * s.G + 63) / 64 * 64);
+    return s;
 }
 
 template <class IO, int MODE>
 hipError_t bwd_epi_launch(const Geom& g, const void* x, const void* z, const void* dout, const fastvim_params& p,
                           const BwdWorkspace& ws, void* dx, void* dz, hipStream_t st) {
-    const int64_t VE = g.E / IO::V;
-    int64_t G = 512 / VE;
-    if (G < 1) G = 1;
-    const int64_t seg_len = MODE == kModeMasked ? g.K : g.w;
-    const int64_t segs_per_img = MODE == kModeMasked ? 1 : g.h;
-    if (G * kU > seg_len) G = (seg_len + kU - 1) / kU;
-    if (G < 1) G = 1;
-    const int64_t blocks_per_seg = (seg_len + G * kU - 1) / (G * kU);
-    const int threads = (int)((VE * G + 63) / 64 * 64);
+    const BwdEpiShape sh = bwd_epi_shape(g);
+    const size_t lds = (size_t)(sh.G * g.E) * sizeof(float);
     using elem = typename IO::elem;
-    const int64_t blocks = g.B * segs_per_img * blocks_per_seg;
-    hipLaunchKernelGGL((bwd_epilogue_kernel<IO, MODE>), dim3((unsigned)blocks), dim3(threads), 0, st,
+    hipLaunchKernelGGL((bwd_epilogue_kernel<IO, MODE>), dim3((unsigned)sh.blocks), dim3(sh.threads), lds, st,
                        static_cast<const elem*>(x), static_cast<const elem*>(z), static_cast<const elem*>(dout),
                        ws.fwd.s_f, ws.fwd.s_b, ws.du, p.fwd.D, p.bwd.D, static_cast<elem*>(dx),
-                       static_cast<elem*>(dz), ws.fwd.rows, g.T, g.h, g.w, g.K, g.E, (int)VE, (int)G, seg_len,
-                       blocks_per_seg, segs_per_img, 1.0f / (float)g.P);
+                       static_cast<elem*>(dz), ws.fwd.rows, ws.dDp, g.T, g.h, g.w, g.K, g.E, (int)sh.VE, (int)sh.G,
+                       sh.seg_len, sh.blocks_per_seg, sh.segs_per_img, 1.0f / (float)g.P);
     return hipGetLastError();
 }
 
@@ -480,9 +514,11 @@ hipError_t bwd_epi_dispatch(const Geom& g, const void* x, const void* z, const v
 
 }  // namespace
 
+int64_t bwd_dd_parts(const Geom& g) { return bwd_epi_shape(g).blocks; }
+
 hipError_t launch_bwd_pool(const Geom& g, const void* x, const void* z, const void* dout, const BwdWorkspace& ws,
                            hipStream_t st) {
-    return g.io == FASTVIM_BF16 ? bwd_pool_t<IoBf16>(g, x, z, dout, ws, st) : bwd_pool_t<IoF32>(g, x, z, dout, ws, st);
+    return g.io == FASTVIM_BF16 ? bwd_pool_io<IoBf16>(g, x, z, dout, ws, st) : bwd_pool_io<IoF32>(g, x, z, dout, ws, st);
 }
 
 hipError_t launch_bwd_dv(const Geom& g, const BwdWorkspace& ws, hipStream_t st) {

@@ -16,7 +16,7 @@ constexpr int kColRowsPerBlock = 256;  // rows per first-stage block of a column
 struct BwdWorkspace {
     Workspace fwd;
     float* gs;     // (B, T, E) dL/ds: the gated upstream gradient summed over the pooled axis
-    float* dDp;    // (B, T, E) per pooled row: sum over its cells of dL/dy * x
+    float* dDp;    // (bwd_dd_parts, E) per second-pass workgroup: sum over its tokens of dL/dy * x
     float* du_f;   // (B, T, E) scan part of dL/du, forward direction
     float* du_b;   // (B, T, E) the same, backward direction
     float* du;     // (B, T, E) dL/du, both directions, scan and x_proj
@@ -28,6 +28,7 @@ struct BwdWorkspace {
     float* dWxp;   // (MC, 2, NX, E) per token chunk d x_proj_w
     float* tmp;    // first-stage sums of the column reductions
     int64_t G, S, MC, tmp_floats;
+    bool u_saved = false;  // fwd.u is the caller's saved pooled tokens (pass 1 does not pool x)
 };
 
 struct BwdScanArgs {
@@ -44,6 +45,9 @@ struct BwdScanArgs {
 };
 
 int bwd_rmax(int64_t R);  // the dt-rank bound (16, 32, 48, 64) whose kernel instance serves R
+// Second-pass workgroups (each a run of consecutive tokens of one grid row,
+// or of one image's kept tokens when masked): the rows of dDp.
+int64_t bwd_dd_parts(const Geom& g);
 size_t bwd_workspace_layout(const Geom& g, void* base, BwdWorkspace* ws);
 
 hipError_t launch_bwd_pool(const Geom& g, const void* x, const void* z, const void* dout, const BwdWorkspace& ws,

@@ -32,7 +32,7 @@ def test_library_exports_every_declared_function():
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(Bd.EXPORTED_SYMBOLS)
-    assert lib.fastvim_abi_version() == 6
+    assert lib.fastvim_abi_version() == 7
 
 
 def test_status_strings():
@@ -44,9 +44,11 @@ def test_status_strings():
 
 def test_struct_layout_matches_header():
     # int64 x 7 + int32 x 2; five pointers; two dir structs + ptr + size_t + 2 x u32 + 2 ptrs + f32 + u32
+    # + 2 conv ptrs + saved_u
     assert ctypes.sizeof(Bd.Dims) == 64
     assert ctypes.sizeof(Bd.DirParams) == 40
-    assert ctypes.sizeof(Bd.Params) == 2 * 40 + 8 + 8 + 8 + 8 + 8 + 4 + 4 + 8 + 8
+    assert ctypes.sizeof(Bd.Params) == 2 * 40 + 8 + 8 + 8 + 8 + 8 + 4 + 4 + 8 + 8 + 8
+    assert Bd.Params.saved_u.offset == ctypes.sizeof(Bd.Params) - 8
     assert ctypes.sizeof(Bd.DirGrads) == 40 and ctypes.sizeof(Bd.Grads) == 80
 
 
@@ -279,6 +281,40 @@ class FakeBwd:
     def bwd(self):
         return P.lib().fastvim_ssm_bwd(self.x, self.z, self.dout, ctypes.byref(self.params), ctypes.byref(self.dims),
                                        self.axis, self.idx, self.dx, self.dz, ctypes.byref(self.grads), None)
+
+
+def test_saved_u_checks_forward():
+    far = 1 << 44  # an address far from every other argument
+    c = FakeCall(axis=P.POOL_NONE_ROWMAJOR)
+    c.params.saved_u = far
+    expect(c, EARG)  # unpooled: no pooled tokens to keep
+    c = FakeCall()
+    c.params.saved_u = far + 4
+    expect(c, EALIGN)
+    for target in ("x", "z", "out"):
+        c = FakeCall()
+        c.params.saved_u = getattr(c, target)
+        expect(c, EOVERLAP)
+    c = FakeCall()
+    c.params.saved_u = c.params.workspace + 256
+    expect(c, EOVERLAP)
+
+
+def test_saved_u_checks_backward():
+    far = 1 << 44
+    c = FakeBwd()
+    c.params.saved_u = far + 8
+    assert c.bwd() == EALIGN
+    for target in ("dx", "dz"):
+        c = FakeBwd()
+        c.params.saved_u = getattr(c, target)
+        assert c.bwd() == EOVERLAP, target
+    c = FakeBwd()
+    c.params.saved_u = c.params.workspace
+    assert c.bwd() == EOVERLAP
+    c = FakeBwd()
+    c.params.saved_u = c.grads.fwd.D
+    assert c.bwd() == EOVERLAP
 
 
 def test_bwd_workspace_bytes():

@@ -11,7 +11,9 @@ inputs and upstream gradient).  Full-size workloads run on the GPU at their
 real shape with the upstream gradient nonzero on a sample of images only:
 every gradient then comes from those images alone, so the oracle on the
 sample gives every parameter gradient, and the other images' dx and dz must
-be exactly zero.
+be exactly zero.  Cases marked "saved" run the GPU forward first, with
+saved_u, and give the backward those pooled tokens instead of letting it
+pool x again.
 """
 from __future__ import annotations
 
@@ -41,10 +43,17 @@ def _gpu():
     torch.cuda.synchronize()
 
 
-def gpu_bwd(x, z, dout, prm, axis, idx=None, hw=None, dtype=torch.float32, flags=0):
+def gpu_bwd(x, z, dout, prm, axis, idx=None, hw=None, dtype=torch.float32, flags=0, saved=None):
+    """saved: None (the backward pools x itself) or the flags of a forward call
+    that first writes the pooled tokens the backward then reads (saved_u)."""
     idd = None if idx is None else dev(idx, torch.int32)
-    call = P.BwdCall(dev(x, dtype), dev(z, dtype), dev(dout, dtype), dev_params(prm), axis, mask_idx=idd, hw=hw,
-                     flags=flags)
+    xd, zd, pd = dev(x, dtype), dev(z, dtype), dev_params(prm)
+    su = None
+    if saved is not None:
+        h, w = (x.shape[1], x.shape[2]) if idx is None else hw
+        su = torch.full((x.shape[0], h if axis == P.POOL_COLS else w, x.shape[-1]), float("nan"), device="cuda")
+        P.SSMCall(xd, zd, pd, axis, mask_idx=idd, hw=hw, flags=saved, saved_u=su).run()
+    call = P.BwdCall(xd, zd, dev(dout, dtype), pd, axis, mask_idx=idd, hw=hw, flags=flags, saved_u=su)
     res = call.run()
     torch.cuda.synchronize()
     return {"dx": host(res["dx"]), "dz": host(res["dz"]),
@@ -61,14 +70,14 @@ def compare(got, ref, tol, tag, sel=None, params=True):
                 check(got[d][f], ref[d][f], tol, "%s d%s.%s" % (tag, d, f))
 
 
-def bwd_check(x, z, dout, prm, axis, tol, dtype, tag, idx=None, hw=None, twin=True):
+def bwd_check(x, z, dout, prm, axis, tol, dtype, tag, idx=None, hw=None, twin=True, saved=None):
     """GPU gradients and those of the D = 0 twin against the oracle."""
-    got = gpu_bwd(x, z, dout, prm, axis, idx=idx, hw=hw, dtype=dtype)
+    got = gpu_bwd(x, z, dout, prm, axis, idx=idx, hw=hw, dtype=dtype, saved=saved)
     ref = oracle.layer_bwd(x, z, dout, prm["fwd"], prm["bwd"], axis, idx=idx, hw=hw)
     compare(got, ref, tol, tag)
     if twin:
         p0 = zero_D(prm)
-        got0 = gpu_bwd(x, z, dout, p0, axis, idx=idx, hw=hw, dtype=dtype)
+        got0 = gpu_bwd(x, z, dout, p0, axis, idx=idx, hw=hw, dtype=dtype, saved=saved)
         ref0 = oracle.layer_bwd(x, z, dout, p0["fwd"], p0["bwd"], axis, idx=idx, hw=hw)
         compare(got0, ref0, tol, tag + " (D=0)", params=False)
     return got
@@ -108,10 +117,17 @@ RAGGED = [
 ]
 
 
+# forward path whose pooled tokens the backward reads: None (it pools x
+# itself), or the single launch where the layer allows it (else the stage kernels)
+SAVED = [None, P.FLAG_FUSED]
+SAVED_IDS = ["pools", "saved"]
+
+
+@pytest.mark.parametrize("saved", SAVED, ids=SAVED_IDS)
 @pytest.mark.parametrize("shape", RAGGED, ids=["x".join(map(str, s)) for s in RAGGED])
 @pytest.mark.parametrize("axis", (P.POOL_COLS, P.POOL_ROWS))
 @pytest.mark.parametrize("io", ["f32", "bf16"])
-def test_bwd_ragged_shapes(shape, axis, io):
+def test_bwd_ragged_shapes(shape, axis, io, saved):
     B, h, w, E, R = shape
     if (h if axis == P.POOL_COLS else w) > 128:
         pytest.skip("scan longer than the backward pass supports")
@@ -122,13 +138,14 @@ def test_bwd_ragged_shapes(shape, axis, io):
     x, z, dout = _io(io, x, z, dout)
     prm = {"fwd": rand_dir(rng, E, 16, R, 0.1), "bwd": rand_dir(rng, E, 16, R, 0.1)}
     tol, dt = _tol(io)
-    bwd_check(x, z, dout, prm, axis, tol, dt, "ragged %s %s axis %d" % (shape, io, axis))
+    bwd_check(x, z, dout, prm, axis, tol, dt, "ragged %s %s axis %d" % (shape, io, axis), saved=saved)
 
 
+@pytest.mark.parametrize("saved", [None, 0], ids=SAVED_IDS)
 @pytest.mark.parametrize("axis", (P.POOL_COLS, P.POOL_ROWS))
 @pytest.mark.parametrize("io", ["f32", "bf16"])
 @pytest.mark.parametrize("K", [1, 17, 42])
-def test_bwd_masked_small(axis, io, K):
+def test_bwd_masked_small(axis, io, K, saved):
     B, h, w, E, R = 5, 6, 7, 64, 6
     rng = np.random.default_rng(200 + K + 7 * axis)
     x = rng.standard_normal((B, K, E)).astype(np.float32)
@@ -138,7 +155,8 @@ def test_bwd_masked_small(axis, io, K):
     idx = random_mask(rng, B, h, w, K)
     prm = {"fwd": rand_dir(rng, E, 16, R, 0.1), "bwd": rand_dir(rng, E, 16, R, 0.1)}
     tol, dt = _tol(io)
-    bwd_check(x, z, dout, prm, axis, tol, dt, "masked K=%d %s axis %d" % (K, io, axis), idx=idx, hw=(h, w))
+    bwd_check(x, z, dout, prm, axis, tol, dt, "masked K=%d %s axis %d" % (K, io, axis), idx=idx, hw=(h, w),
+              saved=saved)
 
 
 def test_bwd_masked_invalid_indices():
@@ -217,7 +235,7 @@ def test_bwd_rows_is_cols_on_transposed_grid():
 
 
 # ------------------------------------------------------------------ full size
-def _sampled_full_size(cfg, axis=P.POOL_COLS):
+def _sampled_full_size(cfg, axis=P.POOL_COLS, saved=None):
     wl = draw_workload(cfg)
     x, z, prm, idx = wl["x"], wl["z"][0], wl["params"][0], wl["idx"]
     sel = np.array([0, cfg.B - 1])
@@ -228,9 +246,10 @@ def _sampled_full_size(cfg, axis=P.POOL_COLS):
         dout = round_to_bf16(dout)
     tol, dt = _tol(cfg.io_dtype)
     hw = (cfg.h, cfg.w) if cfg.masked else None
-    print("\n[%s bwd] B=%d grid=%dx%d E=%d, upstream gradient on images %s" % (cfg.name, cfg.B, cfg.h, cfg.w, cfg.E,
-                                                                           list(sel)), flush=True)
-    got = gpu_bwd(x, z, dout, prm, axis, idx=idx, hw=hw, dtype=dt)
+    print("\n[%s bwd] B=%d grid=%dx%d E=%d axis %d, upstream gradient on images %s, pooled tokens %s"
+          % (cfg.name, cfg.B, cfg.h, cfg.w, cfg.E, axis, list(sel), "saved" if saved is not None else "recomputed"),
+          flush=True)
+    got = gpu_bwd(x, z, dout, prm, axis, idx=idx, hw=hw, dtype=dt, saved=saved)
     rest = np.setdiff1d(np.arange(cfg.B), sel)
     for name in ("dx", "dz"):
         assert np.count_nonzero(got[name][rest]) == 0, name + " nonzero on images without upstream gradient"
@@ -239,11 +258,27 @@ def _sampled_full_size(cfg, axis=P.POOL_COLS):
     compare(got, ref, tol, cfg.name, sel=sel)
 
 
+@pytest.mark.parametrize("saved", [None, 0], ids=SAVED_IDS)
 @pytest.mark.parametrize("axis", (P.POOL_COLS, P.POOL_ROWS))
-def test_bwd_full_size_2048(axis):
-    _sampled_full_size(C.HIRES_2048, axis)
+def test_bwd_full_size_2048(axis, saved):
+    _sampled_full_size(C.HIRES_2048, axis, saved)
 
 
+@pytest.mark.parametrize("saved", [None, 0], ids=SAVED_IDS)
 @pytest.mark.parametrize("cfg", [C.SHORT_224_S, C.MASKED_B], ids=lambda c: c.name)
-def test_bwd_full_size_other(cfg):
-    _sampled_full_size(cfg)
+def test_bwd_full_size_other(cfg, saved):
+    _sampled_full_size(cfg, saved=saved)
+
+
+def test_bwd_saved_u_matches_pooling_again():
+    """The two ways of getting the pooled tokens give the same gradients within
+    fp32 rounding (only u's summation order differs)."""
+    B, h, w, E, R = 3, 40, 36, 96, 10
+    rng = np.random.default_rng(41)
+    x, z, dout = (rng.standard_normal((B, h, w, E)).astype(np.float32) for _ in range(3))
+    prm = {"fwd": rand_dir(rng, E, 16, R, 0.1), "bwd": rand_dir(rng, E, 16, R, 0.1)}
+    for axis in (P.POOL_COLS, P.POOL_ROWS):
+        a = gpu_bwd(x, z, dout, prm, axis)
+        for fl in (P.FLAG_STAGED, P.FLAG_FUSED):
+            b = gpu_bwd(x, z, dout, prm, axis, saved=fl)
+            compare(b, a, 1e-5, "saved vs pooled again, axis %d flags %d" % (axis, fl))

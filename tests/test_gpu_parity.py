@@ -360,6 +360,45 @@ def test_fused_matches_staged(axis):
         assert rel_inf(host(f.export(what)), host(s.export(what))) <= 1e-5, what
 
 
+@pytest.mark.parametrize("flags", (P.FLAG_STAGED, P.FLAG_FUSED), ids=["staged", "fused"])
+@pytest.mark.parametrize("axis", (P.POOL_COLS, P.POOL_ROWS))
+def test_saved_u_forward(axis, flags):
+    """With saved_u the forward writes the pooled tokens to the caller's buffer
+    (equal to the oracle's u, and to the workspace's u of a call without it),
+    and out is bit for bit the same as without saved_u."""
+    wl = draw_workload(C.CHAIN_1024, batch=4)
+    x, z, prm = wl["x"], wl["z"][0], wl["params"][0]
+    plain = gpu_call(x, z, prm, axis, flags=flags)
+    o1 = plain.run().clone()
+    T = x.shape[1] if axis == P.POOL_COLS else x.shape[2]
+    su = torch.full((x.shape[0], T, x.shape[-1]), float("nan"), device="cuda")
+    kept = P.SSMCall(plain.x, plain.z, dev_params(prm), axis, flags=flags, saved_u=su)
+    o2 = kept.run()
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+    assert torch.equal(su, plain.export(P.EXPORT_U))
+    assert torch.equal(kept.export(P.EXPORT_U), su)
+    sel = np.array([0, x.shape[0] - 1])
+    ref = oracle.layer(x[sel], z[sel], prm["fwd"], prm["bwd"], axis, stages=True)
+    check(host(su[sel]), ref["u"], FP32_TOL, "saved u")
+
+
+def test_saved_u_forward_masked():
+    B, h, w, E, R, K = 3, 6, 7, 64, 6, 20
+    rng = np.random.default_rng(23)
+    x, z = (rng.standard_normal((B, K, E)).astype(np.float32) for _ in range(2))
+    idx = random_mask(rng, B, h, w, K)
+    prm = {"fwd": rand_dir(rng, E, 16, R, 0.1), "bwd": rand_dir(rng, E, 16, R, 0.1)}
+    su = torch.full((B, h, E), float("nan"), device="cuda")
+    call = P.SSMCall(dev(x), dev(z), dev_params(prm), P.POOL_COLS, mask_idx=dev(idx, torch.int32), hw=(h, w),
+                     saved_u=su)
+    out = host(call.run())
+    torch.cuda.synchronize()
+    ref = oracle.layer(x, z, prm["fwd"], prm["bwd"], P.POOL_COLS, idx=idx, hw=(h, w), stages=True)
+    check(host(su), ref["u"], FP32_TOL, "masked saved u")
+    check(out, ref["out"], FP32_TOL, "masked out with saved u")
+
+
 # --------------------------------------------------------------- full-size workloads
 _cache = {}
 
