@@ -29,6 +29,7 @@
 // stream 16-byte vectors with every load of a batch issued before any
 // arithmetic, like the forward pool and epilogue kernels.
 #include "bwd_internal.h"
+#include "mask_list.h"
 
 namespace fastvim {
 namespace {
@@ -107,7 +108,9 @@ bwd_pool_dense_kernel(const typename IO::elem* __restrict__ x, const typename IO
 
 // Masked pass 1: workgroup (b, t) takes the kept tokens whose row is t; the
 // pooled sum is divided by the fixed row length P.  Tokens with an invalid
-// mask entry (row -1) belong to no row.
+// mask entry (row -1) belong to no row.  As in the forward pooling, the row's
+// tokens of each slice of blockDim.x kept tokens are listed first
+// (mask_list.h) and then loaded kB at a time per lane.
 template <class IO, bool POOL>
 __global__ void __launch_bounds__(1024)
 bwd_pool_masked_kernel(const typename IO::elem* __restrict__ x, const typename IO::elem* __restrict__ z,
@@ -115,29 +118,44 @@ bwd_pool_masked_kernel(const typename IO::elem* __restrict__ x, const typename I
                        float* __restrict__ u, float* __restrict__ gs, int64_t T, int64_t K, int VE, int G,
                        int64_t E, float inv_p) {
     constexpr int V = IO::V;
+    constexpr int kB = 16 / V;  // list entries in flight per lane (64 bytes of each stream)
     extern __shared__ float red[];  // [POOL ? 2 : 1][G][VE * V]
+    __shared__ int list[1024];
+    __shared__ int wave_cnt[kMaxListWaves];
     const int64_t bt = blockIdx.x;
     const int64_t b = bt / T, t = bt - b * T;
     const int tid = threadIdx.x;
     const int c = tid % VE, g = tid / VE;
     const int width = VE * V;
-    if (g < G) {
-        float au[V], ag[V];
+    float au[V], ag[V];
 #pragma unroll
-        for (int k = 0; k < V; ++k) au[k] = ag[k] = 0.f;
-        for (int64_t k = g; k < K; k += G) {
-            if (rows[b * K + k] != t) continue;
-            const int64_t o = (b * K + k) * E + (int64_t)c * V;
-            float xv[V], zv[V], dv[V];
-            if (POOL) load_vec<false>(x + o, xv);
-            load_vec<false>(z + o, zv);
-            load_vec<false>(dout + o, dv);
+    for (int k = 0; k < V; ++k) au[k] = ag[k] = 0.f;
+    for (int64_t k0 = 0; k0 < K; k0 += blockDim.x) {
+        const int n = row_token_list(rows + b * K, K, t, k0, list, wave_cnt);
+        if (g >= G) continue;
+        const int64_t base = (b * K + k0) * E + (int64_t)c * V;
+        for (int i0 = g; i0 < n; i0 += kB * G) {
+            float xv[kB][V], zv[kB][V], dv[kB][V];
 #pragma unroll
-            for (int q = 0; q < V; ++q) {
-                ag[q] += dv[q] * zv[q] * sigmoid_f(zv[q]);
-                if (POOL) au[q] += xv[q];
-            }
+            for (int j = 0; j < kB; ++j)
+                if (i0 + j * G < n) {
+                    const int64_t o = base + (int64_t)list[i0 + j * G] * E;
+                    if (POOL) load_vec<false>(x + o, xv[j]);
+                    load_vec<false>(z + o, zv[j]);
+                    load_vec<false>(dout + o, dv[j]);
+                }
+#pragma unroll
+            for (int j = 0; j < kB; ++j)
+                if (i0 + j * G < n) {
+#pragma unroll
+                    for (int q = 0; q < V; ++q) {
+                        ag[q] += dv[j][q] * zv[j][q] * sigmoid_f(zv[j][q]);
+                        if (POOL) au[q] += xv[j][q];
+                    }
+                }
         }
+    }
+    if (g < G) {
 #pragma unroll
         for (int k = 0; k < V; ++k) {
             const int64_t o = ((int64_t)g * VE + c) * V + k;

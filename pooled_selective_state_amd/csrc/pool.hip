@@ -13,6 +13,7 @@
 // E, group g sums the pooled positions p = g, g+G, ...; the G partial sums are
 // combined through LDS in a fixed order, so results are deterministic.
 #include "fastvim_internal.h"
+#include "mask_list.h"
 
 namespace fastvim {
 namespace {
@@ -92,28 +93,43 @@ mask_rows_kernel(const int32_t* __restrict__ idx, int32_t* __restrict__ rows, in
 }
 
 // Masked pooling: workgroup (b, t) sums the kept tokens whose row is t and
-// divides by the fixed row length P.
+// divides by the fixed row length P.  The image's kept tokens are taken in
+// slices of blockDim.x: the slice's tokens of row t are listed first
+// (mask_list.h), then group g loads list entries g, g + G, ... kB at a time.
 template <class IO>
 __global__ void __launch_bounds__(1024)
 pool_masked_kernel(const typename IO::elem* __restrict__ x, const int32_t* __restrict__ rows,
                    float* __restrict__ u, int64_t T, int64_t K, int VE, int G, int64_t E, float inv_p) {
     constexpr int V = IO::V;
+    constexpr int kB = 16 / V;  // list entries in flight per lane (64 bytes of each stream)
     extern __shared__ float red[];  // [G][VE * V]
+    __shared__ int list[1024];
+    __shared__ int wave_cnt[kMaxListWaves];
     const int64_t bt = blockIdx.x;
     const int64_t b = bt / T, t = bt - b * T;
     const int tid = threadIdx.x;
     const int c = tid % VE, g = tid / VE;
-    if (g < G) {
-        float acc[V];
+    float acc[V];
 #pragma unroll
-        for (int k = 0; k < V; ++k) acc[k] = 0.f;
-        for (int64_t k = g; k < K; k += G) {
-            if (rows[b * K + k] != t) continue;
-            float a0[V];
-            load_vec<false>(x + (b * K + k) * E + (int64_t)c * V, a0);
+    for (int k = 0; k < V; ++k) acc[k] = 0.f;
+    for (int64_t k0 = 0; k0 < K; k0 += blockDim.x) {
+        const int n = row_token_list(rows + b * K, K, t, k0, list, wave_cnt);
+        if (g >= G) continue;
+        const typename IO::elem* xs = x + (b * K + k0) * E + (int64_t)c * V;
+        for (int i0 = g; i0 < n; i0 += kB * G) {
+            float a[kB][V];
 #pragma unroll
-            for (int q = 0; q < V; ++q) acc[q] += a0[q];
+            for (int j = 0; j < kB; ++j)
+                if (i0 + j * G < n) load_vec<false>(xs + (int64_t)list[i0 + j * G] * E, a[j]);
+#pragma unroll
+            for (int j = 0; j < kB; ++j)
+                if (i0 + j * G < n) {
+#pragma unroll
+                    for (int q = 0; q < V; ++q) acc[q] += a[j][q];
+                }
         }
+    }
+    if (g < G) {
 #pragma unroll
         for (int k = 0; k < V; ++k) red[((int64_t)g * VE + c) * V + k] = acc[k];
     }
