@@ -263,15 +263,26 @@ int run_bwd(const Geom& g, const void* x, const void* z, const void* dout, const
     if (!ok(launch_scan_bwd(a, s)) || !ok(launch_bwd_dv(g, ws, s)) || !ok(launch_bwd_du(g, p, ws, s)) ||
         !ok(launch_bwd_dwx(g, ws, s)))
         return FASTVIM_ERR_HIP;
+    // parameter gradients: sums of per-chunk and per-image partials; those of
+    // at most kColRowsPerBlock rows share one launch
     const fastvim_dir_grads* gd[2] = {&gr.fwd, &gr.bwd};
     const int64_t E = g.E, NX = g.NX, R = g.R, B = g.B;
+    ColsumBatch batch{};
     for (int d = 0; d < 2; ++d) {
-        if (!ok(launch_colsum(ws.dWxp + d * NX * E, ws.MC, NX * E, 2 * NX * E, gd[d]->x_proj_w, nullptr, ws.tmp, s)) ||
-            !ok(launch_colsum(ws.dAp + d * B * E * 16, B, E * 16, E * 16, gd[d]->A_log, nullptr, ws.tmp, s)) ||
-            !ok(launch_colsum(ws.dWdtp + d * B * E * R, B, E * R, E * R, gd[d]->dt_proj_w, nullptr, ws.tmp, s)) ||
-            !ok(launch_colsum(ws.dbp + d * B * E, B, E, E, gd[d]->dt_proj_b, nullptr, ws.tmp, s)))
-            return FASTVIM_ERR_HIP;
+        const ColsumSeg segs[4] = {
+            {ws.dWxp + d * NX * E, ws.MC, NX * E, 2 * NX * E, gd[d]->x_proj_w, nullptr, 0},
+            {ws.dAp + d * B * E * 16, B, E * 16, E * 16, gd[d]->A_log, nullptr, 0},
+            {ws.dWdtp + d * B * E * R, B, E * R, E * R, gd[d]->dt_proj_w, nullptr, 0},
+            {ws.dbp + d * B * E, B, E, E, gd[d]->dt_proj_b, nullptr, 0}};
+        for (const ColsumSeg& sg : segs) {
+            if (sg.rows <= kColRowsPerBlock) {
+                batch.seg[batch.n++] = sg;
+            } else if (!ok(launch_colsum(sg.in, sg.rows, sg.cols, sg.ld, sg.out, nullptr, ws.tmp, s))) {
+                return FASTVIM_ERR_HIP;
+            }
+        }
     }
+    if (!ok(launch_colsum_batch(batch, s))) return FASTVIM_ERR_HIP;
     if (!ok(launch_bwd_epilogue(g, x, z, dout, p, ws, dx, dz, s))) return FASTVIM_ERR_HIP;
     if (!ok(launch_colsum(ws.dDp, bwd_dd_parts(g), E, E, gr.fwd.D, gr.bwd.D, ws.tmp, s))) return FASTVIM_ERR_HIP;
     return FASTVIM_OK;

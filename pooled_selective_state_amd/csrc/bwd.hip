@@ -41,8 +41,9 @@ __device__ __forceinline__ float sigmoid_f(float q) { return __builtin_amdgcn_rc
 // owning the 16-byte column [c V, c V + V) of E, group g taking the pooled
 // positions p = g, g + G, ...; the G partial sums are added through LDS in a
 // fixed order.  POOL: also pool x into u (else u is the caller's saved copy
-// and x is not read here).
-template <class IO, bool POOL>
+// and x is not read here).  NT: non-temporal loads (the pass reads more than
+// the Infinity Cache holds, so nothing it reads is still there for pass 2).
+template <class IO, bool POOL, bool NT>
 __global__ void __launch_bounds__(1024)
 bwd_pool_dense_kernel(const typename IO::elem* __restrict__ x, const typename IO::elem* __restrict__ z,
                       const typename IO::elem* __restrict__ dout, float* __restrict__ u, float* __restrict__ gs,
@@ -69,9 +70,9 @@ bwd_pool_dense_kernel(const typename IO::elem* __restrict__ x, const typename IO
                 const int64_t p = p0 + (int64_t)i * G;
                 if (p < P) {
                     const int64_t o = off + p * p_stride;
-                    if (POOL) xr[i] = load_raw<false>(x + o);
-                    zr[i] = load_raw<false>(z + o);
-                    dr[i] = load_raw<false>(dout + o);
+                    if (POOL) xr[i] = load_raw<NT>(x + o);
+                    zr[i] = load_raw<NT>(z + o);
+                    dr[i] = load_raw<NT>(dout + o);
                 }
             }
 #pragma unroll
@@ -188,6 +189,7 @@ void pick_groups_bwd(int64_t VE, int64_t n, int* G, int* threads) {
 template <class IO, bool POOL>
 hipError_t bwd_pool_t(const Geom& g, const void* x, const void* z, const void* dout, const BwdWorkspace& ws,
                       hipStream_t st) {
+    constexpr int64_t kMallBytes = 256ll << 20;  // Infinity Cache
     using elem = typename IO::elem;
     const int64_t VE = g.E / IO::V;
     int G, threads;
@@ -202,9 +204,15 @@ hipError_t bwd_pool_t(const Geom& g, const void* x, const void* z, const void* d
     } else {
         const int64_t t_stride = g.axis == FASTVIM_POOL_COLS ? g.w * g.E : g.E;
         const int64_t p_stride = g.axis == FASTVIM_POOL_COLS ? g.E : g.w * g.E;
-        hipLaunchKernelGGL((bwd_pool_dense_kernel<IO, POOL>), dim3((unsigned)(g.B * g.T)), dim3(threads), lds, st,
-                           xe, ze, de, ws.fwd.u, ws.gs, g.T, g.P, (int)VE, G, g.E, g.h * g.w * g.E, t_stride,
-                           p_stride, 1.0f / (float)g.P);
+        const int64_t bytes = (POOL ? 3 : 2) * g.B * g.h * g.w * g.E * (int64_t)sizeof(elem);
+        if (bytes > kMallBytes)
+            hipLaunchKernelGGL((bwd_pool_dense_kernel<IO, POOL, true>), dim3((unsigned)(g.B * g.T)), dim3(threads),
+                               lds, st, xe, ze, de, ws.fwd.u, ws.gs, g.T, g.P, (int)VE, G, g.E, g.h * g.w * g.E,
+                               t_stride, p_stride, 1.0f / (float)g.P);
+        else
+            hipLaunchKernelGGL((bwd_pool_dense_kernel<IO, POOL, false>), dim3((unsigned)(g.B * g.T)), dim3(threads),
+                               lds, st, xe, ze, de, ws.fwd.u, ws.gs, g.T, g.P, (int)VE, G, g.E, g.h * g.w * g.E,
+                               t_stride, p_stride, 1.0f / (float)g.P);
     }
     return hipGetLastError();
 }
@@ -338,14 +346,13 @@ bwd_dwx_kernel(const float* __restrict__ dv, const float* __restrict__ u, float*
 // summing rows g, g + 8, ...; the 8 group sums are added in a fixed order.
 constexpr int kColTile = 32;
 constexpr int kColGroups = 8;
-__global__ void __launch_bounds__(256)
-colsum_kernel(const float* __restrict__ in, int64_t rows, int64_t cols, int64_t ld, int64_t rpb,
-              float* __restrict__ out, float* __restrict__ out2) {
+// Columns [tile * kColTile, + kColTile) of rows [r0, r1), into out[j] (and out2).
+__device__ __forceinline__ void colsum_tile(const float* __restrict__ in, int64_t r0, int64_t r1, int64_t cols,
+                                            int64_t ld, int64_t tile, float* __restrict__ out,
+                                            float* __restrict__ out2) {
     __shared__ float part[kColGroups][kColTile];
     const int cl = threadIdx.x % kColTile, g = threadIdx.x / kColTile;
-    const int64_t j = (int64_t)blockIdx.x * kColTile + cl;
-    const int64_t c = blockIdx.y;
-    const int64_t r0 = c * rpb, r1 = r0 + rpb < rows ? r0 + rpb : rows;
+    const int64_t j = tile * kColTile + cl;
     float s = 0.f;
     if (j < cols)
         for (int64_t i = r0 + g; i < r1; i += kColGroups) s += in[i * ld + j];
@@ -354,9 +361,27 @@ colsum_kernel(const float* __restrict__ in, int64_t rows, int64_t cols, int64_t 
     if (g == 0 && j < cols) {
 #pragma unroll
         for (int k = 1; k < kColGroups; ++k) s += part[k][cl];
-        out[c * cols + j] = s;
-        if (out2) out2[c * cols + j] = s;
+        out[j] = s;
+        if (out2) out2[j] = s;
     }
+}
+
+__global__ void __launch_bounds__(256)
+colsum_kernel(const float* __restrict__ in, int64_t rows, int64_t cols, int64_t ld, int64_t rpb,
+              float* __restrict__ out, float* __restrict__ out2) {
+    const int64_t c = blockIdx.y;
+    const int64_t r0 = c * rpb, r1 = r0 + rpb < rows ? r0 + rpb : rows;
+    colsum_tile(in, r0, r1, cols, ld, blockIdx.x, out + c * cols, out2 ? out2 + c * cols : nullptr);
+}
+
+// Several single-stage column sums in one launch: segment k takes workgroups
+// [blk0[k], blk0[k + 1]), one column tile each, with the arithmetic of
+// colsum_kernel.
+__global__ void __launch_bounds__(256) colsum_batch_kernel(ColsumBatch bt) {
+    int k = 0;
+    while (k + 1 < bt.n && (int64_t)blockIdx.x >= bt.seg[k + 1].blk0) ++k;
+    const ColsumSeg& sg = bt.seg[k];
+    colsum_tile(sg.in, 0, sg.rows, sg.cols, sg.ld, (int64_t)blockIdx.x - sg.blk0, sg.out, sg.out2);
 }
 
 __global__ void __launch_bounds__(256) fill_zero_kernel(float* __restrict__ p, int64_t n) {
@@ -573,6 +598,17 @@ hipError_t launch_colsum(const float* in, int64_t rows, int64_t cols, int64_t ld
                        (int64_t)kColRowsPerBlock, tmp, (float*)nullptr);
     hipLaunchKernelGGL(colsum_kernel, dim3(cb, 1), dim3(256), 0, st, (const float*)tmp, nc, cols, cols, nc, out,
                        out2);
+    return hipGetLastError();
+}
+
+hipError_t launch_colsum_batch(ColsumBatch bt, hipStream_t st) {
+    int64_t blk = 0;
+    for (int k = 0; k < bt.n; ++k) {
+        bt.seg[k].blk0 = blk;
+        blk += (bt.seg[k].cols + kColTile - 1) / kColTile;
+    }
+    if (blk == 0) return hipSuccess;
+    hipLaunchKernelGGL(colsum_batch_kernel, dim3((unsigned)blk), dim3(256), 0, st, bt);
     return hipGetLastError();
 }
 

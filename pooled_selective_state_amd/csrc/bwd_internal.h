@@ -61,6 +61,20 @@ hipError_t launch_bwd_dwx(const Geom& g, const BwdWorkspace& ws, hipStream_t st)
 // (ceil(rows / kColRowsPerBlock) * cols floats).
 hipError_t launch_colsum(const float* in, int64_t rows, int64_t cols, int64_t ld, float* out, float* out2,
                          float* tmp, hipStream_t st);
+// Up to kColsumSegs column sums of at most kColRowsPerBlock rows each, in one
+// launch, with the arithmetic of launch_colsum (blk0 is filled in).
+constexpr int kColsumSegs = 8;
+struct ColsumSeg {
+    const float* in;
+    int64_t rows, cols, ld;
+    float *out, *out2;
+    int64_t blk0;
+};
+struct ColsumBatch {
+    ColsumSeg seg[kColsumSegs];
+    int n;
+};
+hipError_t launch_colsum_batch(ColsumBatch bt, hipStream_t st);
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st);
 hipError_t launch_bwd_epilogue(const Geom& g, const void* x, const void* z, const void* dout,
                                const fastvim_params& p, const BwdWorkspace& ws, void* dx, void* dz, hipStream_t st);
