@@ -291,52 +291,67 @@ bwd_du_kernel(const float* __restrict__ du_f, const float* __restrict__ du_b, co
 }
 
 // --------------------------------------------------------------------- dwx
-// Partial of d x_proj_w over one chunk of kBwdTokChunk pooled tokens:
-//   dWxp[chunk, d, o, e] = sum_{m in chunk} dv[m, d, o] u[m, e]
-// The chunk's dv rows of direction d are staged in LDS with vector loads;
-// lane = channel, wave w takes the outputs o = w * og ... and reads them as
-// LDS broadcasts; the token values of 8 tokens are loaded before their
-// products.
-constexpr int kOG = 24;   // outputs per wave: NX <= 96
-constexpr int kDwxU = 8;  // tokens in flight per lane
+// Partial of d x_proj_w over one chunk of kBwdTokChunk pooled tokens, both
+// directions at once (rows o < NO = 2 NX: [0, NX) forward, [NX, NO) backward):
+//   dWxp[chunk, o, e] = sum_{m in chunk} dv[m, o] u[m, e]
+// an (NO x chunk) . (chunk x E) contraction on the matrix cores
+// (v_mfma_f32_16x16x4f32, fp32 products and sums).  A workgroup takes one
+// chunk and 64 channels.  The chunk's dv rows are staged in LDS transposed,
+// dvt[o][k], zero past the chunk and past NO, so a lane reads its A operand
+// (row o = 16 rt + l % 16, tokens k0 + 4 (l / 16) .. + 3) as one 16-byte
+// vector.  Wave w owns channels e0 + 16 w .. + 15 and every row tile, and
+// loads its B operand (token k0 + 4 (l / 16) + i, channel e0 + 16 w + l % 16)
+// from u; MFMA i of a 16-token step covers token k0 + 4 (l / 16) + i for both
+// operands.  Accumulator register r of lane l holds row 16 rt + 4 (l / 16) + r,
+// channel e0 + 16 w + l % 16.
+// RT row tiles cover NO (instances per dt-rank bound: NO <= 2 (RMAX + 32)).
+constexpr int kDwxLd = kBwdTokChunk + 4;  // LDS row stride of dvt (spreads the rows over the banks)
+template <int RT>
 __global__ void __launch_bounds__(256)
 bwd_dwx_kernel(const float* __restrict__ dv, const float* __restrict__ u, float* __restrict__ dWxp, int64_t M,
-               int64_t E, int NX) {
-    __shared__ float dvs[kBwdTokChunk * 96];  // [token][o], o < NX <= 96
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+               int64_t E, int NO) {
+    __shared__ __attribute__((aligned(16))) float dvt[16 * RT * kDwxLd];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int ri = lane & 15, kk = lane >> 4;
     const int64_t chunk = blockIdx.x;
-    const int64_t e = (int64_t)blockIdx.y * 64 + lane;
-    const int64_t ec = e < E ? e : E - 1;
-    const int d = blockIdx.z;
-    const int og = (NX + 3) / 4;
-    const int o0 = wave * og;
     const int64_t m0 = chunk * kBwdTokChunk;
     const int nm = (int)(m0 + kBwdTokChunk < M ? kBwdTokChunk : M - m0);
-    for (int idx = threadIdx.x; idx < nm * NX; idx += 256) {
-        const int mm = idx / NX, o = idx - mm * NX;
-        dvs[mm * NX + o] = dv[((m0 + mm) * 2 + d) * NX + o];
+    constexpr int rows = 16 * RT;
+    for (int idx = threadIdx.x; idx < rows * kBwdTokChunk; idx += 256) {
+        const int k = idx / rows, o = idx - k * rows;  // consecutive threads read consecutive entries of a dv row
+        dvt[o * kDwxLd + k] = (k < nm && o < NO) ? dv[(m0 + k) * NO + o] : 0.f;
     }
     __syncthreads();
-    float acc[kOG];
+    const int64_t e = (int64_t)blockIdx.y * 64 + wv * 16 + ri;
+    const int64_t ec = e < E ? e : E - 1;
+    f32x4 acc[RT];
 #pragma unroll
-    for (int i = 0; i < kOG; ++i) acc[i] = 0.f;
-    for (int mb = 0; mb < nm; mb += kDwxU) {
-        float uv[kDwxU];
+    for (int rt = 0; rt < RT; ++rt) acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int k0 = 0; k0 < kBwdTokChunk; k0 += 16) {
+        float bv[4];
 #pragma unroll
-        for (int k = 0; k < kDwxU; ++k) uv[k] = mb + k < nm ? u[(m0 + mb + k) * E + ec] : 0.f;
+        for (int i = 0; i < 4; ++i) {
+            const int k = k0 + 4 * kk + i;
+            bv[i] = k < nm ? u[(m0 + k) * E + ec] : 0.f;
+        }
 #pragma unroll
-        for (int k = 0; k < kDwxU; ++k) {
-            const float* dvr = dvs + (mb + k < nm ? mb + k : nm - 1) * NX + o0;  // past the chunk: a zero token value
-#pragma unroll
-            for (int i = 0; i < kOG; ++i)
-                if (i < og && o0 + i < NX) acc[i] = fmaf(dvr[i], uv[k], acc[i]);
+        for (int rt = 0; rt < RT; ++rt) {
+            const f32x4 a4 = *reinterpret_cast<const f32x4*>(dvt + (rt * 16 + ri) * kDwxLd + k0 + 4 * kk);
+            acc[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a4.x, bv[0], acc[rt], 0, 0, 0);
+            acc[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a4.y, bv[1], acc[rt], 0, 0, 0);
+            acc[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a4.z, bv[2], acc[rt], 0, 0, 0);
+            acc[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a4.w, bv[3], acc[rt], 0, 0, 0);
         }
     }
     if (e < E) {
 #pragma unroll
-        for (int i = 0; i < kOG; ++i)
-            if (i < og && o0 + i < NX) dWxp[((chunk * 2 + d) * NX + o0 + i) * E + e] = acc[i];
+        for (int rt = 0; rt < RT; ++rt) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int o = rt * 16 + 4 * kk + r;
+                if (o < NO) dWxp[(chunk * NO + o) * E + e] = acc[rt][r];
+            }
+        }
     }
 }
 
@@ -581,8 +596,14 @@ hipError_t launch_bwd_du(const Geom& g, const fastvim_params& p, const BwdWorksp
 
 hipError_t launch_bwd_dwx(const Geom& g, const BwdWorkspace& ws, hipStream_t st) {
     const int64_t M = g.B * g.T;
-    const dim3 grid((unsigned)ws.MC, (unsigned)((g.E + 63) / 64), 2);
-    hipLaunchKernelGGL(bwd_dwx_kernel, grid, dim3(256), 0, st, ws.dv, ws.fwd.u, ws.dWxp, M, g.E, (int)g.NX);
+    const int NO = (int)(2 * g.NX);
+    const dim3 grid((unsigned)ws.MC, (unsigned)((g.E + 63) / 64));
+    switch (bwd_rmax(g.R)) {  // NO <= 2 (RMAX + 32)
+        case 16: hipLaunchKernelGGL(bwd_dwx_kernel<6>, grid, dim3(256), 0, st, ws.dv, ws.fwd.u, ws.dWxp, M, g.E, NO); break;
+        case 32: hipLaunchKernelGGL(bwd_dwx_kernel<8>, grid, dim3(256), 0, st, ws.dv, ws.fwd.u, ws.dWxp, M, g.E, NO); break;
+        case 48: hipLaunchKernelGGL(bwd_dwx_kernel<10>, grid, dim3(256), 0, st, ws.dv, ws.fwd.u, ws.dWxp, M, g.E, NO); break;
+        default: hipLaunchKernelGGL(bwd_dwx_kernel<12>, grid, dim3(256), 0, st, ws.dv, ws.fwd.u, ws.dWxp, M, g.E, NO); break;
+    }
     return hipGetLastError();
 }
 
