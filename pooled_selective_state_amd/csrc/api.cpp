@@ -259,7 +259,7 @@ int run_bwd(const Geom& g, const void* x, const void* z, const void* dout, const
     if (!ok(launch_bwd_pool(g, x, z, dout, ws, s))) return FASTVIM_ERR_HIP;
     if (!ok(launch_proj(g, x, p, ws.fwd, s))) return FASTVIM_ERR_HIP;
     BwdScanArgs a{ws.fwd.xdbl, ws.fwd.u, ws.gs, p.fwd, p.bwd, ws.fwd.s_f, ws.fwd.s_b, ws.du_f, ws.du_b, ws.dvp,
-                  ws.dAp, ws.dWdtp, ws.dbp, g.B, g.T, g.E, (int)g.R, (int)g.NX, (int)ws.G};
+                  ws.ckpt, ws.dAp, ws.dWdtp, ws.dbp, g.B, g.T, g.E, (int)g.R, (int)g.NX, (int)ws.G};
     if (!ok(launch_scan_bwd(a, s)) || !ok(launch_bwd_dv(g, ws, s)) || !ok(launch_bwd_du(g, p, ws, s)) ||
         !ok(launch_bwd_dwx(g, ws, s)))
         return FASTVIM_ERR_HIP;
@@ -338,6 +338,7 @@ size_t bwd_workspace_layout(const Geom& g, void* base, BwdWorkspace* ws) {
     const size_t o_gs = take(bte), o_dDp = take((size_t)(ND * E) * sizeof(float));
     const size_t o_duf = take(bte), o_dub = take(bte), o_du = take(bte);
     const size_t o_dvp = take((size_t)(2 * B * G * T * S) * sizeof(float));
+    const size_t o_ck = take((size_t)(2 * B * G * (kBwdTMax / 16) * 256 * 4) * sizeof(float));
     const size_t o_dv = take((size_t)(M * 2 * NX) * sizeof(float));
     const size_t o_dAp = take((size_t)(2 * B * E * 16) * sizeof(float));
     const size_t o_dWdtp = take((size_t)(2 * B * E * R) * sizeof(float));
@@ -366,6 +367,7 @@ size_t bwd_workspace_layout(const Geom& g, void* base, BwdWorkspace* ws) {
         ws->du_b = f(o_dub);
         ws->du = f(o_du);
         ws->dvp = f(o_dvp);
+        ws->ckpt = f(o_ck);
         ws->dv = f(o_dv);
         ws->dAp = f(o_dAp);
         ws->dWdtp = f(o_dWdtp);

@@ -21,6 +21,7 @@ struct BwdWorkspace {
     float* du_b;   // (B, T, E) the same, backward direction
     float* du;     // (B, T, E) dL/du, both directions, scan and x_proj
     float* dvp;    // (2, B, G, T, S) channel-group partials of dL/dv, in the scan's LDS row layout
+    float* ckpt;   // (2, B, G, kBwdTMax / 16, 256, 4) scan adjoint: each lane's states entering each chunk
     float* dv;     // (B, T, 2, NX) dL/dv of both directions
     float* dAp;    // (2, B, E, 16) per-image d A_log
     float* dWdtp;  // (2, B, E, R) per-image d dt_proj_w
@@ -39,6 +40,7 @@ struct BwdScanArgs {
     float *s_f, *s_b;     // (B, T, E) recomputed scan outputs
     float *du_f, *du_b;   // (B, T, E)
     float* dvp;           // (2, B, G, T, S)
+    float* ckpt;          // (2, B, G, kBwdTMax / 16, 256, 4)
     float *dAp, *dWdtp, *dbp;
     int64_t B, T, E;
     int R, NX, G;

@@ -20,15 +20,19 @@
 // One 256-thread workgroup takes (image b, channel group g, direction d),
 // with the lane layout of the forward scan: 4 lanes per channel, lane q
 // holding the states n = 4q .. 4q + 3.  All x_proj rows of the sequence are
-// staged in LDS once (the forward scan's row layout, zero-filled past T), and
-// each lane keeps the token values u and adjoint inputs gs of its own steps
-// q + 4j in registers.  Then:
+// staged in LDS once (the forward scan's row layout, zero-filled past T); a
+// lane loads the token values u and adjoint inputs gs of its own steps
+// q + 4j one chunk ahead of their use.  Then:
 //   1. a forward sweep (the forward scan's own chunk code) recomputes the
-//      states, writes s^d (needed by the output adjoint) and keeps the state
-//      entering every chunk of kChunk steps as a register checkpoint;
-//   2. a reverse sweep over the chunks, last first, recomputes the chunk's
-//      step sizes and its kChunk states from the checkpoint, then walks the
-//      chunk's steps backwards carrying lambda.
+//      states, writes s^d (needed by the output adjoint) and stores the state
+//      entering every chunk of kChunk steps to the lane's own checkpoint
+//      region of the workspace (L2-resident until the reverse sweep);
+//   2. a reverse sweep over the chunks, last first, reads the chunk's
+//      checkpoint (one chunk ahead), recomputes the chunk's step sizes and its
+//      kChunk states from it, then walks the chunk's steps backwards carrying
+//      lambda.
+// The sweeps are bound by instruction issue (three exp2 per state and step:
+// forward, per chunk and per group of 4 steps), not by memory or occupancy.
 // Sums over n stay inside a quad (DPP).  Sums over channels e (dB, dC and
 // ddelta, needed per step) are taken over the 4 channels of each DPP row of
 // 16 lanes with two row rotations, written by the row's first quad into an
@@ -149,64 +153,46 @@ __global__ void __launch_bounds__(kBwdThreads) scan_bwd_kernel(BwdScanArgs a) {
             }
         }
     }
-    // token values and adjoint inputs of the lane's own steps (zero past T and
-    // for channels past E, which then contribute nothing to the channel sums)
-    float uall[kBwdCM][kJ], gall[kBwdCM][kJ];
-    {
-        const float* ub = a.u + b * T * E + ec;
-        const float* gb = a.gs + b * T * E + ec;
+    // Token values and adjoint inputs of the lane's own steps of chunk c (zero
+    // past T and for channels past E, which then contribute nothing to the
+    // channel sums), loaded one chunk ahead of their use.
+    const float* ub = a.u + b * T * E + ec;
+    const float* gb = a.gs + b * T * E + ec;
+    auto load_steps = [&](const float* src, int c, float (&v)[kJ]) {
 #pragma unroll
-        for (int c = 0; c < kBwdCM; ++c)
-#pragma unroll
-            for (int j = 0; j < kJ; ++j) {
-                const int tj = c * kChunk + q + 4 * j;
-                const int t = dir ? T - 1 - tj : tj;
-                const bool in = valid && tj < T;
-                uall[c][j] = in ? ub[(int64_t)t * E] : 0.f;
-                gall[c][j] = in ? gb[(int64_t)t * E] : 0.f;
-            }
-    }
+        for (int j = 0; j < kJ; ++j) {
+            const int tj = c * kChunk + q + 4 * j;
+            const int t = dir ? T - 1 - tj : tj;
+            v[j] = (valid && tj < T) ? src[(int64_t)t * E] : 0.f;
+        }
+    };
+    // The lane's states entering chunk c, written by the forward sweep and
+    // read back by the reverse sweep (its own region of the workspace).
+    float* ck = a.ckpt + (((int64_t)dir * a.B + b) * a.G + gi) * kBwdCM * kBwdThreads * 4 + tid * 4;
+    float un[kJ];
+    load_steps(ub, 0, un);
     __syncthreads();
 
-    // 1. forward sweep: outputs s^d and the state entering every chunk.
-    // uall / gall rotate left one chunk per step and hck is a shift register,
-    // so every register index is a constant.
+    // 1. forward sweep: outputs s^d and the state entering every chunk
     ScanArgs sa{};
     sa.T = T;
-    float hck[kBwdCM][kNs];
 #pragma unroll 1
     for (int c = 0; c < nch; ++c) {
+        *reinterpret_cast<f32x4*>(ck + c * kBwdThreads * 4) = f32x4{L.hs[0], L.hs[1], L.hs[2], L.hs[3]};
+        float ucur[kJ];
 #pragma unroll
-        for (int k = 0; k + 1 < kBwdCM; ++k)
-#pragma unroll
-            for (int n = 0; n < kNs; ++n) hck[k][n] = hck[k + 1][n];
-#pragma unroll
-        for (int n = 0; n < kNs; ++n) hck[kBwdCM - 1][n] = L.hs[n];
-        float ucur[kJ], u0[kJ], g0[kJ];
-#pragma unroll
-        for (int j = 0; j < kJ; ++j) {
-            ucur[j] = u0[j] = uall[0][j];
-            g0[j] = gall[0][j];
-        }
-#pragma unroll
-        for (int k = 0; k + 1 < kBwdCM; ++k)
-#pragma unroll
-            for (int j = 0; j < kJ; ++j) {
-                uall[k][j] = uall[k + 1][j];
-                gall[k][j] = gall[k + 1][j];
-            }
-#pragma unroll
-        for (int j = 0; j < kJ; ++j) {
-            uall[kBwdCM - 1][j] = u0[j];
-            gall[kBwdCM - 1][j] = g0[j];
-        }
+        for (int j = 0; j < kJ; ++j) ucur[j] = un[j];
+        if (c + 1 < nch) load_steps(ub, c + 1, un);
         scan_chunk<RMAX, false>(sa, L, rows + c * kChunk * S, ucur, (int64_t)c * kChunk);
     }
-    // After nch left rotations, chunk c sits at index c - nch + kBwdCM, so the
-    // last chunk is at kBwdCM - 1; the reverse sweep rotates right.
 
     // 2. reverse sweep
     float carry[kNs], dA[kNs], dW[kWQ], db = 0.f;
+    float gn[kJ];
+    f32x4 hn;
+    load_steps(ub, nch - 1, un);
+    load_steps(gb, nch - 1, gn);
+    hn = *reinterpret_cast<const f32x4*>(ck + (nch - 1) * kBwdThreads * 4);
 #pragma unroll
     for (int n = 0; n < kNs; ++n) carry[n] = dA[n] = 0.f;
 #pragma unroll
@@ -220,28 +206,17 @@ __global__ void __launch_bounds__(kBwdThreads) scan_bwd_kernel(BwdScanArgs a) {
     for (int c = nch - 1; c >= 0; --c) {
         const float* dr = rows + c * kChunk * S;
         const int base = c * kChunk;
-        float uc[kJ], gc[kJ], h0[kNs];
+        float uc[kJ], gc[kJ];
 #pragma unroll
         for (int j = 0; j < kJ; ++j) {
-            uc[j] = uall[kBwdCM - 1][j];
-            gc[j] = gall[kBwdCM - 1][j];
+            uc[j] = un[j];
+            gc[j] = gn[j];
         }
-#pragma unroll
-        for (int n = 0; n < kNs; ++n) h0[n] = hck[kBwdCM - 1][n];
-#pragma unroll
-        for (int k = kBwdCM - 1; k > 0; --k) {
-#pragma unroll
-            for (int j = 0; j < kJ; ++j) {
-                uall[k][j] = uall[k - 1][j];
-                gall[k][j] = gall[k - 1][j];
-            }
-#pragma unroll
-            for (int n = 0; n < kNs; ++n) hck[k][n] = hck[k - 1][n];
-        }
-#pragma unroll
-        for (int j = 0; j < kJ; ++j) {
-            uall[0][j] = uc[j];
-            gall[0][j] = gc[j];
+        const float h0[kNs] = {hn.x, hn.y, hn.z, hn.w};
+        if (c > 0) {  // the next (earlier) chunk's inputs and state, while this one computes
+            load_steps(ub, c - 1, un);
+            load_steps(gb, c - 1, gn);
+            hn = *reinterpret_cast<const f32x4*>(ck + (c - 1) * kBwdThreads * 4);
         }
         // step sizes (and sigmoid of their pre-activation) of the own steps
         float qv[kJ], dl[kJ], sg[kJ];
