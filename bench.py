@@ -360,6 +360,13 @@ def main():
             l_proj, _ = time_steps(lambda: lcall.stage(P.STAGE_PROJ, stream), reps, stream)
             lb[name] = {"layer_ms": l_ms, "scan_ms": l_scan, "proj_ms": l_proj}
             del lcall
+        # the pooled layer's default is the single launch; its stage kernels for comparison
+        lcall = P.SSMCall(x, z, prm, P.POOL_COLS, out=call.out, flags=P.FLAG_LOCAL_BWD | P.FLAG_STAGED)
+        lcall.run(stream)
+        lb["pooled"]["stage_kernels_ms"], _ = time_steps(lambda: lcall.run(stream), n, stream)
+        lb["pooled"]["path"] = "single launch"
+        lb["pooled"]["layer_vs_bidirectional"] = lb["pooled"]["layer_ms"] / ms
+        del lcall
         lb["unpooled"]["scan_vs_bidirectional"] = lb["unpooled"]["scan_ms"] / u_scan
         lb["unpooled"]["layer_vs_bidirectional"] = lb["unpooled"]["layer_ms"] / u_ms
         lb["window"] = P.LOCAL_WINDOW

@@ -195,9 +195,12 @@ typedef struct fastvim_params {
  * t mod FASTVIM_LOCAL_WINDOW = FASTVIM_LOCAL_WINDOW - 1); the layer is
  *   out = (s_fwd + s_bwd + (D_fwd + D_bwd) x) silu(z)
  * as before.  Of params.bwd only D is read (the other four may be NULL); pass
- * D_bwd = 0 for a single skip.  Any pooled, masked or unpooled layer, as
- * stage kernels (FASTVIM_FLAG_FUSED is ignored); combines with the other
- * options.  The backward pass returns FASTVIM_ERR_UNSUPPORTED for it. */
+ * D_bwd = 0 for a single skip.  Any pooled, masked or unpooled layer, and
+ * combines with the other options.  Dense pooled layers take the single
+ * launch under the same rules as without it (the size rule by default,
+ * FASTVIM_FLAG_FUSED to force it), except with FASTVIM_FLAG_POST_NORM; other
+ * layers run as stage kernels.  The backward pass returns
+ * FASTVIM_ERR_UNSUPPORTED for it. */
 #define FASTVIM_FLAG_LOCAL_BWD 16u
 #define FASTVIM_LOCAL_WINDOW 16
 

@@ -406,12 +406,12 @@ int fastvim_ssm_fwd(const void* x, const void* z, const fastvim_params* params, 
     if (launch_zero_sync(ws, sync_words(g), s) != hipSuccess) return FASTVIM_ERR_HIP;
     const fastvim_params q = effective_params(*params);
     const bool norm = (params->flags & FASTVIM_FLAG_POST_NORM) != 0;
-    const bool single = !(params->flags & (FASTVIM_FLAG_CONV | FASTVIM_FLAG_LOCAL_BWD)) &&
+    const bool local = (params->flags & FASTVIM_FLAG_LOCAL_BWD) != 0;
+    const bool single = !(params->flags & FASTVIM_FLAG_CONV) &&
                         ((params->flags & FASTVIM_FLAG_FUSED)
-                             ? fused_supported(g, norm)
-                             : !(params->flags & FASTVIM_FLAG_STAGED) && fused_preferred(g, norm));
-    if (single)
-        return launch_fused(g, x, z, *params, ws, out, s) == hipSuccess ? FASTVIM_OK : FASTVIM_ERR_HIP;
+                             ? fused_supported(g, norm, local)
+                             : !(params->flags & FASTVIM_FLAG_STAGED) && fused_preferred(g, norm, local));
+    if (single) return launch_fused(g, x, z, q, ws, out, s) == hipSuccess ? FASTVIM_OK : FASTVIM_ERR_HIP;
     for (int stage = FASTVIM_STAGE_ROWS; stage <= FASTVIM_STAGE_EPILOGUE; ++stage) {
         st = run_stage(stage, g, x, z, q, mask_idx, out, ws, s);
         if (st) return st;

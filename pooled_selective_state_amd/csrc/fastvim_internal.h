@@ -56,8 +56,8 @@ hipError_t launch_epilogue_norm(const Geom& g, const void* x, const void* z, con
                                 const Workspace& ws, void* out, hipStream_t st);
 // Single-launch dense pooled layer (fused.hip).
 // norm: with the post-SSM LayerNorm (FASTVIM_FLAG_POST_NORM).
-bool fused_supported(const Geom& g, bool norm);
-bool fused_preferred(const Geom& g, bool norm);  // the default path for this geometry is the single launch
+bool fused_supported(const Geom& g, bool norm, bool local);
+bool fused_preferred(const Geom& g, bool norm, bool local);  // the default path for this geometry is the single launch
 hipError_t launch_fused(const Geom& g, const void* x, const void* z, const fastvim_params& p, const Workspace& ws,
                         void* out, hipStream_t st);
 hipError_t launch_zero_sync(const Workspace& ws, int64_t n, hipStream_t st);

@@ -20,7 +20,9 @@
 //   A(b, k)  pool scan positions [k*RG, k*RG + RG) of image b and project the
 //            pooled tokens (both directions); count it in rowsDone[b];
 //   S(b, k)  once rowsDone[b] == nA, scan channels [64k, 64k + 64) of image b
-//            in both directions (scan_core.h); count it in scanDone[b];
+//            in both directions (scan_core.h), or with LBMamba's local
+//            backward scan, channels [128k, 128k + 128) forward with each
+//            chunk's local backward scan; count it in scanDone[b];
 //   E(b, k)  once scanDone[b] == nS, repeat + skip + gate a block of image
 //            b: grid rows [k*RE, k*RE + RE) (COLS), or RE rows x CJ columns
 //            with the block's scan rows staged in LDS (ROWS); with the
@@ -457,7 +459,7 @@ __device__ void item_epilogue_norm(const FusedArgs& a, int64_t b, int k, float* 
 }
 
 // ---------------------------------------------------------------- kernel
-template <class IO, bool COLS, int RMAX, bool NORM>
+template <class IO, bool COLS, int RMAX, bool NORM, bool LOCAL>
 __global__ void __launch_bounds__(kFT) fused_layer_kernel(FusedArgs a) {
     __shared__ FusedSmem sm;
     __shared__ unsigned s_ticket;
@@ -486,7 +488,8 @@ __global__ void __launch_bounds__(kFT) fused_layer_kernel(FusedArgs a) {
             __syncthreads();
             __builtin_amdgcn_s_setprio(2);  // the scan is on the critical path of its image
             ScanArgs sa{a.xdbl, a.pf, a.pb, a.s_f, a.s_b, a.T, a.E, a.R, a.NX};
-            scan_tile_resident<RMAX, true>(sa, USrcPooled{a.u, a.T, a.E}, bs, (int64_t)r * kScanCh, sm.scan);
+            scan_tile_resident<RMAX, true, USrcPooled, LOCAL>(sa, USrcPooled{a.u, a.T, a.E}, bs,
+                                                              (int64_t)r * (LOCAL ? 2 : 1) * kScanCh, sm.scan);
             __builtin_amdgcn_s_setprio(0);
             publish(&a.sync[2 + a.B + bs]);
             return;
@@ -509,9 +512,10 @@ int env_int(const char* name, int dflt) {
 }
 
 // Item sizes and ticket layout for a geometry; false if not covered.  norm:
-// with the post-SSM LayerNorm (E items of whole grid rows, E / V <= 128).
-bool plan(const Geom& g, FusedArgs* a, bool norm) {
-    if (!g.pooled || g.masked || g.B < 1) return false;
+// with the post-SSM LayerNorm (E items of whole grid rows, E / V <= 128);
+// local: with LBMamba's local backward scan (not with the norm).
+bool plan(const Geom& g, FusedArgs* a, bool norm, bool local) {
+    if (!g.pooled || g.masked || g.B < 1 || (norm && local)) return false;
     // the scan items hold a whole sequence's x_proj rows in LDS
     const int64_t tmax = g.R <= 16 ? resident_tmax<16>() : g.R <= 32 ? resident_tmax<32>() : resident_tmax<64>();
     if (g.T > tmax) return false;
@@ -551,7 +555,8 @@ bool plan(const Geom& g, FusedArgs* a, bool norm) {
     a->R = (int)g.R; a->NX = (int)g.NX; a->axis = g.axis;
     a->VE = (int)VE; a->G = G; a->KS = KS; a->RG = (int)RG; a->RE = (int)RE; a->CJ = (int)CJ;
     a->nA = (int)((g.T + RG - 1) / RG);
-    a->nS = (int)((g.E + kScanCh - 1) / kScanCh);
+    const int64_t sch = (local ? 2 : 1) * kScanCh;  // channels per scan item
+    a->nS = (int)((g.E + sch - 1) / sch);
     a->nE = (int)(((g.h + RE - 1) / RE) * ((g.w + CJ - 1) / CJ));
     // Lags.  Between the A items of image b (slot b) and its E items (slot
     // b + LE) the pipeline reads LE other images' x with allocating loads;
@@ -595,36 +600,38 @@ bool plan(const Geom& g, FusedArgs* a, bool norm) {
     return a->niv > 0 && a->total < (int64_t)UINT32_MAX;
 }
 
-template <class IO, int RMAX, bool NORM>
+template <class IO, int RMAX, bool NORM, bool LOCAL>
 hipError_t fused_launch_n(const FusedArgs& a, hipStream_t st) {
     if (a.axis == FASTVIM_POOL_COLS)
-        hipLaunchKernelGGL((fused_layer_kernel<IO, true, RMAX, NORM>), dim3((unsigned)a.total), dim3(kFT), 0, st, a);
+        hipLaunchKernelGGL((fused_layer_kernel<IO, true, RMAX, NORM, LOCAL>), dim3((unsigned)a.total), dim3(kFT), 0,
+                           st, a);
     else
-        hipLaunchKernelGGL((fused_layer_kernel<IO, false, RMAX, NORM>), dim3((unsigned)a.total), dim3(kFT), 0, st,
-                           a);
+        hipLaunchKernelGGL((fused_layer_kernel<IO, false, RMAX, NORM, LOCAL>), dim3((unsigned)a.total), dim3(kFT), 0,
+                           st, a);
     return hipGetLastError();
 }
 
 template <class IO, int RMAX>
-hipError_t fused_launch_r(const FusedArgs& a, hipStream_t st) {
-    return a.ln_w ? fused_launch_n<IO, RMAX, true>(a, st) : fused_launch_n<IO, RMAX, false>(a, st);
+hipError_t fused_launch_r(const FusedArgs& a, hipStream_t st, bool local) {
+    if (a.ln_w) return fused_launch_n<IO, RMAX, true, false>(a, st);
+    return local ? fused_launch_n<IO, RMAX, false, true>(a, st) : fused_launch_n<IO, RMAX, false, false>(a, st);
 }
 
 template <class IO>
-hipError_t fused_launch_io(const FusedArgs& a, hipStream_t st) {
-    if (a.R <= 16) return fused_launch_r<IO, 16>(a, st);
-    if (a.R <= 32) return fused_launch_r<IO, 32>(a, st);
-    return fused_launch_r<IO, 64>(a, st);
+hipError_t fused_launch_io(const FusedArgs& a, hipStream_t st, bool local) {
+    if (a.R <= 16) return fused_launch_r<IO, 16>(a, st, local);
+    if (a.R <= 32) return fused_launch_r<IO, 32>(a, st, local);
+    return fused_launch_r<IO, 64>(a, st, local);
 }
 
 }  // namespace
 
-bool fused_supported(const Geom& g, bool norm) {
+bool fused_supported(const Geom& g, bool norm, bool local) {
     FusedArgs a;
-    return plan(g, &a, norm);
+    return plan(g, &a, norm, local);
 }
 
-bool fused_preferred(const Geom& g, bool norm) {
+bool fused_preferred(const Geom& g, bool norm, bool local) {
     // The pipeline's fixed costs (scan latency per image, fill and drain)
     // pay off once an image's x is several MB: measured faster than the stage
     // kernels at 2048^2 (25 MB fp32, 12.6 MB bf16), slower at 1024^2 (6.3 MB)
@@ -634,7 +641,7 @@ bool fused_preferred(const Geom& g, bool norm) {
     // staged in LDS) is faster.
     const int64_t esz = g.io == FASTVIM_BF16 ? 2 : 4;
     if (norm && g.axis != FASTVIM_POOL_COLS) return false;
-    return g.h * g.w * g.E * esz >= (8ll << 20) && fused_supported(g, norm);
+    return g.h * g.w * g.E * esz >= (8ll << 20) && fused_supported(g, norm, local);
 }
 
 hipError_t launch_zero_sync(const Workspace& ws, int64_t n, hipStream_t st) {
@@ -646,7 +653,8 @@ hipError_t launch_fused(const Geom& g, const void* x, const void* z, const fastv
                         void* out, hipStream_t st) {
     FusedArgs a;
     const bool norm = (p.flags & FASTVIM_FLAG_POST_NORM) != 0;
-    if (!plan(g, &a, norm)) return hipErrorInvalidValue;
+    const bool local = (p.flags & FASTVIM_FLAG_LOCAL_BWD) != 0;
+    if (!plan(g, &a, norm, local)) return hipErrorInvalidValue;
     a.x = x; a.z = z; a.out = out;
     a.pf = p.fwd; a.pb = p.bwd;
     a.ln_w = norm ? p.ln_weight : nullptr;
@@ -654,7 +662,7 @@ hipError_t launch_fused(const Geom& g, const void* x, const void* z, const fastv
     a.ln_eps = norm ? p.ln_eps : 0.f;
     a.u = ws.u; a.xdbl = ws.xdbl; a.s_f = ws.s_f; a.s_b = ws.s_b;
     a.sync = ws.sync;
-    return g.io == FASTVIM_BF16 ? fused_launch_io<IoBf16>(a, st) : fused_launch_io<IoF32>(a, st);
+    return g.io == FASTVIM_BF16 ? fused_launch_io<IoBf16>(a, st, local) : fused_launch_io<IoF32>(a, st, local);
 }
 
 }  // namespace fastvim

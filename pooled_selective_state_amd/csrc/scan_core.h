@@ -254,15 +254,18 @@ __device__ __forceinline__ void scan_step_preact(const ScanLane<RMAX>& L, const 
 // LBMamba's local backward scan over the same kChunk steps, last first, from
 // a zero state -- the window of kChunk steps aligned at t = 0 -- and stores
 // it to s_bwd.  Step t of that scan decays by the same exp(Delta_t A) as step
-// t of the forward scan, so the chunk's decays are kept in registers and the
-// local scan needs no exponential and no second step-size pass.
-template <int RMAX, bool WRITE_THROUGH, bool LOCAL = false>
+// t of the forward scan.  KEEP_DECAYS: the chunk's decays are kept in
+// registers (64 more per lane) and the local scan needs no exponential;
+// otherwise it keeps the step sizes and recomputes them (where occupancy
+// matters more than the exponentials).  Neither needs a second step-size pass.
+template <int RMAX, bool WRITE_THROUGH, bool LOCAL = false, bool KEEP_DECAYS = true>
 __device__ __forceinline__ void scan_chunk(const ScanArgs& a, ScanLane<RMAX>& L, const float* dr,
                                            const float (&ucur)[kJ], int64_t base) {
     constexpr int S = row_stride_lds<RMAX>();
+    constexpr bool kKeep = LOCAL && KEEP_DECAYS;
     const int64_t T = a.T;
-    float dl[kJ], du[kJ], du0[kJ];
-    float aS[LOCAL ? kChunk : 1][kNs];  // decays of the chunk's steps (LOCAL)
+    float dl[kJ], du[kJ], du0[kJ], dl0[kJ];
+    float aS[kKeep ? kChunk : 1][kNs];  // decays of the chunk's steps (LOCAL, KEEP_DECAYS)
     {
         float qv[kJ];
         scan_step_preact<RMAX>(L, dr, qv);
@@ -273,6 +276,7 @@ __device__ __forceinline__ void scan_chunk(const ScanArgs& a, ScanLane<RMAX>& L,
             dl[j] = in ? d : 0.f;
             du[j] = in ? d * ucur[j] : 0.f;
             du0[j] = du[j];
+            dl0[j] = dl[j];
         }
     }
     // the recurrence, four steps (one per quad lane's step size) at a time;
@@ -309,7 +313,7 @@ __device__ __forceinline__ void scan_chunk(const ScanArgs& a, ScanLane<RMAX>& L,
 #pragma unroll
             for (int n = 0; n < kNs; ++n) {
                 const float dA = __builtin_amdgcn_exp2f(dlt * L.A2[n]);
-                if (LOCAL) aS[LOCAL ? s : 0][n] = dA;
+                if (kKeep) aS[kKeep ? s : 0][n] = dA;
                 L.hs[n] = fmaf(dA, L.hs[n], dus * bt[n]);
                 part = fmaf(ct[n], L.hs[n], part);
             }
@@ -340,19 +344,27 @@ __device__ __forceinline__ void scan_chunk(const ScanArgs& a, ScanLane<RMAX>& L,
                 const int s = 4 * k + m;
                 const float dus = m == 0 ? quad_bcast<0>(du0[k]) : m == 1 ? quad_bcast<1>(du0[k])
                                 : m == 2 ? quad_bcast<2>(du0[k]) : quad_bcast<3>(du0[k]);
+                const float dlt = kKeep ? 0.f
+                                : m == 0 ? quad_bcast<0>(dl0[k]) : m == 1 ? quad_bcast<1>(dl0[k])
+                                : m == 2 ? quad_bcast<2>(dl0[k]) : quad_bcast<3>(dl0[k]);
                 const f32x4 b4 = *reinterpret_cast<const f32x4*>(lrows + s * S);
                 const f32x4 c4 = *reinterpret_cast<const f32x4*>(lrows + s * S + 16);
                 const float bt[kNs] = {b4.x, b4.y, b4.z, b4.w}, ct[kNs] = {c4.x, c4.y, c4.z, c4.w};
                 float part = 0.f;
 #pragma unroll
                 for (int n = 0; n < kNs; ++n) {
-                    hl[n] = fmaf(aS[LOCAL ? s : 0][n], hl[n], dus * bt[n]);
+                    const float dA = kKeep ? aS[kKeep ? s : 0][n] : __builtin_amdgcn_exp2f(dlt * L.A2[n]);
+                    hl[n] = fmaf(dA, hl[n], dus * bt[n]);
                     part = fmaf(ct[n], hl[n], part);
                 }
                 part = seq_sum(part);
                 keep = (m == L.q) ? part : keep;
             }
-            if (L.valid && base + 4 * k + L.q < T) L.sqb[(base + 4 * k) * a.E] = keep;
+            if (L.valid && base + 4 * k + L.q < T) {
+                float* dst = L.sqb + (base + 4 * k) * a.E;
+                if (WRITE_THROUGH) __hip_atomic_store(dst, keep, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                else *dst = keep;
+            }
         }
     }
 }
@@ -426,7 +438,11 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, const USrc& usrc, i
 // T - 1 - t (backward).  Each lane holds the token values of its steps
 // q + 4j for the whole sequence (resident_tmax / 4 registers), rotated one
 // chunk at a time so register indices stay constant.  One barrier in all.
-template <int RMAX, bool WRITE_THROUGH, class USrc>
+// LOCAL: every lane scans forward, the workgroup covering 2 kScanCh channels
+// from e0, and each chunk's local backward scan follows it (scan_chunk, its
+// decays recomputed: this variant serves the single-launch kernel, whose
+// streaming items share the scan items' register budget).
+template <int RMAX, bool WRITE_THROUGH, class USrc, bool LOCAL = false>
 __device__ __forceinline__ void scan_tile_resident(const ScanArgs& a, const USrc& usrc, int64_t b, int64_t e0,
                                                    ScanSmem& sm) {
     constexpr int S = row_stride_lds<RMAX>();
@@ -438,7 +454,7 @@ __device__ __forceinline__ void scan_tile_resident(const ScanArgs& a, const USrc
     static_assert(2 * TM % kRowsPerPass == 0 && TM % kChunk == 0, "whole passes and chunks");
     ScanLane<RMAX> L;
     int64_t ec;
-    scan_lane_setup<RMAX>(a, b, e0, L, ec);
+    scan_lane_setup<RMAX, LOCAL>(a, b, e0, L, ec);
     const int tid = threadIdx.x;
     const int NX = a.NX;
     const int64_t T = a.T;
@@ -489,7 +505,7 @@ __device__ __forceinline__ void scan_tile_resident(const ScanArgs& a, const USrc
         for (int k = 0; k + 1 < kCM; ++k)
 #pragma unroll
             for (int j = 0; j < kJ; ++j) uall[k][j] = uall[k + 1][j];
-        scan_chunk<RMAX, WRITE_THROUGH>(a, L, dr + c * kChunk * S, ucur, (int64_t)c * kChunk);
+        scan_chunk<RMAX, WRITE_THROUGH, LOCAL, false>(a, L, dr + c * kChunk * S, ucur, (int64_t)c * kChunk);
     }
 }
 
