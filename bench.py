@@ -18,7 +18,9 @@ Reported besides images/s:
                 HBM traffic the hardware counters recorded for it, when the
                 recorded counter summary belongs to the current kernel source;
   cpu_baseline  the fp64 CPU oracle on the same host arrays, cycled over the
-                batch for at least --cpu-seconds;
+                batch for at least --cpu-seconds (with the extras, also the
+                oracle on one thread for the small workloads and on the
+                unpooled layer, extrapolated from 8 images);
   extras        the stage-kernel path and its per-stage times, the other
                 pooling axis, the layer with the post-SSM LayerNorm, the layer
                 with the producer Conv1D fused, the backward pass, the
@@ -140,6 +142,51 @@ def cpu_baseline(x, z, prm, axis, seconds):
     return {"value": done / dt, "unit": "images/s", "cores": min(threads, chunk), "kind": "oracle",
             "sample": "%d images (the batch of %d cycled in chunks of %d) of the same seeded host arrays, whole "
                       "layer in fp64, %.1f s wall; CPU %s" % (done, B, chunk, dt, cpu_model())}
+
+
+def oracle_timings(C, wl_big, seconds=1.0):
+    """The fp64 oracle on the other workloads: one thread on the small ones
+    (whole layer, the chain's two blocks in turn), and the unpooled 2048^2
+    layer on 8 images with all threads, extrapolated to the batch (linear in
+    B: images are independent)."""
+    import oracle
+    from pooled_selective_state_amd.inputs import draw_workload
+    out = {}
+    full = oracle.max_threads()
+
+    def rate(fn, n_img):
+        done, t0 = 0, time.perf_counter()
+        while True:
+            fn()
+            done += n_img
+            dt = time.perf_counter() - t0
+            if dt >= seconds:
+                return done / dt
+    try:
+        oracle.set_threads(1)
+        for cfg, batch in ((C.TINY, None), (C.SHORT_224_S, None), (C.CHAIN_1024, 8), (C.MASKED_B, 32)):
+            wl = draw_workload(cfg, batch=batch)
+            x, zs, ps, idx = wl["x"], wl["z"], wl["params"], wl["idx"]
+            hw = (cfg.h, cfg.w) if cfg.masked else None
+
+            def run():
+                y = x
+                for k, axis in enumerate(cfg.axes):
+                    y = oracle.layer(y, zs[k], ps[k]["fwd"], ps[k]["bwd"], axis, idx=idx, hw=hw).astype(np.float32)
+            out[cfg.name] = {"images_per_s": rate(run, wl["B"]), "threads": 1,
+                             "sample": "%d images, %s" % (wl["B"], "two blocks" if len(cfg.axes) > 1 else "one layer")}
+        oracle.set_threads(full)
+        sel = slice(0, 8)
+        t0 = time.perf_counter()
+        oracle.layer(wl_big["x"][sel], wl_big["z"][0][sel], wl_big["params"][0]["fwd"], wl_big["params"][0]["bwd"], 2)
+        dt = time.perf_counter() - t0
+        B = wl_big["x"].shape[0]
+        out["unpooled_2048"] = {"images_per_s": 8 / dt, "threads": min(full, 8), "seconds_for_8": dt,
+                                "batch_seconds_extrapolated": dt * B / 8,
+                                "sample": "8 of %d images, T = 16384, extrapolated (linear in B)" % B}
+    finally:
+        oracle.set_threads(full)
+    return out
 
 
 def small_configs(P, C, torch, stream, nsets=4, calls=200):
@@ -408,6 +455,9 @@ def main():
     if not args.no_cpu_baseline:
         log("timing the CPU oracle (>= %.0f s)" % args.cpu_seconds)
         result["cpu_baseline"] = cpu_baseline(wl["x"], wl["z"][0], wl["params"][0], 0, args.cpu_seconds)
+        if not args.no_extras:
+            log("timing the CPU oracle on the other workloads")
+            result["extras"]["oracle_timings"] = oracle_timings(C, wl)
 
     print(json.dumps(result), flush=True)
 

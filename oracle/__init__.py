@@ -78,6 +78,8 @@ class Oracle:
         lib = ctypes.CDLL(path)
         i64, vp, ci = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
         lib.fvo_max_threads.restype = ci
+        lib.fvo_set_threads.argtypes = [ci]
+        lib.fvo_set_threads.restype = None
         lib.fvo_pool_dense.argtypes = [vp, i64, i64, i64, i64, ci, vp]
         lib.fvo_pool_dense.restype = ci
         lib.fvo_mask_rows.argtypes = [vp, i64, i64, i64, i64, ci, vp]
@@ -111,6 +113,10 @@ class Oracle:
     def max_threads(self) -> int:
         """OpenMP threads the oracle's image-parallel loops use."""
         return int(self._lib.fvo_max_threads())
+
+    def set_threads(self, n: int) -> None:
+        """Threads for later calls (timing only: results do not depend on it)."""
+        self._lib.fvo_set_threads(int(n))
 
     def pool_dense(self, x, axis):
         """u (B,T,E) from a dense grid x (B,h,w,E)."""
@@ -329,6 +335,10 @@ def get() -> Oracle:
 
 def max_threads():
     return get().max_threads()
+
+
+def set_threads(n):
+    get().set_threads(n)
 
 
 def pool_dense(x, axis):

@@ -72,6 +72,17 @@ int fvo_max_threads(void)
 #endif
 }
 
+/* Threads for the following calls' image-parallel loops (timing only; the
+ * results do not depend on it: images are independent). */
+void fvo_set_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* Scan length T and pooled-axis length P for a dense grid. */
 static void seq_shape(int axis, int64_t h, int64_t w, int64_t *T, int64_t *P)
 {
