@@ -105,6 +105,7 @@ class Oracle:
             vp, vp, vp, ctypes.POINTER(_Dir), ctypes.POINTER(_Dir),
             i64, i64, i64, i64, i64, i64, i64, ci, vp,
             vp, vp, ctypes.POINTER(_DirGrad), ctypes.POINTER(_DirGrad), ctypes.POINTER(_BwdStages),
+            vp, vp, ctypes.c_double, vp, vp,
         ]
         lib.fvo_layer_bwd.restype = ci
         self._lib = lib
@@ -263,13 +264,19 @@ class Oracle:
             return out
         return {"out": out, "u": u, "rows": rows, "fwd": st["fwd"], "bwd": st["bwd"]}
 
-    def layer_bwd(self, x, z, dout, fwd, bwd, axis, idx=None, hw=None, stages=False):
-        """Gradients of sum(dout * layer(x, z, ...)) (no LayerNorm).  Arguments as
-        layer(); dout is shaped like x.  Returns a dict with dx, dz (fp64, shaped
-        like x) and "fwd" / "bwd" dicts of parameter gradients keyed like the
-        parameters; with stages=True also gs, du (B,T,E) and dv_fwd, dv_bwd
-        (B,T,NX)."""
+    def layer_bwd(self, x, z, dout, fwd, bwd, axis, idx=None, hw=None, stages=False, ln=None):
+        """Gradients of sum(dout * layer(x, z, ...)).  Arguments as layer();
+        dout is shaped like x.  Returns a dict with dx, dz (fp64, shaped like
+        x) and "fwd" / "bwd" dicts of parameter gradients keyed like the
+        parameters; with ln (as in layer()) also "ln": {"weight", "bias"}, the
+        LayerNorm's gradients; with stages=True also gs (dL/ds, which is dL/dy
+        of the LayerNorm's input when ln is given), du (B,T,E) and dv_fwd,
+        dv_bwd (B,T,NX)."""
         x, z, dout = _f32(x), _f32(z), _f32(dout)
+        ln_w = ln_b = dln_w = dln_b = None
+        ln_eps = 0.0
+        if ln is not None:
+            ln_w, ln_b, ln_eps = _f32(ln["weight"]), _f32(ln["bias"]), float(ln["eps"])
         assert dout.shape == x.shape
         keep = []
         pf, pb = _dir_struct(fwd, keep), _dir_struct(bwd, keep)
@@ -295,6 +302,9 @@ class Oracle:
             structs.append(_DirGrad(*[grads[name][k].ctypes.data for k in PARAM_NAMES]))
         st = None
         res = {"dx": dx, "dz": dz, "fwd": grads["fwd"], "bwd": grads["bwd"]}
+        if ln is not None:
+            dln_w, dln_b = np.empty(E, np.float64), np.empty(E, np.float64)
+            res["ln"] = {"weight": dln_w, "bias": dln_b}
         if stages:
             res["gs"] = np.empty((B, T, E), np.float64)
             res["du"] = np.empty((B, T, E), np.float64)
@@ -306,6 +316,7 @@ class Oracle:
             B, h, w, E, N, R, K, axis, _ptr(idx_a), _ptr(dx), _ptr(dz),
             ctypes.byref(structs[0]), ctypes.byref(structs[1]),
             ctypes.byref(st) if st is not None else None,
+            _ptr(ln_w), _ptr(ln_b), ln_eps, _ptr(dln_w), _ptr(dln_b),
         )
         if rc:
             raise ValueError("fvo_layer_bwd failed: %d" % rc)
@@ -374,5 +385,5 @@ def conv_silu(x, axis, conv):
     return get().conv_silu(x, axis, conv)
 
 
-def layer_bwd(x, z, dout, fwd, bwd, axis, idx=None, hw=None, stages=False):
-    return get().layer_bwd(x, z, dout, fwd, bwd, axis, idx=idx, hw=hw, stages=stages)
+def layer_bwd(x, z, dout, fwd, bwd, axis, idx=None, hw=None, stages=False, ln=None):
+    return get().layer_bwd(x, z, dout, fwd, bwd, axis, idx=idx, hw=hw, stages=stages, ln=ln)

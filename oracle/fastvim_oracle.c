@@ -538,6 +538,59 @@ static void output_token_adjoint(const double *sf, const double *sb, const float
 }
 
 /*
+ * Adjoint of the output of one token with the post-SSM LayerNorm (the output
+ * of output_token with ln_w set; FastVim summary page, section 方法详解,
+ * bullet 5).  With y = s_fwd + s_bwd + (D_fwd + D_bwd) x, its mean and
+ * population variance over the token's E channels, r = 1 / sqrt(var + eps),
+ * n = (y - mean) r, o = n ln_w + ln_b and out = o silu(z):
+ *   dz       = dout o silu'(z)
+ *   dln_w   += dout silu(z) n,   dln_b += dout silu(z)
+ *   dn       = dout silu(z) ln_w
+ *   g = dL/dy = r (dn - mean(dn) - n mean(dn n))     (also dL/ds of both scans)
+ *   dx_skip  = g (D_fwd + D_bwd),   dD += g x
+ * ny is caller scratch of E doubles.
+ */
+static void output_token_adjoint_ln(const double *sf, const double *sb, const float *x, const float *z,
+                                    const float *dout, const fvo_dir *pf, const fvo_dir *pb, int64_t E,
+                                    const float *ln_w, const float *ln_b, double ln_eps, double *ny, double *g,
+                                    double *dz, double *dx_skip, double *dD, double *dln_w, double *dln_b)
+{
+    double mean = 0.0, var = 0.0;
+    for (int64_t e = 0; e < E; ++e) {
+        const double Ds = (double)pf->D[e] + (double)pb->D[e];
+        ny[e] = sf[e] + sb[e] + Ds * (double)x[e];
+        mean += ny[e];
+    }
+    mean /= (double)E;
+    for (int64_t e = 0; e < E; ++e) {
+        const double d = ny[e] - mean;
+        var += d * d;
+    }
+    const double r = 1.0 / sqrt(var / (double)E + ln_eps);
+    double m1 = 0.0, m2 = 0.0;
+    for (int64_t e = 0; e < E; ++e) {
+        ny[e] = (ny[e] - mean) * r;
+        const double ze = (double)z[e], de = (double)dout[e], sg = sigmoid(ze);
+        const double o = (double)ln_b[e] + ny[e] * (double)ln_w[e];
+        const double go = de * silu(ze);
+        dz[e] = de * o * sg * (1.0 + ze * (1.0 - sg));
+        dln_w[e] += go * ny[e];
+        dln_b[e] += go;
+        g[e] = go * (double)ln_w[e];  /* dn, for now */
+        m1 += g[e];
+        m2 += g[e] * ny[e];
+    }
+    m1 /= (double)E;
+    m2 /= (double)E;
+    for (int64_t e = 0; e < E; ++e) {
+        const double Ds = (double)pf->D[e] + (double)pb->D[e];
+        g[e] = r * (g[e] - m1 - ny[e] * m2);
+        dx_skip[e] = g[e] * Ds;
+        dD[e] += g[e] * (double)x[e];
+    }
+}
+
+/*
  * Adjoint of one selective scan (the recurrence of fvo_scan).  With k the
  * scan step (t = k forward, t = T-1-k backward), a_k[n] = exp(delta_k A[n]),
  * H_k = a_k H_{k-1} + delta_k B_k u_k and s_k = sum_n C_k[n] H_k[n], the state
@@ -630,9 +683,11 @@ static void xproj_adjoint(const double *u, const double *dv, int64_t M, int64_t 
 }
 
 /*
- * The whole backward pass (no LayerNorm).  Inputs as fvo_layer plus dout
- * (shaped like x).  Outputs dx, dz (shaped like x) and the gradients of both
- * directions' parameters (overwritten).  The pool's adjoint spreads du of a
+ * The whole backward pass.  Inputs as fvo_layer plus dout (shaped like x).
+ * Outputs dx, dz (shaped like x) and the gradients of both directions'
+ * parameters (overwritten).  ln_w == NULL: no LayerNorm; otherwise the layer
+ * has the post-SSM LayerNorm (ln_w, ln_b, ln_eps) and its weight and bias
+ * gradients go to dln_w, dln_b (E each, overwritten).  The pool's adjoint spreads du of a
  * scan position over its cells: dx[b, cell, e] = dx_skip + du[b, t(cell), e] / P
  * (P = 1 unpooled; the fixed row length for masked tokens).  Returns 0, -2,
  * -3 or -9 as fvo_layer.
@@ -640,7 +695,8 @@ static void xproj_adjoint(const double *u, const double *dv, int64_t M, int64_t 
 int fvo_layer_bwd(const float *x, const float *z, const float *dout, const fvo_dir *pf, const fvo_dir *pb,
                   int64_t B, int64_t h, int64_t w, int64_t E, int64_t N, int64_t R, int64_t K, int axis,
                   const int32_t *idx, double *dx, double *dz, fvo_dir_grad *gf, fvo_dir_grad *gb,
-                  fvo_bwd_stages *st)
+                  fvo_bwd_stages *st, const float *ln_w, const float *ln_b, double ln_eps, double *dln_w,
+                  double *dln_b)
 {
     int64_t T, P;
     const int masked = idx != NULL;
@@ -654,7 +710,7 @@ int fvo_layer_bwd(const float *x, const float *z, const float *dout, const fvo_d
 
     double *u = (double *)malloc(me), *gs = (double *)calloc((size_t)(M * E), sizeof(double));
     double *du = (double *)calloc((size_t)(M * E), sizeof(double)), *dd = (double *)malloc(me);
-    double *g = (double *)malloc((size_t)E * sizeof(double));
+    double *g = (double *)malloc((size_t)E * sizeof(double)), *ny = (double *)malloc((size_t)E * sizeof(double));
     double *dxs = (double *)malloc((size_t)(ntok * E) * sizeof(double));
     double *dD = (double *)calloc((size_t)E, sizeof(double));
     double *v[2], *q[2], *dl[2], *s[2], *dv[2];
@@ -663,7 +719,9 @@ int fvo_layer_bwd(const float *x, const float *z, const float *dout, const fvo_d
         v[d] = (double *)malloc(mx); q[d] = (double *)malloc(me); dl[d] = (double *)malloc(me);
         s[d] = (double *)malloc(me); dv[d] = (double *)calloc((size_t)(M * NX), sizeof(double));
     }
-    if (!u || !gs || !du || !dd || !g || !dxs || !dD || (masked && !rows)) { rc = -9; goto done; }
+    if (!u || !gs || !du || !dd || !g || !ny || !dxs || !dD || (masked && !rows)) { rc = -9; goto done; }
+    if (ln_w)
+        for (int64_t e = 0; e < E; ++e) dln_w[e] = dln_b[e] = 0.0;
     for (int d = 0; d < 2; ++d)
         if (!v[d] || !q[d] || !dl[d] || !s[d] || !dv[d]) { rc = -9; goto done; }
 
@@ -690,8 +748,12 @@ int fvo_layer_bwd(const float *x, const float *z, const float *dout, const fvo_d
             if (masked) t = rows[b * K + c];
             else t = seq_pos(axis, h, w, c / w, c % w);
             const int64_t off = (b * ncell + c) * E, mt = (b * T + t) * E;
-            output_token_adjoint(s[0] + mt, s[1] + mt, x + off, z + off, dout + off, pf, pb, E, g, dz + off,
-                                 dxs + off, dD);
+            if (ln_w)
+                output_token_adjoint_ln(s[0] + mt, s[1] + mt, x + off, z + off, dout + off, pf, pb, E, ln_w, ln_b,
+                                        ln_eps, ny, g, dz + off, dxs + off, dD, dln_w, dln_b);
+            else
+                output_token_adjoint(s[0] + mt, s[1] + mt, x + off, z + off, dout + off, pf, pb, E, g, dz + off,
+                                     dxs + off, dD);
             for (int64_t e = 0; e < E; ++e) gs[mt + e] += g[e];
         }
     }
@@ -732,7 +794,7 @@ int fvo_layer_bwd(const float *x, const float *z, const float *dout, const fvo_d
     }
 
 done:
-    free(u); free(gs); free(du); free(dd); free(g); free(dxs); free(dD); free(rows);
+    free(u); free(gs); free(du); free(dd); free(g); free(ny); free(dxs); free(dD); free(rows);
     for (int d = 0; d < 2; ++d) { free(v[d]); free(q[d]); free(dl[d]); free(s[d]); free(dv[d]); }
     return rc;
 }

@@ -520,8 +520,8 @@ def _bwd_case(rng, axis, masked, B_=2, h=4, w=3, E=5, N=3, R=2):
     return pf, pb, x, z, dout, idx, (h, w)
 
 
-def _loss(O, x, z, dout, pf, pb, axis, idx, hw):
-    return float(np.sum(dout.astype(np.float64) * O.layer(x, z, pf, pb, axis, idx=idx, hw=hw)))
+def _loss(O, x, z, dout, pf, pb, axis, idx, hw, ln=None):
+    return float(np.sum(dout.astype(np.float64) * O.layer(x, z, pf, pb, axis, idx=idx, hw=hw, ln=ln)))
 
 
 def _perturbed(a, V, eps):
@@ -568,23 +568,62 @@ def pin_bwd_finite_differences(O):
                 "difference %.12g" % (axis, masked, d, k or "", an, fd)
 
 
+def pin_bwd_finite_differences_ln(O):
+    """The same check for a layer with the post-SSM LayerNorm: every gradient,
+    the LayerNorm's weight and bias included, matches the central difference
+    of the forward oracle with the norm along a random +-1 direction."""
+    eps = 2.0 ** -14
+    rng = np.random.default_rng(42)
+    for axis, masked in ((COLS, False), (ROWS, False), (NONE_ROWMAJOR, False), (ROWS, True)):
+        pf, pb, x, z, dout, idx, hw = _bwd_case(rng, axis, masked)
+        E = x.shape[-1]
+        ln = {k: _dyadic(v) if k != "eps" else v for k, v in rand_ln(rng, E).items()}
+        g = O.layer_bwd(x, z, dout, pf, pb, axis, idx=idx, hw=hw, ln=ln)
+        targets = [("x", None), ("z", None), ("ln", "weight"), ("ln", "bias")] + \
+            [(d, k) for d in ("fwd", "bwd") for k in ("x_proj_w", "dt_proj_w", "dt_proj_b", "A_log", "D")]
+        for d, k in targets:
+            if k is None:
+                base, grad = (x, g["dx"]) if d == "x" else (z, g["dz"])
+            elif d == "ln":
+                base, grad = ln[k], g["ln"][k]
+            else:
+                base, grad = (pf if d == "fwd" else pb)[k], g[d][k]
+            V = rng.choice([-1.0, 1.0], size=base.shape)
+            L = []
+            for sgn in (1.0, -1.0):
+                arg = {"x": x, "z": z, "pf": dict(pf), "pb": dict(pb), "ln": dict(ln)}
+                pert = _perturbed(base, sgn * V, eps)
+                if k is None:
+                    arg[d] = pert
+                else:
+                    arg["ln" if d == "ln" else ("pf" if d == "fwd" else "pb")][k] = pert
+                L.append(_loss(O, arg["x"], arg["z"], dout, arg["pf"], arg["pb"], axis, idx, hw, ln=arg["ln"]))
+            fd = (L[0] - L[1]) / (2.0 * eps)
+            an = float(np.sum(grad * V))
+            scale = max(float(np.linalg.norm(grad)), 1e-30)
+            assert abs(fd - an) <= 1e-6 * scale, "LayerNorm axis %d masked %s: d/d%s %s: analytic %.12g, " \
+                "finite difference %.12g" % (axis, masked, d, k or "", an, fd)
+
+
 def pin_bwd_masked_equals_zero_filled(O):
     """The masked backward pass equals the dense one on the zero-filled grid
     (x, z and dout scattered into zeros): every parameter gradient agrees, and
     dx, dz agree at the kept cells (an unkept cell has z = 0, so silu(0) = 0
-    removes it from the pooled adjoint and from dD)."""
+    removes it from the pooled adjoint and from dD); also with the post-SSM
+    LayerNorm, whose statistics are per token."""
     rng = np.random.default_rng(41)
-    for axis in (COLS, ROWS):
+    for axis, norm in ((COLS, False), (ROWS, False), (COLS, True)):
         pf, pb, x, z, dout, idx, (h, w) = _bwd_case(rng, axis, True)
         B_, K, E = x.shape
+        ln = rand_ln(rng, E) if norm else None
         dense = [np.zeros((B_, h * w, E), np.float32) for _ in range(3)]
         for b in range(B_):
             for arr, src in zip(dense, (x, z, dout)):
                 arr[b, idx[b]] = src[b]
         xd, zd, dd = (a.reshape(B_, h, w, E) for a in dense)
-        gm = O.layer_bwd(x, z, dout, pf, pb, axis, idx=idx, hw=(h, w))
-        gd = O.layer_bwd(xd, zd, dd, pf, pb, axis)
-        for d in ("fwd", "bwd"):
+        gm = O.layer_bwd(x, z, dout, pf, pb, axis, idx=idx, hw=(h, w), ln=ln)
+        gd = O.layer_bwd(xd, zd, dd, pf, pb, axis, ln=ln)
+        for d in ("fwd", "bwd") + (("ln",) if norm else ()):
             for k in gm[d]:
                 _close(gm[d][k], gd[d][k], tol=1e-12, what="masked %s %s" % (d, k))
         for name in ("dx", "dz"):
@@ -756,6 +795,7 @@ ALL_PINS = [
     pin_layernorm_affine,
     pin_layernorm_library,
     pin_bwd_finite_differences,
+    pin_bwd_finite_differences_ln,
     pin_bwd_masked_equals_zero_filled,
     pin_conv_library,
     pin_conv_closed_forms,

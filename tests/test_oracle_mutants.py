@@ -93,7 +93,7 @@ MUTANTS = [
     ("x_proj adjoint does not reach du", "du[m * E + e] += (double)x_proj_w[o * E + e] * dv[m * NX + o];",
      "(void)du;", 1),
     ("pool adjoint not normalised", "du[mt + e] / (double)P", "du[mt + e]", 1),
-    ("silu derivative without its second term", "sg * (1.0 + ze * (1.0 - sg))", "sg", 1),
+    ("silu derivative without its second term", "sg * (1.0 + ze * (1.0 - sg))", "sg", 2),
     ("dz without the skip", "const double y = sf[e] + sb[e] + Ds * xe;", "const double y = sf[e] + sb[e];", 1),
     ("dD of the backward direction zero", "o->D[e] = dD[e];", "o->D[e] = d == 0 ? dD[e] : 0.0;", 1),
     ("scan adjoint fed dout without the gate", "g[e] = de * silu(ze);", "g[e] = de;", 1),
@@ -101,6 +101,24 @@ MUTANTS = [
     ("dx without the skip", "dx[off + e] = dxs[off + e] + du[mt + e] / (double)P;",
      "dx[off + e] = du[mt + e] / (double)P;", 1),
     ("du of the scan without B", "duk += lam[n] * d * Bn;", "duk += lam[n] * d;", 1),
+    # backward pass through the post-SSM LayerNorm
+    ("LayerNorm adjoint without the mean of dn", "g[e] = r * (g[e] - m1 - ny[e] * m2);",
+     "g[e] = r * (g[e] - ny[e] * m2);", 1),
+    ("LayerNorm adjoint without the variance term", "g[e] = r * (g[e] - m1 - ny[e] * m2);",
+     "g[e] = r * (g[e] - m1);", 1),
+    ("LayerNorm adjoint without the scale r", "g[e] = r * (g[e] - m1 - ny[e] * m2);",
+     "g[e] = g[e] - m1 - ny[e] * m2;", 1),
+    ("LayerNorm adjoint with the unbiased variance", "sqrt(var / (double)E + ln_eps)",
+     "sqrt(var / (double)(E - 1) + ln_eps)", 1),
+    ("LayerNorm weight gradient without the normalised value", "dln_w[e] += go * ny[e];", "dln_w[e] += go;", 1),
+    ("LayerNorm bias gradient without the gate", "dln_b[e] += go;", "dln_b[e] += de;", 1),
+    ("LayerNorm adjoint without its weight", "g[e] = go * (double)ln_w[e];", "g[e] = go;", 1),
+    ("LayerNorm adjoint's skip with only the forward D",
+     "const double Ds = (double)pf->D[e] + (double)pb->D[e];\n        g[e] = r",
+     "const double Ds = (double)pf->D[e];\n        g[e] = r", 1),
+    ("LayerNorm adjoint's recomputed input without the skip",
+     "ny[e] = sf[e] + sb[e] + Ds * (double)x[e];", "ny[e] = sf[e] + sb[e];", 1),
+    ("dz through the norm without its affine map", "dz[e] = de * o * sg", "dz[e] = de * ny[e] * sg", 1),
     ("adjoint uses the current state for the decay", "dd += lam[n] * (A * a * prev + Bn * ut);",
      "dd += lam[n] * (A * a * Hs[k * N + n] + Bn * ut);", 1),
 ]
