@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define FASTVIM_ABI_VERSION 7
+#define FASTVIM_ABI_VERSION 8
 
 typedef enum fastvim_status {
     FASTVIM_OK = 0,
@@ -287,10 +287,26 @@ size_t fastvim_ssm_export_bytes(const fastvim_dims *dims, int pool_axis, int wha
  * is fp32; every sum has a fixed order (no atomics), so results are
  * run-to-run identical.
  *
+ * With FASTVIM_FLAG_POST_NORM (params->ln_weight, ln_bias, ln_eps as for the
+ * forward call; FastVim summary page, section 方法详解, bullet 5) the adjoint
+ * of the output goes through the LayerNorm: with y as above, its mean and
+ * population variance over the token's E channels, r = 1 / sqrt(var + eps),
+ * n = (y - mean) r and o = n ln_weight + ln_bias,
+ *   dz    = dout * o * sigmoid(z) * (1 + z * (1 - sigmoid(z)))
+ *   d ln_weight = sum over all cells of dout silu(z) n,  d ln_bias = sum of dout silu(z)
+ *   dn    = dout silu(z) ln_weight,   g = r (dn - mean(dn) - n mean(dn n))
+ * and g takes the place of dL/dy above.  Since g needs the scan outputs, the
+ * call first recomputes the pooled tokens (unless saved_u is given), the
+ * projections and both scans; its first pass then reads x, z and dout, writes
+ * dz and leaves g in dx, which the second pass turns into dx (for bf16 I/O g
+ * is rounded to bf16 there).  grads->ln_weight and ln_bias receive the norm's
+ * gradients.
+ *
  * Supported: pooled layers (COLS or ROWS, dense or masked) with T <= 128 scan
- * steps and the limits of the forward call; FASTVIM_ERR_UNSUPPORTED for
- * unpooled layers, longer scans, and the flags FASTVIM_FLAG_FUSED,
- * FASTVIM_FLAG_POST_NORM, FASTVIM_FLAG_CONV and FASTVIM_FLAG_LOCAL_BWD (0 and
+ * steps and the limits of the forward call, with or without
+ * FASTVIM_FLAG_POST_NORM (then E <= 2048); FASTVIM_ERR_UNSUPPORTED for
+ * unpooled layers, longer scans, the LayerNorm with E > 2048, and the flags
+ * FASTVIM_FLAG_FUSED, FASTVIM_FLAG_CONV and FASTVIM_FLAG_LOCAL_BWD (0 and
  * FASTVIM_FLAG_STAGED run the same kernels). */
 
 /* Gradients of one direction's parameters: fp32 device buffers shaped like
@@ -305,6 +321,11 @@ typedef struct fastvim_dir_grads {
 
 typedef struct fastvim_grads {
     fastvim_dir_grads fwd, bwd;
+    /* With FASTVIM_FLAG_POST_NORM: the LayerNorm's weight and bias gradients,
+     * (E) fp32 each, 4-byte aligned, overwritten; ignored (may be NULL)
+     * otherwise. */
+    float *ln_weight;
+    float *ln_bias;
 } fastvim_grads;
 
 /* Bytes of workspace fastvim_ssm_bwd needs (0 if the sizes are invalid or
@@ -318,8 +339,8 @@ size_t fastvim_ssm_bwd_workspace_bytes(const fastvim_dims *dims, int pool_axis);
  * its workspace at least fastvim_ssm_bwd_workspace_bytes (256-byte aligned);
  * mask_idx as for the forward call (a token with an invalid index gets NaN in
  * dx and dz and takes no part in the pooled sums).  dx, dz, the workspace and
- * the ten gradient buffers must overlap neither each other nor any input or
- * parameter (FASTVIM_ERR_OVERLAP).  B == 0 writes zero gradients.  Errors as
+ * the ten (twelve with the LayerNorm) gradient buffers must overlap neither
+ * each other nor any input or parameter (FASTVIM_ERR_OVERLAP).  B == 0 writes zero gradients.  Errors as
  * fastvim_ssm_fwd, plus FASTVIM_ERR_NULL for a NULL grads or gradient buffer.
  * Enqueues its kernels on stream and returns. */
 int fastvim_ssm_bwd(const void *x, const void *z, const void *dout, const fastvim_params *params,

@@ -74,7 +74,7 @@ class DirGrads(ctypes.Structure):
 
 
 class Grads(ctypes.Structure):
-    _fields_ = [("fwd", DirGrads), ("bwd", DirGrads)]
+    _fields_ = [("fwd", DirGrads), ("bwd", DirGrads), ("ln_weight", ctypes.c_void_p), ("ln_bias", ctypes.c_void_p)]
 
 
 EXPORTED_SYMBOLS = (
@@ -296,9 +296,11 @@ class BwdCall:
 
     Arguments as SSMCall, plus dout shaped like x.  dx, dz (like x) and the
     gradients grads = {"fwd": {...}, "bwd": {...}} (fp32, shaped like the
-    parameters) are allocated unless given.  saved_u: the pooled tokens a
-    forward call with the same x wrote (then x is read once, not twice).
-    run() returns {"dx": dx, "dz": dz, "fwd": {...}, "bwd": {...}}."""
+    parameters; with ln also "ln": {"weight", "bias"}) are allocated unless
+    given.  ln: the post-SSM LayerNorm of the forward call.  saved_u: the
+    pooled tokens a forward call with the same x wrote (then x is read once,
+    not twice).  run() returns {"dx": dx, "dz": dz, "fwd": {...}, "bwd": {...}}
+    and, with ln, "ln": {"weight": ..., "bias": ...}."""
 
     def __init__(self, x: torch.Tensor, z: torch.Tensor, dout: torch.Tensor,
                  params: Dict[str, Dict[str, torch.Tensor]], pool_axis: int,
@@ -306,7 +308,7 @@ class BwdCall:
                  dx: Optional[torch.Tensor] = None, dz: Optional[torch.Tensor] = None,
                  grads: Optional[Dict[str, Dict[str, torch.Tensor]]] = None,
                  workspace: Optional[torch.Tensor] = None, flags: int = 0,
-                 saved_u: Optional[torch.Tensor] = None):
+                 saved_u: Optional[torch.Tensor] = None, ln: Optional[Dict[str, object]] = None):
         self.dims = _layer_dims(x, z, params, mask_idx, hw)
         if dout.dtype != x.dtype or dout.shape != x.shape:
             raise ValueError("dout must match x in shape and dtype")
@@ -318,6 +320,21 @@ class BwdCall:
         dirs = _dir_params(params, self._keep)
         if grads is None:
             grads = {d: {f: torch.empty_like(params[d][f]) for f in DIR_FIELDS} for d in ("fwd", "bwd")}
+        ln_w = ln_b = None
+        ln_eps = 0.0
+        if ln is not None:
+            ln_w, ln_b, ln_eps = ln["weight"], ln["bias"], float(ln["eps"])
+            for t in (ln_w, ln_b):
+                if t.dtype != torch.float32 or not t.is_contiguous():
+                    raise ValueError("LayerNorm weight and bias must be contiguous float32")
+            self._keep.extend([ln_w, ln_b])
+            flags |= FLAG_POST_NORM
+            if "ln" not in grads:
+                grads = dict(grads, ln={"weight": torch.empty_like(ln_w), "bias": torch.empty_like(ln_b)})
+            for f in ("weight", "bias"):
+                t = grads["ln"][f]
+                if t.dtype != torch.float32 or not t.is_contiguous() or t.shape != ln_w.shape:
+                    raise ValueError("LayerNorm gradient %s must be contiguous float32 shaped like the weight" % f)
         self.grads = grads
         gd = []
         for d in ("fwd", "bwd"):
@@ -326,7 +343,8 @@ class BwdCall:
                 if t.dtype != torch.float32 or not t.is_contiguous() or t.shape != params[d][f].shape:
                     raise ValueError("gradient %s.%s must be contiguous float32 shaped like the parameter" % (d, f))
             gd.append(DirGrads(*[grads[d][f].data_ptr() for f in DIR_FIELDS]))
-        self.cgrads = Grads(gd[0], gd[1])
+        lg = grads["ln"] if ln is not None else None
+        self.cgrads = Grads(gd[0], gd[1], _ptr(lg["weight"]) if lg else None, _ptr(lg["bias"]) if lg else None)
         nbytes = bwd_workspace_bytes(self.dims, pool_axis)
         if workspace is None:
             workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=x.device)
@@ -334,7 +352,7 @@ class BwdCall:
         _check_saved_u(saved_u)
         self.saved_u = saved_u
         self.params = Params(dirs[0], dirs[1], workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-                             flags, 0, None, None, 0.0, 0, None, None, _ptr(saved_u))
+                             flags, 0, _ptr(ln_w), _ptr(ln_b), ln_eps, 0, None, None, _ptr(saved_u))
 
     def run(self, stream=None) -> Dict[str, object]:
         st = lib().fastvim_ssm_bwd(_ptr(self.x), _ptr(self.z), _ptr(self.dout), ctypes.byref(self.params),
@@ -342,14 +360,17 @@ class BwdCall:
                                    _ptr(self.dz), ctypes.byref(self.cgrads), _stream(stream))
         if st:
             raise FastVimError(st, "fastvim_ssm_bwd")
-        return {"dx": self.dx, "dz": self.dz, "fwd": self.grads["fwd"], "bwd": self.grads["bwd"]}
+        res = {"dx": self.dx, "dz": self.dz, "fwd": self.grads["fwd"], "bwd": self.grads["bwd"]}
+        if "ln" in self.grads and self.params.flags & FLAG_POST_NORM:
+            res["ln"] = self.grads["ln"]
+        return res
 
 
 def ssm_bwd(x, z, dout, params, pool_axis=POOL_COLS, mask_idx=None, hw=None, workspace=None, stream=None,
-            flags=0, saved_u=None):
-    """Gradients of the layer; returns {"dx", "dz", "fwd": {...}, "bwd": {...}}."""
+            flags=0, saved_u=None, ln=None):
+    """Gradients of the layer; returns {"dx", "dz", "fwd": {...}, "bwd": {...}} (and "ln" with ln)."""
     return BwdCall(x, z, dout, params, pool_axis, mask_idx=mask_idx, hw=hw, workspace=workspace,
-                   flags=flags, saved_u=saved_u).run(stream)
+                   flags=flags, saved_u=saved_u, ln=ln).run(stream)
 
 
 def calib_copy(dst: torch.Tensor, src: torch.Tensor, stream=None) -> None:

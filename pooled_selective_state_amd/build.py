@@ -17,7 +17,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfastvim.so")
 SOURCES = ["api.cpp", "pool.hip", "proj.hip", "scan.hip", "epilogue.hip", "fused.hip", "calib.hip", "epilogue_norm.hip",
-           "scan_bwd.hip", "bwd.hip", "conv.hip"]
+           "scan_bwd.hip", "bwd.hip", "bwd_norm.hip", "conv.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -173,8 +173,8 @@ size_t export_bytes(const Geom& g, int what) {
     }
 }
 
-// The backward pass covers the pooled layer (dense or masked) without the
-// post-SSM norm, with scans of at most kBwdTMax steps.
+// The backward pass covers the pooled layer (dense or masked), with scans of
+// at most kBwdTMax steps; with the post-SSM norm, E <= 2048 (bwd_norm.hip).
 bool bwd_supported(const Geom& g) { return g.pooled && g.T <= kBwdTMax; }
 
 struct Span {
@@ -187,19 +187,26 @@ int validate_bwd(const void* x, const void* z, const void* dout, const fastvim_p
                  int axis, const int32_t* idx, const void* dx, const void* dz, const fastvim_grads* gr, Geom* g,
                  BwdWorkspace* ws, bool* empty) {
     if (!prm) return FASTVIM_ERR_NULL;
-    const uint32_t unsupported =
-        FASTVIM_FLAG_FUSED | FASTVIM_FLAG_POST_NORM | FASTVIM_FLAG_CONV | FASTVIM_FLAG_LOCAL_BWD;
-    if (prm->flags & ~(FASTVIM_FLAG_STAGED | unsupported)) return FASTVIM_ERR_ARG;
+    const uint32_t unsupported = FASTVIM_FLAG_FUSED | FASTVIM_FLAG_CONV | FASTVIM_FLAG_LOCAL_BWD;
+    if (prm->flags & ~(FASTVIM_FLAG_STAGED | FASTVIM_FLAG_POST_NORM | unsupported)) return FASTVIM_ERR_ARG;
     if (prm->flags & unsupported) return FASTVIM_ERR_UNSUPPORTED;
+    const bool norm = (prm->flags & FASTVIM_FLAG_POST_NORM) != 0;
     int st = resolve_geom(d, axis, g);
     if (st) return st;
-    if (!bwd_supported(*g)) return FASTVIM_ERR_UNSUPPORTED;
+    if (!bwd_supported(*g) || (norm && !bwd_norm_supported(*g))) return FASTVIM_ERR_UNSUPPORTED;
     if (!g->masked && idx) return FASTVIM_ERR_ARG;
     if (!gr) return FASTVIM_ERR_NULL;
+    if (norm) {
+        if (!prm->ln_weight || !prm->ln_bias || !gr->ln_weight || !gr->ln_bias) return FASTVIM_ERR_NULL;
+        if (!aligned(prm->ln_weight, 16) || !aligned(prm->ln_bias, 16) || !aligned(gr->ln_weight, 4) ||
+            !aligned(gr->ln_bias, 4))
+            return FASTVIM_ERR_ALIGN;
+        if (!(prm->ln_eps > 0.f) || !(prm->ln_eps < 3.4e38f)) return FASTVIM_ERR_ARG;
+    }
     const fastvim_dir_grads* gd[2] = {&gr->fwd, &gr->bwd};
     const size_t gsz[5] = {(size_t)(g->NX * g->E), (size_t)(g->E * g->R), (size_t)g->E, (size_t)(g->E * g->N),
                            (size_t)g->E};
-    Span gs[10];
+    Span gs[12];
     for (int k = 0; k < 2; ++k) {
         const float* ps[5] = {gd[k]->x_proj_w, gd[k]->dt_proj_w, gd[k]->dt_proj_b, gd[k]->A_log, gd[k]->D};
         for (int i = 0; i < 5; ++i) {
@@ -208,8 +215,13 @@ int validate_bwd(const void* x, const void* z, const void* dout, const fastvim_p
             gs[5 * k + i] = Span{ps[i], gsz[i] * sizeof(float)};
         }
     }
-    for (int i = 0; i < 10; ++i)
-        for (int j = i + 1; j < 10; ++j)
+    const int ngs = norm ? 12 : 10;
+    if (norm) {
+        gs[10] = Span{gr->ln_weight, (size_t)g->E * sizeof(float)};
+        gs[11] = Span{gr->ln_bias, (size_t)g->E * sizeof(float)};
+    }
+    for (int i = 0; i < ngs; ++i)
+        for (int j = i + 1; j < ngs; ++j)
             if (overlap(gs[i].p, gs[i].n, gs[j].p, gs[j].n)) return FASTVIM_ERR_OVERLAP;
     *empty = g->B == 0;
     if (*empty) return FASTVIM_OK;
@@ -224,7 +236,7 @@ int validate_bwd(const void* x, const void* z, const void* dout, const fastvim_p
     const size_t io = (size_t)(g->B * (g->masked ? g->K : g->h * g->w) * g->E) * (g->io == FASTVIM_F32 ? 4 : 2);
     // outputs (dx, dz, the workspace and every gradient) overlap neither each
     // other nor an input; parameters count as inputs
-    Span ins[14] = {{x, io}, {z, io}, {dout, io}};
+    Span ins[16] = {{x, io}, {z, io}, {dout, io}};
     int nin = 3;
     for (const fastvim_dir_params* pd : {&prm->fwd, &prm->bwd}) {
         const float* ps[5] = {pd->x_proj_w, pd->dt_proj_w, pd->dt_proj_b, pd->A_log, pd->D};
@@ -232,12 +244,17 @@ int validate_bwd(const void* x, const void* z, const void* dout, const fastvim_p
     }
     if (prm->saved_u && !aligned(prm->saved_u, 16)) return FASTVIM_ERR_ALIGN;
     ins[nin++] = Span{prm->saved_u, prm->saved_u ? (size_t)(g->B * g->T * g->E) * sizeof(float) : 0};
-    Span outs[13] = {{dx, io}, {dz, io}, {prm->workspace, need}};
-    for (int i = 0; i < 10; ++i) outs[3 + i] = gs[i];
-    for (int i = 0; i < 13; ++i) {
+    if (norm) {
+        ins[nin++] = Span{prm->ln_weight, (size_t)g->E * sizeof(float)};
+        ins[nin++] = Span{prm->ln_bias, (size_t)g->E * sizeof(float)};
+    }
+    Span outs[15] = {{dx, io}, {dz, io}, {prm->workspace, need}};
+    const int nout = 3 + ngs;
+    for (int i = 0; i < ngs; ++i) outs[3 + i] = gs[i];
+    for (int i = 0; i < nout; ++i) {
         for (int j = 0; j < nin; ++j)
             if (overlap(outs[i].p, outs[i].n, ins[j].p, ins[j].n)) return FASTVIM_ERR_OVERLAP;
-        for (int j = i + 1; j < 13; ++j)
+        for (int j = i + 1; j < nout; ++j)
             if (overlap(outs[i].p, outs[i].n, outs[j].p, outs[j].n)) return FASTVIM_ERR_OVERLAP;
     }
     bwd_workspace_layout(*g, prm->workspace, ws);
@@ -255,9 +272,25 @@ int run_bwd(const Geom& g, const void* x, const void* z, const void* dout, const
         if (e == hipSuccess) e = r;
         return e == hipSuccess;
     };
+    const bool norm = (p.flags & FASTVIM_FLAG_POST_NORM) != 0;
     if (g.masked && !ok(launch_mask_rows(g, idx, ws.fwd, s))) return FASTVIM_ERR_HIP;
-    if (!ok(launch_bwd_pool(g, x, z, dout, ws, s))) return FASTVIM_ERR_HIP;
-    if (!ok(launch_proj(g, x, p, ws.fwd, s))) return FASTVIM_ERR_HIP;
+    if (norm) {
+        // the norm's adjoint needs y, hence both scans' outputs: recompute the
+        // forward stages first, then the first pass with the norm, whose
+        // per-(b, t) partials of dD, d ln_w and d ln_b (in du, du_f, du_b) are
+        // summed before the scan adjoint overwrites those buffers
+        if ((!ws.u_saved && !ok(launch_pool(g, x, ws.fwd, s))) || !ok(launch_proj(g, x, p, ws.fwd, s)) ||
+            !ok(launch_scan(g, x, p, ws.fwd, s)) || !ok(launch_bwd_norm_pass1(g, x, z, dout, p, ws, dx, dz, s)))
+            return FASTVIM_ERR_HIP;
+        const int64_t M = g.B * g.T;
+        if (!ok(launch_colsum(ws.du, M, g.E, g.E, gr.fwd.D, gr.bwd.D, ws.tmp, s)) ||
+            !ok(launch_colsum(ws.du_f, M, g.E, g.E, gr.ln_weight, nullptr, ws.tmp, s)) ||
+            !ok(launch_colsum(ws.du_b, M, g.E, g.E, gr.ln_bias, nullptr, ws.tmp, s)))
+            return FASTVIM_ERR_HIP;
+    } else {
+        if (!ok(launch_bwd_pool(g, x, z, dout, ws, s)) || !ok(launch_proj(g, x, p, ws.fwd, s)))
+            return FASTVIM_ERR_HIP;
+    }
     BwdScanArgs a{ws.fwd.xdbl, ws.fwd.u, ws.gs, p.fwd, p.bwd, ws.fwd.s_f, ws.fwd.s_b, ws.du_f, ws.du_b, ws.dvp,
                   ws.ckpt, ws.dAp, ws.dWdtp, ws.dbp, g.B, g.T, g.E, (int)g.R, (int)g.NX, (int)ws.G};
     if (!ok(launch_scan_bwd(a, s)) || !ok(launch_bwd_dv(g, ws, s)) || !ok(launch_bwd_du(g, p, ws, s)) ||
@@ -283,6 +316,7 @@ int run_bwd(const Geom& g, const void* x, const void* z, const void* dout, const
         }
     }
     if (!ok(launch_colsum_batch(batch, s))) return FASTVIM_ERR_HIP;
+    if (norm) return ok(launch_bwd_norm_pass2(g, p, ws, dx, dz, s)) ? FASTVIM_OK : FASTVIM_ERR_HIP;
     if (!ok(launch_bwd_epilogue(g, x, z, dout, p, ws, dx, dz, s))) return FASTVIM_ERR_HIP;
     if (!ok(launch_colsum(ws.dDp, bwd_dd_parts(g), E, E, gr.fwd.D, gr.bwd.D, ws.tmp, s))) return FASTVIM_ERR_HIP;
     return FASTVIM_OK;
@@ -348,7 +382,8 @@ size_t bwd_workspace_layout(const Geom& g, void* base, BwdWorkspace* ws) {
         return rows > kColRowsPerBlock ? (rows + kColRowsPerBlock - 1) / kColRowsPerBlock * cols : int64_t(0);
     };
     int64_t tmpf = 1;
-    for (int64_t v : {stage1(ND, E), stage1(B, E * 16), stage1(B, E * R), stage1(B, E), stage1(MC, NX * E)})
+    for (int64_t v : {stage1(ND, E), stage1(M, E), stage1(B, E * 16), stage1(B, E * R), stage1(B, E),
+                      stage1(MC, NX * E)})
         tmpf = v > tmpf ? v : tmpf;
     const size_t o_tmp = take((size_t)tmpf * sizeof(float));
     if (base && ws) {
@@ -486,6 +521,10 @@ int fastvim_ssm_bwd(const void* x, const void* z, const void* dout, const fastvi
             for (int i = 0; i < 5; ++i)
                 if (launch_fill_zero(ps[i], n[i], s) != hipSuccess) return FASTVIM_ERR_HIP;
         }
+        if ((params->flags & FASTVIM_FLAG_POST_NORM) &&
+            (launch_fill_zero(grads->ln_weight, g.E, s) != hipSuccess ||
+             launch_fill_zero(grads->ln_bias, g.E, s) != hipSuccess))
+            return FASTVIM_ERR_HIP;
         return FASTVIM_OK;
     }
     return run_bwd(g, x, z, dout, *params, mask_idx, dx, dz, *grads, ws, s);

@@ -17,9 +17,11 @@ struct BwdWorkspace {
     Workspace fwd;
     float* gs;     // (B, T, E) dL/ds: the gated upstream gradient summed over the pooled axis
     float* dDp;    // (bwd_dd_parts, E) per second-pass workgroup: sum over its tokens of dL/dy * x
-    float* du_f;   // (B, T, E) scan part of dL/du, forward direction
-    float* du_b;   // (B, T, E) the same, backward direction
-    float* du;     // (B, T, E) dL/du, both directions, scan and x_proj
+    float* du_f;   // (B, T, E) scan part of dL/du, forward direction; with the LayerNorm first
+                   //           the (b, t) partials of d ln_w
+    float* du_b;   // (B, T, E) the same, backward direction; with the LayerNorm first those of d ln_b
+    float* du;     // (B, T, E) dL/du, both directions, scan and x_proj; with the LayerNorm first
+                   //           the (b, t) partials of dD
     float* dvp;    // (2, B, G, T, S) channel-group partials of dL/dv, in the scan's LDS row layout
     float* ckpt;   // (2, B, G, kBwdTMax / 16, 256, 4) scan adjoint: each lane's states entering each chunk
     float* dv;     // (B, T, 2, NX) dL/dv of both directions
@@ -80,5 +82,16 @@ hipError_t launch_colsum_batch(ColsumBatch bt, hipStream_t st);
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st);
 hipError_t launch_bwd_epilogue(const Geom& g, const void* x, const void* z, const void* dout,
                                const fastvim_params& p, const BwdWorkspace& ws, void* dx, void* dz, hipStream_t st);
+
+// Backward through the post-SSM LayerNorm (bwd_norm.hip), for E <= 2048.
+// Pass 1 needs fwd.s_f and fwd.s_b; it writes dz, g = dL/dy into dx, gs, and
+// the (B T, E) partials of dD, d ln_w and d ln_b into du, du_f and du_b.
+// Pass 2 needs du and turns dx into dL/dx.
+bool bwd_norm_supported(const Geom& g);
+hipError_t launch_bwd_norm_pass1(const Geom& g, const void* x, const void* z, const void* dout,
+                                 const fastvim_params& p, const BwdWorkspace& ws, void* dx, void* dz,
+                                 hipStream_t st);
+hipError_t launch_bwd_norm_pass2(const Geom& g, const fastvim_params& p, const BwdWorkspace& ws, void* dx,
+                                 void* dz, hipStream_t st);
 
 }  // namespace fastvim

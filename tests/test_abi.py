@@ -32,7 +32,7 @@ def test_library_exports_every_declared_function():
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(Bd.EXPORTED_SYMBOLS)
-    assert lib.fastvim_abi_version() == 7
+    assert lib.fastvim_abi_version() == 8
 
 
 def test_status_strings():
@@ -49,7 +49,8 @@ def test_struct_layout_matches_header():
     assert ctypes.sizeof(Bd.DirParams) == 40
     assert ctypes.sizeof(Bd.Params) == 2 * 40 + 8 + 8 + 8 + 8 + 8 + 4 + 4 + 8 + 8 + 8
     assert Bd.Params.saved_u.offset == ctypes.sizeof(Bd.Params) - 8
-    assert ctypes.sizeof(Bd.DirGrads) == 40 and ctypes.sizeof(Bd.Grads) == 80
+    assert ctypes.sizeof(Bd.DirGrads) == 40 and ctypes.sizeof(Bd.Grads) == 96
+    assert Bd.Grads.ln_weight.offset == 80 and Bd.Grads.ln_bias.offset == 88
 
 
 def _ws(dims, axis):
@@ -357,7 +358,7 @@ def test_bwd_unsupported_and_bad_flags():
         assert FakeBwd(axis=axis).bwd() == EUNSUP
     assert FakeBwd(h=129).bwd() == EUNSUP
     assert FakeBwd(N=8).bwd() == EUNSUP
-    for flags, code in ((P.FLAG_FUSED, EUNSUP), (P.FLAG_POST_NORM, EUNSUP), (P.FLAG_CONV, EUNSUP), (P.FLAG_LOCAL_BWD, EUNSUP), (32, EARG),
+    for flags, code in ((P.FLAG_FUSED, EUNSUP), (P.FLAG_CONV, EUNSUP), (P.FLAG_LOCAL_BWD, EUNSUP), (32, EARG),
                         (P.FLAG_STAGED, OK)):
         c = FakeBwd()
         c.params.flags = flags
@@ -366,6 +367,56 @@ def test_bwd_unsupported_and_bad_flags():
     c = FakeBwd()
     c.idx = c.dx + (1 << 30)
     assert c.bwd() == EARG  # mask_idx with a dense layer
+
+
+def _norm_bwd(**kw):
+    """A backward call with the post-SSM LayerNorm (fake addresses)."""
+    c = FakeBwd(**kw)
+    far = 1 << 45
+    c.params.flags = P.FLAG_POST_NORM
+    c.params.ln_weight, c.params.ln_bias, c.params.ln_eps = far, far + 65536, 1e-5
+    c.grads.ln_weight, c.grads.ln_bias = far + 2 * 65536, far + 3 * 65536
+    return c
+
+
+def test_bwd_post_norm_validation():
+    """The LayerNorm's parameters and gradient buffers of a backward call are
+    checked before any launch; E > 2048 is not supported with the norm."""
+    for attr in ("ln_weight", "ln_bias"):
+        c = _norm_bwd()
+        setattr(c.params, attr, None)
+        assert c.bwd() == ENULL, attr
+        c = _norm_bwd()
+        setattr(c.grads, attr, None)
+        assert c.bwd() == ENULL, "grad " + attr
+    c = _norm_bwd()
+    c.params.ln_bias += 4
+    assert c.bwd() == EALIGN
+    c = _norm_bwd()
+    c.grads.ln_weight += 2
+    assert c.bwd() == EALIGN
+    for eps in (0.0, -1.0, float("nan"), float("inf")):
+        c = _norm_bwd()
+        c.params.ln_eps = eps
+        assert c.bwd() == EARG, eps
+    c = _norm_bwd()
+    c.grads.ln_bias = c.grads.ln_weight + 32  # the two gradients overlap
+    assert c.bwd() == EOVERLAP
+    c = _norm_bwd()
+    c.grads.ln_weight = c.params.ln_weight  # gradient over its parameter
+    assert c.bwd() == EOVERLAP
+    c = _norm_bwd()
+    c.grads.ln_bias = c.dz + 64
+    assert c.bwd() == EOVERLAP
+    c = _norm_bwd()
+    c.grads.ln_weight = c.grads.fwd.D
+    assert c.bwd() == EOVERLAP
+    assert _norm_bwd(E=2056).bwd() == EUNSUP
+    # without the flag the norm's pointers are not looked at
+    c = FakeBwd()
+    c.grads.ln_weight = c.grads.ln_bias = c.dx
+    c.params.workspace_bytes -= 1
+    assert c.bwd() == EWS  # the call got past every other check
 
 
 def test_bwd_alignment():

@@ -26,7 +26,7 @@ import torch
 import oracle
 import pooled_selective_state_amd as P
 from gpu_util import BF16_TOL, FP32_TOL, check, dev, dev_params, host
-from pins import rand_dir
+from pins import rand_dir, rand_ln
 from pooled_selective_state_amd import configs as C
 from pooled_selective_state_amd.inputs import DIRECTIONS, draw_workload, random_mask, round_to_bf16, zero_D
 
@@ -43,21 +43,32 @@ def _gpu():
     torch.cuda.synchronize()
 
 
-def gpu_bwd(x, z, dout, prm, axis, idx=None, hw=None, dtype=torch.float32, flags=0, saved=None):
+def _dev_ln(ln):
+    if ln is None:
+        return None
+    return {"weight": dev(ln["weight"], torch.float32), "bias": dev(ln["bias"], torch.float32), "eps": ln["eps"]}
+
+
+def gpu_bwd(x, z, dout, prm, axis, idx=None, hw=None, dtype=torch.float32, flags=0, saved=None, ln=None):
     """saved: None (the backward pools x itself) or the flags of a forward call
-    that first writes the pooled tokens the backward then reads (saved_u)."""
+    that first writes the pooled tokens the backward then reads (saved_u).
+    ln: the post-SSM LayerNorm (host arrays), for both calls."""
     idd = None if idx is None else dev(idx, torch.int32)
     xd, zd, pd = dev(x, dtype), dev(z, dtype), dev_params(prm)
+    lnd = _dev_ln(ln)
     su = None
     if saved is not None:
         h, w = (x.shape[1], x.shape[2]) if idx is None else hw
         su = torch.full((x.shape[0], h if axis == P.POOL_COLS else w, x.shape[-1]), float("nan"), device="cuda")
-        P.SSMCall(xd, zd, pd, axis, mask_idx=idd, hw=hw, flags=saved, saved_u=su).run()
-    call = P.BwdCall(xd, zd, dev(dout, dtype), pd, axis, mask_idx=idd, hw=hw, flags=flags, saved_u=su)
+        P.SSMCall(xd, zd, pd, axis, mask_idx=idd, hw=hw, flags=saved, saved_u=su, ln=lnd).run()
+    call = P.BwdCall(xd, zd, dev(dout, dtype), pd, axis, mask_idx=idd, hw=hw, flags=flags, saved_u=su, ln=lnd)
     res = call.run()
     torch.cuda.synchronize()
-    return {"dx": host(res["dx"]), "dz": host(res["dz"]),
-            **{d: {f: host(res[d][f]) for f in FIELDS} for d in DIRECTIONS}}
+    out = {"dx": host(res["dx"]), "dz": host(res["dz"]),
+           **{d: {f: host(res[d][f]) for f in FIELDS} for d in DIRECTIONS}}
+    if ln is not None:
+        out["ln"] = {f: host(res["ln"][f]) for f in ("weight", "bias")}
+    return out
 
 
 def compare(got, ref, tol, tag, sel=None, params=True):
@@ -68,17 +79,20 @@ def compare(got, ref, tol, tag, sel=None, params=True):
         for d in DIRECTIONS:
             for f in FIELDS:
                 check(got[d][f], ref[d][f], tol, "%s d%s.%s" % (tag, d, f))
+        if "ln" in ref:
+            for f in ("weight", "bias"):
+                check(got["ln"][f], ref["ln"][f], tol, "%s d ln_%s" % (tag, f))
 
 
-def bwd_check(x, z, dout, prm, axis, tol, dtype, tag, idx=None, hw=None, twin=True, saved=None):
+def bwd_check(x, z, dout, prm, axis, tol, dtype, tag, idx=None, hw=None, twin=True, saved=None, ln=None):
     """GPU gradients and those of the D = 0 twin against the oracle."""
-    got = gpu_bwd(x, z, dout, prm, axis, idx=idx, hw=hw, dtype=dtype, saved=saved)
-    ref = oracle.layer_bwd(x, z, dout, prm["fwd"], prm["bwd"], axis, idx=idx, hw=hw)
+    got = gpu_bwd(x, z, dout, prm, axis, idx=idx, hw=hw, dtype=dtype, saved=saved, ln=ln)
+    ref = oracle.layer_bwd(x, z, dout, prm["fwd"], prm["bwd"], axis, idx=idx, hw=hw, ln=ln)
     compare(got, ref, tol, tag)
     if twin:
         p0 = zero_D(prm)
-        got0 = gpu_bwd(x, z, dout, p0, axis, idx=idx, hw=hw, dtype=dtype, saved=saved)
-        ref0 = oracle.layer_bwd(x, z, dout, p0["fwd"], p0["bwd"], axis, idx=idx, hw=hw)
+        got0 = gpu_bwd(x, z, dout, p0, axis, idx=idx, hw=hw, dtype=dtype, saved=saved, ln=ln)
+        ref0 = oracle.layer_bwd(x, z, dout, p0["fwd"], p0["bwd"], axis, idx=idx, hw=hw, ln=ln)
         compare(got0, ref0, tol, tag + " (D=0)", params=False)
     return got
 
@@ -235,9 +249,10 @@ def test_bwd_rows_is_cols_on_transposed_grid():
 
 
 # ------------------------------------------------------------------ full size
-def _sampled_full_size(cfg, axis=P.POOL_COLS, saved=None):
+def _sampled_full_size(cfg, axis=P.POOL_COLS, saved=None, norm=False):
     wl = draw_workload(cfg)
     x, z, prm, idx = wl["x"], wl["z"][0], wl["params"][0], wl["idx"]
+    ln = rand_ln(np.random.default_rng(78), cfg.E) if norm else None
     sel = np.array([0, cfg.B - 1])
     rng = np.random.default_rng(77)
     dout = np.zeros_like(x)
@@ -246,15 +261,15 @@ def _sampled_full_size(cfg, axis=P.POOL_COLS, saved=None):
         dout = round_to_bf16(dout)
     tol, dt = _tol(cfg.io_dtype)
     hw = (cfg.h, cfg.w) if cfg.masked else None
-    print("\n[%s bwd] B=%d grid=%dx%d E=%d axis %d, upstream gradient on images %s, pooled tokens %s"
-          % (cfg.name, cfg.B, cfg.h, cfg.w, cfg.E, axis, list(sel), "saved" if saved is not None else "recomputed"),
-          flush=True)
-    got = gpu_bwd(x, z, dout, prm, axis, idx=idx, hw=hw, dtype=dt, saved=saved)
+    print("\n[%s bwd] B=%d grid=%dx%d E=%d axis %d, upstream gradient on images %s, pooled tokens %s%s"
+          % (cfg.name, cfg.B, cfg.h, cfg.w, cfg.E, axis, list(sel), "saved" if saved is not None else "recomputed",
+             ", post-SSM LayerNorm" if norm else ""), flush=True)
+    got = gpu_bwd(x, z, dout, prm, axis, idx=idx, hw=hw, dtype=dt, saved=saved, ln=ln)
     rest = np.setdiff1d(np.arange(cfg.B), sel)
     for name in ("dx", "dz"):
         assert np.count_nonzero(got[name][rest]) == 0, name + " nonzero on images without upstream gradient"
     ref = oracle.layer_bwd(x[sel], z[sel], dout[sel], prm["fwd"], prm["bwd"], axis,
-                           idx=None if idx is None else idx[sel], hw=hw)
+                           idx=None if idx is None else idx[sel], hw=hw, ln=ln)
     compare(got, ref, tol, cfg.name, sel=sel)
 
 
@@ -282,3 +297,129 @@ def test_bwd_saved_u_matches_pooling_again():
         for fl in (P.FLAG_STAGED, P.FLAG_FUSED):
             b = gpu_bwd(x, z, dout, prm, axis, saved=fl)
             compare(b, a, 1e-5, "saved vs pooled again, axis %d flags %d" % (axis, fl))
+
+
+# ------------------------------------------------------------------ post-SSM LayerNorm
+# widths that reach every team shape of the norm's first pass: fp32 E = 8 ..
+# 200 (16-lane teams, 1 to 4 vectors a lane), 384 and 504 (32 lanes), 768,
+# 1024 and 1032 (64 lanes, up to 8 vectors); bf16 E = 8, 200 (16 lanes), 384
+# (32), 1024, 1032 and 2048 (64)
+NORM_SHAPES = {
+    "f32": [(2, 5, 7, 8, 3), (3, 13, 7, 72, 5), (2, 9, 11, 136, 12), (1, 6, 33, 200, 20), (2, 16, 16, 384, 12),
+            (1, 7, 5, 504, 33), (1, 9, 4, 768, 48), (1, 4, 9, 1024, 64), (1, 3, 5, 1032, 7)],
+    "bf16": [(2, 5, 7, 8, 3), (1, 6, 33, 200, 20), (2, 16, 16, 384, 12), (1, 4, 9, 1024, 64), (1, 3, 5, 1032, 7),
+             (1, 3, 4, 2048, 16)],
+}
+NORM_CASES = [(io, s) for io in ("f32", "bf16") for s in NORM_SHAPES[io]]
+
+
+@pytest.mark.parametrize("axis", (P.POOL_COLS, P.POOL_ROWS))
+@pytest.mark.parametrize("io,shape", NORM_CASES, ids=["%s-%s" % (io, "x".join(map(str, s))) for io, s in NORM_CASES])
+def test_bwd_norm_shapes(io, shape, axis):
+    B, h, w, E, R = shape
+    rng = np.random.default_rng(zlib.crc32(repr(("bwd-norm", shape, axis, io)).encode()))
+    x, z, dout = (rng.standard_normal((B, h, w, E)).astype(np.float32) for _ in range(3))
+    x, z, dout = _io(io, x, z, dout)
+    prm = {"fwd": rand_dir(rng, E, 16, R, 0.1), "bwd": rand_dir(rng, E, 16, R, 0.1)}
+    ln = rand_ln(rng, E)
+    tol, dt = _tol(io)
+    bwd_check(x, z, dout, prm, axis, tol, dt, "norm %s %s axis %d" % (shape, io, axis), ln=ln)
+
+
+@pytest.mark.parametrize("saved", [None, 0], ids=SAVED_IDS)
+@pytest.mark.parametrize("axis", (P.POOL_COLS, P.POOL_ROWS))
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_bwd_norm_saved_and_ragged(axis, io, saved):
+    B, h, w, E, R = 3, 21, 10, 136, 9
+    rng = np.random.default_rng(301 + axis + (saved is not None))
+    x, z, dout = (rng.standard_normal((B, h, w, E)).astype(np.float32) for _ in range(3))
+    x, z, dout = _io(io, x, z, dout)
+    prm = {"fwd": rand_dir(rng, E, 16, R, 0.1), "bwd": rand_dir(rng, E, 16, R, 0.1)}
+    ln = rand_ln(rng, E)
+    tol, dt = _tol(io)
+    bwd_check(x, z, dout, prm, axis, tol, dt, "norm ragged %s axis %d" % (io, axis), saved=saved, ln=ln)
+
+
+@pytest.mark.parametrize("axis", (P.POOL_COLS, P.POOL_ROWS))
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("K", [1, 17, 42])
+def test_bwd_norm_masked(axis, io, K):
+    B, h, w, E, R = 4, 6, 7, 96, 6
+    rng = np.random.default_rng(400 + K + 7 * axis)
+    x, z, dout = (rng.standard_normal((B, K, E)).astype(np.float32) for _ in range(3))
+    x, z, dout = _io(io, x, z, dout)
+    idx = random_mask(rng, B, h, w, K)
+    prm = {"fwd": rand_dir(rng, E, 16, R, 0.1), "bwd": rand_dir(rng, E, 16, R, 0.1)}
+    ln = rand_ln(rng, E)
+    tol, dt = _tol(io)
+    bwd_check(x, z, dout, prm, axis, tol, dt, "norm masked K=%d %s axis %d" % (K, io, axis), idx=idx, hw=(h, w),
+              ln=ln)
+
+
+def test_bwd_norm_masked_invalid_indices():
+    """With the LayerNorm too, tokens with an invalid index get NaN in dx and
+    dz and the rest (every gradient included) equals the oracle on the valid
+    tokens."""
+    B, h, w, E, R, K = 3, 5, 6, 48, 4, 9
+    rng = np.random.default_rng(23)
+    idx = random_mask(rng, B, h, w, K)
+    idx[0, 2] = h * w
+    idx[1, 4] = idx[1, 7]
+    idx[2, 0] = -5
+    x, z, dout = (rng.standard_normal((B, K, E)).astype(np.float32) for _ in range(3))
+    prm = {"fwd": rand_dir(rng, E, 16, R, 0.1), "bwd": rand_dir(rng, E, 16, R, 0.1)}
+    ln = rand_ln(rng, E)
+    got = gpu_bwd(x, z, dout, prm, P.POOL_ROWS, idx=idx, hw=(h, w), ln=ln)
+    invalid = {(0, 2), (1, 4), (1, 7), (2, 0)}
+    refs = []
+    for b in range(B):
+        keep = [k for k in range(K) if (b, k) not in invalid]
+        bad = [k for k in range(K) if (b, k) in invalid]
+        for name in ("dx", "dz"):
+            assert np.all(np.isnan(got[name][b, bad])), "invalid token of image %d not NaN in %s" % (b, name)
+        ref = oracle.layer_bwd(x[b:b + 1, keep], z[b:b + 1, keep], dout[b:b + 1, keep], prm["fwd"], prm["bwd"],
+                               P.POOL_ROWS, idx=idx[b:b + 1, keep], hw=(h, w), ln=ln)
+        check(got["dx"][b:b + 1, keep], ref["dx"], FP32_TOL, "norm invalid-index image %d dx" % b)
+        check(got["dz"][b:b + 1, keep], ref["dz"], FP32_TOL, "norm invalid-index image %d dz" % b)
+        refs.append(ref)
+    for d in DIRECTIONS:
+        for f in FIELDS:
+            check(got[d][f], sum(r[d][f] for r in refs), FP32_TOL, "norm invalid-index d%s.%s" % (d, f))
+    for f in ("weight", "bias"):
+        check(got["ln"][f], sum(r["ln"][f] for r in refs), FP32_TOL, "norm invalid-index d ln_" + f)
+
+
+def test_bwd_norm_deterministic_and_empty():
+    """Fixed-order sums with the norm too; B = 0 zeroes the norm's gradients."""
+    B, h, w, E, R = 3, 12, 20, 200, 12
+    rng = np.random.default_rng(7)
+    x, z, dout = (rng.standard_normal((B, h, w, E)).astype(np.float32) for _ in range(3))
+    prm = {"fwd": rand_dir(rng, E, 16, R, 0.1), "bwd": rand_dir(rng, E, 16, R, 0.1)}
+    ln = rand_ln(rng, E)
+    a = gpu_bwd(x, z, dout, prm, P.POOL_COLS, ln=ln)
+    b = gpu_bwd(x, z, dout, prm, P.POOL_COLS, ln=ln)
+    for k in ("dx", "dz"):
+        assert np.array_equal(a[k], b[k])
+    for f in ("weight", "bias"):
+        assert np.array_equal(a["ln"][f], b["ln"][f])
+    pd = dev_params(prm)
+    xe = torch.empty((0, h, w, E), device="cuda")
+    grads = {d: {f: torch.full_like(pd[d][f], 7.0) for f in FIELDS} for d in DIRECTIONS}
+    grads["ln"] = {f: torch.full((E,), 7.0, device="cuda") for f in ("weight", "bias")}
+    res = P.BwdCall(xe, xe.clone(), xe.clone(), pd, P.POOL_COLS, grads=grads, ln=_dev_ln(ln)).run()
+    torch.cuda.synchronize()
+    for f in ("weight", "bias"):
+        assert torch.count_nonzero(res["ln"][f]).item() == 0
+
+
+@pytest.mark.parametrize("axis", (P.POOL_COLS, P.POOL_ROWS))
+def test_bwd_norm_full_size_2048(axis):
+    _sampled_full_size(C.HIRES_2048, axis, saved=0 if axis == P.POOL_COLS else None, norm=True)
+
+
+def test_bwd_norm_full_size_vim_s():
+    _sampled_full_size(C.SHORT_224_S, norm=True)
+
+
+def test_bwd_norm_full_size_masked_b():
+    _sampled_full_size(C.MASKED_B, norm=True)

@@ -4,8 +4,9 @@ both element types, both paths of a dense pooled layer and the options that
 combine with it (post-SSM LayerNorm, producer Conv1D, LBMamba's local
 backward scan), so that combinations the fixed cases do not list are checked
 too.  Each case compares out, the out of its D = 0 twin, and both scan
-outputs, each on its own scale; cases of plain pooled layers also run the
-backward pass, with and without the pooled tokens saved by the forward call.
+outputs, each on its own scale; cases of pooled layers without the Conv1D or
+the local scan also run the backward pass (with the LayerNorm where the case
+has it), with and without the pooled tokens saved by the forward call.
 Bar: 1e-4 fp32, 2e-2 bf16 (oracle on the bf16-rounded inputs).
 """
 from __future__ import annotations
@@ -104,25 +105,30 @@ def test_random_layer(seed):
     check(sf, ref["fwd"]["s"], tol, tag + " s_fwd")
     check(sb, ref["bwd"]["s"], tol, tag + " s_bwd")
 
-    # the backward pass covers pooled layers without the options
-    if axis in (P.POOL_COLS, P.POOL_ROWS) and not (c["norm"] or c["conv"] or c["local"]) and \
+    # the backward pass covers pooled layers, with the norm but not the other options
+    if axis in (P.POOL_COLS, P.POOL_ROWS) and not (c["conv"] or c["local"]) and \
             (c["w"] if axis == P.POOL_ROWS else c["h"]) <= 128:
         dout = rng.standard_normal(shape).astype(np.float32)
         if c["io"] == "bf16":
             dout = round_to_bf16(dout)
         xd, zd, pd = dev(x, dt), dev(z, dt), dev_params(prm)
         idd = None if idx is None else dev(idx, torch.int32)
+        lnd = None if ln is None else {"weight": dev(ln["weight"], torch.float32),
+                                       "bias": dev(ln["bias"], torch.float32), "eps": ln["eps"]}
         su = None
         if seed % 2:
             T = c["h"] if axis == P.POOL_COLS else c["w"]
             su = torch.full((c["B"], T, c["E"]), float("nan"), device="cuda")
-            P.SSMCall(xd, zd, pd, axis, mask_idx=idd, hw=hw, saved_u=su).run()
-        res = P.BwdCall(xd, zd, dev(dout, dt), pd, axis, mask_idx=idd, hw=hw, saved_u=su).run()
+            P.SSMCall(xd, zd, pd, axis, mask_idx=idd, hw=hw, saved_u=su, ln=lnd).run()
+        res = P.BwdCall(xd, zd, dev(dout, dt), pd, axis, mask_idx=idd, hw=hw, saved_u=su, ln=lnd).run()
         torch.cuda.synchronize()
-        rb = oracle.layer_bwd(x, z, dout, prm["fwd"], prm["bwd"], axis, idx=idx, hw=hw)
+        rb = oracle.layer_bwd(x, z, dout, prm["fwd"], prm["bwd"], axis, idx=idx, hw=hw, ln=ln)
         btag = tag + (" bwd saved-u" if su is not None else " bwd")
         check(host(res["dx"]), rb["dx"], tol, btag + " dx")
         check(host(res["dz"]), rb["dz"], tol, btag + " dz")
         for d in DIRECTIONS:
             for f in FIELDS:
                 check(host(res[d][f]), rb[d][f], tol, "%s d%s.%s" % (btag, d, f))
+        if ln is not None:
+            for f in ("weight", "bias"):
+                check(host(res["ln"][f]), rb["ln"][f], tol, "%s d ln_%s" % (btag, f))
