@@ -96,7 +96,7 @@ class Oracle:
             vp, vp, ctypes.POINTER(_Dir), ctypes.POINTER(_Dir),
             i64, i64, i64, i64, i64, i64, i64, ci, vp,
             vp, vp, vp, ctypes.POINTER(_DirOut), ctypes.POINTER(_DirOut),
-            vp, vp, ctypes.c_double, vp, vp, i64, i64,
+            vp, vp, ctypes.c_double, vp, vp, i64, i64, ctypes.c_double,
         ]
         lib.fvo_layer.restype = ci
         lib.fvo_conv_silu.argtypes = [vp, i64, i64, i64, i64, ci, vp, vp, i64, vp]
@@ -105,7 +105,7 @@ class Oracle:
             vp, vp, vp, ctypes.POINTER(_Dir), ctypes.POINTER(_Dir),
             i64, i64, i64, i64, i64, i64, i64, ci, vp,
             vp, vp, ctypes.POINTER(_DirGrad), ctypes.POINTER(_DirGrad), ctypes.POINTER(_BwdStages),
-            vp, vp, ctypes.c_double, vp, vp,
+            vp, vp, ctypes.c_double, vp, vp, ctypes.c_double,
         ]
         lib.fvo_layer_bwd.restype = ci
         self._lib = lib
@@ -198,7 +198,8 @@ class Oracle:
             raise ValueError("fvo_conv_silu failed: %d" % rc)
         return xc
 
-    def layer(self, x, z, fwd, bwd, axis, idx=None, hw=None, stages=False, ln=None, conv=None, local_window=0):
+    def layer(self, x, z, fwd, bwd, axis, idx=None, hw=None, stages=False, ln=None, conv=None, local_window=0,
+              pool_scale=1.0):
         """Full layer.  Dense: x, z (B,h,w,E).  Masked: x, z (B,K,E), idx (B,K),
         hw=(h, w).  fwd / bwd: dicts with x_proj_w, dt_proj_w, dt_proj_b, A_log, D.
         ln: None, or {"weight": (E,), "bias": (E,), "eps": float} for the
@@ -207,7 +208,7 @@ class Oracle:
         conv_silu(x) (dense layers only).  local_window = L > 0: LBMamba's
         local backward scan (forward parameters, state reset at the top of
         every window of L steps) replaces the global backward scan; of bwd only
-        D is used.
+        D is used.  pool_scale multiplies the pooled tokens u (not the skip).
         Returns out (fp64), or with stages=True a dict of out, u, rows and the
         per-direction v, delta, s."""
         x, z = _f32(x), _f32(z)
@@ -257,6 +258,7 @@ class Oracle:
             ctypes.byref(fo) if fo is not None else None,
             ctypes.byref(bo) if bo is not None else None,
             _ptr(ln_w), _ptr(ln_b), ln_eps, _ptr(conv_w), _ptr(conv_b), conv_k, int(local_window),
+            float(pool_scale),
         )
         if rc:
             raise ValueError("fvo_layer failed: %d" % rc)
@@ -264,7 +266,7 @@ class Oracle:
             return out
         return {"out": out, "u": u, "rows": rows, "fwd": st["fwd"], "bwd": st["bwd"]}
 
-    def layer_bwd(self, x, z, dout, fwd, bwd, axis, idx=None, hw=None, stages=False, ln=None):
+    def layer_bwd(self, x, z, dout, fwd, bwd, axis, idx=None, hw=None, stages=False, ln=None, pool_scale=1.0):
         """Gradients of sum(dout * layer(x, z, ...)).  Arguments as layer();
         dout is shaped like x.  Returns a dict with dx, dz (fp64, shaped like
         x) and "fwd" / "bwd" dicts of parameter gradients keyed like the
@@ -316,7 +318,7 @@ class Oracle:
             B, h, w, E, N, R, K, axis, _ptr(idx_a), _ptr(dx), _ptr(dz),
             ctypes.byref(structs[0]), ctypes.byref(structs[1]),
             ctypes.byref(st) if st is not None else None,
-            _ptr(ln_w), _ptr(ln_b), ln_eps, _ptr(dln_w), _ptr(dln_b),
+            _ptr(ln_w), _ptr(ln_b), ln_eps, _ptr(dln_w), _ptr(dln_b), float(pool_scale),
         )
         if rc:
             raise ValueError("fvo_layer_bwd failed: %d" % rc)
@@ -376,14 +378,16 @@ def scan(u, dlt, v, A_log, R, reverse=False, reset=None):
     return get().scan(u, dlt, v, A_log, R, reverse=reverse, reset=reset)
 
 
-def layer(x, z, fwd, bwd, axis, idx=None, hw=None, stages=False, ln=None, conv=None, local_window=0):
+def layer(x, z, fwd, bwd, axis, idx=None, hw=None, stages=False, ln=None, conv=None, local_window=0,
+          pool_scale=1.0):
     return get().layer(x, z, fwd, bwd, axis, idx=idx, hw=hw, stages=stages, ln=ln, conv=conv,
-                       local_window=local_window)
+                       local_window=local_window, pool_scale=pool_scale)
 
 
 def conv_silu(x, axis, conv):
     return get().conv_silu(x, axis, conv)
 
 
-def layer_bwd(x, z, dout, fwd, bwd, axis, idx=None, hw=None, stages=False, ln=None):
-    return get().layer_bwd(x, z, dout, fwd, bwd, axis, idx=idx, hw=hw, stages=stages, ln=ln)
+def layer_bwd(x, z, dout, fwd, bwd, axis, idx=None, hw=None, stages=False, ln=None, pool_scale=1.0):
+    return get().layer_bwd(x, z, dout, fwd, bwd, axis, idx=idx, hw=hw, stages=stages, ln=ln,
+                           pool_scale=pool_scale)

@@ -392,12 +392,18 @@ static void output_token(const double *sf, const double *sb, const float *x, con
  * direction's projection, step size and decay (the same inputs the forward
  * scan holds), whose state starts from zero at the top of every window of L
  * steps, windows aligned at t = 0: a reset at every t with t mod L = L - 1.
- * Of the backward parameters only D is used, in the skip. */
+ * Of the backward parameters only D is used, in the skip.
+ *
+ * pool_scale multiplies the pooled tokens u (1 for the layer as defined): the
+ * constant factor the MAE transfer recipe applies when pooling during
+ * fine-tuning and linear probing, 0.25 there [Pith review, referee_report,
+ * major comment on the MAE experiments].  Only u is scaled; the skip reads
+ * the full-resolution x as before. */
 int fvo_layer(const float *x, const float *z, const fvo_dir *pf, const fvo_dir *pb, int64_t B, int64_t h,
               int64_t w, int64_t E, int64_t N, int64_t R, int64_t K, int axis, const int32_t *idx,
               double *out, double *u_out, int32_t *rows_out, fvo_dir_out *fwd, fvo_dir_out *bwd,
               const float *ln_w, const float *ln_b, double ln_eps, const float *conv_w, const float *conv_b,
-              int64_t conv_k, int64_t local_window)
+              int64_t conv_k, int64_t local_window, double pool_scale)
 {
     int64_t T, P;
     const int masked = idx != NULL;
@@ -424,6 +430,7 @@ int fvo_layer(const float *x, const float *z, const fvo_dir *pf, const fvo_dir *
     } else {
         pool_dense_any(x, xc, B, h, w, E, axis, u);
     }
+    for (int64_t i = 0; i < M * E; ++i) u[i] *= pool_scale;
 
     rc = run_direction(u, B, T, E, N, R, pf, 0, NULL, fwd, sf);
     if (rc) goto done;
@@ -687,16 +694,17 @@ static void xproj_adjoint(const double *u, const double *dv, int64_t M, int64_t 
  * Outputs dx, dz (shaped like x) and the gradients of both directions'
  * parameters (overwritten).  ln_w == NULL: no LayerNorm; otherwise the layer
  * has the post-SSM LayerNorm (ln_w, ln_b, ln_eps) and its weight and bias
- * gradients go to dln_w, dln_b (E each, overwritten).  The pool's adjoint spreads du of a
- * scan position over its cells: dx[b, cell, e] = dx_skip + du[b, t(cell), e] / P
- * (P = 1 unpooled; the fixed row length for masked tokens).  Returns 0, -2,
+ * gradients go to dln_w, dln_b (E each, overwritten).  pool_scale as in
+ * fvo_layer.  The pool's adjoint spreads du of a scan position over its
+ * cells: dx[b, cell, e] = dx_skip + pool_scale du[b, t(cell), e] / P (P = 1
+ * unpooled; the fixed row length for masked tokens).  Returns 0, -2,
  * -3 or -9 as fvo_layer.
  */
 int fvo_layer_bwd(const float *x, const float *z, const float *dout, const fvo_dir *pf, const fvo_dir *pb,
                   int64_t B, int64_t h, int64_t w, int64_t E, int64_t N, int64_t R, int64_t K, int axis,
                   const int32_t *idx, double *dx, double *dz, fvo_dir_grad *gf, fvo_dir_grad *gb,
                   fvo_bwd_stages *st, const float *ln_w, const float *ln_b, double ln_eps, double *dln_w,
-                  double *dln_b)
+                  double *dln_b, double pool_scale)
 {
     int64_t T, P;
     const int masked = idx != NULL;
@@ -733,6 +741,7 @@ int fvo_layer_bwd(const float *x, const float *z, const float *dout, const fvo_d
     } else {
         fvo_pool_dense(x, B, h, w, E, axis, u);
     }
+    for (int64_t i = 0; i < M * E; ++i) u[i] *= pool_scale;
     for (int d = 0; d < 2; ++d) {
         fvo_xproj(u, M, E, pd[d]->x_proj_w, NX, v[d]);
         dt_preact(v[d], M, NX, R, pd[d]->dt_proj_w, pd[d]->dt_proj_b, E, q[d]);
@@ -782,7 +791,7 @@ int fvo_layer_bwd(const float *x, const float *z, const float *dout, const fvo_d
             if (masked) t = rows[b * K + c];
             else t = seq_pos(axis, h, w, c / w, c % w);
             const int64_t off = (b * ncell + c) * E, mt = (b * T + t) * E;
-            for (int64_t e = 0; e < E; ++e) dx[off + e] = dxs[off + e] + du[mt + e] / (double)P;
+            for (int64_t e = 0; e < E; ++e) dx[off + e] = dxs[off + e] + du[mt + e] * pool_scale / (double)P;
         }
     }
 

@@ -520,8 +520,9 @@ def _bwd_case(rng, axis, masked, B_=2, h=4, w=3, E=5, N=3, R=2):
     return pf, pb, x, z, dout, idx, (h, w)
 
 
-def _loss(O, x, z, dout, pf, pb, axis, idx, hw, ln=None):
-    return float(np.sum(dout.astype(np.float64) * O.layer(x, z, pf, pb, axis, idx=idx, hw=hw, ln=ln)))
+def _loss(O, x, z, dout, pf, pb, axis, idx, hw, ln=None, pool_scale=1.0):
+    return float(np.sum(dout.astype(np.float64) * O.layer(x, z, pf, pb, axis, idx=idx, hw=hw, ln=ln,
+                                                          pool_scale=pool_scale)))
 
 
 def _perturbed(a, V, eps):
@@ -535,13 +536,19 @@ def pin_bwd_finite_differences(O):
     each direction) matches the central difference of the pinned forward
     oracle along a random +-1 direction.  Inputs sit on a dyadic grid, so the
     perturbed inputs are exact and the difference quotient carries only its
-    O(eps^2) truncation error (~1e-9 relative at eps = 2^-14)."""
+    O(eps^2) truncation error (~1e-9 relative at eps = 2^-14) and the fp64
+    rounding of the two losses, at most a few ulps of sum |dout out| divided
+    by 2 eps (which matters only for a gradient near zero); also with the
+    pooled tokens scaled by 1/4."""
     eps = 2.0 ** -14
     rng = np.random.default_rng(40)
-    cases = ((COLS, False), (ROWS, False), (NONE_ROWMAJOR, False), (NONE_COLMAJOR, False), (COLS, True), (ROWS, True))
-    for axis, masked in cases:
+    cases = ((COLS, False, 1.0), (ROWS, False, 1.0), (NONE_ROWMAJOR, False, 1.0), (NONE_COLMAJOR, False, 1.0),
+             (COLS, True, 1.0), (ROWS, True, 1.0), (COLS, False, 0.25), (ROWS, True, 0.25))
+    for axis, masked, scale in cases:
         pf, pb, x, z, dout, idx, hw = _bwd_case(rng, axis, masked)
-        g = O.layer_bwd(x, z, dout, pf, pb, axis, idx=idx, hw=hw)
+        g = O.layer_bwd(x, z, dout, pf, pb, axis, idx=idx, hw=hw, pool_scale=scale)
+        out = O.layer(x, z, pf, pb, axis, idx=idx, hw=hw, pool_scale=scale)
+        floor = 64 * 2.0 ** -52 * float(np.sum(np.abs(dout * out))) / (2.0 * eps)
         targets = [("x", None), ("z", None)] + [(d, k) for d in ("fwd", "bwd") for k in
                                                  ("x_proj_w", "dt_proj_w", "dt_proj_b", "A_log", "D")]
         for d, k in targets:
@@ -560,12 +567,12 @@ def pin_bwd_finite_differences(O):
                     arg[d] = pert
                 else:
                     arg["pf" if d == "fwd" else "pb"][k] = pert
-                L.append(_loss(O, arg["x"], arg["z"], dout, arg["pf"], arg["pb"], axis, idx, hw))
+                L.append(_loss(O, arg["x"], arg["z"], dout, arg["pf"], arg["pb"], axis, idx, hw, pool_scale=scale))
             fd = (L[0] - L[1]) / (2.0 * eps)
             an = float(np.sum(grad * V))
-            scale = max(float(np.linalg.norm(grad)), 1e-30)
-            assert abs(fd - an) <= 1e-6 * scale, "axis %d masked %s: d/d%s %s: analytic %.12g, finite " \
-                "difference %.12g" % (axis, masked, d, k or "", an, fd)
+            size = max(float(np.linalg.norm(grad)), 1e-30)
+            assert abs(fd - an) <= 1e-6 * size + floor, "axis %d masked %s pool scale %g: d/d%s %s: analytic %.12g, " \
+                "finite difference %.12g" % (axis, masked, scale, d, k or "", an, fd)
 
 
 def pin_bwd_finite_differences_ln(O):
@@ -603,6 +610,31 @@ def pin_bwd_finite_differences_ln(O):
             scale = max(float(np.linalg.norm(grad)), 1e-30)
             assert abs(fd - an) <= 1e-6 * scale, "LayerNorm axis %d masked %s: d/d%s %s: analytic %.12g, " \
                 "finite difference %.12g" % (axis, masked, d, k or "", an, fd)
+
+
+def pin_pool_scale_is_a_scaled_input(O):
+    """Scaling the pooled tokens by s equals running the layer on s x with the
+    skip weights divided by s: the pooled tokens are then s times the row
+    means and the skip term (D / s)(s x) is unchanged.  With s = 1/4 both
+    rescalings are exact in fp32, so the two agree to fp64 rounding; dense
+    COLS and ROWS, masked, with the post-SSM LayerNorm and with the local
+    backward scan."""
+    rng = np.random.default_rng(43)
+    s = 0.25
+    for axis, masked, norm, local in ((COLS, False, False, 0), (ROWS, False, True, 0), (COLS, True, False, 0),
+                                      (ROWS, True, True, 0), (COLS, False, False, 4)):
+        pf, pb, x, z, dout, idx, hw = _bwd_case(rng, axis, masked)
+        ln = rand_ln(rng, x.shape[-1]) if norm else None
+        got = O.layer(x, z, pf, pb, axis, idx=idx, hw=hw, ln=ln, local_window=local, pool_scale=s)
+        qf, qb = dict(pf), dict(pb)
+        qf["D"] = (pf["D"].astype(np.float64) / s).astype(np.float32)
+        qb["D"] = (pb["D"].astype(np.float64) / s).astype(np.float32)
+        want = O.layer((x.astype(np.float64) * s).astype(np.float32), z, qf, qb, axis, idx=idx, hw=hw, ln=ln,
+                       local_window=local)
+        _close(got, want, tol=1e-12, what="pool scale axis %d masked %s norm %s local %d" % (axis, masked, norm,
+                                                                                             local))
+        plain = O.layer(x, z, pf, pb, axis, idx=idx, hw=hw, ln=ln, local_window=local)
+        assert np.max(np.abs(got - plain)) > 1e-6 * np.max(np.abs(plain)), "the pool scale changed nothing"
 
 
 def pin_bwd_masked_equals_zero_filled(O):
@@ -796,6 +828,7 @@ ALL_PINS = [
     pin_layernorm_library,
     pin_bwd_finite_differences,
     pin_bwd_finite_differences_ln,
+    pin_pool_scale_is_a_scaled_input,
     pin_bwd_masked_equals_zero_filled,
     pin_conv_library,
     pin_conv_closed_forms,

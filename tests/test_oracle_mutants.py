@@ -54,6 +54,13 @@ MUTANTS = [
     ("LayerNorm eps outside the root", "1.0 / sqrt(var + ln_eps)", "1.0 / (sqrt(var) + ln_eps)", 1),
     ("LayerNorm without centring", "y[e] = (y[e] - mean) * r", "y[e] = y[e] * r", 1),
     ("LayerNorm scale and shift swapped", "* (double)ln_w[e] + (double)ln_b[e]", "* (double)ln_b[e] + (double)ln_w[e]", 1),
+    ("pool scale not applied", "    for (int64_t i = 0; i < M * E; ++i) u[i] *= pool_scale;\n\n    rc = run_direction",
+     "\n    rc = run_direction", 1),
+    ("pool scale applied as a divisor", "    for (int64_t i = 0; i < M * E; ++i) u[i] *= pool_scale;\n\n    rc = run_direction",
+     "    for (int64_t i = 0; i < M * E; ++i) u[i] /= pool_scale;\n\n    rc = run_direction", 1),
+    ("backward recomputes u without the pool scale",
+     "    for (int64_t i = 0; i < M * E; ++i) u[i] *= pool_scale;\n    for (int d = 0; d < 2; ++d) {",
+     "    for (int d = 0; d < 2; ++d) {", 1),
     ("reset ignored", "(reset && reset[t]) ? 0.0 : exp(d * A)", "exp(d * A)", 1),
     ("duplicate mask index accepted", "if (q < 0 || q >= h * w || seen[q])", "if (q < 0 || q >= h * w)", 1),
     # producer Conv1D
@@ -92,14 +99,15 @@ MUTANTS = [
     ("dt_proj adjoint does not reach dv", "dv[m * NX + r] += (double)dt_proj_w[e * R + r] * dq;", "(void)dv;", 1),
     ("x_proj adjoint does not reach du", "du[m * E + e] += (double)x_proj_w[o * E + e] * dv[m * NX + o];",
      "(void)du;", 1),
-    ("pool adjoint not normalised", "du[mt + e] / (double)P", "du[mt + e]", 1),
+    ("pool adjoint not normalised", "du[mt + e] * pool_scale / (double)P", "du[mt + e] * pool_scale", 1),
+    ("pool adjoint without the pool scale", "du[mt + e] * pool_scale / (double)P", "du[mt + e] / (double)P", 1),
     ("silu derivative without its second term", "sg * (1.0 + ze * (1.0 - sg))", "sg", 2),
     ("dz without the skip", "const double y = sf[e] + sb[e] + Ds * xe;", "const double y = sf[e] + sb[e];", 1),
     ("dD of the backward direction zero", "o->D[e] = dD[e];", "o->D[e] = d == 0 ? dD[e] : 0.0;", 1),
     ("scan adjoint fed dout without the gate", "g[e] = de * silu(ze);", "g[e] = de;", 1),
     ("backward direction's adjoint not reversed", "pd[d]->A_log, d, du, dd", "pd[d]->A_log, 0, du, dd", 1),
-    ("dx without the skip", "dx[off + e] = dxs[off + e] + du[mt + e] / (double)P;",
-     "dx[off + e] = du[mt + e] / (double)P;", 1),
+    ("dx without the skip", "dx[off + e] = dxs[off + e] + du[mt + e] * pool_scale / (double)P;",
+     "dx[off + e] = du[mt + e] * pool_scale / (double)P;", 1),
     ("du of the scan without B", "duk += lam[n] * d * Bn;", "duk += lam[n] * d;", 1),
     # backward pass through the post-SSM LayerNorm
     ("LayerNorm adjoint without the mean of dn", "g[e] = r * (g[e] - m1 - ny[e] * m2);",
