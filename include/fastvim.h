@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define FASTVIM_ABI_VERSION 8
+#define FASTVIM_ABI_VERSION 9
 
 typedef enum fastvim_status {
     FASTVIM_OK = 0,
@@ -120,7 +120,9 @@ typedef struct fastvim_params {
     const float *ln_weight;
     const float *ln_bias;
     float ln_eps;
-    uint32_t reserved2;
+    /* Factor on the pooled tokens, used with FASTVIM_FLAG_POOL_SCALE only
+     * (the layer as defined has 1). */
+    float pool_scale;
     /* Producer Conv1D, used with FASTVIM_FLAG_CONV only: depthwise taps
      * (E, FASTVIM_CONV_TAPS) fp32, oldest tap first, 16-byte aligned, and bias
      * (E) fp32. */
@@ -132,8 +134,8 @@ typedef struct fastvim_params {
      * writes the pooled tokens u here instead of into the workspace, and
      * fastvim_ssm_bwd reads them from here instead of pooling x again, so its
      * first pass reads z and dout only.  The caller keeps the buffer between
-     * the two calls and passes the same x, mask and pool axis to both; the
-     * library does not check that the contents match.  Errors: FASTVIM_ERR_ARG
+     * the two calls and passes the same x, mask, pool axis and pool scale to
+     * both; the library does not check that the contents match.  Errors: FASTVIM_ERR_ARG
      * (unpooled layer), FASTVIM_ERR_ALIGN, FASTVIM_ERR_OVERLAP (it overlaps
      * an input, an output or the workspace). */
     float *saved_u;
@@ -203,6 +205,19 @@ typedef struct fastvim_params {
  * FASTVIM_ERR_UNSUPPORTED for it. */
 #define FASTVIM_FLAG_LOCAL_BWD 16u
 #define FASTVIM_LOCAL_WINDOW 16
+
+/* FASTVIM_FLAG_POOL_SCALE multiplies the pooled tokens by params.pool_scale:
+ * u = pool_scale * (row sum) / P, for the projections and the scans, while
+ * the skip term reads x unscaled.  It is the constant the MAE transfer
+ * recipe applies when pooling in fine-tuning and linear probing of a model
+ * pre-trained on 75 %-masked inputs, 0.25 there (Pith review on 2502.00594,
+ * referee report, major comments: the MAE experiments): with the fixed
+ * normaliser P, pooled rows of a masked image are about a quarter of those of
+ * a full one.  Pooled layers (dense or masked) and every option and path; the
+ * backward pass takes it too (the pool's adjoint becomes pool_scale / P).
+ * Errors: FASTVIM_ERR_ARG for an unpooled layer or a pool_scale that is not
+ * finite. */
+#define FASTVIM_FLAG_POOL_SCALE 32u
 
 /* Bytes of workspace a call with these sizes needs (0 if the sizes are
  * invalid).  Dense pooled layers need 4 * B * T * (3E + 2(R + 2N)) bytes plus

@@ -6,7 +6,7 @@ The layer runs in hand-written HIP kernels behind the C ABI declared in
 from .binding import (  # noqa: F401
     BF16, F32, POOL_COLS, POOL_NONE_COLMAJOR, POOL_NONE_ROWMAJOR, POOL_ROWS,
     EXPORT_BAD_TOKENS, EXPORT_ROWS, EXPORT_S_BWD, EXPORT_S_FWD, EXPORT_STATUS, EXPORT_U, EXPORT_XDBL, FLAG_CONV, FLAG_FUSED, FLAG_POST_NORM, FLAG_STAGED,
-    CONV_TAPS, FLAG_LOCAL_BWD, LOCAL_WINDOW,
+    CONV_TAPS, FLAG_LOCAL_BWD, FLAG_POOL_SCALE, LOCAL_WINDOW,
     STAGE_EPILOGUE, STAGE_POOL, STAGE_PROJ, STAGE_ROWS, STAGE_SCAN,
     BwdCall, FastVimError, SSMCall, bwd_workspace_bytes, calib_copy, lib, make_dims, ssm_bwd, ssm_fwd,
     workspace_bytes,

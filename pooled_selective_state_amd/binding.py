@@ -34,6 +34,8 @@ FLAG_CONV = 8
 CONV_TAPS = 4
 FLAG_LOCAL_BWD = 16
 LOCAL_WINDOW = 16
+# FLAG_POOL_SCALE: the pooled tokens times params.pool_scale (0.25 in the MAE transfer recipe)
+FLAG_POOL_SCALE = 32
 
 STATUS = {
     0: "FASTVIM_OK", -1: "FASTVIM_ERR_NULL", -2: "FASTVIM_ERR_DIMS", -3: "FASTVIM_ERR_UNSUPPORTED",
@@ -65,7 +67,7 @@ class Params(ctypes.Structure):
     _fields_ = [("fwd", DirParams), ("bwd", DirParams), ("workspace", ctypes.c_void_p),
                 ("workspace_bytes", ctypes.c_size_t), ("flags", ctypes.c_uint32), ("reserved", ctypes.c_uint32),
                 ("ln_weight", ctypes.c_void_p), ("ln_bias", ctypes.c_void_p), ("ln_eps", ctypes.c_float),
-                ("reserved2", ctypes.c_uint32), ("conv_w", ctypes.c_void_p), ("conv_b", ctypes.c_void_p),
+                ("pool_scale", ctypes.c_float), ("conv_w", ctypes.c_void_p), ("conv_b", ctypes.c_void_p),
                 ("saved_u", ctypes.c_void_p)]
 
 
@@ -211,13 +213,15 @@ class SSMCall:
     conv = {"weight": (E, 4), "bias": (E,)} (fp32 device tensors) makes x the
     input of the producer Conv1D + SiLU, computed inside the layer.
     saved_u (B, T, E) fp32 (pooled layers) receives the pooled tokens, for a
-    later backward call given the same tensor."""
+    later backward call given the same tensor.  pool_scale (pooled layers):
+    multiply the pooled tokens by this factor (FLAG_POOL_SCALE)."""
 
     def __init__(self, x: torch.Tensor, z: torch.Tensor, params: Dict[str, Dict[str, torch.Tensor]],
                  pool_axis: int, mask_idx: Optional[torch.Tensor] = None, hw: Optional[Tuple[int, int]] = None,
                  out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
                  flags: int = 0, ln: Optional[Dict[str, object]] = None,
-                 conv: Optional[Dict[str, torch.Tensor]] = None, saved_u: Optional[torch.Tensor] = None):
+                 conv: Optional[Dict[str, torch.Tensor]] = None, saved_u: Optional[torch.Tensor] = None,
+                 pool_scale: Optional[float] = None):
         self.dims = _layer_dims(x, z, params, mask_idx, hw)
         self.pool_axis = pool_axis
         self.x, self.z, self.mask_idx = x, z, mask_idx
@@ -247,8 +251,11 @@ class SSMCall:
             flags |= FLAG_CONV
         _check_saved_u(saved_u)
         self.saved_u = saved_u
+        if pool_scale is not None:
+            flags |= FLAG_POOL_SCALE
         self.params = Params(dirs[0], dirs[1], workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-                             flags, 0, _ptr(ln_w), _ptr(ln_b), ln_eps, 0, _ptr(conv_w), _ptr(conv_b),
+                             flags, 0, _ptr(ln_w), _ptr(ln_b), ln_eps,
+                             1.0 if pool_scale is None else float(pool_scale), _ptr(conv_w), _ptr(conv_b),
                              _ptr(saved_u))
 
     def _args(self):
@@ -285,10 +292,10 @@ class SSMCall:
 
 
 def ssm_fwd(x, z, params, pool_axis=POOL_COLS, mask_idx=None, hw=None, out=None, workspace=None, stream=None,
-            flags=0, ln=None, conv=None, saved_u=None):
+            flags=0, ln=None, conv=None, saved_u=None, pool_scale=None):
     """The pooled bidirectional selective-scan layer; returns out."""
     return SSMCall(x, z, params, pool_axis, mask_idx=mask_idx, hw=hw, out=out, workspace=workspace,
-                   flags=flags, ln=ln, conv=conv, saved_u=saved_u).run(stream)
+                   flags=flags, ln=ln, conv=conv, saved_u=saved_u, pool_scale=pool_scale).run(stream)
 
 
 class BwdCall:
@@ -299,8 +306,9 @@ class BwdCall:
     parameters; with ln also "ln": {"weight", "bias"}) are allocated unless
     given.  ln: the post-SSM LayerNorm of the forward call.  saved_u: the
     pooled tokens a forward call with the same x wrote (then x is read once,
-    not twice).  run() returns {"dx": dx, "dz": dz, "fwd": {...}, "bwd": {...}}
-    and, with ln, "ln": {"weight": ..., "bias": ...}."""
+    not twice).  pool_scale: as for the forward call.  run() returns
+    {"dx": dx, "dz": dz, "fwd": {...}, "bwd": {...}} and, with ln,
+    "ln": {"weight": ..., "bias": ...}."""
 
     def __init__(self, x: torch.Tensor, z: torch.Tensor, dout: torch.Tensor,
                  params: Dict[str, Dict[str, torch.Tensor]], pool_axis: int,
@@ -308,7 +316,8 @@ class BwdCall:
                  dx: Optional[torch.Tensor] = None, dz: Optional[torch.Tensor] = None,
                  grads: Optional[Dict[str, Dict[str, torch.Tensor]]] = None,
                  workspace: Optional[torch.Tensor] = None, flags: int = 0,
-                 saved_u: Optional[torch.Tensor] = None, ln: Optional[Dict[str, object]] = None):
+                 saved_u: Optional[torch.Tensor] = None, ln: Optional[Dict[str, object]] = None,
+                 pool_scale: Optional[float] = None):
         self.dims = _layer_dims(x, z, params, mask_idx, hw)
         if dout.dtype != x.dtype or dout.shape != x.shape:
             raise ValueError("dout must match x in shape and dtype")
@@ -351,8 +360,11 @@ class BwdCall:
         self.workspace = workspace
         _check_saved_u(saved_u)
         self.saved_u = saved_u
+        if pool_scale is not None:
+            flags |= FLAG_POOL_SCALE
         self.params = Params(dirs[0], dirs[1], workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-                             flags, 0, _ptr(ln_w), _ptr(ln_b), ln_eps, 0, None, None, _ptr(saved_u))
+                             flags, 0, _ptr(ln_w), _ptr(ln_b), ln_eps,
+                             1.0 if pool_scale is None else float(pool_scale), None, None, _ptr(saved_u))
 
     def run(self, stream=None) -> Dict[str, object]:
         st = lib().fastvim_ssm_bwd(_ptr(self.x), _ptr(self.z), _ptr(self.dout), ctypes.byref(self.params),
@@ -367,10 +379,10 @@ class BwdCall:
 
 
 def ssm_bwd(x, z, dout, params, pool_axis=POOL_COLS, mask_idx=None, hw=None, workspace=None, stream=None,
-            flags=0, saved_u=None, ln=None):
+            flags=0, saved_u=None, ln=None, pool_scale=None):
     """Gradients of the layer; returns {"dx", "dz", "fwd": {...}, "bwd": {...}} (and "ln" with ln)."""
     return BwdCall(x, z, dout, params, pool_axis, mask_idx=mask_idx, hw=hw, workspace=workspace,
-                   flags=flags, saved_u=saved_u, ln=ln).run(stream)
+                   flags=flags, saved_u=saved_u, ln=ln, pool_scale=pool_scale).run(stream)
 
 
 def calib_copy(dst: torch.Tensor, src: torch.Tensor, stream=None) -> None:

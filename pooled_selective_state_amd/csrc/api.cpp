@@ -1,6 +1,7 @@
 // Host side of the C ABI: argument validation, workspace layout, stage
 // dispatch and intermediate-result export.  Every check runs on the host
 // before anything is enqueued, so an argument error launches nothing.
+#include <cmath>
 #include <cstdint>
 #include <cstring>
 
@@ -84,15 +85,25 @@ fastvim_params effective_params(const fastvim_params& p) {
     return q;
 }
 
+// FASTVIM_FLAG_POOL_SCALE: a finite factor, pooled layers only, into g.
+int apply_pool_scale(const fastvim_params& p, Geom* g) {
+    if (!(p.flags & FASTVIM_FLAG_POOL_SCALE)) return FASTVIM_OK;
+    if (!g->pooled || !std::isfinite(p.pool_scale)) return FASTVIM_ERR_ARG;
+    g->pool_scale = p.pool_scale;
+    return FASTVIM_OK;
+}
+
 // Full validation of a layer call.  *empty is set for B == 0.
 int validate(const void* x, const void* z, const fastvim_params* prm, const fastvim_dims* d, int axis,
              const int32_t* idx, const void* out, Geom* g, Workspace* ws, bool* empty) {
     if (!prm) return FASTVIM_ERR_NULL;
     const uint32_t paths = FASTVIM_FLAG_STAGED | FASTVIM_FLAG_FUSED;
-    const uint32_t options = FASTVIM_FLAG_POST_NORM | FASTVIM_FLAG_CONV | FASTVIM_FLAG_LOCAL_BWD;
+    const uint32_t options =
+        FASTVIM_FLAG_POST_NORM | FASTVIM_FLAG_CONV | FASTVIM_FLAG_LOCAL_BWD | FASTVIM_FLAG_POOL_SCALE;
     if ((prm->flags & ~(paths | options)) || (prm->flags & paths) == paths) return FASTVIM_ERR_ARG;
     int st = resolve_geom(d, axis, g);
     if (st) return st;
+    if ((st = apply_pool_scale(*prm, g))) return st;
     if ((prm->flags & FASTVIM_FLAG_CONV) &&
         (!g->pooled || g->masked || (prm->flags & FASTVIM_FLAG_POST_NORM)))
         return FASTVIM_ERR_UNSUPPORTED;
@@ -188,11 +199,13 @@ int validate_bwd(const void* x, const void* z, const void* dout, const fastvim_p
                  BwdWorkspace* ws, bool* empty) {
     if (!prm) return FASTVIM_ERR_NULL;
     const uint32_t unsupported = FASTVIM_FLAG_FUSED | FASTVIM_FLAG_CONV | FASTVIM_FLAG_LOCAL_BWD;
-    if (prm->flags & ~(FASTVIM_FLAG_STAGED | FASTVIM_FLAG_POST_NORM | unsupported)) return FASTVIM_ERR_ARG;
+    const uint32_t options = FASTVIM_FLAG_STAGED | FASTVIM_FLAG_POST_NORM | FASTVIM_FLAG_POOL_SCALE;
+    if (prm->flags & ~(options | unsupported)) return FASTVIM_ERR_ARG;
     if (prm->flags & unsupported) return FASTVIM_ERR_UNSUPPORTED;
     const bool norm = (prm->flags & FASTVIM_FLAG_POST_NORM) != 0;
     int st = resolve_geom(d, axis, g);
     if (st) return st;
+    if ((st = apply_pool_scale(*prm, g))) return st;
     if (!bwd_supported(*g) || (norm && !bwd_norm_supported(*g))) return FASTVIM_ERR_UNSUPPORTED;
     if (!g->masked && idx) return FASTVIM_ERR_ARG;
     if (!gr) return FASTVIM_ERR_NULL;

@@ -200,7 +200,7 @@ hipError_t bwd_pool_t(const Geom& g, const void* x, const void* z, const void* d
     if (g.masked) {
         hipLaunchKernelGGL((bwd_pool_masked_kernel<IO, POOL>), dim3((unsigned)(g.B * g.T)), dim3(threads), lds, st,
                            xe, ze, de, ws.fwd.rows, ws.fwd.u, ws.gs, g.T, g.K, (int)VE, G, g.E,
-                           1.0f / (float)g.P);
+                           pool_norm(g));
     } else {
         const int64_t t_stride = g.axis == FASTVIM_POOL_COLS ? g.w * g.E : g.E;
         const int64_t p_stride = g.axis == FASTVIM_POOL_COLS ? g.E : g.w * g.E;
@@ -208,11 +208,11 @@ hipError_t bwd_pool_t(const Geom& g, const void* x, const void* z, const void* d
         if (bytes > kMallBytes)
             hipLaunchKernelGGL((bwd_pool_dense_kernel<IO, POOL, true>), dim3((unsigned)(g.B * g.T)), dim3(threads),
                                lds, st, xe, ze, de, ws.fwd.u, ws.gs, g.T, g.P, (int)VE, G, g.E, g.h * g.w * g.E,
-                               t_stride, p_stride, 1.0f / (float)g.P);
+                               t_stride, p_stride, pool_norm(g));
         else
             hipLaunchKernelGGL((bwd_pool_dense_kernel<IO, POOL, false>), dim3((unsigned)(g.B * g.T)), dim3(threads),
                                lds, st, xe, ze, de, ws.fwd.u, ws.gs, g.T, g.P, (int)VE, G, g.E, g.h * g.w * g.E,
-                               t_stride, p_stride, 1.0f / (float)g.P);
+                               t_stride, p_stride, pool_norm(g));
     }
     return hipGetLastError();
 }
@@ -558,7 +558,7 @@ hipError_t bwd_epi_launch(const Geom& g, const void* x, const void* z, const voi
                        static_cast<const elem*>(x), static_cast<const elem*>(z), static_cast<const elem*>(dout),
                        ws.fwd.s_f, ws.fwd.s_b, ws.du, p.fwd.D, p.bwd.D, static_cast<elem*>(dx),
                        static_cast<elem*>(dz), ws.fwd.rows, ws.dDp, g.T, g.h, g.w, g.K, g.E, (int)sh.VE, (int)sh.G,
-                       sh.seg_len, sh.blocks_per_seg, sh.segs_per_img, 1.0f / (float)g.P);
+                       sh.seg_len, sh.blocks_per_seg, sh.segs_per_img, pool_norm(g));
     return hipGetLastError();
 }
 

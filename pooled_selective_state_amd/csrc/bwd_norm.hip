@@ -311,7 +311,7 @@ hipError_t pass2_dispatch(const Geom& g, const fastvim_params& p, const BwdWorks
     const int64_t bpi = (ncell * VE + 256 * kP2 - 1) / (256 * kP2);
     const dim3 grid((unsigned)(g.B * bpi)), block(256);
     elem *xe = static_cast<elem*>(dx), *ze = static_cast<elem*>(dz);
-    const float ip = 1.0f / (float)g.P;
+    const float ip = pool_norm(g);
     if (g.masked)
         hipLaunchKernelGGL((bwd_norm_pass2_kernel<IO, 2>), grid, block, 0, st, xe, ze, ws.du, p.fwd.D, p.bwd.D,
                            ws.fwd.rows, g.T, g.w, ncell, (int)VE, bpi, ip);

@@ -249,11 +249,11 @@ hipError_t conv_pool_t(const Geom& g, const void* x, const fastvim_params& p, co
     if (g.axis == FASTVIM_POOL_COLS)
         hipLaunchKernelGGL((conv_pool_kernel<IO, true>), dim3((unsigned)(g.B * g.T)), dim3(threads), lds, st, xe,
                            p.conv_w, p.conv_b, ws.u, (int)g.T, (int)g.P, (int)g.h, (int)g.w, (int)VE, (int)G,
-                           (int)g.E, 1.0f / (float)g.P);
+                           (int)g.E, pool_norm(g));
     else
         hipLaunchKernelGGL((conv_pool_kernel<IO, false>), dim3((unsigned)(g.B * g.T)), dim3(threads), lds, st, xe,
                            p.conv_w, p.conv_b, ws.u, (int)g.T, (int)g.P, (int)g.h, (int)g.w, (int)VE, (int)G,
-                           (int)g.E, 1.0f / (float)g.P);
+                           (int)g.E, pool_norm(g));
     return hipGetLastError();
 }
 

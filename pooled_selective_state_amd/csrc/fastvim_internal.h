@@ -20,7 +20,11 @@ struct Geom {
     bool masked;  // K > 0
     bool pooled;  // axis is COLS or ROWS
     int io;       // fastvim_dtype
+    float pool_scale = 1.f;  // factor on the pooled tokens (FASTVIM_FLAG_POOL_SCALE)
 };
+
+// What a pooled row sum is multiplied by: pool_scale / P.
+inline float pool_norm(const Geom& g) { return g.pool_scale / (float)g.P; }
 
 // Workspace carve-up (every region 256-byte aligned).
 struct Workspace {

@@ -73,6 +73,7 @@ struct FusedArgs {
     const float* ln_w;  // post-SSM LayerNorm (NORM instances)
     const float* ln_b;
     float ln_eps;
+    float pool_norm;  // pool_scale / P
     unsigned* sync;  // [0] ticket, [1] status, [2, 2+B) rowsDone, [2+B, 2+2B) scanDone
     int64_t B, h, w, E, T, P;
     int R, NX, axis;
@@ -132,7 +133,7 @@ __device__ void item_pool_proj(const FusedArgs& a, int64_t b, int k, float* lds)
     const int npos = (int)(T - t0 < a.RG ? T - t0 : a.RG);
     const bool cols = a.axis == FASTVIM_POOL_COLS;
     const int64_t p_stride = cols ? E : a.w * E;
-    const float inv_p = 1.0f / (float)P;
+    const float inv_p = a.pool_norm;
     const int NO = 2 * a.NX;
     float* red = lds;                        // [G][E]
     float* urow = lds + (int64_t)G * E;      // [RG][E]
@@ -552,6 +553,7 @@ bool plan(const Geom& g, FusedArgs* a, bool norm, bool local) {
     }
     RE = RE < 1 ? 1 : (RE > g.h ? g.h : RE);
     a->B = g.B; a->h = g.h; a->w = g.w; a->E = g.E; a->T = g.T; a->P = g.P;
+    a->pool_norm = pool_norm(g);
     a->R = (int)g.R; a->NX = (int)g.NX; a->axis = g.axis;
     a->VE = (int)VE; a->G = G; a->KS = KS; a->RG = (int)RG; a->RE = (int)RE; a->CJ = (int)CJ;
     a->nA = (int)((g.T + RG - 1) / RG);

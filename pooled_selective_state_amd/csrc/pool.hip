@@ -164,7 +164,7 @@ hipError_t pool_dense_t(const Geom& g, const void* x, const Workspace& ws, hipSt
     const int64_t p_stride = g.axis == FASTVIM_POOL_COLS ? g.E : g.w * g.E;
     hipLaunchKernelGGL(pool_dense_kernel<IO>, dim3((unsigned)(g.B * g.T)), dim3(threads), lds, st,
                        static_cast<const typename IO::elem*>(x), ws.u, g.T, g.P, (int)VE, G, g.E,
-                       g.h * g.w * g.E, t_stride, p_stride, 1.0f / (float)g.P);
+                       g.h * g.w * g.E, t_stride, p_stride, pool_norm(g));
     return hipGetLastError();
 }
 
@@ -176,7 +176,7 @@ hipError_t pool_masked_t(const Geom& g, const void* x, const Workspace& ws, hipS
     const size_t lds = (size_t)G * VE * IO::V * sizeof(float);
     hipLaunchKernelGGL(pool_masked_kernel<IO>, dim3((unsigned)(g.B * g.T)), dim3(threads), lds, st,
                        static_cast<const typename IO::elem*>(x), ws.rows, ws.u, g.T, g.K, (int)VE, G, g.E,
-                       1.0f / (float)g.P);
+                       pool_norm(g));
     return hipGetLastError();
 }
 

@@ -46,15 +46,18 @@ def io_dtype(cfg_or_name):
     return torch.bfloat16 if cfg_or_name == "bf16" else torch.float32
 
 
-def gpu_call(x, z, params, axis, idx=None, hw=None, dtype=torch.float32, flags=0, ln=None, conv=None):
+def gpu_call(x, z, params, axis, idx=None, hw=None, dtype=torch.float32, flags=0, ln=None, conv=None,
+             pool_scale=None):
     """Prepared call on device copies of numpy inputs; returns the SSMCall.
     ln: None or {"weight", "bias", "eps"} (numpy) for the post-SSM LayerNorm;
-    conv: None or {"weight", "bias"} (numpy) for the producer Conv1D."""
+    conv: None or {"weight", "bias"} (numpy) for the producer Conv1D;
+    pool_scale: None or the factor on the pooled tokens."""
     xd, zd = dev(x, dtype), dev(z, dtype)
     idd = None if idx is None else dev(idx, torch.int32)
     lnd = None if ln is None else {"weight": dev(ln["weight"]), "bias": dev(ln["bias"]), "eps": ln["eps"]}
     cvd = None if conv is None else {"weight": dev(conv["weight"]), "bias": dev(conv["bias"])}
-    return P.SSMCall(xd, zd, dev_params(params), axis, mask_idx=idd, hw=hw, flags=flags, ln=lnd, conv=cvd)
+    return P.SSMCall(xd, zd, dev_params(params), axis, mask_idx=idd, hw=hw, flags=flags, ln=lnd, conv=cvd,
+                     pool_scale=pool_scale)
 
 
 def status_ok(call):

@@ -32,7 +32,7 @@ def test_library_exports_every_declared_function():
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(Bd.EXPORTED_SYMBOLS)
-    assert lib.fastvim_abi_version() == 8
+    assert lib.fastvim_abi_version() == 9
 
 
 def test_status_strings():
@@ -49,6 +49,7 @@ def test_struct_layout_matches_header():
     assert ctypes.sizeof(Bd.DirParams) == 40
     assert ctypes.sizeof(Bd.Params) == 2 * 40 + 8 + 8 + 8 + 8 + 8 + 4 + 4 + 8 + 8 + 8
     assert Bd.Params.saved_u.offset == ctypes.sizeof(Bd.Params) - 8
+    assert Bd.Params.pool_scale.offset == Bd.Params.ln_eps.offset + 4
     assert ctypes.sizeof(Bd.DirGrads) == 40 and ctypes.sizeof(Bd.Grads) == 96
     assert Bd.Grads.ln_weight.offset == 80 and Bd.Grads.ln_bias.offset == 88
 
@@ -153,7 +154,7 @@ def test_bad_enums():
     c = FakeCall()
     assert lib.fastvim_ssm_stage(5, c.x, c.z, ctypes.byref(c.params), ctypes.byref(c.dims), 0, None, c.out,
                                  None) == EARG
-    for flags in (P.FLAG_STAGED | P.FLAG_FUSED, 32, 1 << 31):  # conflicting or unknown flags
+    for flags in (P.FLAG_STAGED | P.FLAG_FUSED, 64, 1 << 31):  # conflicting or unknown flags
         c = FakeCall()
         c.params.flags = flags
         expect(c, EARG)
@@ -358,7 +359,7 @@ def test_bwd_unsupported_and_bad_flags():
         assert FakeBwd(axis=axis).bwd() == EUNSUP
     assert FakeBwd(h=129).bwd() == EUNSUP
     assert FakeBwd(N=8).bwd() == EUNSUP
-    for flags, code in ((P.FLAG_FUSED, EUNSUP), (P.FLAG_CONV, EUNSUP), (P.FLAG_LOCAL_BWD, EUNSUP), (32, EARG),
+    for flags, code in ((P.FLAG_FUSED, EUNSUP), (P.FLAG_CONV, EUNSUP), (P.FLAG_LOCAL_BWD, EUNSUP), (64, EARG),
                         (P.FLAG_STAGED, OK)):
         c = FakeBwd()
         c.params.flags = flags
@@ -377,6 +378,36 @@ def _norm_bwd(**kw):
     c.params.ln_weight, c.params.ln_bias, c.params.ln_eps = far, far + 65536, 1e-5
     c.grads.ln_weight, c.grads.ln_bias = far + 2 * 65536, far + 3 * 65536
     return c
+
+
+def test_pool_scale_validation():
+    """The pool scale needs a pooled layer and a finite value, in both calls;
+    a valid one passes every check (the call then stops at the workspace)."""
+    for axis in (P.POOL_NONE_ROWMAJOR, P.POOL_NONE_COLMAJOR):
+        c = FakeCall(axis=axis)
+        c.params.flags, c.params.pool_scale = P.FLAG_POOL_SCALE, 0.25
+        expect(c, EARG)
+    for v in (float("nan"), float("inf"), -float("inf")):
+        c = FakeCall()
+        c.params.flags, c.params.pool_scale = P.FLAG_POOL_SCALE, v
+        expect(c, EARG)
+        c = FakeBwd()
+        c.params.flags, c.params.pool_scale = P.FLAG_POOL_SCALE, v
+        assert c.bwd() == EARG
+    for v in (0.25, -3.0, 0.0):
+        c = FakeCall(K=3)
+        c.params.flags, c.params.pool_scale = P.FLAG_POOL_SCALE, v
+        c.params.workspace_bytes -= 1
+        expect(c, EWS)
+        c = FakeBwd()
+        c.params.flags, c.params.pool_scale = P.FLAG_POOL_SCALE, v
+        c.params.workspace_bytes -= 1
+        assert c.bwd() == EWS
+    # without the flag the field is not looked at
+    c = FakeCall()
+    c.params.pool_scale = float("nan")
+    c.params.workspace_bytes -= 1
+    expect(c, EWS)
 
 
 def test_bwd_post_norm_validation():
@@ -486,7 +517,7 @@ def test_conv_validation():
     c.params.flags = P.FLAG_CONV
     assert c.bwd() == EUNSUP
     c = FakeCall()
-    c.params.flags = 32
+    c.params.flags = 64
     expect(c, EARG)
 
 
