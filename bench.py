@@ -29,8 +29,9 @@ Reported besides images/s:
                 bidirectional one, the 1024^2 two-block chain, and the small
                 workloads over rotating input sets.
 --profile-run times a few steps and the calibration copy only (for profiler
-runs); --profile-bwd adds three backward calls of the same workload, then
-three more given the pooled tokens a forward call saved.
+runs); --profile-bwd adds three backward calls of the same workload, three
+more given the pooled tokens a forward call saved, and three with the
+post-SSM LayerNorm (pooled tokens saved).
 """
 from __future__ import annotations
 
@@ -306,8 +307,11 @@ def main():
         dout = torch.randn(x.shape, device=dev, generator=torch.Generator(device="cuda").manual_seed(2))
         su = torch.empty((cfg.B, cfg.h, cfg.E), device=dev)
         P.SSMCall(x, z, prm, P.POOL_COLS, workspace=call.workspace, out=call.out, saved_u=su).run(stream)
-        for kept in (None, su):
-            bcall = P.BwdCall(x, z, dout, prm, P.POOL_COLS, saved_u=kept)
+        g_ln = torch.Generator(device="cuda").manual_seed(1)
+        ln = {"weight": 1.0 + 0.1 * torch.randn(cfg.E, device=dev, generator=g_ln),
+              "bias": 0.1 * torch.randn(cfg.E, device=dev, generator=g_ln), "eps": 1e-5}
+        for kept, lnk in ((None, None), (su, None), (su, ln)):
+            bcall = P.BwdCall(x, z, dout, prm, P.POOL_COLS, saved_u=kept, ln=lnk)
             for _ in range(3):
                 bcall.run(stream)
             torch.cuda.synchronize()
@@ -381,8 +385,23 @@ def main():
                 del bcall
             extras["backward_2048"][name] = res
             del su
-        del dout
-        log("backward %.3f ms (cols, saved u)" % extras["backward_2048"]["cols"]["saved_u"]["ms"])
+        # with the post-SSM LayerNorm: the forward stages run first, the norm's
+        # adjoint in the first pass, and the second pass turns g into dx in place
+        su = torch.empty((cfg.B, cfg.h, cfg.E), device=dev)
+        P.SSMCall(x, z, prm, P.POOL_COLS, workspace=call.workspace, out=call.out, saved_u=su, ln=ln).run(stream)
+        res = {}
+        for kind, kept in (("pools_x", None), ("saved_u", su)):
+            bcall = P.BwdCall(x, z, dout, prm, P.POOL_COLS, saved_u=kept, ln=ln)
+            bcall.run(stream)
+            b_ms, _ = time_steps(lambda: bcall.run(stream), n, stream)
+            res[kind] = {"ms": b_ms, "images_per_s": cfg.B / (b_ms * 1e-3),
+                         "GBps": bwd_bytes / (b_ms * 1e-3) / 1e9,
+                         "hbm_frac": bwd_bytes / (b_ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+            del bcall
+        extras["backward_2048"]["post_norm_cols"] = res
+        del su, dout
+        log("backward %.3f ms (cols, saved u), with the LayerNorm %.3f ms"
+            % (extras["backward_2048"]["cols"]["saved_u"]["ms"], res["saved_u"]["ms"]))
         # torch's device copy, for comparison with the calibration copy
         dst = torch.empty_like(x)
         tc_ms, _ = time_steps(lambda: dst.copy_(x), 3, stream)
