@@ -105,7 +105,7 @@ class Oracle:
             vp, vp, vp, ctypes.POINTER(_Dir), ctypes.POINTER(_Dir),
             i64, i64, i64, i64, i64, i64, i64, ci, vp,
             vp, vp, ctypes.POINTER(_DirGrad), ctypes.POINTER(_DirGrad), ctypes.POINTER(_BwdStages),
-            vp, vp, ctypes.c_double, vp, vp, ctypes.c_double,
+            vp, vp, ctypes.c_double, vp, vp, ctypes.c_double, i64,
         ]
         lib.fvo_layer_bwd.restype = ci
         self._lib = lib
@@ -266,14 +266,18 @@ class Oracle:
             return out
         return {"out": out, "u": u, "rows": rows, "fwd": st["fwd"], "bwd": st["bwd"]}
 
-    def layer_bwd(self, x, z, dout, fwd, bwd, axis, idx=None, hw=None, stages=False, ln=None, pool_scale=1.0):
+    def layer_bwd(self, x, z, dout, fwd, bwd, axis, idx=None, hw=None, stages=False, ln=None, pool_scale=1.0,
+                  local_window=0):
         """Gradients of sum(dout * layer(x, z, ...)).  Arguments as layer();
         dout is shaped like x.  Returns a dict with dx, dz (fp64, shaped like
         x) and "fwd" / "bwd" dicts of parameter gradients keyed like the
         parameters; with ln (as in layer()) also "ln": {"weight", "bias"}, the
         LayerNorm's gradients; with stages=True also gs (dL/ds, which is dL/dy
         of the LayerNorm's input when ln is given), du (B,T,E) and dv_fwd,
-        dv_bwd (B,T,NX)."""
+        dv_bwd (B,T,NX).  local_window, pool_scale: as in layer(); with the local
+        backward scan the shared parameters' gradients are in "fwd" and the
+        backward set's x_proj_w, dt_proj_w, dt_proj_b and A_log gradients
+        are zero."""
         x, z, dout = _f32(x), _f32(z), _f32(dout)
         ln_w = ln_b = dln_w = dln_b = None
         ln_eps = 0.0
@@ -318,7 +322,7 @@ class Oracle:
             B, h, w, E, N, R, K, axis, _ptr(idx_a), _ptr(dx), _ptr(dz),
             ctypes.byref(structs[0]), ctypes.byref(structs[1]),
             ctypes.byref(st) if st is not None else None,
-            _ptr(ln_w), _ptr(ln_b), ln_eps, _ptr(dln_w), _ptr(dln_b), float(pool_scale),
+            _ptr(ln_w), _ptr(ln_b), ln_eps, _ptr(dln_w), _ptr(dln_b), float(pool_scale), int(local_window),
         )
         if rc:
             raise ValueError("fvo_layer_bwd failed: %d" % rc)
@@ -388,6 +392,7 @@ def conv_silu(x, axis, conv):
     return get().conv_silu(x, axis, conv)
 
 
-def layer_bwd(x, z, dout, fwd, bwd, axis, idx=None, hw=None, stages=False, ln=None, pool_scale=1.0):
+def layer_bwd(x, z, dout, fwd, bwd, axis, idx=None, hw=None, stages=False, ln=None, pool_scale=1.0,
+              local_window=0):
     return get().layer_bwd(x, z, dout, fwd, bwd, axis, idx=idx, hw=hw, stages=stages, ln=ln,
-                           pool_scale=pool_scale)
+                           pool_scale=pool_scale, local_window=local_window)

@@ -610,11 +610,13 @@ static void output_token_adjoint_ln(const double *sf, const double *sb, const fl
  *   dC_k[n]   += gs_k H_k[n]                     (summed over channels e)
  *   dA[e, n]  += lambda_k[n] a_k[n] delta_k H_{k-1}[n]
  * dB and dC land in dv[m, R + n] and dv[m, R + N + n].  The states of the
- * forward sweep are kept whole (T*N doubles per channel).
+ * forward sweep are kept whole (T*N doubles per channel).  reset (per time t,
+ * or NULL) as in fvo_scan: a step with reset[t] set has the decay a_k = 0, so
+ * no state and no adjoint cross it, and its decay terms vanish.
  */
 static int scan_adjoint(const double *u, const double *delta, const double *v, const double *gs, int64_t B,
                         int64_t T, int64_t E, int64_t N, int64_t R, int64_t NX, const float *A_log, int reverse,
-                        double *du, double *ddelta, double *dv, double *dA)
+                        const unsigned char *reset, double *du, double *ddelta, double *dv, double *dA)
 {
     double *Hs = (double *)malloc((size_t)(T * N) * sizeof(double));
     double *lam = (double *)malloc((size_t)N * sizeof(double));
@@ -624,22 +626,23 @@ static int scan_adjoint(const double *u, const double *delta, const double *v, c
         for (int64_t e = 0; e < E; ++e) {
             /* forward sweep, keeping every state */
             for (int64_t k = 0; k < T; ++k) {
-                const int64_t m = b * T + (reverse ? T - 1 - k : k);
+                const int64_t t = reverse ? T - 1 - k : k, m = b * T + t;
                 for (int64_t n = 0; n < N; ++n) {
                     const double A = -exp((double)A_log[e * N + n]);
                     const double prev = k > 0 ? Hs[(k - 1) * N + n] : 0.0;
-                    Hs[k * N + n] = exp(delta[m * E + e] * A) * prev + delta[m * E + e] * v[m * NX + R + n] * u[m * E + e];
+                    const double a = (reset && reset[t]) ? 0.0 : exp(delta[m * E + e] * A);
+                    Hs[k * N + n] = a * prev + delta[m * E + e] * v[m * NX + R + n] * u[m * E + e];
                 }
             }
             /* reverse sweep */
             for (int64_t n = 0; n < N; ++n) carry[n] = 0.0;
             for (int64_t k = T - 1; k >= 0; --k) {
-                const int64_t m = b * T + (reverse ? T - 1 - k : k);
+                const int64_t t = reverse ? T - 1 - k : k, m = b * T + t;
                 const double d = delta[m * E + e], ut = u[m * E + e], g = gs[m * E + e];
                 double dd = 0.0, duk = 0.0;
                 for (int64_t n = 0; n < N; ++n) {
                     const double A = -exp((double)A_log[e * N + n]);
-                    const double a = exp(d * A);
+                    const double a = reset && reset[t] ? 0.0 : exp(A * d);
                     const double Bn = v[m * NX + R + n], Cn = v[m * NX + R + N + n];
                     const double prev = k > 0 ? Hs[(k - 1) * N + n] : 0.0;
                     lam[n] = Cn * g + carry[n];
@@ -697,14 +700,21 @@ static void xproj_adjoint(const double *u, const double *dv, int64_t M, int64_t 
  * gradients go to dln_w, dln_b (E each, overwritten).  pool_scale as in
  * fvo_layer.  The pool's adjoint spreads du of a scan position over its
  * cells: dx[b, cell, e] = dx_skip + pool_scale du[b, t(cell), e] / P (P = 1
- * unpooled; the fixed row length for masked tokens).  Returns 0, -2,
+ * unpooled; the fixed row length for masked tokens).  local_window = L > 0:
+ * the layer of fvo_layer with LBMamba's local backward scan, which runs on
+ * the forward direction's x_proj, dt_proj and A_log with a reset at every t
+ * with t mod L = L - 1; the gradients of those shared parameters are the sums
+ * of both scans' contributions and go to the forward direction's gradients,
+ * while the backward direction's x_proj_w, dt_proj_w, dt_proj_b and A_log
+ * gradients are zero (the layer does not read them) and its D gradient is dD
+ * as usual.  Returns 0, -2,
  * -3 or -9 as fvo_layer.
  */
 int fvo_layer_bwd(const float *x, const float *z, const float *dout, const fvo_dir *pf, const fvo_dir *pb,
                   int64_t B, int64_t h, int64_t w, int64_t E, int64_t N, int64_t R, int64_t K, int axis,
                   const int32_t *idx, double *dx, double *dz, fvo_dir_grad *gf, fvo_dir_grad *gb,
                   fvo_bwd_stages *st, const float *ln_w, const float *ln_b, double ln_eps, double *dln_w,
-                  double *dln_b, double pool_scale)
+                  double *dln_b, double pool_scale, int64_t local_window)
 {
     int64_t T, P;
     const int masked = idx != NULL;
@@ -712,8 +722,11 @@ int fvo_layer_bwd(const float *x, const float *z, const float *dout, const fvo_d
     seq_shape(axis, h, w, &T, &P);
     const int64_t NX = R + 2 * N, M = B * T, ntok = masked ? B * K : B * h * w;
     const size_t me = (size_t)(M * E) * sizeof(double), mx = (size_t)(M * NX) * sizeof(double);
-    const fvo_dir *pd[2] = {pf, pb};
+    fvo_dir pl = *pf; /* the local scan: the forward set with the backward D */
+    pl.D = pb->D;
+    const fvo_dir *pd[2] = {pf, local_window > 0 ? &pl : pb};
     fvo_dir_grad *gd[2] = {gf, gb};
+    unsigned char *reset = NULL;
     int rc = 0;
 
     double *u = (double *)malloc(me), *gs = (double *)calloc((size_t)(M * E), sizeof(double));
@@ -732,6 +745,11 @@ int fvo_layer_bwd(const float *x, const float *z, const float *dout, const fvo_d
         for (int64_t e = 0; e < E; ++e) dln_w[e] = dln_b[e] = 0.0;
     for (int d = 0; d < 2; ++d)
         if (!v[d] || !q[d] || !dl[d] || !s[d] || !dv[d]) { rc = -9; goto done; }
+    if (local_window > 0) {
+        reset = (unsigned char *)malloc((size_t)T);
+        if (!reset) { rc = -9; goto done; }
+        for (int64_t t = 0; t < T; ++t) reset[t] = (unsigned char)((t + 1) % local_window == 0);
+    }
 
     /* forward recomputation: pooled input, per-direction v, q, delta, s */
     if (masked) {
@@ -746,7 +764,7 @@ int fvo_layer_bwd(const float *x, const float *z, const float *dout, const fvo_d
         fvo_xproj(u, M, E, pd[d]->x_proj_w, NX, v[d]);
         dt_preact(v[d], M, NX, R, pd[d]->dt_proj_w, pd[d]->dt_proj_b, E, q[d]);
         for (int64_t i = 0; i < M * E; ++i) dl[d][i] = softplus(q[d][i]);
-        fvo_scan(u, dl[d], v[d], B, T, E, N, R, NX, pd[d]->A_log, d, NULL, s[d]);
+        fvo_scan(u, dl[d], v[d], B, T, E, N, R, NX, pd[d]->A_log, d, d == 1 ? reset : NULL, s[d]);
     }
 
     /* adjoint of the output (gate, skip, repeat): dz, the skip part of dx, dD and gs */
@@ -774,13 +792,22 @@ int fvo_layer_bwd(const float *x, const float *z, const float *dout, const fvo_d
         for (int64_t i = 0; i < E * R; ++i) o->dt_proj_w[i] = 0.0;
         for (int64_t i = 0; i < E * N; ++i) o->A_log[i] = 0.0;
         for (int64_t e = 0; e < E; ++e) o->dt_proj_b[e] = 0.0;
-        rc = scan_adjoint(u, dl[d], v[d], gs, B, T, E, N, R, NX, pd[d]->A_log, d, du, dd, dv[d], o->A_log);
+        rc = scan_adjoint(u, dl[d], v[d], gs, B, T, E, N, R, NX, pd[d]->A_log, d, d == 1 ? reset : NULL, du, dd,
+                          dv[d], o->A_log);
         if (rc) goto done;
         /* dA -> dA_log: A = -exp(A_log), so dA/dA_log = A */
         for (int64_t i = 0; i < E * N; ++i) o->A_log[i] *= -exp((double)pd[d]->A_log[i]);
         step_size_adjoint(q[d], dd, v[d], M, NX, R, E, pd[d]->dt_proj_w, o->dt_proj_w, o->dt_proj_b, dv[d]);
         xproj_adjoint(u, dv[d], M, NX, E, pd[d]->x_proj_w, o->x_proj_w, du);
         for (int64_t e = 0; e < E; ++e) o->D[e] = dD[e];
+    }
+    if (local_window > 0) {
+        /* the local scan's parameters are the forward direction's: add its
+         * contributions there; the backward set's unused gradients are zero */
+        for (int64_t i = 0; i < NX * E; ++i) { gf->x_proj_w[i] += gb->x_proj_w[i]; gb->x_proj_w[i] = 0.0; }
+        for (int64_t i = 0; i < E * R; ++i) { gf->dt_proj_w[i] += gb->dt_proj_w[i]; gb->dt_proj_w[i] = 0.0; }
+        for (int64_t i = 0; i < E * N; ++i) { gf->A_log[i] += gb->A_log[i]; gb->A_log[i] = 0.0; }
+        for (int64_t e = 0; e < E; ++e) { gf->dt_proj_b[e] += gb->dt_proj_b[e]; gb->dt_proj_b[e] = 0.0; }
     }
 
     /* adjoint of the pool */
@@ -803,7 +830,7 @@ int fvo_layer_bwd(const float *x, const float *z, const float *dout, const fvo_d
     }
 
 done:
-    free(u); free(gs); free(du); free(dd); free(g); free(ny); free(dxs); free(dD); free(rows);
+    free(u); free(gs); free(du); free(dd); free(g); free(ny); free(dxs); free(dD); free(rows); free(reset);
     for (int d = 0; d < 2; ++d) { free(v[d]); free(q[d]); free(dl[d]); free(s[d]); free(dv[d]); }
     return rc;
 }

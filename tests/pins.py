@@ -520,9 +520,9 @@ def _bwd_case(rng, axis, masked, B_=2, h=4, w=3, E=5, N=3, R=2):
     return pf, pb, x, z, dout, idx, (h, w)
 
 
-def _loss(O, x, z, dout, pf, pb, axis, idx, hw, ln=None, pool_scale=1.0):
+def _loss(O, x, z, dout, pf, pb, axis, idx, hw, ln=None, pool_scale=1.0, local=0):
     return float(np.sum(dout.astype(np.float64) * O.layer(x, z, pf, pb, axis, idx=idx, hw=hw, ln=ln,
-                                                          pool_scale=pool_scale)))
+                                                          pool_scale=pool_scale, local_window=local)))
 
 
 def _perturbed(a, V, eps):
@@ -539,15 +539,18 @@ def pin_bwd_finite_differences(O):
     O(eps^2) truncation error (~1e-9 relative at eps = 2^-14) and the fp64
     rounding of the two losses, at most a few ulps of sum |dout out| divided
     by 2 eps (which matters only for a gradient near zero); also with the
-    pooled tokens scaled by 1/4."""
+    pooled tokens scaled by 1/4, and with LBMamba's local backward scan
+    (windows of 2, 3 and 5 steps, the last one partial; the backward set's
+    unused parameters then have zero gradients)."""
     eps = 2.0 ** -14
     rng = np.random.default_rng(40)
-    cases = ((COLS, False, 1.0), (ROWS, False, 1.0), (NONE_ROWMAJOR, False, 1.0), (NONE_COLMAJOR, False, 1.0),
-             (COLS, True, 1.0), (ROWS, True, 1.0), (COLS, False, 0.25), (ROWS, True, 0.25))
-    for axis, masked, scale in cases:
+    cases = ((COLS, False, 1.0, 0), (ROWS, False, 1.0, 0), (NONE_ROWMAJOR, False, 1.0, 0),
+             (NONE_COLMAJOR, False, 1.0, 0), (COLS, True, 1.0, 0), (ROWS, True, 1.0, 0), (COLS, False, 0.25, 0),
+             (ROWS, True, 0.25, 0), (COLS, False, 1.0, 3), (ROWS, True, 1.0, 2), (NONE_ROWMAJOR, False, 0.25, 5))
+    for axis, masked, scale, local in cases:
         pf, pb, x, z, dout, idx, hw = _bwd_case(rng, axis, masked)
-        g = O.layer_bwd(x, z, dout, pf, pb, axis, idx=idx, hw=hw, pool_scale=scale)
-        out = O.layer(x, z, pf, pb, axis, idx=idx, hw=hw, pool_scale=scale)
+        g = O.layer_bwd(x, z, dout, pf, pb, axis, idx=idx, hw=hw, pool_scale=scale, local_window=local)
+        out = O.layer(x, z, pf, pb, axis, idx=idx, hw=hw, pool_scale=scale, local_window=local)
         floor = 64 * 2.0 ** -52 * float(np.sum(np.abs(dout * out))) / (2.0 * eps)
         targets = [("x", None), ("z", None)] + [(d, k) for d in ("fwd", "bwd") for k in
                                                  ("x_proj_w", "dt_proj_w", "dt_proj_b", "A_log", "D")]
@@ -567,12 +570,13 @@ def pin_bwd_finite_differences(O):
                     arg[d] = pert
                 else:
                     arg["pf" if d == "fwd" else "pb"][k] = pert
-                L.append(_loss(O, arg["x"], arg["z"], dout, arg["pf"], arg["pb"], axis, idx, hw, pool_scale=scale))
+                L.append(_loss(O, arg["x"], arg["z"], dout, arg["pf"], arg["pb"], axis, idx, hw, pool_scale=scale,
+                               local=local))
             fd = (L[0] - L[1]) / (2.0 * eps)
             an = float(np.sum(grad * V))
             size = max(float(np.linalg.norm(grad)), 1e-30)
-            assert abs(fd - an) <= 1e-6 * size + floor, "axis %d masked %s pool scale %g: d/d%s %s: analytic %.12g, " \
-                "finite difference %.12g" % (axis, masked, scale, d, k or "", an, fd)
+            assert abs(fd - an) <= 1e-6 * size + floor, "axis %d masked %s pool scale %g local %d: d/d%s %s: " \
+                "analytic %.12g, finite difference %.12g" % (axis, masked, scale, local, d, k or "", an, fd)
 
 
 def pin_bwd_finite_differences_ln(O):
@@ -581,11 +585,12 @@ def pin_bwd_finite_differences_ln(O):
     of the forward oracle with the norm along a random +-1 direction."""
     eps = 2.0 ** -14
     rng = np.random.default_rng(42)
-    for axis, masked in ((COLS, False), (ROWS, False), (NONE_ROWMAJOR, False), (ROWS, True)):
+    for axis, masked, local in ((COLS, False, 0), (ROWS, False, 0), (NONE_ROWMAJOR, False, 0), (ROWS, True, 0),
+                                (COLS, False, 3)):
         pf, pb, x, z, dout, idx, hw = _bwd_case(rng, axis, masked)
         E = x.shape[-1]
         ln = {k: _dyadic(v) if k != "eps" else v for k, v in rand_ln(rng, E).items()}
-        g = O.layer_bwd(x, z, dout, pf, pb, axis, idx=idx, hw=hw, ln=ln)
+        g = O.layer_bwd(x, z, dout, pf, pb, axis, idx=idx, hw=hw, ln=ln, local_window=local)
         targets = [("x", None), ("z", None), ("ln", "weight"), ("ln", "bias")] + \
             [(d, k) for d in ("fwd", "bwd") for k in ("x_proj_w", "dt_proj_w", "dt_proj_b", "A_log", "D")]
         for d, k in targets:
@@ -604,7 +609,8 @@ def pin_bwd_finite_differences_ln(O):
                     arg[d] = pert
                 else:
                     arg["ln" if d == "ln" else ("pf" if d == "fwd" else "pb")][k] = pert
-                L.append(_loss(O, arg["x"], arg["z"], dout, arg["pf"], arg["pb"], axis, idx, hw, ln=arg["ln"]))
+                L.append(_loss(O, arg["x"], arg["z"], dout, arg["pf"], arg["pb"], axis, idx, hw, ln=arg["ln"],
+                               local=local))
             fd = (L[0] - L[1]) / (2.0 * eps)
             an = float(np.sum(grad * V))
             scale = max(float(np.linalg.norm(grad)), 1e-30)

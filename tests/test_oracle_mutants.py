@@ -105,7 +105,8 @@ MUTANTS = [
     ("dz without the skip", "const double y = sf[e] + sb[e] + Ds * xe;", "const double y = sf[e] + sb[e];", 1),
     ("dD of the backward direction zero", "o->D[e] = dD[e];", "o->D[e] = d == 0 ? dD[e] : 0.0;", 1),
     ("scan adjoint fed dout without the gate", "g[e] = de * silu(ze);", "g[e] = de;", 1),
-    ("backward direction's adjoint not reversed", "pd[d]->A_log, d, du, dd", "pd[d]->A_log, 0, du, dd", 1),
+    ("backward direction's adjoint not reversed", "pd[d]->A_log, d, d == 1 ? reset : NULL, du, dd",
+     "pd[d]->A_log, 0, d == 1 ? reset : NULL, du, dd", 1),
     ("dx without the skip", "dx[off + e] = dxs[off + e] + du[mt + e] * pool_scale / (double)P;",
      "dx[off + e] = du[mt + e] * pool_scale / (double)P;", 1),
     ("du of the scan without B", "duk += lam[n] * d * Bn;", "duk += lam[n] * d;", 1),
@@ -127,6 +128,20 @@ MUTANTS = [
     ("LayerNorm adjoint's recomputed input without the skip",
      "ny[e] = sf[e] + sb[e] + Ds * (double)x[e];", "ny[e] = sf[e] + sb[e];", 1),
     ("dz through the norm without its affine map", "dz[e] = de * o * sg", "dz[e] = de * ny[e] * sg", 1),
+    # backward pass of the local backward scan
+    ("adjoint's state recompute ignores the reset",
+     "const double a = (reset && reset[t]) ? 0.0 : exp(delta[m * E + e] * A);",
+     "const double a = exp(delta[m * E + e] * A);", 1),
+    ("adjoint's reverse sweep ignores the reset", "const double a = reset && reset[t] ? 0.0 : exp(A * d);",
+     "const double a = exp(A * d);", 1),
+    ("backward's local windows aligned one step early", "reset[t] = (unsigned char)((t + 1) % local_window == 0);",
+     "reset[t] = (unsigned char)(t % local_window == 0);", 1),
+    ("local scan's x_proj gradient not added to the forward set",
+     "gf->x_proj_w[i] += gb->x_proj_w[i]; gb->x_proj_w[i] = 0.0;", "gb->x_proj_w[i] = 0.0;", 1),
+    ("local scan's A_log gradient left in the backward set",
+     "gf->A_log[i] += gb->A_log[i]; gb->A_log[i] = 0.0;", "gf->A_log[i] += gb->A_log[i];", 1),
+    ("local scan's adjoint with the backward set's parameters",
+     "const fvo_dir *pd[2] = {pf, local_window > 0 ? &pl : pb};", "const fvo_dir *pd[2] = {pf, pb};", 1),
     ("adjoint uses the current state for the decay", "dd += lam[n] * (A * a * prev + Bn * ut);",
      "dd += lam[n] * (A * a * Hs[k * N + n] + Bn * ut);", 1),
 ]
