@@ -201,8 +201,10 @@ typedef struct fastvim_params {
  * combines with the other options.  Dense pooled layers take the single
  * launch under the same rules as without it (the size rule by default,
  * FASTVIM_FLAG_FUSED to force it), except with FASTVIM_FLAG_POST_NORM; other
- * layers run as stage kernels.  The backward pass returns
- * FASTVIM_ERR_UNSUPPORTED for it. */
+ * layers run as stage kernels.  The backward pass takes it for pooled layers:
+ * the gradients of the shared x_proj_w, dt_proj_w, dt_proj_b and A_log sum
+ * both scans' contributions and go to grads->fwd, grads->bwd receives zeros
+ * for those four (its buffers are still required) and dD as usual. */
 #define FASTVIM_FLAG_LOCAL_BWD 16u
 #define FASTVIM_LOCAL_WINDOW 16
 
@@ -317,12 +319,17 @@ size_t fastvim_ssm_export_bytes(const fastvim_dims *dims, int pool_axis, int wha
  * is rounded to bf16 there).  grads->ln_weight and ln_bias receive the norm's
  * gradients.
  *
+ * With FASTVIM_FLAG_LOCAL_BWD the backward scan is LBMamba's local one (see
+ * the flag): its adjoint runs within each window, on the forward direction's
+ * parameters, and nothing carries across a window's reset.
+ *
  * Supported: pooled layers (COLS or ROWS, dense or masked) with T <= 128 scan
  * steps and the limits of the forward call, with or without
- * FASTVIM_FLAG_POST_NORM (then E <= 2048); FASTVIM_ERR_UNSUPPORTED for
+ * FASTVIM_FLAG_POST_NORM (then E <= 2048), FASTVIM_FLAG_POOL_SCALE and
+ * FASTVIM_FLAG_LOCAL_BWD, in any combination; FASTVIM_ERR_UNSUPPORTED for
  * unpooled layers, longer scans, the LayerNorm with E > 2048, and the flags
- * FASTVIM_FLAG_FUSED, FASTVIM_FLAG_CONV and FASTVIM_FLAG_LOCAL_BWD (0 and
- * FASTVIM_FLAG_STAGED run the same kernels). */
+ * FASTVIM_FLAG_FUSED and FASTVIM_FLAG_CONV (0 and FASTVIM_FLAG_STAGED run the
+ * same kernels). */
 
 /* Gradients of one direction's parameters: fp32 device buffers shaped like
  * the parameters, 4-byte aligned, overwritten by the call. */

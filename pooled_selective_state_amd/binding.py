@@ -327,8 +327,10 @@ class BwdCall:
         self.dz = torch.empty_like(x) if dz is None else dz
         self._keep = []
         dirs = _dir_params(params, self._keep)
+        # gradients are shaped like the forward set (the backward set may lack
+        # all but D with FLAG_LOCAL_BWD)
         if grads is None:
-            grads = {d: {f: torch.empty_like(params[d][f]) for f in DIR_FIELDS} for d in ("fwd", "bwd")}
+            grads = {d: {f: torch.empty_like(params["fwd"][f]) for f in DIR_FIELDS} for d in ("fwd", "bwd")}
         ln_w = ln_b = None
         ln_eps = 0.0
         if ln is not None:
@@ -349,7 +351,7 @@ class BwdCall:
         for d in ("fwd", "bwd"):
             for f in DIR_FIELDS:
                 t = grads[d][f]
-                if t.dtype != torch.float32 or not t.is_contiguous() or t.shape != params[d][f].shape:
+                if t.dtype != torch.float32 or not t.is_contiguous() or t.shape != params["fwd"][f].shape:
                     raise ValueError("gradient %s.%s must be contiguous float32 shaped like the parameter" % (d, f))
             gd.append(DirGrads(*[grads[d][f].data_ptr() for f in DIR_FIELDS]))
         lg = grads["ln"] if ln is not None else None

@@ -198,8 +198,9 @@ int validate_bwd(const void* x, const void* z, const void* dout, const fastvim_p
                  int axis, const int32_t* idx, const void* dx, const void* dz, const fastvim_grads* gr, Geom* g,
                  BwdWorkspace* ws, bool* empty) {
     if (!prm) return FASTVIM_ERR_NULL;
-    const uint32_t unsupported = FASTVIM_FLAG_FUSED | FASTVIM_FLAG_CONV | FASTVIM_FLAG_LOCAL_BWD;
-    const uint32_t options = FASTVIM_FLAG_STAGED | FASTVIM_FLAG_POST_NORM | FASTVIM_FLAG_POOL_SCALE;
+    const uint32_t unsupported = FASTVIM_FLAG_FUSED | FASTVIM_FLAG_CONV;
+    const uint32_t options =
+        FASTVIM_FLAG_STAGED | FASTVIM_FLAG_POST_NORM | FASTVIM_FLAG_POOL_SCALE | FASTVIM_FLAG_LOCAL_BWD;
     if (prm->flags & ~(options | unsupported)) return FASTVIM_ERR_ARG;
     if (prm->flags & unsupported) return FASTVIM_ERR_UNSUPPORTED;
     const bool norm = (prm->flags & FASTVIM_FLAG_POST_NORM) != 0;
@@ -239,7 +240,8 @@ int validate_bwd(const void* x, const void* z, const void* dout, const fastvim_p
     *empty = g->B == 0;
     if (*empty) return FASTVIM_OK;
     if (!x || !z || !dout || !dx || !dz || (g->masked && !idx)) return FASTVIM_ERR_NULL;
-    if ((st = check_dir(prm->fwd)) || (st = check_dir(prm->bwd))) return st;
+    const fastvim_params eff = effective_params(*prm);
+    if ((st = check_dir(eff.fwd)) || (st = check_dir(eff.bwd))) return st;
     if (!prm->workspace) return FASTVIM_ERR_WORKSPACE;
     if (!aligned(x, 16) || !aligned(z, 16) || !aligned(dout, 16) || !aligned(dx, 16) || !aligned(dz, 16) ||
         !aligned(prm->workspace, 256) || (idx && !aligned(idx, 4)))
@@ -251,7 +253,7 @@ int validate_bwd(const void* x, const void* z, const void* dout, const fastvim_p
     // other nor an input; parameters count as inputs
     Span ins[16] = {{x, io}, {z, io}, {dout, io}};
     int nin = 3;
-    for (const fastvim_dir_params* pd : {&prm->fwd, &prm->bwd}) {
+    for (const fastvim_dir_params* pd : {&eff.fwd, &eff.bwd}) {
         const float* ps[5] = {pd->x_proj_w, pd->dt_proj_w, pd->dt_proj_b, pd->A_log, pd->D};
         for (int i = 0; i < 5; ++i) ins[nin++] = Span{ps[i], gsz[i] * sizeof(float)};
     }
@@ -286,6 +288,7 @@ int run_bwd(const Geom& g, const void* x, const void* z, const void* dout, const
         return e == hipSuccess;
     };
     const bool norm = (p.flags & FASTVIM_FLAG_POST_NORM) != 0;
+    const bool local = (p.flags & FASTVIM_FLAG_LOCAL_BWD) != 0;  // p holds the effective parameters
     if (g.masked && !ok(launch_mask_rows(g, idx, ws.fwd, s))) return FASTVIM_ERR_HIP;
     if (norm) {
         // the norm's adjoint needs y, hence both scans' outputs: recompute the
@@ -303,9 +306,12 @@ int run_bwd(const Geom& g, const void* x, const void* z, const void* dout, const
     } else {
         if (!ok(launch_bwd_pool(g, x, z, dout, ws, s)) || !ok(launch_proj(g, x, p, ws.fwd, s)))
             return FASTVIM_ERR_HIP;
+        // the local backward scan's outputs (the second pass needs s_bwd) come
+        // from the forward scan; the scan adjoint does not rerun that scan
+        if (local && !ok(launch_scan(g, x, p, ws.fwd, s))) return FASTVIM_ERR_HIP;
     }
     BwdScanArgs a{ws.fwd.xdbl, ws.fwd.u, ws.gs, p.fwd, p.bwd, ws.fwd.s_f, ws.fwd.s_b, ws.du_f, ws.du_b, ws.dvp,
-                  ws.ckpt, ws.dAp, ws.dWdtp, ws.dbp, g.B, g.T, g.E, (int)g.R, (int)g.NX, (int)ws.G};
+                  ws.ckpt, ws.dAp, ws.dWdtp, ws.dbp, g.B, g.T, g.E, (int)g.R, (int)g.NX, (int)ws.G, local};
     if (!ok(launch_scan_bwd(a, s)) || !ok(launch_bwd_dv(g, ws, s)) || !ok(launch_bwd_du(g, p, ws, s)) ||
         !ok(launch_bwd_dwx(g, ws, s)))
         return FASTVIM_ERR_HIP;
@@ -314,12 +320,23 @@ int run_bwd(const Geom& g, const void* x, const void* z, const void* dout, const
     const fastvim_dir_grads* gd[2] = {&gr.fwd, &gr.bwd};
     const int64_t E = g.E, NX = g.NX, R = g.R, B = g.B;
     ColsumBatch batch{};
-    for (int d = 0; d < 2; ++d) {
+    if (local) {
+        // the local scan's parameters are the forward direction's: its partials
+        // join the forward sums below; the backward set's four are zero
+        const fastvim_dir_grads& gb = gr.bwd;
+        if (!ok(launch_fill_zero(gb.x_proj_w, NX * E, s)) || !ok(launch_fill_zero(gb.A_log, E * 16, s)) ||
+            !ok(launch_fill_zero(gb.dt_proj_w, E * R, s)) || !ok(launch_fill_zero(gb.dt_proj_b, E, s)))
+            return FASTVIM_ERR_HIP;
+    }
+    for (int d = 0; d < (local ? 1 : 2); ++d) {
+        // with the local scan, direction 0's sums run over both directions'
+        // partials (d x_proj_w: (MC, 2) rows; the others: (2, B) rows)
+        const int64_t k = local ? 2 : 1;
         const ColsumSeg segs[4] = {
-            {ws.dWxp + d * NX * E, ws.MC, NX * E, 2 * NX * E, gd[d]->x_proj_w, nullptr, 0},
-            {ws.dAp + d * B * E * 16, B, E * 16, E * 16, gd[d]->A_log, nullptr, 0},
-            {ws.dWdtp + d * B * E * R, B, E * R, E * R, gd[d]->dt_proj_w, nullptr, 0},
-            {ws.dbp + d * B * E, B, E, E, gd[d]->dt_proj_b, nullptr, 0}};
+            {ws.dWxp + d * NX * E, k * ws.MC, NX * E, (local ? 1 : 2) * NX * E, gd[d]->x_proj_w, nullptr, 0},
+            {ws.dAp + d * B * E * 16, k * B, E * 16, E * 16, gd[d]->A_log, nullptr, 0},
+            {ws.dWdtp + d * B * E * R, k * B, E * R, E * R, gd[d]->dt_proj_w, nullptr, 0},
+            {ws.dbp + d * B * E, k * B, E, E, gd[d]->dt_proj_b, nullptr, 0}};
         for (const ColsumSeg& sg : segs) {
             if (sg.rows <= kColRowsPerBlock) {
                 batch.seg[batch.n++] = sg;
@@ -395,8 +412,9 @@ size_t bwd_workspace_layout(const Geom& g, void* base, BwdWorkspace* ws) {
         return rows > kColRowsPerBlock ? (rows + kColRowsPerBlock - 1) / kColRowsPerBlock * cols : int64_t(0);
     };
     int64_t tmpf = 1;
-    for (int64_t v : {stage1(ND, E), stage1(M, E), stage1(B, E * 16), stage1(B, E * R), stage1(B, E),
-                      stage1(MC, NX * E)})
+    // (the local backward scan sums twice the rows of the per-image and per-chunk partials)
+    for (int64_t v : {stage1(ND, E), stage1(M, E), stage1(2 * B, E * 16), stage1(2 * B, E * R), stage1(2 * B, E),
+                      stage1(2 * MC, NX * E)})
         tmpf = v > tmpf ? v : tmpf;
     const size_t o_tmp = take((size_t)tmpf * sizeof(float));
     if (base && ws) {
@@ -540,7 +558,7 @@ int fastvim_ssm_bwd(const void* x, const void* z, const void* dout, const fastvi
             return FASTVIM_ERR_HIP;
         return FASTVIM_OK;
     }
-    return run_bwd(g, x, z, dout, *params, mask_idx, dx, dz, *grads, ws, s);
+    return run_bwd(g, x, z, dout, effective_params(*params), mask_idx, dx, dz, *grads, ws, s);
 }
 
 int fastvim_calib_copy(void* dst, const void* src, size_t bytes, void* stream) {

@@ -46,6 +46,7 @@ struct BwdScanArgs {
     float *dAp, *dWdtp, *dbp;
     int64_t B, T, E;
     int R, NX, G;
+    bool local;  // direction 1 is the local backward scan (pb holds the forward parameters)
 };
 
 int bwd_rmax(int64_t R);  // the dt-rank bound (16, 32, 48, 64) whose kernel instance serves R

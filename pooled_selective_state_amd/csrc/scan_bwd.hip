@@ -42,6 +42,17 @@
 // partials of the parameter gradients (summed over t) go to (B, E, ...)
 // buffers, summed over images by a later kernel.  No atomics: every sum has
 // a fixed order.
+//
+// LOCAL: direction 1 is LBMamba's local backward scan (LBMamba article,
+// 论文创新点 1-2), run on the forward direction's parameters (the caller
+// passes them in pb) with its state reset at the top of every window of
+// kChunk steps aligned at t = 0.  Its traversal is padded at the start to
+// nrow = kChunk ceil(T / kChunk) steps, traversal step ti being
+// t = nrow - 1 - ti, so that each chunk is exactly one window: the state
+// entering every chunk is zero (no forward sweep, no checkpoints), no
+// adjoint crosses a chunk boundary (the reset step's decay is zero), and the
+// padding steps (t >= T: zero rows, inputs and adjoint inputs, step size 0)
+// contribute nothing.  Its s_bwd comes from the forward scan kernel.
 #include "scan_core.h"
 #include "bwd_internal.h"
 
@@ -54,6 +65,7 @@ constexpr int kBwdRows = kBwdThreads / 16;         // DPP rows of 16 lanes per w
 constexpr int kBwdCM = kBwdTMax / kChunk;          // chunks at most (8)
 static_assert(kBwdThreads / kLps == kScanCh && kScanCh == kBwdCh, "a workgroup covers one channel group");
 static_assert(kChunk % kBwdFlush == 0, "whole flushes per chunk");
+static_assert(kChunk == FASTVIM_LOCAL_WINDOW, "the local scan's windows are the chunks");
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_row(float v) {
@@ -84,7 +96,7 @@ __device__ __forceinline__ void recompute_step(float (&hs)[kNs], const float* ro
     for (int n = 0; n < kNs; ++n) hs[n] = fmaf(__builtin_amdgcn_exp2f(dlt * A2[n]), hs[n], du * bt[n]);
 }
 
-template <int RMAX>
+template <int RMAX, bool LOCAL>
 __global__ void __launch_bounds__(kBwdThreads) scan_bwd_kernel(BwdScanArgs a) {
     constexpr int S = row_stride_lds<RMAX>();
     constexpr int kWQ = RMAX / 4;
@@ -129,8 +141,14 @@ __global__ void __launch_bounds__(kBwdThreads) scan_bwd_kernel(BwdScanArgs a) {
     // stage this direction's x_proj rows at their traversal steps, zeros past T
     const int nch = (T + kChunk - 1) / kChunk;
     const int nrow = nch * kChunk;
+    const bool lw = LOCAL && dir == 1;   // local backward scan: windows = chunks
+    const int toff = lw ? nrow - T : 0;  // padding steps at the start of its traversal
+    // time of traversal step ti (outside [0, T) for padding and steps past T)
+    auto time_of = [&](int ti) { return dir ? T - 1 + toff - ti : ti; };
     {
-        const float* xb = a.xdbl + (b * T * 2 + dir) * (int64_t)NX;  // row t at xb + 2 t NX
+        // row t at xb + 2 t NX; the local scan reads the forward direction's
+        // rows (the projection stage writes only those in local mode)
+        const float* xb = a.xdbl + (b * T * 2 + (lw ? 0 : dir)) * (int64_t)NX;
         const int prow = tid / 16, po = tid % 16;
         int scol[kPre];
 #pragma unroll
@@ -139,9 +157,10 @@ __global__ void __launch_bounds__(kBwdThreads) scan_bwd_kernel(BwdScanArgs a) {
 #pragma unroll
         for (int ps = 0; ps < kPasses; ++ps) {
             const int ti = prow + 16 * ps;
-            const int t = dir ? T - 1 - ti : ti;
+            const int t = time_of(ti);
+            const bool real = t >= 0 && t < T;
 #pragma unroll
-            for (int i = 0; i < kPre; ++i) stage[ps][i] = (ti < T && scol[i] >= 0) ? xb[2 * t * NX + scol[i]] : 0.f;
+            for (int i = 0; i < kPre; ++i) stage[ps][i] = (real && scol[i] >= 0) ? xb[2 * t * NX + scol[i]] : 0.f;
         }
 #pragma unroll
         for (int ps = 0; ps < kPasses; ++ps) {
@@ -161,9 +180,8 @@ __global__ void __launch_bounds__(kBwdThreads) scan_bwd_kernel(BwdScanArgs a) {
     auto load_steps = [&](const float* src, int c, float (&v)[kJ]) {
 #pragma unroll
         for (int j = 0; j < kJ; ++j) {
-            const int tj = c * kChunk + q + 4 * j;
-            const int t = dir ? T - 1 - tj : tj;
-            v[j] = (valid && tj < T) ? src[(int64_t)t * E] : 0.f;
+            const int t = time_of(c * kChunk + q + 4 * j);
+            v[j] = (valid && t >= 0 && t < T) ? src[(int64_t)t * E] : 0.f;
         }
     };
     // The lane's states entering chunk c, written by the forward sweep and
@@ -173,11 +191,12 @@ __global__ void __launch_bounds__(kBwdThreads) scan_bwd_kernel(BwdScanArgs a) {
     load_steps(ub, 0, un);
     __syncthreads();
 
-    // 1. forward sweep: outputs s^d and the state entering every chunk
+    // 1. forward sweep: outputs s^d and the state entering every chunk (not
+    // for the local scan, whose chunks all start from zero)
     ScanArgs sa{};
     sa.T = T;
 #pragma unroll 1
-    for (int c = 0; c < nch; ++c) {
+    for (int c = 0; c < (lw ? 0 : nch); ++c) {
         *reinterpret_cast<f32x4*>(ck + c * kBwdThreads * 4) = f32x4{L.hs[0], L.hs[1], L.hs[2], L.hs[3]};
         float ucur[kJ];
 #pragma unroll
@@ -192,7 +211,8 @@ __global__ void __launch_bounds__(kBwdThreads) scan_bwd_kernel(BwdScanArgs a) {
     f32x4 hn;
     load_steps(ub, nch - 1, un);
     load_steps(gb, nch - 1, gn);
-    hn = *reinterpret_cast<const f32x4*>(ck + (nch - 1) * kBwdThreads * 4);
+    const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+    hn = lw ? zero4 : *reinterpret_cast<const f32x4*>(ck + (nch - 1) * kBwdThreads * 4);
 #pragma unroll
     for (int n = 0; n < kNs; ++n) carry[n] = dA[n] = 0.f;
 #pragma unroll
@@ -216,14 +236,15 @@ __global__ void __launch_bounds__(kBwdThreads) scan_bwd_kernel(BwdScanArgs a) {
         if (c > 0) {  // the next (earlier) chunk's inputs and state, while this one computes
             load_steps(ub, c - 1, un);
             load_steps(gb, c - 1, gn);
-            hn = *reinterpret_cast<const f32x4*>(ck + (c - 1) * kBwdThreads * 4);
+            hn = lw ? zero4 : *reinterpret_cast<const f32x4*>(ck + (c - 1) * kBwdThreads * 4);
         }
         // step sizes (and sigmoid of their pre-activation) of the own steps
         float qv[kJ], dl[kJ], sg[kJ];
         scan_step_preact<RMAX>(L, dr, qv);
 #pragma unroll
         for (int j = 0; j < kJ; ++j) {
-            const bool in = base + q + 4 * j < T;
+            const int t = time_of(base + q + 4 * j);
+            const bool in = t >= 0 && t < T;
             dl[j] = in ? softplus_f(qv[j]) : 0.f;
             sg[j] = in ? sigmoid_f(qv[j]) : 0.f;
         }
@@ -326,20 +347,20 @@ __global__ void __launch_bounds__(kBwdThreads) scan_bwd_kernel(BwdScanArgs a) {
                 }
             }
             {
-                const int ti = base + 4 * j + q;
-                if (valid && ti < T) du_dir[(int64_t)(dir ? T - 1 - ti : ti) * E] = duo;
+                const int t = time_of(base + 4 * j + q);
+                if (valid && t >= 0 && t < T) du_dir[(int64_t)t * E] = duo;
             }
             if ((4 * j) % kBwdFlush == 0) {
                 // add the 16 row partials of these kBwdFlush steps; one partial per channel group
                 __syncthreads();
                 for (int o = tid; o < kBwdFlush * S; o += kBwdThreads) {
                     const int st = o / S, pos = o - st * S;
-                    const int ti = base + half * kBwdFlush + st;
+                    const int t = time_of(base + half * kBwdFlush + st);
                     const float* src = red + st * kBwdRows * S + pos;
                     float sum = 0.f;
 #pragma unroll
                     for (int r = 0; r < kBwdRows; ++r) sum += src[r * S];
-                    if (ti < T) dvp[(int64_t)(dir ? T - 1 - ti : ti) * S + pos] = sum;
+                    if (t >= 0 && t < T) dvp[(int64_t)t * S + pos] = sum;
                 }
                 __syncthreads();
             }
@@ -353,6 +374,10 @@ __global__ void __launch_bounds__(kBwdThreads) scan_bwd_kernel(BwdScanArgs a) {
 #pragma unroll
                 for (int n = 0; n < kNs; ++n) hb[k][n] = hb[k - 1][n];
             }
+        }
+        if (lw) {  // the chunk's first step is a reset: nothing carries into the previous window
+#pragma unroll
+            for (int n = 0; n < kNs; ++n) carry[n] = 0.f;
         }
     }
 
@@ -372,7 +397,12 @@ __global__ void __launch_bounds__(kBwdThreads) scan_bwd_kernel(BwdScanArgs a) {
 
 template <int RMAX>
 hipError_t scan_bwd_launch(const BwdScanArgs& a, hipStream_t st) {
-    hipLaunchKernelGGL((scan_bwd_kernel<RMAX>), dim3((unsigned)(a.B * a.G), 2), dim3(kBwdThreads), 0, st, a);
+    if (a.local)
+        hipLaunchKernelGGL((scan_bwd_kernel<RMAX, true>), dim3((unsigned)(a.B * a.G), 2), dim3(kBwdThreads), 0, st,
+                           a);
+    else
+        hipLaunchKernelGGL((scan_bwd_kernel<RMAX, false>), dim3((unsigned)(a.B * a.G), 2), dim3(kBwdThreads), 0, st,
+                           a);
     return hipGetLastError();
 }
 

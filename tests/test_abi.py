@@ -359,7 +359,7 @@ def test_bwd_unsupported_and_bad_flags():
         assert FakeBwd(axis=axis).bwd() == EUNSUP
     assert FakeBwd(h=129).bwd() == EUNSUP
     assert FakeBwd(N=8).bwd() == EUNSUP
-    for flags, code in ((P.FLAG_FUSED, EUNSUP), (P.FLAG_CONV, EUNSUP), (P.FLAG_LOCAL_BWD, EUNSUP), (64, EARG),
+    for flags, code in ((P.FLAG_FUSED, EUNSUP), (P.FLAG_CONV, EUNSUP), (64, EARG),
                         (P.FLAG_STAGED, OK)):
         c = FakeBwd()
         c.params.flags = flags
@@ -450,6 +450,26 @@ def test_bwd_post_norm_validation():
     assert c.bwd() == EWS  # the call got past every other check
 
 
+def test_bwd_local_scan_validation():
+    """With the local backward scan the backward set's x_proj_w, dt_proj_w,
+    dt_proj_b and A_log may be NULL (the call then gets past every check),
+    while its D and every gradient buffer stay required."""
+    c = FakeBwd()
+    c.params.flags = P.FLAG_LOCAL_BWD
+    for f in ("x_proj_w", "dt_proj_w", "dt_proj_b", "A_log"):
+        setattr(c.params.bwd, f, None)
+    c.params.workspace_bytes -= 1
+    assert c.bwd() == EWS
+    c = FakeBwd()
+    c.params.flags = P.FLAG_LOCAL_BWD
+    c.params.bwd.D = None
+    assert c.bwd() == ENULL
+    c = FakeBwd()
+    c.params.flags = P.FLAG_LOCAL_BWD
+    c.grads.bwd.A_log = None
+    assert c.bwd() == ENULL
+
+
 def test_bwd_alignment():
     for attr, off in (("dx", 4), ("dz", 8), ("dout", 4), ("x", 2)):
         c = FakeBwd()
@@ -523,8 +543,7 @@ def test_conv_validation():
 
 def test_local_bwd_validation():
     """LBMamba's local backward scan reads only D of the backward parameters:
-    a NULL backward D is an error, misaligned D too; the backward pass does
-    not take the option."""
+    a NULL backward D is an error, misaligned D too."""
     c = FakeCall()
     c.params.flags = P.FLAG_LOCAL_BWD
     c.params.bwd.D = None
@@ -537,6 +556,3 @@ def test_local_bwd_validation():
     c.params.flags = P.FLAG_LOCAL_BWD
     c.params.fwd.A_log = None  # the forward set is still read
     expect(c, ENULL)
-    c = FakeBwd()
-    c.params.flags = P.FLAG_LOCAL_BWD
-    assert c.bwd() == EUNSUP

@@ -49,7 +49,8 @@ def _dev_ln(ln):
     return {"weight": dev(ln["weight"], torch.float32), "bias": dev(ln["bias"], torch.float32), "eps": ln["eps"]}
 
 
-def gpu_bwd(x, z, dout, prm, axis, idx=None, hw=None, dtype=torch.float32, flags=0, saved=None, ln=None):
+def gpu_bwd(x, z, dout, prm, axis, idx=None, hw=None, dtype=torch.float32, flags=0, saved=None, ln=None,
+            pool_scale=None):
     """saved: None (the backward pools x itself) or the flags of a forward call
     that first writes the pooled tokens the backward then reads (saved_u).
     ln: the post-SSM LayerNorm (host arrays), for both calls."""
@@ -60,8 +61,10 @@ def gpu_bwd(x, z, dout, prm, axis, idx=None, hw=None, dtype=torch.float32, flags
     if saved is not None:
         h, w = (x.shape[1], x.shape[2]) if idx is None else hw
         su = torch.full((x.shape[0], h if axis == P.POOL_COLS else w, x.shape[-1]), float("nan"), device="cuda")
-        P.SSMCall(xd, zd, pd, axis, mask_idx=idd, hw=hw, flags=saved, saved_u=su, ln=lnd).run()
-    call = P.BwdCall(xd, zd, dev(dout, dtype), pd, axis, mask_idx=idd, hw=hw, flags=flags, saved_u=su, ln=lnd)
+        P.SSMCall(xd, zd, pd, axis, mask_idx=idd, hw=hw, flags=saved | (flags & P.FLAG_LOCAL_BWD), saved_u=su,
+                  ln=lnd, pool_scale=pool_scale).run()
+    call = P.BwdCall(xd, zd, dev(dout, dtype), pd, axis, mask_idx=idd, hw=hw, flags=flags, saved_u=su, ln=lnd,
+                     pool_scale=pool_scale)
     res = call.run()
     torch.cuda.synchronize()
     out = {"dx": host(res["dx"]), "dz": host(res["dz"]),
@@ -249,7 +252,7 @@ def test_bwd_rows_is_cols_on_transposed_grid():
 
 
 # ------------------------------------------------------------------ full size
-def _sampled_full_size(cfg, axis=P.POOL_COLS, saved=None, norm=False):
+def _sampled_full_size(cfg, axis=P.POOL_COLS, saved=None, norm=False, local=False):
     wl = draw_workload(cfg)
     x, z, prm, idx = wl["x"], wl["z"][0], wl["params"][0], wl["idx"]
     ln = rand_ln(np.random.default_rng(78), cfg.E) if norm else None
@@ -261,15 +264,17 @@ def _sampled_full_size(cfg, axis=P.POOL_COLS, saved=None, norm=False):
         dout = round_to_bf16(dout)
     tol, dt = _tol(cfg.io_dtype)
     hw = (cfg.h, cfg.w) if cfg.masked else None
-    print("\n[%s bwd] B=%d grid=%dx%d E=%d axis %d, upstream gradient on images %s, pooled tokens %s%s"
+    print("\n[%s bwd] B=%d grid=%dx%d E=%d axis %d, upstream gradient on images %s, pooled tokens %s%s%s"
           % (cfg.name, cfg.B, cfg.h, cfg.w, cfg.E, axis, list(sel), "saved" if saved is not None else "recomputed",
-             ", post-SSM LayerNorm" if norm else ""), flush=True)
-    got = gpu_bwd(x, z, dout, prm, axis, idx=idx, hw=hw, dtype=dt, saved=saved, ln=ln)
+             ", post-SSM LayerNorm" if norm else "", ", local backward scan" if local else ""), flush=True)
+    got = gpu_bwd(x, z, dout, prm, axis, idx=idx, hw=hw, dtype=dt, saved=saved, ln=ln,
+                  flags=P.FLAG_LOCAL_BWD if local else 0)
     rest = np.setdiff1d(np.arange(cfg.B), sel)
     for name in ("dx", "dz"):
         assert np.count_nonzero(got[name][rest]) == 0, name + " nonzero on images without upstream gradient"
     ref = oracle.layer_bwd(x[sel], z[sel], dout[sel], prm["fwd"], prm["bwd"], axis,
-                           idx=None if idx is None else idx[sel], hw=hw, ln=ln)
+                           idx=None if idx is None else idx[sel], hw=hw, ln=ln,
+                           local_window=P.LOCAL_WINDOW if local else 0)
     compare(got, ref, tol, cfg.name, sel=sel)
 
 
@@ -423,3 +428,76 @@ def test_bwd_norm_full_size_vim_s():
 
 def test_bwd_norm_full_size_masked_b():
     _sampled_full_size(C.MASKED_B, norm=True)
+
+
+# ------------------------------------------------------------------ LBMamba's local backward scan
+# scan lengths below, at and above one window, with a partial last window, and the longest
+LOCAL_T = [1, 7, 16, 21, 48, 128]
+
+
+def _local_case(rng, T, axis, io, B=2, P_=5, E=72, R=6, masked=False):
+    h, w = (T, P_) if axis == P.POOL_COLS else (P_, T)
+    if masked:
+        K = max(1, (h * w) // 2)
+        shape, idx, hw = (B, K, E), random_mask(rng, B, h, w, K), (h, w)
+    else:
+        shape, idx, hw = (B, h, w, E), None, None
+    x, z, dout = (rng.standard_normal(shape).astype(np.float32) for _ in range(3))
+    x, z, dout = _io(io, x, z, dout)
+    prm = {"fwd": rand_dir(rng, E, 16, R, 0.1), "bwd": rand_dir(rng, E, 16, R, 0.1)}
+    return x, z, dout, prm, idx, hw
+
+
+def _local_check(x, z, dout, prm, axis, io, tag, idx=None, hw=None, saved=None, ln=None, pool_scale=None):
+    tol, dt = _tol(io)
+    got = gpu_bwd(x, z, dout, prm, axis, idx=idx, hw=hw, dtype=dt, flags=P.FLAG_LOCAL_BWD, saved=saved, ln=ln,
+                  pool_scale=pool_scale)
+    ref = oracle.layer_bwd(x, z, dout, prm["fwd"], prm["bwd"], axis, idx=idx, hw=hw, ln=ln,
+                           pool_scale=1.0 if pool_scale is None else pool_scale, local_window=P.LOCAL_WINDOW)
+    compare(got, ref, tol, tag)
+    for f in FIELDS[:4]:  # the backward set's unused parameters get zero gradients
+        assert np.count_nonzero(got["bwd"][f]) == 0, tag + " nonzero d bwd." + f
+    return got
+
+
+@pytest.mark.parametrize("saved", [None, 0], ids=SAVED_IDS)
+@pytest.mark.parametrize("T", LOCAL_T)
+@pytest.mark.parametrize("axis", (P.POOL_COLS, P.POOL_ROWS))
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_bwd_local_scan(io, axis, T, saved):
+    rng = np.random.default_rng(zlib.crc32(repr(("bwd-local", io, axis, T, saved)).encode()))
+    x, z, dout, prm, idx, hw = _local_case(rng, T, axis, io)
+    _local_check(x, z, dout, prm, axis, io, "local T=%d %s axis %d" % (T, io, axis), saved=saved)
+
+
+@pytest.mark.parametrize("variant", ["masked", "norm", "pool_scale", "masked_norm_scale"])
+@pytest.mark.parametrize("axis", (P.POOL_COLS, P.POOL_ROWS))
+def test_bwd_local_scan_options(axis, variant):
+    rng = np.random.default_rng(zlib.crc32(repr(("bwd-local-opt", axis, variant)).encode()))
+    masked = variant.startswith("masked")
+    x, z, dout, prm, idx, hw = _local_case(rng, 37, axis, "f32", E=136, masked=masked)
+    ln = rand_ln(rng, x.shape[-1]) if "norm" in variant else None
+    scale = 0.25 if "scale" in variant else None
+    _local_check(x, z, dout, prm, axis, "f32", "local %s axis %d" % (variant, axis), idx=idx, hw=hw, ln=ln,
+                 pool_scale=scale)
+
+
+def test_bwd_local_scan_backward_set_may_be_null():
+    """Only D of the backward set is read: the call with the other four
+    absent gives the same gradients as with them present."""
+    rng = np.random.default_rng(88)
+    x, z, dout, prm, idx, hw = _local_case(rng, 30, P.POOL_COLS, "f32")
+    full = gpu_bwd(x, z, dout, prm, P.POOL_COLS, flags=P.FLAG_LOCAL_BWD)
+    slim = {"fwd": prm["fwd"], "bwd": {"D": prm["bwd"]["D"]}}
+    xd, zd = dev(x), dev(z)
+    pd = {"fwd": {k: dev(v) for k, v in slim["fwd"].items()}, "bwd": {"D": dev(slim["bwd"]["D"])}}
+    res = P.BwdCall(xd, zd, dev(dout), pd, P.POOL_COLS, flags=P.FLAG_LOCAL_BWD).run()
+    torch.cuda.synchronize()
+    assert np.array_equal(host(res["dx"]), full["dx"]) and np.array_equal(host(res["dz"]), full["dz"])
+    for d in DIRECTIONS:
+        for f in FIELDS:
+            assert np.array_equal(host(res[d][f]), full[d][f]), (d, f)
+
+
+def test_bwd_local_scan_full_size_2048():
+    _sampled_full_size(C.HIRES_2048, P.POOL_COLS, saved=0, local=True)

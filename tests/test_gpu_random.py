@@ -4,9 +4,9 @@ both element types, both paths of a dense pooled layer and the options that
 combine with it (post-SSM LayerNorm, producer Conv1D, LBMamba's local
 backward scan), so that combinations the fixed cases do not list are checked
 too.  Each case compares out, the out of its D = 0 twin, and both scan
-outputs, each on its own scale; cases of pooled layers without the Conv1D or
-the local scan also run the backward pass (with the LayerNorm where the case
-has it), with and without the pooled tokens saved by the forward call.
+outputs, each on its own scale; cases of pooled layers without the Conv1D
+also run the backward pass (with the LayerNorm and the local scan where the
+case has them), with and without the pooled tokens saved by the forward call.
 Bar: 1e-4 fp32, 2e-2 bf16 (oracle on the bf16-rounded inputs).
 """
 from __future__ import annotations
@@ -105,8 +105,8 @@ def test_random_layer(seed):
     check(sf, ref["fwd"]["s"], tol, tag + " s_fwd")
     check(sb, ref["bwd"]["s"], tol, tag + " s_bwd")
 
-    # the backward pass covers pooled layers, with the norm but not the other options
-    if axis in (P.POOL_COLS, P.POOL_ROWS) and not (c["conv"] or c["local"]) and \
+    # the backward pass covers pooled layers, with every option but the Conv1D
+    if axis in (P.POOL_COLS, P.POOL_ROWS) and not c["conv"] and \
             (c["w"] if axis == P.POOL_ROWS else c["h"]) <= 128:
         dout = rng.standard_normal(shape).astype(np.float32)
         if c["io"] == "bf16":
@@ -120,9 +120,10 @@ def test_random_layer(seed):
             T = c["h"] if axis == P.POOL_COLS else c["w"]
             su = torch.full((c["B"], T, c["E"]), float("nan"), device="cuda")
             P.SSMCall(xd, zd, pd, axis, mask_idx=idd, hw=hw, saved_u=su, ln=lnd).run()
-        res = P.BwdCall(xd, zd, dev(dout, dt), pd, axis, mask_idx=idd, hw=hw, saved_u=su, ln=lnd).run()
+        bflags = P.FLAG_LOCAL_BWD if c["local"] else 0
+        res = P.BwdCall(xd, zd, dev(dout, dt), pd, axis, mask_idx=idd, hw=hw, saved_u=su, ln=lnd, flags=bflags).run()
         torch.cuda.synchronize()
-        rb = oracle.layer_bwd(x, z, dout, prm["fwd"], prm["bwd"], axis, idx=idx, hw=hw, ln=ln)
+        rb = oracle.layer_bwd(x, z, dout, prm["fwd"], prm["bwd"], axis, idx=idx, hw=hw, ln=ln, local_window=window)
         btag = tag + (" bwd saved-u" if su is not None else " bwd")
         check(host(res["dx"]), rb["dx"], tol, btag + " dx")
         check(host(res["dz"]), rb["dz"], tol, btag + " dz")
