@@ -399,7 +399,14 @@ def main():
                          "hbm_frac": bwd_bytes / (b_ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
             del bcall
         extras["backward_2048"]["post_norm_cols"] = res
-        del su, dout
+        # with LBMamba's local backward scan (pooled tokens saved)
+        bcall = P.BwdCall(x, z, dout, prm, P.POOL_COLS, saved_u=su, flags=P.FLAG_LOCAL_BWD)
+        bcall.run(stream)
+        b_ms, _ = time_steps(lambda: bcall.run(stream), n, stream)
+        extras["backward_2048"]["local_scan_cols"] = {"saved_u": {
+            "ms": b_ms, "images_per_s": cfg.B / (b_ms * 1e-3), "GBps": bwd_bytes / (b_ms * 1e-3) / 1e9,
+            "hbm_frac": bwd_bytes / (b_ms * 1e-3) / 1e9 / HBM_PEAK_GBS}}
+        del bcall, su, dout
         log("backward %.3f ms (cols, saved u), with the LayerNorm %.3f ms"
             % (extras["backward_2048"]["cols"]["saved_u"]["ms"], res["saved_u"]["ms"]))
         # torch's device copy, for comparison with the calibration copy
