@@ -105,7 +105,7 @@ class Oracle:
             vp, vp, vp, ctypes.POINTER(_Dir), ctypes.POINTER(_Dir),
             i64, i64, i64, i64, i64, i64, i64, ci, vp,
             vp, vp, ctypes.POINTER(_DirGrad), ctypes.POINTER(_DirGrad), ctypes.POINTER(_BwdStages),
-            vp, vp, ctypes.c_double, vp, vp, ctypes.c_double, i64,
+            vp, vp, ctypes.c_double, vp, vp, ctypes.c_double, i64, vp, vp, i64, vp, vp,
         ]
         lib.fvo_layer_bwd.restype = ci
         self._lib = lib
@@ -267,7 +267,7 @@ class Oracle:
         return {"out": out, "u": u, "rows": rows, "fwd": st["fwd"], "bwd": st["bwd"]}
 
     def layer_bwd(self, x, z, dout, fwd, bwd, axis, idx=None, hw=None, stages=False, ln=None, pool_scale=1.0,
-                  local_window=0):
+                  local_window=0, conv=None):
         """Gradients of sum(dout * layer(x, z, ...)).  Arguments as layer();
         dout is shaped like x.  Returns a dict with dx, dz (fp64, shaped like
         x) and "fwd" / "bwd" dicts of parameter gradients keyed like the
@@ -277,8 +277,15 @@ class Oracle:
         dv_bwd (B,T,NX).  local_window, pool_scale: as in layer(); with the local
         backward scan the shared parameters' gradients are in "fwd" and the
         backward set's x_proj_w, dt_proj_w, dt_proj_b and A_log gradients
-        are zero."""
+        are zero.  conv (dense layers): as in layer(); dx is then the gradient
+        of the Conv1D's input and "conv": {"weight", "bias"} holds the conv's
+        gradients."""
         x, z, dout = _f32(x), _f32(z), _f32(dout)
+        conv_w = conv_b = dcw = dcb = None
+        conv_k = 0
+        if conv is not None:
+            conv_w, conv_b = _f32(conv["weight"]), _f32(conv["bias"])
+            conv_k = conv_w.shape[1]
         ln_w = ln_b = dln_w = dln_b = None
         ln_eps = 0.0
         if ln is not None:
@@ -311,6 +318,9 @@ class Oracle:
         if ln is not None:
             dln_w, dln_b = np.empty(E, np.float64), np.empty(E, np.float64)
             res["ln"] = {"weight": dln_w, "bias": dln_b}
+        if conv is not None:
+            dcw, dcb = np.empty((E, conv_k), np.float64), np.empty(E, np.float64)
+            res["conv"] = {"weight": dcw, "bias": dcb}
         if stages:
             res["gs"] = np.empty((B, T, E), np.float64)
             res["du"] = np.empty((B, T, E), np.float64)
@@ -323,6 +333,7 @@ class Oracle:
             ctypes.byref(structs[0]), ctypes.byref(structs[1]),
             ctypes.byref(st) if st is not None else None,
             _ptr(ln_w), _ptr(ln_b), ln_eps, _ptr(dln_w), _ptr(dln_b), float(pool_scale), int(local_window),
+            _ptr(conv_w), _ptr(conv_b), conv_k, _ptr(dcw), _ptr(dcb),
         )
         if rc:
             raise ValueError("fvo_layer_bwd failed: %d" % rc)
@@ -393,6 +404,6 @@ def conv_silu(x, axis, conv):
 
 
 def layer_bwd(x, z, dout, fwd, bwd, axis, idx=None, hw=None, stages=False, ln=None, pool_scale=1.0,
-              local_window=0):
+              local_window=0, conv=None):
     return get().layer_bwd(x, z, dout, fwd, bwd, axis, idx=idx, hw=hw, stages=stages, ln=ln,
-                           pool_scale=pool_scale, local_window=local_window)
+                           pool_scale=pool_scale, local_window=local_window, conv=conv)

@@ -527,14 +527,15 @@ static void dt_preact(const double *v, int64_t M, int64_t NX, int64_t R, const f
  *   dz      = dout y silu'(z),  silu'(q) = sigmoid(q) (1 + q (1 - sigmoid(q)))
  *   dx_skip = g (D_fwd + D_bwd)
  *   dD     += g x          (the same for D_fwd and D_bwd)
+ * xd, when given, is the layer's x in double (the Conv1D's output) in place of x.
  */
-static void output_token_adjoint(const double *sf, const double *sb, const float *x, const float *z,
-                                 const float *dout, const fvo_dir *pf, const fvo_dir *pb, int64_t E, double *g,
-                                 double *dz, double *dx_skip, double *dD)
+static void output_token_adjoint(const double *sf, const double *sb, const float *x, const double *xd,
+                                 const float *z, const float *dout, const fvo_dir *pf, const fvo_dir *pb, int64_t E,
+                                 double *g, double *dz, double *dx_skip, double *dD)
 {
     for (int64_t e = 0; e < E; ++e) {
         const double Ds = (double)pf->D[e] + (double)pb->D[e];
-        const double xe = (double)x[e], ze = (double)z[e], de = (double)dout[e];
+        const double xe = xd ? xd[e] : (double)x[e], ze = (double)z[e], de = (double)dout[e];
         const double y = sf[e] + sb[e] + Ds * xe;
         const double sg = sigmoid(ze);
         g[e] = de * silu(ze);
@@ -555,17 +556,18 @@ static void output_token_adjoint(const double *sf, const double *sb, const float
  *   dn       = dout silu(z) ln_w
  *   g = dL/dy = r (dn - mean(dn) - n mean(dn n))     (also dL/ds of both scans)
  *   dx_skip  = g (D_fwd + D_bwd),   dD += g x
- * ny is caller scratch of E doubles.
+ * ny is caller scratch of E doubles; xd as in output_token_adjoint.
  */
-static void output_token_adjoint_ln(const double *sf, const double *sb, const float *x, const float *z,
+static void output_token_adjoint_ln(const double *sf, const double *sb, const float *x, const double *xd,
+                                    const float *z,
                                     const float *dout, const fvo_dir *pf, const fvo_dir *pb, int64_t E,
                                     const float *ln_w, const float *ln_b, double ln_eps, double *ny, double *g,
                                     double *dz, double *dx_skip, double *dD, double *dln_w, double *dln_b)
 {
     double mean = 0.0, var = 0.0;
     for (int64_t e = 0; e < E; ++e) {
-        const double Ds = (double)pf->D[e] + (double)pb->D[e];
-        ny[e] = sf[e] + sb[e] + Ds * (double)x[e];
+        const double Ds = (double)pf->D[e] + (double)pb->D[e], xe = xd ? xd[e] : (double)x[e];
+        ny[e] = sf[e] + sb[e] + Ds * xe;
         mean += ny[e];
     }
     mean /= (double)E;
@@ -593,7 +595,8 @@ static void output_token_adjoint_ln(const double *sf, const double *sb, const fl
         const double Ds = (double)pf->D[e] + (double)pb->D[e];
         g[e] = r * (g[e] - m1 - ny[e] * m2);
         dx_skip[e] = g[e] * Ds;
-        dD[e] += g[e] * (double)x[e];
+        const double xe = xd ? xd[e] : (double)x[e];
+        dD[e] += g[e] * xe;
     }
 }
 
@@ -693,6 +696,49 @@ static void xproj_adjoint(const double *u, const double *dv, int64_t M, int64_t 
 }
 
 /*
+ * Adjoint of fvo_conv_silu (the producer Conv1D + SiLU on the oriented grid's
+ * sequence).  With a[r] the pre-activation of position r and gxc = dL/dxc:
+ *   da[r]          = gxc[r] silu'(a[r])
+ *   d conv_b[e]    = sum_r da[r, e]
+ *   d conv_w[e, k] = sum_r da[r, e] x[r - KC + 1 + k, e]
+ *   dx[r', e]      = sum_k conv_w[e, k] da[r' + KC - 1 - k, e]   (positions inside the sequence)
+ * dx, dcw (E, KC) and dcb (E) are overwritten.
+ */
+static void conv_silu_adjoint(const float *x, const double *gxc, int64_t B, int64_t h, int64_t w, int64_t E,
+                              int axis, const float *conv_w, const float *conv_b, int64_t KC, double *dx,
+                              double *dcw, double *dcb)
+{
+    const int colmajor = axis == FVO_NONE_COLMAJOR || axis == FVO_ROWS;
+    const int64_t n = h * w;
+    for (int64_t i = 0; i < B * n * E; ++i) dx[i] = 0.0;
+    for (int64_t i = 0; i < E * KC; ++i) dcw[i] = 0.0;
+    for (int64_t e = 0; e < E; ++e) dcb[e] = 0.0;
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t r = 0; r < n; ++r) {
+            const int64_t cell = colmajor ? (r % h) * w + r / h : r;
+            for (int64_t e = 0; e < E; ++e) {
+                double a = (double)conv_b[e];
+                for (int64_t k = 0; k < KC; ++k) {
+                    const int64_t rr = r + k - (KC - 1);
+                    if (rr < 0) continue;
+                    const int64_t cc = colmajor ? (rr % h) * w + rr / h : rr;
+                    a += (double)conv_w[e * KC + k] * (double)x[(b * n + cc) * E + e];
+                }
+                const double sg = sigmoid(a);
+                const double da = gxc[(b * n + cell) * E + e] * sg * (1.0 + a * (1.0 - sg));
+                dcb[e] += da;
+                for (int64_t k = 0; k < KC; ++k) {
+                    const int64_t rr = r + k - (KC - 1);
+                    if (rr < 0) continue;
+                    const int64_t cc = colmajor ? (rr % h) * w + rr / h : rr;
+                    dcw[e * KC + k] += da * (double)x[(b * n + cc) * E + e];
+                    dx[(b * n + cc) * E + e] += (double)conv_w[e * KC + k] * da;
+                }
+            }
+        }
+}
+
+/*
  * The whole backward pass.  Inputs as fvo_layer plus dout (shaped like x).
  * Outputs dx, dz (shaped like x) and the gradients of both directions'
  * parameters (overwritten).  ln_w == NULL: no LayerNorm; otherwise the layer
@@ -707,18 +753,22 @@ static void xproj_adjoint(const double *u, const double *dv, int64_t M, int64_t 
  * of both scans' contributions and go to the forward direction's gradients,
  * while the backward direction's x_proj_w, dt_proj_w, dt_proj_b and A_log
  * gradients are zero (the layer does not read them) and its D gradient is dD
- * as usual.  Returns 0, -2,
+ * as usual.  conv_w != NULL (dense layers only): x is the Conv1D's input as in
+ * fvo_layer; the layer's adjoint with respect to its x (the Conv1D's output)
+ * goes through conv_silu_adjoint into dx, and the conv's weight and bias
+ * gradients into dconv_w (E, conv_k) and dconv_b (E).  Returns 0, -2,
  * -3 or -9 as fvo_layer.
  */
 int fvo_layer_bwd(const float *x, const float *z, const float *dout, const fvo_dir *pf, const fvo_dir *pb,
                   int64_t B, int64_t h, int64_t w, int64_t E, int64_t N, int64_t R, int64_t K, int axis,
                   const int32_t *idx, double *dx, double *dz, fvo_dir_grad *gf, fvo_dir_grad *gb,
                   fvo_bwd_stages *st, const float *ln_w, const float *ln_b, double ln_eps, double *dln_w,
-                  double *dln_b, double pool_scale, int64_t local_window)
+                  double *dln_b, double pool_scale, int64_t local_window, const float *conv_w,
+                  const float *conv_b, int64_t conv_k, double *dconv_w, double *dconv_b)
 {
     int64_t T, P;
     const int masked = idx != NULL;
-    if (axis < 0 || axis > 3 || (masked && axis > FVO_ROWS)) return -2;
+    if (axis < 0 || axis > 3 || (masked && axis > FVO_ROWS) || (masked && conv_w)) return -2;
     seq_shape(axis, h, w, &T, &P);
     const int64_t NX = R + 2 * N, M = B * T, ntok = masked ? B * K : B * h * w;
     const size_t me = (size_t)(M * E) * sizeof(double), mx = (size_t)(M * NX) * sizeof(double);
@@ -734,13 +784,19 @@ int fvo_layer_bwd(const float *x, const float *z, const float *dout, const fvo_d
     double *g = (double *)malloc((size_t)E * sizeof(double)), *ny = (double *)malloc((size_t)E * sizeof(double));
     double *dxs = (double *)malloc((size_t)(ntok * E) * sizeof(double));
     double *dD = (double *)calloc((size_t)E, sizeof(double));
+    double *xc = conv_w ? (double *)malloc((size_t)(ntok * E) * sizeof(double)) : NULL;
+    double *dxc = conv_w ? (double *)malloc((size_t)(ntok * E) * sizeof(double)) : NULL;
     double *v[2], *q[2], *dl[2], *s[2], *dv[2];
     int32_t *rows = masked ? (int32_t *)malloc((size_t)(B * K) * sizeof(int32_t)) : NULL;
     for (int d = 0; d < 2; ++d) {
         v[d] = (double *)malloc(mx); q[d] = (double *)malloc(me); dl[d] = (double *)malloc(me);
         s[d] = (double *)malloc(me); dv[d] = (double *)calloc((size_t)(M * NX), sizeof(double));
     }
-    if (!u || !gs || !du || !dd || !g || !ny || !dxs || !dD || (masked && !rows)) { rc = -9; goto done; }
+    if (!u || !gs || !du || !dd || !g || !ny || !dxs || !dD || (masked && !rows) || (conv_w && (!xc || !dxc))) {
+        rc = -9;
+        goto done;
+    }
+    if (conv_w) fvo_conv_silu(x, B, h, w, E, axis, conv_w, conv_b, conv_k, xc);
     if (ln_w)
         for (int64_t e = 0; e < E; ++e) dln_w[e] = dln_b[e] = 0.0;
     for (int d = 0; d < 2; ++d)
@@ -757,7 +813,7 @@ int fvo_layer_bwd(const float *x, const float *z, const float *dout, const fvo_d
         if (rc) goto done;
         fvo_pool_masked(x, rows, B, K, T, P, E, u);
     } else {
-        fvo_pool_dense(x, B, h, w, E, axis, u);
+        pool_dense_any(x, xc, B, h, w, E, axis, u);
     }
     for (int64_t i = 0; i < M * E; ++i) u[i] *= pool_scale;
     for (int d = 0; d < 2; ++d) {
@@ -775,12 +831,13 @@ int fvo_layer_bwd(const float *x, const float *z, const float *dout, const fvo_d
             if (masked) t = rows[b * K + c];
             else t = seq_pos(axis, h, w, c / w, c % w);
             const int64_t off = (b * ncell + c) * E, mt = (b * T + t) * E;
+            const double *xco = xc ? xc + off : NULL;
             if (ln_w)
-                output_token_adjoint_ln(s[0] + mt, s[1] + mt, x + off, z + off, dout + off, pf, pb, E, ln_w, ln_b,
-                                        ln_eps, ny, g, dz + off, dxs + off, dD, dln_w, dln_b);
+                output_token_adjoint_ln(s[0] + mt, s[1] + mt, x + off, xco, z + off, dout + off, pf, pb, E, ln_w,
+                                        ln_b, ln_eps, ny, g, dz + off, dxs + off, dD, dln_w, dln_b);
             else
-                output_token_adjoint(s[0] + mt, s[1] + mt, x + off, z + off, dout + off, pf, pb, E, g, dz + off,
-                                     dxs + off, dD);
+                output_token_adjoint(s[0] + mt, s[1] + mt, x + off, xco, z + off, dout + off, pf, pb, E, g,
+                                     dz + off, dxs + off, dD);
             for (int64_t e = 0; e < E; ++e) gs[mt + e] += g[e];
         }
     }
@@ -821,6 +878,11 @@ int fvo_layer_bwd(const float *x, const float *z, const float *dout, const fvo_d
             for (int64_t e = 0; e < E; ++e) dx[off + e] = dxs[off + e] + du[mt + e] * pool_scale / (double)P;
         }
     }
+    if (conv_w) {
+        /* dx holds dL/d(the conv's output): take it through the conv */
+        memcpy(dxc, dx, (size_t)(ntok * E) * sizeof(double));
+        conv_silu_adjoint(x, dxc, B, h, w, E, axis, conv_w, conv_b, conv_k, dx, dconv_w, dconv_b);
+    }
 
     if (st) {
         if (st->gs) memcpy(st->gs, gs, me);
@@ -831,6 +893,7 @@ int fvo_layer_bwd(const float *x, const float *z, const float *dout, const fvo_d
 
 done:
     free(u); free(gs); free(du); free(dd); free(g); free(ny); free(dxs); free(dD); free(rows); free(reset);
+    free(xc); free(dxc);
     for (int d = 0; d < 2; ++d) { free(v[d]); free(q[d]); free(dl[d]); free(s[d]); free(dv[d]); }
     return rc;
 }

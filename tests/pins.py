@@ -520,9 +520,9 @@ def _bwd_case(rng, axis, masked, B_=2, h=4, w=3, E=5, N=3, R=2):
     return pf, pb, x, z, dout, idx, (h, w)
 
 
-def _loss(O, x, z, dout, pf, pb, axis, idx, hw, ln=None, pool_scale=1.0, local=0):
+def _loss(O, x, z, dout, pf, pb, axis, idx, hw, ln=None, pool_scale=1.0, local=0, conv=None):
     return float(np.sum(dout.astype(np.float64) * O.layer(x, z, pf, pb, axis, idx=idx, hw=hw, ln=ln,
-                                                          pool_scale=pool_scale, local_window=local)))
+                                                          pool_scale=pool_scale, local_window=local, conv=conv)))
 
 
 def _perturbed(a, V, eps):
@@ -616,6 +616,47 @@ def pin_bwd_finite_differences_ln(O):
             scale = max(float(np.linalg.norm(grad)), 1e-30)
             assert abs(fd - an) <= 1e-6 * scale, "LayerNorm axis %d masked %s: d/d%s %s: analytic %.12g, " \
                 "finite difference %.12g" % (axis, masked, d, k or "", an, fd)
+
+
+def pin_bwd_finite_differences_conv(O):
+    """The same check for a layer whose x is the producer Conv1D's input: every
+    gradient, dx through the conv and the conv's weight and bias included,
+    matches the central difference of the forward oracle with the conv (both
+    pooling axes, the pool scale and the local backward scan)."""
+    eps = 2.0 ** -14
+    rng = np.random.default_rng(44)
+    for axis, scale, local in ((COLS, 1.0, 0), (ROWS, 0.25, 0), (COLS, 1.0, 3), (ROWS, 1.0, 2)):
+        pf, pb, x, z, dout, idx, hw = _bwd_case(rng, axis, False)
+        E = x.shape[-1]
+        conv = {k: _dyadic(v) for k, v in rand_conv(rng, E).items()}
+        g = O.layer_bwd(x, z, dout, pf, pb, axis, pool_scale=scale, local_window=local, conv=conv)
+        out = O.layer(x, z, pf, pb, axis, pool_scale=scale, local_window=local, conv=conv)
+        floor = 64 * 2.0 ** -52 * float(np.sum(np.abs(dout * out))) / (2.0 * eps)
+        targets = [("x", None), ("z", None), ("conv", "weight"), ("conv", "bias")] + \
+            [(d, k) for d in ("fwd", "bwd") for k in ("x_proj_w", "dt_proj_w", "dt_proj_b", "A_log", "D")]
+        for d, k in targets:
+            if k is None:
+                base, grad = (x, g["dx"]) if d == "x" else (z, g["dz"])
+            elif d == "conv":
+                base, grad = conv[k], g["conv"][k]
+            else:
+                base, grad = (pf if d == "fwd" else pb)[k], g[d][k]
+            V = rng.choice([-1.0, 1.0], size=base.shape)
+            L = []
+            for sgn in (1.0, -1.0):
+                arg = {"x": x, "z": z, "pf": dict(pf), "pb": dict(pb), "conv": dict(conv)}
+                pert = _perturbed(base, sgn * V, eps)
+                if k is None:
+                    arg[d] = pert
+                else:
+                    arg["conv" if d == "conv" else ("pf" if d == "fwd" else "pb")][k] = pert
+                L.append(_loss(O, arg["x"], arg["z"], dout, arg["pf"], arg["pb"], axis, None, None, pool_scale=scale,
+                               local=local, conv=arg["conv"]))
+            fd = (L[0] - L[1]) / (2.0 * eps)
+            an = float(np.sum(grad * V))
+            size = max(float(np.linalg.norm(grad)), 1e-30)
+            assert abs(fd - an) <= 1e-6 * size + floor, "Conv1D axis %d scale %g local %d: d/d%s %s: analytic " \
+                "%.12g, finite difference %.12g" % (axis, scale, local, d, k or "", an, fd)
 
 
 def pin_pool_scale_is_a_scaled_input(O):
@@ -835,6 +876,7 @@ ALL_PINS = [
     pin_bwd_finite_differences,
     pin_bwd_finite_differences_ln,
     pin_pool_scale_is_a_scaled_input,
+    pin_bwd_finite_differences_conv,
     pin_bwd_masked_equals_zero_filled,
     pin_conv_library,
     pin_conv_closed_forms,

@@ -126,7 +126,7 @@ MUTANTS = [
      "const double Ds = (double)pf->D[e] + (double)pb->D[e];\n        g[e] = r",
      "const double Ds = (double)pf->D[e];\n        g[e] = r", 1),
     ("LayerNorm adjoint's recomputed input without the skip",
-     "ny[e] = sf[e] + sb[e] + Ds * (double)x[e];", "ny[e] = sf[e] + sb[e];", 1),
+     "ny[e] = sf[e] + sb[e] + Ds * xe;", "ny[e] = sf[e] + sb[e];", 1),
     ("dz through the norm without its affine map", "dz[e] = de * o * sg", "dz[e] = de * ny[e] * sg", 1),
     # backward pass of the local backward scan
     ("adjoint's state recompute ignores the reset",
@@ -142,6 +142,21 @@ MUTANTS = [
      "gf->A_log[i] += gb->A_log[i]; gb->A_log[i] = 0.0;", "gf->A_log[i] += gb->A_log[i];", 1),
     ("local scan's adjoint with the backward set's parameters",
      "const fvo_dir *pd[2] = {pf, local_window > 0 ? &pl : pb};", "const fvo_dir *pd[2] = {pf, pb};", 1),
+    # backward pass through the producer Conv1D
+    ("conv adjoint without the SiLU derivative", "const double da = gxc[(b * n + cell) * E + e] * sg * (1.0 + a * (1.0 - sg));",
+     "const double da = gxc[(b * n + cell) * E + e] * sg;", 1),
+    ("conv adjoint spreads to the wrong tap", "dx[(b * n + cc) * E + e] += (double)conv_w[e * KC + k] * da;",
+     "dx[(b * n + cc) * E + e] += (double)conv_w[e * KC + (KC - 1 - k)] * da;", 1),
+    ("conv weight gradient from the output position", "dcw[e * KC + k] += da * (double)x[(b * n + cc) * E + e];",
+     "dcw[e * KC + k] += da * (double)x[(b * n + cell) * E + e];", 1),
+    ("conv bias gradient without the SiLU derivative", "                dcb[e] += da;",
+     "                dcb[e] += gxc[(b * n + cell) * E + e];", 1),
+    ("backward pools the conv's input", "        pool_dense_any(x, xc, B, h, w, E, axis, u);\n    }\n    for (int64_t i = 0; i < M * E; ++i) u[i] *= pool_scale;\n    for (int d",
+     "        pool_dense_any(x, NULL, B, h, w, E, axis, u);\n    }\n    for (int64_t i = 0; i < M * E; ++i) u[i] *= pool_scale;\n    for (int d", 1),
+    ("conv adjoint row-major on the transposed grid",
+     "const int colmajor = axis == FVO_NONE_COLMAJOR || axis == FVO_ROWS;",
+     "const int colmajor = axis == FVO_NONE_COLMAJOR;", 1),
+    ("output adjoint reads the conv's input", "const double *xco = xc ? xc + off : NULL;", "const double *xco = NULL;", 1),
     ("adjoint uses the current state for the decay", "dd += lam[n] * (A * a * prev + Bn * ut);",
      "dd += lam[n] * (A * a * Hs[k * N + n] + Bn * ut);", 1),
 ]
