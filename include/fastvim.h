@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define FASTVIM_ABI_VERSION 9
+#define FASTVIM_ABI_VERSION 10
 
 typedef enum fastvim_status {
     FASTVIM_OK = 0,
@@ -323,13 +323,25 @@ size_t fastvim_ssm_export_bytes(const fastvim_dims *dims, int pool_axis, int wha
  * the flag): its adjoint runs within each window, on the forward direction's
  * parameters, and nothing carries across a window's reset.
  *
+ * With FASTVIM_FLAG_CONV (params->conv_w, conv_b as for the forward call) x
+ * is the Conv1D's input and dx its gradient: with a[r] the conv's
+ * pre-activation at sequence position r, dxc the layer's gradient with
+ * respect to the conv's output and da = dxc silu'(a),
+ *   dx[r] = sum_k conv_w[k] da[r + 3 - k],  d conv_w[k] = sum_r da[r] x[r - 3 + k],
+ *   d conv_b = sum_r da[r]
+ * (per channel, along the oriented grid's sequence), written to
+ * grads->conv_w and conv_b.  The first pass pools x_conv (unless saved_u is
+ * given) and the second computes x_conv and da where it reads x, so neither
+ * is written.
+ *
  * Supported: pooled layers (COLS or ROWS, dense or masked) with T <= 128 scan
  * steps and the limits of the forward call, with or without
- * FASTVIM_FLAG_POST_NORM (then E <= 2048), FASTVIM_FLAG_POOL_SCALE and
- * FASTVIM_FLAG_LOCAL_BWD, in any combination; FASTVIM_ERR_UNSUPPORTED for
- * unpooled layers, longer scans, the LayerNorm with E > 2048, and the flags
- * FASTVIM_FLAG_FUSED and FASTVIM_FLAG_CONV (0 and FASTVIM_FLAG_STAGED run the
- * same kernels). */
+ * FASTVIM_FLAG_POST_NORM (then E <= 2048), FASTVIM_FLAG_POOL_SCALE,
+ * FASTVIM_FLAG_LOCAL_BWD and FASTVIM_FLAG_CONV (dense layers, not with the
+ * LayerNorm, as in the forward call), in any other combination;
+ * FASTVIM_ERR_UNSUPPORTED for unpooled layers, longer scans, the LayerNorm
+ * with E > 2048, the cases the forward call does not take, and
+ * FASTVIM_FLAG_FUSED (0 and FASTVIM_FLAG_STAGED run the same kernels). */
 
 /* Gradients of one direction's parameters: fp32 device buffers shaped like
  * the parameters, 4-byte aligned, overwritten by the call. */
@@ -348,6 +360,11 @@ typedef struct fastvim_grads {
      * otherwise. */
     float *ln_weight;
     float *ln_bias;
+    /* With FASTVIM_FLAG_CONV: the Conv1D's weight (E, FASTVIM_CONV_TAPS) and
+     * bias (E) gradients, fp32, 4-byte aligned, overwritten; ignored (may be
+     * NULL) otherwise. */
+    float *conv_w;
+    float *conv_b;
 } fastvim_grads;
 
 /* Bytes of workspace fastvim_ssm_bwd needs (0 if the sizes are invalid or
@@ -361,8 +378,8 @@ size_t fastvim_ssm_bwd_workspace_bytes(const fastvim_dims *dims, int pool_axis);
  * its workspace at least fastvim_ssm_bwd_workspace_bytes (256-byte aligned);
  * mask_idx as for the forward call (a token with an invalid index gets NaN in
  * dx and dz and takes no part in the pooled sums).  dx, dz, the workspace and
- * the ten (twelve with the LayerNorm) gradient buffers must overlap neither
- * each other nor any input or parameter (FASTVIM_ERR_OVERLAP).  B == 0 writes zero gradients.  Errors as
+ * the ten gradient buffers (and the LayerNorm's or the Conv1D's two) must
+ * overlap neither each other nor any input or parameter (FASTVIM_ERR_OVERLAP).  B == 0 writes zero gradients.  Errors as
  * fastvim_ssm_fwd, plus FASTVIM_ERR_NULL for a NULL grads or gradient buffer.
  * Enqueues its kernels on stream and returns. */
 int fastvim_ssm_bwd(const void *x, const void *z, const void *dout, const fastvim_params *params,

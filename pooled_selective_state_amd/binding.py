@@ -76,7 +76,8 @@ class DirGrads(ctypes.Structure):
 
 
 class Grads(ctypes.Structure):
-    _fields_ = [("fwd", DirGrads), ("bwd", DirGrads), ("ln_weight", ctypes.c_void_p), ("ln_bias", ctypes.c_void_p)]
+    _fields_ = [("fwd", DirGrads), ("bwd", DirGrads), ("ln_weight", ctypes.c_void_p), ("ln_bias", ctypes.c_void_p),
+                ("conv_w", ctypes.c_void_p), ("conv_b", ctypes.c_void_p)]
 
 
 EXPORTED_SYMBOLS = (
@@ -317,7 +318,7 @@ class BwdCall:
                  grads: Optional[Dict[str, Dict[str, torch.Tensor]]] = None,
                  workspace: Optional[torch.Tensor] = None, flags: int = 0,
                  saved_u: Optional[torch.Tensor] = None, ln: Optional[Dict[str, object]] = None,
-                 pool_scale: Optional[float] = None):
+                 pool_scale: Optional[float] = None, conv: Optional[Dict[str, torch.Tensor]] = None):
         self.dims = _layer_dims(x, z, params, mask_idx, hw)
         if dout.dtype != x.dtype or dout.shape != x.shape:
             raise ValueError("dout must match x in shape and dtype")
@@ -354,8 +355,25 @@ class BwdCall:
                 if t.dtype != torch.float32 or not t.is_contiguous() or t.shape != params["fwd"][f].shape:
                     raise ValueError("gradient %s.%s must be contiguous float32 shaped like the parameter" % (d, f))
             gd.append(DirGrads(*[grads[d][f].data_ptr() for f in DIR_FIELDS]))
+        conv_w = conv_b = None
+        if conv is not None:
+            conv_w, conv_b = conv["weight"], conv["bias"]
+            for t in (conv_w, conv_b):
+                if t.dtype != torch.float32 or not t.is_contiguous():
+                    raise ValueError("Conv1D weight and bias must be contiguous float32")
+            self._keep.extend([conv_w, conv_b])
+            flags |= FLAG_CONV
+            if "conv" not in grads:
+                grads = dict(grads, conv={"weight": torch.empty_like(conv_w), "bias": torch.empty_like(conv_b)})
+            for f, ref in (("weight", conv_w), ("bias", conv_b)):
+                t = grads["conv"][f]
+                if t.dtype != torch.float32 or not t.is_contiguous() or t.shape != ref.shape:
+                    raise ValueError("Conv1D gradient %s must be contiguous float32 shaped like the parameter" % f)
+            self.grads = grads
         lg = grads["ln"] if ln is not None else None
-        self.cgrads = Grads(gd[0], gd[1], _ptr(lg["weight"]) if lg else None, _ptr(lg["bias"]) if lg else None)
+        cg = grads["conv"] if conv is not None else None
+        self.cgrads = Grads(gd[0], gd[1], _ptr(lg["weight"]) if lg else None, _ptr(lg["bias"]) if lg else None,
+                            _ptr(cg["weight"]) if cg else None, _ptr(cg["bias"]) if cg else None)
         nbytes = bwd_workspace_bytes(self.dims, pool_axis)
         if workspace is None:
             workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=x.device)
@@ -366,7 +384,8 @@ class BwdCall:
             flags |= FLAG_POOL_SCALE
         self.params = Params(dirs[0], dirs[1], workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                              flags, 0, _ptr(ln_w), _ptr(ln_b), ln_eps,
-                             1.0 if pool_scale is None else float(pool_scale), None, None, _ptr(saved_u))
+                             1.0 if pool_scale is None else float(pool_scale), _ptr(conv_w), _ptr(conv_b),
+                             _ptr(saved_u))
 
     def run(self, stream=None) -> Dict[str, object]:
         st = lib().fastvim_ssm_bwd(_ptr(self.x), _ptr(self.z), _ptr(self.dout), ctypes.byref(self.params),
@@ -377,14 +396,16 @@ class BwdCall:
         res = {"dx": self.dx, "dz": self.dz, "fwd": self.grads["fwd"], "bwd": self.grads["bwd"]}
         if "ln" in self.grads and self.params.flags & FLAG_POST_NORM:
             res["ln"] = self.grads["ln"]
+        if "conv" in self.grads and self.params.flags & FLAG_CONV:
+            res["conv"] = self.grads["conv"]
         return res
 
 
 def ssm_bwd(x, z, dout, params, pool_axis=POOL_COLS, mask_idx=None, hw=None, workspace=None, stream=None,
-            flags=0, saved_u=None, ln=None, pool_scale=None):
-    """Gradients of the layer; returns {"dx", "dz", "fwd": {...}, "bwd": {...}} (and "ln" with ln)."""
+            flags=0, saved_u=None, ln=None, pool_scale=None, conv=None):
+    """Gradients of the layer; returns {"dx", "dz", "fwd": {...}, "bwd": {...}} (and "ln" / "conv" with those)."""
     return BwdCall(x, z, dout, params, pool_axis, mask_idx=mask_idx, hw=hw, workspace=workspace,
-                   flags=flags, saved_u=saved_u, ln=ln, pool_scale=pool_scale).run(stream)
+                   flags=flags, saved_u=saved_u, ln=ln, pool_scale=pool_scale, conv=conv).run(stream)
 
 
 def calib_copy(dst: torch.Tensor, src: torch.Tensor, stream=None) -> None:

@@ -198,18 +198,26 @@ int validate_bwd(const void* x, const void* z, const void* dout, const fastvim_p
                  int axis, const int32_t* idx, const void* dx, const void* dz, const fastvim_grads* gr, Geom* g,
                  BwdWorkspace* ws, bool* empty) {
     if (!prm) return FASTVIM_ERR_NULL;
-    const uint32_t unsupported = FASTVIM_FLAG_FUSED | FASTVIM_FLAG_CONV;
-    const uint32_t options =
-        FASTVIM_FLAG_STAGED | FASTVIM_FLAG_POST_NORM | FASTVIM_FLAG_POOL_SCALE | FASTVIM_FLAG_LOCAL_BWD;
+    const uint32_t unsupported = FASTVIM_FLAG_FUSED;
+    const uint32_t options = FASTVIM_FLAG_STAGED | FASTVIM_FLAG_POST_NORM | FASTVIM_FLAG_POOL_SCALE |
+                             FASTVIM_FLAG_LOCAL_BWD | FASTVIM_FLAG_CONV;
     if (prm->flags & ~(options | unsupported)) return FASTVIM_ERR_ARG;
     if (prm->flags & unsupported) return FASTVIM_ERR_UNSUPPORTED;
     const bool norm = (prm->flags & FASTVIM_FLAG_POST_NORM) != 0;
+    const bool conv = (prm->flags & FASTVIM_FLAG_CONV) != 0;
     int st = resolve_geom(d, axis, g);
     if (st) return st;
     if ((st = apply_pool_scale(*prm, g))) return st;
     if (!bwd_supported(*g) || (norm && !bwd_norm_supported(*g))) return FASTVIM_ERR_UNSUPPORTED;
+    if (conv && (g->masked || norm)) return FASTVIM_ERR_UNSUPPORTED;  // as the forward call
     if (!g->masked && idx) return FASTVIM_ERR_ARG;
     if (!gr) return FASTVIM_ERR_NULL;
+    if (conv) {
+        if (!prm->conv_w || !prm->conv_b || !gr->conv_w || !gr->conv_b) return FASTVIM_ERR_NULL;
+        if (!aligned(prm->conv_w, 16) || !aligned(prm->conv_b, 4) || !aligned(gr->conv_w, 4) ||
+            !aligned(gr->conv_b, 4))
+            return FASTVIM_ERR_ALIGN;
+    }
     if (norm) {
         if (!prm->ln_weight || !prm->ln_bias || !gr->ln_weight || !gr->ln_bias) return FASTVIM_ERR_NULL;
         if (!aligned(prm->ln_weight, 16) || !aligned(prm->ln_bias, 16) || !aligned(gr->ln_weight, 4) ||
@@ -229,10 +237,13 @@ int validate_bwd(const void* x, const void* z, const void* dout, const fastvim_p
             gs[5 * k + i] = Span{ps[i], gsz[i] * sizeof(float)};
         }
     }
-    const int ngs = norm ? 12 : 10;
+    const int ngs = norm || conv ? 12 : 10;
     if (norm) {
         gs[10] = Span{gr->ln_weight, (size_t)g->E * sizeof(float)};
         gs[11] = Span{gr->ln_bias, (size_t)g->E * sizeof(float)};
+    } else if (conv) {
+        gs[10] = Span{gr->conv_w, (size_t)(g->E * FASTVIM_CONV_TAPS) * sizeof(float)};
+        gs[11] = Span{gr->conv_b, (size_t)g->E * sizeof(float)};
     }
     for (int i = 0; i < ngs; ++i)
         for (int j = i + 1; j < ngs; ++j)
@@ -262,6 +273,9 @@ int validate_bwd(const void* x, const void* z, const void* dout, const fastvim_p
     if (norm) {
         ins[nin++] = Span{prm->ln_weight, (size_t)g->E * sizeof(float)};
         ins[nin++] = Span{prm->ln_bias, (size_t)g->E * sizeof(float)};
+    } else if (conv) {
+        ins[nin++] = Span{prm->conv_w, (size_t)(g->E * FASTVIM_CONV_TAPS) * sizeof(float)};
+        ins[nin++] = Span{prm->conv_b, (size_t)g->E * sizeof(float)};
     }
     Span outs[15] = {{dx, io}, {dz, io}, {prm->workspace, need}};
     const int nout = 3 + ngs;
@@ -289,6 +303,7 @@ int run_bwd(const Geom& g, const void* x, const void* z, const void* dout, const
     };
     const bool norm = (p.flags & FASTVIM_FLAG_POST_NORM) != 0;
     const bool local = (p.flags & FASTVIM_FLAG_LOCAL_BWD) != 0;  // p holds the effective parameters
+    const bool conv = (p.flags & FASTVIM_FLAG_CONV) != 0;
     if (g.masked && !ok(launch_mask_rows(g, idx, ws.fwd, s))) return FASTVIM_ERR_HIP;
     if (norm) {
         // the norm's adjoint needs y, hence both scans' outputs: recompute the
@@ -303,6 +318,14 @@ int run_bwd(const Geom& g, const void* x, const void* z, const void* dout, const
             !ok(launch_colsum(ws.du_f, M, g.E, g.E, gr.ln_weight, nullptr, ws.tmp, s)) ||
             !ok(launch_colsum(ws.du_b, M, g.E, g.E, gr.ln_bias, nullptr, ws.tmp, s)))
             return FASTVIM_ERR_HIP;
+    } else if (conv) {
+        // u pools the conv's output (unless saved); the first pass then sums g only
+        BwdWorkspace wg = ws;
+        wg.u_saved = true;
+        if ((!ws.u_saved && !ok(launch_conv_pool(g, x, p, ws.fwd, s))) ||
+            !ok(launch_bwd_pool(g, x, z, dout, wg, s)) || !ok(launch_proj(g, x, p, ws.fwd, s)))
+            return FASTVIM_ERR_HIP;
+        if (local && !ok(launch_scan(g, x, p, ws.fwd, s))) return FASTVIM_ERR_HIP;
     } else {
         if (!ok(launch_bwd_pool(g, x, z, dout, ws, s)) || !ok(launch_proj(g, x, p, ws.fwd, s)))
             return FASTVIM_ERR_HIP;
@@ -347,6 +370,18 @@ int run_bwd(const Geom& g, const void* x, const void* z, const void* dout, const
     }
     if (!ok(launch_colsum_batch(batch, s))) return FASTVIM_ERR_HIP;
     if (norm) return ok(launch_bwd_norm_pass2(g, p, ws, dx, dz, s)) ? FASTVIM_OK : FASTVIM_ERR_HIP;
+    if (conv) {
+        // second pass through the conv; its partial rows go to the checkpoint
+        // region (free once the scan adjoint has run; large enough: see
+        // bwd_workspace_layout)
+        const int64_t np = bwd_conv_parts(g);
+        if (!ok(launch_bwd_conv_epilogue(g, x, z, dout, p, ws.fwd.s_f, ws.fwd.s_b, ws.du, ws.ckpt, dx, dz, s)) ||
+            !ok(launch_colsum(ws.ckpt, np, E, 6 * E, gr.fwd.D, gr.bwd.D, ws.tmp, s)) ||
+            !ok(launch_colsum(ws.ckpt + E, np, E, 6 * E, gr.conv_b, nullptr, ws.tmp, s)) ||
+            !ok(launch_colsum(ws.ckpt + 2 * E, np, 4 * E, 6 * E, gr.conv_w, nullptr, ws.tmp, s)))
+            return FASTVIM_ERR_HIP;
+        return FASTVIM_OK;
+    }
     if (!ok(launch_bwd_epilogue(g, x, z, dout, p, ws, dx, dz, s))) return FASTVIM_ERR_HIP;
     if (!ok(launch_colsum(ws.dDp, bwd_dd_parts(g), E, E, gr.fwd.D, gr.bwd.D, ws.tmp, s))) return FASTVIM_ERR_HIP;
     return FASTVIM_OK;
@@ -413,8 +448,11 @@ size_t bwd_workspace_layout(const Geom& g, void* base, BwdWorkspace* ws) {
     };
     int64_t tmpf = 1;
     // (the local backward scan sums twice the rows of the per-image and per-chunk partials)
+    // (the Conv1D's second pass leaves bwd_conv_parts(g) rows of 6 E partials
+    // in the checkpoint region, which holds at least 16384 B ceil(E / 64) >=
+    // 256 B E floats against at most 32 B * 6 E)
     for (int64_t v : {stage1(ND, E), stage1(M, E), stage1(2 * B, E * 16), stage1(2 * B, E * R), stage1(2 * B, E),
-                      stage1(2 * MC, NX * E)})
+                      stage1(2 * MC, NX * E), stage1(bwd_conv_parts(g), 4 * E)})
         tmpf = v > tmpf ? v : tmpf;
     const size_t o_tmp = take((size_t)tmpf * sizeof(float));
     if (base && ws) {
@@ -555,6 +593,10 @@ int fastvim_ssm_bwd(const void* x, const void* z, const void* dout, const fastvi
         if ((params->flags & FASTVIM_FLAG_POST_NORM) &&
             (launch_fill_zero(grads->ln_weight, g.E, s) != hipSuccess ||
              launch_fill_zero(grads->ln_bias, g.E, s) != hipSuccess))
+            return FASTVIM_ERR_HIP;
+        if ((params->flags & FASTVIM_FLAG_CONV) &&
+            (launch_fill_zero(grads->conv_w, g.E * FASTVIM_CONV_TAPS, s) != hipSuccess ||
+             launch_fill_zero(grads->conv_b, g.E, s) != hipSuccess))
             return FASTVIM_ERR_HIP;
         return FASTVIM_OK;
     }

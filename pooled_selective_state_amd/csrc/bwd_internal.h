@@ -89,6 +89,14 @@ hipError_t launch_bwd_epilogue(const Geom& g, const void* x, const void* z, cons
 // the (B T, E) partials of dD, d ln_w and d ln_b into du, du_f and du_b.
 // Pass 2 needs du and turns dx into dL/dx.
 bool bwd_norm_supported(const Geom& g);
+
+// Backward second pass of a layer whose x is the producer Conv1D's input
+// (conv.hip): dx (through the conv) and dz, and bwd_conv_parts(g) rows of
+// partials [dD (E) | d conv_b (E) | d conv_w (E, 4)] into parts.
+int64_t bwd_conv_parts(const Geom& g);
+hipError_t launch_bwd_conv_epilogue(const Geom& g, const void* x, const void* z, const void* dout,
+                                    const fastvim_params& p, const float* sf, const float* sb, const float* du,
+                                    float* parts, void* dx, void* dz, hipStream_t st);
 hipError_t launch_bwd_norm_pass1(const Geom& g, const void* x, const void* z, const void* dout,
                                  const fastvim_params& p, const BwdWorkspace& ws, void* dx, void* dz,
                                  hipStream_t st);

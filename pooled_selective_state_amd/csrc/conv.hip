@@ -19,7 +19,7 @@
 // is the neighbouring lane's cells, loaded at about the same time, and comes
 // from the caches.  The kernels follow the pool and epilogue kernels
 // (pool.hip, epilogue.hip) otherwise.
-#include "fastvim_internal.h"
+#include "bwd_internal.h"
 
 namespace fastvim {
 namespace {
@@ -297,6 +297,219 @@ hipError_t launch_conv_epilogue(const Geom& g, const void* x, const void* z, con
                                 const Workspace& ws, void* out, hipStream_t st) {
     return g.io == FASTVIM_BF16 ? conv_epi_t<IoBf16>(g, x, z, p, ws, out, st)
                                 : conv_epi_t<IoF32>(g, x, z, p, ws, out, st);
+}
+
+namespace {
+
+// ------------------------------------------------------- backward, pass 2
+// The second pass of the backward pass of a layer whose x is the Conv1D's
+// input.  The layer's own adjoint gives, per sequence position q (cell of
+// scan position t(q) = q / P),
+//   g[q]   = dout silu(z),  dxc[q] = g (D_fwd + D_bwd) + du[b, t(q)] / P
+//   dz[q]  = dout (s_fwd + s_bwd + (D_fwd + D_bwd) x_conv) silu'(z)
+// and the conv's adjoint, with a[q] the pre-activation and da = dxc silu'(a),
+//   dx[r]  = sum_k conv_w[k] da[r + 3 - k],  d conv_w[k] += da[r] x[r - 3 + k],
+//   d conv_b += da[r],  dD += g[r] x_conv[r].
+// A lane walks a run of the sequence positions of one scan position with a
+// front q = r + 3 three steps ahead of the position r it finishes: at the
+// front it loads x, z and dout and forms da[q]; at r it has x[r - 3 .. r + 3]
+// in a window and da[r .. r + 3] in a ring.  Positions before the sequence
+// have x = 0, positions after it da = 0.  Workgroups loop over the (image,
+// scan position) items and keep per-lane sums; at the end each workgroup
+// writes one row of partials [dD | d conv_b | d conv_w] (6 E floats, its
+// channel slice), summed over the rows by a later kernel.
+constexpr int kCbThreads = 256;
+constexpr int kCbSlice = 64;  // vector lanes per workgroup channel slice
+
+template <class IO, bool COLS>
+__global__ void __launch_bounds__(kCbThreads)
+bwd_conv_epilogue_kernel(const typename IO::elem* __restrict__ x, const typename IO::elem* __restrict__ z,
+                         const typename IO::elem* __restrict__ dout, const float* __restrict__ cw,
+                         const float* __restrict__ cb, const float* __restrict__ sf, const float* __restrict__ sb,
+                         const float* __restrict__ du, const float* __restrict__ Df, const float* __restrict__ Db,
+                         typename IO::elem* __restrict__ dx, typename IO::elem* __restrict__ dz,
+                         float* __restrict__ parts, int B, int T, int P, int h, int w, int E, int VE, int VEs, int G,
+                         float inv_p) {
+    constexpr int V = IO::V;
+    using raw = typename IO::raw;
+    extern __shared__ float red[];  // [G][6][VEs V]
+    const int tid = threadIdx.x, c = tid % VEs, g = tid / VEs;
+    const int vc = blockIdx.y * VEs + c;  // vector lane of the channel dimension
+    const bool act = g < G && vc < VE;
+    const int coff = vc * V;
+    const int n = h * w;
+    const int run = (P + G - 1) / G;
+    float aD[V], aB[V], aW[V][kTaps];
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+        aD[v] = aB[v] = 0.f;
+#pragma unroll
+        for (int k = 0; k < kTaps; ++k) aW[v][k] = 0.f;
+    }
+    if (act) {
+        ConvW<V> W;
+        load_conv_w<V>(cw, cb, coff, W);
+        float dsum[V];
+#pragma unroll
+        for (int v = 0; v < V; ++v) dsum[v] = Df[coff + v] + Db[coff + v];
+        // token (within the image) of sequence position q
+        auto tok_of = [&](int q) { return COLS ? q : (q % h) * w + q / h; };
+        for (int64_t item = blockIdx.x; item < (int64_t)B * T; item += gridDim.x) {
+            const int64_t b = item / T;
+            const int t = (int)(item - b * T);
+            const int ra = t * P + g * run;
+            const int rb = ra + run < (t + 1) * P ? ra + run : (t + 1) * P;
+            if (ra >= rb) continue;
+            const int64_t img = b * (int64_t)n * E;
+            float sv[V];
+#pragma unroll
+            for (int v = 0; v < V; v += 4) {
+                const f32x4 q1 = load_raw<false>(sf + (b * T + t) * E + coff + v);
+                const f32x4 q2 = load_raw<false>(sb + (b * T + t) * E + coff + v);
+                sv[v] = q1.x + q2.x;
+                sv[v + 1] = q1.y + q2.y;
+                sv[v + 2] = q1.z + q2.z;
+                sv[v + 3] = q1.w + q2.w;
+            }
+            raw xw[7];  // x[q - 6 .. q]
+            raw zR[4], oR[4];  // z, dout of positions q - 3 .. q
+            float dR[4][V];    // da of positions q - 3 .. q
+#pragma unroll
+            for (int k = 0; k < 7; ++k) xw[k] = raw{};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                zR[k] = oR[k] = raw{};
+#pragma unroll
+                for (int v = 0; v < V; ++v) dR[k][v] = 0.f;
+            }
+            for (int q = ra - 3; q < rb + 3; ++q) {
+#pragma unroll
+                for (int k = 0; k < 6; ++k) xw[k] = xw[k + 1];
+#pragma unroll
+                for (int k = 0; k < 3; ++k) {
+                    zR[k] = zR[k + 1];
+                    oR[k] = oR[k + 1];
+#pragma unroll
+                    for (int v = 0; v < V; ++v) dR[k][v] = dR[k + 1][v];
+                }
+                const bool inseq = q >= 0 && q < n;
+                const int64_t off = img + (int64_t)tok_of(inseq ? q : 0) * E + coff;
+                xw[6] = inseq ? load_raw<false>(x + off) : raw{};
+                if (q >= ra) {  // front: da[q]
+                    if (inseq) {
+                        zR[3] = load_raw<false>(z + off);
+                        oR[3] = load_raw<false>(dout + off);
+                        const float* ur = du + (b * T + q / P) * E + coff;
+#pragma unroll
+                        for (int v = 0; v < V; ++v) {
+                            float a = fmaf(W.w[v][3], raw_at(xw[6], v), W.b[v]);
+                            a = fmaf(W.w[v][2], raw_at(xw[5], v), a);
+                            a = fmaf(W.w[v][1], raw_at(xw[4], v), a);
+                            a = fmaf(W.w[v][0], raw_at(xw[3], v), a);
+                            const float zv = raw_at(zR[3], v), sgz = __builtin_amdgcn_rcpf(1.f + __expf(-zv));
+                            const float gv = raw_at(oR[3], v) * zv * sgz;
+                            const float dxc = fmaf(gv, dsum[v], ur[v] * inv_p);
+                            const float sga = __builtin_amdgcn_rcpf(1.f + __expf(-a));
+                            dR[3][v] = dxc * sga * fmaf(a, 1.f - sga, 1.f);
+                        }
+                    } else {
+#pragma unroll
+                        for (int v = 0; v < V; ++v) dR[3][v] = 0.f;
+                    }
+                }
+                if (q >= ra + 3) {  // finish r = q - 3 (x[r - 3 .. r] = xw[0 .. 3])
+                    const int r = q - 3;
+                    float ox[V], oz[V];
+#pragma unroll
+                    for (int v = 0; v < V; ++v) {
+                        float a = fmaf(W.w[v][3], raw_at(xw[3], v), W.b[v]);
+                        a = fmaf(W.w[v][2], raw_at(xw[2], v), a);
+                        a = fmaf(W.w[v][1], raw_at(xw[1], v), a);
+                        a = fmaf(W.w[v][0], raw_at(xw[0], v), a);
+                        const float xc = silu(a);
+                        const float zv = raw_at(zR[0], v), dv = raw_at(oR[0], v);
+                        const float sgz = __builtin_amdgcn_rcpf(1.f + __expf(-zv));
+                        const float gv = dv * zv * sgz;
+                        oz[v] = dv * fmaf(dsum[v], xc, sv[v]) * sgz * fmaf(zv, 1.f - sgz, 1.f);
+                        ox[v] = fmaf(W.w[v][0], dR[3][v],
+                                     fmaf(W.w[v][1], dR[2][v], fmaf(W.w[v][2], dR[1][v], W.w[v][3] * dR[0][v])));
+                        aD[v] = fmaf(gv, xc, aD[v]);
+                        aB[v] += dR[0][v];
+#pragma unroll
+                        for (int k = 0; k < kTaps; ++k) aW[v][k] = fmaf(dR[0][v], raw_at(xw[k], v), aW[v][k]);
+                    }
+                    const int64_t ro = img + (int64_t)tok_of(r) * E + coff;
+                    store_vec<true>(dx + ro, ox);
+                    store_vec<true>(dz + ro, oz);
+                }
+            }
+        }
+    }
+    // the workgroup's partial row: groups added through LDS in a fixed order
+    const int width = VEs * V;
+    if (g < G) {
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+            float* rg = red + (int64_t)g * 6 * width + c * V + v;
+            rg[0] = aD[v];
+            rg[width] = aB[v];
+#pragma unroll
+            for (int k = 0; k < kTaps; ++k) rg[(2 + k) * width] = aW[v][k];
+        }
+    }
+    __syncthreads();
+    float* prow = parts + (int64_t)blockIdx.x * 6 * E;
+    const int col0 = blockIdx.y * VEs * V;
+    for (int o = tid; o < 6 * width; o += kCbThreads) {
+        const int k = o / width, cc = o - k * width;
+        if (col0 + cc >= E) continue;
+        float s = red[o];
+        for (int gg = 1; gg < G; ++gg) s += red[(int64_t)gg * 6 * width + o];
+        if (k < 2) prow[k * E + col0 + cc] = s;
+        else prow[2 * E + (col0 + cc) * kTaps + (k - 2)] = s;
+    }
+}
+
+template <class IO>
+hipError_t bwd_conv_epi_t(const Geom& g, const void* x, const void* z, const void* dout, const fastvim_params& p,
+                          const float* sf, const float* sb, const float* du, float* parts, int64_t nparts, void* dx,
+                          void* dz, hipStream_t st) {
+    using elem = typename IO::elem;
+    const int VE = (int)(g.E / IO::V);
+    const int VEs = VE < kCbSlice ? VE : kCbSlice;
+    int G = kCbThreads / VEs;
+    if (G > g.P) G = (int)g.P;
+    const dim3 grid((unsigned)nparts, (unsigned)((VE + VEs - 1) / VEs));
+    const size_t lds = (size_t)G * 6 * VEs * IO::V * sizeof(float);
+    const auto* xe = static_cast<const elem*>(x);
+    const auto* ze = static_cast<const elem*>(z);
+    const auto* de = static_cast<const elem*>(dout);
+    auto* dxe = static_cast<elem*>(dx);
+    auto* dze = static_cast<elem*>(dz);
+    if (g.axis == FASTVIM_POOL_COLS)
+        hipLaunchKernelGGL((bwd_conv_epilogue_kernel<IO, true>), grid, dim3(kCbThreads), lds, st, xe, ze, de, p.conv_w,
+                           p.conv_b, sf, sb, du, p.fwd.D, p.bwd.D, dxe, dze, parts, (int)g.B, (int)g.T, (int)g.P,
+                           (int)g.h, (int)g.w, (int)g.E, VE, VEs, G, pool_norm(g));
+    else
+        hipLaunchKernelGGL((bwd_conv_epilogue_kernel<IO, false>), grid, dim3(kCbThreads), lds, st, xe, ze, de,
+                           p.conv_w, p.conv_b, sf, sb, du, p.fwd.D, p.bwd.D, dxe, dze, parts, (int)g.B, (int)g.T,
+                           (int)g.P, (int)g.h, (int)g.w, (int)g.E, VE, VEs, G, pool_norm(g));
+    return hipGetLastError();
+}
+
+}  // namespace
+
+int64_t bwd_conv_parts(const Geom& g) {
+    const int64_t items = g.B * g.T, cap = 32 * g.B;
+    return items < cap ? items : cap;
+}
+
+hipError_t launch_bwd_conv_epilogue(const Geom& g, const void* x, const void* z, const void* dout,
+                                    const fastvim_params& p, const float* sf, const float* sb, const float* du,
+                                    float* parts, void* dx, void* dz, hipStream_t st) {
+    const int64_t np = bwd_conv_parts(g);
+    return g.io == FASTVIM_BF16 ? bwd_conv_epi_t<IoBf16>(g, x, z, dout, p, sf, sb, du, parts, np, dx, dz, st)
+                                : bwd_conv_epi_t<IoF32>(g, x, z, dout, p, sf, sb, du, parts, np, dx, dz, st);
 }
 
 }  // namespace fastvim

@@ -32,7 +32,7 @@ def test_library_exports_every_declared_function():
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(Bd.EXPORTED_SYMBOLS)
-    assert lib.fastvim_abi_version() == 9
+    assert lib.fastvim_abi_version() == 10
 
 
 def test_status_strings():
@@ -50,8 +50,9 @@ def test_struct_layout_matches_header():
     assert ctypes.sizeof(Bd.Params) == 2 * 40 + 8 + 8 + 8 + 8 + 8 + 4 + 4 + 8 + 8 + 8
     assert Bd.Params.saved_u.offset == ctypes.sizeof(Bd.Params) - 8
     assert Bd.Params.pool_scale.offset == Bd.Params.ln_eps.offset + 4
-    assert ctypes.sizeof(Bd.DirGrads) == 40 and ctypes.sizeof(Bd.Grads) == 96
+    assert ctypes.sizeof(Bd.DirGrads) == 40 and ctypes.sizeof(Bd.Grads) == 112
     assert Bd.Grads.ln_weight.offset == 80 and Bd.Grads.ln_bias.offset == 88
+    assert Bd.Grads.conv_w.offset == 96 and Bd.Grads.conv_b.offset == 104
 
 
 def _ws(dims, axis):
@@ -359,7 +360,7 @@ def test_bwd_unsupported_and_bad_flags():
         assert FakeBwd(axis=axis).bwd() == EUNSUP
     assert FakeBwd(h=129).bwd() == EUNSUP
     assert FakeBwd(N=8).bwd() == EUNSUP
-    for flags, code in ((P.FLAG_FUSED, EUNSUP), (P.FLAG_CONV, EUNSUP), (64, EARG),
+    for flags, code in ((P.FLAG_FUSED, EUNSUP), (64, EARG),
                         (P.FLAG_STAGED, OK)):
         c = FakeBwd()
         c.params.flags = flags
@@ -470,6 +471,51 @@ def test_bwd_local_scan_validation():
     assert c.bwd() == ENULL
 
 
+def _conv_bwd(**kw):
+    """A backward call with the producer Conv1D (fake addresses)."""
+    c = FakeBwd(**kw)
+    far = 1 << 45
+    c.params.flags = P.FLAG_CONV
+    c.params.conv_w, c.params.conv_b = far, far + 65536
+    c.grads.conv_w, c.grads.conv_b = far + 2 * 65536, far + 3 * 65536
+    return c
+
+
+def test_bwd_conv_validation():
+    """The Conv1D's parameters and gradient buffers of a backward call are
+    checked before any launch; masked layers and the LayerNorm are not
+    supported with it, as in the forward call."""
+    for attr in ("conv_w", "conv_b"):
+        c = _conv_bwd()
+        setattr(c.params, attr, None)
+        assert c.bwd() == ENULL, attr
+        c = _conv_bwd()
+        setattr(c.grads, attr, None)
+        assert c.bwd() == ENULL, "grad " + attr
+    c = _conv_bwd()
+    c.params.conv_w += 4
+    assert c.bwd() == EALIGN
+    c = _conv_bwd()
+    c.grads.conv_b += 2
+    assert c.bwd() == EALIGN
+    c = _conv_bwd()
+    c.grads.conv_b = c.grads.conv_w + 16  # the two gradients overlap
+    assert c.bwd() == EOVERLAP
+    c = _conv_bwd()
+    c.grads.conv_w = c.params.conv_w
+    assert c.bwd() == EOVERLAP
+    c = _conv_bwd()
+    c.grads.conv_b = c.dx + 32
+    assert c.bwd() == EOVERLAP
+    assert _conv_bwd(K=3).bwd() == EUNSUP
+    c = _conv_bwd()
+    c.params.flags |= P.FLAG_POST_NORM
+    assert c.bwd() == EUNSUP
+    c = _conv_bwd()
+    c.params.workspace_bytes -= 1
+    assert c.bwd() == EWS  # past every other check
+
+
 def test_bwd_alignment():
     for attr, off in (("dx", 4), ("dz", 8), ("dout", 4), ("x", 2)):
         c = FakeBwd()
@@ -535,7 +581,7 @@ def test_conv_validation():
     expect(c, EUNSUP)
     c = FakeBwd()
     c.params.flags = P.FLAG_CONV
-    assert c.bwd() == EUNSUP
+    assert c.bwd() == ENULL  # the backward pass takes the conv, and needs its parameters
     c = FakeCall()
     c.params.flags = 64
     expect(c, EARG)

@@ -26,7 +26,7 @@ import torch
 import oracle
 import pooled_selective_state_amd as P
 from gpu_util import BF16_TOL, FP32_TOL, check, dev, dev_params, host
-from pins import rand_dir, rand_ln
+from pins import rand_conv, rand_dir, rand_ln
 from pooled_selective_state_amd import configs as C
 from pooled_selective_state_amd.inputs import DIRECTIONS, draw_workload, random_mask, round_to_bf16, zero_D
 
@@ -50,27 +50,30 @@ def _dev_ln(ln):
 
 
 def gpu_bwd(x, z, dout, prm, axis, idx=None, hw=None, dtype=torch.float32, flags=0, saved=None, ln=None,
-            pool_scale=None):
+            pool_scale=None, conv=None):
     """saved: None (the backward pools x itself) or the flags of a forward call
     that first writes the pooled tokens the backward then reads (saved_u).
     ln: the post-SSM LayerNorm (host arrays), for both calls."""
     idd = None if idx is None else dev(idx, torch.int32)
     xd, zd, pd = dev(x, dtype), dev(z, dtype), dev_params(prm)
     lnd = _dev_ln(ln)
+    cvd = None if conv is None else {"weight": dev(conv["weight"]), "bias": dev(conv["bias"])}
     su = None
     if saved is not None:
         h, w = (x.shape[1], x.shape[2]) if idx is None else hw
         su = torch.full((x.shape[0], h if axis == P.POOL_COLS else w, x.shape[-1]), float("nan"), device="cuda")
         P.SSMCall(xd, zd, pd, axis, mask_idx=idd, hw=hw, flags=saved | (flags & P.FLAG_LOCAL_BWD), saved_u=su,
-                  ln=lnd, pool_scale=pool_scale).run()
+                  ln=lnd, pool_scale=pool_scale, conv=cvd).run()
     call = P.BwdCall(xd, zd, dev(dout, dtype), pd, axis, mask_idx=idd, hw=hw, flags=flags, saved_u=su, ln=lnd,
-                     pool_scale=pool_scale)
+                     pool_scale=pool_scale, conv=cvd)
     res = call.run()
     torch.cuda.synchronize()
     out = {"dx": host(res["dx"]), "dz": host(res["dz"]),
            **{d: {f: host(res[d][f]) for f in FIELDS} for d in DIRECTIONS}}
     if ln is not None:
         out["ln"] = {f: host(res["ln"][f]) for f in ("weight", "bias")}
+    if conv is not None:
+        out["conv"] = {f: host(res["conv"][f]) for f in ("weight", "bias")}
     return out
 
 
@@ -82,20 +85,27 @@ def compare(got, ref, tol, tag, sel=None, params=True):
         for d in DIRECTIONS:
             for f in FIELDS:
                 check(got[d][f], ref[d][f], tol, "%s d%s.%s" % (tag, d, f))
-        if "ln" in ref:
-            for f in ("weight", "bias"):
-                check(got["ln"][f], ref["ln"][f], tol, "%s d ln_%s" % (tag, f))
+        for opt in ("ln", "conv"):
+            if opt in ref:
+                for f in ("weight", "bias"):
+                    check(got[opt][f], ref[opt][f], tol, "%s d %s_%s" % (tag, opt, f))
 
 
-def bwd_check(x, z, dout, prm, axis, tol, dtype, tag, idx=None, hw=None, twin=True, saved=None, ln=None):
+def bwd_check(x, z, dout, prm, axis, tol, dtype, tag, idx=None, hw=None, twin=True, saved=None, ln=None,
+              conv=None, flags=0, pool_scale=None):
     """GPU gradients and those of the D = 0 twin against the oracle."""
-    got = gpu_bwd(x, z, dout, prm, axis, idx=idx, hw=hw, dtype=dtype, saved=saved, ln=ln)
-    ref = oracle.layer_bwd(x, z, dout, prm["fwd"], prm["bwd"], axis, idx=idx, hw=hw, ln=ln)
+    local = P.LOCAL_WINDOW if flags & P.FLAG_LOCAL_BWD else 0
+    ps = 1.0 if pool_scale is None else pool_scale
+    kw = dict(idx=idx, hw=hw, dtype=dtype, saved=saved, ln=ln, conv=conv, flags=flags, pool_scale=pool_scale)
+    got = gpu_bwd(x, z, dout, prm, axis, **kw)
+    ref = oracle.layer_bwd(x, z, dout, prm["fwd"], prm["bwd"], axis, idx=idx, hw=hw, ln=ln, conv=conv,
+                           local_window=local, pool_scale=ps)
     compare(got, ref, tol, tag)
     if twin:
         p0 = zero_D(prm)
-        got0 = gpu_bwd(x, z, dout, p0, axis, idx=idx, hw=hw, dtype=dtype, saved=saved, ln=ln)
-        ref0 = oracle.layer_bwd(x, z, dout, p0["fwd"], p0["bwd"], axis, idx=idx, hw=hw, ln=ln)
+        got0 = gpu_bwd(x, z, dout, p0, axis, **kw)
+        ref0 = oracle.layer_bwd(x, z, dout, p0["fwd"], p0["bwd"], axis, idx=idx, hw=hw, ln=ln, conv=conv,
+                                local_window=local, pool_scale=ps)
         compare(got0, ref0, tol, tag + " (D=0)", params=False)
     return got
 
@@ -252,10 +262,11 @@ def test_bwd_rows_is_cols_on_transposed_grid():
 
 
 # ------------------------------------------------------------------ full size
-def _sampled_full_size(cfg, axis=P.POOL_COLS, saved=None, norm=False, local=False):
+def _sampled_full_size(cfg, axis=P.POOL_COLS, saved=None, norm=False, local=False, with_conv=False):
     wl = draw_workload(cfg)
     x, z, prm, idx = wl["x"], wl["z"][0], wl["params"][0], wl["idx"]
     ln = rand_ln(np.random.default_rng(78), cfg.E) if norm else None
+    conv = rand_conv(np.random.default_rng(79), cfg.E) if with_conv else None
     sel = np.array([0, cfg.B - 1])
     rng = np.random.default_rng(77)
     dout = np.zeros_like(x)
@@ -266,14 +277,15 @@ def _sampled_full_size(cfg, axis=P.POOL_COLS, saved=None, norm=False, local=Fals
     hw = (cfg.h, cfg.w) if cfg.masked else None
     print("\n[%s bwd] B=%d grid=%dx%d E=%d axis %d, upstream gradient on images %s, pooled tokens %s%s%s"
           % (cfg.name, cfg.B, cfg.h, cfg.w, cfg.E, axis, list(sel), "saved" if saved is not None else "recomputed",
-             ", post-SSM LayerNorm" if norm else "", ", local backward scan" if local else ""), flush=True)
-    got = gpu_bwd(x, z, dout, prm, axis, idx=idx, hw=hw, dtype=dt, saved=saved, ln=ln,
+             ", post-SSM LayerNorm" if norm else "", ", local backward scan" if local else "")
+          + (", producer Conv1D" if with_conv else ""), flush=True)
+    got = gpu_bwd(x, z, dout, prm, axis, idx=idx, hw=hw, dtype=dt, saved=saved, ln=ln, conv=conv,
                   flags=P.FLAG_LOCAL_BWD if local else 0)
     rest = np.setdiff1d(np.arange(cfg.B), sel)
     for name in ("dx", "dz"):
         assert np.count_nonzero(got[name][rest]) == 0, name + " nonzero on images without upstream gradient"
     ref = oracle.layer_bwd(x[sel], z[sel], dout[sel], prm["fwd"], prm["bwd"], axis,
-                           idx=None if idx is None else idx[sel], hw=hw, ln=ln,
+                           idx=None if idx is None else idx[sel], hw=hw, ln=ln, conv=conv,
                            local_window=P.LOCAL_WINDOW if local else 0)
     compare(got, ref, tol, cfg.name, sel=sel)
 
@@ -501,3 +513,46 @@ def test_bwd_local_scan_backward_set_may_be_null():
 
 def test_bwd_local_scan_full_size_2048():
     _sampled_full_size(C.HIRES_2048, P.POOL_COLS, saved=0, local=True)
+
+
+# ------------------------------------------------------------------ producer Conv1D
+# grids whose sequence windows cross grid rows (COLS) or columns (ROWS) at
+# every size, including one- and two-cell axes, and every channel slicing
+CONV_SHAPES = [(2, 5, 7, 8, 3), (2, 13, 9, 72, 6), (1, 7, 33, 136, 12), (2, 16, 16, 384, 12), (1, 3, 2, 200, 5),
+               (1, 1, 1, 8, 1), (1, 2, 40, 1032, 33), (2, 31, 1, 64, 4)]
+
+
+@pytest.mark.parametrize("saved", [None, 0], ids=SAVED_IDS)
+@pytest.mark.parametrize("shape", CONV_SHAPES, ids=["x".join(map(str, s)) for s in CONV_SHAPES])
+@pytest.mark.parametrize("axis", (P.POOL_COLS, P.POOL_ROWS))
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_bwd_conv(io, axis, shape, saved):
+    B, h, w, E, R = shape
+    if (h if axis == P.POOL_COLS else w) > 128:
+        pytest.skip("scan longer than the backward pass supports")
+    rng = np.random.default_rng(zlib.crc32(repr(("bwd-conv", shape, axis, io, saved)).encode()))
+    x, z, dout = (rng.standard_normal((B, h, w, E)).astype(np.float32) for _ in range(3))
+    x, z, dout = _io(io, x, z, dout)
+    prm = {"fwd": rand_dir(rng, E, 16, R, 0.1), "bwd": rand_dir(rng, E, 16, R, 0.1)}
+    conv = rand_conv(rng, E)
+    tol, dt = _tol(io)
+    bwd_check(x, z, dout, prm, axis, tol, dt, "conv %s %s axis %d" % (shape, io, axis), saved=saved, conv=conv)
+
+
+@pytest.mark.parametrize("variant", ["pool_scale", "local", "local_scale"])
+@pytest.mark.parametrize("axis", (P.POOL_COLS, P.POOL_ROWS))
+def test_bwd_conv_options(axis, variant):
+    B, h, w, E, R = 2, 21, 18, 136, 9
+    rng = np.random.default_rng(zlib.crc32(repr(("bwd-conv-opt", axis, variant)).encode()))
+    x, z, dout = (rng.standard_normal((B, h, w, E)).astype(np.float32) for _ in range(3))
+    prm = {"fwd": rand_dir(rng, E, 16, R, 0.1), "bwd": rand_dir(rng, E, 16, R, 0.1)}
+    conv = rand_conv(rng, E)
+    flags = P.FLAG_LOCAL_BWD if "local" in variant else 0
+    scale = 0.25 if "scale" in variant else None
+    bwd_check(x, z, dout, prm, axis, FP32_TOL, torch.float32, "conv %s axis %d" % (variant, axis), conv=conv,
+              flags=flags, pool_scale=scale)
+
+
+@pytest.mark.parametrize("axis", (P.POOL_COLS, P.POOL_ROWS))
+def test_bwd_conv_full_size_2048(axis):
+    _sampled_full_size(C.HIRES_2048, axis, saved=0 if axis == P.POOL_COLS else None, with_conv=True)

@@ -4,9 +4,9 @@ both element types, both paths of a dense pooled layer and the options that
 combine with it (post-SSM LayerNorm, producer Conv1D, LBMamba's local
 backward scan), so that combinations the fixed cases do not list are checked
 too.  Each case compares out, the out of its D = 0 twin, and both scan
-outputs, each on its own scale; cases of pooled layers without the Conv1D
-also run the backward pass (with the LayerNorm and the local scan where the
-case has them), with and without the pooled tokens saved by the forward call.
+outputs, each on its own scale; cases of pooled layers also run the backward
+pass (with the options the case has), with and without the pooled tokens
+saved by the forward call.
 Bar: 1e-4 fp32, 2e-2 bf16 (oracle on the bf16-rounded inputs).
 """
 from __future__ import annotations
@@ -105,8 +105,8 @@ def test_random_layer(seed):
     check(sf, ref["fwd"]["s"], tol, tag + " s_fwd")
     check(sb, ref["bwd"]["s"], tol, tag + " s_bwd")
 
-    # the backward pass covers pooled layers, with every option but the Conv1D
-    if axis in (P.POOL_COLS, P.POOL_ROWS) and not c["conv"] and \
+    # the backward pass covers pooled layers with every option
+    if axis in (P.POOL_COLS, P.POOL_ROWS) and \
             (c["w"] if axis == P.POOL_ROWS else c["h"]) <= 128:
         dout = rng.standard_normal(shape).astype(np.float32)
         if c["io"] == "bf16":
@@ -115,21 +115,25 @@ def test_random_layer(seed):
         idd = None if idx is None else dev(idx, torch.int32)
         lnd = None if ln is None else {"weight": dev(ln["weight"], torch.float32),
                                        "bias": dev(ln["bias"], torch.float32), "eps": ln["eps"]}
+        cvd = None if conv is None else {"weight": dev(conv["weight"]), "bias": dev(conv["bias"])}
         su = None
         if seed % 2:
             T = c["h"] if axis == P.POOL_COLS else c["w"]
             su = torch.full((c["B"], T, c["E"]), float("nan"), device="cuda")
-            P.SSMCall(xd, zd, pd, axis, mask_idx=idd, hw=hw, saved_u=su, ln=lnd).run()
+            P.SSMCall(xd, zd, pd, axis, mask_idx=idd, hw=hw, saved_u=su, ln=lnd, conv=cvd).run()
         bflags = P.FLAG_LOCAL_BWD if c["local"] else 0
-        res = P.BwdCall(xd, zd, dev(dout, dt), pd, axis, mask_idx=idd, hw=hw, saved_u=su, ln=lnd, flags=bflags).run()
+        res = P.BwdCall(xd, zd, dev(dout, dt), pd, axis, mask_idx=idd, hw=hw, saved_u=su, ln=lnd, flags=bflags,
+                        conv=cvd).run()
         torch.cuda.synchronize()
-        rb = oracle.layer_bwd(x, z, dout, prm["fwd"], prm["bwd"], axis, idx=idx, hw=hw, ln=ln, local_window=window)
+        rb = oracle.layer_bwd(x, z, dout, prm["fwd"], prm["bwd"], axis, idx=idx, hw=hw, ln=ln, local_window=window,
+                              conv=conv)
         btag = tag + (" bwd saved-u" if su is not None else " bwd")
         check(host(res["dx"]), rb["dx"], tol, btag + " dx")
         check(host(res["dz"]), rb["dz"], tol, btag + " dz")
         for d in DIRECTIONS:
             for f in FIELDS:
                 check(host(res[d][f]), rb[d][f], tol, "%s d%s.%s" % (btag, d, f))
-        if ln is not None:
-            for f in ("weight", "bias"):
-                check(host(res["ln"][f]), rb["ln"][f], tol, "%s d ln_%s" % (btag, f))
+        for opt in ("ln", "conv"):
+            if opt in rb:
+                for f in ("weight", "bias"):
+                    check(host(res[opt][f]), rb[opt][f], tol, "%s d %s_%s" % (btag, opt, f))
