@@ -406,6 +406,15 @@ def main():
         extras["backward_2048"]["local_scan_cols"] = {"saved_u": {
             "ms": b_ms, "images_per_s": cfg.B / (b_ms * 1e-3), "GBps": bwd_bytes / (b_ms * 1e-3) / 1e9,
             "hbm_frac": bwd_bytes / (b_ms * 1e-3) / 1e9 / HBM_PEAK_GBS}}
+        del bcall
+        # with the producer Conv1D (x is the conv's input; pooled tokens saved by a conv forward call)
+        P.SSMCall(x, z, prm, P.POOL_COLS, workspace=call.workspace, out=call.out, saved_u=su, conv=conv).run(stream)
+        bcall = P.BwdCall(x, z, dout, prm, P.POOL_COLS, saved_u=su, conv=conv)
+        bcall.run(stream)
+        b_ms, _ = time_steps(lambda: bcall.run(stream), n, stream)
+        extras["backward_2048"]["conv_producer_cols"] = {"saved_u": {
+            "ms": b_ms, "images_per_s": cfg.B / (b_ms * 1e-3), "GBps": bwd_bytes / (b_ms * 1e-3) / 1e9,
+            "hbm_frac": bwd_bytes / (b_ms * 1e-3) / 1e9 / HBM_PEAK_GBS}}
         del bcall, su, dout
         log("backward %.3f ms (cols, saved u), with the LayerNorm %.3f ms"
             % (extras["backward_2048"]["cols"]["saved_u"]["ms"], res["saved_u"]["ms"]))
