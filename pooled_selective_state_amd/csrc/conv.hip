@@ -318,8 +318,8 @@ namespace {
 // scan position) items and keep per-lane sums; at the end each workgroup
 // writes one row of partials [dD | d conv_b | d conv_w] (6 E floats, its
 // channel slice), summed over the rows by a later kernel.
-constexpr int kCbThreads = 256;
-constexpr int kCbSlice = 64;  // vector lanes per workgroup channel slice
+constexpr int kCbThreads = 256;  // at most; a workgroup holds G groups of VEs lanes
+constexpr int kCbSlice = 128;    // most vector lanes in a workgroup's channel slice (even slices)
 
 template <class IO, bool COLS>
 __global__ void __launch_bounds__(kCbThreads)
@@ -382,6 +382,7 @@ bwd_conv_epilogue_kernel(const typename IO::elem* __restrict__ x, const typename
 #pragma unroll
                 for (int v = 0; v < V; ++v) dR[k][v] = 0.f;
             }
+#pragma unroll 2
             for (int q = ra - 3; q < rb + 3; ++q) {
 #pragma unroll
                 for (int k = 0; k < 6; ++k) xw[k] = xw[k + 1];
@@ -460,7 +461,7 @@ bwd_conv_epilogue_kernel(const typename IO::elem* __restrict__ x, const typename
     __syncthreads();
     float* prow = parts + (int64_t)blockIdx.x * 6 * E;
     const int col0 = blockIdx.y * VEs * V;
-    for (int o = tid; o < 6 * width; o += kCbThreads) {
+    for (int o = tid; o < 6 * width; o += blockDim.x) {
         const int k = o / width, cc = o - k * width;
         if (col0 + cc >= E) continue;
         float s = red[o];
@@ -476,10 +477,13 @@ hipError_t bwd_conv_epi_t(const Geom& g, const void* x, const void* z, const voi
                           void* dz, hipStream_t st) {
     using elem = typename IO::elem;
     const int VE = (int)(g.E / IO::V);
-    const int VEs = VE < kCbSlice ? VE : kCbSlice;
+    const int nsl = (VE + kCbSlice - 1) / kCbSlice;  // channel slices of equal width
+    const int VEs = (VE + nsl - 1) / nsl;
     int G = kCbThreads / VEs;
     if (G > g.P) G = (int)g.P;
-    const dim3 grid((unsigned)nparts, (unsigned)((VE + VEs - 1) / VEs));
+    if (G < 1) G = 1;
+    const int threads = (VEs * G + 63) / 64 * 64;
+    const dim3 grid((unsigned)nparts, (unsigned)nsl);
     const size_t lds = (size_t)G * 6 * VEs * IO::V * sizeof(float);
     const auto* xe = static_cast<const elem*>(x);
     const auto* ze = static_cast<const elem*>(z);
@@ -487,11 +491,11 @@ hipError_t bwd_conv_epi_t(const Geom& g, const void* x, const void* z, const voi
     auto* dxe = static_cast<elem*>(dx);
     auto* dze = static_cast<elem*>(dz);
     if (g.axis == FASTVIM_POOL_COLS)
-        hipLaunchKernelGGL((bwd_conv_epilogue_kernel<IO, true>), grid, dim3(kCbThreads), lds, st, xe, ze, de, p.conv_w,
+        hipLaunchKernelGGL((bwd_conv_epilogue_kernel<IO, true>), grid, dim3(threads), lds, st, xe, ze, de, p.conv_w,
                            p.conv_b, sf, sb, du, p.fwd.D, p.bwd.D, dxe, dze, parts, (int)g.B, (int)g.T, (int)g.P,
                            (int)g.h, (int)g.w, (int)g.E, VE, VEs, G, pool_norm(g));
     else
-        hipLaunchKernelGGL((bwd_conv_epilogue_kernel<IO, false>), grid, dim3(kCbThreads), lds, st, xe, ze, de,
+        hipLaunchKernelGGL((bwd_conv_epilogue_kernel<IO, false>), grid, dim3(threads), lds, st, xe, ze, de,
                            p.conv_w, p.conv_b, sf, sb, du, p.fwd.D, p.bwd.D, dxe, dze, parts, (int)g.B, (int)g.T,
                            (int)g.P, (int)g.h, (int)g.w, (int)g.E, VE, VEs, G, pool_norm(g));
     return hipGetLastError();
