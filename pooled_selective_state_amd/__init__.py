@@ -11,3 +11,4 @@ from .binding import (  # noqa: F401
     BwdCall, FastVimError, SSMCall, bwd_workspace_bytes, calib_copy, lib, make_dims, ssm_bwd, ssm_fwd,
     workspace_bytes,
 )
+from .autograd import pooled_ssm  # noqa: F401,E402
