@@ -375,6 +375,8 @@ int run_bwd(const Geom& g, const void* x, const void* z, const void* dout, const
         // region (free once the scan adjoint has run; large enough: see
         // bwd_workspace_layout)
         const int64_t np = bwd_conv_parts(g);
+        const int64_t ckpt_floats = 2 * g.B * ws.G * (kBwdTMax / 16) * 256 * 4;
+        if (np * 6 * E > ckpt_floats) return FASTVIM_ERR_WORKSPACE;  // cannot happen with the sizes above
         if (!ok(launch_bwd_conv_epilogue(g, x, z, dout, p, ws.fwd.s_f, ws.fwd.s_b, ws.du, ws.ckpt, dx, dz, s)) ||
             !ok(launch_colsum(ws.ckpt, np, E, 6 * E, gr.fwd.D, gr.bwd.D, ws.tmp, s)) ||
             !ok(launch_colsum(ws.ckpt + E, np, E, 6 * E, gr.conv_b, nullptr, ws.tmp, s)) ||
