@@ -27,7 +27,7 @@ KINDS = ("cols", "rows", "masked_cols", "masked_rows", "unpooled_row", "unpooled
 AXIS = {"cols": P.POOL_COLS, "rows": P.POOL_ROWS, "masked_cols": P.POOL_COLS, "masked_rows": P.POOL_ROWS,
         "unpooled_row": P.POOL_NONE_ROWMAJOR, "unpooled_col": P.POOL_NONE_COLMAJOR}
 FIELDS = ("x_proj_w", "dt_proj_w", "dt_proj_b", "A_log", "D")
-SEEDS = range(160)
+SEEDS = range(400)
 
 
 @pytest.fixture(scope="module", autouse=True)
