@@ -13,7 +13,11 @@ every gradient then comes from those images alone, so the oracle on the
 sample gives every parameter gradient, and the other images' dx and dz must
 be exactly zero.  Cases marked "saved" run the GPU forward first, with
 saved_u, and give the backward those pooled tokens instead of letting it
-pool x again.
+pool x again.  The later sections cover the options: the post-SSM LayerNorm
+(every team shape of its first pass, masked layers and invalid indices),
+LBMamba's local backward scan (T from one partial window to eight whole
+ones), and the producer Conv1D (grids whose windows cross rows and columns),
+each also at full size.
 """
 from __future__ import annotations
 
