@@ -30,8 +30,9 @@ Reported besides images/s:
                 workloads over rotating input sets.
 --profile-run times a few steps and the calibration copy only (for profiler
 runs); --profile-bwd adds three backward calls of the same workload, three
-more given the pooled tokens a forward call saved, and three with the
-post-SSM LayerNorm (pooled tokens saved).
+more given the pooled tokens a forward call saved, and three each with the
+post-SSM LayerNorm, the local backward scan and the producer Conv1D (pooled
+tokens saved).
 """
 from __future__ import annotations
 
@@ -310,8 +311,11 @@ def main():
         g_ln = torch.Generator(device="cuda").manual_seed(1)
         ln = {"weight": 1.0 + 0.1 * torch.randn(cfg.E, device=dev, generator=g_ln),
               "bias": 0.1 * torch.randn(cfg.E, device=dev, generator=g_ln), "eps": 1e-5}
-        for kept, lnk in ((None, None), (su, None), (su, ln)):
-            bcall = P.BwdCall(x, z, dout, prm, P.POOL_COLS, saved_u=kept, ln=lnk)
+        conv = {"weight": 0.5 * torch.randn(cfg.E, P.CONV_TAPS, device=dev, generator=g_ln),
+                "bias": 0.1 * torch.randn(cfg.E, device=dev, generator=g_ln)}
+        for kept, lnk, cv, fl in ((None, None, None, 0), (su, None, None, 0), (su, ln, None, 0),
+                                  (su, None, None, P.FLAG_LOCAL_BWD), (su, None, conv, 0)):
+            bcall = P.BwdCall(x, z, dout, prm, P.POOL_COLS, saved_u=kept, ln=lnk, conv=cv, flags=fl)
             for _ in range(3):
                 bcall.run(stream)
             torch.cuda.synchronize()
