@@ -419,7 +419,18 @@ def main():
         extras["backward_2048"]["conv_producer_cols"] = {"saved_u": {
             "ms": b_ms, "images_per_s": cfg.B / (b_ms * 1e-3), "GBps": bwd_bytes / (b_ms * 1e-3) / 1e9,
             "hbm_frac": bwd_bytes / (b_ms * 1e-3) / 1e9 / HBM_PEAK_GBS}}
-        del bcall, su, dout
+        del bcall
+        # bf16 I/O (x, z, dout, dx, dz in bf16; parameters and arithmetic fp32), pooled tokens saved
+        xb, zb, db = (t.to(torch.bfloat16) for t in (x, z, dout))
+        P.SSMCall(xb, zb, prm, P.POOL_COLS, saved_u=su).run(stream)
+        bcall = P.BwdCall(xb, zb, db, prm, P.POOL_COLS, saved_u=su)
+        bcall.run(stream)
+        b_ms, _ = time_steps(lambda: bcall.run(stream), n, stream)
+        bf_bytes = bwd_bytes // 2
+        extras["backward_2048"]["bf16_cols"] = {"saved_u": {
+            "ms": b_ms, "images_per_s": cfg.B / (b_ms * 1e-3), "alg_bytes": bf_bytes,
+            "GBps": bf_bytes / (b_ms * 1e-3) / 1e9, "hbm_frac": bf_bytes / (b_ms * 1e-3) / 1e9 / HBM_PEAK_GBS}}
+        del bcall, xb, zb, db, su, dout
         log("backward %.3f ms (cols, saved u), with the LayerNorm %.3f ms"
             % (extras["backward_2048"]["cols"]["saved_u"]["ms"], res["saved_u"]["ms"]))
         # torch's device copy, for comparison with the calibration copy
