@@ -17,12 +17,15 @@
  *                      sections "方法详解" (method details, six bullets),
  *                      "术语表" (glossary) and "技术贡献".
  *   [Pith review]      pith.science verdict on 2502.00594, JSON fields
- *                      "key_machinery", "core_discovery", "minor_comments".
+ *                      "key_machinery", "core_discovery", "minor_comments",
+ *                      "referee_report" (major comments: the MAE experiments).
  *   [Vim article]      ijyty.com/news/106204, section 2.1, vim_block sketch.
  *   [SF-Mamba article] glsqs.com/news/422358, section 二 (batch folding with
  *                      periodic state reset).
+ *   [LBMamba article]  pswp.cn page on LBMamba, 论文创新点 1-2 (the local
+ *                      backward scan inside the forward scan).
  *
- * Readings of points the pages leave open (each is listed in the design doc):
+ * Readings of points the pages leave open:
  *   - x_proj output is split [delta_lowrank (R) | B (N) | C (N)];
  *   - s_delta(x) is the low-rank map W_dt * delta_lowrank plus a bias;
  *   - A = -exp(A_log) (negative real, so the recurrence is stable);
@@ -33,7 +36,15 @@
  *   - optionally a post-SSM LayerNorm over the channels of each token sits
  *     between the skip and the gate (population variance, eps inside the
  *     root, per-channel scale and shift);
- *   - initial state is zero; no state is output.
+ *   - initial state is zero; no state is output;
+ *   - the producer Conv1D is depthwise, causal, with its taps along the
+ *     oriented grid's sequence and SiLU after it; the layer's x is its output;
+ *   - the local backward scan runs on the forward direction's inputs, its
+ *     state reset at the top of every window of L steps aligned at t = 0;
+ *   - the MAE recipe's pooling factor multiplies the pooled tokens only.
+ * The backward pass is the chain rule through these definitions, one adjoint
+ * per forward step; it is pinned by central differences of the forward
+ * functions, not by a second derivation.
  *
  * Layouts (all row-major, last index fastest):
  *   dense x, z, out   (B, h, w, E)            masked x, z, out   (B, K, E)
