@@ -35,6 +35,30 @@ def rel_inf(got, ref):
     return float(np.max(np.abs(got - ref)) / max(scale, 1e-30))
 
 
+class MaxErr:
+    """rel_inf accumulated over pieces of a tensor (images compared in groups):
+    max |gpu - oracle| and max |oracle| per named tensor, so the error checked
+    at the end is that of the whole tensor."""
+
+    def __init__(self):
+        self.num, self.den = {}, {}
+
+    def add(self, what, got, ref):
+        got = np.asarray(got, np.float64)
+        ref = np.asarray(ref, np.float64)
+        assert got.shape == ref.shape, (what, got.shape, ref.shape)
+        assert np.all(np.isfinite(got)), "non-finite GPU output in " + what
+        if ref.size:
+            self.num[what] = max(self.num.get(what, 0.0), float(np.max(np.abs(got - ref))))
+            self.den[what] = max(self.den.get(what, 0.0), float(np.max(np.abs(ref))))
+
+    def check(self, tol):
+        for what in self.num:
+            err = self.num[what] / max(self.den[what], 1e-30)
+            print("  %-28s rel_inf=%.3e (tol %.0e)" % (what, err, tol), flush=True)
+            assert err <= tol, "%s: rel_inf %.3e > %.1e" % (what, err, tol)
+
+
 def check(got, ref, tol, what):
     err = rel_inf(got, ref)
     print("  %-28s rel_inf=%.3e (tol %.0e)" % (what, err, tol), flush=True)

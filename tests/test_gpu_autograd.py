@@ -14,9 +14,9 @@ import torch
 
 import oracle
 import pooled_selective_state_amd as P
-from gpu_util import BF16_TOL, FP32_TOL, check, dev, host
+from gpu_util import BF16_TOL, FP32_TOL, check, compare_stages, dev, gpu_call, host, stage_exports
 from pins import rand_conv, rand_dir, rand_ln
-from pooled_selective_state_amd.inputs import DIRECTIONS, random_mask, round_to_bf16
+from pooled_selective_state_amd.inputs import DIRECTIONS, random_mask, round_to_bf16, zero_D
 
 pytestmark = pytest.mark.gpu
 FIELDS = ("x_proj_w", "dt_proj_w", "dt_proj_b", "A_log", "D")
@@ -109,6 +109,22 @@ def test_autograd_two_block_chain():
     # block 2's oracle input is the GPU block 1's output rounded to fp32 as the GPU passes it on
     o1_gpu = host(out1).astype(np.float32)
     check(o1_gpu, o1, FP32_TOL, "chain block 1 out")
+    # each block's forward on its own input, where out alone could hide the
+    # scan under the skip term: the same call through the C ABI gives the
+    # autograd forward's out bit for bit, its stage exports (pooled tokens,
+    # both x_proj directions, s_fwd, s_bwd) and its D = 0 twin match the oracle
+    for tag, xin, zin, prm, axis, got in (("chain block 1", x, z1, p1, P.POOL_COLS, out1),
+                                          ("chain block 2", o1_gpu, z2, p2, P.POOL_ROWS, out2)):
+        call = gpu_call(xin, zin, prm, axis)
+        same = call.run()
+        torch.cuda.synchronize()
+        assert torch.equal(same, got.detach()), tag + ": C ABI call differs from the autograd forward"
+        ref = oracle.layer(xin, zin, prm["fwd"], prm["bwd"], axis, stages=True)
+        compare_stages(stage_exports(call), ref, FP32_TOL, tag)
+        twin = gpu_call(xin, zin, zero_D(prm), axis).run()
+        torch.cuda.synchronize()
+        check(host(twin), oracle.layer(xin, zin, zero_D(prm)["fwd"], zero_D(prm)["bwd"], axis), FP32_TOL,
+              tag + " out(D=0)")
     r2 = oracle.layer_bwd(o1_gpu, z2, dout, p2["fwd"], p2["bwd"], P.POOL_ROWS)
     r1 = oracle.layer_bwd(x, z1, r2["dx"].astype(np.float32), p1["fwd"], p1["bwd"], P.POOL_COLS)
     check(host(z2d.grad), r2["dz"], FP32_TOL, "chain dz2")
