@@ -37,7 +37,10 @@
  * Conventions for every entry point:
  *   - device pointers (x, z, out, mask_idx, parameters, workspace) are HIP
  *     device memory owned by the caller; the library keeps no pointer after a
- *     call returns and allocates nothing;
+ *     call returns and holds no memory between calls.  A layer call given a
+ *     NULL workspace takes its scratch from the stream-ordered allocator
+ *     instead (hipMallocAsync before its kernels, hipFreeAsync after them,
+ *     both on the call's stream);
  *   - stream is a hipStream_t passed as void* (NULL = the legacy default
  *     stream); work is only enqueued on it, nothing synchronises the host;
  *   - the return value is FASTVIM_OK (0) or a negative fastvim_status; on an
@@ -55,7 +58,7 @@
 extern "C" {
 #endif
 
-#define FASTVIM_ABI_VERSION 10
+#define FASTVIM_ABI_VERSION 11
 
 typedef enum fastvim_status {
     FASTVIM_OK = 0,
@@ -65,9 +68,14 @@ typedef enum fastvim_status {
                                      an image of 2^31 elements or more) */
     FASTVIM_ERR_ALIGN = -4,       /* x, z, out, x_proj_w not 16-byte aligned; workspace not 256-byte; others not 4-byte */
     FASTVIM_ERR_OVERLAP = -5,     /* out overlaps x or z, or the workspace overlaps an input or output */
-    FASTVIM_ERR_WORKSPACE = -6,   /* workspace NULL or smaller than fastvim_ssm_workspace_bytes */
-    FASTVIM_ERR_HIP = -7,         /* a HIP launch or copy reported an error */
-    FASTVIM_ERR_ARG = -8          /* bad enum value, stage id or export id, or mask_idx given with K = 0 */
+    FASTVIM_ERR_WORKSPACE = -6,   /* workspace smaller than fastvim_ssm_workspace_bytes, or NULL where a
+                                     call needs the caller's (stages, exports, device errors) */
+    FASTVIM_ERR_HIP = -7,         /* a HIP launch, copy or stream-ordered allocation reported an error */
+    FASTVIM_ERR_ARG = -8,         /* bad enum value, stage id or export id, or mask_idx given with K = 0 */
+    /* reported by fastvim_get_device_error only, for the last call that ran
+     * its kernels with the workspace: */
+    FASTVIM_ERR_BAD_INDEX = -9,   /* FASTVIM_FLAG_CHECK_IDX found an invalid mask index */
+    FASTVIM_ERR_DEVICE_WAIT = -10 /* a wait inside the single launch gave up; its outputs are invalid */
 } fastvim_status;
 
 /* Element type of x, z and out.  Parameters are always fp32; all arithmetic
@@ -111,10 +119,12 @@ typedef struct fastvim_dir_params {
 typedef struct fastvim_params {
     fastvim_dir_params fwd; /* forward scan (t ascending) */
     fastvim_dir_params bwd; /* backward scan (t descending) */
-    void *workspace;        /* device scratch, >= fastvim_ssm_workspace_bytes, 256-byte aligned */
+    void *workspace;        /* device scratch, >= fastvim_ssm_workspace_bytes, 256-byte aligned, or NULL
+                               (fastvim_ssm_fwd, fastvim_ssm_fwd_stages and fastvim_ssm_bwd then allocate
+                               and free it on the call's stream) */
     size_t workspace_bytes;
     uint32_t flags;         /* FASTVIM_FLAG_* bits, else 0 */
-    uint32_t reserved;
+    uint32_t tuning;        /* 0, or FASTVIM_TUNING_* fields (measurement and tests) */
     /* Post-SSM LayerNorm, used with FASTVIM_FLAG_POST_NORM only: per-channel
      * scale and shift (E) fp32, 16-byte aligned, and eps > 0. */
     const float *ln_weight;
@@ -150,11 +160,22 @@ typedef struct fastvim_params {
  * whatever its size.  Both paths give the same results within rounding.
  * Setting both bits is FASTVIM_ERR_ARG.  The single launch pipelines images:
  * an image's scans start LS images after its pooling and its outputs LE
- * images after; both follow the image size, and the environment variables
- * FASTVIM_FUSED_LS and FASTVIM_FUSED_LE (read at each call) override them,
- * for measurement. */
+ * images after; both follow the image size (LE = 180 MB / bytes of x per
+ * image, LS = max(3, LE / 4)), and params.tuning overrides them. */
 #define FASTVIM_FLAG_STAGED 1u
 #define FASTVIM_FLAG_FUSED 2u
+
+/* params.tuning: measurement and test settings of the single launch, 0 for
+ * the defaults.  Bits 0-7: LS (0 = automatic), bits 8-15: LE (0 =
+ * automatic; raised to LS if smaller).  FASTVIM_TUNING_POLL1 makes every
+ * wait inside the single launch give up after one poll, so that tests can
+ * exercise the give-up path (the kernel then finishes with invalid outputs,
+ * NaN in every output block that follows a failed wait, and
+ * fastvim_get_device_error reports FASTVIM_ERR_DEVICE_WAIT).  Other bits:
+ * FASTVIM_ERR_ARG. */
+#define FASTVIM_TUNING_LS(n) ((uint32_t)(n) & 0xffu)
+#define FASTVIM_TUNING_LE(n) (((uint32_t)(n) & 0xffu) << 8)
+#define FASTVIM_TUNING_POLL1 (1u << 16)
 
 /* FASTVIM_FLAG_POST_NORM adds the post-SSM LayerNorm between the skip and the
  * gate (FastVim summary page, section 方法详解, bullet 5: LayerNorm after the
@@ -221,10 +242,19 @@ typedef struct fastvim_params {
  * finite. */
 #define FASTVIM_FLAG_POOL_SCALE 32u
 
+/* FASTVIM_FLAG_CHECK_IDX (masked layers) records, on the device, whether any
+ * mask index was invalid (outside [0, h*w), or repeated within its image);
+ * fastvim_get_device_error then reports FASTVIM_ERR_BAD_INDEX.  The check
+ * itself always runs (an invalid index is never dereferenced, its tokens get
+ * NaN, see fastvim_ssm_fwd); the flag adds the error report.  Forward and
+ * backward calls; ignored for dense layers. */
+#define FASTVIM_FLAG_CHECK_IDX 64u
+
 /* Bytes of workspace a call with these sizes needs (0 if the sizes are
  * invalid).  Dense pooled layers need 4 * B * T * (3E + 2(R + 2N)) bytes plus
  * 4 * (2 + 2B) bytes of counters and alignment; unpooled layers hold the per-token projections and scan outputs
- * (at B = 128, h = w = 128, E = 384 about 7.2 GB). */
+ * (at B = 128, h = w = 128, E = 384 about 7.2 GB).  The workspace begins
+ * with the call's status word (see fastvim_get_device_error). */
 size_t fastvim_ssm_workspace_bytes(const fastvim_dims *dims, int pool_axis);
 
 /* The layer.  x, z, out: (B, h, w, E) dense or (B, K, E) masked, contiguous,
@@ -236,6 +266,31 @@ size_t fastvim_ssm_workspace_bytes(const fastvim_dims *dims, int pool_axis);
  * were absent.  Enqueues its kernels on stream and returns. */
 int fastvim_ssm_fwd(const void *x, const void *z, const fastvim_params *params, const fastvim_dims *dims,
                     int pool_axis, const int32_t *mask_idx, void *out, void *stream);
+
+/* The layer, as fastvim_ssm_fwd, also copying its intermediate results into
+ * caller buffers in the same call (for stage-by-stage checks; works with a
+ * NULL workspace too, the copies are enqueued before it is freed).  Each
+ * destination is device memory, 4-byte aligned, or NULL to skip it:
+ *   u_out        (B, T, E) fp32 pooled tokens (pooled layers only, else FASTVIM_ERR_ARG)
+ *   s_f_out      (B, T, E) fp32 forward scan output
+ *   s_b_out      (B, T, E) fp32 backward scan output
+ *   row_of_token (B, K) int32 scan row (COLS) or column (ROWS) of each kept token,
+ *                -1 for an invalid index (masked layers only, else FASTVIM_ERR_ARG)
+ * A destination must not overlap x, z, out, the workspace or another
+ * destination (FASTVIM_ERR_OVERLAP). */
+int fastvim_ssm_fwd_stages(const void *x, const void *z, const fastvim_params *params, const fastvim_dims *dims,
+                           int pool_axis, const int32_t *mask_idx, void *out, void *stream, float *u_out,
+                           float *s_f_out, float *s_b_out, int32_t *row_of_token);
+
+/* Errors found on the device by the last call that ran its kernels with
+ * params->workspace (forward or backward): FASTVIM_ERR_DEVICE_WAIT if a wait
+ * inside the single launch gave up (its outputs are then invalid; a broken
+ * invariant, never expected), else FASTVIM_ERR_BAD_INDEX if that call had
+ * FASTVIM_FLAG_CHECK_IDX and found an invalid mask index, else FASTVIM_OK.
+ * Reads the status word at the start of the workspace: synchronises stream
+ * (waits for the work enqueued on it).  FASTVIM_ERR_WORKSPACE for a NULL
+ * workspace (a call that allocated its own keeps no status). */
+int fastvim_get_device_error(const fastvim_params *params, void *stream);
 
 /* The layer's stages, for timing and inspection.  fastvim_ssm_fwd runs
  * ROWS (masked only), POOL (pooled only), PROJ, SCAN and EPILOGUE in that

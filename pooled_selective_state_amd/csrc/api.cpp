@@ -58,7 +58,12 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) &
 
 bool overlap(const void* a, size_t na, const void* b, size_t nb) {
     const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
-    return na && nb && pa < pb + nb && pb < pa + na;
+    return a && b && na && nb && pa < pb + nb && pb < pa + na;
+}
+
+// Bytes of x (and of z, out, dout, dx, dz) of a call.
+size_t io_span(const Geom& g) {
+    return (size_t)(g.B * (g.masked ? g.K : g.h * g.w) * g.E) * (g.io == FASTVIM_F32 ? 4 : 2);
 }
 
 // x_proj_w is read with 16-byte vector loads, the others with scalar loads.
@@ -93,16 +98,25 @@ int apply_pool_scale(const fastvim_params& p, Geom* g) {
     return FASTVIM_OK;
 }
 
-// Full validation of a layer call.  *empty is set for B == 0.
-int validate(const void* x, const void* z, const fastvim_params* prm, const fastvim_dims* d, int axis,
-             const int32_t* idx, const void* out, Geom* g, Workspace* ws, bool* empty) {
-    if (!prm) return FASTVIM_ERR_NULL;
+// Flags and tuning word of a call.
+int check_flags(const fastvim_params& p) {
     const uint32_t paths = FASTVIM_FLAG_STAGED | FASTVIM_FLAG_FUSED;
-    const uint32_t options =
-        FASTVIM_FLAG_POST_NORM | FASTVIM_FLAG_CONV | FASTVIM_FLAG_LOCAL_BWD | FASTVIM_FLAG_POOL_SCALE;
-    if ((prm->flags & ~(paths | options)) || (prm->flags & paths) == paths) return FASTVIM_ERR_ARG;
-    int st = resolve_geom(d, axis, g);
+    const uint32_t options = FASTVIM_FLAG_POST_NORM | FASTVIM_FLAG_CONV | FASTVIM_FLAG_LOCAL_BWD |
+                             FASTVIM_FLAG_POOL_SCALE | FASTVIM_FLAG_CHECK_IDX;
+    if ((p.flags & ~(paths | options)) || (p.flags & paths) == paths) return FASTVIM_ERR_ARG;
+    if (p.tuning & ~(FASTVIM_TUNING_LS(0xff) | FASTVIM_TUNING_LE(0xff) | FASTVIM_TUNING_POLL1)) return FASTVIM_ERR_ARG;
+    return FASTVIM_OK;
+}
+
+// Validation of a layer call's arguments other than the workspace.  *empty is
+// set for B == 0.
+int validate(const void* x, const void* z, const fastvim_params* prm, const fastvim_dims* d, int axis,
+             const int32_t* idx, const void* out, Geom* g, bool* empty) {
+    if (!prm) return FASTVIM_ERR_NULL;
+    int st = check_flags(*prm);
     if (st) return st;
+    if ((st = resolve_geom(d, axis, g))) return st;
+    g->tuning = prm->tuning;
     if ((st = apply_pool_scale(*prm, g))) return st;
     if ((prm->flags & FASTVIM_FLAG_CONV) &&
         (!g->pooled || g->masked || (prm->flags & FASTVIM_FLAG_POST_NORM)))
@@ -123,37 +137,70 @@ int validate(const void* x, const void* z, const fastvim_params* prm, const fast
         if (!prm->conv_w || !prm->conv_b) return FASTVIM_ERR_NULL;
         if (!aligned(prm->conv_w, 16) || !aligned(prm->conv_b, 4)) return FASTVIM_ERR_ALIGN;
     }
-    if (!prm->workspace) return FASTVIM_ERR_WORKSPACE;
-    if (!aligned(x, 16) || !aligned(z, 16) || !aligned(out, 16) || !aligned(prm->workspace, 256) ||
-        (idx && !aligned(idx, 4)))
+    if (!aligned(x, 16) || !aligned(z, 16) || !aligned(out, 16) || (idx && !aligned(idx, 4)))
         return FASTVIM_ERR_ALIGN;
-    const size_t need = workspace_layout(*g, nullptr, nullptr);
-    if (prm->workspace_bytes < need) return FASTVIM_ERR_WORKSPACE;
-    const size_t io_bytes =
-        (size_t)(g->B * (g->masked ? g->K : g->h * g->w) * g->E) * (g->io == FASTVIM_F32 ? 4 : 2);
+    const size_t io_bytes = io_span(*g);
     if (overlap(out, io_bytes, x, io_bytes) || overlap(out, io_bytes, z, io_bytes)) return FASTVIM_ERR_OVERLAP;
-    const void* w = prm->workspace;
-    if (overlap(w, need, x, io_bytes) || overlap(w, need, z, io_bytes) || overlap(w, need, out, io_bytes))
-        return FASTVIM_ERR_OVERLAP;
     if (prm->saved_u) {
         const void* su = prm->saved_u;
         const size_t ub = (size_t)(g->B * g->T * g->E) * sizeof(float);
         if (!aligned(su, 16)) return FASTVIM_ERR_ALIGN;
-        if (overlap(su, ub, x, io_bytes) || overlap(su, ub, z, io_bytes) || overlap(su, ub, out, io_bytes) ||
-            overlap(su, ub, w, need))
+        if (overlap(su, ub, x, io_bytes) || overlap(su, ub, z, io_bytes) || overlap(su, ub, out, io_bytes))
             return FASTVIM_ERR_OVERLAP;
     }
-    workspace_layout(*g, prm->workspace, ws);
-    if (prm->saved_u) ws->u = prm->saved_u;
     return FASTVIM_OK;
 }
+
+// The caller's workspace of a validated layer call: present, aligned, large
+// enough and clear of x, z, out and saved_u.  Lays it out into *ws.
+int bind_workspace(const Geom& g, const void* x, const void* z, const fastvim_params& prm, const void* out,
+                   Workspace* ws) {
+    if (!prm.workspace) return FASTVIM_ERR_WORKSPACE;
+    if (!aligned(prm.workspace, 256)) return FASTVIM_ERR_ALIGN;
+    const size_t need = workspace_layout(g, nullptr, nullptr);
+    if (prm.workspace_bytes < need) return FASTVIM_ERR_WORKSPACE;
+    const size_t io_bytes = io_span(g);
+    const void* w = prm.workspace;
+    if (overlap(w, need, x, io_bytes) || overlap(w, need, z, io_bytes) || overlap(w, need, out, io_bytes) ||
+        overlap(w, need, prm.saved_u, prm.saved_u ? (size_t)(g.B * g.T * g.E) * sizeof(float) : 0))
+        return FASTVIM_ERR_OVERLAP;
+    workspace_layout(g, prm.workspace, ws);
+    if (prm.saved_u) ws->u = prm.saved_u;
+    return FASTVIM_OK;
+}
+
+// Scratch of a call made with a NULL workspace, from the stream-ordered
+// allocator: taken on the call's stream before its kernels are enqueued and
+// given back on it after them, so it is never held between calls.
+struct StreamScratch {
+    void* raw = nullptr;
+    hipStream_t s = nullptr;
+    // bytes, 256-byte aligned, into *base
+    int take(size_t bytes, hipStream_t st, void** base) {
+        s = st;
+        if (hipMallocAsync(&raw, bytes + 256, st) != hipSuccess) {
+            raw = nullptr;
+            (void)hipGetLastError();
+            return FASTVIM_ERR_HIP;
+        }
+        *base = reinterpret_cast<void*>((reinterpret_cast<uintptr_t>(raw) + 255) & ~uintptr_t(255));
+        return FASTVIM_OK;
+    }
+    // Enqueues the free; folds a failure into st.
+    int give_back(int st) {
+        if (raw && hipFreeAsync(raw, s) != hipSuccess && st == FASTVIM_OK) st = FASTVIM_ERR_HIP;
+        raw = nullptr;
+        return st;
+    }
+};
 
 int run_stage(int stage, const Geom& g, const void* x, const void* z, const fastvim_params& p,
               const int32_t* idx, void* out, const Workspace& ws, hipStream_t st) {
     hipError_t e = hipSuccess;
     switch (stage) {
         case FASTVIM_STAGE_ROWS:
-            if (g.masked) e = launch_mask_rows(g, idx, ws, st);
+            if (g.masked)
+                e = launch_mask_rows(g, idx, ws, (p.flags & FASTVIM_FLAG_CHECK_IDX) ? ws.sync + 1 : nullptr, st);
             break;
         case FASTVIM_STAGE_POOL:
             if (g.pooled)
@@ -194,14 +241,18 @@ struct Span {
 };
 
 // Full validation of a backward call.  *empty is set for B == 0.
+// Full validation of a backward call.  *empty is set for B == 0.  A NULL
+// workspace passes (the call then takes its own stream-ordered scratch);
+// a caller's workspace is checked for alignment, size and overlap.
 int validate_bwd(const void* x, const void* z, const void* dout, const fastvim_params* prm, const fastvim_dims* d,
                  int axis, const int32_t* idx, const void* dx, const void* dz, const fastvim_grads* gr, Geom* g,
-                 BwdWorkspace* ws, bool* empty) {
+                 bool* empty) {
     if (!prm) return FASTVIM_ERR_NULL;
     const uint32_t unsupported = FASTVIM_FLAG_FUSED;
     const uint32_t options = FASTVIM_FLAG_STAGED | FASTVIM_FLAG_POST_NORM | FASTVIM_FLAG_POOL_SCALE |
-                             FASTVIM_FLAG_LOCAL_BWD | FASTVIM_FLAG_CONV;
+                             FASTVIM_FLAG_LOCAL_BWD | FASTVIM_FLAG_CONV | FASTVIM_FLAG_CHECK_IDX;
     if (prm->flags & ~(options | unsupported)) return FASTVIM_ERR_ARG;
+    if (prm->tuning) return FASTVIM_ERR_ARG;  // the backward pass has no single launch to tune
     if (prm->flags & unsupported) return FASTVIM_ERR_UNSUPPORTED;
     const bool norm = (prm->flags & FASTVIM_FLAG_POST_NORM) != 0;
     const bool conv = (prm->flags & FASTVIM_FLAG_CONV) != 0;
@@ -253,13 +304,15 @@ int validate_bwd(const void* x, const void* z, const void* dout, const fastvim_p
     if (!x || !z || !dout || !dx || !dz || (g->masked && !idx)) return FASTVIM_ERR_NULL;
     const fastvim_params eff = effective_params(*prm);
     if ((st = check_dir(eff.fwd)) || (st = check_dir(eff.bwd))) return st;
-    if (!prm->workspace) return FASTVIM_ERR_WORKSPACE;
     if (!aligned(x, 16) || !aligned(z, 16) || !aligned(dout, 16) || !aligned(dx, 16) || !aligned(dz, 16) ||
-        !aligned(prm->workspace, 256) || (idx && !aligned(idx, 4)))
+        (idx && !aligned(idx, 4)))
         return FASTVIM_ERR_ALIGN;
     const size_t need = bwd_workspace_layout(*g, nullptr, nullptr);
-    if (prm->workspace_bytes < need) return FASTVIM_ERR_WORKSPACE;
-    const size_t io = (size_t)(g->B * (g->masked ? g->K : g->h * g->w) * g->E) * (g->io == FASTVIM_F32 ? 4 : 2);
+    if (prm->workspace) {
+        if (!aligned(prm->workspace, 256)) return FASTVIM_ERR_ALIGN;
+        if (prm->workspace_bytes < need) return FASTVIM_ERR_WORKSPACE;
+    }
+    const size_t io = io_span(*g);
     // outputs (dx, dz, the workspace and every gradient) overlap neither each
     // other nor an input; parameters count as inputs
     Span ins[16] = {{x, io}, {z, io}, {dout, io}};
@@ -286,12 +339,16 @@ int validate_bwd(const void* x, const void* z, const void* dout, const fastvim_p
         for (int j = i + 1; j < nout; ++j)
             if (overlap(outs[i].p, outs[i].n, outs[j].p, outs[j].n)) return FASTVIM_ERR_OVERLAP;
     }
-    bwd_workspace_layout(*g, prm->workspace, ws);
-    if (prm->saved_u) {
-        ws->fwd.u = prm->saved_u;
+    return FASTVIM_OK;
+}
+
+// Lays out a backward workspace at base (the caller's or the call's own).
+void bind_bwd_workspace(const Geom& g, const fastvim_params& prm, void* base, BwdWorkspace* ws) {
+    bwd_workspace_layout(g, base, ws);
+    if (prm.saved_u) {
+        ws->fwd.u = prm.saved_u;
         ws->u_saved = true;
     }
-    return FASTVIM_OK;
 }
 
 int run_bwd(const Geom& g, const void* x, const void* z, const void* dout, const fastvim_params& p,
@@ -304,7 +361,10 @@ int run_bwd(const Geom& g, const void* x, const void* z, const void* dout, const
     const bool norm = (p.flags & FASTVIM_FLAG_POST_NORM) != 0;
     const bool local = (p.flags & FASTVIM_FLAG_LOCAL_BWD) != 0;  // p holds the effective parameters
     const bool conv = (p.flags & FASTVIM_FLAG_CONV) != 0;
-    if (g.masked && !ok(launch_mask_rows(g, idx, ws.fwd, s))) return FASTVIM_ERR_HIP;
+    if (!ok(launch_zero_sync(ws.fwd, kBwdStatusWords, s))) return FASTVIM_ERR_HIP;
+    if (g.masked &&
+        !ok(launch_mask_rows(g, idx, ws.fwd, (p.flags & FASTVIM_FLAG_CHECK_IDX) ? ws.fwd.sync + 1 : nullptr, s)))
+        return FASTVIM_ERR_HIP;
     if (norm) {
         // the norm's adjoint needs y, hence both scans' outputs: recompute the
         // forward stages first, then the first pass with the norm, whose
@@ -389,6 +449,93 @@ int run_bwd(const Geom& g, const void* x, const void* z, const void* dout, const
     return FASTVIM_OK;
 }
 
+// Destinations of fastvim_ssm_fwd_stages (each NULL to skip).
+struct StageDst {
+    float* u;
+    float* s_f;
+    float* s_b;
+    int32_t* rows;
+};
+
+// The stage destinations of a validated call: present only where the layer
+// has them, 4-byte aligned, clear of x, z, out, saved_u and each other.
+int check_stage_dst(const Geom& g, const StageDst& d, const void* x, const void* z, const void* out,
+                    const fastvim_params& prm) {
+    if ((d.u && !g.pooled) || (d.rows && !g.masked)) return FASTVIM_ERR_ARG;
+    const size_t bte = (size_t)(g.B * g.T * g.E) * sizeof(float);
+    const Span dsts[4] = {{d.u, bte}, {d.s_f, bte}, {d.s_b, bte}, {d.rows, (size_t)(g.B * g.K) * sizeof(int32_t)}};
+    const size_t io = io_span(g);
+    const Span others[4] = {{x, io}, {z, io}, {out, io}, {prm.saved_u, prm.saved_u ? bte : 0}};
+    for (int i = 0; i < 4; ++i) {
+        if (dsts[i].p && !aligned(dsts[i].p, 4)) return FASTVIM_ERR_ALIGN;
+        for (const Span& o : others)
+            if (overlap(dsts[i].p, dsts[i].n, o.p, o.n)) return FASTVIM_ERR_OVERLAP;
+        for (int j = i + 1; j < 4; ++j)
+            if (overlap(dsts[i].p, dsts[i].n, dsts[j].p, dsts[j].n)) return FASTVIM_ERR_OVERLAP;
+        if (prm.workspace && overlap(dsts[i].p, dsts[i].n, prm.workspace, workspace_layout(g, nullptr, nullptr)))
+            return FASTVIM_ERR_OVERLAP;
+    }
+    return FASTVIM_OK;
+}
+
+// The layer on a bound workspace: counters cleared, then the single launch or
+// the stage kernels.
+int run_fwd(const Geom& g, const void* x, const void* z, const fastvim_params& prm, const int32_t* idx, void* out,
+            const Workspace& ws, hipStream_t s) {
+    if (launch_zero_sync(ws, sync_words(g), s) != hipSuccess) return FASTVIM_ERR_HIP;
+    const fastvim_params q = effective_params(prm);
+    const bool norm = (prm.flags & FASTVIM_FLAG_POST_NORM) != 0;
+    const bool local = (prm.flags & FASTVIM_FLAG_LOCAL_BWD) != 0;
+    const bool single = !(prm.flags & FASTVIM_FLAG_CONV) &&
+                        ((prm.flags & FASTVIM_FLAG_FUSED)
+                             ? fused_supported(g, norm, local)
+                             : !(prm.flags & FASTVIM_FLAG_STAGED) && fused_preferred(g, norm, local));
+    if (single) return launch_fused(g, x, z, q, ws, out, s) == hipSuccess ? FASTVIM_OK : FASTVIM_ERR_HIP;
+    for (int stage = FASTVIM_STAGE_ROWS; stage <= FASTVIM_STAGE_EPILOGUE; ++stage) {
+        const int st = run_stage(stage, g, x, z, q, idx, out, ws, s);
+        if (st) return st;
+    }
+    return FASTVIM_OK;
+}
+
+// fastvim_ssm_fwd and fastvim_ssm_fwd_stages (dst != NULL): validate, bind or
+// take the workspace, run, copy the stages out, give the scratch back.
+int fwd_entry(const void* x, const void* z, const fastvim_params* params, const fastvim_dims* dims, int axis,
+              const int32_t* idx, void* out, hipStream_t s, const StageDst* dst) {
+    Geom g;
+    bool empty = false;
+    int st = validate(x, z, params, dims, axis, idx, out, &g, &empty);
+    if (st) return st;
+    if (dst && (st = check_stage_dst(g, *dst, x, z, out, *params))) return st;
+    if (empty) return FASTVIM_OK;
+    Workspace ws;
+    StreamScratch scratch;
+    if (params->workspace) {
+        if ((st = bind_workspace(g, x, z, *params, out, &ws))) return st;
+    } else {
+        void* base = nullptr;
+        if ((st = scratch.take(workspace_layout(g, nullptr, nullptr), s, &base))) return st;
+        workspace_layout(g, base, &ws);
+        if (params->saved_u) ws.u = params->saved_u;
+    }
+    st = run_fwd(g, x, z, *params, idx, out, ws, s);
+    if (st == FASTVIM_OK && dst) {
+        const size_t bte = (size_t)(g.B * g.T * g.E) * sizeof(float);
+        const struct {
+            void* to;
+            const void* from;
+            size_t n;
+        } copies[4] = {{dst->u, ws.u, bte}, {dst->s_f, ws.s_f, bte}, {dst->s_b, ws.s_b, bte},
+                       {dst->rows, ws.rows, (size_t)(g.B * g.K) * sizeof(int32_t)}};
+        for (const auto& c : copies)
+            if (c.to && hipMemcpyAsync(c.to, c.from, c.n, hipMemcpyDeviceToDevice, s) != hipSuccess) {
+                st = FASTVIM_ERR_HIP;
+                break;
+            }
+    }
+    return scratch.give_back(st);
+}
+
 }  // namespace
 
 size_t workspace_layout(const Geom& g, void* base, Workspace* ws) {
@@ -399,13 +546,13 @@ size_t workspace_layout(const Geom& g, void* base, Workspace* ws) {
         return o;
     };
     const size_t bte = (size_t)(g.B * g.T * g.E) * sizeof(float);
+    const size_t o_sync = take((size_t)sync_words(g) * sizeof(unsigned));  // first: the status word at byte 4
     const size_t o_u = g.pooled ? take(bte) : 0;
     const size_t o_x = take((size_t)(g.B * g.T * 2 * g.NX) * sizeof(float));
     const size_t o_sf = take(bte);
     const size_t o_sb = take(bte);
     const size_t o_rows = g.masked ? take((size_t)(g.B * g.K) * sizeof(int32_t)) : 0;
     const size_t o_bad = g.masked ? take((size_t)g.B * sizeof(int32_t)) : 0;
-    const size_t o_sync = take((size_t)sync_words(g) * sizeof(unsigned));
     if (base && ws) {
         char* c = static_cast<char*>(base);
         ws->u = g.pooled ? reinterpret_cast<float*>(c + o_u) : nullptr;
@@ -430,6 +577,7 @@ size_t bwd_workspace_layout(const Geom& g, void* base, BwdWorkspace* ws) {
     const int64_t G = (E + kBwdCh - 1) / kBwdCh, S = bwd_rmax(R) + 32;
     const int64_t MC = (M + kBwdTokChunk - 1) / kBwdTokChunk;
     const size_t bte = (size_t)(M * E) * sizeof(float);
+    const size_t o_hdr = take(kBwdStatusWords * sizeof(unsigned));  // first: the status word at byte 4
     const size_t o_u = take(bte);
     const size_t o_x = take((size_t)(M * 2 * NX) * sizeof(float));
     const size_t o_sf = take(bte), o_sb = take(bte);
@@ -466,7 +614,7 @@ size_t bwd_workspace_layout(const Geom& g, void* base, BwdWorkspace* ws) {
         ws->fwd.s_b = f(o_sb);
         ws->fwd.rows = g.masked ? reinterpret_cast<int32_t*>(c + o_rows) : nullptr;
         ws->fwd.bad = g.masked ? reinterpret_cast<int32_t*>(c + o_bad) : nullptr;
-        ws->fwd.sync = nullptr;
+        ws->fwd.sync = reinterpret_cast<unsigned*>(c + o_hdr);
         ws->gs = f(o_gs);
         ws->dDp = f(o_dDp);
         ws->du_f = f(o_duf);
@@ -503,26 +651,14 @@ size_t fastvim_ssm_workspace_bytes(const fastvim_dims* dims, int pool_axis) {
 
 int fastvim_ssm_fwd(const void* x, const void* z, const fastvim_params* params, const fastvim_dims* dims,
                     int pool_axis, const int32_t* mask_idx, void* out, void* stream) {
-    Geom g;
-    Workspace ws;
-    bool empty = false;
-    int st = validate(x, z, params, dims, pool_axis, mask_idx, out, &g, &ws, &empty);
-    if (st || empty) return st;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    if (launch_zero_sync(ws, sync_words(g), s) != hipSuccess) return FASTVIM_ERR_HIP;
-    const fastvim_params q = effective_params(*params);
-    const bool norm = (params->flags & FASTVIM_FLAG_POST_NORM) != 0;
-    const bool local = (params->flags & FASTVIM_FLAG_LOCAL_BWD) != 0;
-    const bool single = !(params->flags & FASTVIM_FLAG_CONV) &&
-                        ((params->flags & FASTVIM_FLAG_FUSED)
-                             ? fused_supported(g, norm, local)
-                             : !(params->flags & FASTVIM_FLAG_STAGED) && fused_preferred(g, norm, local));
-    if (single) return launch_fused(g, x, z, q, ws, out, s) == hipSuccess ? FASTVIM_OK : FASTVIM_ERR_HIP;
-    for (int stage = FASTVIM_STAGE_ROWS; stage <= FASTVIM_STAGE_EPILOGUE; ++stage) {
-        st = run_stage(stage, g, x, z, q, mask_idx, out, ws, s);
-        if (st) return st;
-    }
-    return FASTVIM_OK;
+    return fwd_entry(x, z, params, dims, pool_axis, mask_idx, out, static_cast<hipStream_t>(stream), nullptr);
+}
+
+int fastvim_ssm_fwd_stages(const void* x, const void* z, const fastvim_params* params, const fastvim_dims* dims,
+                           int pool_axis, const int32_t* mask_idx, void* out, void* stream, float* u_out,
+                           float* s_f_out, float* s_b_out, int32_t* row_of_token) {
+    const StageDst dst{u_out, s_f_out, s_b_out, row_of_token};
+    return fwd_entry(x, z, params, dims, pool_axis, mask_idx, out, static_cast<hipStream_t>(stream), &dst);
 }
 
 int fastvim_ssm_stage(int stage, const void* x, const void* z, const fastvim_params* params,
@@ -531,8 +667,9 @@ int fastvim_ssm_stage(int stage, const void* x, const void* z, const fastvim_par
     Geom g;
     Workspace ws;
     bool empty = false;
-    int st = validate(x, z, params, dims, pool_axis, mask_idx, out, &g, &ws, &empty);
+    int st = validate(x, z, params, dims, pool_axis, mask_idx, out, &g, &empty);
     if (st || empty) return st;
+    if ((st = bind_workspace(g, x, z, *params, out, &ws))) return st;
     return run_stage(stage, g, x, z, effective_params(*params), mask_idx, out, ws, static_cast<hipStream_t>(stream));
 }
 
@@ -551,7 +688,8 @@ int fastvim_ssm_export(const fastvim_params* params, const fastvim_dims* dims, i
     const size_t n = export_bytes(g, what);
     if (n == 0) return g.B == 0 && what >= FASTVIM_EXPORT_U && what <= FASTVIM_EXPORT_STATUS ? FASTVIM_OK
                                                                                              : FASTVIM_ERR_ARG;
-    if (!dst || !params->workspace) return FASTVIM_ERR_NULL;
+    if (!dst) return FASTVIM_ERR_NULL;
+    if (!params->workspace) return FASTVIM_ERR_WORKSPACE;
     if (dst_bytes < n) return FASTVIM_ERR_DIMS;
     if (params->workspace_bytes < workspace_layout(g, nullptr, nullptr)) return FASTVIM_ERR_WORKSPACE;
     Workspace ws;
@@ -580,9 +718,8 @@ int fastvim_ssm_bwd(const void* x, const void* z, const void* dout, const fastvi
                     const fastvim_dims* dims, int pool_axis, const int32_t* mask_idx, void* dx, void* dz,
                     const fastvim_grads* grads, void* stream) {
     Geom g;
-    BwdWorkspace ws;
     bool empty = false;
-    const int st = validate_bwd(x, z, dout, params, dims, pool_axis, mask_idx, dx, dz, grads, &g, &ws, &empty);
+    int st = validate_bwd(x, z, dout, params, dims, pool_axis, mask_idx, dx, dz, grads, &g, &empty);
     if (st) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (empty) {  // no tokens: every gradient is zero
@@ -602,7 +739,27 @@ int fastvim_ssm_bwd(const void* x, const void* z, const void* dout, const fastvi
             return FASTVIM_ERR_HIP;
         return FASTVIM_OK;
     }
-    return run_bwd(g, x, z, dout, effective_params(*params), mask_idx, dx, dz, *grads, ws, s);
+    StreamScratch scratch;
+    void* base = params->workspace;
+    if (!base && (st = scratch.take(bwd_workspace_layout(g, nullptr, nullptr), s, &base))) return st;
+    BwdWorkspace ws;
+    bind_bwd_workspace(g, *params, base, &ws);
+    st = run_bwd(g, x, z, dout, effective_params(*params), mask_idx, dx, dz, *grads, ws, s);
+    return scratch.give_back(st);
+}
+
+int fastvim_get_device_error(const fastvim_params* params, void* stream) {
+    if (!params) return FASTVIM_ERR_NULL;
+    if (!params->workspace || params->workspace_bytes < 2 * sizeof(unsigned)) return FASTVIM_ERR_WORKSPACE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    unsigned word = 0;
+    const unsigned* src = static_cast<const unsigned*>(params->workspace) + 1;
+    if (hipMemcpyAsync(&word, src, sizeof(word), hipMemcpyDeviceToHost, s) != hipSuccess ||
+        hipStreamSynchronize(s) != hipSuccess)
+        return FASTVIM_ERR_HIP;
+    if (word & kStatusWaitGaveUp) return FASTVIM_ERR_DEVICE_WAIT;
+    if (word & kStatusBadIndex) return FASTVIM_ERR_BAD_INDEX;
+    return FASTVIM_OK;
 }
 
 int fastvim_calib_copy(void* dst, const void* src, size_t bytes, void* stream) {
@@ -623,9 +780,11 @@ const char* fastvim_status_string(int status) {
         case FASTVIM_ERR_UNSUPPORTED: return "shape not supported by this build (N != 16, R > 64, E > 4096 or E not a multiple of the vector width, h*w*E >= 2^31, masked grid > 16384 cells)";
         case FASTVIM_ERR_ALIGN: return "misaligned pointer (x, z, out, x_proj_w need 16 bytes, workspace 256, others 4)";
         case FASTVIM_ERR_OVERLAP: return "out overlaps x or z, or the workspace overlaps an input or output";
-        case FASTVIM_ERR_WORKSPACE: return "workspace missing or smaller than fastvim_ssm_workspace_bytes";
-        case FASTVIM_ERR_HIP: return "HIP reported an error while enqueuing work";
-        case FASTVIM_ERR_ARG: return "bad enum, stage or export id, unknown or conflicting flags, or mask_idx given for a dense layer";
+        case FASTVIM_ERR_WORKSPACE: return "workspace smaller than fastvim_ssm_workspace_bytes, or NULL where the call needs the caller's";
+        case FASTVIM_ERR_HIP: return "HIP reported an error while enqueuing work or allocating stream-ordered scratch";
+        case FASTVIM_ERR_ARG: return "bad enum, stage or export id, unknown or conflicting flags or tuning bits, or mask_idx given for a dense layer";
+        case FASTVIM_ERR_BAD_INDEX: return "the device found an invalid mask index (out of range or repeated)";
+        case FASTVIM_ERR_DEVICE_WAIT: return "a wait inside the single launch gave up; its outputs are invalid";
         default: return "unknown status";
     }
 }

@@ -10,9 +10,12 @@ constexpr int kBwdTMax = 128;        // longest scan the backward kernels take (
 constexpr int kBwdCh = 64;           // channels per scan-adjoint workgroup (one channel group)
 constexpr int kBwdTokChunk = 64;     // pooled tokens per partial of d x_proj_w
 constexpr int kColRowsPerBlock = 256;  // rows per first-stage block of a column sum
+constexpr int kBwdStatusWords = 2;     // header of a backward workspace: [0] unused, [1] status word
 
 // Workspace of one backward call (every region 256-byte aligned).  fwd views
-// the part shared with the forward stages (u, xdbl, s_f, s_b, rows, bad).
+// the part shared with the forward stages (u, xdbl, s_f, s_b, rows, bad) and
+// its sync points to the workspace's header (kBwdStatusWords words at its
+// start; word 1 is the call's status word, as in a forward workspace).
 struct BwdWorkspace {
     Workspace fwd;
     float* gs;     // (B, T, E) dL/ds: the gated upstream gradient summed over the pooled axis

@@ -21,6 +21,7 @@ struct Geom {
     bool pooled;  // axis is COLS or ROWS
     int io;       // fastvim_dtype
     float pool_scale = 1.f;  // factor on the pooled tokens (FASTVIM_FLAG_POOL_SCALE)
+    uint32_t tuning = 0;     // params.tuning (single-launch lags, poll limit)
 };
 
 // What a pooled row sum is multiplied by: pool_scale / P.
@@ -34,17 +35,25 @@ struct Workspace {
     float* s_b;       // (B, T, E) backward scan output
     int32_t* rows;    // (B, K) masked: scan row of each kept token, -1 if invalid
     int32_t* bad;     // (B) masked: invalid mask entries per image
-    unsigned* sync;   // (2 + 2B) ticket, status word, per-image progress counters
+    unsigned* sync;   // (2 + 2B) ticket, status word, per-image progress counters; first in the
+                      // workspace, so the status word sits at byte offset 4
 };
 
 // Words of the sync region: ticket, status, and two counters per image.
 inline int64_t sync_words(const Geom& g) { return 2 + 2 * g.B; }
 
+// Status word bits (sync[1]): a wait in the single launch gave up; an invalid
+// mask index was found (FASTVIM_FLAG_CHECK_IDX).
+constexpr unsigned kStatusWaitGaveUp = 1u;
+constexpr unsigned kStatusBadIndex = 2u;
+
 // Bytes needed; when base != nullptr also fills *ws.
 size_t workspace_layout(const Geom& g, void* base, Workspace* ws);
 
 // Stage launchers (enqueue only; return the launch's hipError_t).
-hipError_t launch_mask_rows(const Geom& g, const int32_t* idx, const Workspace& ws, hipStream_t st);
+// status: NULL, or the status word that gets kStatusBadIndex when an index is invalid.
+hipError_t launch_mask_rows(const Geom& g, const int32_t* idx, const Workspace& ws, unsigned* status,
+                            hipStream_t st);
 hipError_t launch_pool(const Geom& g, const void* x, const Workspace& ws, hipStream_t st);
 hipError_t launch_proj(const Geom& g, const void* x, const fastvim_params& p, const Workspace& ws,
                        hipStream_t st);

@@ -34,15 +34,15 @@
 // when it starts and waits only for items with smaller tickets, which were
 // taken by workgroups that had already started, so every wait ends whatever
 // the grid size or residency.  As a guard against a broken invariant a wait
-// also gives up after a bounded number of polls and raises a status bit.
+// also gives up after a bounded number of polls and raises a status bit; an
+// output item that sees the bit after its wait writes NaN over its block, so
+// a give-up shows in the result, not only in the status word.
 //
 // Publication without L2 write-backs: a producer stores its results with
 // agent-scope atomic stores (written through to the device-coherent level),
 // waits for them to complete, then bumps the counter; a consumer polls the
 // counter, then executes an agent-scope acquire (invalidating its CU's L1 and
 // its XCD's L2) before reading with ordinary loads.
-#include <cstdlib>
-
 #include "epilogue_norm.h"
 #include "scan_core.h"
 
@@ -75,6 +75,7 @@ struct FusedArgs {
     float ln_eps;
     float pool_norm;  // pool_scale / P
     unsigned* sync;  // [0] ticket, [1] status, [2, 2+B) rowsDone, [2+B, 2+2B) scanDone
+    unsigned spin_limit;  // polls before a wait gives up
     int64_t B, h, w, E, T, P;
     int R, NX, axis;
     int nA, nS, nE, RG, RE, CJ, G, VE, KS;
@@ -91,17 +92,48 @@ union alignas(16) FusedSmem {
     float buf[kLdsFloats];
 };
 
-// Thread 0 only: poll until *cnt >= target, then acquire at agent scope.
-__device__ __forceinline__ void wait_at_least(unsigned* cnt, unsigned target, unsigned* status) {
+// Thread 0 only: poll until *cnt >= target (at most `limit` polls, then
+// raise status bit 0 and go on), then acquire at agent scope.
+__device__ __forceinline__ void wait_at_least(unsigned* cnt, unsigned target, unsigned* status, unsigned limit) {
     unsigned spins = 0;
     while (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
         __builtin_amdgcn_s_sleep(2);
-        if (++spins > kSpinLimit) {
+        if (++spins >= limit) {
             __hip_atomic_fetch_or(status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             break;
         }
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+}
+
+// Output items: wait until image b's scans are done; true (for every thread)
+// if any wait of the launch gave up before that, the status word then being
+// set.  A give-up upstream of this image raised the bit before counting its
+// item done, so it is seen here.
+__device__ __forceinline__ bool wait_scans(const FusedArgs& a, int64_t b) {
+    __shared__ unsigned s_status;
+    if (threadIdx.x == 0) {
+        wait_at_least(&a.sync[2 + a.B + b], (unsigned)a.nS, &a.sync[1], a.spin_limit);
+        s_status = __hip_atomic_load(&a.sync[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & 1u;
+    }
+    __syncthreads();
+    return s_status != 0u;
+}
+
+// NaN over grid rows [i0, i0 + ni) x columns [j0, j0 + nj) of image b's out.
+template <class IO>
+__device__ void poison_block(const FusedArgs& a, int64_t b, int64_t i0, int64_t ni, int64_t j0, int64_t nj) {
+    using elem = typename IO::elem;
+    float nanv[IO::V];
+#pragma unroll
+    for (int v = 0; v < IO::V; ++v) nanv[v] = __builtin_nanf("");
+    elem* o = static_cast<elem*>(a.out);
+    const int64_t n = ni * nj * a.VE;
+    for (int64_t q = threadIdx.x; q < n; q += kFT) {
+        const int64_t cell = q / a.VE, v = q - cell * a.VE;
+        const int64_t i = i0 + cell / nj, j = j0 + cell % nj;
+        store_vec<true>(o + ((b * a.h + i) * a.w + j) * a.E + v * IO::V, nanv);
+    }
 }
 
 // All threads: wait for this thread's write-through stores to complete, then
@@ -232,8 +264,12 @@ __device__ void item_epilogue(const FusedArgs& a, int64_t b, int k) {
     using elem = typename IO::elem;
     using raw = typename IO::raw;
     const int tid = threadIdx.x;
-    if (tid == 0) wait_at_least(&a.sync[2 + a.B + b], (unsigned)a.nS, &a.sync[1]);
-    __syncthreads();
+    const int64_t i0 = (int64_t)k * a.RE;
+    const int64_t i1 = i0 + a.RE < a.h ? i0 + a.RE : a.h;
+    if (wait_scans(a, b)) {
+        poison_block<IO>(a, b, i0, i1 - i0, 0, a.w);
+        return;
+    }
     const int VE = a.VE, G = a.G;
     const int c = tid % VE, g = tid / VE;
     if (g >= G) return;
@@ -243,8 +279,6 @@ __device__ void item_epilogue(const FusedArgs& a, int64_t b, int k) {
 #pragma unroll
     for (int v = 0; v < V; ++v) dsum[v] = a.pf.D[col + v] + a.pb.D[col + v];
 
-    const int64_t i0 = (int64_t)k * a.RE;
-    const int64_t i1 = i0 + a.RE < a.h ? i0 + a.RE : a.h;
     const int iw = (int)w, iE = (int)E, coff = (int)col;
     for (int64_t i = i0; i < i1; ++i) {
         // wave-uniform row bases, 32-bit lane offsets
@@ -297,14 +331,16 @@ __device__ void item_epilogue_rows(const FusedArgs& a, int64_t b, int k, float* 
     using elem = typename IO::elem;
     using raw = typename IO::raw;
     const int tid = threadIdx.x;
-    if (tid == 0) wait_at_least(&a.sync[2 + a.B + b], (unsigned)a.nS, &a.sync[1]);
-    __syncthreads();
     const int64_t E = a.E, w = a.w;
     const int nJB = (int)((w + a.CJ - 1) / a.CJ);
     const int ib = k / nJB, jb = k - ib * nJB;
     const int64_t i0 = (int64_t)ib * a.RE, j0 = (int64_t)jb * a.CJ;
     const int ni = (int)(i0 + a.RE < a.h ? a.RE : a.h - i0);
     const int nj = (int)(j0 + a.CJ < w ? a.CJ : w - j0);
+    if (wait_scans(a, b)) {
+        poison_block<IO>(a, b, i0, ni, j0, nj);
+        return;
+    }
     const int iE = (int)E, iw = (int)w;
     {
         // all loads in flight at once: the rows come from beyond this XCD's L2
@@ -392,7 +428,13 @@ __device__ void item_epilogue_norm(const FusedArgs& a, int64_t b, int k, float* 
     using elem = typename IO::elem;
     constexpr int kTeams = kFT / kNormTL;
     const int tid = threadIdx.x;
-    if (tid == 0) wait_at_least(&a.sync[2 + a.B + b], (unsigned)a.nS, &a.sync[1]);
+    {
+        const int64_t r0 = (int64_t)k * a.RE, r1 = r0 + a.RE < a.h ? r0 + a.RE : a.h;
+        if (wait_scans(a, b)) {
+            poison_block<IO>(a, b, r0, r1 - r0, 0, a.w);
+            return;
+        }
+    }
     const int w = (int)a.w, E = (int)a.E;
     float* ds = lds;              // [E] D_fwd + D_bwd
     float* gw = lds + E;          // [E] norm weight
@@ -485,7 +527,7 @@ __global__ void __launch_bounds__(kFT) fused_layer_kernel(FusedArgs a) {
     const int64_t bs = slot - a.LS;
     if (bs >= 0 && bs < a.B) {
         if (r < a.nS) {
-            if (threadIdx.x == 0) wait_at_least(&a.sync[2 + bs], (unsigned)a.nA, &a.sync[1]);
+            if (threadIdx.x == 0) wait_at_least(&a.sync[2 + bs], (unsigned)a.nA, &a.sync[1], a.spin_limit);
             __syncthreads();
             __builtin_amdgcn_s_setprio(2);  // the scan is on the critical path of its image
             ScanArgs sa{a.xdbl, a.pf, a.pb, a.s_f, a.s_b, a.T, a.E, a.R, a.NX};
@@ -505,11 +547,6 @@ __global__ void __launch_bounds__(kFT) fused_layer_kernel(FusedArgs a) {
 __global__ void zero_sync_kernel(unsigned* sync, int64_t n) {
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
         sync[i] = 0u;
-}
-
-int env_int(const char* name, int dflt) {
-    const char* s = getenv(name);
-    return s ? atoi(s) : dflt;
 }
 
 // Item sizes and ticket layout for a geometry; false if not covered.  norm:
@@ -566,16 +603,17 @@ bool plan(const Geom& g, FusedArgs* a, bool norm, bool local) {
     // within about 180 MB, so LE = 180 MB / x bytes per image (7 images at
     // 2048^2 fp32, 14 in bf16: measured best, 7-8 and 12-16).  The scans
     // start LS slots after pooling, enough for the image's A items to drain.
-    // The environment variables override both (for lag sweeps).
+    // The call's tuning word can override both (for lag sweeps).
     const int64_t x_img = g.h * g.w * g.E * esz;
     int64_t le = (180ll << 20) / x_img;
     le = le < 1 ? 1 : (le > g.B ? g.B : le);
     int64_t ls = le / 4 < 3 ? 3 : le / 4;
     if (ls > le) ls = le;
-    a->LS = env_int("FASTVIM_FUSED_LS", (int)ls);
-    a->LE = env_int("FASTVIM_FUSED_LE", (int)le);
-    if (a->LS < 1) a->LS = 1;
+    const int ls_set = (int)(g.tuning & 0xffu), le_set = (int)((g.tuning >> 8) & 0xffu);
+    a->LS = ls_set ? ls_set : (int)ls;
+    a->LE = le_set ? le_set : (int)le;
     if (a->LE < a->LS) a->LE = a->LS;
+    a->spin_limit = (g.tuning & FASTVIM_TUNING_POLL1) ? 1u : kSpinLimit;
     // slots [0, B + LE): piecewise-constant item counts between the breakpoints
     int64_t pts[6] = {0, a->LS, a->LE, g.B, g.B + a->LS, g.B + a->LE};
     for (int i = 1; i < 6; ++i)  // insertion sort

@@ -68,7 +68,7 @@ pool_dense_kernel(const typename IO::elem* __restrict__ x, float* __restrict__ u
 // [0, h*w) or one that occurs twice gets row -1 (its outputs become NaN).
 __global__ void __launch_bounds__(256)
 mask_rows_kernel(const int32_t* __restrict__ idx, int32_t* __restrict__ rows, int32_t* __restrict__ bad,
-                 int64_t K, int64_t hw, int64_t w, int axis) {
+                 unsigned* __restrict__ status, int64_t K, int64_t hw, int64_t w, int axis) {
     extern __shared__ uint32_t cnt[];  // [hw]
     __shared__ uint32_t nbad;
     const int64_t b = blockIdx.x;
@@ -89,7 +89,10 @@ mask_rows_kernel(const int32_t* __restrict__ idx, int32_t* __restrict__ rows, in
     }
     if (mine) atomicAdd(&nbad, mine);
     __syncthreads();
-    if (threadIdx.x == 0) bad[b] = (int32_t)nbad;
+    if (threadIdx.x == 0) {
+        bad[b] = (int32_t)nbad;
+        if (status && nbad) atomicOr(status, kStatusBadIndex);
+    }
 }
 
 // Masked pooling: workgroup (b, t) sums the kept tokens whose row is t and
@@ -182,10 +185,11 @@ hipError_t pool_masked_t(const Geom& g, const void* x, const Workspace& ws, hipS
 
 }  // namespace
 
-hipError_t launch_mask_rows(const Geom& g, const int32_t* idx, const Workspace& ws, hipStream_t st) {
+hipError_t launch_mask_rows(const Geom& g, const int32_t* idx, const Workspace& ws, unsigned* status,
+                            hipStream_t st) {
     const size_t lds = (size_t)(g.h * g.w) * sizeof(uint32_t);
-    hipLaunchKernelGGL(mask_rows_kernel, dim3((unsigned)g.B), dim3(256), lds, st, idx, ws.rows, ws.bad, g.K,
-                       g.h * g.w, g.w, g.axis);
+    hipLaunchKernelGGL(mask_rows_kernel, dim3((unsigned)g.B), dim3(256), lds, st, idx, ws.rows, ws.bad, status,
+                       g.K, g.h * g.w, g.w, g.axis);
     return hipGetLastError();
 }
 

@@ -16,7 +16,7 @@ from pooled_selective_state_amd import binding as Bd
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "fastvim.h")
 
-OK, ENULL, EDIMS, EUNSUP, EALIGN, EOVERLAP, EWS, EHIP, EARG = 0, -1, -2, -3, -4, -5, -6, -7, -8
+OK, ENULL, EDIMS, EUNSUP, EALIGN, EOVERLAP, EWS, EHIP, EARG, EBADIDX, EWAIT = 0, -1, -2, -3, -4, -5, -6, -7, -8, -9, -10
 
 
 def declared_functions():
@@ -32,12 +32,12 @@ def test_library_exports_every_declared_function():
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(Bd.EXPORTED_SYMBOLS)
-    assert lib.fastvim_abi_version() == 10
+    assert lib.fastvim_abi_version() == 11
 
 
 def test_status_strings():
     lib = P.lib()
-    for code in (OK, ENULL, EDIMS, EUNSUP, EALIGN, EOVERLAP, EWS, EHIP, EARG):
+    for code in (OK, ENULL, EDIMS, EUNSUP, EALIGN, EOVERLAP, EWS, EHIP, EARG, EBADIDX, EWAIT):
         assert lib.fastvim_status_string(code)
     assert lib.fastvim_status_string(123) == b"unknown status"
 
@@ -155,9 +155,13 @@ def test_bad_enums():
     c = FakeCall()
     assert lib.fastvim_ssm_stage(5, c.x, c.z, ctypes.byref(c.params), ctypes.byref(c.dims), 0, None, c.out,
                                  None) == EARG
-    for flags in (P.FLAG_STAGED | P.FLAG_FUSED, 64, 1 << 31):  # conflicting or unknown flags
+    for flags in (P.FLAG_STAGED | P.FLAG_FUSED, 128, 1 << 31):  # conflicting or unknown flags
         c = FakeCall()
         c.params.flags = flags
+        expect(c, EARG)
+    for tuning in (1 << 17, 1 << 31):  # unknown tuning bits
+        c = FakeCall()
+        c.params.tuning = tuning
         expect(c, EARG)
 
 
@@ -201,8 +205,73 @@ def test_workspace_checks():
     c.params.workspace_bytes -= 1
     expect(c, EWS)
     c = FakeCall()
+    c.params.workspace = c.params.workspace + 64
+    expect(c, EALIGN)
+    # a NULL workspace is the stream-ordered allocator's: every argument is
+    # still checked first, before anything is allocated
+    c = FakeCall()
     c.params.workspace = None
-    expect(c, EWS)
+    c.x += 4
+    expect(c, EALIGN)
+    c = FakeCall()
+    c.params.workspace = None
+    c.out = c.x
+    expect(c, EOVERLAP)
+    # calls that need the caller's workspace
+    lib = P.lib()
+    c = FakeCall()
+    c.params.workspace = None
+    assert lib.fastvim_ssm_stage(P.STAGE_POOL, c.x, c.z, ctypes.byref(c.params), ctypes.byref(c.dims), c.axis,
+                                 None, c.out, None) == EWS
+    assert lib.fastvim_ssm_export(ctypes.byref(c.params), ctypes.byref(c.dims), c.axis, P.EXPORT_U, c.out,
+                                  1 << 20, None) == EWS
+    assert lib.fastvim_get_device_error(ctypes.byref(c.params), None) == EWS
+    assert lib.fastvim_get_device_error(None, None) == ENULL
+
+
+class FakeStages(FakeCall):
+    """fastvim_ssm_fwd_stages with fake destinations far from the other arguments."""
+
+    def __init__(self, **kw):
+        super().__init__(**kw)
+        far = 1 << 43
+        self.u, self.sf, self.sb, self.rows = far, far + (1 << 30), far + (2 << 30), far + (3 << 30)
+
+    def fwd(self):
+        return P.lib().fastvim_ssm_fwd_stages(self.x, self.z, ctypes.byref(self.params), ctypes.byref(self.dims),
+                                              self.axis, self.idx, self.out, None, self.u, self.sf, self.sb,
+                                              self.rows)
+
+
+def test_fwd_stages_validation():
+    c = FakeStages()
+    expect(c, EARG)  # row ids of a dense layer
+    c = FakeStages(axis=P.POOL_NONE_ROWMAJOR)
+    c.rows = None
+    expect(c, EARG)  # pooled tokens of an unpooled layer
+    c = FakeStages()
+    c.rows = None
+    c.sf += 2
+    expect(c, EALIGN)
+    c = FakeStages()
+    c.rows = None
+    c.sb = c.x
+    expect(c, EOVERLAP)  # a destination over an input
+    c = FakeStages()
+    c.rows = None
+    c.sb = c.sf + 64
+    expect(c, EOVERLAP)  # two destinations over each other
+    c = FakeStages()
+    c.rows = None
+    c.u = c.params.workspace
+    expect(c, EOVERLAP)  # a destination over the workspace
+    c = FakeStages()
+    c.rows = None
+    c.x += 4
+    expect(c, EALIGN)  # the layer's own arguments as fastvim_ssm_fwd
+    c = FakeStages(B=0)
+    c.rows = None
+    expect(c, OK)  # nothing to run or copy
 
 
 def test_empty_batch_is_a_noop():
@@ -360,7 +429,7 @@ def test_bwd_unsupported_and_bad_flags():
         assert FakeBwd(axis=axis).bwd() == EUNSUP
     assert FakeBwd(h=129).bwd() == EUNSUP
     assert FakeBwd(N=8).bwd() == EUNSUP
-    for flags, code in ((P.FLAG_FUSED, EUNSUP), (64, EARG),
+    for flags, code in ((P.FLAG_FUSED, EUNSUP), (128, EARG),
                         (P.FLAG_STAGED, OK)):
         c = FakeBwd()
         c.params.flags = flags
@@ -369,6 +438,9 @@ def test_bwd_unsupported_and_bad_flags():
     c = FakeBwd()
     c.idx = c.dx + (1 << 30)
     assert c.bwd() == EARG  # mask_idx with a dense layer
+    c = FakeBwd()
+    c.params.tuning = 1
+    assert c.bwd() == EARG  # no single launch to tune
 
 
 def _norm_bwd(**kw):
@@ -555,9 +627,15 @@ def test_bwd_workspace_checks():
     c = FakeBwd()
     c.params.workspace_bytes -= 1
     assert c.bwd() == EWS
+    # NULL: the stream-ordered allocator's; the other arguments are checked first
     c = FakeBwd()
     c.params.workspace = None
-    assert c.bwd() == EWS
+    c.dz = c.dx
+    assert c.bwd() == EOVERLAP
+    c = FakeBwd()
+    c.params.workspace = None
+    c.grads.fwd.D = None
+    assert c.bwd() == ENULL
 
 
 def test_conv_validation():
@@ -583,7 +661,7 @@ def test_conv_validation():
     c.params.flags = P.FLAG_CONV
     assert c.bwd() == ENULL  # the backward pass takes the conv, and needs its parameters
     c = FakeCall()
-    c.params.flags = 64
+    c.params.flags = 128
     expect(c, EARG)
 
 
