@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define FASTVIM_ABI_VERSION 11
+#define FASTVIM_ABI_VERSION 12
 
 typedef enum fastvim_status {
     FASTVIM_OK = 0,
@@ -75,7 +75,9 @@ typedef enum fastvim_status {
     /* reported by fastvim_get_device_error only, for the last call that ran
      * its kernels with the workspace: */
     FASTVIM_ERR_BAD_INDEX = -9,   /* FASTVIM_FLAG_CHECK_IDX found an invalid mask index */
-    FASTVIM_ERR_DEVICE_WAIT = -10 /* a wait inside the single launch gave up; its outputs are invalid */
+    FASTVIM_ERR_DEVICE_WAIT = -10, /* a wait inside the single launch gave up; its outputs are invalid */
+    FASTVIM_ERR_SCRATCH = -11     /* fastvim_ssm_fwd_noalloc: the layer needs more than
+                                     FASTVIM_NOALLOC_SCRATCH_BYTES of scratch */
 } fastvim_status;
 
 /* Element type of x, z and out.  Parameters are always fp32; all arithmetic
@@ -291,6 +293,26 @@ int fastvim_ssm_fwd_stages(const void *x, const void *z, const fastvim_params *p
  * (waits for the work enqueued on it).  FASTVIM_ERR_WORKSPACE for a NULL
  * workspace (a call that allocated its own keeps no status). */
 int fastvim_get_device_error(const fastvim_params *params, void *stream);
+
+/* The layer for callers that cannot allocate: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid device allocation.  The same
+ * arguments and results as fastvim_ssm_fwd, except that params->workspace and
+ * params->workspace_bytes are not read: the scratch is a fixed buffer of
+ * FASTVIM_NOALLOC_SCRATCH_BYTES inside the library, one per GPU, held from
+ * the library's first use on that GPU until the process ends.  The call
+ * allocates nothing (no hipMalloc, hipMallocAsync or hipFree), also not on
+ * its first call on a GPU, which only looks up that GPU's buffer.  Layers whose
+ * fastvim_ssm_workspace_bytes exceeds the buffer get FASTVIM_ERR_SCRATCH
+ * (every pooled layer of this build's workloads fits; unpooled layers of
+ * large grids do not).  All calls on one GPU share its buffer, which keeps
+ * the last call's intermediates: calls that overlap in time on one GPU
+ * (different streams, different threads) race and give wrong results, so
+ * the caller serialises them, e.g. on one stream.  Every counter the layer
+ * needs zeroed is cleared by the call itself, by a kernel.  No export or
+ * device-error read reaches this buffer. */
+#define FASTVIM_NOALLOC_SCRATCH_BYTES ((size_t)96 << 20)
+int fastvim_ssm_fwd_noalloc(const void *x, const void *z, const fastvim_params *params, const fastvim_dims *dims,
+                            int pool_axis, const int32_t *mask_idx, void *out, void *stream);
 
 /* The layer's stages, for timing and inspection.  fastvim_ssm_fwd runs
  * ROWS (masked only), POOL (pooled only), PROJ, SCAN and EPILOGUE in that

@@ -54,8 +54,11 @@ NO_WORKSPACE = "stream-ordered"
 STATUS = {
     0: "FASTVIM_OK", -1: "FASTVIM_ERR_NULL", -2: "FASTVIM_ERR_DIMS", -3: "FASTVIM_ERR_UNSUPPORTED",
     -4: "FASTVIM_ERR_ALIGN", -5: "FASTVIM_ERR_OVERLAP", -6: "FASTVIM_ERR_WORKSPACE", -7: "FASTVIM_ERR_HIP",
-    -8: "FASTVIM_ERR_ARG", -9: "FASTVIM_ERR_BAD_INDEX", -10: "FASTVIM_ERR_DEVICE_WAIT",
+    -8: "FASTVIM_ERR_ARG", -9: "FASTVIM_ERR_BAD_INDEX", -10: "FASTVIM_ERR_DEVICE_WAIT", -11: "FASTVIM_ERR_SCRATCH",
 }
+
+# fastvim_ssm_fwd_noalloc's fixed scratch buffer (one per GPU, inside the library)
+NOALLOC_SCRATCH_BYTES = 96 << 20
 
 DIR_FIELDS = ("x_proj_w", "dt_proj_w", "dt_proj_b", "A_log", "D")
 
@@ -95,7 +98,8 @@ class Grads(ctypes.Structure):
 
 
 EXPORTED_SYMBOLS = (
-    "fastvim_ssm_workspace_bytes", "fastvim_ssm_fwd", "fastvim_ssm_fwd_stages", "fastvim_get_device_error",
+    "fastvim_ssm_workspace_bytes", "fastvim_ssm_fwd", "fastvim_ssm_fwd_stages", "fastvim_ssm_fwd_noalloc",
+    "fastvim_get_device_error",
     "fastvim_ssm_stage", "fastvim_ssm_export", "fastvim_ssm_export_bytes", "fastvim_ssm_bwd_workspace_bytes",
     "fastvim_ssm_bwd", "fastvim_calib_copy", "fastvim_status_string", "fastvim_abi_version",
 )
@@ -120,6 +124,8 @@ def lib():
             L.fastvim_ssm_fwd.restype = ci
             L.fastvim_ssm_fwd_stages.argtypes = [vp, vp, PP, PD, ci, vp, vp, vp, vp, vp, vp, vp]
             L.fastvim_ssm_fwd_stages.restype = ci
+            L.fastvim_ssm_fwd_noalloc.argtypes = [vp, vp, PP, PD, ci, vp, vp, vp]
+            L.fastvim_ssm_fwd_noalloc.restype = ci
             L.fastvim_get_device_error.argtypes = [PP, vp]
             L.fastvim_get_device_error.restype = ci
             L.fastvim_ssm_stage.argtypes = [ci, vp, vp, PP, PD, ci, vp, vp, vp]
@@ -404,6 +410,17 @@ class SSMCall:
         if st:
             raise FastVimError(st, "fastvim_ssm_fwd")
         self._after(stream, check_device)
+        return self.out
+
+    def run_noalloc(self, stream=None) -> torch.Tensor:
+        """The layer through fastvim_ssm_fwd_noalloc: scratch from the
+        library's fixed per-GPU buffer, nothing allocated (construct the call
+        with workspace=NO_WORKSPACE and an out tensor to allocate nothing
+        here either).  Calls that overlap on one GPU race."""
+        st = lib().fastvim_ssm_fwd_noalloc(*self._args(), _stream(stream))
+        if st:
+            raise FastVimError(st, "fastvim_ssm_fwd_noalloc")
+        self._after(stream, False)
         return self.out
 
     def run_stages(self, stream=None, u: bool = True, s: bool = True, rows: bool = True) -> Dict[str, torch.Tensor]:

@@ -538,6 +538,21 @@ int fwd_entry(const void* x, const void* z, const fastvim_params* params, const 
 
 }  // namespace
 
+int fwd_on_scratch(const void* x, const void* z, const fastvim_params* params, const fastvim_dims* dims, int axis,
+                   const int32_t* idx, void* out, hipStream_t s, int (*scratch)(void**), size_t cap) {
+    Geom g;
+    bool empty = false;
+    int st = validate(x, z, params, dims, axis, idx, out, &g, &empty);
+    if (st || empty) return st;
+    if (workspace_layout(g, nullptr, nullptr) > cap) return FASTVIM_ERR_SCRATCH;
+    void* base = nullptr;
+    if ((st = scratch(&base))) return st;
+    Workspace ws;
+    workspace_layout(g, base, &ws);
+    if (params->saved_u) ws.u = params->saved_u;
+    return run_fwd(g, x, z, *params, idx, out, ws, s);
+}
+
 size_t workspace_layout(const Geom& g, void* base, Workspace* ws) {
     size_t off = 0;
     auto take = [&](size_t bytes) {
@@ -785,6 +800,7 @@ const char* fastvim_status_string(int status) {
         case FASTVIM_ERR_ARG: return "bad enum, stage or export id, unknown or conflicting flags or tuning bits, or mask_idx given for a dense layer";
         case FASTVIM_ERR_BAD_INDEX: return "the device found an invalid mask index (out of range or repeated)";
         case FASTVIM_ERR_DEVICE_WAIT: return "a wait inside the single launch gave up; its outputs are invalid";
+        case FASTVIM_ERR_SCRATCH: return "the layer needs more scratch than the fixed buffer of fastvim_ssm_fwd_noalloc holds (FASTVIM_NOALLOC_SCRATCH_BYTES)";
         default: return "unknown status";
     }
 }

@@ -50,6 +50,13 @@ constexpr unsigned kStatusBadIndex = 2u;
 // Bytes needed; when base != nullptr also fills *ws.
 size_t workspace_layout(const Geom& g, void* base, Workspace* ws);
 
+// fastvim_ssm_fwd on a scratch region of cap bytes whose device address
+// scratch() gives, asked only once every argument has passed validation
+// (params->workspace is not read); FASTVIM_ERR_SCRATCH when the layer needs
+// more than cap.  Enqueues no allocation.
+int fwd_on_scratch(const void* x, const void* z, const fastvim_params* params, const fastvim_dims* dims, int axis,
+                   const int32_t* idx, void* out, hipStream_t s, int (*scratch)(void**), size_t cap);
+
 // Stage launchers (enqueue only; return the launch's hipError_t).
 // status: NULL, or the status word that gets kStatusBadIndex when an index is invalid.
 hipError_t launch_mask_rows(const Geom& g, const int32_t* idx, const Workspace& ws, unsigned* status,

@@ -16,7 +16,8 @@ from pooled_selective_state_amd import binding as Bd
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "fastvim.h")
 
-OK, ENULL, EDIMS, EUNSUP, EALIGN, EOVERLAP, EWS, EHIP, EARG, EBADIDX, EWAIT = 0, -1, -2, -3, -4, -5, -6, -7, -8, -9, -10
+OK, ENULL, EDIMS, EUNSUP, EALIGN, EOVERLAP, EWS, EHIP, EARG, EBADIDX, EWAIT, ESCRATCH = (0, -1, -2, -3, -4, -5, -6, -7, -8,
+                                                                     -9, -10, -11)
 
 
 def declared_functions():
@@ -32,12 +33,12 @@ def test_library_exports_every_declared_function():
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(Bd.EXPORTED_SYMBOLS)
-    assert lib.fastvim_abi_version() == 11
+    assert lib.fastvim_abi_version() == 12
 
 
 def test_status_strings():
     lib = P.lib()
-    for code in (OK, ENULL, EDIMS, EUNSUP, EALIGN, EOVERLAP, EWS, EHIP, EARG, EBADIDX, EWAIT):
+    for code in (OK, ENULL, EDIMS, EUNSUP, EALIGN, EOVERLAP, EWS, EHIP, EARG, EBADIDX, EWAIT, ESCRATCH):
         assert lib.fastvim_status_string(code)
     assert lib.fastvim_status_string(123) == b"unknown status"
 
@@ -680,3 +681,32 @@ def test_local_bwd_validation():
     c.params.flags = P.FLAG_LOCAL_BWD
     c.params.fwd.A_log = None  # the forward set is still read
     expect(c, ENULL)
+
+
+class FakeNoalloc(FakeCall):
+    def fwd(self):
+        return P.lib().fastvim_ssm_fwd_noalloc(self.x, self.z, ctypes.byref(self.params), ctypes.byref(self.dims),
+                                               self.axis, self.idx, self.out, None)
+
+
+def test_noalloc_validation():
+    """fastvim_ssm_fwd_noalloc checks its arguments as fastvim_ssm_fwd does
+    (the workspace fields are not read), and rejects a layer whose scratch
+    exceeds its fixed buffer, before touching the GPU."""
+    c = FakeNoalloc()
+    c.params.workspace = None
+    c.x += 4
+    expect(c, EALIGN)
+    c = FakeNoalloc(K=3)
+    c.idx = None
+    expect(c, ENULL)
+    c = FakeNoalloc(B=0)
+    c.x = c.z = c.out = None
+    expect(c, OK)
+    big = FakeNoalloc(B=4, h=128, w=128, E=256, axis=P.POOL_NONE_ROWMAJOR)
+    assert _ws(big.dims, big.axis) > Bd.NOALLOC_SCRATCH_BYTES
+    expect(big, ESCRATCH)
+    for cfg_dims, axis in ((P.make_dims(128, 128, 128, 384, 16, 12), P.POOL_COLS),
+                           (P.make_dims(128, 128, 128, 384, 16, 12), P.POOL_ROWS),
+                           (P.make_dims(256, 14, 14, 1536, 16, 48, 49, P.BF16), P.POOL_COLS)):
+        assert _ws(cfg_dims, axis) <= Bd.NOALLOC_SCRATCH_BYTES  # the pooled workloads fit
