@@ -205,7 +205,7 @@ class Oracle:
         ln: None, or {"weight": (E,), "bias": (E,), "eps": float} for the
         post-SSM LayerNorm before the gate.  conv: None, or {"weight": (E, KC),
         "bias": (E,)}: x is then the Conv1D's input and the layer runs on
-        conv_silu(x) (dense layers only).  local_window = L > 0: LBMamba's
+        conv_silu(x) (masked: the conv along the kept tokens k = 0..K-1).  local_window = L > 0: LBMamba's
         local backward scan (forward parameters, state reset at the top of
         every window of L steps) replaces the global backward scan; of bwd only
         D is used.  pool_scale multiplies the pooled tokens u (not the skip).

@@ -221,8 +221,19 @@ int fvo_mask_rows(const int32_t *idx, int64_t B, int64_t K, int64_t h, int64_t w
  * kept token pools to zero and is still scanned.
  *   u[b, t, e] = (1/P) * sum_{k : rows[b,k] = t} x[b, k, e]
  */
+static void pool_masked_any(const float *x, const double *xd, const int32_t *rows, int64_t B, int64_t K,
+                            int64_t T, int64_t P, int64_t E, double *u);
+
 int fvo_pool_masked(const float *x, const int32_t *rows, int64_t B, int64_t K, int64_t T, int64_t P,
                     int64_t E, double *u)
+{
+    pool_masked_any(x, NULL, rows, B, K, T, P, E, u);
+    return 0;
+}
+
+/* The same, reading the kept tokens from xd (double) when xd is given. */
+static void pool_masked_any(const float *x, const double *xd, const int32_t *rows, int64_t B, int64_t K,
+                            int64_t T, int64_t P, int64_t E, double *u)
 {
 #pragma omp parallel for schedule(static)
     for (int64_t b = 0; b < B; ++b) {
@@ -231,12 +242,25 @@ int fvo_pool_masked(const float *x, const int32_t *rows, int64_t B, int64_t K, i
         for (int64_t k = 0; k < K; ++k) {
             const int64_t t = rows[b * K + k];
             if (t < 0 || t >= T) continue;
-            const float *xv = x + (b * K + k) * E;
-            for (int64_t e = 0; e < E; ++e) ub[t * E + e] += (double)xv[e];
+            const int64_t c = (b * K + k) * E;
+            for (int64_t e = 0; e < E; ++e) ub[t * E + e] += xd ? xd[c + e] : (double)x[c + e];
         }
         for (int64_t k = 0; k < T * E; ++k) ub[k] /= (double)P;
     }
-    return 0;
+}
+
+/*
+ * The producer Conv1D of a masked layer runs along the sequence of kept
+ * tokens as they are given, k = 0 .. K-1: FastMaskVim's block sees only the
+ * kept tokens (the MAE encoder drops the masked ones), and the Conv1D is a
+ * sequence operation of that block [FastVim summary, 方法详解 bullets 1-2
+ * and 6].  In fvo_conv_silu's terms that sequence is a K x 1 grid in row-major
+ * order.
+ */
+static void conv_silu_masked(const float *x, int64_t B, int64_t K, int64_t E, const float *conv_w,
+                             const float *conv_b, int64_t KC, double *xc)
+{
+    fvo_conv_silu(x, B, K, 1, E, FVO_COLS, conv_w, conv_b, KC, xc);
 }
 
 /*
@@ -394,7 +418,8 @@ static void output_token(const double *sf, const double *sb, const float *x, con
 
 /* ln_w == NULL: no post-SSM LayerNorm.  conv_w == NULL: x is the layer's
  * input itself; else x is the Conv1D's input and the layer runs on
- * fvo_conv_silu(x) (dense layers only).
+ * fvo_conv_silu(x) (masked layers: on conv_silu_masked(x), the conv along the
+ * kept tokens in their given order).
  *
  * local_window = L > 0: the local backward scan of LBMamba [LBMamba article,
  * 论文创新点 1-2: a light backward scan inside the forward selective scan, run
@@ -418,26 +443,27 @@ int fvo_layer(const float *x, const float *z, const fvo_dir *pf, const fvo_dir *
 {
     int64_t T, P;
     const int masked = idx != NULL;
-    if (axis < 0 || axis > 3 || (masked && axis > FVO_ROWS) || (masked && conv_w)) return -2;
+    if (axis < 0 || axis > 3 || (masked && axis > FVO_ROWS)) return -2;
     seq_shape(axis, h, w, &T, &P);
-    const int64_t M = B * T;
+    const int64_t M = B * T, ntok = masked ? B * K : B * h * w;
 
     double *u = u_out ? u_out : (double *)malloc((size_t)(M * E) * sizeof(double));
     double *sf = fwd && fwd->s ? fwd->s : (double *)malloc((size_t)(M * E) * sizeof(double));
     double *sb = bwd && bwd->s ? bwd->s : (double *)malloc((size_t)(M * E) * sizeof(double));
-    double *xc = conv_w ? (double *)malloc((size_t)(B * h * w * E) * sizeof(double)) : NULL;
+    double *xc = conv_w ? (double *)malloc((size_t)(ntok * E) * sizeof(double)) : NULL;
     unsigned char *reset = NULL;
     int32_t *rows = NULL;
     int rc = 0;
     if (!u || !sf || !sb || (conv_w && !xc)) { rc = -9; goto done; }
-    if (conv_w) fvo_conv_silu(x, B, h, w, E, axis, conv_w, conv_b, conv_k, xc);
+    if (conv_w && masked) conv_silu_masked(x, B, K, E, conv_w, conv_b, conv_k, xc);
+    else if (conv_w) fvo_conv_silu(x, B, h, w, E, axis, conv_w, conv_b, conv_k, xc);
 
     if (masked) {
         rows = rows_out ? rows_out : (int32_t *)malloc((size_t)(B * K) * sizeof(int32_t));
         if (!rows) { rc = -9; goto done; }
         rc = fvo_mask_rows(idx, B, K, h, w, axis, rows);
         if (rc) goto done;
-        fvo_pool_masked(x, rows, B, K, T, P, E, u);
+        pool_masked_any(x, xc, rows, B, K, T, P, E, u);
     } else {
         pool_dense_any(x, xc, B, h, w, E, axis, u);
     }
@@ -462,8 +488,8 @@ int fvo_layer(const float *x, const float *z, const fvo_dir *pf, const fvo_dir *
             double *y = (double *)malloc((size_t)E * sizeof(double));
             for (int64_t k = 0; y && k < K; ++k) {
                 const int64_t t = rows[b * K + k], c = (b * K + k) * E;
-                output_token(sf + (b * T + t) * E, sb + (b * T + t) * E, x + c, NULL, z + c, pf, pb, E, ln_w,
-                             ln_b, ln_eps, y, out + c);
+                output_token(sf + (b * T + t) * E, sb + (b * T + t) * E, x + c, xc ? xc + c : NULL, z + c, pf, pb,
+                             E, ln_w, ln_b, ln_eps, y, out + c);
             }
             free(y);
         }
@@ -764,7 +790,7 @@ static void conv_silu_adjoint(const float *x, const double *gxc, int64_t B, int6
  * of both scans' contributions and go to the forward direction's gradients,
  * while the backward direction's x_proj_w, dt_proj_w, dt_proj_b and A_log
  * gradients are zero (the layer does not read them) and its D gradient is dD
- * as usual.  conv_w != NULL (dense layers only): x is the Conv1D's input as in
+ * as usual.  conv_w != NULL: x is the Conv1D's input as in
  * fvo_layer; the layer's adjoint with respect to its x (the Conv1D's output)
  * goes through conv_silu_adjoint into dx, and the conv's weight and bias
  * gradients into dconv_w (E, conv_k) and dconv_b (E).  Returns 0, -2,
@@ -779,7 +805,7 @@ int fvo_layer_bwd(const float *x, const float *z, const float *dout, const fvo_d
 {
     int64_t T, P;
     const int masked = idx != NULL;
-    if (axis < 0 || axis > 3 || (masked && axis > FVO_ROWS) || (masked && conv_w)) return -2;
+    if (axis < 0 || axis > 3 || (masked && axis > FVO_ROWS)) return -2;
     seq_shape(axis, h, w, &T, &P);
     const int64_t NX = R + 2 * N, M = B * T, ntok = masked ? B * K : B * h * w;
     const size_t me = (size_t)(M * E) * sizeof(double), mx = (size_t)(M * NX) * sizeof(double);
@@ -807,7 +833,8 @@ int fvo_layer_bwd(const float *x, const float *z, const float *dout, const fvo_d
         rc = -9;
         goto done;
     }
-    if (conv_w) fvo_conv_silu(x, B, h, w, E, axis, conv_w, conv_b, conv_k, xc);
+    if (conv_w && masked) conv_silu_masked(x, B, K, E, conv_w, conv_b, conv_k, xc);
+    else if (conv_w) fvo_conv_silu(x, B, h, w, E, axis, conv_w, conv_b, conv_k, xc);
     if (ln_w)
         for (int64_t e = 0; e < E; ++e) dln_w[e] = dln_b[e] = 0.0;
     for (int d = 0; d < 2; ++d)
@@ -822,7 +849,7 @@ int fvo_layer_bwd(const float *x, const float *z, const float *dout, const fvo_d
     if (masked) {
         rc = fvo_mask_rows(idx, B, K, h, w, axis, rows);
         if (rc) goto done;
-        fvo_pool_masked(x, rows, B, K, T, P, E, u);
+        pool_masked_any(x, xc, rows, B, K, T, P, E, u);
     } else {
         pool_dense_any(x, xc, B, h, w, E, axis, u);
     }
@@ -892,7 +919,10 @@ int fvo_layer_bwd(const float *x, const float *z, const float *dout, const fvo_d
     if (conv_w) {
         /* dx holds dL/d(the conv's output): take it through the conv */
         memcpy(dxc, dx, (size_t)(ntok * E) * sizeof(double));
-        conv_silu_adjoint(x, dxc, B, h, w, E, axis, conv_w, conv_b, conv_k, dx, dconv_w, dconv_b);
+        if (masked) /* along the kept-token sequence, as conv_silu_masked */
+            conv_silu_adjoint(x, dxc, B, K, 1, E, FVO_COLS, conv_w, conv_b, conv_k, dx, dconv_w, dconv_b);
+        else
+            conv_silu_adjoint(x, dxc, B, h, w, E, axis, conv_w, conv_b, conv_k, dx, dconv_w, dconv_b);
     }
 
     if (st) {

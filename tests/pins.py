@@ -621,42 +621,56 @@ def pin_bwd_finite_differences_ln(O):
 def pin_bwd_finite_differences_conv(O):
     """The same check for a layer whose x is the producer Conv1D's input: every
     gradient, dx through the conv and the conv's weight and bias included,
-    matches the central difference of the forward oracle with the conv (both
-    pooling axes, the pool scale and the local backward scan)."""
+    matches the central difference of the forward oracle with the conv: both
+    pooling axes, the pool scale, the local backward scan, the post-SSM
+    LayerNorm (the whole block: conv, pool, scans, skip, norm, gate, with the
+    norm's gradients too) and masked layers (the conv along the kept tokens)."""
     eps = 2.0 ** -14
     rng = np.random.default_rng(44)
-    for axis, scale, local in ((COLS, 1.0, 0), (ROWS, 0.25, 0), (COLS, 1.0, 3), (ROWS, 1.0, 2)):
-        pf, pb, x, z, dout, idx, hw = _bwd_case(rng, axis, False)
+    cases = ((COLS, 1.0, 0, False, False), (ROWS, 0.25, 0, False, False), (COLS, 1.0, 3, False, False),
+             (ROWS, 1.0, 2, False, False), (COLS, 1.0, 0, False, True), (ROWS, 0.25, 0, False, True),
+             (COLS, 1.0, 0, True, False), (ROWS, 1.0, 2, True, True))
+    for axis, scale, local, masked, with_ln in cases:
+        pf, pb, x, z, dout, idx, hw = _bwd_case(rng, axis, masked)
+        if not masked:
+            idx = hw = None
         E = x.shape[-1]
         conv = {k: _dyadic(v) for k, v in rand_conv(rng, E).items()}
-        g = O.layer_bwd(x, z, dout, pf, pb, axis, pool_scale=scale, local_window=local, conv=conv)
-        out = O.layer(x, z, pf, pb, axis, pool_scale=scale, local_window=local, conv=conv)
+        ln = {"weight": _dyadic(rng.uniform(0.5, 1.5, E)), "bias": _dyadic(rng.uniform(-0.5, 0.5, E)),
+              "eps": 2.0 ** -6} if with_ln else None
+        g = O.layer_bwd(x, z, dout, pf, pb, axis, idx=idx, hw=hw, pool_scale=scale, local_window=local, conv=conv,
+                        ln=ln)
+        out = O.layer(x, z, pf, pb, axis, idx=idx, hw=hw, pool_scale=scale, local_window=local, conv=conv, ln=ln)
         floor = 64 * 2.0 ** -52 * float(np.sum(np.abs(dout * out))) / (2.0 * eps)
         targets = [("x", None), ("z", None), ("conv", "weight"), ("conv", "bias")] + \
             [(d, k) for d in ("fwd", "bwd") for k in ("x_proj_w", "dt_proj_w", "dt_proj_b", "A_log", "D")]
+        if with_ln:
+            targets += [("ln", "weight"), ("ln", "bias")]
         for d, k in targets:
             if k is None:
                 base, grad = (x, g["dx"]) if d == "x" else (z, g["dz"])
-            elif d == "conv":
-                base, grad = conv[k], g["conv"][k]
+            elif d in ("conv", "ln"):
+                base, grad = (conv if d == "conv" else ln)[k], g[d][k]
             else:
                 base, grad = (pf if d == "fwd" else pb)[k], g[d][k]
             V = rng.choice([-1.0, 1.0], size=base.shape)
             L = []
             for sgn in (1.0, -1.0):
-                arg = {"x": x, "z": z, "pf": dict(pf), "pb": dict(pb), "conv": dict(conv)}
+                arg = {"x": x, "z": z, "pf": dict(pf), "pb": dict(pb), "conv": dict(conv),
+                       "ln": dict(ln) if ln else None}
                 pert = _perturbed(base, sgn * V, eps)
                 if k is None:
                     arg[d] = pert
                 else:
-                    arg["conv" if d == "conv" else ("pf" if d == "fwd" else "pb")][k] = pert
-                L.append(_loss(O, arg["x"], arg["z"], dout, arg["pf"], arg["pb"], axis, None, None, pool_scale=scale,
-                               local=local, conv=arg["conv"]))
+                    arg[d if d in ("conv", "ln") else ("pf" if d == "fwd" else "pb")][k] = pert
+                L.append(_loss(O, arg["x"], arg["z"], dout, arg["pf"], arg["pb"], axis, idx, hw, ln=arg["ln"],
+                               pool_scale=scale, local=local, conv=arg["conv"]))
             fd = (L[0] - L[1]) / (2.0 * eps)
             an = float(np.sum(grad * V))
             size = max(float(np.linalg.norm(grad)), 1e-30)
-            assert abs(fd - an) <= 1e-6 * size + floor, "Conv1D axis %d scale %g local %d: d/d%s %s: analytic " \
-                "%.12g, finite difference %.12g" % (axis, scale, local, d, k or "", an, fd)
+            assert abs(fd - an) <= 1e-6 * size + floor, "Conv1D axis %d scale %g local %d masked %s norm %s: " \
+                "d/d%s %s: analytic %.12g, finite difference %.12g" % (axis, scale, local, masked, with_ln, d,
+                                                                     k or "", an, fd)
 
 
 def pin_pool_scale_is_a_scaled_input(O):
@@ -805,6 +819,112 @@ def pin_conv_causal(O):
             assert changed == set(range(r0, min(r0 + KC, h * w))), (axis, r0, sorted(changed))
 
 
+def _np_conv_silu_seq(seq, conv):
+    """numpy: causal depthwise conv + SiLU along axis 1 of seq (B, n, E)."""
+    B_, n, E = seq.shape
+    out = np.empty(seq.shape)
+    for b in range(B_):
+        for e in range(E):
+            a = np.convolve(seq[b, :, e].astype(np.float64), conv["weight"][e, ::-1].astype(np.float64))[:n]
+            a = a + float(conv["bias"][e])
+            out[b, :, e] = a * expit(a)
+    return out
+
+
+def _np_layernorm(y, ln):
+    mu = y.mean(axis=-1, keepdims=True)
+    var = ((y - mu) ** 2).mean(axis=-1, keepdims=True)
+    return (y - mu) / np.sqrt(var + ln["eps"]) * ln["weight"].astype(np.float64) + ln["bias"].astype(np.float64)
+
+
+def pin_conv_masked_sequence(O):
+    """A masked layer's Conv1D runs along its kept tokens in the given order:
+    its pooled tokens are the fixed-width row means of numpy's causal
+    convolution + SiLU along k, and with x_proj_w = 0 out is (D_fwd + D_bwd)
+    x_conv silu(z) exactly -- with the post-SSM LayerNorm, numpy's
+    normalisation of (D_fwd + D_bwd) x_conv, gated."""
+    rng = np.random.default_rng(54)
+    B_, h, w, K, E, N, R = 3, 5, 4, 9, 6, 4, 3
+    x = rng.standard_normal((B_, K, E)).astype(np.float32)
+    z = rng.standard_normal((B_, K, E)).astype(np.float32)
+    idx = np.stack([rng.permutation(h * w)[:K] for _ in range(B_)]).astype(np.int32)
+    pf, pb = rand_dir(rng, E, N, R), rand_dir(rng, E, N, R)
+    conv = rand_conv(rng, E)
+    xc = _np_conv_silu_seq(x, conv)
+    Ds = pf["D"].astype(np.float64) + pb["D"].astype(np.float64)
+    for axis, T, P in ((COLS, h, w), (ROWS, w, h)):
+        st = O.layer(x, z, pf, pb, axis, idx=idx, hw=(h, w), stages=True, conv=conv)
+        rows = idx // w if axis == COLS else idx % w
+        u = np.zeros((B_, T, E))
+        for b in range(B_):
+            for k in range(K):
+                u[b, rows[b, k]] += xc[b, k]
+        _close(st["u"], u / P, what="masked conv pooled tokens axis %d" % axis)
+        pf0, pb0 = dict(pf), dict(pb)
+        pf0["x_proj_w"] = np.zeros_like(pf["x_proj_w"])
+        pb0["x_proj_w"] = np.zeros_like(pb["x_proj_w"])
+        out = O.layer(x, z, pf0, pb0, axis, idx=idx, hw=(h, w), conv=conv)
+        _close(out, Ds * xc * silu(z), what="masked conv with zero projection axis %d" % axis)
+        ln = rand_ln(rng, E)
+        out = O.layer(x, z, pf0, pb0, axis, idx=idx, hw=(h, w), conv=conv, ln=ln)
+        _close(out, _np_layernorm(Ds * xc, ln) * silu(z), what="masked conv + norm, zero projection")
+
+
+def pin_conv_masked_all_kept(O):
+    """Every token kept, in the oriented grid's sequence order (row-major for
+    COLS, column-major for ROWS): the masked layer with the Conv1D (and with
+    the LayerNorm) equals the dense one, forward and backward."""
+    rng = np.random.default_rng(55)
+    B_, h, w, E, N, R = 2, 4, 3, 5, 3, 2
+    x = rng.standard_normal((B_, h, w, E)).astype(np.float32)
+    z = rng.standard_normal((B_, h, w, E)).astype(np.float32)
+    dout = rng.standard_normal((B_, h, w, E)).astype(np.float32)
+    pf, pb = rand_dir(rng, E, N, R), rand_dir(rng, E, N, R)
+    conv = rand_conv(rng, E)
+    for axis in (COLS, ROWS):
+        order = np.arange(h * w) if axis == COLS else np.array([i * w + j for j in range(w) for i in range(h)])
+        idx = np.broadcast_to(order.astype(np.int32), (B_, h * w)).copy()
+        for ln in (None, rand_ln(rng, E)):
+            take = lambda a: a.reshape(B_, h * w, E)[:, order]
+            dense = O.layer(x, z, pf, pb, axis, conv=conv, ln=ln)
+            masked = O.layer(take(x), take(z), pf, pb, axis, idx=idx, hw=(h, w), conv=conv, ln=ln)
+            _close(masked, take(dense), what="all kept, conv, axis %d" % axis)
+            gd = O.layer_bwd(x, z, dout, pf, pb, axis, conv=conv, ln=ln)
+            gm = O.layer_bwd(take(x), take(z), take(dout), pf, pb, axis, idx=idx, hw=(h, w), conv=conv, ln=ln)
+            _close(gm["dx"], take(gd["dx"]), what="all kept, conv, dx")
+            _close(gm["dz"], take(gd["dz"]), what="all kept, conv, dz")
+            for k in ("weight", "bias"):
+                _close(gm["conv"][k], gd["conv"][k], what="all kept, conv, d conv " + k)
+            for d in ("fwd", "bwd"):
+                for k in ("x_proj_w", "dt_proj_w", "dt_proj_b", "A_log", "D"):
+                    _close(gm[d][k], gd[d][k], what="all kept, conv, d%s.%s" % (d, k))
+
+
+def pin_conv_norm_zero_projection(O):
+    """The whole block (Conv1D, pool, scans, skip, LayerNorm, gate) with
+    x_proj_w = 0: the scans give zero, so out is numpy's LayerNorm of
+    (D_fwd + D_bwd) x_conv times silu(z), x_conv from numpy's convolution
+    along the oriented sequence (both axes)."""
+    rng = np.random.default_rng(56)
+    B_, h, w, E, N, R = 2, 3, 4, 6, 4, 3
+    x = rng.standard_normal((B_, h, w, E)).astype(np.float32)
+    z = rng.standard_normal((B_, h, w, E)).astype(np.float32)
+    pf, pb = rand_dir(rng, E, N, R), rand_dir(rng, E, N, R)
+    pf["x_proj_w"] = np.zeros_like(pf["x_proj_w"])
+    pb["x_proj_w"] = np.zeros_like(pb["x_proj_w"])
+    conv, ln = rand_conv(rng, E), rand_ln(rng, E)
+    Ds = pf["D"].astype(np.float64) + pb["D"].astype(np.float64)
+    for axis in (COLS, ROWS):
+        seq = _oriented_seq(x, axis)
+        xc_seq = _np_conv_silu_seq(seq, conv)
+        if axis == ROWS:
+            xc = xc_seq.reshape(B_, w, h, E).transpose(0, 2, 1, 3)
+        else:
+            xc = xc_seq.reshape(B_, h, w, E)
+        out = O.layer(x, z, pf, pb, axis, conv=conv, ln=ln)
+        _close(out, _np_layernorm(Ds * xc, ln) * silu(z), what="conv + norm, zero projection, axis %d" % axis)
+
+
 # ---------------------------------------------------------------- LBMamba local backward scan
 def _local_case(rng, B_=2, h=10, w=3, E=5, N=4, R=3):
     pf, pb = rand_dir(rng, E, N, R), rand_dir(rng, E, N, R)
@@ -882,6 +1002,9 @@ ALL_PINS = [
     pin_conv_closed_forms,
     pin_conv_transpose,
     pin_conv_causal,
+    pin_conv_masked_sequence,
+    pin_conv_masked_all_kept,
+    pin_conv_norm_zero_projection,
     pin_local_window_covers_sequence,
     pin_local_window_one,
     pin_local_windows_independent,

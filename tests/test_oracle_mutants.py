@@ -34,8 +34,8 @@ MUTANTS = [
     ("backward scan not reversed", "reverse ? T - 1 - step : step", "step", 1),
     ("dense pool not normalised", "        for (int64_t k = 0; k < T * E; ++k) ub[k] /= (double)P;\n    }\n}\n\n/*\n * Producer side",
      "    }\n}\n\n/*\n * Producer side", 1),
-    ("masked pool normalised by E", "            for (int64_t e = 0; e < E; ++e) ub[t * E + e] += (double)xv[e];\n        }\n        for (int64_t k = 0; k < T * E; ++k) ub[k] /= (double)P;",
-     "            for (int64_t e = 0; e < E; ++e) ub[t * E + e] += (double)xv[e];\n        }\n        for (int64_t k = 0; k < T * E; ++k) ub[k] /= (double)K;", 1),
+    ("masked pool normalised by K", "            for (int64_t e = 0; e < E; ++e) ub[t * E + e] += xd ? xd[c + e] : (double)x[c + e];\n        }\n        for (int64_t k = 0; k < T * E; ++k) ub[k] /= (double)P;",
+     "            for (int64_t e = 0; e < E; ++e) ub[t * E + e] += xd ? xd[c + e] : (double)x[c + e];\n        }\n        for (int64_t k = 0; k < T * E; ++k) ub[k] /= (double)K;", 1),
     ("only the forward D in the skip", "((double)pf->D[e] + (double)pb->D[e])", "((double)pf->D[e])", 1),
     ("gate uses sigmoid(-z)", "return q / (1.0 + exp(-q));", "return q / (1.0 + exp(q));", 1),
     ("softplus without log", "log1p(exp(-fabs(q)))", "exp(-fabs(q))", 1),
@@ -72,7 +72,8 @@ MUTANTS = [
     ("conv row-major on the transposed grid", "const int colmajor = axis == FVO_ROWS || axis == FVO_NONE_COLMAJOR;",
      "const int colmajor = axis == FVO_NONE_COLMAJOR;", 1),
     ("skip reads the conv's input", "(xd ? xd[e] : (double)x[e])", "((double)x[e])", 1),
-    ("pool reads the conv's input", "xd ? xd[c + e] : (double)x[c + e]", "(double)x[c + e]", 1),
+    ("pool reads the conv's input", "xd ? xd[c + e] : (double)x[c + e];\n            }",
+     "(double)x[c + e];\n            }", 1),
     # LBMamba local backward scan
     ("local windows aligned one step late", "reset[t] = (unsigned char)(t % local_window == local_window - 1);",
      "reset[t] = (unsigned char)(t % local_window == 0);", 1),
@@ -159,6 +160,15 @@ MUTANTS = [
     ("output adjoint reads the conv's input", "const double *xco = xc ? xc + off : NULL;", "const double *xco = NULL;", 1),
     ("adjoint uses the current state for the decay", "dd += lam[n] * (A * a * prev + Bn * ut);",
      "dd += lam[n] * (A * a * Hs[k * N + n] + Bn * ut);", 1),
+    # Conv1D with masked layers (along the kept tokens)
+    ("masked skip reads x, not the conv's output",
+     "x + c, xc ? xc + c : NULL, z + c, pf, pb,\n                             E, ln_w",
+     "x + c, NULL, z + c, pf, pb,\n                             E, ln_w", 1),
+    ("masked pool reads x, not the conv's output", "pool_masked_any(x, xc, rows, B, K, T, P, E, u);",
+     "pool_masked_any(x, NULL, rows, B, K, T, P, E, u);", 2),
+    ("masked conv adjoint one tap short",
+     "conv_silu_adjoint(x, dxc, B, K, 1, E, FVO_COLS, conv_w, conv_b, conv_k, dx, dconv_w, dconv_b);",
+     "conv_silu_adjoint(x, dxc, B, K, 1, E, FVO_COLS, conv_w, conv_b, conv_k - 1, dx, dconv_w, dconv_b);", 1),
 ]
 
 
