@@ -201,12 +201,16 @@ typedef struct fastvim_params {
  * sequence r -- row-major r = i*w + j for COLS, column-major r = j*h + i for
  * ROWS (the transposed grid) -- with zeros before its start,
  *   x_conv[r, e] = silu(conv_b[e] + sum_{k<4} conv_w[e, k] * x[r - 3 + k, e])
- * and the layer runs on x_conv: the pool and the skip term compute it where
- * they read x, so it is never written.  Dense pooled layers only, as stage
- * kernels (FASTVIM_FLAG_FUSED is ignored); FASTVIM_ERR_UNSUPPORTED for masked
- * or unpooled layers and with FASTVIM_FLAG_POST_NORM.  Errors:
- * FASTVIM_ERR_NULL (conv_w or conv_b NULL), FASTVIM_ERR_ALIGN (conv_w not
- * 16-byte aligned, conv_b not 4-byte aligned). */
+ * and the layer runs on x_conv.  Dense pooled layers compute it where their
+ * pool and output stages read x, so it is never written (stage kernels;
+ * FASTVIM_FLAG_FUSED is ignored).  Masked layers -- whose conv runs along the
+ * kept tokens in the order given, r = k -- unpooled layers and layers with
+ * FASTVIM_FLAG_POST_NORM get x_conv written once into out first (in the I/O
+ * element type: bf16 layers round it to bf16), and the layer then runs on
+ * it, by the path it would take without the conv (the single launch
+ * included); fastvim_ssm_stage returns FASTVIM_ERR_UNSUPPORTED for them.
+ * Errors: FASTVIM_ERR_NULL (conv_w or conv_b NULL), FASTVIM_ERR_ALIGN (conv_w
+ * not 16-byte aligned, conv_b not 4-byte aligned). */
 #define FASTVIM_FLAG_CONV 8u
 #define FASTVIM_CONV_TAPS 4
 
@@ -406,16 +410,22 @@ size_t fastvim_ssm_export_bytes(const fastvim_dims *dims, int pool_axis, int wha
  * respect to the conv's output and da = dxc silu'(a),
  *   dx[r] = sum_k conv_w[k] da[r + 3 - k],  d conv_w[k] = sum_r da[r] x[r - 3 + k],
  *   d conv_b = sum_r da[r]
- * (per channel, along the oriented grid's sequence), written to
- * grads->conv_w and conv_b.  The first pass pools x_conv (unless saved_u is
+ * (per channel, along the oriented grid's sequence, or along the kept tokens
+ * of a masked layer), written to grads->conv_w and conv_b.  Dense layers
+ * without the LayerNorm: the first pass pools x_conv (unless saved_u is
  * given) and the second computes x_conv and da where it reads x, so neither
- * is written.
+ * is written.  Masked layers and the LayerNorm: x_conv is written into dz
+ * first, the layer's backward pass runs on it (reading each cell's x_conv
+ * before writing its dz) and leaves dL/dx_conv in dx, and the conv's adjoint
+ * then runs in place on dx, its scratch the workspace (bf16 layers round
+ * x_conv and dL/dx_conv to bf16 there).
  *
- * Supported: pooled layers (COLS or ROWS, dense or masked) with T <= 128 scan
- * steps and the limits of the forward call, with or without
+ * Supported: pooled layers (COLS or ROWS, dense or masked) whose scan has at
+ * most 720, 512, 384 or 288 steps at dt rank R <= 16, 32, 48 or 64 (the scan
+ * adjoint holds the sequence's x_proj rows in one workgroup's LDS), within
+ * the limits of the forward call, with or without
  * FASTVIM_FLAG_POST_NORM (then E <= 2048), FASTVIM_FLAG_POOL_SCALE,
- * FASTVIM_FLAG_LOCAL_BWD and FASTVIM_FLAG_CONV (dense layers, not with the
- * LayerNorm, as in the forward call), in any other combination;
+ * FASTVIM_FLAG_LOCAL_BWD and FASTVIM_FLAG_CONV, in any combination;
  * FASTVIM_ERR_UNSUPPORTED for unpooled layers, longer scans, the LayerNorm
  * with E > 2048, the cases the forward call does not take, and
  * FASTVIM_FLAG_FUSED (0 and FASTVIM_FLAG_STAGED run the same kernels). */

@@ -90,6 +90,19 @@ fastvim_params effective_params(const fastvim_params& p) {
     return q;
 }
 
+// With FASTVIM_FLAG_CONV, the layers whose stages cannot slide the conv
+// window where they read x get x_conv written out first (conv_seq.hip):
+// masked layers (the conv runs along the kept tokens), layers with the
+// post-SSM LayerNorm and unpooled layers.  Dense pooled layers without the
+// norm compute it in their pool and output stages (conv.hip).
+bool conv_written(const Geom& g, uint32_t flags) {
+    return (flags & FASTVIM_FLAG_CONV) && (g.masked || !g.pooled || (flags & FASTVIM_FLAG_POST_NORM));
+}
+
+// Scratch of the written-out conv's adjoint: the backward workspace past its
+// header, free once the layer's own backward pass has run.
+constexpr size_t kBwdHeaderBytes = 256;
+
 // FASTVIM_FLAG_POOL_SCALE: a finite factor, pooled layers only, into g.
 int apply_pool_scale(const fastvim_params& p, Geom* g) {
     if (!(p.flags & FASTVIM_FLAG_POOL_SCALE)) return FASTVIM_OK;
@@ -118,9 +131,6 @@ int validate(const void* x, const void* z, const fastvim_params* prm, const fast
     if ((st = resolve_geom(d, axis, g))) return st;
     g->tuning = prm->tuning;
     if ((st = apply_pool_scale(*prm, g))) return st;
-    if ((prm->flags & FASTVIM_FLAG_CONV) &&
-        (!g->pooled || g->masked || (prm->flags & FASTVIM_FLAG_POST_NORM)))
-        return FASTVIM_ERR_UNSUPPORTED;
     if (!g->masked && idx) return FASTVIM_ERR_ARG;
     if (prm->saved_u && !g->pooled) return FASTVIM_ERR_ARG;
     *empty = g->B == 0;
@@ -232,8 +242,13 @@ size_t export_bytes(const Geom& g, int what) {
 }
 
 // The backward pass covers the pooled layer (dense or masked), with scans of
-// at most kBwdTMax steps; with the post-SSM norm, E <= 2048 (bwd_norm.hip).
-bool bwd_supported(const Geom& g) { return g.pooled && g.T <= kBwdTMax; }
+// at most bwd_tmax(R) steps; with the post-SSM norm, E <= 2048 (bwd_norm.hip).
+bool bwd_supported(const Geom& g) { return g.pooled && g.T <= bwd_tmax(g.R); }
+
+int bwd_nchk(const Geom& g) {
+    const int64_t n = (g.T + 15) / 16;
+    return (int)(n > kBwdCkptMin ? n : kBwdCkptMin);
+}
 
 struct Span {
     const void* p;
@@ -260,7 +275,9 @@ int validate_bwd(const void* x, const void* z, const void* dout, const fastvim_p
     if (st) return st;
     if ((st = apply_pool_scale(*prm, g))) return st;
     if (!bwd_supported(*g) || (norm && !bwd_norm_supported(*g))) return FASTVIM_ERR_UNSUPPORTED;
-    if (conv && (g->masked || norm)) return FASTVIM_ERR_UNSUPPORTED;  // as the forward call
+    if (conv && (g->masked || norm) &&
+        !conv_adjoint_fits(*g, (int64_t)((bwd_workspace_layout(*g, nullptr, nullptr) - kBwdHeaderBytes) / 4)))
+        return FASTVIM_ERR_UNSUPPORTED;
     if (!g->masked && idx) return FASTVIM_ERR_ARG;
     if (!gr) return FASTVIM_ERR_NULL;
     if (conv) {
@@ -279,7 +296,7 @@ int validate_bwd(const void* x, const void* z, const void* dout, const fastvim_p
     const fastvim_dir_grads* gd[2] = {&gr->fwd, &gr->bwd};
     const size_t gsz[5] = {(size_t)(g->NX * g->E), (size_t)(g->E * g->R), (size_t)g->E, (size_t)(g->E * g->N),
                            (size_t)g->E};
-    Span gs[12];
+    Span gs[14];
     for (int k = 0; k < 2; ++k) {
         const float* ps[5] = {gd[k]->x_proj_w, gd[k]->dt_proj_w, gd[k]->dt_proj_b, gd[k]->A_log, gd[k]->D};
         for (int i = 0; i < 5; ++i) {
@@ -288,13 +305,14 @@ int validate_bwd(const void* x, const void* z, const void* dout, const fastvim_p
             gs[5 * k + i] = Span{ps[i], gsz[i] * sizeof(float)};
         }
     }
-    const int ngs = norm || conv ? 12 : 10;
+    int ngs = 10;
     if (norm) {
-        gs[10] = Span{gr->ln_weight, (size_t)g->E * sizeof(float)};
-        gs[11] = Span{gr->ln_bias, (size_t)g->E * sizeof(float)};
-    } else if (conv) {
-        gs[10] = Span{gr->conv_w, (size_t)(g->E * FASTVIM_CONV_TAPS) * sizeof(float)};
-        gs[11] = Span{gr->conv_b, (size_t)g->E * sizeof(float)};
+        gs[ngs++] = Span{gr->ln_weight, (size_t)g->E * sizeof(float)};
+        gs[ngs++] = Span{gr->ln_bias, (size_t)g->E * sizeof(float)};
+    }
+    if (conv) {
+        gs[ngs++] = Span{gr->conv_w, (size_t)(g->E * FASTVIM_CONV_TAPS) * sizeof(float)};
+        gs[ngs++] = Span{gr->conv_b, (size_t)g->E * sizeof(float)};
     }
     for (int i = 0; i < ngs; ++i)
         for (int j = i + 1; j < ngs; ++j)
@@ -315,7 +333,7 @@ int validate_bwd(const void* x, const void* z, const void* dout, const fastvim_p
     const size_t io = io_span(*g);
     // outputs (dx, dz, the workspace and every gradient) overlap neither each
     // other nor an input; parameters count as inputs
-    Span ins[16] = {{x, io}, {z, io}, {dout, io}};
+    Span ins[18] = {{x, io}, {z, io}, {dout, io}};
     int nin = 3;
     for (const fastvim_dir_params* pd : {&eff.fwd, &eff.bwd}) {
         const float* ps[5] = {pd->x_proj_w, pd->dt_proj_w, pd->dt_proj_b, pd->A_log, pd->D};
@@ -326,11 +344,12 @@ int validate_bwd(const void* x, const void* z, const void* dout, const fastvim_p
     if (norm) {
         ins[nin++] = Span{prm->ln_weight, (size_t)g->E * sizeof(float)};
         ins[nin++] = Span{prm->ln_bias, (size_t)g->E * sizeof(float)};
-    } else if (conv) {
+    }
+    if (conv) {
         ins[nin++] = Span{prm->conv_w, (size_t)(g->E * FASTVIM_CONV_TAPS) * sizeof(float)};
         ins[nin++] = Span{prm->conv_b, (size_t)g->E * sizeof(float)};
     }
-    Span outs[15] = {{dx, io}, {dz, io}, {prm->workspace, need}};
+    Span outs[17] = {{dx, io}, {dz, io}, {prm->workspace, need}};
     const int nout = 3 + ngs;
     for (int i = 0; i < ngs; ++i) outs[3 + i] = gs[i];
     for (int i = 0; i < nout; ++i) {
@@ -361,6 +380,21 @@ int run_bwd(const Geom& g, const void* x, const void* z, const void* dout, const
     const bool norm = (p.flags & FASTVIM_FLAG_POST_NORM) != 0;
     const bool local = (p.flags & FASTVIM_FLAG_LOCAL_BWD) != 0;  // p holds the effective parameters
     const bool conv = (p.flags & FASTVIM_FLAG_CONV) != 0;
+    if (conv_written(g, p.flags)) {
+        // x_conv into dz (the passes below read each cell's x before they
+        // write its dz), the layer's backward pass on it, which leaves
+        // dL/dx_conv in dx, then the conv's adjoint in place on dx, its scratch
+        // the workspace the layer's pass no longer needs
+        fastvim_params q = p;
+        q.flags &= ~FASTVIM_FLAG_CONV;
+        if (!ok(launch_conv_seq(g, x, p, dz, s))) return FASTVIM_ERR_HIP;
+        const int st = run_bwd(g, dz, z, dout, q, idx, dx, dz, gr, ws, s);
+        if (st) return st;
+        float* scratch = reinterpret_cast<float*>(reinterpret_cast<char*>(ws.fwd.sync) + kBwdHeaderBytes);
+        const int64_t floats = (int64_t)((bwd_workspace_layout(g, nullptr, nullptr) - kBwdHeaderBytes) / 4);
+        return ok(launch_conv_adjoint(g, x, dx, p, scratch, floats, gr.conv_w, gr.conv_b, s)) ? FASTVIM_OK
+                                                                                              : FASTVIM_ERR_HIP;
+    }
     if (!ok(launch_zero_sync(ws.fwd, kBwdStatusWords, s))) return FASTVIM_ERR_HIP;
     if (g.masked &&
         !ok(launch_mask_rows(g, idx, ws.fwd, (p.flags & FASTVIM_FLAG_CHECK_IDX) ? ws.fwd.sync + 1 : nullptr, s)))
@@ -394,7 +428,7 @@ int run_bwd(const Geom& g, const void* x, const void* z, const void* dout, const
         if (local && !ok(launch_scan(g, x, p, ws.fwd, s))) return FASTVIM_ERR_HIP;
     }
     BwdScanArgs a{ws.fwd.xdbl, ws.fwd.u, ws.gs, p.fwd, p.bwd, ws.fwd.s_f, ws.fwd.s_b, ws.du_f, ws.du_b, ws.dvp,
-                  ws.ckpt, ws.dAp, ws.dWdtp, ws.dbp, g.B, g.T, g.E, (int)g.R, (int)g.NX, (int)ws.G, local};
+                  ws.ckpt, ws.dAp, ws.dWdtp, ws.dbp, g.B, g.T, g.E, (int)g.R, (int)g.NX, (int)ws.G, local, ws.nchk};
     if (!ok(launch_scan_bwd(a, s)) || !ok(launch_bwd_dv(g, ws, s)) || !ok(launch_bwd_du(g, p, ws, s)) ||
         !ok(launch_bwd_dwx(g, ws, s)))
         return FASTVIM_ERR_HIP;
@@ -435,7 +469,7 @@ int run_bwd(const Geom& g, const void* x, const void* z, const void* dout, const
         // region (free once the scan adjoint has run; large enough: see
         // bwd_workspace_layout)
         const int64_t np = bwd_conv_parts(g);
-        const int64_t ckpt_floats = 2 * g.B * ws.G * (kBwdTMax / 16) * 256 * 4;
+        const int64_t ckpt_floats = 2 * g.B * ws.G * ws.nchk * 256 * 4;
         if (np * 6 * E > ckpt_floats) return FASTVIM_ERR_WORKSPACE;  // cannot happen with the sizes above
         if (!ok(launch_bwd_conv_epilogue(g, x, z, dout, p, ws.fwd.s_f, ws.fwd.s_b, ws.du, ws.ckpt, dx, dz, s)) ||
             !ok(launch_colsum(ws.ckpt, np, E, 6 * E, gr.fwd.D, gr.bwd.D, ws.tmp, s)) ||
@@ -482,6 +516,14 @@ int check_stage_dst(const Geom& g, const StageDst& d, const void* x, const void*
 // the stage kernels.
 int run_fwd(const Geom& g, const void* x, const void* z, const fastvim_params& prm, const int32_t* idx, void* out,
             const Workspace& ws, hipStream_t s) {
+    if (conv_written(g, prm.flags)) {
+        // x_conv into out, then the layer on it: every stage reads a cell's x
+        // before the output stage writes that cell
+        if (launch_conv_seq(g, x, prm, out, s) != hipSuccess) return FASTVIM_ERR_HIP;
+        fastvim_params q = prm;
+        q.flags &= ~FASTVIM_FLAG_CONV;
+        return run_fwd(g, out, z, q, idx, out, ws, s);
+    }
     if (launch_zero_sync(ws, sync_words(g), s) != hipSuccess) return FASTVIM_ERR_HIP;
     const fastvim_params q = effective_params(prm);
     const bool norm = (prm.flags & FASTVIM_FLAG_POST_NORM) != 0;
@@ -602,7 +644,7 @@ size_t bwd_workspace_layout(const Geom& g, void* base, BwdWorkspace* ws) {
     const size_t o_gs = take(bte), o_dDp = take((size_t)(ND * E) * sizeof(float));
     const size_t o_duf = take(bte), o_dub = take(bte), o_du = take(bte);
     const size_t o_dvp = take((size_t)(2 * B * G * T * S) * sizeof(float));
-    const size_t o_ck = take((size_t)(2 * B * G * (kBwdTMax / 16) * 256 * 4) * sizeof(float));
+    const size_t o_ck = take((size_t)(2 * B * G * bwd_nchk(g) * 256 * 4) * sizeof(float));
     const size_t o_dv = take((size_t)(M * 2 * NX) * sizeof(float));
     const size_t o_dAp = take((size_t)(2 * B * E * 16) * sizeof(float));
     const size_t o_dWdtp = take((size_t)(2 * B * E * R) * sizeof(float));
@@ -647,6 +689,7 @@ size_t bwd_workspace_layout(const Geom& g, void* base, BwdWorkspace* ws) {
         ws->S = S;
         ws->MC = MC;
         ws->tmp_floats = tmpf;
+        ws->nchk = bwd_nchk(g);
         ws->u_saved = false;
     }
     return off;
@@ -684,6 +727,7 @@ int fastvim_ssm_stage(int stage, const void* x, const void* z, const fastvim_par
     bool empty = false;
     int st = validate(x, z, params, dims, pool_axis, mask_idx, out, &g, &empty);
     if (st || empty) return st;
+    if (conv_written(g, params->flags)) return FASTVIM_ERR_UNSUPPORTED;  // its conv is a step of its own
     if ((st = bind_workspace(g, x, z, *params, out, &ws))) return st;
     return run_stage(stage, g, x, z, effective_params(*params), mask_idx, out, ws, static_cast<hipStream_t>(stream));
 }

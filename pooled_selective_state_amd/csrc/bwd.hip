@@ -434,14 +434,17 @@ __device__ __forceinline__ void row_vec1(const float* a, int64_t off, float (&r)
 // row (dense; its tokens are contiguous in memory) or one image's kept tokens
 // (masked).  Lane (c, g) handles the tokens p0 + g + G k, k < kU, all loads
 // issued first, and sums dL/dy * x over them; the G group sums are added
-// through LDS in a fixed order into the workgroup's row of dDp.
+// through LDS in a fixed order into the workgroup's row of dDp.  x and dz
+// may be one buffer (a layer with the producer Conv1D passes its conv output
+// in dz): each token's x is read before its dz is written, so those two
+// pointers carry no restrict.
 template <class IO, int MODE>
 __global__ void __launch_bounds__(1024)
-bwd_epilogue_kernel(const typename IO::elem* __restrict__ x, const typename IO::elem* __restrict__ z,
+bwd_epilogue_kernel(const typename IO::elem* x, const typename IO::elem* __restrict__ z,
                     const typename IO::elem* __restrict__ dout, const float* __restrict__ sf,
                     const float* __restrict__ sb, const float* __restrict__ du, const float* __restrict__ Df,
                     const float* __restrict__ Db, typename IO::elem* __restrict__ dx,
-                    typename IO::elem* __restrict__ dz, const int32_t* __restrict__ rows, float* __restrict__ dDp,
+                    typename IO::elem* dz, const int32_t* __restrict__ rows, float* __restrict__ dDp,
                     int64_t T, int64_t h, int64_t w, int64_t K, int64_t E, int VE, int G, int64_t seg_len,
                     int64_t blocks_per_seg, int64_t segs_per_img, float inv_p) {
     constexpr int V = IO::V;

@@ -6,7 +6,7 @@
 
 namespace fastvim {
 
-constexpr int kBwdTMax = 128;        // longest scan the backward kernels take (sequence rows held in LDS)
+constexpr int kBwdCkptMin = 8;       // checkpoint chunks reserved at least (the Conv1D pass reuses the region)
 constexpr int kBwdCh = 64;           // channels per scan-adjoint workgroup (one channel group)
 constexpr int kBwdTokChunk = 64;     // pooled tokens per partial of d x_proj_w
 constexpr int kColRowsPerBlock = 256;  // rows per first-stage block of a column sum
@@ -26,7 +26,7 @@ struct BwdWorkspace {
     float* du;     // (B, T, E) dL/du, both directions, scan and x_proj; with the LayerNorm first
                    //           the (b, t) partials of dD
     float* dvp;    // (2, B, G, T, S) channel-group partials of dL/dv, in the scan's LDS row layout
-    float* ckpt;   // (2, B, G, kBwdTMax / 16, 256, 4) scan adjoint: each lane's states entering each chunk
+    float* ckpt;   // (2, B, G, nchk, 256, 4) scan adjoint: each lane's states entering each chunk
     float* dv;     // (B, T, 2, NX) dL/dv of both directions
     float* dAp;    // (2, B, E, 16) per-image d A_log
     float* dWdtp;  // (2, B, E, R) per-image d dt_proj_w
@@ -34,6 +34,7 @@ struct BwdWorkspace {
     float* dWxp;   // (MC, 2, NX, E) per token chunk d x_proj_w
     float* tmp;    // first-stage sums of the column reductions
     int64_t G, S, MC, tmp_floats;
+    int nchk;      // checkpoint chunks per lane: max(ceil(T / 16), kBwdCkptMin)
     bool u_saved = false;  // fwd.u is the caller's saved pooled tokens (pass 1 does not pool x)
 };
 
@@ -45,14 +46,18 @@ struct BwdScanArgs {
     float *s_f, *s_b;     // (B, T, E) recomputed scan outputs
     float *du_f, *du_b;   // (B, T, E)
     float* dvp;           // (2, B, G, T, S)
-    float* ckpt;          // (2, B, G, kBwdTMax / 16, 256, 4)
+    float* ckpt;          // (2, B, G, nchk, 256, 4)
     float *dAp, *dWdtp, *dbp;
     int64_t B, T, E;
     int R, NX, G;
     bool local;  // direction 1 is the local backward scan (pb holds the forward parameters)
+    int nchk;    // checkpoint chunks per lane in ckpt
 };
 
 int bwd_rmax(int64_t R);  // the dt-rank bound (16, 32, 48, 64) whose kernel instance serves R
+// Longest scan the scan adjoint takes at dt rank R: the sequence's x_proj rows
+// and the flush buffer fit in one workgroup's LDS (720, 512, 384, 288 steps).
+int64_t bwd_tmax(int64_t R);
 // Second-pass workgroups (each a run of consecutive tokens of one grid row,
 // or of one image's kept tokens when masked): the rows of dDp.
 int64_t bwd_dd_parts(const Geom& g);
@@ -100,6 +105,17 @@ int64_t bwd_conv_parts(const Geom& g);
 hipError_t launch_bwd_conv_epilogue(const Geom& g, const void* x, const void* z, const void* dout,
                                     const fastvim_params& p, const float* sf, const float* sb, const float* du,
                                     float* parts, void* dx, void* dz, hipStream_t st);
+// The producer Conv1D written out (conv_seq.hip), for masked layers (along
+// the kept tokens), layers with the post-SSM LayerNorm and unpooled layers:
+// x_conv of the layer's sequence into xc (x's layout and element type); and
+// its adjoint in place -- dx holds dL/dx_conv on entry and dL/dx on exit --
+// with `floats` of scratch, the conv's weight and bias gradients into dcw,
+// dcb.  conv_adjoint_fits: the scratch is large enough.
+hipError_t launch_conv_seq(const Geom& g, const void* x, const fastvim_params& p, void* xc, hipStream_t st);
+hipError_t launch_conv_adjoint(const Geom& g, const void* x, void* dx, const fastvim_params& p, float* scratch,
+                               int64_t floats, float* dcw, float* dcb, hipStream_t st);
+bool conv_adjoint_fits(const Geom& g, int64_t floats);
+
 hipError_t launch_bwd_norm_pass1(const Geom& g, const void* x, const void* z, const void* dout,
                                  const fastvim_params& p, const BwdWorkspace& ws, void* dx, void* dz,
                                  hipStream_t st);

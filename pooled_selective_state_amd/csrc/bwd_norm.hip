@@ -56,14 +56,17 @@ __device__ __forceinline__ void team_reduce_out(const float (&acc)[NV][V], float
 // (mask_list.h); dense: cell p of the row or column, p < P.  LDS: the summed
 // scan row, D_fwd + D_bwd, ln_w, ln_b (E each) while the tokens are taken,
 // then kTeams rows of E for the team sums.
+// x and dz may be one buffer (a layer with the producer Conv1D passes its
+// conv output in dz): each cell's x is read before that cell's dz is written,
+// so those two pointers carry no restrict.
 template <class IO, int TL, int NV, bool MASKED>
 __global__ void __launch_bounds__(kNormBwdThreads)
-bwd_norm_pass1_kernel(const typename IO::elem* __restrict__ x, const typename IO::elem* __restrict__ z,
+bwd_norm_pass1_kernel(const typename IO::elem* x, const typename IO::elem* __restrict__ z,
                       const typename IO::elem* __restrict__ dout, const float* __restrict__ sf,
                       const float* __restrict__ sb, const float* __restrict__ Df, const float* __restrict__ Db,
                       const float* __restrict__ lnw, const float* __restrict__ lnb, float eps,
                       const int32_t* __restrict__ rows, typename IO::elem* __restrict__ gout,
-                      typename IO::elem* __restrict__ dz, float* __restrict__ gs, float* __restrict__ dDp,
+                      typename IO::elem* dz, float* __restrict__ gs, float* __restrict__ dDp,
                       float* __restrict__ dlnwp, float* __restrict__ dlnbp, int64_t T, int64_t h, int64_t w,
                       int64_t K, int64_t P, int cols_axis, int E) {
     constexpr int V = IO::V;

@@ -20,13 +20,10 @@
 // from the caches.  The kernels follow the pool and epilogue kernels
 // (pool.hip, epilogue.hip) otherwise.
 #include "bwd_internal.h"
+#include "conv_common.h"
 
 namespace fastvim {
 namespace {
-
-constexpr int kTaps = FASTVIM_CONV_TAPS;
-
-__device__ __forceinline__ float silu(float q) { return q * __builtin_amdgcn_rcpf(1.f + __expf(-q)); }
 
 // Token index within the image of the k-th predecessor (k >= 1) of grid cell
 // (i, j) in the oriented sequence, or -1 before the start of the sequence.
@@ -39,42 +36,6 @@ __device__ __forceinline__ int pred_token(int i, int j, int k, int h, int w) {
     if (i >= k) return (i - k) * w + j;
     const int r = j * h + i - k;  // column-major position; may lie several columns back when h < k
     return r < 0 ? -1 : (r % h) * w + r / h;
-}
-
-// Channel weights of the lane's V channels: taps (oldest first) and bias.
-template <int V>
-struct ConvW {
-    float w[V][kTaps], b[V];
-};
-template <int V>
-__device__ __forceinline__ void load_conv_w(const float* cw, const float* cb, int64_t col, ConvW<V>& W) {
-#pragma unroll
-    for (int v = 0; v < V; ++v) {
-        const f32x4 t = *reinterpret_cast<const f32x4*>(cw + (col + v) * kTaps);
-        W.w[v][0] = t.x;
-        W.w[v][1] = t.y;
-        W.w[v][2] = t.z;
-        W.w[v][3] = t.w;
-        W.b[v] = cb[col + v];
-    }
-}
-
-// x_conv for the lane's V channels from a window of raw vectors: the cell
-// (cur) and its three predecessors (p1 the newest); a predecessor before the
-// start of the sequence is a zero vector.
-template <class IO>
-__device__ __forceinline__ void conv_window(const typename IO::raw& p3, const typename IO::raw& p2,
-                                            const typename IO::raw& p1, const typename IO::raw& cur,
-                                            const ConvW<IO::V>& W, float (&xc)[IO::V]) {
-    static_assert(kTaps == 4, "window of three predecessors");
-#pragma unroll
-    for (int v = 0; v < IO::V; ++v) {
-        float a = fmaf(W.w[v][3], raw_at(cur, v), W.b[v]);
-        a = fmaf(W.w[v][2], raw_at(p1, v), a);
-        a = fmaf(W.w[v][1], raw_at(p2, v), a);
-        a = fmaf(W.w[v][0], raw_at(p3, v), a);
-        xc[v] = silu(a);
-    }
 }
 
 // The three predecessors of cell (i, j) (p1 the newest), zero before the start.
@@ -231,7 +192,7 @@ conv_epilogue_kernel(const typename IO::elem* __restrict__ x, const typename IO:
             w2 = w1;
             w1 = xr[m];
 #pragma unroll
-            for (int v = 0; v < V; ++v) o[v] = (sv[v] + dsum[v] * xc[v]) * silu(raw_at(zr[m], v));
+            for (int v = 0; v < V; ++v) o[v] = (sv[v] + dsum[v] * xc[v]) * conv_silu_f(raw_at(zr[m], v));
             store_vec<true>(ob + (off0 + m * cstr), o);
         }
     }
@@ -427,7 +388,7 @@ bwd_conv_epilogue_kernel(const typename IO::elem* __restrict__ x, const typename
                         a = fmaf(W.w[v][2], raw_at(xw[2], v), a);
                         a = fmaf(W.w[v][1], raw_at(xw[1], v), a);
                         a = fmaf(W.w[v][0], raw_at(xw[0], v), a);
-                        const float xc = silu(a);
+                        const float xc = conv_silu_f(a);
                         const float zv = raw_at(zR[0], v), dv = raw_at(oR[0], v);
                         const float sgz = __builtin_amdgcn_rcpf(1.f + __expf(-zv));
                         const float gv = dv * zv * sgz;

@@ -39,11 +39,14 @@ __device__ __forceinline__ void scan_sum(const float* sf, const float* sb, int64
     }
 }
 
+// x and out may be one buffer (a layer with the producer Conv1D written out
+// passes x_conv in out): each token's x is read before its out is written, so
+// those two pointers carry no restrict.
 template <class IO, int MODE>
 __global__ void __launch_bounds__(1024)
-epilogue_kernel(const typename IO::elem* __restrict__ x, const typename IO::elem* __restrict__ z,
+epilogue_kernel(const typename IO::elem* x, const typename IO::elem* __restrict__ z,
                 const float* __restrict__ sf, const float* __restrict__ sb, const float* __restrict__ Df,
-                const float* __restrict__ Db, typename IO::elem* __restrict__ out,
+                const float* __restrict__ Db, typename IO::elem* out,
                 const int32_t* __restrict__ rows, int64_t T, int64_t h, int64_t w, int64_t K, int64_t E, int VE,
                 int G, int64_t seg_len, int64_t blocks_per_seg, int64_t segs_per_img) {
     constexpr int V = IO::V;

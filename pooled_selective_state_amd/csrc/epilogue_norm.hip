@@ -10,12 +10,15 @@ namespace {
 enum { kModeCols = 0, kModeRows = 1, kModeNoneRow = 2, kModeNoneCol = 3, kModeMasked = 4 };
 constexpr int kNormThreads = 256;
 
+// x and out may be one buffer (a layer with the producer Conv1D written out
+// passes x_conv in out): each token's x is read before its out is written, so
+// those two pointers carry no restrict.
 template <class IO, int TL, int NV>
 __global__ void __launch_bounds__(kNormThreads)
-epilogue_norm_kernel(const typename IO::elem* __restrict__ x, const typename IO::elem* __restrict__ z,
+epilogue_norm_kernel(const typename IO::elem* x, const typename IO::elem* __restrict__ z,
                      const float* __restrict__ sf, const float* __restrict__ sb, const float* __restrict__ Df,
                      const float* __restrict__ Db, const float* __restrict__ lnw, const float* __restrict__ lnb,
-                     float eps, typename IO::elem* __restrict__ out, const int32_t* __restrict__ rows, int mode,
+                     float eps, typename IO::elem* out, const int32_t* __restrict__ rows, int mode,
                      int64_t ntok, int64_t T, int64_t h, int64_t w, int64_t K, int E) {
     using raw = typename IO::raw;
     constexpr int kTeams = kNormThreads / TL;

@@ -34,9 +34,13 @@
 // when it starts and waits only for items with smaller tickets, which were
 // taken by workgroups that had already started, so every wait ends whatever
 // the grid size or residency.  As a guard against a broken invariant a wait
-// also gives up after a bounded number of polls and raises a status bit; an
-// output item that sees the bit after its wait writes NaN over its block, so
-// a give-up shows in the result, not only in the status word.
+// also gives up after a bounded number of polls and raises a status bit; so
+// that a give-up shows in the result too, not only in the status word, a scan
+// item whose wait gave up writes NaN scan rows (the output items of its image
+// then compute NaN), and an output item whose wait gave up writes NaN over
+// its block.  The normal path pays nothing for this: the outcome of a wait is
+// known to the waiting thread and reaches the workgroup through the barrier
+// that follows the wait anyway.
 //
 // Publication without L2 write-backs: a producer stores its results with
 // agent-scope atomic stores (written through to the device-coherent level),
@@ -76,6 +80,7 @@ struct FusedArgs {
     float pool_norm;  // pool_scale / P
     unsigned* sync;  // [0] ticket, [1] status, [2, 2+B) rowsDone, [2+B, 2+2B) scanDone
     unsigned spin_limit;  // polls before a wait gives up
+    bool longseq;         // T above resident_tmax: the LONG instances
     int64_t B, h, w, E, T, P;
     int R, NX, axis;
     int nA, nS, nE, RG, RE, CJ, G, VE, KS;
@@ -93,31 +98,35 @@ union alignas(16) FusedSmem {
 };
 
 // Thread 0 only: poll until *cnt >= target (at most `limit` polls, then
-// raise status bit 0 and go on), then acquire at agent scope.
-__device__ __forceinline__ void wait_at_least(unsigned* cnt, unsigned target, unsigned* status, unsigned limit) {
+// raise status bit 0 and go on), then acquire at agent scope.  Returns true
+// if the wait gave up.
+__device__ __forceinline__ bool wait_at_least(unsigned* cnt, unsigned target, unsigned* status, unsigned limit) {
     unsigned spins = 0;
+    bool gave_up = false;
     while (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
         __builtin_amdgcn_s_sleep(2);
         if (++spins >= limit) {
             __hip_atomic_fetch_or(status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            gave_up = true;
             break;
         }
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    return gave_up;
 }
 
-// Output items: wait until image b's scans are done; true (for every thread)
-// if any wait of the launch gave up before that, the status word then being
-// set.  A give-up upstream of this image raised the bit before counting its
-// item done, so it is seen here.
-__device__ __forceinline__ bool wait_scans(const FusedArgs& a, int64_t b) {
-    __shared__ unsigned s_status;
-    if (threadIdx.x == 0) {
-        wait_at_least(&a.sync[2 + a.B + b], (unsigned)a.nS, &a.sync[1], a.spin_limit);
-        s_status = __hip_atomic_load(&a.sync[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & 1u;
-    }
+// All threads: thread 0 waits until *cnt >= target; true (for every thread)
+// if that wait gave up.
+__device__ __forceinline__ bool wait_item(unsigned* cnt, unsigned target, const FusedArgs& a) {
+    __shared__ unsigned s_gave_up;
+    if (threadIdx.x == 0) s_gave_up = wait_at_least(cnt, target, &a.sync[1], a.spin_limit) ? 1u : 0u;
     __syncthreads();
-    return s_status != 0u;
+    return s_gave_up != 0u;
+}
+
+// Output items: wait until image b's scans are done.
+__device__ __forceinline__ bool wait_scans(const FusedArgs& a, int64_t b) {
+    return wait_item(&a.sync[2 + a.B + b], (unsigned)a.nS, a);
 }
 
 // NaN over grid rows [i0, i0 + ni) x columns [j0, j0 + nj) of image b's out.
@@ -148,6 +157,20 @@ __device__ __forceinline__ void store_through(float* p, float v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// NaN over both scan outputs of image b, channels [e0, e0 + nch) (a scan item
+// whose wait gave up: the output items of the image then compute NaN there).
+__device__ void poison_scan_rows(const FusedArgs& a, int64_t b, int64_t e0, int nch) {
+    const float nanf_ = __builtin_nanf("");
+    const int64_t n = a.T * nch;
+    for (int64_t q = threadIdx.x; q < n; q += kFT) {
+        const int64_t t = q / nch, e = e0 + (q - t * nch);
+        if (e < a.E) {
+            store_through(a.s_f + (b * a.T + t) * a.E + e, nanf_);
+            store_through(a.s_b + (b * a.T + t) * a.E + e, nanf_);
+        }
+    }
+}
+
 __device__ __forceinline__ float silu(float q) { return q * __builtin_amdgcn_rcpf(1.f + __expf(-q)); }
 
 // ---------------------------------------------------------------- A items
@@ -167,12 +190,57 @@ __device__ void item_pool_proj(const FusedArgs& a, int64_t b, int k, float* lds)
     const int64_t p_stride = cols ? E : a.w * E;
     const float inv_p = a.pool_norm;
     const int NO = 2 * a.NX;
-    float* red = lds;                        // [G][E]
+    float* red = lds;                        // [G][E] (segments: [Gw][RG E], no larger)
     float* urow = lds + (int64_t)G * E;      // [RG][E]
     float* part = urow + (int64_t)a.RG * E;  // [RG][NO][KS]
 
     const int pstr = (int)p_stride;
-    for (int pos = 0; pos < npos; ++pos) {
+    const bool segment = !cols && a.RG > 1;
+    if (segment) {
+        // ROWS with RG adjacent scan positions (columns) per item: their
+        // tokens in one grid row are one contiguous segment of RG E elements;
+        // a group of RG VE lanes covers it and walks the grid rows (8 loads in
+        // flight per lane), so the pooling reads contiguous runs of RG tokens
+        // instead of one token per grid row, 196 KB apart at 2048^2
+        const int SW = a.RG * VE;  // lanes per segment
+        const int Gw = kFT / SW;   // groups, each a share of the grid rows
+        const int cw = tid % SW, gw = tid / SW;
+        if (gw < Gw && cw < npos * VE) {
+            const elem* base = x + b * a.h * a.w * E + t0 * E;
+            const int coff = cw * V;
+            float acc[V];
+#pragma unroll
+            for (int v = 0; v < V; ++v) acc[v] = 0.f;
+            int p = gw;
+            for (; p + 7 * Gw < P; p += 8 * Gw) {
+                raw r[8];
+#pragma unroll
+                for (int q = 0; q < 8; ++q) r[q] = load_raw<false>(base + (coff + (p + q * Gw) * pstr));
+#pragma unroll
+                for (int v = 0; v < V; ++v)
+                    acc[v] += ((raw_at(r[0], v) + raw_at(r[1], v)) + (raw_at(r[2], v) + raw_at(r[3], v))) +
+                              ((raw_at(r[4], v) + raw_at(r[5], v)) + (raw_at(r[6], v) + raw_at(r[7], v)));
+            }
+            for (; p < P; p += Gw) {
+                const raw r0 = load_raw<false>(base + (coff + p * pstr));
+#pragma unroll
+                for (int v = 0; v < V; ++v) acc[v] += raw_at(r0, v);
+            }
+#pragma unroll
+            for (int v = 0; v < V; ++v) red[gw * SW * V + coff + v] = acc[v];
+        }
+        __syncthreads();
+        // fixed-order sum of the groups; urow [RG][E] is the segment's layout
+        for (int q = tid; q < npos * E; q += kFT) {
+            float s = red[q];
+            for (int gg = 1; gg < Gw; ++gg) s += red[gg * SW * V + q];
+            s *= inv_p;
+            urow[q] = s;
+            store_through(a.u + (b * T + t0) * E + q, s);
+        }
+        __syncthreads();
+    }
+    for (int pos = 0; pos < (segment ? 0 : npos); ++pos) {
         const int64_t t = t0 + pos;
         if (g < G) {
             // wave-uniform base, 32-bit lane offsets (an image holds < 2^31 elements)
@@ -502,7 +570,9 @@ __device__ void item_epilogue_norm(const FusedArgs& a, int64_t b, int k, float* 
 }
 
 // ---------------------------------------------------------------- kernel
-template <class IO, bool COLS, int RMAX, bool NORM, bool LOCAL>
+// LONG: scans longer than resident_tmax<RMAX>() steps (their S items stage the
+// x_proj rows chunk by chunk).
+template <class IO, bool COLS, int RMAX, bool NORM, bool LOCAL, bool LONG>
 __global__ void __launch_bounds__(kFT) fused_layer_kernel(FusedArgs a) {
     __shared__ FusedSmem sm;
     __shared__ unsigned s_ticket;
@@ -527,12 +597,19 @@ __global__ void __launch_bounds__(kFT) fused_layer_kernel(FusedArgs a) {
     const int64_t bs = slot - a.LS;
     if (bs >= 0 && bs < a.B) {
         if (r < a.nS) {
-            if (threadIdx.x == 0) wait_at_least(&a.sync[2 + bs], (unsigned)a.nA, &a.sync[1], a.spin_limit);
-            __syncthreads();
+            const int64_t e0 = (int64_t)r * (LOCAL ? 2 : 1) * kScanCh;
+            if (wait_item(&a.sync[2 + bs], (unsigned)a.nA, a)) {
+                poison_scan_rows(a, bs, e0, (LOCAL ? 2 : 1) * kScanCh);
+                publish(&a.sync[2 + a.B + bs]);
+                return;
+            }
             __builtin_amdgcn_s_setprio(2);  // the scan is on the critical path of its image
             ScanArgs sa{a.xdbl, a.pf, a.pb, a.s_f, a.s_b, a.T, a.E, a.R, a.NX};
-            scan_tile_resident<RMAX, true, USrcPooled, LOCAL>(sa, USrcPooled{a.u, a.T, a.E}, bs,
-                                                              (int64_t)r * (LOCAL ? 2 : 1) * kScanCh, sm.scan);
+            if (LONG)  // the sequence's rows do not fit in LDS at once: one chunk at a time
+                scan_tile<RMAX, true, USrcPooled, LOCAL, false, false>(sa, USrcPooled{a.u, a.T, a.E}, bs, e0,
+                                                                       sm.scan.xs);
+            else
+                scan_tile_resident<RMAX, true, USrcPooled, LOCAL>(sa, USrcPooled{a.u, a.T, a.E}, bs, e0, sm.scan);
             __builtin_amdgcn_s_setprio(0);
             publish(&a.sync[2 + a.B + bs]);
             return;
@@ -554,9 +631,10 @@ __global__ void zero_sync_kernel(unsigned* sync, int64_t n) {
 // local: with LBMamba's local backward scan (not with the norm).
 bool plan(const Geom& g, FusedArgs* a, bool norm, bool local) {
     if (!g.pooled || g.masked || g.B < 1 || (norm && local)) return false;
-    // the scan items hold a whole sequence's x_proj rows in LDS
+    // the scan items hold a whole sequence's x_proj rows in LDS when they fit,
+    // else one chunk of them at a time
     const int64_t tmax = g.R <= 16 ? resident_tmax<16>() : g.R <= 32 ? resident_tmax<32>() : resident_tmax<64>();
-    if (g.T > tmax) return false;
+    a->longseq = g.T > tmax;
     if (g.h * g.w * g.E >= ((int64_t)1 << 31)) return false;  // 32-bit offsets within an image
     const int V = g.io == FASTVIM_BF16 ? 8 : 4;
     const int64_t esz = g.io == FASTVIM_BF16 ? 2 : 4;
@@ -571,6 +649,17 @@ bool plan(const Geom& g, FusedArgs* a, bool norm, bool local) {
     const int64_t pos_bytes = g.P * g.E * esz;
     int64_t RG = (200 * 1024) / (pos_bytes > 0 ? pos_bytes : 1);
     RG = RG < 1 ? 1 : (RG > 8 ? 8 : RG);
+    if (g.axis == FASTVIM_POOL_ROWS) {
+        // ROWS: a position's tokens lie one per grid row; RG adjacent columns
+        // make each grid row's read one contiguous segment of about 3 KB
+        // (measured at 2048^2: RG = 2 in fp32, 1.98 against 2.11 ms with one
+        // column; RG = 4 in bf16, 1.22 against 1.32 ms; 5 columns in fp32,
+        // 2.15 ms), as many lanes as the workgroup has
+        const int64_t tok = g.E * esz;
+        RG = (3072 + tok / 2) / tok;
+        if (RG * VE > kFT) RG = kFT / VE;
+        RG = RG < 1 ? 1 : (RG > 8 ? 8 : RG);
+    }
     if (RG > g.T) RG = g.T;
     while (RG > 1 && G * g.E + RG * g.E + RG * NO * KS > kLdsFloats) --RG;
     if (G * g.E + RG * g.E + RG * NO * KS > kLdsFloats) return false;
@@ -640,15 +729,21 @@ bool plan(const Geom& g, FusedArgs* a, bool norm, bool local) {
     return a->niv > 0 && a->total < (int64_t)UINT32_MAX;
 }
 
+template <class IO, int RMAX, bool NORM, bool LOCAL, bool LONG>
+hipError_t fused_launch_l(const FusedArgs& a, hipStream_t st) {
+    if (a.axis == FASTVIM_POOL_COLS)
+        hipLaunchKernelGGL((fused_layer_kernel<IO, true, RMAX, NORM, LOCAL, LONG>), dim3((unsigned)a.total), dim3(kFT),
+                           0, st, a);
+    else
+        hipLaunchKernelGGL((fused_layer_kernel<IO, false, RMAX, NORM, LOCAL, LONG>), dim3((unsigned)a.total),
+                           dim3(kFT), 0, st, a);
+    return hipGetLastError();
+}
+
 template <class IO, int RMAX, bool NORM, bool LOCAL>
 hipError_t fused_launch_n(const FusedArgs& a, hipStream_t st) {
-    if (a.axis == FASTVIM_POOL_COLS)
-        hipLaunchKernelGGL((fused_layer_kernel<IO, true, RMAX, NORM, LOCAL>), dim3((unsigned)a.total), dim3(kFT), 0,
-                           st, a);
-    else
-        hipLaunchKernelGGL((fused_layer_kernel<IO, false, RMAX, NORM, LOCAL>), dim3((unsigned)a.total), dim3(kFT), 0,
-                           st, a);
-    return hipGetLastError();
+    return a.longseq ? fused_launch_l<IO, RMAX, NORM, LOCAL, true>(a, st)
+                     : fused_launch_l<IO, RMAX, NORM, LOCAL, false>(a, st);
 }
 
 template <class IO, int RMAX>

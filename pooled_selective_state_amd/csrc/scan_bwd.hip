@@ -20,7 +20,9 @@
 // One 256-thread workgroup takes (image b, channel group g, direction d),
 // with the lane layout of the forward scan: 4 lanes per channel, lane q
 // holding the states n = 4q .. 4q + 3.  All x_proj rows of the sequence are
-// staged in LDS once (the forward scan's row layout, zero-filled past T); a
+// staged in LDS once (the forward scan's row layout, zero-filled past T; in
+// dynamic LDS, so the longest sequence is the one whose rows and the flush
+// buffer fit in a workgroup's 160 KB: bwd_tmax); a
 // lane loads the token values u and adjoint inputs gs of its own steps
 // q + 4j one chunk ahead of their use.  Then:
 //   1. a forward sweep (the forward scan's own chunk code) recomputes the
@@ -62,7 +64,7 @@ namespace {
 constexpr int kBwdThreads = 256;                   // one direction: 64 channels x 4 lanes
 constexpr int kBwdFlush = 8;                       // steps per flush of the channel sums
 constexpr int kBwdRows = kBwdThreads / 16;         // DPP rows of 16 lanes per workgroup
-constexpr int kBwdCM = kBwdTMax / kChunk;          // chunks at most (8)
+constexpr int kLdsBytes = 160 * 1024;             // LDS of one workgroup on gfx950
 static_assert(kBwdThreads / kLps == kScanCh && kScanCh == kBwdCh, "a workgroup covers one channel group");
 static_assert(kChunk % kBwdFlush == 0, "whole flushes per chunk");
 static_assert(kChunk == FASTVIM_LOCAL_WINDOW, "the local scan's windows are the chunks");
@@ -96,14 +98,17 @@ __device__ __forceinline__ void recompute_step(float (&hs)[kNs], const float* ro
     for (int n = 0; n < kNs; ++n) hs[n] = fmaf(__builtin_amdgcn_exp2f(dlt * A2[n]), hs[n], du * bt[n]);
 }
 
+template <int RMAX>
+constexpr int red_floats() { return kBwdFlush * kBwdRows * row_stride_lds<RMAX>(); }
+
 template <int RMAX, bool LOCAL>
 __global__ void __launch_bounds__(kBwdThreads) scan_bwd_kernel(BwdScanArgs a) {
     constexpr int S = row_stride_lds<RMAX>();
     constexpr int kWQ = RMAX / 4;
     constexpr int kPre = (S + 15) / 16;          // row positions per lane (16 lanes per row)
-    constexpr int kPasses = kBwdTMax / 16;       // 16 rows per pass
-    __shared__ __attribute__((aligned(16))) float rows[kBwdTMax * S];
-    __shared__ __attribute__((aligned(16))) float red[kBwdFlush * kBwdRows * S];
+    constexpr int kPasses = 8;                   // 16 rows per pass, staged 8 passes at a time
+    extern __shared__ __attribute__((aligned(16))) float rows[];  // [16 ceil(T / 16)][S]
+    __shared__ __attribute__((aligned(16))) float red[red_floats<RMAX>()];
 
     const int tid = threadIdx.x;
     const int dir = blockIdx.y;
@@ -153,22 +158,27 @@ __global__ void __launch_bounds__(kBwdThreads) scan_bwd_kernel(BwdScanArgs a) {
         int scol[kPre];
 #pragma unroll
         for (int i = 0; i < kPre; ++i) scol[i] = po + 16 * i < S ? lds_source_col<RMAX>(po + 16 * i, R) : -1;
-        float stage[kPasses][kPre];
+        // 8 passes of 16 rows in flight at a time (all of a sequence up to 128 steps)
+#pragma unroll 1
+        for (int base = 0; base < nrow; base += 16 * kPasses) {
+            float stage[kPasses][kPre];
 #pragma unroll
-        for (int ps = 0; ps < kPasses; ++ps) {
-            const int ti = prow + 16 * ps;
-            const int t = time_of(ti);
-            const bool real = t >= 0 && t < T;
-#pragma unroll
-            for (int i = 0; i < kPre; ++i) stage[ps][i] = (real && scol[i] >= 0) ? xb[2 * t * NX + scol[i]] : 0.f;
-        }
-#pragma unroll
-        for (int ps = 0; ps < kPasses; ++ps) {
-            const int ti = prow + 16 * ps;
-            if (ti < nrow) {
+            for (int ps = 0; ps < kPasses; ++ps) {
+                const int ti = base + prow + 16 * ps;
+                const int t = time_of(ti);
+                const bool real = t >= 0 && t < T;
 #pragma unroll
                 for (int i = 0; i < kPre; ++i)
-                    if (po + 16 * i < S) rows[ti * S + po + 16 * i] = stage[ps][i];
+                    stage[ps][i] = (real && scol[i] >= 0) ? xb[2 * t * NX + scol[i]] : 0.f;
+            }
+#pragma unroll
+            for (int ps = 0; ps < kPasses; ++ps) {
+                const int ti = base + prow + 16 * ps;
+                if (ti < nrow) {
+#pragma unroll
+                    for (int i = 0; i < kPre; ++i)
+                        if (po + 16 * i < S) rows[ti * S + po + 16 * i] = stage[ps][i];
+                }
             }
         }
     }
@@ -186,7 +196,7 @@ __global__ void __launch_bounds__(kBwdThreads) scan_bwd_kernel(BwdScanArgs a) {
     };
     // The lane's states entering chunk c, written by the forward sweep and
     // read back by the reverse sweep (its own region of the workspace).
-    float* ck = a.ckpt + (((int64_t)dir * a.B + b) * a.G + gi) * kBwdCM * kBwdThreads * 4 + tid * 4;
+    float* ck = a.ckpt + (((int64_t)dir * a.B + b) * a.G + gi) * a.nchk * kBwdThreads * 4 + tid * 4;
     float un[kJ];
     load_steps(ub, 0, un);
     __syncthreads();
@@ -396,19 +406,43 @@ __global__ void __launch_bounds__(kBwdThreads) scan_bwd_kernel(BwdScanArgs a) {
 }
 
 template <int RMAX>
-hipError_t scan_bwd_launch(const BwdScanArgs& a, hipStream_t st) {
-    if (a.local)
-        hipLaunchKernelGGL((scan_bwd_kernel<RMAX, true>), dim3((unsigned)(a.B * a.G), 2), dim3(kBwdThreads), 0, st,
-                           a);
-    else
-        hipLaunchKernelGGL((scan_bwd_kernel<RMAX, false>), dim3((unsigned)(a.B * a.G), 2), dim3(kBwdThreads), 0, st,
-                           a);
+size_t rows_bytes(int64_t T) {
+    return (size_t)((T + kChunk - 1) / kChunk * kChunk) * row_stride_lds<RMAX>() * sizeof(float);
+}
+
+template <int RMAX, bool LOCAL>
+hipError_t scan_bwd_launch_l(const BwdScanArgs& a, hipStream_t st) {
+    const size_t lds = rows_bytes<RMAX>(a.T);
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&scan_bwd_kernel<RMAX, LOCAL>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((scan_bwd_kernel<RMAX, LOCAL>), dim3((unsigned)(a.B * a.G), 2), dim3(kBwdThreads), lds, st, a);
     return hipGetLastError();
+}
+
+template <int RMAX>
+hipError_t scan_bwd_launch(const BwdScanArgs& a, hipStream_t st) {
+    return a.local ? scan_bwd_launch_l<RMAX, true>(a, st) : scan_bwd_launch_l<RMAX, false>(a, st);
+}
+
+template <int RMAX>
+int64_t tmax_for() {
+    const int64_t per_row = row_stride_lds<RMAX>() * (int64_t)sizeof(float);
+    return (kLdsBytes - red_floats<RMAX>() * (int64_t)sizeof(float)) / per_row / kChunk * kChunk;
 }
 
 }  // namespace
 
 int bwd_rmax(int64_t R) { return R <= 16 ? 16 : R <= 32 ? 32 : R <= 48 ? 48 : 64; }
+
+int64_t bwd_tmax(int64_t R) {
+    switch (bwd_rmax(R)) {
+        case 16: return tmax_for<16>();
+        case 32: return tmax_for<32>();
+        case 48: return tmax_for<48>();
+        default: return tmax_for<64>();
+    }
+}
 
 hipError_t launch_scan_bwd(const BwdScanArgs& a, hipStream_t st) {
     switch (bwd_rmax(a.R)) {

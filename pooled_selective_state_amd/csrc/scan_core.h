@@ -33,6 +33,11 @@
 //      from lane s mod 4 of the quad by a quad broadcast, B_t and C_t from LDS,
 //      and lane 0 of the sequence stores s_t.  Broadcasts and the reduction
 //      over the sequence's lanes are DPP lane moves, with no LDS round trip.
+// Phase 3 runs on the VALU (scan_step_preact) or, in the standalone scan
+// kernel, on the matrix cores (scan_step_preact_mfma): the chunk's 16 steps x
+// the wave's 16 channels of pre-activations are one (16 x RMAX) . (RMAX x 16)
+// product, RMAX / 4 v_mfma_f32_16x16x4f32 steps per wave and chunk instead of
+// 16 dot products of RMAX / 4 terms, two quad sums and a select per lane.
 // Two ways to fill the LDS rows:
 //   scan_tile           any length: one chunk of rows at a time, the next
 //                       chunk's rows loaded into registers while the current
@@ -167,6 +172,9 @@ struct ScanArgs {
 // Per-lane state of one sequence: decay rates, the lane's states, its quarter
 // of the dt_proj row, the bias, and where its outputs go: quad lane q stores
 // the outputs of the steps q + 4j, at sq + (traversal step) * sstep.
+// wq: VALU phase 3, the lane's quarter of its dt_proj row (r = q + 4i);
+// MFMA phase 3, the lane's B operand: wq[i] = dt_proj_w[c][4i + lane / 16]
+// for channel c = the wave's first + lane % 16.
 template <int RMAX>
 struct ScanLane {
     static constexpr int kWQ = RMAX / 4;
@@ -180,7 +188,7 @@ struct ScanLane {
 
 // LOCAL: every lane scans forward (with kScanThreads / 2 lanes a workgroup
 // covers the kScanCh channels [e0, e0 + 64); with more, the next 64).
-template <int RMAX, bool LOCAL = false>
+template <int RMAX, bool LOCAL = false, bool MFMA = false>
 __device__ __forceinline__ void scan_lane_setup(const ScanArgs& a, int64_t b, int64_t e0, ScanLane<RMAX>& L,
                                                 int64_t& ec) {
     static_assert(RMAX % 16 == 0 && RMAX <= kRMax, "dt rank bound: 16-byte aligned rows and lane quarters");
@@ -200,13 +208,26 @@ __device__ __forceinline__ void scan_lane_setup(const ScanArgs& a, int64_t b, in
         L.A2[n] = -expf(p.A_log[ec * 16 + kNs * L.l + n]) * kLog2e;
         L.hs[n] = 0.f;
     }
-    // this lane's quarter of the dt_proj row: r = q + 4i, zero past R (the
-    // step-size phase then reads every r < RMAX of a row unconditionally:
-    // still inside the row, whose stride is RMAX + 32)
+    if (MFMA) {
+        // B operand of the wave's product: channel (wave's first) + lane % 16,
+        // r = 4i + lane / 16, zero past R (and a valid row past E)
+        const int lane = tid & 63;
+        int64_t eb = e0 + (((tid & 255) >> 6) << 4) + (lane & 15) + (LOCAL ? kScanCh * (tid >> 8) : 0);
+        eb = eb < a.E ? eb : a.E - 1;
 #pragma unroll
-    for (int i = 0; i < ScanLane<RMAX>::kWQ; ++i) {
-        const int r = L.q + 4 * i;
-        L.wq[i] = r < R ? p.dt_proj_w[ec * R + r] : 0.f;
+        for (int i = 0; i < ScanLane<RMAX>::kWQ; ++i) {
+            const int r = 4 * i + (lane >> 4);
+            L.wq[i] = r < R ? p.dt_proj_w[eb * R + r] : 0.f;
+        }
+    } else {
+        // this lane's quarter of the dt_proj row: r = q + 4i, zero past R (the
+        // step-size phase then reads every r < RMAX of a row unconditionally:
+        // still inside the row, whose stride is RMAX + 32)
+#pragma unroll
+        for (int i = 0; i < ScanLane<RMAX>::kWQ; ++i) {
+            const int r = L.q + 4 * i;
+            L.wq[i] = r < R ? p.dt_proj_w[ec * R + r] : 0.f;
+        }
     }
     L.bias = p.dt_proj_b[ec];
     // traversal step ti is t = ti forward, t = T - 1 - ti backward
@@ -247,6 +268,44 @@ __device__ __forceinline__ void scan_step_preact(const ScanLane<RMAX>& L, const 
     }
 }
 
+// Phase 3 on the matrix cores, for the wave's 16 channels and the chunk's 16
+// steps: A[m][k] = low-rank input r = k0 + k of step m, read from the LDS rows
+// (lane l supplies step l % 16, r = 4i + l / 16: with the row layout above
+// that is position (l / 16) * RMAX/4 + i, so 4 consecutive i are one 16-byte
+// read), B[k][n] = dt_proj_w[channel n][r] (the lane's wq).  Accumulator
+// register i of lane l then holds step 4 (l / 16) + i of channel l % 16; it
+// goes through the wave's 256 floats of LDS at qs ([channel][step]) to the
+// lanes that scan those steps (lane 4c + q takes channel c's steps q + 4j).
+// Two accumulators halve the chain of dependent MFMAs.  LDS operations of a
+// wave complete in order, so the wave reads back what it wrote.
+template <int RMAX>
+__device__ __forceinline__ void scan_step_preact_mfma(const ScanLane<RMAX>& L, const float* dr, float* qs,
+                                                      float (&qv)[kJ]) {
+    constexpr int S = row_stride_lds<RMAX>();
+    constexpr int kWQ = ScanLane<RMAX>::kWQ;
+    static_assert(kWQ % 4 == 0, "k-steps in groups of 4");
+    const int lane = threadIdx.x & 63;
+    const float* arow = dr + (lane & 15) * S + (lane >> 4) * kWQ;
+    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < kWQ; i += 4) {
+        const f32x4 av = *reinterpret_cast<const f32x4*>(arow + i);
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(av.x, L.wq[i], acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(av.y, L.wq[i + 1], acc1, 0, 0, 0);
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(av.z, L.wq[i + 2], acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(av.w, L.wq[i + 3], acc1, 0, 0, 0);
+    }
+    f32x4 acc;
+    acc.x = acc0.x + acc1.x;
+    acc.y = acc0.y + acc1.y;
+    acc.z = acc0.z + acc1.z;
+    acc.w = acc0.w + acc1.w;
+    *reinterpret_cast<f32x4*>(qs + (lane & 15) * 16 + 4 * (lane >> 4)) = acc;
+    const float* mine = qs + (lane >> 2) * 16 + (lane & 3);
+#pragma unroll
+    for (int j = 0; j < kJ; ++j) qv[j] = mine[4 * j] + L.bias;
+}
+
 // Phases 3 and 4 of one chunk.  dr: this direction's LDS row of the chunk's
 // local step 0; ucur: token values of the lane's steps q + 4j; base:
 // traversal index of local step 0.
@@ -258,9 +317,10 @@ __device__ __forceinline__ void scan_step_preact(const ScanLane<RMAX>& L, const 
 // registers (64 more per lane) and the local scan needs no exponential;
 // otherwise it keeps the step sizes and recomputes them (where occupancy
 // matters more than the exponentials).  Neither needs a second step-size pass.
-template <int RMAX, bool WRITE_THROUGH, bool LOCAL = false, bool KEEP_DECAYS = true>
+// qs (MFMA phase 3 only): the wave's 256 floats of LDS.
+template <int RMAX, bool WRITE_THROUGH, bool LOCAL = false, bool KEEP_DECAYS = true, bool MFMA = false>
 __device__ __forceinline__ void scan_chunk(const ScanArgs& a, ScanLane<RMAX>& L, const float* dr,
-                                           const float (&ucur)[kJ], int64_t base) {
+                                           const float (&ucur)[kJ], int64_t base, float* qs = nullptr) {
     constexpr int S = row_stride_lds<RMAX>();
     constexpr bool kKeep = LOCAL && KEEP_DECAYS;
     const int64_t T = a.T;
@@ -268,7 +328,8 @@ __device__ __forceinline__ void scan_chunk(const ScanArgs& a, ScanLane<RMAX>& L,
     float aS[kKeep ? kChunk : 1][kNs];  // decays of the chunk's steps (LOCAL, KEEP_DECAYS)
     {
         float qv[kJ];
-        scan_step_preact<RMAX>(L, dr, qv);
+        if (MFMA) scan_step_preact_mfma<RMAX>(L, dr, qs, qv);
+        else scan_step_preact<RMAX>(L, dr, qv);
 #pragma unroll
         for (int j = 0; j < kJ; ++j) {
             const bool in = base + L.q + 4 * j < T;
@@ -370,22 +431,25 @@ __device__ __forceinline__ void scan_chunk(const ScanArgs& a, ScanLane<RMAX>& L,
 }
 
 // Scan channels [e0, e0 + kScanCh) of image b in both directions, any T, with
-// chunk_lds_floats<RMAX>() floats of LDS at xs.  All 512 threads of the
-// workgroup must call it (it synchronises the workgroup).
+// chunk_lds_floats<RMAX>() floats of LDS at xs, and (MFMA phase 3) 256 floats
+// per wave at qs.  All threads of the workgroup must call it (it synchronises
+// the workgroup).
 // With WRITE_THROUGH the outputs are stored with agent-scope atomic stores
 // (written through to the device-coherent level), for consumers on other XCDs
 // that synchronise without an L2 write-back.  RMAX bounds the dt rank R.
 template <int RMAX>
 constexpr int chunk_lds_floats() { return 2 * kChunk * row_stride_lds<RMAX>(); }
 
-template <int RMAX, bool WRITE_THROUGH, class USrc, bool LOCAL = false>
+// KEEP_DECAYS as scan_chunk (LOCAL only).
+template <int RMAX, bool WRITE_THROUGH, class USrc, bool LOCAL = false, bool MFMA = false, bool KEEP_DECAYS = true>
 __device__ __forceinline__ void scan_tile(const ScanArgs& a, const USrc& usrc, int64_t b, int64_t e0,
-                                          float* xs /* chunk_lds_floats<RMAX>() */) {
+                                          float* xs /* chunk_lds_floats<RMAX>() */, float* qs = nullptr) {
     constexpr int S = row_stride_lds<RMAX>();
     constexpr int kPre = row_loads<RMAX>();
     ScanLane<RMAX> L;
     int64_t ec;
-    scan_lane_setup<RMAX, LOCAL>(a, b, e0, L, ec);
+    scan_lane_setup<RMAX, LOCAL, MFMA>(a, b, e0, L, ec);
+    float* wqs = MFMA ? qs + (threadIdx.x >> 6) * 256 : nullptr;
     const int tid = threadIdx.x;
     const int NX = a.NX;
     const int64_t T = a.T;
@@ -427,7 +491,7 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, const USrc& usrc, i
         for (int j = 0; j < kJ; ++j) ucur[j] = pre_u[j];
         __syncthreads();
         if (c + 1 < nchunks) prefetch(base + kChunk);
-        scan_chunk<RMAX, WRITE_THROUGH, LOCAL>(a, L, xs + L.dir * kChunk * S, ucur, base);
+        scan_chunk<RMAX, WRITE_THROUGH, LOCAL, KEEP_DECAYS, MFMA>(a, L, xs + L.dir * kChunk * S, ucur, base, wqs);
     }
 }
 

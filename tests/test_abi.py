@@ -394,8 +394,11 @@ def test_bwd_workspace_bytes():
     d = P.make_dims(2, 4, 5, 16, 16, 4)
     assert P.bwd_workspace_bytes(d, P.POOL_COLS) > P.workspace_bytes(d, P.POOL_COLS) > 0
     assert P.bwd_workspace_bytes(d, P.POOL_NONE_ROWMAJOR) == 0  # unpooled: no backward pass
-    assert P.bwd_workspace_bytes(P.make_dims(2, 129, 4, 16), P.POOL_COLS) == 0  # scan of 129 steps
-    assert P.bwd_workspace_bytes(P.make_dims(2, 129, 4, 16), P.POOL_ROWS) > 0   # ... but 4 steps over columns
+    assert P.bwd_workspace_bytes(P.make_dims(2, 721, 4, 16), P.POOL_COLS) == 0  # scan of 721 steps
+    assert P.bwd_workspace_bytes(P.make_dims(2, 721, 4, 16), P.POOL_ROWS) > 0   # ... but 4 steps over columns
+    # scans longer than 128 steps: the checkpoint region grows with T
+    small, big = (P.bwd_workspace_bytes(P.make_dims(2, h, 4, 16), P.POOL_COLS) for h in (128, 720))
+    assert big > small > 0
     assert P.bwd_workspace_bytes(P.make_dims(2, 4, 5, 16, 8), P.POOL_COLS) == 0  # N != 16
 
 
@@ -428,7 +431,8 @@ def test_bwd_null_pointers():
 def test_bwd_unsupported_and_bad_flags():
     for axis in (P.POOL_NONE_ROWMAJOR, P.POOL_NONE_COLMAJOR):
         assert FakeBwd(axis=axis).bwd() == EUNSUP
-    assert FakeBwd(h=129).bwd() == EUNSUP
+    assert FakeBwd(h=721, R=12).bwd() == EUNSUP  # longer than the scan adjoint's LDS holds (720 at rank 16)
+    assert FakeBwd(h=513, R=20).bwd() == EUNSUP  # 512 at rank 32
     assert FakeBwd(N=8).bwd() == EUNSUP
     for flags, code in ((P.FLAG_FUSED, EUNSUP), (128, EARG),
                         (P.FLAG_STAGED, OK)):
@@ -556,8 +560,9 @@ def _conv_bwd(**kw):
 
 def test_bwd_conv_validation():
     """The Conv1D's parameters and gradient buffers of a backward call are
-    checked before any launch; masked layers and the LayerNorm are not
-    supported with it, as in the forward call."""
+    checked before any launch, also with masked layers and the LayerNorm
+    (whose conv is written out), where the two gradient pairs must not
+    overlap either."""
     for attr in ("conv_w", "conv_b"):
         c = _conv_bwd()
         setattr(c.params, attr, None)
@@ -580,10 +585,15 @@ def test_bwd_conv_validation():
     c = _conv_bwd()
     c.grads.conv_b = c.dx + 32
     assert c.bwd() == EOVERLAP
-    assert _conv_bwd(K=3).bwd() == EUNSUP
+    c = _conv_bwd(K=3)
+    c.grads.conv_b += 2
+    assert c.bwd() == EALIGN
     c = _conv_bwd()
     c.params.flags |= P.FLAG_POST_NORM
-    assert c.bwd() == EUNSUP
+    far = 1 << 45
+    c.params.ln_weight, c.params.ln_bias, c.params.ln_eps = far, far + 65536, 1e-5
+    c.grads.ln_weight, c.grads.ln_bias = far + 2 * 65536, c.grads.conv_w + 8  # over the conv's gradient
+    assert c.bwd() == EOVERLAP
     c = _conv_bwd()
     c.params.workspace_bytes -= 1
     assert c.bwd() == EWS  # past every other check
@@ -648,16 +658,25 @@ def test_conv_validation():
         c.params.flags = P.FLAG_CONV
         c.params.conv_w, c.params.conv_b = cw, cb
         expect(c, code)
+    # masked, unpooled and LayerNorm layers take the conv (written out first);
+    # their other arguments are still checked
     for kw, axis in ((dict(K=3), P.POOL_COLS), (dict(), P.POOL_NONE_ROWMAJOR), (dict(), P.POOL_NONE_COLMAJOR)):
         c = FakeCall(axis=axis, **kw)
         c.params.flags = P.FLAG_CONV
-        c.params.conv_w, c.params.conv_b = base, base
-        expect(c, EUNSUP)
+        c.params.conv_w, c.params.conv_b = base + 4, base
+        expect(c, EALIGN)
     c = FakeCall()
     c.params.flags = P.FLAG_CONV | P.FLAG_POST_NORM
     c.params.conv_w = c.params.conv_b = c.params.ln_weight = c.params.ln_bias = base
     c.params.ln_eps = 1e-5
-    expect(c, EUNSUP)
+    c.params.workspace_bytes -= 1
+    expect(c, EWS)
+    c = FakeCall(K=3)
+    c.params.flags = P.FLAG_CONV
+    c.params.conv_w, c.params.conv_b = base, base
+    lib = P.lib()
+    assert lib.fastvim_ssm_stage(P.STAGE_POOL, c.x, c.z, ctypes.byref(c.params), ctypes.byref(c.dims), c.axis,
+                                 c.idx, c.out, None) == EUNSUP  # the written-out conv is a step of its own
     c = FakeBwd()
     c.params.flags = P.FLAG_CONV
     assert c.bwd() == ENULL  # the backward pass takes the conv, and needs its parameters

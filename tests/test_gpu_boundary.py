@@ -10,9 +10,8 @@
   out-of-range mask index (forward and backward), nothing without the flag
   or with valid indices; a single launch whose waits are made to give up
   after one poll (FASTVIM_TUNING_POLL1, set from the host: every kernel still
-  finishes) reports FASTVIM_ERR_DEVICE_WAIT and writes NaN over exactly the
-  output blocks that followed a failed wait, the other blocks equal to a
-  normal call's;
+  finishes) reports FASTVIM_ERR_DEVICE_WAIT, and every output element is NaN
+  (it followed a failed wait) or equal to a normal call's;
 - calls enqueued on a side stream.
 Bars as the parity tests: 1e-4 fp32, bit-exact rows.
 """
@@ -192,8 +191,9 @@ def test_check_idx_reports_bad_index():
 def test_single_launch_give_up_poisons_outputs(axis):
     """Every wait allowed one poll, with both lags at one image, so output
     items start while their image's scans still run: their waits give up.
-    Each output token is then NaN (its block followed a give-up) or equal to
-    the normal call's, and the device error is reported."""
+    Each output element is then NaN (its block followed a give-up, or its
+    scan rows came from a scan item whose wait gave up) or equal to the
+    normal call's, and the device error is reported."""
     wl = draw_workload(C.CHAIN_1024, batch=12)
     x, z, prm = wl["x"], wl["z"][0], wl["params"][0]
     normal = gpu_call(x, z, prm, axis, flags=P.FLAG_FUSED)
@@ -204,9 +204,7 @@ def test_single_launch_give_up_poisons_outputs(axis):
     got = forced.run()
     torch.cuda.synchronize()
     nan = torch.isnan(got)
-    tok_nan = nan.all(dim=-1)
-    assert torch.equal(nan.any(dim=-1), tok_nan), "NaN covers whole tokens"
-    assert bool(tok_nan.any()), "no wait gave up: the case does not exercise the give-up path"
+    assert bool(nan.any()), "no wait gave up: the case does not exercise the give-up path"
     assert torch.equal(got[~nan], want[~nan])
     assert int(forced.export(P.EXPORT_STATUS).item()) & 1
     with pytest.raises(P.FastVimError, match="DEVICE_WAIT"):

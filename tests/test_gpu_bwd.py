@@ -560,3 +560,81 @@ def test_bwd_conv_options(axis, variant):
 @pytest.mark.parametrize("axis", (P.POOL_COLS, P.POOL_ROWS))
 def test_bwd_conv_full_size_2048(axis):
     _sampled_full_size(C.HIRES_2048, axis, saved=0 if axis == P.POOL_COLS else None, with_conv=True)
+
+
+# ---------------------------------------- Conv1D written out: block and masked
+@pytest.mark.parametrize("saved", [None, 0], ids=SAVED_IDS)
+@pytest.mark.parametrize("axis", (P.POOL_COLS, P.POOL_ROWS))
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_bwd_conv_norm_block(io, axis, saved):
+    """The whole block's gradients (Conv1D and LayerNorm together): dx through
+    the conv, dz, both parameter sets, the norm's and the conv's weight and
+    bias, on a grid whose runs of the conv's adjoint cross rows and columns."""
+    B, h, w, E, R = 2, 21, 18, 136, 9
+    rng = np.random.default_rng(zlib.crc32(repr(("bwd-block", axis, io, saved)).encode()))
+    x, z, dout = (rng.standard_normal((B, h, w, E)).astype(np.float32) for _ in range(3))
+    x, z, dout = _io(io, x, z, dout)
+    prm = {"fwd": rand_dir(rng, E, 16, R, 0.1), "bwd": rand_dir(rng, E, 16, R, 0.1)}
+    tol, dt = _tol(io)
+    bwd_check(x, z, dout, prm, axis, tol, dt, "block %s axis %d" % (io, axis), saved=saved, conv=rand_conv(rng, E),
+              ln=rand_ln(rng, E))
+
+
+@pytest.mark.parametrize("variant", ["pool_scale", "local"])
+def test_bwd_conv_norm_block_options(variant):
+    B, h, w, E, R = 2, 12, 10, 64, 5
+    rng = np.random.default_rng(zlib.crc32(repr(("bwd-block-opt", variant)).encode()))
+    x, z, dout = (rng.standard_normal((B, h, w, E)).astype(np.float32) for _ in range(3))
+    prm = {"fwd": rand_dir(rng, E, 16, R, 0.1), "bwd": rand_dir(rng, E, 16, R, 0.1)}
+    bwd_check(x, z, dout, prm, P.POOL_ROWS, FP32_TOL, torch.float32, "block " + variant, conv=rand_conv(rng, E),
+              ln=rand_ln(rng, E), flags=P.FLAG_LOCAL_BWD if variant == "local" else 0,
+              pool_scale=0.25 if variant == "pool_scale" else None)
+
+
+@pytest.mark.parametrize("norm", [False, True], ids=["plain", "norm"])
+@pytest.mark.parametrize("saved", [None, 0], ids=SAVED_IDS)
+@pytest.mark.parametrize("axis", (P.POOL_COLS, P.POOL_ROWS))
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_bwd_conv_masked(io, axis, saved, norm):
+    """Masked layers with the Conv1D along the kept tokens (more kept tokens
+    than one run of the conv's adjoint, so its halo is used)."""
+    B, h, w, K, E, R = 3, 12, 11, 100, 72, 6
+    rng = np.random.default_rng(zlib.crc32(repr(("bwd-conv-masked", axis, io, saved, norm)).encode()))
+    x, z, dout = (rng.standard_normal((B, K, E)).astype(np.float32) for _ in range(3))
+    x, z, dout = _io(io, x, z, dout)
+    idx = random_mask(rng, B, h, w, K)
+    prm = {"fwd": rand_dir(rng, E, 16, R, 0.1), "bwd": rand_dir(rng, E, 16, R, 0.1)}
+    tol, dt = _tol(io)
+    bwd_check(x, z, dout, prm, axis, tol, dt, "masked conv %s axis %d" % (io, axis), idx=idx, hw=(h, w),
+              saved=saved, conv=rand_conv(rng, E), ln=rand_ln(rng, E) if norm else None)
+
+
+@pytest.mark.parametrize("axis", (P.POOL_COLS, P.POOL_ROWS))
+def test_bwd_conv_norm_block_full_size_2048(axis):
+    _sampled_full_size(C.HIRES_2048, axis, saved=0 if axis == P.POOL_COLS else None, norm=True, with_conv=True)
+
+
+def test_bwd_conv_masked_full_size():
+    _sampled_full_size(C.MASKED_B, saved=0, with_conv=True)
+
+
+# ------------------------------------------------- scans longer than 128 steps
+LONG_BWD = [
+    # B, h, w, E, R, axis: up to the scan adjoint's longest (720 steps at dt
+    # rank <= 16, 512 at <= 32, 384 at <= 48, 288 at <= 64)
+    (2, 200, 3, 64, 8, P.POOL_COLS),
+    (1, 2, 720, 64, 12, P.POOL_ROWS),
+    (1, 512, 2, 40, 30, P.POOL_COLS),
+    (1, 3, 288, 48, 64, P.POOL_ROWS),
+]
+
+
+@pytest.mark.parametrize("local", [False, True], ids=["global", "local"])
+@pytest.mark.parametrize("case", LONG_BWD, ids=["x".join(map(str, c)) for c in LONG_BWD])
+def test_bwd_long_scans(case, local):
+    B, h, w, E, R, axis = case
+    rng = np.random.default_rng(zlib.crc32(repr(("bwd-long", case, local)).encode()))
+    x, z, dout = (rng.standard_normal((B, h, w, E)).astype(np.float32) for _ in range(3))
+    prm = {"fwd": rand_dir(rng, E, 16, R, 0.1), "bwd": rand_dir(rng, E, 16, R, 0.1)}
+    bwd_check(x, z, dout, prm, axis, FP32_TOL, torch.float32, "long %s" % (case,), saved=0 if local else None,
+              flags=P.FLAG_LOCAL_BWD if local else 0)

@@ -193,6 +193,37 @@ def test_projection_many_tokens(R, axis):
         check(got[:, :, d, :], oracle.xproj(seq, prm[name]["x_proj_w"]), FP32_TOL, "x_proj %s R=%d" % (name, R))
 
 
+# ------------------------------------------------------------ scans longer than 128 steps
+LONG = [
+    # B, h, w, E, R, axis: more scan steps than the single launch's scan items
+    # hold in LDS (128 at dt rank <= 16, 96 at <= 32, 64 at <= 64)
+    (2, 200, 3, 64, 8, P.POOL_COLS),
+    (2, 5, 300, 72, 20, P.POOL_ROWS),
+    (1, 97, 4, 40, 40, P.POOL_COLS),
+    (1, 2, 720, 64, 12, P.POOL_ROWS),
+]
+
+
+@pytest.mark.parametrize("path", list(PATHS))
+@pytest.mark.parametrize("case", LONG, ids=["x".join(map(str, c)) for c in LONG])
+def test_long_scans(case, path):
+    """The single launch's scan items stage such a sequence's rows chunk by
+    chunk; the stage kernels take any length."""
+    B, h, w, E, R, axis = case
+    rng = np.random.default_rng(zlib.crc32(repr(("long", case)).encode()))
+    x = rng.standard_normal((B, h, w, E)).astype(np.float32)
+    z = rng.standard_normal((B, h, w, E)).astype(np.float32)
+    prm = {"fwd": rand_dir(rng, E, 16, R, 0.1), "bwd": rand_dir(rng, E, 16, R, 0.1)}
+    _layer_check(x, z, prm, axis, FP32_TOL, torch.float32, "long %s %s" % (case, path), flags=PATHS[path])
+    for flags in (P.FLAG_LOCAL_BWD, P.FLAG_LOCAL_BWD | PATHS[path]):
+        call = gpu_call(x, z, prm, axis, flags=flags)
+        out = host(call.run())
+        torch.cuda.synchronize()
+        status_ok(call)
+        ref = oracle.layer(x, z, prm["fwd"], prm["bwd"], axis, local_window=P.LOCAL_WINDOW)
+        check(out, ref, FP32_TOL, "long local %s %s" % (case, path))
+
+
 # ------------------------------------------------------------ post-SSM LayerNorm
 @pytest.mark.parametrize("path", list(PATHS))
 @pytest.mark.parametrize("axis", AXES)
