@@ -368,6 +368,31 @@ def main():
                                         "epilogue_GBps": alg_bytes / (cv_epi * 1e-3) / 1e9}
         del ccall
         log("conv-fused layer %.3f ms" % cv_ms)
+        # the whole FastVim block in one call: the producer Conv1D (written out
+        # into out first) and the post-SSM LayerNorm between the skip and the gate
+        blk = {"path": "x_conv written out, then the LayerNorm layer by its default path"}
+        for name, axis in (("cols", P.POOL_COLS), ("rows", P.POOL_ROWS)):
+            bk = P.SSMCall(x, z, prm, axis, workspace=call.workspace, out=call.out, conv=conv, ln=ln)
+            bk.run(stream)
+            f_ms, _ = time_steps(lambda: bk.run(stream), n, stream)
+            blk[name] = {"forward_ms": f_ms, "images_per_s": cfg.B / (f_ms * 1e-3),
+                         "alg_GBps": alg_bytes / (f_ms * 1e-3) / 1e9,
+                         "hbm_frac": alg_bytes / (f_ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+            del bk
+        extras["block_conv_norm_2048"] = blk
+        log("conv + norm block %.3f ms (cols), %.3f ms (rows)" % (blk["cols"]["forward_ms"], blk["rows"]["forward_ms"]))
+        # bf16 I/O, both axes, on the default path (the single launch)
+        xb16, zb16 = x.to(torch.bfloat16), z.to(torch.bfloat16)
+        b16 = {}
+        for name, axis in (("cols", P.POOL_COLS), ("rows", P.POOL_ROWS)):
+            bc = P.SSMCall(xb16, zb16, prm, axis)
+            bc.run(stream)
+            f_ms, _ = time_steps(lambda: bc.run(stream), n, stream)
+            b16[name] = {"ms": f_ms, "images_per_s": cfg.B / (f_ms * 1e-3),
+                         "hbm_frac": (alg_bytes // 2) / (f_ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+            del bc
+        extras["bf16_2048"] = b16
+        del xb16, zb16
         # the backward pass (gradients of sum(dout * out)) on the same inputs
         g_b = torch.Generator(device="cuda").manual_seed(2)
         dout = torch.randn(x.shape, device=dev, generator=g_b)
@@ -417,6 +442,16 @@ def main():
         bcall.run(stream)
         b_ms, _ = time_steps(lambda: bcall.run(stream), n, stream)
         extras["backward_2048"]["conv_producer_cols"] = {"saved_u": {
+            "ms": b_ms, "images_per_s": cfg.B / (b_ms * 1e-3), "GBps": bwd_bytes / (b_ms * 1e-3) / 1e9,
+            "hbm_frac": bwd_bytes / (b_ms * 1e-3) / 1e9 / HBM_PEAK_GBS}}
+        del bcall
+        # the whole block (Conv1D and LayerNorm), pooled tokens saved by its forward call
+        P.SSMCall(x, z, prm, P.POOL_COLS, workspace=call.workspace, out=call.out, saved_u=su, conv=conv,
+                  ln=ln).run(stream)
+        bcall = P.BwdCall(x, z, dout, prm, P.POOL_COLS, saved_u=su, conv=conv, ln=ln)
+        bcall.run(stream)
+        b_ms, _ = time_steps(lambda: bcall.run(stream), n, stream)
+        extras["backward_2048"]["block_conv_norm_cols"] = {"saved_u": {
             "ms": b_ms, "images_per_s": cfg.B / (b_ms * 1e-3), "GBps": bwd_bytes / (b_ms * 1e-3) / 1e9,
             "hbm_frac": bwd_bytes / (b_ms * 1e-3) / 1e9 / HBM_PEAK_GBS}}
         del bcall
