@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define FASTVIM_ABI_VERSION 12
+#define FASTVIM_ABI_VERSION 13
 
 typedef enum fastvim_status {
     FASTVIM_OK = 0,
@@ -173,11 +173,15 @@ typedef struct fastvim_params {
  * wait inside the single launch give up after one poll, so that tests can
  * exercise the give-up path (the kernel then finishes with invalid outputs,
  * NaN in every output block that follows a failed wait, and
- * fastvim_get_device_error reports FASTVIM_ERR_DEVICE_WAIT).  Other bits:
- * FASTVIM_ERR_ARG. */
+ * fastvim_get_device_error reports FASTVIM_ERR_DEVICE_WAIT).  Other bits,
+ * except FASTVIM_TUNING_BWD_GROUPS below: FASTVIM_ERR_ARG. */
 #define FASTVIM_TUNING_LS(n) ((uint32_t)(n) & 0xffu)
 #define FASTVIM_TUNING_LE(n) (((uint32_t)(n) & 0xffu) << 8)
 #define FASTVIM_TUNING_POLL1 (1u << 16)
+/* Bits 20-25: image groups of fastvim_ssm_bwd (0 = automatic, 1 = none,
+ * at most 32; see fastvim_ssm_bwd).  The forward calls ignore them, the
+ * backward call takes no other tuning bits. */
+#define FASTVIM_TUNING_BWD_GROUPS(n) (((uint32_t)(n) & 0x3fu) << 20)
 
 /* FASTVIM_FLAG_POST_NORM adds the post-SSM LayerNorm between the skip and the
  * gate (FastVim summary page, section 方法详解, bullet 5: LayerNorm after the
@@ -457,7 +461,7 @@ typedef struct fastvim_grads {
 /* Bytes of workspace fastvim_ssm_bwd needs (0 if the sizes are invalid or
  * the backward pass does not support them): about 4 * B * T * (8E + 4(R + 2N))
  * plus per-image and per-chunk partial sums (at B = 128, h = w = 128, E = 384,
- * R = 12: about 270 MB). */
+ * R = 12: about 530 MB, enough for every image grouping). */
 size_t fastvim_ssm_bwd_workspace_bytes(const fastvim_dims *dims, int pool_axis);
 
 /* The backward pass.  x, z, dout, dx, dz: like x of fastvim_ssm_fwd (same
@@ -468,7 +472,22 @@ size_t fastvim_ssm_bwd_workspace_bytes(const fastvim_dims *dims, int pool_axis);
  * the ten gradient buffers (and the LayerNorm's or the Conv1D's two) must
  * overlap neither each other nor any input or parameter (FASTVIM_ERR_OVERLAP).  B == 0 writes zero gradients.  Errors as
  * fastvim_ssm_fwd, plus FASTVIM_ERR_NULL for a NULL grads or gradient buffer.
- * Enqueues its kernels on stream and returns. */
+ * Enqueues its kernels on stream and returns.
+ *
+ * Image groups.  A large call (by default: B >= 16 and h w E >= 2^20, or
+ * K E >= 2^20 when masked: 4 groups, 2 with the LayerNorm, none with the
+ * Conv1D computed on load; params.tuning's FASTVIM_TUNING_BWD_GROUPS sets the
+ * count) runs in groups of ceil(B / groups) images: the first passes of all
+ * groups, then their second passes, in order on stream, while each group's
+ * scan adjoint and parameter sums run on a second stream of the library's
+ * own (one per device, default priority, created on the first such call and
+ * kept until the process ends) between events recorded on both streams, so
+ * that they overlap the streaming passes.  Every piece of work the call
+ * enqueues there comes after what stream held when the call was made, and
+ * stream's own later work comes after all of it.  Parameter gradients are
+ * the groups' sums added in group order: run-to-run identical for a given
+ * grouping, equal to the ungrouped call's within rounding.  The workspace
+ * size covers every grouping. */
 int fastvim_ssm_bwd(const void *x, const void *z, const void *dout, const fastvim_params *params,
                     const fastvim_dims *dims, int pool_axis, const int32_t *mask_idx, void *dx, void *dz,
                     const fastvim_grads *grads, void *stream);

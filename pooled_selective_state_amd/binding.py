@@ -41,6 +41,12 @@ FLAG_CHECK_IDX = 64
 # params.tuning: single-launch lags (bits 0-7 LS, 8-15 LE; 0 = automatic) and
 # TUNING_POLL1 (every wait gives up after one poll: tests of the give-up path)
 TUNING_POLL1 = 1 << 16
+# bits 20-25: image groups of the backward call (0 = automatic, 1 = none, at most 32)
+MAX_BWD_GROUPS = 32
+
+
+def tuning_bwd_groups(n: int) -> int:
+    return (int(n) & 0x3F) << 20
 
 
 def tuning_lags(ls: int = 0, le: int = 0) -> int:
@@ -505,7 +511,9 @@ class BwdCall:
     parameters; with ln also "ln": {"weight", "bias"}) are allocated unless
     given.  ln: the post-SSM LayerNorm of the forward call.  saved_u: the
     pooled tokens a forward call with the same x wrote (then x is read once,
-    not twice).  pool_scale: as for the forward call.  run() returns
+    not twice).  pool_scale: as for the forward call.  groups: the call's
+    image groups (0: the library's choice, 1: none; see fastvim_ssm_bwd in
+    fastvim.h).  run() returns
     {"dx": dx, "dz": dz, "fwd": {...}, "bwd": {...}} and, with ln,
     "ln": {"weight": ..., "bias": ...}."""
 
@@ -516,9 +524,12 @@ class BwdCall:
                  grads: Optional[Dict[str, Dict[str, torch.Tensor]]] = None,
                  workspace=None, flags: int = 0,
                  saved_u: Optional[torch.Tensor] = None, ln: Optional[Dict[str, object]] = None,
-                 pool_scale: Optional[float] = None, conv: Optional[Dict[str, torch.Tensor]] = None):
+                 pool_scale: Optional[float] = None, conv: Optional[Dict[str, torch.Tensor]] = None,
+                 groups: int = 0):
         self.dims = _layer_dims(x, z, params, mask_idx, hw)
         E = self.dims.E
+        if not (isinstance(groups, int) and 0 <= groups <= MAX_BWD_GROUPS):
+            raise ValueError("groups must be an int in [0, %d] (0: automatic)" % MAX_BWD_GROUPS)
         _check_tensor("dout", dout, x.dtype, x.shape)
         for name, t in (("dx", dx), ("dz", dz)):
             if t is not None:
@@ -589,7 +600,8 @@ class BwdCall:
         self.saved_u = saved_u
         if pool_scale is not None:
             flags |= FLAG_POOL_SCALE
-        self.params = Params(dirs[0], dirs[1], ws_ptr, ws_bytes, flags, 0, _ptr(ln_w), _ptr(ln_b), ln_eps,
+        self.params = Params(dirs[0], dirs[1], ws_ptr, ws_bytes, flags, tuning_bwd_groups(groups), _ptr(ln_w),
+                             _ptr(ln_b), ln_eps,
                              1.0 if pool_scale is None else float(pool_scale), _ptr(conv_w), _ptr(conv_b),
                              _ptr(saved_u))
 
@@ -615,10 +627,11 @@ class BwdCall:
 
 
 def ssm_bwd(x, z, dout, params, pool_axis=POOL_COLS, mask_idx=None, hw=None, workspace=None, stream=None,
-            flags=0, saved_u=None, ln=None, pool_scale=None, conv=None, check_device=False):
+            flags=0, saved_u=None, ln=None, pool_scale=None, conv=None, check_device=False, groups=0):
     """Gradients of the layer; returns {"dx", "dz", "fwd": {...}, "bwd": {...}} (and "ln" / "conv" with those)."""
     return BwdCall(x, z, dout, params, pool_axis, mask_idx=mask_idx, hw=hw, workspace=workspace,
-                   flags=flags, saved_u=saved_u, ln=ln, pool_scale=pool_scale, conv=conv).run(stream, check_device)
+                   flags=flags, saved_u=saved_u, ln=ln, pool_scale=pool_scale, conv=conv,
+                   groups=groups).run(stream, check_device)
 
 
 def calib_copy(dst: torch.Tensor, src: torch.Tensor, stream=None) -> None:

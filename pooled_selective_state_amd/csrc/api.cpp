@@ -4,6 +4,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "bwd_internal.h"
 
@@ -117,7 +118,9 @@ int check_flags(const fastvim_params& p) {
     const uint32_t options = FASTVIM_FLAG_POST_NORM | FASTVIM_FLAG_CONV | FASTVIM_FLAG_LOCAL_BWD |
                              FASTVIM_FLAG_POOL_SCALE | FASTVIM_FLAG_CHECK_IDX;
     if ((p.flags & ~(paths | options)) || (p.flags & paths) == paths) return FASTVIM_ERR_ARG;
-    if (p.tuning & ~(FASTVIM_TUNING_LS(0xff) | FASTVIM_TUNING_LE(0xff) | FASTVIM_TUNING_POLL1)) return FASTVIM_ERR_ARG;
+    if (p.tuning & ~(FASTVIM_TUNING_LS(0xff) | FASTVIM_TUNING_LE(0xff) | FASTVIM_TUNING_POLL1 |
+                     FASTVIM_TUNING_BWD_GROUPS(0x3f)))
+        return FASTVIM_ERR_ARG;
     return FASTVIM_OK;
 }
 
@@ -255,7 +258,8 @@ struct Span {
     size_t n;
 };
 
-// Full validation of a backward call.  *empty is set for B == 0.
+size_t bwd_total_bytes(const Geom& g);
+
 // Full validation of a backward call.  *empty is set for B == 0.  A NULL
 // workspace passes (the call then takes its own stream-ordered scratch);
 // a caller's workspace is checked for alignment, size and overlap.
@@ -267,16 +271,19 @@ int validate_bwd(const void* x, const void* z, const void* dout, const fastvim_p
     const uint32_t options = FASTVIM_FLAG_STAGED | FASTVIM_FLAG_POST_NORM | FASTVIM_FLAG_POOL_SCALE |
                              FASTVIM_FLAG_LOCAL_BWD | FASTVIM_FLAG_CONV | FASTVIM_FLAG_CHECK_IDX;
     if (prm->flags & ~(options | unsupported)) return FASTVIM_ERR_ARG;
-    if (prm->tuning) return FASTVIM_ERR_ARG;  // the backward pass has no single launch to tune
+    // the backward pass has no single launch to tune: only its image groups
+    if (prm->tuning & ~FASTVIM_TUNING_BWD_GROUPS(0x3f)) return FASTVIM_ERR_ARG;
+    if (((prm->tuning >> 20) & 0x3fu) > 32) return FASTVIM_ERR_ARG;
     if (prm->flags & unsupported) return FASTVIM_ERR_UNSUPPORTED;
     const bool norm = (prm->flags & FASTVIM_FLAG_POST_NORM) != 0;
     const bool conv = (prm->flags & FASTVIM_FLAG_CONV) != 0;
     int st = resolve_geom(d, axis, g);
     if (st) return st;
+    g->tuning = prm->tuning;
     if ((st = apply_pool_scale(*prm, g))) return st;
     if (!bwd_supported(*g) || (norm && !bwd_norm_supported(*g))) return FASTVIM_ERR_UNSUPPORTED;
     if (conv && (g->masked || norm) &&
-        !conv_adjoint_fits(*g, (int64_t)((bwd_workspace_layout(*g, nullptr, nullptr) - kBwdHeaderBytes) / 4)))
+        !conv_adjoint_fits(*g, (int64_t)((bwd_total_bytes(*g) - kBwdHeaderBytes) / 4)))
         return FASTVIM_ERR_UNSUPPORTED;
     if (!g->masked && idx) return FASTVIM_ERR_ARG;
     if (!gr) return FASTVIM_ERR_NULL;
@@ -325,7 +332,7 @@ int validate_bwd(const void* x, const void* z, const void* dout, const fastvim_p
     if (!aligned(x, 16) || !aligned(z, 16) || !aligned(dout, 16) || !aligned(dx, 16) || !aligned(dz, 16) ||
         (idx && !aligned(idx, 4)))
         return FASTVIM_ERR_ALIGN;
-    const size_t need = bwd_workspace_layout(*g, nullptr, nullptr);
+    const size_t need = bwd_total_bytes(*g);
     if (prm->workspace) {
         if (!aligned(prm->workspace, 256)) return FASTVIM_ERR_ALIGN;
         if (prm->workspace_bytes < need) return FASTVIM_ERR_WORKSPACE;
@@ -370,8 +377,14 @@ void bind_bwd_workspace(const Geom& g, const fastvim_params& prm, void* base, Bw
     }
 }
 
-int run_bwd(const Geom& g, const void* x, const void* z, const void* dout, const fastvim_params& p,
-            const int32_t* idx, void* dx, void* dz, const fastvim_grads& gr, const BwdWorkspace& ws, hipStream_t s) {
+// The three phases of a backward call over one group of images, on one
+// stream.  front: the first pass over the grid (and what it needs: the mask
+// rows; with the LayerNorm, the forward stages and the norm's own sums).
+// mid: the scan adjoint, dv, du, d x_proj_w's partials and the parameter
+// sums (gr).  back: the second pass, which writes dx and dz, and its sums.
+int bwd_front(const Geom& g, const void* x, const void* z, const void* dout, const fastvim_params& p,
+              const int32_t* idx, void* dx, void* dz, const fastvim_grads& gr, const BwdWorkspace& ws,
+              hipStream_t s) {
     hipError_t e = hipSuccess;
     auto ok = [&](hipError_t r) {
         if (e == hipSuccess) e = r;
@@ -380,22 +393,6 @@ int run_bwd(const Geom& g, const void* x, const void* z, const void* dout, const
     const bool norm = (p.flags & FASTVIM_FLAG_POST_NORM) != 0;
     const bool local = (p.flags & FASTVIM_FLAG_LOCAL_BWD) != 0;  // p holds the effective parameters
     const bool conv = (p.flags & FASTVIM_FLAG_CONV) != 0;
-    if (conv_written(g, p.flags)) {
-        // x_conv into dz (the passes below read each cell's x before they
-        // write its dz), the layer's backward pass on it, which leaves
-        // dL/dx_conv in dx, then the conv's adjoint in place on dx, its scratch
-        // the workspace the layer's pass no longer needs
-        fastvim_params q = p;
-        q.flags &= ~FASTVIM_FLAG_CONV;
-        if (!ok(launch_conv_seq(g, x, p, dz, s))) return FASTVIM_ERR_HIP;
-        const int st = run_bwd(g, dz, z, dout, q, idx, dx, dz, gr, ws, s);
-        if (st) return st;
-        float* scratch = reinterpret_cast<float*>(reinterpret_cast<char*>(ws.fwd.sync) + kBwdHeaderBytes);
-        const int64_t floats = (int64_t)((bwd_workspace_layout(g, nullptr, nullptr) - kBwdHeaderBytes) / 4);
-        return ok(launch_conv_adjoint(g, x, dx, p, scratch, floats, gr.conv_w, gr.conv_b, s)) ? FASTVIM_OK
-                                                                                              : FASTVIM_ERR_HIP;
-    }
-    if (!ok(launch_zero_sync(ws.fwd, kBwdStatusWords, s))) return FASTVIM_ERR_HIP;
     if (g.masked &&
         !ok(launch_mask_rows(g, idx, ws.fwd, (p.flags & FASTVIM_FLAG_CHECK_IDX) ? ws.fwd.sync + 1 : nullptr, s)))
         return FASTVIM_ERR_HIP;
@@ -427,6 +424,17 @@ int run_bwd(const Geom& g, const void* x, const void* z, const void* dout, const
         // from the forward scan; the scan adjoint does not rerun that scan
         if (local && !ok(launch_scan(g, x, p, ws.fwd, s))) return FASTVIM_ERR_HIP;
     }
+    return FASTVIM_OK;
+}
+
+int bwd_mid(const Geom& g, const fastvim_params& p, const fastvim_grads& gr, const BwdWorkspace& ws,
+            hipStream_t s) {
+    hipError_t e = hipSuccess;
+    auto ok = [&](hipError_t r) {
+        if (e == hipSuccess) e = r;
+        return e == hipSuccess;
+    };
+    const bool local = (p.flags & FASTVIM_FLAG_LOCAL_BWD) != 0;
     BwdScanArgs a{ws.fwd.xdbl, ws.fwd.u, ws.gs, p.fwd, p.bwd, ws.fwd.s_f, ws.fwd.s_b, ws.du_f, ws.du_b, ws.dvp,
                   ws.ckpt, ws.dAp, ws.dWdtp, ws.dbp, g.B, g.T, g.E, (int)g.R, (int)g.NX, (int)ws.G, local, ws.nchk};
     if (!ok(launch_scan_bwd(a, s)) || !ok(launch_bwd_dv(g, ws, s)) || !ok(launch_bwd_du(g, p, ws, s)) ||
@@ -462,9 +470,20 @@ int run_bwd(const Geom& g, const void* x, const void* z, const void* dout, const
             }
         }
     }
-    if (!ok(launch_colsum_batch(batch, s))) return FASTVIM_ERR_HIP;
-    if (norm) return ok(launch_bwd_norm_pass2(g, p, ws, dx, dz, s)) ? FASTVIM_OK : FASTVIM_ERR_HIP;
-    if (conv) {
+    return ok(launch_colsum_batch(batch, s)) ? FASTVIM_OK : FASTVIM_ERR_HIP;
+}
+
+int bwd_back(const Geom& g, const void* x, const void* z, const void* dout, const fastvim_params& p, void* dx,
+             void* dz, const fastvim_grads& gr, const BwdWorkspace& ws, hipStream_t s) {
+    hipError_t e = hipSuccess;
+    auto ok = [&](hipError_t r) {
+        if (e == hipSuccess) e = r;
+        return e == hipSuccess;
+    };
+    const int64_t E = g.E;
+    if (p.flags & FASTVIM_FLAG_POST_NORM)
+        return ok(launch_bwd_norm_pass2(g, p, ws, dx, dz, s)) ? FASTVIM_OK : FASTVIM_ERR_HIP;
+    if (p.flags & FASTVIM_FLAG_CONV) {
         // second pass through the conv; its partial rows go to the checkpoint
         // region (free once the scan adjoint has run; large enough: see
         // bwd_workspace_layout)
@@ -481,6 +500,257 @@ int run_bwd(const Geom& g, const void* x, const void* z, const void* dout, const
     if (!ok(launch_bwd_epilogue(g, x, z, dout, p, ws, dx, dz, s))) return FASTVIM_ERR_HIP;
     if (!ok(launch_colsum(ws.dDp, bwd_dd_parts(g), E, E, gr.fwd.D, gr.bwd.D, ws.tmp, s))) return FASTVIM_ERR_HIP;
     return FASTVIM_OK;
+}
+
+// ---------------------------------------------------------------- image groups
+// A large backward call runs as groups of images: the first passes of all
+// groups, then the second passes, on the call's stream, while each group's
+// mid phase runs on a second stream as soon as its first pass is done.  The
+// mid phase (scan adjoint, projections' adjoints, parameter sums: latency
+// bound, little HBM traffic) then hides under the streaming passes.  Each
+// group has a backward workspace of its own and writes its parameter sums to
+// a record of its own; the records are added in group order at the end, so
+// results stay bitwise deterministic for a given grouping.
+
+constexpr int kMaxBwdGroups = 32;
+
+// Floats of one group's record of parameter sums: per direction x_proj_w,
+// dt_proj_w, dt_proj_b, A_log, D; then ln_w, ln_b, conv_w, conv_b.
+int64_t bwd_record_floats(const Geom& g) {
+    const int64_t E = g.E;
+    return 2 * (g.NX * E + E * g.R + E + E * 16 + E) + 2 * E + 4 * E + E;
+}
+
+// The record's layout as a fastvim_grads.
+fastvim_grads bwd_record(const Geom& g, float* r) {
+    const int64_t E = g.E;
+    fastvim_grads gr{};
+    fastvim_dir_grads* d[2] = {&gr.fwd, &gr.bwd};
+    for (fastvim_dir_grads* dd : d) {
+        dd->x_proj_w = r; r += g.NX * E;
+        dd->dt_proj_w = r; r += E * g.R;
+        dd->dt_proj_b = r; r += E;
+        dd->A_log = r; r += E * 16;
+        dd->D = r; r += E;
+    }
+    gr.ln_weight = r; r += E;
+    gr.ln_bias = r; r += E;
+    gr.conv_w = r; r += 4 * E;
+    gr.conv_b = r;
+    return gr;
+}
+
+// Images per group, and the group count, for k requested groups.
+void bwd_group_shape(const Geom& g, int k, int64_t* per, int* n) {
+    *per = (g.B + k - 1) / k;
+    *n = (int)((g.B + *per - 1) / *per);
+}
+
+// Bytes of a workspace for k groups: a 256-byte header (the call's status
+// word), one backward workspace per group sized for its largest group, then
+// the groups' records.
+size_t bwd_grouped_bytes(const Geom& g, int k) {
+    int64_t per;
+    int n;
+    bwd_group_shape(g, k, &per, &n);
+    Geom gp = g;
+    gp.B = per;
+    const size_t sub = align256(bwd_workspace_layout(gp, nullptr, nullptr));
+    return kBwdHeaderBytes + (size_t)n * sub + align256((size_t)(n * bwd_record_floats(g)) * sizeof(float));
+}
+
+// Groups a call runs as: FASTVIM_TUNING_BWD_GROUPS when set (1: none), else,
+// for batches of at least 16 images of at least 2^20 cells x channels
+// (2048^2 FastVim-T has 6.3 M), the measured best at 2048^2, B = 128: 4
+// groups (4.43 -> 4.13 ms with saved pooled tokens, 4.99 -> 4.66 ms
+// pooling x again), 2 with the LayerNorm (whose first pass needs the
+// forward scans, recomputed per group: 4.82 -> 4.64 ms) and none with the
+// Conv1D on load (5.09 ms alone, 5.17 in 2 groups); else none.
+int bwd_groups(const Geom& g, uint32_t flags) {
+    const int set = (int)((g.tuning >> 20) & 0x3fu);
+    int k = set ? set : 1;
+    if (!set) {
+        const int64_t cells = (g.masked ? g.K : g.h * g.w) * g.E;
+        if (cells >= (int64_t(1) << 20) && g.B >= 16)
+            k = (flags & FASTVIM_FLAG_CONV) ? 1 : (flags & FASTVIM_FLAG_POST_NORM) ? 2 : 4;
+    }
+    if (k > g.B) k = (int)g.B;
+    return k < 1 ? 1 : k;
+}
+
+// Workspace bytes of a backward call: enough for its layer in one group and
+// in every grouping the tuning word may ask for.
+size_t bwd_total_bytes(const Geom& g) {
+    size_t need = bwd_workspace_layout(g, nullptr, nullptr);
+    for (int k = 2; k <= kMaxBwdGroups && k <= g.B; ++k) {
+        const size_t b = bwd_grouped_bytes(g, k);
+        if (b > need) need = b;
+    }
+    return need;
+}
+
+// The second stream of grouped calls on the stream's device: default
+// priority, non-blocking, created on first use and kept until the process
+// ends.  Calls on one device share it (their mid phases then queue).
+int side_stream(hipStream_t s, hipStream_t* out) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static hipStream_t tab[kMaxDevices] = {};
+    int cur = -1, dev = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return FASTVIM_ERR_HIP;
+    dev = cur;
+    if (s && hipStreamGetDevice(s, &dev) != hipSuccess) return FASTVIM_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return FASTVIM_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!tab[dev]) {
+        if (dev != cur && hipSetDevice(dev) != hipSuccess) return FASTVIM_ERR_HIP;
+        const hipError_t e = hipStreamCreateWithFlags(&tab[dev], hipStreamNonBlocking);
+        if (dev != cur) (void)hipSetDevice(cur);
+        if (e != hipSuccess) {
+            tab[dev] = nullptr;
+            return FASTVIM_ERR_HIP;
+        }
+    }
+    *out = tab[dev];
+    return FASTVIM_OK;
+}
+
+// Events of one grouped call, destroyed when it returns (HIP releases an
+// event that is still pending once it completes).
+struct CallEvents {
+    hipEvent_t ev[2 * kMaxBwdGroups + 1] = {};
+    int n = 0;
+    int make(int count) {
+        for (; n < count; ++n)
+            if (hipEventCreateWithFlags(&ev[n], hipEventDisableTiming) != hipSuccess) return FASTVIM_ERR_HIP;
+        return FASTVIM_OK;
+    }
+    ~CallEvents() {
+        for (int i = 0; i < n; ++i) (void)hipEventDestroy(ev[i]);
+    }
+};
+
+int run_bwd_grouped(const Geom& g, int k, const void* x, const void* z, const void* dout, const fastvim_params& p,
+                    const int32_t* idx, void* dx, void* dz, const fastvim_grads& gr, void* base, hipStream_t s) {
+    int64_t per;
+    int n;
+    bwd_group_shape(g, k, &per, &n);
+    Geom gp = g;
+    gp.B = per;
+    const size_t sub = align256(bwd_workspace_layout(gp, nullptr, nullptr));
+    char* c = static_cast<char*>(base);
+    unsigned* header = reinterpret_cast<unsigned*>(c);
+    float* records = reinterpret_cast<float*>(c + kBwdHeaderBytes + (size_t)n * sub);
+    const int64_t rf = bwd_record_floats(g);
+    const size_t img = io_span(g) / (size_t)g.B;  // bytes of one image of x (z, dout, dx, dz)
+    const int64_t idx_img = g.masked ? g.K : 0;
+    hipStream_t side = nullptr;
+    int st = side_stream(s, &side);
+    if (st) return st;
+    CallEvents evs;
+    if ((st = evs.make(2 * n + 1))) return st;
+    hipEvent_t* front_done = evs.ev;
+    hipEvent_t* mid_done = evs.ev + n;
+    hipEvent_t start = evs.ev[2 * n];
+    Workspace hdr{};
+    hdr.sync = header;
+    if (launch_zero_sync(hdr, kBwdStatusWords, s) != hipSuccess) return FASTVIM_ERR_HIP;
+    // the side stream starts behind everything the caller queued before
+    if (hipEventRecord(start, s) != hipSuccess || hipStreamWaitEvent(side, start, 0) != hipSuccess)
+        return FASTVIM_ERR_HIP;
+    struct Group {
+        Geom g;
+        BwdWorkspace ws;
+        fastvim_grads rec;
+        size_t off;
+    } grp[kMaxBwdGroups];
+    for (int i = 0; i < n; ++i) {
+        Group& q = grp[i];
+        q.g = g;
+        q.g.B = (i + 1) * per <= g.B ? per : g.B - i * per;
+        bwd_workspace_layout(q.g, c + kBwdHeaderBytes + (size_t)i * sub, &q.ws);
+        q.ws.fwd.sync = header;  // one status word for the call
+        if (p.saved_u) {
+            q.ws.fwd.u = p.saved_u + (size_t)(i * per) * (size_t)(g.T * g.E);
+            q.ws.u_saved = true;
+        }
+        q.rec = bwd_record(g, records + i * rf);
+        q.off = (size_t)(i * per) * img;
+    }
+    auto at = [](const void* ptr, size_t off) { return static_cast<const char*>(ptr) + off; };
+    auto atw = [](void* ptr, size_t off) { return static_cast<char*>(ptr) + off; };
+    for (int i = 0; i < n; ++i) {
+        const Group& q = grp[i];
+        const int32_t* qi = g.masked ? idx + (size_t)(i * per) * (size_t)idx_img : nullptr;
+        if ((st = bwd_front(q.g, at(x, q.off), at(z, q.off), at(dout, q.off), p, qi, atw(dx, q.off),
+                            atw(dz, q.off), q.rec, q.ws, s)))
+            return st;
+        if (hipEventRecord(front_done[i], s) != hipSuccess || hipStreamWaitEvent(side, front_done[i], 0) != hipSuccess)
+            return FASTVIM_ERR_HIP;
+        if ((st = bwd_mid(q.g, p, q.rec, q.ws, side))) return st;
+        if (hipEventRecord(mid_done[i], side) != hipSuccess) return FASTVIM_ERR_HIP;
+    }
+    for (int i = 0; i < n; ++i) {
+        const Group& q = grp[i];
+        if (hipStreamWaitEvent(s, mid_done[i], 0) != hipSuccess) return FASTVIM_ERR_HIP;
+        if ((st = bwd_back(q.g, at(x, q.off), at(z, q.off), at(dout, q.off), p, atw(dx, q.off), atw(dz, q.off),
+                           q.rec, q.ws, s)))
+            return st;
+    }
+    // the groups' records, added in group order into the caller's gradients
+    const fastvim_grads r0 = bwd_record(g, records);
+    const int64_t E = g.E;
+    ColsumBatch b1{}, b2{};
+    const fastvim_dir_grads* rd[2] = {&r0.fwd, &r0.bwd};
+    const fastvim_dir_grads* od[2] = {&gr.fwd, &gr.bwd};
+    for (int d = 0; d < 2; ++d) {
+        b1.seg[b1.n++] = ColsumSeg{rd[d]->x_proj_w, n, g.NX * E, rf, od[d]->x_proj_w, nullptr, 0};
+        b1.seg[b1.n++] = ColsumSeg{rd[d]->dt_proj_w, n, E * g.R, rf, od[d]->dt_proj_w, nullptr, 0};
+        b1.seg[b1.n++] = ColsumSeg{rd[d]->dt_proj_b, n, E, rf, od[d]->dt_proj_b, nullptr, 0};
+        b1.seg[b1.n++] = ColsumSeg{rd[d]->A_log, n, E * 16, rf, od[d]->A_log, nullptr, 0};
+    }
+    b2.seg[b2.n++] = ColsumSeg{r0.fwd.D, n, E, rf, gr.fwd.D, gr.bwd.D, 0};
+    if (p.flags & FASTVIM_FLAG_POST_NORM) {
+        b2.seg[b2.n++] = ColsumSeg{r0.ln_weight, n, E, rf, gr.ln_weight, nullptr, 0};
+        b2.seg[b2.n++] = ColsumSeg{r0.ln_bias, n, E, rf, gr.ln_bias, nullptr, 0};
+    }
+    if (p.flags & FASTVIM_FLAG_CONV) {
+        b2.seg[b2.n++] = ColsumSeg{r0.conv_w, n, 4 * E, rf, gr.conv_w, nullptr, 0};
+        b2.seg[b2.n++] = ColsumSeg{r0.conv_b, n, E, rf, gr.conv_b, nullptr, 0};
+    }
+    if (launch_colsum_batch(b1, s) != hipSuccess || launch_colsum_batch(b2, s) != hipSuccess)
+        return FASTVIM_ERR_HIP;
+    return FASTVIM_OK;
+}
+
+// A backward call on its workspace at base (bwd_total_bytes(g) bytes).
+int run_bwd(const Geom& g, const void* x, const void* z, const void* dout, const fastvim_params& p,
+            const int32_t* idx, void* dx, void* dz, const fastvim_grads& gr, void* base, hipStream_t s) {
+    if (conv_written(g, p.flags)) {
+        // x_conv into dz (the passes below read each cell's x before they
+        // write its dz), the layer's backward pass on it, which leaves
+        // dL/dx_conv in dx, then the conv's adjoint in place on dx, its scratch
+        // the workspace the layer's pass no longer needs
+        fastvim_params q = p;
+        q.flags &= ~FASTVIM_FLAG_CONV;
+        if (launch_conv_seq(g, x, p, dz, s) != hipSuccess) return FASTVIM_ERR_HIP;
+        const int st = run_bwd(g, dz, z, dout, q, idx, dx, dz, gr, base, s);
+        if (st) return st;
+        float* scratch = reinterpret_cast<float*>(static_cast<char*>(base) + kBwdHeaderBytes);
+        const int64_t floats = (int64_t)((bwd_total_bytes(g) - kBwdHeaderBytes) / 4);
+        return launch_conv_adjoint(g, x, dx, p, scratch, floats, gr.conv_w, gr.conv_b, s) == hipSuccess
+                   ? FASTVIM_OK
+                   : FASTVIM_ERR_HIP;
+    }
+    const int k = bwd_groups(g, p.flags);
+    if (k > 1) return run_bwd_grouped(g, k, x, z, dout, p, idx, dx, dz, gr, base, s);
+    BwdWorkspace ws;
+    bind_bwd_workspace(g, p, base, &ws);
+    if (launch_zero_sync(ws.fwd, kBwdStatusWords, s) != hipSuccess) return FASTVIM_ERR_HIP;
+    int st = bwd_front(g, x, z, dout, p, idx, dx, dz, gr, ws, s);
+    if (!st) st = bwd_mid(g, p, gr, ws, s);
+    if (!st) st = bwd_back(g, x, z, dout, p, dx, dz, gr, ws, s);
+    return st;
 }
 
 // Destinations of fastvim_ssm_fwd_stages (each NULL to skip).
@@ -770,7 +1040,7 @@ int fastvim_ssm_export(const fastvim_params* params, const fastvim_dims* dims, i
 size_t fastvim_ssm_bwd_workspace_bytes(const fastvim_dims* dims, int pool_axis) {
     Geom g;
     if (resolve_geom(dims, pool_axis, &g) != FASTVIM_OK || !bwd_supported(g)) return 0;
-    return bwd_workspace_layout(g, nullptr, nullptr);
+    return bwd_total_bytes(g);
 }
 
 int fastvim_ssm_bwd(const void* x, const void* z, const void* dout, const fastvim_params* params,
@@ -800,10 +1070,8 @@ int fastvim_ssm_bwd(const void* x, const void* z, const void* dout, const fastvi
     }
     StreamScratch scratch;
     void* base = params->workspace;
-    if (!base && (st = scratch.take(bwd_workspace_layout(g, nullptr, nullptr), s, &base))) return st;
-    BwdWorkspace ws;
-    bind_bwd_workspace(g, *params, base, &ws);
-    st = run_bwd(g, x, z, dout, effective_params(*params), mask_idx, dx, dz, *grads, ws, s);
+    if (!base && (st = scratch.take(bwd_total_bytes(g), s, &base))) return st;
+    st = run_bwd(g, x, z, dout, effective_params(*params), mask_idx, dx, dz, *grads, base, s);
     return scratch.give_back(st);
 }
 

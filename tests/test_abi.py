@@ -33,7 +33,7 @@ def test_library_exports_every_declared_function():
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(Bd.EXPORTED_SYMBOLS)
-    assert lib.fastvim_abi_version() == 12
+    assert lib.fastvim_abi_version() == 13
 
 
 def test_status_strings():
@@ -446,6 +446,38 @@ def test_bwd_unsupported_and_bad_flags():
     c = FakeBwd()
     c.params.tuning = 1
     assert c.bwd() == EARG  # no single launch to tune
+    for tuning in (P.TUNING_POLL1, P.tuning_bwd_groups(33), P.tuning_bwd_groups(63), 1 << 26):
+        c = FakeBwd()
+        c.params.tuning = tuning
+        assert c.bwd() == EARG, hex(tuning)  # only the image groups, at most 32
+    for groups in (0, 1, 4, 32):
+        # accepted: the call goes on to the next check (a misaligned dx here)
+        c = FakeBwd()
+        c.params.tuning = P.tuning_bwd_groups(groups)
+        c.dx += 4
+        assert c.bwd() == EALIGN, groups
+
+
+def test_forward_accepts_the_backward_groups():
+    """A params struct shared by the forward and backward calls may carry the
+    backward's image groups: the forward calls ignore them."""
+    c = FakeCall()
+    c.params.tuning = P.tuning_bwd_groups(8) | P.tuning_lags(3, 7)
+    c.x += 4
+    expect(c, EALIGN)
+    for bad in (P.tuning_bwd_groups(8) | (1 << 26), 1 << 17):
+        c = FakeCall()
+        c.params.tuning = bad
+        expect(c, EARG)
+
+
+def test_bwd_workspace_covers_every_grouping():
+    """The backward workspace size does not depend on the tuning word, so it
+    covers the largest of the groupings a call may ask for: never smaller
+    than for fewer images, and growing about linearly in B."""
+    sizes = [P.bwd_workspace_bytes(P.make_dims(B, 128, 128, 384, 16, 12), P.POOL_COLS) for B in (1, 16, 128)]
+    assert 0 < sizes[0] < sizes[1] < sizes[2]
+    assert sizes[2] < 9 * sizes[1]
 
 
 def _norm_bwd(**kw):

@@ -54,10 +54,11 @@ def _dev_ln(ln):
 
 
 def gpu_bwd(x, z, dout, prm, axis, idx=None, hw=None, dtype=torch.float32, flags=0, saved=None, ln=None,
-            pool_scale=None, conv=None):
+            pool_scale=None, conv=None, groups=0):
     """saved: None (the backward pools x itself) or the flags of a forward call
     that first writes the pooled tokens the backward then reads (saved_u).
-    ln: the post-SSM LayerNorm (host arrays), for both calls."""
+    ln: the post-SSM LayerNorm (host arrays), for both calls.  groups: the
+    backward call's image groups (0: the library's choice)."""
     idd = None if idx is None else dev(idx, torch.int32)
     xd, zd, pd = dev(x, dtype), dev(z, dtype), dev_params(prm)
     lnd = _dev_ln(ln)
@@ -69,7 +70,7 @@ def gpu_bwd(x, z, dout, prm, axis, idx=None, hw=None, dtype=torch.float32, flags
         P.SSMCall(xd, zd, pd, axis, mask_idx=idd, hw=hw, flags=saved | (flags & P.FLAG_LOCAL_BWD), saved_u=su,
                   ln=lnd, pool_scale=pool_scale, conv=cvd).run()
     call = P.BwdCall(xd, zd, dev(dout, dtype), pd, axis, mask_idx=idd, hw=hw, flags=flags, saved_u=su, ln=lnd,
-                     pool_scale=pool_scale, conv=cvd)
+                     pool_scale=pool_scale, conv=cvd, groups=groups)
     res = call.run()
     torch.cuda.synchronize()
     out = {"dx": host(res["dx"]), "dz": host(res["dz"]),
@@ -638,3 +639,109 @@ def test_bwd_long_scans(case, local):
     prm = {"fwd": rand_dir(rng, E, 16, R, 0.1), "bwd": rand_dir(rng, E, 16, R, 0.1)}
     bwd_check(x, z, dout, prm, axis, FP32_TOL, torch.float32, "long %s" % (case,), saved=0 if local else None,
               flags=P.FLAG_LOCAL_BWD if local else 0)
+
+
+# ------------------------------------------------------------------ image groups
+# A backward call in image groups: each group's first pass, scan adjoint
+# (on the library's second stream) and second pass, and the groups' parameter
+# sums added at the end.  dx and dz are per-image results and must equal the
+# single-group call's bit for bit; the parameter gradients differ only by the
+# order of their sums.
+GROUP_CASES = [
+    # B, h, w, E, R, groups
+    (7, 12, 10, 64, 4, 3),    # groups of 3, 3 and 1 images
+    (5, 9, 14, 136, 12, 5),   # one image a group
+    (3, 16, 16, 64, 8, 32),   # more groups asked for than images
+]
+GROUP_VARIANTS = ["plain", "saved", "norm", "conv", "block", "local", "masked", "masked_conv", "bf16"]
+
+
+def _group_inputs(case, variant):
+    B, h, w, E, R, groups = case
+    rng = np.random.default_rng(zlib.crc32(repr(("bwd-groups", case, variant)).encode()))
+    masked = variant.startswith("masked")
+    K = (h * w * 2) // 3
+    shape = (B, K, E) if masked else (B, h, w, E)
+    x, z, dout = (rng.standard_normal(shape).astype(np.float32) for _ in range(3))
+    io = "bf16" if variant == "bf16" else "f32"
+    x, z, dout = _io(io, x, z, dout)
+    prm = {"fwd": rand_dir(rng, E, 16, R, 0.1), "bwd": rand_dir(rng, E, 16, R, 0.1)}
+    kw = dict(dtype=_tol(io)[1])
+    if masked:
+        kw.update(idx=random_mask(rng, B, h, w, K), hw=(h, w))
+    if variant == "saved":
+        kw["saved"] = P.FLAG_FUSED
+    if variant in ("norm", "block"):
+        kw["ln"] = rand_ln(rng, E)
+    if variant in ("conv", "block", "masked_conv"):
+        kw["conv"] = rand_conv(rng, E)
+    if variant == "local":
+        kw["flags"] = P.FLAG_LOCAL_BWD
+    return (x, z, dout, prm), kw, groups, io
+
+
+def _same(a, b, tag):
+    assert np.array_equal(a, b, equal_nan=True), tag + " differs from the single-group call"
+
+
+@pytest.mark.parametrize("variant", GROUP_VARIANTS)
+@pytest.mark.parametrize("case", GROUP_CASES, ids=["x".join(map(str, c)) for c in GROUP_CASES])
+@pytest.mark.parametrize("axis", (P.POOL_COLS, P.POOL_ROWS))
+def test_bwd_groups_match_single_group(axis, case, variant):
+    args, kw, groups, io = _group_inputs(case, variant)
+    one = gpu_bwd(*args, axis, groups=1, **kw)
+    many = gpu_bwd(*args, axis, groups=groups, **kw)
+    tag = "groups=%d %s axis %d %s" % (groups, variant, axis, case)
+    _same(many["dx"], one["dx"], tag + " dx")
+    _same(many["dz"], one["dz"], tag + " dz")
+    compare(many, one, FP32_TOL, tag)
+    again = gpu_bwd(*args, axis, groups=groups, **kw)
+    for d in DIRECTIONS:
+        for f in FIELDS:
+            _same(again[d][f], many[d][f], tag + " rerun d%s.%s" % (d, f))
+
+
+@pytest.mark.parametrize("variant", ["plain", "block", "masked_conv"])
+def test_bwd_groups_against_oracle(variant):
+    """The grouped call against the oracle directly (with its D = 0 twin)."""
+    args, kw, groups, io = _group_inputs(GROUP_CASES[0], variant)
+    x, z, dout, prm = args
+    tol, dt = _tol(io)
+    for axis in (P.POOL_COLS, P.POOL_ROWS):
+        local = P.LOCAL_WINDOW if kw.get("flags", 0) & P.FLAG_LOCAL_BWD else 0
+        got = gpu_bwd(x, z, dout, prm, axis, groups=groups, **kw)
+        ref = oracle.layer_bwd(x, z, dout, prm["fwd"], prm["bwd"], axis, idx=kw.get("idx"), hw=kw.get("hw"),
+                               ln=kw.get("ln"), conv=kw.get("conv"), local_window=local)
+        compare(got, ref, tol, "grouped %s axis %d" % (variant, axis))
+        p0 = zero_D(prm)
+        got0 = gpu_bwd(x, z, dout, p0, axis, groups=groups, **kw)
+        ref0 = oracle.layer_bwd(x, z, dout, p0["fwd"], p0["bwd"], axis, idx=kw.get("idx"), hw=kw.get("hw"),
+                                ln=kw.get("ln"), conv=kw.get("conv"), local_window=local)
+        compare(got0, ref0, tol, "grouped %s axis %d (D=0)" % (variant, axis), params=False)
+
+
+def test_bwd_groups_default_at_full_size_is_deterministic():
+    """The 2048^2 layer runs in the library's default grouping: two calls give
+    bitwise identical results, and they equal the single-group call's dx and
+    dz bit for bit."""
+    wl = draw_workload(C.HIRES_2048)
+    rng = np.random.default_rng(81)
+    x, z, prm = wl["x"], wl["z"][0], wl["params"][0]
+    dout = rng.standard_normal(x.shape).astype(np.float32)
+    print("\n[2048^2 bwd] default grouping twice, then one group", flush=True)
+    xd, zd, dd, pd = dev(x), dev(z), dev(dout), dev_params(prm)
+    res = []
+    for groups in (0, 0, 1):
+        r = P.BwdCall(xd, zd, dd, pd, P.POOL_COLS, groups=groups).run()
+        torch.cuda.synchronize()
+        res.append({"dx": r["dx"].clone(), "dz": r["dz"].clone(),
+                    **{d: {f: r[d][f].clone() for f in FIELDS} for d in DIRECTIONS}})
+        del r
+    a, b, one = res
+    for k in ("dx", "dz"):
+        assert torch.equal(a[k], b[k]), k
+        assert torch.equal(a[k], one[k]), k
+    for d in DIRECTIONS:
+        for f in FIELDS:
+            assert torch.equal(a[d][f], b[d][f]), (d, f)
+            check(host(a[d][f]), host(one[d][f]), FP32_TOL, "default grouping d%s.%s" % (d, f))
