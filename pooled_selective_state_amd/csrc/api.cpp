@@ -95,7 +95,9 @@ fastvim_params effective_params(const fastvim_params& p) {
 // window where they read x get x_conv written out first (conv_seq.hip):
 // masked layers (the conv runs along the kept tokens), layers with the
 // post-SSM LayerNorm and unpooled layers.  Dense pooled layers without the
-// norm compute it in their pool and output stages (conv.hip).
+// norm compute it in their pool and output stages (conv.hip), and the
+// forward pass's single launch computes it on load for dense COLS layers,
+// with or without the norm (fused.hip; run_fwd asks it first).
 bool conv_written(const Geom& g, uint32_t flags) {
     return (flags & FASTVIM_FLAG_CONV) && (g.masked || !g.pooled || (flags & FASTVIM_FLAG_POST_NORM));
 }
@@ -786,7 +788,15 @@ int check_stage_dst(const Geom& g, const StageDst& d, const void* x, const void*
 // the stage kernels.
 int run_fwd(const Geom& g, const void* x, const void* z, const fastvim_params& prm, const int32_t* idx, void* out,
             const Workspace& ws, hipStream_t s) {
-    if (conv_written(g, prm.flags)) {
+    const bool norm = (prm.flags & FASTVIM_FLAG_POST_NORM) != 0;
+    const bool local = (prm.flags & FASTVIM_FLAG_LOCAL_BWD) != 0;
+    const bool conv = (prm.flags & FASTVIM_FLAG_CONV) != 0;
+    // the single launch (with the Conv1D computed on load where it takes it:
+    // dense COLS layers)
+    const bool single = (prm.flags & FASTVIM_FLAG_FUSED)
+                            ? fused_supported(g, norm, local, conv)
+                            : !(prm.flags & FASTVIM_FLAG_STAGED) && fused_preferred(g, norm, local, conv);
+    if (!single && conv_written(g, prm.flags)) {
         // x_conv into out, then the layer on it: every stage reads a cell's x
         // before the output stage writes that cell
         if (launch_conv_seq(g, x, prm, out, s) != hipSuccess) return FASTVIM_ERR_HIP;
@@ -796,12 +806,6 @@ int run_fwd(const Geom& g, const void* x, const void* z, const fastvim_params& p
     }
     if (launch_zero_sync(ws, sync_words(g), s) != hipSuccess) return FASTVIM_ERR_HIP;
     const fastvim_params q = effective_params(prm);
-    const bool norm = (prm.flags & FASTVIM_FLAG_POST_NORM) != 0;
-    const bool local = (prm.flags & FASTVIM_FLAG_LOCAL_BWD) != 0;
-    const bool single = !(prm.flags & FASTVIM_FLAG_CONV) &&
-                        ((prm.flags & FASTVIM_FLAG_FUSED)
-                             ? fused_supported(g, norm, local)
-                             : !(prm.flags & FASTVIM_FLAG_STAGED) && fused_preferred(g, norm, local));
     if (single) return launch_fused(g, x, z, q, ws, out, s) == hipSuccess ? FASTVIM_OK : FASTVIM_ERR_HIP;
     for (int stage = FASTVIM_STAGE_ROWS; stage <= FASTVIM_STAGE_EPILOGUE; ++stage) {
         const int st = run_stage(stage, g, x, z, q, idx, out, ws, s);

@@ -50,6 +50,35 @@ __device__ __forceinline__ void conv_window(const typename IO::raw& p3, const ty
     }
 }
 
+// Token index within the image of the k-th predecessor (k >= 1) of grid cell
+// (i, j) in the oriented sequence, or -1 before the start of the sequence.
+template <bool COLS>
+__device__ __forceinline__ int pred_token(int i, int j, int k, int h, int w) {
+    if (COLS) {
+        const int r = i * w + j - k;
+        return r;  // row-major: memory order; negative before the start
+    }
+    if (i >= k) return (i - k) * w + j;
+    const int r = j * h + i - k;  // column-major position; may lie several columns back when h < k
+    return r < 0 ? -1 : (r % h) * w + r / h;
+}
+
+// The three predecessors of cell (i, j) (p1 the newest), zero before the start.
+template <class IO, bool COLS>
+__device__ __forceinline__ void load_halo(const typename IO::elem* xb, int coff, int E, int i, int j, int h, int w,
+                                          typename IO::raw& p3, typename IO::raw& p2, typename IO::raw& p1) {
+    typename IO::raw r[3];
+#pragma unroll
+    for (int k = 1; k <= 3; ++k) {
+        const int tok = pred_token<COLS>(i, j, k, h, w);
+        r[k - 1] = typename IO::raw{};
+        if (tok >= 0) r[k - 1] = load_raw<false>(xb + (coff + tok * E));
+    }
+    p1 = r[0];
+    p2 = r[1];
+    p3 = r[2];
+}
+
 // d silu(a) / da = sigmoid(a) (1 + a (1 - sigmoid(a))).
 __device__ __forceinline__ float conv_silu_grad(float a) {
     const float sg = __builtin_amdgcn_rcpf(1.f + __expf(-a));

@@ -65,15 +65,16 @@ __device__ __forceinline__ void norm_load(const typename IO::elem* xb, const typ
 }
 
 // The rest of the token: s rows, D, the norm and the gate, then the
-// non-temporal store of out.  s1, s2: the token's two scan rows and d1, d2
-// the two D vectors; SUMMED: s1 already holds s_fwd + s_bwd and d1 holds
-// D_fwd + D_bwd (s2, d2 unused) -- staged in LDS by a caller that reuses
-// them over many tokens.
+// non-temporal store of out.  xv: the token's x values held by this lane
+// (x itself, or x_conv when the producer Conv1D is computed on load).  s1,
+// s2: the token's two scan rows and d1, d2 the two D vectors; SUMMED: s1
+// already holds s_fwd + s_bwd and d1 holds D_fwd + D_bwd (s2, d2 unused) --
+// staged in LDS by a caller that reuses them over many tokens.
 template <class IO, int TL, int NV, bool SUMMED = false>
-__device__ __forceinline__ void norm_finish(const typename IO::raw (&xr)[NV], const typename IO::raw (&zr)[NV],
-                                            const float* s1, const float* s2, const float* d1, const float* d2,
-                                            const float* lnw, const float* lnb, float eps, typename IO::elem* ob,
-                                            int E, int lane) {
+__device__ __forceinline__ void norm_finish_f(const float (&xv)[NV][IO::V], const typename IO::raw (&zr)[NV],
+                                              const float* s1, const float* s2, const float* d1, const float* d2,
+                                              const float* lnw, const float* lnb, float eps, typename IO::elem* ob,
+                                              int E, int lane) {
     constexpr int V = IO::V;
     float y[NV][V];
     float sum = 0.f;
@@ -97,7 +98,7 @@ __device__ __forceinline__ void norm_finish(const typename IO::raw (&xr)[NV], co
                 }
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    y[v][k + q] = fmaf(ds[q], raw_at(xr[v], k + q), sa[q]);
+                    y[v][k + q] = fmaf(ds[q], xv[v][k + q], sa[q]);
                     sum += y[v][k + q];
                 }
             }
@@ -137,6 +138,20 @@ __device__ __forceinline__ void norm_finish(const typename IO::raw (&xr)[NV], co
             store_vec<true>(ob + c, o);
         }
     }
+}
+
+// norm_finish_f on the token's raw x vectors.
+template <class IO, int TL, int NV, bool SUMMED = false>
+__device__ __forceinline__ void norm_finish(const typename IO::raw (&xr)[NV], const typename IO::raw (&zr)[NV],
+                                            const float* s1, const float* s2, const float* d1, const float* d2,
+                                            const float* lnw, const float* lnb, float eps, typename IO::elem* ob,
+                                            int E, int lane) {
+    float xv[NV][IO::V];
+#pragma unroll
+    for (int v = 0; v < NV; ++v)
+#pragma unroll
+        for (int k = 0; k < IO::V; ++k) xv[v][k] = raw_at(xr[v], k);
+    norm_finish_f<IO, TL, NV, SUMMED>(xv, zr, s1, s2, d1, d2, lnw, lnb, eps, ob, E, lane);
 }
 
 // NaN in every channel of the token (a masked token with an invalid index).

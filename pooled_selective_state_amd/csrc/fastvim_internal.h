@@ -75,9 +75,10 @@ hipError_t launch_conv_epilogue(const Geom& g, const void* x, const void* z, con
 hipError_t launch_epilogue_norm(const Geom& g, const void* x, const void* z, const fastvim_params& p,
                                 const Workspace& ws, void* out, hipStream_t st);
 // Single-launch dense pooled layer (fused.hip).
-// norm: with the post-SSM LayerNorm (FASTVIM_FLAG_POST_NORM).
-bool fused_supported(const Geom& g, bool norm, bool local);
-bool fused_preferred(const Geom& g, bool norm, bool local);  // the default path for this geometry is the single launch
+// norm: with the post-SSM LayerNorm (FASTVIM_FLAG_POST_NORM); conv: with the
+// producer Conv1D computed on load (FASTVIM_FLAG_CONV; COLS only).
+bool fused_supported(const Geom& g, bool norm, bool local, bool conv);
+bool fused_preferred(const Geom& g, bool norm, bool local, bool conv);  // the default path is the single launch
 hipError_t launch_fused(const Geom& g, const void* x, const void* z, const fastvim_params& p, const Workspace& ws,
                         void* out, hipStream_t st);
 hipError_t launch_zero_sync(const Workspace& ws, int64_t n, hipStream_t st);

@@ -47,6 +47,7 @@
 // waits for them to complete, then bumps the counter; a consumer polls the
 // counter, then executes an agent-scope acquire (invalidating its CU's L1 and
 // its XCD's L2) before reading with ordinary loads.
+#include "conv_common.h"
 #include "epilogue_norm.h"
 #include "scan_core.h"
 
@@ -77,6 +78,8 @@ struct FusedArgs {
     const float* ln_w;  // post-SSM LayerNorm (NORM instances)
     const float* ln_b;
     float ln_eps;
+    const float* conv_w;  // producer Conv1D computed on load (CONV instances, COLS)
+    const float* conv_b;
     float pool_norm;  // pool_scale / P
     unsigned* sync;  // [0] ticket, [1] status, [2, 2+B) rowsDone, [2+B, 2+2B) scanDone
     unsigned spin_limit;  // polls before a wait gives up
@@ -174,7 +177,7 @@ __device__ void poison_scan_rows(const FusedArgs& a, int64_t b, int64_t e0, int 
 __device__ __forceinline__ float silu(float q) { return q * __builtin_amdgcn_rcpf(1.f + __expf(-q)); }
 
 // ---------------------------------------------------------------- A items
-template <class IO>
+template <class IO, bool CONV>
 __device__ void item_pool_proj(const FusedArgs& a, int64_t b, int k, float* lds) {
     constexpr int V = IO::V;
     using elem = typename IO::elem;
@@ -195,7 +198,7 @@ __device__ void item_pool_proj(const FusedArgs& a, int64_t b, int k, float* lds)
     float* part = urow + (int64_t)a.RG * E;  // [RG][NO][KS]
 
     const int pstr = (int)p_stride;
-    const bool segment = !cols && a.RG > 1;
+    const bool segment = !CONV && !cols && a.RG > 1;  // (CONV: COLS only)
     if (segment) {
         // ROWS with RG adjacent scan positions (columns) per item: their
         // tokens in one grid row are one contiguous segment of RG E elements;
@@ -240,9 +243,49 @@ __device__ void item_pool_proj(const FusedArgs& a, int64_t b, int k, float* lds)
         }
         __syncthreads();
     }
+    ConvW<V> cwl;  // CONV: this lane's channels' taps and bias
+    if (CONV && g < G) load_conv_w<V>(a.conv_w, a.conv_b, c * V, cwl);
     for (int pos = 0; pos < (segment ? 0 : npos); ++pos) {
         const int64_t t = t0 + pos;
-        if (g < G) {
+        if (CONV && g < G) {
+            // COLS with the producer Conv1D: lane group g takes the run of grid
+            // row t's tokens [g L, g L + L) in sequence order and slides the
+            // conv's window of three raw vectors over it (a halo of three at
+            // the run's start, the previous grid row's last tokens for the
+            // first run), 8 allocating loads in flight per lane
+            const elem* ximg = x + b * a.h * a.w * E;
+            const int coff = c * V, iE = (int)E;
+            const int L = (int)((P + G - 1) / G);
+            const int p0 = g * L, p1 = p0 + L < (int)P ? p0 + L : (int)P;
+            float acc[V];
+#pragma unroll
+            for (int v = 0; v < V; ++v) acc[v] = 0.f;
+            if (p0 < p1) {
+                raw w3, w2, w1;
+                load_halo<IO, true>(ximg, coff, iE, (int)t, p0, (int)a.h, (int)a.w, w3, w2, w1);
+                const elem* cell = ximg + (coff + ((int)t * (int)a.w + p0) * iE);
+                for (int p = p0; p < p1; p += 8) {
+                    raw r[8];
+#pragma unroll
+                    for (int q = 0; q < 8; ++q)
+                        if (p + q < p1) r[q] = load_raw<false>(cell + (p - p0 + q) * iE);
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) {
+                        if (p + q < p1) {
+                            float xc[V];
+                            conv_window<IO>(w3, w2, w1, r[q], cwl, xc);
+#pragma unroll
+                            for (int v = 0; v < V; ++v) acc[v] += xc[v];
+                            w3 = w2;
+                            w2 = w1;
+                            w1 = r[q];
+                        }
+                    }
+                }
+            }
+#pragma unroll
+            for (int v = 0; v < V; ++v) red[g * (int)E + coff + v] = acc[v];
+        } else if (g < G) {
             // wave-uniform base, 32-bit lane offsets (an image holds < 2^31 elements)
             const elem* base = x + b * a.h * a.w * E + (cols ? t * a.w * E : t * E);
             const int coff = c * V;
@@ -326,7 +369,7 @@ __device__ __forceinline__ void scan_sum(const FusedArgs& a, int64_t b, int64_t 
 // Grid rows [k*RE, k*RE + RE) of image b.  x and z are read for the last time
 // (non-temporal), out is written once (non-temporal).  Lane (c, g) handles the
 // row's tokens g + G*m in batches of kEU, all loads of a batch issued first.
-template <class IO, bool COLS>
+template <class IO, bool COLS, bool CONV>
 __device__ void item_epilogue(const FusedArgs& a, int64_t b, int k) {
     constexpr int V = IO::V;
     using elem = typename IO::elem;
@@ -348,6 +391,8 @@ __device__ void item_epilogue(const FusedArgs& a, int64_t b, int k) {
     for (int v = 0; v < V; ++v) dsum[v] = a.pf.D[col + v] + a.pb.D[col + v];
 
     const int iw = (int)w, iE = (int)E, coff = (int)col;
+    ConvW<V> cwl;  // CONV: this lane's channels' taps and bias
+    if (CONV) load_conv_w<V>(a.conv_w, a.conv_b, coff, cwl);
     for (int64_t i = i0; i < i1; ++i) {
         // wave-uniform row bases, 32-bit lane offsets
         const int64_t rowoff = (b * a.h + i) * w * E;
@@ -356,6 +401,41 @@ __device__ void item_epilogue(const FusedArgs& a, int64_t b, int k) {
         elem* orow = static_cast<elem*>(a.out) + rowoff;
         float srow[V];
         if (COLS) scan_sum<V>(a, b, i, col, srow);
+        if (CONV) {
+            // COLS with the producer Conv1D: lane group g takes the run of the
+            // row's tokens [g L, g L + L) and slides the conv's window over it
+            // (halo of three at its start, from the caches), kEU tokens of x
+            // and z loaded at a time
+            const int L = (iw + G - 1) / G;
+            const int ja = g * L, jb = ja + L < iw ? ja + L : iw;
+            if (ja >= jb) continue;
+            raw w3, w2, w1;
+            load_halo<IO, true>(static_cast<const elem*>(a.x) + b * a.h * w * E, coff, iE, (int)i, ja, (int)a.h, iw,
+                                w3, w2, w1);
+            for (int j = ja; j < jb; j += kEU) {
+                raw xv[kEU], zv[kEU];
+#pragma unroll
+                for (int m = 0; m < kEU; ++m) {
+                    if (j + m < jb) {
+                        xv[m] = load_raw<true>(xr + (coff + (j + m) * iE));
+                        zv[m] = load_raw<true>(zr + (coff + (j + m) * iE));
+                    }
+                }
+#pragma unroll
+                for (int m = 0; m < kEU; ++m) {
+                    if (j + m >= jb) continue;
+                    float xc[V], o[V];
+                    conv_window<IO>(w3, w2, w1, xv[m], cwl, xc);
+                    w3 = w2;
+                    w2 = w1;
+                    w1 = xv[m];
+#pragma unroll
+                    for (int v = 0; v < V; ++v) o[v] = (srow[v] + dsum[v] * xc[v]) * silu(raw_at(zv[m], v));
+                    store_vec<true>(orow + (coff + (j + m) * iE), o);
+                }
+            }
+            continue;
+        }
         for (int j0 = g; j0 < iw; j0 += G * kEU) {
             raw xv[kEU], zv[kEU];
 #pragma unroll
@@ -490,7 +570,7 @@ __device__ void item_epilogue_rows(const FusedArgs& a, int64_t b, int k, float* 
 // per-token norm epilogue, the next two tokens' x and z loads issued before
 // the current two are computed.  ROWS tokens read their scan rows through
 // the caches.
-template <class IO, bool COLS>
+template <class IO, bool COLS, bool CONV>
 __device__ void item_epilogue_norm(const FusedArgs& a, int64_t b, int k, float* lds) {
     using raw = typename IO::raw;
     using elem = typename IO::elem;
@@ -508,11 +588,14 @@ __device__ void item_epilogue_norm(const FusedArgs& a, int64_t b, int k, float* 
     float* gw = lds + E;          // [E] norm weight
     float* gb = lds + 2 * E;      // [E] norm bias
     float* srow = lds + 3 * E;    // [E] COLS: s_fwd + s_bwd of the current grid row
+    float* cwt = lds + 4 * E;     // CONV: [E][4] taps, then [E] bias
     for (int e = tid; e < E; e += kFT) {
         ds[e] = a.pf.D[e] + a.pb.D[e];
         gw[e] = a.ln_w[e];
         gb[e] = a.ln_b[e];
     }
+    if (CONV)
+        for (int e = tid; e < 5 * E; e += kFT) cwt[e] = e < 4 * E ? a.conv_w[e] : a.conv_b[e - 4 * E];
     __syncthreads();
     const int lane = tid % kNormTL, team = tid / kNormTL;
     const int64_t i0 = (int64_t)k * a.RE;
@@ -528,6 +611,62 @@ __device__ void item_epilogue_norm(const FusedArgs& a, int64_t b, int k, float* 
             const float* s2 = a.s_b + (b * a.T + i) * E;
             for (int e = tid; e < E; e += kFT) srow[e] = s1[e] + s2[e];
             __syncthreads();
+        }
+        if (CONV) {
+            // the producer Conv1D on load (COLS): team `team` takes the run of
+            // the row's tokens [team L, team L + L) in sequence order, each
+            // lane sliding the conv's window of three raw vectors over its
+            // vectors (halo of three at the run's start, from the caches);
+            // the next token's x and z are loaded before the current one is
+            // computed
+            const int L = (w + kTeams - 1) / kTeams;
+            const int ja = team * L, jb = ja + L < w ? ja + L : w;
+            if (ja < jb) {
+                const elem* ximg = x + img * E;
+                raw w3[kNormNV], w2[kNormNV], w1[kNormNV], cx[kNormNV], cz[kNormNV], nx[kNormNV], nz[kNormNV];
+#pragma unroll
+                for (int v = 0; v < kNormNV; ++v) {
+                    const int c = (v * kNormTL + lane) * IO::V;
+                    if (c < E) load_halo<IO, true>(ximg, c, E, (int)i, ja, (int)a.h, w, w3[v], w2[v], w1[v]);
+                }
+                norm_load<IO, kNormTL, kNormNV>(x + (img + i * w + ja) * E, z + (img + i * w + ja) * E, E, lane,
+                                                nx, nz);
+                for (int j = ja; j < jb; ++j) {
+#pragma unroll
+                    for (int v = 0; v < kNormNV; ++v) {
+                        cx[v] = nx[v];
+                        cz[v] = nz[v];
+                    }
+                    if (j + 1 < jb)
+                        norm_load<IO, kNormTL, kNormNV>(x + (img + i * w + j + 1) * E, z + (img + i * w + j + 1) * E,
+                                                        E, lane, nx, nz);
+                    float xc[kNormNV][IO::V];
+#pragma unroll
+                    for (int v = 0; v < kNormNV; ++v) {
+                        const int c = (v * kNormTL + lane) * IO::V;
+                        if (c < E) {
+#pragma unroll
+                            for (int q = 0; q < IO::V; ++q) {
+                                const f32x4 t4 = *reinterpret_cast<const f32x4*>(cwt + (c + q) * kTaps);
+                                float av = fmaf(t4.w, raw_at(cx[v], q), cwt[4 * E + c + q]);
+                                av = fmaf(t4.z, raw_at(w1[v], q), av);
+                                av = fmaf(t4.y, raw_at(w2[v], q), av);
+                                av = fmaf(t4.x, raw_at(w3[v], q), av);
+                                xc[v][q] = conv_silu_f(av);
+                            }
+                            w3[v] = w2[v];
+                            w2[v] = w1[v];
+                            w1[v] = cx[v];
+                        } else {
+#pragma unroll
+                            for (int q = 0; q < IO::V; ++q) xc[v][q] = 0.f;
+                        }
+                    }
+                    norm_finish_f<IO, kNormTL, kNormNV, true>(xc, cz, srow, nullptr, ds, nullptr, gw, gb, a.ln_eps,
+                                                              out + (img + i * w + j) * E, E, lane);
+                }
+            }
+            continue;
         }
         // the next pair's x and z are loaded before the current pair is computed
         raw nx1[kNormNV], nz1[kNormNV], nx2[kNormNV], nz2[kNormNV];
@@ -572,8 +711,10 @@ __device__ void item_epilogue_norm(const FusedArgs& a, int64_t b, int k, float* 
 // ---------------------------------------------------------------- kernel
 // LONG: scans longer than resident_tmax<RMAX>() steps (their S items stage the
 // x_proj rows chunk by chunk).
-template <class IO, bool COLS, int RMAX, bool NORM, bool LOCAL, bool LONG>
+// CONV: the producer Conv1D computed where x is read (COLS only).
+template <class IO, bool COLS, int RMAX, bool NORM, bool LOCAL, bool LONG, bool CONV>
 __global__ void __launch_bounds__(kFT) fused_layer_kernel(FusedArgs a) {
+    static_assert(!CONV || (COLS && !LOCAL), "the Conv1D on load: COLS layers without the local scan");
     __shared__ FusedSmem sm;
     __shared__ unsigned s_ticket;
     if (threadIdx.x == 0)
@@ -589,7 +730,7 @@ __global__ void __launch_bounds__(kFT) fused_layer_kernel(FusedArgs a) {
     int64_t r = off % a.iv_sz[iv];
     if (slot < a.B) {
         if (r < a.nA) {
-            item_pool_proj<IO>(a, slot, (int)r, sm.buf);
+            item_pool_proj<IO, CONV>(a, slot, (int)r, sm.buf);
             return;
         }
         r -= a.nA;
@@ -616,8 +757,8 @@ __global__ void __launch_bounds__(kFT) fused_layer_kernel(FusedArgs a) {
         }
         r -= a.nS;
     }
-    if (NORM) item_epilogue_norm<IO, COLS>(a, slot - a.LE, (int)r, sm.buf);
-    else if (COLS) item_epilogue<IO, true>(a, slot - a.LE, (int)r);
+    if (NORM) item_epilogue_norm<IO, COLS, CONV>(a, slot - a.LE, (int)r, sm.buf);
+    else if (COLS) item_epilogue<IO, true, CONV>(a, slot - a.LE, (int)r);
     else item_epilogue_rows<IO>(a, slot - a.LE, (int)r, sm.buf);
 }
 
@@ -629,8 +770,11 @@ __global__ void zero_sync_kernel(unsigned* sync, int64_t n) {
 // Item sizes and ticket layout for a geometry; false if not covered.  norm:
 // with the post-SSM LayerNorm (E items of whole grid rows, E / V <= 128);
 // local: with LBMamba's local backward scan (not with the norm).
-bool plan(const Geom& g, FusedArgs* a, bool norm, bool local) {
+bool plan(const Geom& g, FusedArgs* a, bool norm, bool local, bool conv) {
     if (!g.pooled || g.masked || g.B < 1 || (norm && local)) return false;
+    // the producer Conv1D on load: COLS (its sequence runs along the grid
+    // rows the items stream), without the local scan
+    if (conv && (g.axis != FASTVIM_POOL_COLS || local)) return false;
     // the scan items hold a whole sequence's x_proj rows in LDS when they fit,
     // else one chunk of them at a time
     const int64_t tmax = g.R <= 16 ? resident_tmax<16>() : g.R <= 32 ? resident_tmax<32>() : resident_tmax<64>();
@@ -641,6 +785,7 @@ bool plan(const Geom& g, FusedArgs* a, bool norm, bool local) {
     const int64_t VE = g.E / V;
     if (VE > kFT) return false;
     if (norm && VE > kNormTL * kNormNV) return false;
+    if (norm && (conv ? 9 : 4) * g.E > kLdsFloats) return false;  // norm items' per-channel vectors in LDS
     const int G = (int)(kFT / VE);
     const int64_t NO = 2 * g.NX;
     int KS = (int)(kFT / NO);
@@ -731,11 +876,18 @@ bool plan(const Geom& g, FusedArgs* a, bool norm, bool local) {
 
 template <class IO, int RMAX, bool NORM, bool LOCAL, bool LONG>
 hipError_t fused_launch_l(const FusedArgs& a, hipStream_t st) {
+    if constexpr (!LOCAL) {
+        if (a.conv_w) {  // plan() took the Conv1D on load for COLS only
+            hipLaunchKernelGGL((fused_layer_kernel<IO, true, RMAX, NORM, false, LONG, true>), dim3((unsigned)a.total),
+                               dim3(kFT), 0, st, a);
+            return hipGetLastError();
+        }
+    }
     if (a.axis == FASTVIM_POOL_COLS)
-        hipLaunchKernelGGL((fused_layer_kernel<IO, true, RMAX, NORM, LOCAL, LONG>), dim3((unsigned)a.total), dim3(kFT),
-                           0, st, a);
+        hipLaunchKernelGGL((fused_layer_kernel<IO, true, RMAX, NORM, LOCAL, LONG, false>), dim3((unsigned)a.total),
+                           dim3(kFT), 0, st, a);
     else
-        hipLaunchKernelGGL((fused_layer_kernel<IO, false, RMAX, NORM, LOCAL, LONG>), dim3((unsigned)a.total),
+        hipLaunchKernelGGL((fused_layer_kernel<IO, false, RMAX, NORM, LOCAL, LONG, false>), dim3((unsigned)a.total),
                            dim3(kFT), 0, st, a);
     return hipGetLastError();
 }
@@ -761,22 +913,26 @@ hipError_t fused_launch_io(const FusedArgs& a, hipStream_t st, bool local) {
 
 }  // namespace
 
-bool fused_supported(const Geom& g, bool norm, bool local) {
+bool fused_supported(const Geom& g, bool norm, bool local, bool conv) {
     FusedArgs a;
-    return plan(g, &a, norm, local);
+    return plan(g, &a, norm, local, conv);
 }
 
-bool fused_preferred(const Geom& g, bool norm, bool local) {
+bool fused_preferred(const Geom& g, bool norm, bool local, bool conv) {
     // The pipeline's fixed costs (scan latency per image, fill and drain)
     // pay off once an image's x is several MB: measured faster than the stage
     // kernels at 2048^2 (25 MB fp32, 12.6 MB bf16), slower at 1024^2 (6.3 MB)
     // and below.
     // With the norm, ROWS reads each token's scan rows through the caches and
     // measured slower than its stage kernels; COLS (a scan row per grid row,
-    // staged in LDS) is faster.
+    // staged in LDS) is faster in fp32 (2048^2: 1.90 against 2.31 ms; with
+    // the conv on load 2.23 against 3.60 ms for the conv written out and the
+    // stage kernels).  In bf16 the norm's instances need 133 and 140 VGPRs,
+    // one workgroup per CU, and measured slower than the stage kernels
+    // (1.92 against 1.49 ms; with the conv 3.04 against 2.16 ms).
     const int64_t esz = g.io == FASTVIM_BF16 ? 2 : 4;
-    if (norm && g.axis != FASTVIM_POOL_COLS) return false;
-    return g.h * g.w * g.E * esz >= (8ll << 20) && fused_supported(g, norm, local);
+    if (norm && (g.axis != FASTVIM_POOL_COLS || g.io == FASTVIM_BF16)) return false;
+    return g.h * g.w * g.E * esz >= (8ll << 20) && fused_supported(g, norm, local, conv);
 }
 
 hipError_t launch_zero_sync(const Workspace& ws, int64_t n, hipStream_t st) {
@@ -789,12 +945,15 @@ hipError_t launch_fused(const Geom& g, const void* x, const void* z, const fastv
     FusedArgs a;
     const bool norm = (p.flags & FASTVIM_FLAG_POST_NORM) != 0;
     const bool local = (p.flags & FASTVIM_FLAG_LOCAL_BWD) != 0;
-    if (!plan(g, &a, norm, local)) return hipErrorInvalidValue;
+    const bool conv = (p.flags & FASTVIM_FLAG_CONV) != 0;
+    if (!plan(g, &a, norm, local, conv)) return hipErrorInvalidValue;
     a.x = x; a.z = z; a.out = out;
     a.pf = p.fwd; a.pb = p.bwd;
     a.ln_w = norm ? p.ln_weight : nullptr;
     a.ln_b = norm ? p.ln_bias : nullptr;
     a.ln_eps = norm ? p.ln_eps : 0.f;
+    a.conv_w = conv ? p.conv_w : nullptr;
+    a.conv_b = conv ? p.conv_b : nullptr;
     a.u = ws.u; a.xdbl = ws.xdbl; a.s_f = ws.s_f; a.s_b = ws.s_b;
     a.sync = ws.sync;
     return g.io == FASTVIM_BF16 ? fused_launch_io<IoBf16>(a, st, local) : fused_launch_io<IoF32>(a, st, local);

@@ -78,9 +78,10 @@ def test_conv_layer(shape, axis, io):
                torch.float32 if io == "f32" else torch.bfloat16, "conv %s %s axis %d" % (shape, io, axis))
 
 
-def test_conv_ignores_fused_flag():
-    """The single launch does not take the conv: FASTVIM_FLAG_FUSED falls back
-    to the stage kernels and gives the same result."""
+def test_conv_fused_flag_paths():
+    """FASTVIM_FLAG_FUSED: the single launch computes the conv on load for
+    COLS (equal to the stage kernels within rounding); ROWS layers without the
+    norm keep the stage kernels (bit for bit the staged call)."""
     B, h, w, E, R = 2, 6, 5, 32, 4
     rng = np.random.default_rng(61)
     x, z = (rng.standard_normal((B, h, w, E)).astype(np.float32) for _ in range(2))
@@ -88,6 +89,56 @@ def test_conv_ignores_fused_flag():
     conv = rand_conv(rng, E)
     a = host(gpu_call(x, z, prm, P.POOL_COLS, conv=conv, flags=P.FLAG_FUSED).run())
     b = host(gpu_call(x, z, prm, P.POOL_COLS, conv=conv, flags=P.FLAG_STAGED).run())
+    check(a, b, FP32_TOL, "COLS single launch vs stage kernels")
+    a = host(gpu_call(x, z, prm, P.POOL_ROWS, conv=conv, flags=P.FLAG_FUSED).run())
+    b = host(gpu_call(x, z, prm, P.POOL_ROWS, conv=conv, flags=P.FLAG_STAGED).run())
+    assert np.array_equal(a, b)
+
+
+# COLS layers on the single launch with the conv on load: grids whose runs
+# of the conv's window cross grid rows (the first run of a row takes its halo
+# from the previous row) and reach the image's start, and scans longer than
+# the resident length (the LONG instances)
+FUSED_SHAPES = SHAPES + [(2, 200, 6, 64, 12), (1, 97, 11, 40, 33), (3, 9, 130, 136, 20)]
+
+
+@pytest.mark.parametrize("norm", [False, True], ids=["plain", "norm"])
+@pytest.mark.parametrize("shape", FUSED_SHAPES, ids=["x".join(map(str, s)) for s in FUSED_SHAPES])
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_conv_single_launch(shape, io, norm):
+    """out, its D = 0 twin, the pooled tokens and both scan outputs of the
+    single launch with the Conv1D computed on load (and the post-SSM
+    LayerNorm), against the oracle."""
+    B, h, w, E, R = shape
+    rng = np.random.default_rng(zlib.crc32(repr(("conv-fused", shape, io, norm)).encode()))
+    x = rng.standard_normal((B, h, w, E)).astype(np.float32)
+    z = rng.standard_normal((B, h, w, E)).astype(np.float32)
+    if io == "bf16":
+        x, z = round_to_bf16(x), round_to_bf16(z)
+    prm = {"fwd": rand_dir(rng, E, 16, R, 0.1), "bwd": rand_dir(rng, E, 16, R, 0.1)}
+    conv = rand_conv(rng, E)
+    ln = rand_ln(rng, E) if norm else None
+    block_check(x, z, prm, conv, P.POOL_COLS, FP32_TOL if io == "f32" else BF16_TOL,
+                torch.float32 if io == "f32" else torch.bfloat16,
+                "single launch conv%s %s %s" % (" + norm" if norm else "", shape, io), ln=ln, flags=P.FLAG_FUSED)
+
+
+def test_conv_single_launch_options():
+    """The single launch with the conv on load and the pool scale; with the
+    local backward scan the conv goes to the stage kernels (same result as
+    the staged call, bit for bit)."""
+    B, h, w, E, R = 2, 19, 13, 64, 6
+    rng = np.random.default_rng(65)
+    x, z = (rng.standard_normal((B, h, w, E)).astype(np.float32) for _ in range(2))
+    prm = {"fwd": rand_dir(rng, E, 16, R, 0.1), "bwd": rand_dir(rng, E, 16, R, 0.1)}
+    conv = rand_conv(rng, E)
+    call = gpu_call(x, z, prm, P.POOL_COLS, conv=conv, flags=P.FLAG_FUSED, pool_scale=0.25)
+    out = host(call.run())
+    torch.cuda.synchronize()
+    ref = oracle.layer(x, z, prm["fwd"], prm["bwd"], P.POOL_COLS, conv=conv, pool_scale=0.25)
+    check(out, ref, FP32_TOL, "single launch conv, pool scale 0.25")
+    a = host(gpu_call(x, z, prm, P.POOL_COLS, conv=conv, flags=P.FLAG_FUSED | P.FLAG_LOCAL_BWD).run())
+    b = host(gpu_call(x, z, prm, P.POOL_COLS, conv=conv, flags=P.FLAG_STAGED | P.FLAG_LOCAL_BWD).run())
     assert np.array_equal(a, b)
 
 
@@ -198,8 +249,9 @@ def test_conv_unpooled(axis, norm):
 
 @pytest.mark.parametrize("axis", (P.POOL_COLS, P.POOL_ROWS))
 def test_conv_norm_block_full_size_2048(axis):
-    """The whole block at 2048^2 on the default path (the single launch on the
-    written-out conv for COLS), images covering the pipeline's intervals."""
+    """The whole block at 2048^2 on the default path (COLS: the single launch
+    with the conv on load; ROWS: the conv written out, then the layer),
+    images covering the pipeline's intervals."""
     cfg = C.HIRES_2048
     wl = draw_workload(cfg)
     rng = np.random.default_rng(63)
