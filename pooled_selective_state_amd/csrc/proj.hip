@@ -43,6 +43,7 @@ proj_kernel(const Elem* __restrict__ src, int map_axis, int64_t M, int64_t T, in
     const int ri = lane & 15, kk = lane >> 4;
     const int NO = 2 * NX;
     const int64_t m0 = (int64_t)blockIdx.x * 16;
+    const int c0 = (int)blockIdx.y * CT * 16;  // this workgroup's first output column
 
     // Rows past M and columns past the computed ones read a valid row instead
     // (the last token, a weight row in range): their outputs are never stored,
@@ -57,7 +58,7 @@ proj_kernel(const Elem* __restrict__ src, int map_axis, int64_t M, int64_t T, in
     const float* wrow[CT];
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
-        const int o = ct * 16 + ri;
+        const int o = c0 + ct * 16 + ri;
         wrow[ct] = (o < NX ? Wf + (int64_t)o * E : (o < NO ? Wb + (int64_t)(o - NX) * E : Wf)) + 4 * kk;
     }
 
@@ -116,7 +117,7 @@ proj_kernel(const Elem* __restrict__ src, int map_axis, int64_t M, int64_t T, in
 #pragma unroll
         for (int q = 1; q < kPW; ++q) v += red[q][ct][src_idx];
         const int64_t mm = m0 + i;
-        const int o = ct * 16 + j;
+        const int o = c0 + ct * 16 + j;
         if (mm < M && o < nout) xdbl[mm * NO + o] = v;
     }
 }
@@ -212,11 +213,28 @@ proj_rows_kernel(const Elem* __restrict__ src, int map_axis, int64_t M, int64_t 
 
 constexpr int kRowsRT = 2;                       // row tiles per wave in proj_rows_kernel
 constexpr int64_t kRowsMinTokens = 64 * 1024;    // token count from which it is used
+constexpr int kColSplit = 2;                     // column groups per row tile when row tiles are few ...
+constexpr int64_t kColSplitBelow = 512;          // ... fewer than this (two workgroups per CU)
 
 template <class Elem, int CT>
 hipError_t proj_launch(const Elem* src, int map_axis, const Geom& g, const fastvim_params& p, const Workspace& ws,
                        int nout, hipStream_t st) {
     const int64_t M = g.B * g.T;
+    if (M < kRowsMinTokens && CT > 1) {
+        // Few 16-row tiles: split the output columns over kColSplit
+        // workgroups per row tile, so that there are enough workgroups (two
+        // waves per SIMD) for the MFMAs of one to run while another waits for
+        // its next operands.
+        const int64_t rt = (M + 15) / 16;
+        if (rt < kColSplitBelow) {
+            constexpr int CTS = (CT + kColSplit - 1) / kColSplit;
+            const int ns = (CT + CTS - 1) / CTS;
+            hipLaunchKernelGGL((proj_kernel<Elem, CTS>), dim3((unsigned)rt, (unsigned)ns), dim3(64 * kPW), 0, st, src,
+                               map_axis, M, g.T, g.h, g.w, g.E, p.fwd.x_proj_w, p.bwd.x_proj_w, (int)g.NX, nout,
+                               ws.xdbl);
+            return hipGetLastError();
+        }
+    }
     if (M >= kRowsMinTokens) {
         const int64_t rows = 16 * kRowsRT * kPW;
         hipLaunchKernelGGL((proj_rows_kernel<Elem, CT, kRowsRT>), dim3((unsigned)((M + rows - 1) / rows)),
