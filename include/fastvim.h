@@ -207,12 +207,12 @@ typedef struct fastvim_params {
  *   x_conv[r, e] = silu(conv_b[e] + sum_{k<4} conv_w[e, k] * x[r - 3 + k, e])
  * and the layer runs on x_conv.  Dense pooled layers compute it where their
  * pool and output stages read x, so it is never written: the single launch
- * does so for COLS layers, with or without FASTVIM_FLAG_POST_NORM (and
- * without FASTVIM_FLAG_LOCAL_BWD), where it would run without the conv; the
- * stage kernels for the other dense layers without the norm.  Masked layers
- * -- whose conv runs along the kept tokens in the order given, r = k --
- * unpooled layers and the remaining layers with FASTVIM_FLAG_POST_NORM (ROWS,
- * or on the stage kernels) get x_conv written once into out first (in the I/O
+ * does so on both axes, with or without FASTVIM_FLAG_POST_NORM (and without
+ * FASTVIM_FLAG_LOCAL_BWD), where it would run without the conv; the stage
+ * kernels for the other dense layers without the norm.  Masked layers --
+ * whose conv runs along the kept tokens in the order given, r = k --
+ * unpooled layers and the remaining layers with FASTVIM_FLAG_POST_NORM (on
+ * the stage kernels) get x_conv written once into out first (in the I/O
  * element type: bf16 layers round it to bf16), and the layer then runs on it,
  * by the path it would take without the conv; fastvim_ssm_stage returns
  * FASTVIM_ERR_UNSUPPORTED for them.

@@ -26,8 +26,11 @@
 //   E(b, k)  once scanDone[b] == nS, repeat + skip + gate a block of image
 //            b: grid rows [k*RE, k*RE + RE) (COLS), or RE rows x CJ columns
 //            with the block's scan rows staged in LDS (ROWS); with the
-//            post-SSM LayerNorm, grid rows [k*RE, k*RE + RE) in teams of
-//            lanes per token (epilogue_norm.h), both orientations.
+//            post-SSM LayerNorm the same blocks in teams of lanes per token
+//            (epilogue_norm.h).
+// With the producer Conv1D (CONV instances) the pooling and output items
+// compute x_conv where they read x, walking runs of the conv's sequence:
+// along the grid rows (COLS) or down the columns (ROWS).
 // Items are numbered slot by slot, slot s = [A(s, *)] [S(s - LS, *)]
 // [E(s - LE, *)] with 1 <= LS <= LE (items outside [0, B) are left out), and
 // handed out through one atomic ticket counter.  A workgroup takes its ticket
@@ -198,7 +201,9 @@ __device__ void item_pool_proj(const FusedArgs& a, int64_t b, int k, float* lds)
     float* part = urow + (int64_t)a.RG * E;  // [RG][NO][KS]
 
     const int pstr = (int)p_stride;
-    const bool segment = !CONV && !cols && a.RG > 1;  // (CONV: COLS only)
+    // (ROWS with the conv: always the segment path, whose lane groups then
+    // walk runs of grid rows)
+    const bool segment = !cols && (a.RG > 1 || CONV);
     if (segment) {
         // ROWS with RG adjacent scan positions (columns) per item: their
         // tokens in one grid row are one contiguous segment of RG E elements;
@@ -208,7 +213,48 @@ __device__ void item_pool_proj(const FusedArgs& a, int64_t b, int k, float* lds)
         const int SW = a.RG * VE;  // lanes per segment
         const int Gw = kFT / SW;   // groups, each a share of the grid rows
         const int cw = tid % SW, gw = tid / SW;
-        if (gw < Gw && cw < npos * VE) {
+        if (CONV && gw < Gw && cw < npos * VE) {
+            // the conv's sequence runs down each column: group gw takes the
+            // run of grid rows [gw L, gw L + L), each lane sliding the window
+            // of three raw vectors down its column (halo of three at the
+            // run's top: the rows above, or the previous column's bottom
+            // rows), 8 allocating loads in flight per lane
+            const elem* ximg = x + b * a.h * a.w * E;
+            const elem* base = ximg + t0 * E;
+            const int coff = cw * V, iE = (int)E;
+            const int jcol = (int)t0 + cw / VE, ch = (cw - (cw / VE) * VE) * V;
+            ConvW<V> cws;
+            load_conv_w<V>(a.conv_w, a.conv_b, ch, cws);
+            const int L = (int)((P + Gw - 1) / Gw);
+            const int pa = gw * L, pb = pa + L < (int)P ? pa + L : (int)P;
+            float acc[V];
+#pragma unroll
+            for (int v = 0; v < V; ++v) acc[v] = 0.f;
+            if (pa < pb) {
+                raw w3, w2, w1;
+                load_halo<IO, false>(ximg, ch, iE, pa, jcol, (int)a.h, (int)a.w, w3, w2, w1);
+                for (int p = pa; p < pb; p += 8) {
+                    raw r[8];
+#pragma unroll
+                    for (int q = 0; q < 8; ++q)
+                        if (p + q < pb) r[q] = load_raw<false>(base + (coff + (p + q) * pstr));
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) {
+                        if (p + q < pb) {
+                            float xc[V];
+                            conv_window<IO>(w3, w2, w1, r[q], cws, xc);
+#pragma unroll
+                            for (int v = 0; v < V; ++v) acc[v] += xc[v];
+                            w3 = w2;
+                            w2 = w1;
+                            w1 = r[q];
+                        }
+                    }
+                }
+            }
+#pragma unroll
+            for (int v = 0; v < V; ++v) red[gw * SW * V + coff + v] = acc[v];
+        } else if (gw < Gw && cw < npos * VE) {
             const elem* base = x + b * a.h * a.w * E + t0 * E;
             const int coff = cw * V;
             float acc[V];
@@ -243,11 +289,11 @@ __device__ void item_pool_proj(const FusedArgs& a, int64_t b, int k, float* lds)
         }
         __syncthreads();
     }
-    ConvW<V> cwl;  // CONV: this lane's channels' taps and bias
-    if (CONV && g < G) load_conv_w<V>(a.conv_w, a.conv_b, c * V, cwl);
+    ConvW<V> cwl;  // CONV (COLS): this lane's channels' taps and bias
+    if (CONV && cols && g < G) load_conv_w<V>(a.conv_w, a.conv_b, c * V, cwl);
     for (int pos = 0; pos < (segment ? 0 : npos); ++pos) {
         const int64_t t = t0 + pos;
-        if (CONV && g < G) {
+        if (CONV && cols && g < G) {
             // COLS with the producer Conv1D: lane group g takes the run of grid
             // row t's tokens [g L, g L + L) in sequence order and slides the
             // conv's window of three raw vectors over it (a halo of three at
@@ -473,7 +519,7 @@ __device__ void item_epilogue(const FusedArgs& a, int64_t b, int k) {
 // the block's tokens (each row segment of the block is contiguous in memory)
 // in batches of kEU per lane, all loads of a batch issued first, walking the
 // block row by row without divisions.
-template <class IO>
+template <class IO, bool CONV>
 __device__ void item_epilogue_rows(const FusedArgs& a, int64_t b, int k, float* lds) {
     constexpr int V = IO::V;
     using elem = typename IO::elem;
@@ -524,6 +570,50 @@ __device__ void item_epilogue_rows(const FusedArgs& a, int64_t b, int k, float* 
     const elem* xb = static_cast<const elem*>(a.x) + base;
     const elem* zb = static_cast<const elem*>(a.z) + base;
     elem* ob = static_cast<elem*>(a.out) + base;
+    if (CONV) {
+        // the conv's sequence runs down the columns: lane group g takes the
+        // block's columns g, g + G, ... top to bottom, sliding the window
+        // (halo of three at the top: the rows above, or the previous
+        // column's bottom rows), kEU tokens of x and z loaded at a time
+        ConvW<V> cwl;
+        load_conv_w<V>(a.conv_w, a.conv_b, coff, cwl);
+        const elem* ximg = static_cast<const elem*>(a.x) + b * a.h * w * E;
+        for (int jj = g; jj < nj; jj += G) {
+            raw w3, w2, w1;
+            load_halo<IO, false>(ximg, coff, iE, (int)i0, (int)j0 + jj, (int)a.h, iw, w3, w2, w1);
+            const float* sv = lds + jj * iE + coff;
+            for (int ii = 0; ii < ni; ii += kEU) {
+                raw xv[kEU], zv[kEU];
+#pragma unroll
+                for (int m = 0; m < kEU; ++m) {
+                    if (ii + m < ni) {
+                        const int off = ((ii + m) * iw + jj) * iE + coff;
+                        xv[m] = load_raw<true>(xb + off);
+                        zv[m] = load_raw<true>(zb + off);
+                    }
+                }
+#pragma unroll
+                for (int m = 0; m < kEU; ++m) {
+                    if (ii + m >= ni) continue;
+                    float xc[V], o[V];
+                    conv_window<IO>(w3, w2, w1, xv[m], cwl, xc);
+                    w3 = w2;
+                    w2 = w1;
+                    w1 = xv[m];
+#pragma unroll
+                    for (int v = 0; v < V; v += 4) {
+                        const f32x4 s4 = *reinterpret_cast<const f32x4*>(sv + v);
+                        o[v] = (s4.x + dsum[v] * xc[v]) * silu(raw_at(zv[m], v));
+                        o[v + 1] = (s4.y + dsum[v + 1] * xc[v + 1]) * silu(raw_at(zv[m], v + 1));
+                        o[v + 2] = (s4.z + dsum[v + 2] * xc[v + 2]) * silu(raw_at(zv[m], v + 2));
+                        o[v + 3] = (s4.w + dsum[v + 3] * xc[v + 3]) * silu(raw_at(zv[m], v + 3));
+                    }
+                    store_vec<true>(ob + ((ii + m) * iw + jj) * iE + coff, o);
+                }
+            }
+        }
+        return;
+    }
     int ii = g / nj, jj = g - (g / nj) * nj;  // this lane's next token of the block
     while (ii < ni) {
         int off[kEU], sj[kEU];
@@ -563,14 +653,13 @@ __device__ void item_epilogue_rows(const FusedArgs& a, int64_t b, int k, float* 
     }
 }
 
-// Norm E items: grid rows [k*RE, k*RE + RE) of image b.  The per-channel
-// vectors (D_fwd + D_bwd, the norm's weight and bias) are staged in LDS once
-// per item and, for COLS, the summed scan row once per grid row; each team of
-// kNormTL lanes (a wave) then takes two tokens at a time and runs the
+// COLS norm E items: grid rows [k*RE, k*RE + RE) of image b.  The
+// per-channel vectors (D_fwd + D_bwd, the norm's weight and bias) are staged
+// in LDS once per item and the summed scan row once per grid row; each team
+// of kNormTL lanes (a wave) then takes two tokens at a time and runs the
 // per-token norm epilogue, the next two tokens' x and z loads issued before
-// the current two are computed.  ROWS tokens read their scan rows through
-// the caches.
-template <class IO, bool COLS, bool CONV>
+// the current two are computed.
+template <class IO, bool CONV>
 __device__ void item_epilogue_norm(const FusedArgs& a, int64_t b, int k, float* lds) {
     using raw = typename IO::raw;
     using elem = typename IO::elem;
@@ -587,7 +676,7 @@ __device__ void item_epilogue_norm(const FusedArgs& a, int64_t b, int k, float* 
     float* ds = lds;              // [E] D_fwd + D_bwd
     float* gw = lds + E;          // [E] norm weight
     float* gb = lds + 2 * E;      // [E] norm bias
-    float* srow = lds + 3 * E;    // [E] COLS: s_fwd + s_bwd of the current grid row
+    float* srow = lds + 3 * E;    // [E] s_fwd + s_bwd of the current grid row
     float* cwt = lds + 4 * E;     // CONV: [E][4] taps, then [E] bias
     for (int e = tid; e < E; e += kFT) {
         ds[e] = a.pf.D[e] + a.pb.D[e];
@@ -605,13 +694,13 @@ __device__ void item_epilogue_norm(const FusedArgs& a, int64_t b, int k, float* 
     const elem* z = static_cast<const elem*>(a.z);
     elem* out = static_cast<elem*>(a.out);
     for (int64_t i = i0; i < i1; ++i) {
-        if (COLS) {
-            __syncthreads();  // the previous row's tokens are done with srow
+        __syncthreads();  // the previous row's tokens are done with srow
+        {
             const float* s1 = a.s_f + (b * a.T + i) * E;
             const float* s2 = a.s_b + (b * a.T + i) * E;
             for (int e = tid; e < E; e += kFT) srow[e] = s1[e] + s2[e];
-            __syncthreads();
         }
+        __syncthreads();
         if (CONV) {
             // the producer Conv1D on load (COLS): team `team` takes the run of
             // the row's tokens [team L, team L + L) in sequence order, each
@@ -690,20 +779,128 @@ __device__ void item_epilogue_norm(const FusedArgs& a, int64_t b, int k, float* 
                 z2[v] = nz2[v];
             }
             if (j + 2 * kTeams < w) load_pair(j + 2 * kTeams);
-            if (COLS) {
-                norm_finish<IO, kNormTL, kNormNV, true>(x1, z1, srow, nullptr, ds, nullptr, gw, gb, a.ln_eps,
-                                                        out + c1 * E, E, lane);
-                if (two)
-                    norm_finish<IO, kNormTL, kNormNV, true>(x2, z2, srow, nullptr, ds, nullptr, gw, gb, a.ln_eps,
-                                                            out + c2 * E, E, lane);
-            } else {
-                norm_finish<IO, kNormTL, kNormNV>(x1, z1, a.s_f + (b * a.T + j) * E, a.s_b + (b * a.T + j) * E,
-                                                  a.pf.D, a.pb.D, gw, gb, a.ln_eps, out + c1 * E, E, lane);
-                if (two)
-                    norm_finish<IO, kNormTL, kNormNV>(x2, z2, a.s_f + (b * a.T + j2) * E,
-                                                      a.s_b + (b * a.T + j2) * E, a.pf.D, a.pb.D, gw, gb, a.ln_eps,
-                                                      out + c2 * E, E, lane);
+            norm_finish<IO, kNormTL, kNormNV, true>(x1, z1, srow, nullptr, ds, nullptr, gw, gb, a.ln_eps,
+                                                    out + c1 * E, E, lane);
+            if (two)
+                norm_finish<IO, kNormTL, kNormNV, true>(x2, z2, srow, nullptr, ds, nullptr, gw, gb, a.ln_eps,
+                                                        out + c2 * E, E, lane);
+        }
+    }
+}
+
+// ROWS norm E items: a block of grid rows [i0, i0 + RE) x columns
+// [j0, j0 + CJ) of image b.  The summed scan rows of the block's columns (one
+// per column: token (i, j) is scan position j) are staged in LDS once, with
+// the per-channel vectors; each team of kNormTL lanes then takes one token at
+// a time with the next one's x and z in flight: the block's tokens in
+// row-major order (each row segment of the block is contiguous), or, with
+// the producer Conv1D on load, whole columns of the block top to bottom (the
+// conv's sequence runs down the columns), sliding the conv's window (a halo
+// of three at the column's top: the rows above, or the previous column's
+// bottom rows).
+template <class IO, bool CONV>
+__device__ void item_epilogue_norm_rows(const FusedArgs& a, int64_t b, int k, float* lds) {
+    using raw = typename IO::raw;
+    using elem = typename IO::elem;
+    constexpr int kTeams = kFT / kNormTL;
+    const int tid = threadIdx.x;
+    const int w = (int)a.w, E = (int)a.E;
+    const int nJB = (w + a.CJ - 1) / a.CJ;
+    const int ib = k / nJB, jb = k - ib * nJB;
+    const int i0 = ib * a.RE, j0 = jb * a.CJ;
+    const int ni = i0 + a.RE < (int)a.h ? a.RE : (int)a.h - i0;
+    const int nj = j0 + a.CJ < w ? a.CJ : w - j0;
+    if (wait_scans(a, b)) {
+        poison_block<IO>(a, b, i0, ni, j0, nj);
+        return;
+    }
+    float* ds = lds;                          // [E] D_fwd + D_bwd
+    float* gw = lds + E;                      // [E] norm weight
+    float* gb = lds + 2 * E;                  // [E] norm bias
+    float* cwt = lds + 3 * E;                 // CONV: [E][4] taps, then [E] bias
+    float* srows = lds + (CONV ? 8 : 3) * E;  // [nj][E] s_fwd + s_bwd of the block's columns
+    for (int e = tid; e < E; e += kFT) {
+        ds[e] = a.pf.D[e] + a.pb.D[e];
+        gw[e] = a.ln_w[e];
+        gb[e] = a.ln_b[e];
+    }
+    if (CONV)
+        for (int e = tid; e < 5 * E; e += kFT) cwt[e] = e < 4 * E ? a.conv_w[e] : a.conv_b[e - 4 * E];
+    {
+        const float* s1 = a.s_f + (b * a.T + j0) * E;  // columns j0 .. are consecutive scan rows
+        const float* s2 = a.s_b + (b * a.T + j0) * E;
+        for (int q = 4 * tid; q < nj * E; q += 4 * kFT)
+            *reinterpret_cast<f32x4*>(srows + q) = load_raw<false>(s1 + q) + load_raw<false>(s2 + q);
+    }
+    __syncthreads();
+    const int lane = tid % kNormTL, team = tid / kNormTL;
+    const int64_t img = b * a.h * a.w;
+    const elem* x = static_cast<const elem*>(a.x);
+    const elem* z = static_cast<const elem*>(a.z);
+    elem* out = static_cast<elem*>(a.out);
+    if (!CONV) {
+        const int n = ni * nj;
+        raw nx[kNormNV], nz[kNormNV];
+        auto cell_of = [&](int q) { return img + (int64_t)(i0 + q / nj) * w + j0 + q % nj; };
+        if (team < n) norm_load<IO, kNormTL, kNormNV>(x + cell_of(team) * E, z + cell_of(team) * E, E, lane, nx, nz);
+        for (int q = team; q < n; q += kTeams) {
+            raw cx[kNormNV], cz[kNormNV];
+#pragma unroll
+            for (int v = 0; v < kNormNV; ++v) {
+                cx[v] = nx[v];
+                cz[v] = nz[v];
             }
+            if (q + kTeams < n)
+                norm_load<IO, kNormTL, kNormNV>(x + cell_of(q + kTeams) * E, z + cell_of(q + kTeams) * E, E, lane,
+                                                nx, nz);
+            norm_finish<IO, kNormTL, kNormNV, true>(cx, cz, srows + (q % nj) * E, nullptr, ds, nullptr, gw, gb,
+                                                    a.ln_eps, out + cell_of(q) * E, E, lane);
+        }
+        return;
+    }
+    const elem* ximg = x + img * E;
+    for (int jj = team; jj < nj; jj += kTeams) {
+        const int j = j0 + jj;
+        raw w3[kNormNV], w2[kNormNV], w1[kNormNV], cx[kNormNV], cz[kNormNV], nx[kNormNV], nz[kNormNV];
+#pragma unroll
+        for (int v = 0; v < kNormNV; ++v) {
+            const int c = (v * kNormTL + lane) * IO::V;
+            if (c < E) load_halo<IO, false>(ximg, c, E, i0, j, (int)a.h, w, w3[v], w2[v], w1[v]);
+        }
+        norm_load<IO, kNormTL, kNormNV>(x + (img + (int64_t)i0 * w + j) * E, z + (img + (int64_t)i0 * w + j) * E, E,
+                                        lane, nx, nz);
+        for (int ii = 0; ii < ni; ++ii) {
+            const int64_t cell = img + (int64_t)(i0 + ii) * w + j;
+#pragma unroll
+            for (int v = 0; v < kNormNV; ++v) {
+                cx[v] = nx[v];
+                cz[v] = nz[v];
+            }
+            if (ii + 1 < ni) norm_load<IO, kNormTL, kNormNV>(x + (cell + w) * E, z + (cell + w) * E, E, lane, nx, nz);
+            float xc[kNormNV][IO::V];
+#pragma unroll
+            for (int v = 0; v < kNormNV; ++v) {
+                const int c = (v * kNormTL + lane) * IO::V;
+                if (c < E) {
+#pragma unroll
+                    for (int q = 0; q < IO::V; ++q) {
+                        const f32x4 t4 = *reinterpret_cast<const f32x4*>(cwt + (c + q) * kTaps);
+                        float av = fmaf(t4.w, raw_at(cx[v], q), cwt[4 * E + c + q]);
+                        av = fmaf(t4.z, raw_at(w1[v], q), av);
+                        av = fmaf(t4.y, raw_at(w2[v], q), av);
+                        av = fmaf(t4.x, raw_at(w3[v], q), av);
+                        xc[v][q] = conv_silu_f(av);
+                    }
+                    w3[v] = w2[v];
+                    w2[v] = w1[v];
+                    w1[v] = cx[v];
+                } else {
+#pragma unroll
+                    for (int q = 0; q < IO::V; ++q) xc[v][q] = 0.f;
+                }
+            }
+            norm_finish_f<IO, kNormTL, kNormNV, true>(xc, cz, srows + jj * E, nullptr, ds, nullptr, gw, gb, a.ln_eps,
+                                                      out + cell * E, E, lane);
         }
     }
 }
@@ -714,7 +911,7 @@ __device__ void item_epilogue_norm(const FusedArgs& a, int64_t b, int k, float* 
 // CONV: the producer Conv1D computed where x is read (COLS only).
 template <class IO, bool COLS, int RMAX, bool NORM, bool LOCAL, bool LONG, bool CONV>
 __global__ void __launch_bounds__(kFT) fused_layer_kernel(FusedArgs a) {
-    static_assert(!CONV || (COLS && !LOCAL), "the Conv1D on load: COLS layers without the local scan");
+    static_assert(!CONV || !LOCAL, "the Conv1D on load: layers without the local scan");
     __shared__ FusedSmem sm;
     __shared__ unsigned s_ticket;
     if (threadIdx.x == 0)
@@ -757,9 +954,10 @@ __global__ void __launch_bounds__(kFT) fused_layer_kernel(FusedArgs a) {
         }
         r -= a.nS;
     }
-    if (NORM) item_epilogue_norm<IO, COLS, CONV>(a, slot - a.LE, (int)r, sm.buf);
+    if (NORM && COLS) item_epilogue_norm<IO, CONV>(a, slot - a.LE, (int)r, sm.buf);
+    else if (NORM) item_epilogue_norm_rows<IO, CONV>(a, slot - a.LE, (int)r, sm.buf);
     else if (COLS) item_epilogue<IO, true, CONV>(a, slot - a.LE, (int)r);
-    else item_epilogue_rows<IO>(a, slot - a.LE, (int)r, sm.buf);
+    else item_epilogue_rows<IO, CONV>(a, slot - a.LE, (int)r, sm.buf);
 }
 
 __global__ void zero_sync_kernel(unsigned* sync, int64_t n) {
@@ -772,9 +970,7 @@ __global__ void zero_sync_kernel(unsigned* sync, int64_t n) {
 // local: with LBMamba's local backward scan (not with the norm).
 bool plan(const Geom& g, FusedArgs* a, bool norm, bool local, bool conv) {
     if (!g.pooled || g.masked || g.B < 1 || (norm && local)) return false;
-    // the producer Conv1D on load: COLS (its sequence runs along the grid
-    // rows the items stream), without the local scan
-    if (conv && (g.axis != FASTVIM_POOL_COLS || local)) return false;
+    if (conv && local) return false;  // the producer Conv1D on load: without the local scan
     // the scan items hold a whole sequence's x_proj rows in LDS when they fit,
     // else one chunk of them at a time
     const int64_t tmax = g.R <= 16 ? resident_tmax<16>() : g.R <= 32 ? resident_tmax<32>() : resident_tmax<64>();
@@ -785,7 +981,8 @@ bool plan(const Geom& g, FusedArgs* a, bool norm, bool local, bool conv) {
     const int64_t VE = g.E / V;
     if (VE > kFT) return false;
     if (norm && VE > kNormTL * kNormNV) return false;
-    if (norm && (conv ? 9 : 4) * g.E > kLdsFloats) return false;  // norm items' per-channel vectors in LDS
+    // norm items' per-channel vectors in LDS (ROWS: and at least one column's scan row)
+    if (norm && (conv ? 9 : 4) * g.E > kLdsFloats) return false;
     const int G = (int)(kFT / VE);
     const int64_t NO = 2 * g.NX;
     int KS = (int)(kFT / NO);
@@ -810,14 +1007,17 @@ bool plan(const Geom& g, FusedArgs* a, bool norm, bool local, bool conv) {
     if (G * g.E + RG * g.E + RG * NO * KS > kLdsFloats) return false;
     // E items: about 200 KB of each stream.  COLS: RE whole grid rows.  ROWS:
     // RE rows x CJ columns, CJ as many columns as the LDS holds scan rows of.
+    // ROWS with the conv: 8 columns, so that a block is some 16 rows tall and
+    // the conv's halo of three rows per column stays small; with the norm,
+    // the LDS also holds the per-channel vectors.
     int64_t RE, CJ;
-    if (g.axis == FASTVIM_POOL_COLS || norm) {
+    if (g.axis == FASTVIM_POOL_COLS) {
         const int64_t row_bytes = g.w * g.E * esz;
         RE = (200 * 1024) / row_bytes;
         CJ = g.w;
     } else {
-        CJ = kLdsFloats / g.E;
-        if (CJ > 32) CJ = 32;
+        CJ = kLdsFloats / g.E - (norm ? (conv ? 8 : 3) : 0);
+        if (CJ > (conv ? 8 : 32)) CJ = conv ? 8 : 32;
         if (CJ > g.w) CJ = g.w;
         if (CJ < 1) return false;
         RE = (200 * 1024) / (CJ * g.E * esz);
@@ -877,9 +1077,13 @@ bool plan(const Geom& g, FusedArgs* a, bool norm, bool local, bool conv) {
 template <class IO, int RMAX, bool NORM, bool LOCAL, bool LONG>
 hipError_t fused_launch_l(const FusedArgs& a, hipStream_t st) {
     if constexpr (!LOCAL) {
-        if (a.conv_w) {  // plan() took the Conv1D on load for COLS only
-            hipLaunchKernelGGL((fused_layer_kernel<IO, true, RMAX, NORM, false, LONG, true>), dim3((unsigned)a.total),
-                               dim3(kFT), 0, st, a);
+        if (a.conv_w) {  // the Conv1D on load
+            if (a.axis == FASTVIM_POOL_COLS)
+                hipLaunchKernelGGL((fused_layer_kernel<IO, true, RMAX, NORM, false, LONG, true>),
+                                   dim3((unsigned)a.total), dim3(kFT), 0, st, a);
+            else
+                hipLaunchKernelGGL((fused_layer_kernel<IO, false, RMAX, NORM, false, LONG, true>),
+                                   dim3((unsigned)a.total), dim3(kFT), 0, st, a);
             return hipGetLastError();
         }
     }
@@ -923,15 +1127,16 @@ bool fused_preferred(const Geom& g, bool norm, bool local, bool conv) {
     // pay off once an image's x is several MB: measured faster than the stage
     // kernels at 2048^2 (25 MB fp32, 12.6 MB bf16), slower at 1024^2 (6.3 MB)
     // and below.
-    // With the norm, ROWS reads each token's scan rows through the caches and
-    // measured slower than its stage kernels; COLS (a scan row per grid row,
-    // staged in LDS) is faster in fp32 (2048^2: 1.90 against 2.31 ms; with
-    // the conv on load 2.23 against 3.60 ms for the conv written out and the
-    // stage kernels).  In bf16 the norm's instances need 133 and 140 VGPRs,
-    // one workgroup per CU, and measured slower than the stage kernels
-    // (1.92 against 1.49 ms; with the conv 3.04 against 2.16 ms).
+    // With the norm the single launch is faster in fp32 (2048^2, COLS: 1.90
+    // against 2.30 ms; ROWS, blocks of columns with their scan rows in LDS:
+    // 1.95 against 2.34 ms; with the conv on load 2.24 and 2.25 ms against
+    // 3.60 and 3.75 ms for the conv written out and the stage kernels).  In
+    // bf16 it is not: the COLS norm instances need 133 and 145 VGPRs (one
+    // workgroup per CU; 1.92 against 1.50 ms), ROWS measured the same as the
+    // stage kernels (1.50 ms), and with the conv both were slower (3.03 and
+    // 2.83 against 2.15 ms).
     const int64_t esz = g.io == FASTVIM_BF16 ? 2 : 4;
-    if (norm && (g.axis != FASTVIM_POOL_COLS || g.io == FASTVIM_BF16)) return false;
+    if (norm && g.io == FASTVIM_BF16) return false;
     return g.h * g.w * g.E * esz >= (8ll << 20) && fused_supported(g, norm, local, conv);
 }
 

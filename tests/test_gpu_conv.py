@@ -78,21 +78,18 @@ def test_conv_layer(shape, axis, io):
                torch.float32 if io == "f32" else torch.bfloat16, "conv %s %s axis %d" % (shape, io, axis))
 
 
-def test_conv_fused_flag_paths():
-    """FASTVIM_FLAG_FUSED: the single launch computes the conv on load for
-    COLS (equal to the stage kernels within rounding); ROWS layers without the
-    norm keep the stage kernels (bit for bit the staged call)."""
+@pytest.mark.parametrize("axis", (P.POOL_COLS, P.POOL_ROWS))
+def test_conv_fused_flag_paths(axis):
+    """FASTVIM_FLAG_FUSED: the single launch computes the conv on load (equal
+    to the stage kernels within rounding)."""
     B, h, w, E, R = 2, 6, 5, 32, 4
     rng = np.random.default_rng(61)
     x, z = (rng.standard_normal((B, h, w, E)).astype(np.float32) for _ in range(2))
     prm = {"fwd": rand_dir(rng, E, 16, R, 0.1), "bwd": rand_dir(rng, E, 16, R, 0.1)}
     conv = rand_conv(rng, E)
-    a = host(gpu_call(x, z, prm, P.POOL_COLS, conv=conv, flags=P.FLAG_FUSED).run())
-    b = host(gpu_call(x, z, prm, P.POOL_COLS, conv=conv, flags=P.FLAG_STAGED).run())
-    check(a, b, FP32_TOL, "COLS single launch vs stage kernels")
-    a = host(gpu_call(x, z, prm, P.POOL_ROWS, conv=conv, flags=P.FLAG_FUSED).run())
-    b = host(gpu_call(x, z, prm, P.POOL_ROWS, conv=conv, flags=P.FLAG_STAGED).run())
-    assert np.array_equal(a, b)
+    a = host(gpu_call(x, z, prm, axis, conv=conv, flags=P.FLAG_FUSED).run())
+    b = host(gpu_call(x, z, prm, axis, conv=conv, flags=P.FLAG_STAGED).run())
+    check(a, b, FP32_TOL, "axis %d single launch vs stage kernels" % axis)
 
 
 # COLS layers on the single launch with the conv on load: grids whose runs
@@ -104,13 +101,17 @@ FUSED_SHAPES = SHAPES + [(2, 200, 6, 64, 12), (1, 97, 11, 40, 33), (3, 9, 130, 1
 
 @pytest.mark.parametrize("norm", [False, True], ids=["plain", "norm"])
 @pytest.mark.parametrize("shape", FUSED_SHAPES, ids=["x".join(map(str, s)) for s in FUSED_SHAPES])
+@pytest.mark.parametrize("axis", (P.POOL_COLS, P.POOL_ROWS))
 @pytest.mark.parametrize("io", ["f32", "bf16"])
-def test_conv_single_launch(shape, io, norm):
+def test_conv_single_launch(shape, axis, io, norm):
     """out, its D = 0 twin, the pooled tokens and both scan outputs of the
     single launch with the Conv1D computed on load (and the post-SSM
-    LayerNorm), against the oracle."""
+    LayerNorm), against the oracle: COLS walks the conv's runs along the grid
+    rows, ROWS down the columns."""
     B, h, w, E, R = shape
-    rng = np.random.default_rng(zlib.crc32(repr(("conv-fused", shape, io, norm)).encode()))
+    if axis == P.POOL_ROWS:
+        h, w = w, h  # the same scan lengths on the other axis
+    rng = np.random.default_rng(zlib.crc32(repr(("conv-fused", shape, axis, io, norm)).encode()))
     x = rng.standard_normal((B, h, w, E)).astype(np.float32)
     z = rng.standard_normal((B, h, w, E)).astype(np.float32)
     if io == "bf16":
@@ -118,9 +119,10 @@ def test_conv_single_launch(shape, io, norm):
     prm = {"fwd": rand_dir(rng, E, 16, R, 0.1), "bwd": rand_dir(rng, E, 16, R, 0.1)}
     conv = rand_conv(rng, E)
     ln = rand_ln(rng, E) if norm else None
-    block_check(x, z, prm, conv, P.POOL_COLS, FP32_TOL if io == "f32" else BF16_TOL,
+    block_check(x, z, prm, conv, axis, FP32_TOL if io == "f32" else BF16_TOL,
                 torch.float32 if io == "f32" else torch.bfloat16,
-                "single launch conv%s %s %s" % (" + norm" if norm else "", shape, io), ln=ln, flags=P.FLAG_FUSED)
+                "single launch conv%s %s %s axis %d" % (" + norm" if norm else "", shape, io, axis), ln=ln,
+                flags=P.FLAG_FUSED)
 
 
 def test_conv_single_launch_options():
