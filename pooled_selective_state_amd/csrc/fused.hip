@@ -656,9 +656,9 @@ __device__ void item_epilogue_rows(const FusedArgs& a, int64_t b, int k, float* 
 // COLS norm E items: grid rows [k*RE, k*RE + RE) of image b.  The
 // per-channel vectors (D_fwd + D_bwd, the norm's weight and bias) are staged
 // in LDS once per item and the summed scan row once per grid row; each team
-// of kNormTL lanes (a wave) then takes two tokens at a time and runs the
-// per-token norm epilogue, the next two tokens' x and z loads issued before
-// the current two are computed.
+// of kNormTL lanes (a wave) then takes one token at a time and runs the
+// per-token norm epilogue, the next token's x and z loads issued before the
+// current one is computed.
 template <class IO, bool CONV>
 __device__ void item_epilogue_norm(const FusedArgs& a, int64_t b, int k, float* lds) {
     using raw = typename IO::raw;
@@ -757,33 +757,21 @@ __device__ void item_epilogue_norm(const FusedArgs& a, int64_t b, int k, float* 
             }
             continue;
         }
-        // the next pair's x and z are loaded before the current pair is computed
-        raw nx1[kNormNV], nz1[kNormNV], nx2[kNormNV], nz2[kNormNV];
-        auto load_pair = [&](int j) {
-            const int j2 = j + kTeams;
-            const int64_t c1 = img + i * w + j, c2 = img + i * w + (j2 < w ? j2 : j);
-            norm_load<IO, kNormTL, kNormNV>(x + c1 * E, z + c1 * E, E, lane, nx1, nz1);
-            if (j2 < w) norm_load<IO, kNormTL, kNormNV>(x + c2 * E, z + c2 * E, E, lane, nx2, nz2);
-        };
-        if (team < w) load_pair(team);
-        for (int j = team; j < w; j += 2 * kTeams) {
-            const int j2 = j + kTeams;
-            const bool two = j2 < w;
-            const int64_t c1 = img + i * w + j, c2 = img + i * w + (two ? j2 : j);
-            raw x1[kNormNV], z1[kNormNV], x2[kNormNV], z2[kNormNV];
+        // one token per team at a time, the next one's x and z in flight
+        raw nx[kNormNV], nz[kNormNV];
+        if (team < w) norm_load<IO, kNormTL, kNormNV>(x + (img + i * w + team) * E, z + (img + i * w + team) * E, E,
+                                                      lane, nx, nz);
+        for (int j = team; j < w; j += kTeams) {
+            raw cx[kNormNV], cz[kNormNV];
 #pragma unroll
             for (int v = 0; v < kNormNV; ++v) {
-                x1[v] = nx1[v];
-                z1[v] = nz1[v];
-                x2[v] = nx2[v];
-                z2[v] = nz2[v];
+                cx[v] = nx[v];
+                cz[v] = nz[v];
             }
-            if (j + 2 * kTeams < w) load_pair(j + 2 * kTeams);
-            norm_finish<IO, kNormTL, kNormNV, true>(x1, z1, srow, nullptr, ds, nullptr, gw, gb, a.ln_eps,
-                                                    out + c1 * E, E, lane);
-            if (two)
-                norm_finish<IO, kNormTL, kNormNV, true>(x2, z2, srow, nullptr, ds, nullptr, gw, gb, a.ln_eps,
-                                                        out + c2 * E, E, lane);
+            const int64_t cn = img + i * w + j + kTeams;
+            if (j + kTeams < w) norm_load<IO, kNormTL, kNormNV>(x + cn * E, z + cn * E, E, lane, nx, nz);
+            norm_finish<IO, kNormTL, kNormNV, true>(cx, cz, srow, nullptr, ds, nullptr, gw, gb, a.ln_eps,
+                                                    out + (img + i * w + j) * E, E, lane);
         }
     }
 }
