@@ -102,12 +102,12 @@ struct IoBf16 {
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 
-// fp32 -> bf16 bits, round to nearest even; NaN stays NaN (quiet).
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) | 0x40u) & 0xffffu;
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return u >> 16;
+// Two fp32 values to packed bf16 (the first in the low half) with gfx950's
+// v_cvt_pk_bf16_f32: round to nearest even, NaN stays NaN.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
 }
 
 // 16-byte vector load / store of V I/O elements widened to fp32.
@@ -135,10 +135,10 @@ __device__ __forceinline__ void store_vec(float* p, const float (&v)[4]) {
 template <bool NT>
 __device__ __forceinline__ void store_vec(uint16_t* p, const float (&v)[8]) {
     u32x4 t;
-    t.x = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
-    t.y = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
-    t.z = f32_to_bf16_bits(v[4]) | (f32_to_bf16_bits(v[5]) << 16);
-    t.w = f32_to_bf16_bits(v[6]) | (f32_to_bf16_bits(v[7]) << 16);
+    t.x = f32x2_to_bf16x2(v[0], v[1]);
+    t.y = f32x2_to_bf16x2(v[2], v[3]);
+    t.z = f32x2_to_bf16x2(v[4], v[5]);
+    t.w = f32x2_to_bf16x2(v[6], v[7]);
     if (NT) __builtin_nontemporal_store(t, reinterpret_cast<u32x4*>(p));
     else *reinterpret_cast<u32x4*>(p) = t;
 }
