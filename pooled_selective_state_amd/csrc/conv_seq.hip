@@ -30,7 +30,7 @@ namespace fastvim {
 namespace {
 
 constexpr int kSeqThreads = 256;
-constexpr int kAdjRuns = 16;  // runs per adjoint workgroup (4 waves, each every fourth run)
+constexpr int kAdjRunsPerSlot = 4;  // runs per adjoint workgroup slot
 
 __device__ __forceinline__ int seq_token(int r, int h, int w, bool colmajor) {
     return colmajor ? (r % h) * w + r / h : r;
@@ -126,24 +126,27 @@ conv_adjoint_halo_kernel(const typename IO::elem* x, const typename IO::elem* dx
     }
 }
 
-// The adjoint, in place.  Workgroup (group g, channel block cb): lane l takes
-// vector cb 64 + l, wave v the runs g kAdjRuns + v + 4 i.  A lane walks its
-// run with a front f: at f it loads x and dxc and forms da[f] (past the run,
-// da comes from the halo buffer, past the sequence it is 0), adds the conv's
-// weight and bias gradient terms, and writes dx[f - 3] from da[f - 3 .. f].
-// dxc is read only at positions whose dx is written later by the same lane.
-// At the end the four waves' sums are added in LDS in a fixed order and the
-// workgroup writes its slice of partial row g: [d conv_b (E) | d conv_w (E, 4)].
+// The adjoint, in place.  Workgroup (group g, channel block cb) of k slots of
+// VB lanes (VB = min(VE, 256) vectors of a token, k = 256 / VB): lane l of
+// slot q takes vector cb VB + l and the runs g k R + q + k i (R =
+// kAdjRunsPerSlot), so every lane has work whatever E is.  A lane walks its run with a front f: at f it
+// loads x and dxc and forms da[f] (past the run, da comes from the halo
+// buffer, past the sequence it is 0), adds the conv's weight and bias
+// gradient terms, and writes dx[f - 3] from da[f - 3 .. f].  dxc is read only
+// at positions whose dx is written later by the same lane.  At the end the k
+// slots' sums are added in LDS in a fixed order and the workgroup writes its
+// slice of partial row g: [d conv_b (E) | d conv_w (E, 4)].
 template <class IO>
 __global__ void __launch_bounds__(kSeqThreads)
 conv_adjoint_kernel(const typename IO::elem* x, typename IO::elem* dx, const float* __restrict__ cw,
                     const float* __restrict__ cb, const float* __restrict__ halo, float* __restrict__ parts, int n,
-                    int h, int w, int colmajor, int E, int VE, int L, int nruns, int64_t total_runs) {
+                    int h, int w, int colmajor, int E, int VE, int VB, int L, int nruns, int64_t total_runs) {
     constexpr int V = IO::V;
     using raw = typename IO::raw;
-    __shared__ float red[3][64][5 * V];
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    const int c = (int)blockIdx.y * 64 + lane;
+    extern __shared__ float red[];  // [k][VB][5 V]
+    const int k = (int)blockDim.x / VB;
+    const int slot = (int)threadIdx.x / VB, lane = (int)threadIdx.x - slot * VB;
+    const int c = (int)blockIdx.y * VB + lane;
     const bool valid = c < VE;
     const int coff = (valid ? c : VE - 1) * V;
     const bool cm = colmajor != 0;
@@ -156,9 +159,10 @@ conv_adjoint_kernel(const typename IO::elem* x, typename IO::elem* dx, const flo
 #pragma unroll
         for (int k = 0; k < 4; ++k) sdw[k][v] = 0.f;
     }
-    const int64_t run_end = ((int64_t)blockIdx.x + 1) * kAdjRuns < total_runs ? ((int64_t)blockIdx.x + 1) * kAdjRuns
-                                                                                : total_runs;
-    for (int64_t run = (int64_t)blockIdx.x * kAdjRuns + wv; run < run_end; run += 4) {
+    const int64_t rpg = (int64_t)k * kAdjRunsPerSlot;  // runs per workgroup
+    const int64_t run_end = ((int64_t)blockIdx.x + 1) * rpg < total_runs ? ((int64_t)blockIdx.x + 1) * rpg
+                                                                         : total_runs;
+    for (int64_t run = (int64_t)blockIdx.x * rpg + slot; run < run_end; run += k) {
         const int64_t b = run / nruns;
         const int j = (int)(run - b * nruns);
         const int r0 = j * L, r1 = r0 + L < n ? r0 + L : n;
@@ -228,27 +232,28 @@ conv_adjoint_kernel(const typename IO::elem* x, typename IO::elem* dx, const flo
             }
         }
     }
-    if (wv > 0) {
+    if (slot > 0) {
+        float* mine = red + ((slot - 1) * VB + lane) * 5 * V;
 #pragma unroll
         for (int v = 0; v < V; ++v) {
-            red[wv - 1][lane][v] = sdb[v];
+            mine[v] = sdb[v];
 #pragma unroll
-            for (int k = 0; k < 4; ++k) red[wv - 1][lane][V + 4 * v + k] = sdw[k][v];
+            for (int t = 0; t < 4; ++t) mine[V + 4 * v + t] = sdw[t][v];
         }
     }
     __syncthreads();
-    if (wv == 0 && valid) {
+    if (slot == 0 && valid) {
         float* row = parts + (int64_t)blockIdx.x * 5 * E;
 #pragma unroll
         for (int v = 0; v < V; ++v) {
             float s = sdb[v];
-            for (int u = 0; u < 3; ++u) s += red[u][lane][v];
+            for (int u = 1; u < k; ++u) s += red[((u - 1) * VB + lane) * 5 * V + v];
             row[coff + v] = s;
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                float t = sdw[k][v];
-                for (int u = 0; u < 3; ++u) t += red[u][lane][V + 4 * v + k];
-                row[E + (coff + v) * 4 + k] = t;
+            for (int t = 0; t < 4; ++t) {
+                float q = sdw[t][v];
+                for (int u = 1; u < k; ++u) q += red[((u - 1) * VB + lane) * 5 * V + V + 4 * v + t];
+                row[E + (coff + v) * 4 + t] = q;
             }
         }
     }
@@ -279,15 +284,23 @@ hipError_t conv_seq_t(const Geom& g, const void* x, const fastvim_params& p, voi
     return hipGetLastError();
 }
 
+// Vectors per slot of an adjoint workgroup, and its slots.
+int adjoint_vb(const Geom& g) {
+    const int VE = (int)(g.E / (g.io == FASTVIM_BF16 ? IoBf16::V : IoF32::V));
+    return VE < kSeqThreads ? VE : kSeqThreads;
+}
+int adjoint_slots(const Geom& g) { return kSeqThreads / adjoint_vb(g); }
+
 // Run length of the adjoint whose halo, partial rows and column-sum scratch
 // fit in `floats`: the shortest of 64, 128, ... (a whole sequence as one run
 // needs no halo).  *groups: partial rows.
 int adjoint_run(const Geom& g, int64_t floats, int64_t* groups) {
     const SeqGeom s = seq_geom(g);
+    const int64_t rpg = (int64_t)adjoint_slots(g) * kAdjRunsPerSlot;
     for (int L = 64;; L *= 2) {
         if (L > s.n) L = s.n;
         const int64_t nruns = (s.n + L - 1) / L;
-        const int64_t gr = (g.B * nruns + kAdjRuns - 1) / kAdjRuns;
+        const int64_t gr = (g.B * nruns + rpg - 1) / rpg;
         const int64_t need = (nruns > 1 ? g.B * nruns * 3 * g.E : 0) + gr * 5 * g.E +
                              ((gr + kColRowsPerBlock - 1) / kColRowsPerBlock) * 4 * g.E + 64;
         if (need <= floats || L >= s.n) {
@@ -319,9 +332,11 @@ hipError_t conv_adjoint_t(const Geom& g, const void* x, void* dx, const fastvim_
                            dim3(kSeqThreads), 0, st, xe, static_cast<const elem*>(dx), p.conv_w, p.conv_b, halo, s.n,
                            (int)g.h, (int)g.w, s.colmajor, (int)g.E, VE, L, nruns, items);
     }
-    hipLaunchKernelGGL((conv_adjoint_kernel<IO>), dim3((unsigned)groups, (unsigned)((VE + 63) / 64)),
-                       dim3(kSeqThreads), 0, st, xe, de, p.conv_w, p.conv_b, halo, parts, s.n, (int)g.h, (int)g.w,
-                       s.colmajor, (int)g.E, VE, L, nruns, total_runs);
+    const int VB = adjoint_vb(g), slots = adjoint_slots(g);
+    const size_t lds = (size_t)((slots - 1) * VB * 5 * IO::V) * sizeof(float);
+    hipLaunchKernelGGL((conv_adjoint_kernel<IO>), dim3((unsigned)groups, (unsigned)((VE + VB - 1) / VB)),
+                       dim3((unsigned)(slots * VB)), lds, st, xe, de, p.conv_w, p.conv_b, halo, parts, s.n, (int)g.h,
+                       (int)g.w, s.colmajor, (int)g.E, VE, VB, L, nruns, total_runs);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if ((e = launch_colsum(parts, groups, g.E, 5 * g.E, dcb, nullptr, tmp, st)) != hipSuccess) return e;

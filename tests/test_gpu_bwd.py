@@ -615,6 +615,29 @@ def test_bwd_conv_norm_block_full_size_2048(axis):
     _sampled_full_size(C.HIRES_2048, axis, saved=0 if axis == P.POOL_COLS else None, norm=True, with_conv=True)
 
 
+@pytest.mark.parametrize("variant", ["saved", "block", "conv"])
+def test_bwd_full_size_gradients_everywhere(variant):
+    """2048^2 with an upstream gradient on every image (the image groups,
+    every run of the conv's adjoint and every pass-2 workgroup carry data):
+    dx and dz of sampled images against the oracle on those images alone
+    (an image's dx and dz depend only on its own inputs)."""
+    cfg = C.HIRES_2048
+    wl = draw_workload(cfg)
+    x, z, prm = wl["x"], wl["z"][0], wl["params"][0]
+    rng = np.random.default_rng(83)
+    dout = rng.standard_normal(x.shape).astype(np.float32)
+    ln = rand_ln(np.random.default_rng(84), cfg.E) if variant == "block" else None
+    conv = rand_conv(np.random.default_rng(85), cfg.E) if variant in ("block", "conv") else None
+    axis = P.POOL_ROWS if variant == "block" else P.POOL_COLS
+    print("\n[%s bwd, gradients on every image] %s" % (cfg.name, variant), flush=True)
+    got = gpu_bwd(x, z, dout, prm, axis, saved=0, ln=ln, conv=conv)
+    for i in (0, cfg.B // 2, cfg.B - 1):
+        s = np.array([i])
+        ref = oracle.layer_bwd(x[s], z[s], dout[s], prm["fwd"], prm["bwd"], axis, ln=ln, conv=conv)
+        check(got["dx"][s], ref["dx"], FP32_TOL, "image %d dx" % i)
+        check(got["dz"][s], ref["dz"], FP32_TOL, "image %d dz" % i)
+
+
 def test_bwd_conv_masked_full_size():
     _sampled_full_size(C.MASKED_B, saved=0, with_conv=True)
 
