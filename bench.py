@@ -360,24 +360,23 @@ def main():
         ccall.run(stream)
         cv_ms, _ = time_steps(lambda: ccall.run(stream), n, stream)
         del ccall
-        scall = P.SSMCall(x, z, prm, P.POOL_COLS, workspace=call.workspace, out=call.out, conv=conv,
-                          flags=P.FLAG_STAGED)
-        scall.run(stream)
-        cv_st, _ = time_steps(lambda: scall.run(stream), n, stream)
-        cv_pool, _ = time_steps(lambda: scall.stage(P.STAGE_POOL, stream), n, stream)
-        cv_epi, _ = time_steps(lambda: scall.stage(P.STAGE_EPILOGUE, stream), n, stream)
+        cscall = P.SSMCall(x, z, prm, P.POOL_COLS, workspace=call.workspace, out=call.out, conv=conv,
+                           flags=P.FLAG_STAGED)
+        cscall.run(stream)
+        cv_st, _ = time_steps(lambda: cscall.run(stream), n, stream)
+        cv_pool, _ = time_steps(lambda: cscall.stage(P.STAGE_POOL, stream), n, stream)
+        cv_epi, _ = time_steps(lambda: cscall.stage(P.STAGE_EPILOGUE, stream), n, stream)
         extras["conv_producer_2048"] = {"layer_ms": cv_ms, "path": "single launch, x_conv computed on load",
                                         "layer_GBps": alg_bytes / (cv_ms * 1e-3) / 1e9,
                                         "hbm_frac": alg_bytes / (cv_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                                         "stage_kernels_ms": cv_st, "pool_ms": cv_pool, "epilogue_ms": cv_epi,
                                         "pool_GBps": 4 * elems / (cv_pool * 1e-3) / 1e9,
                                         "epilogue_GBps": alg_bytes / (cv_epi * 1e-3) / 1e9}
-        del scall
+        del cscall
         log("conv-fused layer %.3f ms (single launch), %.3f ms (stage kernels)" % (cv_ms, cv_st))
         # the whole FastVim block in one call: the producer Conv1D (written out
         # into out first) and the post-SSM LayerNorm between the skip and the gate
-        blk = {"path": "COLS: the single launch, x_conv computed on load; ROWS: x_conv written out, then the "
-                       "LayerNorm layer on the stage kernels"}
+        blk = {"path": "the single launch, x_conv computed on load (both axes)"}
         for name, axis in (("cols", P.POOL_COLS), ("rows", P.POOL_ROWS)):
             bk = P.SSMCall(x, z, prm, axis, workspace=call.workspace, out=call.out, conv=conv, ln=ln)
             bk.run(stream)
