@@ -403,8 +403,11 @@ int bwd_front(const Geom& g, const void* x, const void* z, const void* dout, con
         // forward stages first, then the first pass with the norm, whose
         // per-(b, t) partials of dD, d ln_w and d ln_b (in du, du_f, du_b) are
         // summed before the scan adjoint overwrites those buffers
-        if ((!ws.u_saved && !ok(launch_pool(g, x, ws.fwd, s))) || !ok(launch_proj(g, x, p, ws.fwd, s)) ||
-            !ok(launch_scan(g, x, p, ws.fwd, s)) || !ok(launch_bwd_norm_pass1(g, x, z, dout, p, ws, dx, dz, s)))
+        // (with the conv, x is its input: the pool and the first pass compute
+        // x_conv where they read x)
+        if ((!ws.u_saved && !ok(conv ? launch_conv_pool(g, x, p, ws.fwd, s) : launch_pool(g, x, ws.fwd, s))) ||
+            !ok(launch_proj(g, x, p, ws.fwd, s)) || !ok(launch_scan(g, x, p, ws.fwd, s)) ||
+            !ok(launch_bwd_norm_pass1(g, x, z, dout, p, ws, dx, dz, s)))
             return FASTVIM_ERR_HIP;
         const int64_t M = g.B * g.T;
         if (!ok(launch_colsum(ws.du, M, g.E, g.E, gr.fwd.D, gr.bwd.D, ws.tmp, s)) ||
@@ -483,6 +486,15 @@ int bwd_back(const Geom& g, const void* x, const void* z, const void* dout, cons
         return e == hipSuccess;
     };
     const int64_t E = g.E;
+    if ((p.flags & FASTVIM_FLAG_POST_NORM) && (p.flags & FASTVIM_FLAG_CONV)) {
+        // (x is the conv's input) dx holds the norm's g; the conv's adjoint
+        // forms dL/dx_conv = g (D_fwd + D_bwd) + du / P where it reads it, its
+        // scratch the regions before du
+        const DxcFromG fg{ws.du, p.fwd.D, p.bwd.D, g.T, pool_norm(g)};
+        return ok(launch_conv_adjoint(g, x, dx, p, ws.front, ws.du - ws.front, gr.conv_w, gr.conv_b, s, &fg))
+                   ? FASTVIM_OK
+                   : FASTVIM_ERR_HIP;
+    }
     if (p.flags & FASTVIM_FLAG_POST_NORM)
         return ok(launch_bwd_norm_pass2(g, p, ws, dx, dz, s)) ? FASTVIM_OK : FASTVIM_ERR_HIP;
     if (p.flags & FASTVIM_FLAG_CONV) {
@@ -574,7 +586,7 @@ int bwd_groups(const Geom& g, uint32_t flags) {
     if (!set) {
         const int64_t cells = (g.masked ? g.K : g.h * g.w) * g.E;
         if (cells >= (int64_t(1) << 20) && g.B >= 16)
-            k = (flags & FASTVIM_FLAG_CONV) ? 1 : (flags & FASTVIM_FLAG_POST_NORM) ? 2 : 4;
+            k = (flags & FASTVIM_FLAG_POST_NORM) ? 2 : (flags & FASTVIM_FLAG_CONV) ? 1 : 4;
     }
     if (k > g.B) k = (int)g.B;
     return k < 1 ? 1 : k;
@@ -725,10 +737,37 @@ int run_bwd_grouped(const Geom& g, int k, const void* x, const void* z, const vo
     return FASTVIM_OK;
 }
 
+// Whether the conv's adjoint fits in the regions before du of every image
+// group's workspace (bwd_back's scratch when it replaces the norm's second
+// pass).
+bool conv_adjoint_fits_front(const Geom& g, uint32_t flags) {
+    int64_t per;
+    int n;
+    bwd_group_shape(g, bwd_groups(g, flags), &per, &n);
+    for (const int64_t b : {per, g.B - (n - 1) * per}) {
+        Geom gp = g;
+        gp.B = b;
+        // offsets only: the layout of a workspace placed at a dummy aligned address
+        BwdWorkspace w;
+        bwd_workspace_layout(gp, reinterpret_cast<void*>(uintptr_t(1) << 20), &w);
+        if (!conv_adjoint_fits(gp, w.du - w.front)) return false;
+    }
+    return true;
+}
+
+// Whether a backward call writes x_conv out first (conv_written).  A dense
+// pooled layer with the LayerNorm computes x_conv where its first pass reads
+// x, and its conv's adjoint replaces the norm's second pass (bwd_back) when
+// the adjoint fits beside du; tiny layers write it out.
+bool conv_written_bwd(const Geom& g, uint32_t flags) {
+    if (!conv_written(g, flags)) return false;
+    return g.masked || !g.pooled || !conv_adjoint_fits_front(g, flags);
+}
+
 // A backward call on its workspace at base (bwd_total_bytes(g) bytes).
 int run_bwd(const Geom& g, const void* x, const void* z, const void* dout, const fastvim_params& p,
             const int32_t* idx, void* dx, void* dz, const fastvim_grads& gr, void* base, hipStream_t s) {
-    if (conv_written(g, p.flags)) {
+    if (conv_written_bwd(g, p.flags)) {
         // x_conv into dz (the passes below read each cell's x before they
         // write its dz), the layer's backward pass on it, which leaves
         // dL/dx_conv in dx, then the conv's adjoint in place on dx, its scratch
@@ -940,6 +979,7 @@ size_t bwd_workspace_layout(const Geom& g, void* base, BwdWorkspace* ws) {
         char* c = static_cast<char*>(base);
         auto f = [&](size_t o) { return reinterpret_cast<float*>(c + o); };
         ws->fwd.u = f(o_u);
+        ws->front = f(o_u);
         ws->fwd.xdbl = f(o_x);
         ws->fwd.s_f = f(o_sf);
         ws->fwd.s_b = f(o_sb);

@@ -36,6 +36,9 @@ struct BwdWorkspace {
     int64_t G, S, MC, tmp_floats;
     int nchk;      // checkpoint chunks per lane: max(ceil(T / 16), kBwdCkptMin)
     bool u_saved = false;  // fwd.u is the caller's saved pooled tokens (pass 1 does not pool x)
+    // front: the regions before du (u, xdbl, s_f, s_b, gs, dDp, du_f, du_b),
+    // free once the scan adjoint and its sums have run
+    float* front = nullptr;
 };
 
 struct BwdScanArgs {
@@ -111,9 +114,19 @@ hipError_t launch_bwd_conv_epilogue(const Geom& g, const void* x, const void* z,
 // its adjoint in place -- dx holds dL/dx_conv on entry and dL/dx on exit --
 // with `floats` of scratch, the conv's weight and bias gradients into dcw,
 // dcb.  conv_adjoint_fits: the scratch is large enough.
+// fg (dense layers with the post-SSM LayerNorm): dx holds the norm's g, not
+// dL/dx_conv, and the adjoint forms dL/dx_conv = g (D_fwd + D_bwd) + du[b,
+// t] inv_p where it reads it (the norm's second pass folded in).
+struct DxcFromG {
+    const float* du;  // (B, T, E)
+    const float *Df, *Db;
+    int64_t T;
+    float inv_p;
+};
 hipError_t launch_conv_seq(const Geom& g, const void* x, const fastvim_params& p, void* xc, hipStream_t st);
 hipError_t launch_conv_adjoint(const Geom& g, const void* x, void* dx, const fastvim_params& p, float* scratch,
-                               int64_t floats, float* dcw, float* dcb, hipStream_t st);
+                               int64_t floats, float* dcw, float* dcb, hipStream_t st,
+                               const DxcFromG* fg = nullptr);
 bool conv_adjoint_fits(const Geom& g, int64_t floats);
 
 hipError_t launch_bwd_norm_pass1(const Geom& g, const void* x, const void* z, const void* dout,

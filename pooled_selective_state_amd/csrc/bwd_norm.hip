@@ -16,6 +16,7 @@
 // partial sums of dD, d ln_w and d ln_b; pass 2, after the scan adjoint has
 // produced du, turns g into dx in place.
 #include "bwd_internal.h"
+#include "conv_common.h"
 #include "epilogue_norm.h"
 #include "mask_list.h"
 
@@ -54,12 +55,14 @@ __device__ __forceinline__ void team_reduce_out(const float (&acc)[NV][V], float
 // the token, as in the forward norm).  MASKED: the cells are the image's kept
 // tokens whose row is t, listed per slice of kNormBwdThreads tokens
 // (mask_list.h); dense: cell p of the row or column, p < P.  LDS: the summed
-// scan row, D_fwd + D_bwd, ln_w, ln_b (E each) while the tokens are taken,
-// then kTeams rows of E for the team sums.
-// x and dz may be one buffer (a layer with the producer Conv1D passes its
-// conv output in dz): each cell's x is read before that cell's dz is written,
-// so those two pointers carry no restrict.
-template <class IO, int TL, int NV, bool MASKED>
+// scan row, D_fwd + D_bwd, ln_w, ln_b (E each) and, with CONV, the conv's
+// taps and bias (5 E) while the tokens are taken, then kTeams rows of E for
+// the team sums.  CONV (dense layers): x is the producer Conv1D's input and
+// the kernel computes x_conv where it reads x.
+// x and dz may be one buffer (a layer whose conv output is written out passes
+// it in dz): each cell's x is read before that cell's dz is written, so those
+// two pointers carry no restrict.
+template <class IO, int TL, int NV, bool MASKED, bool CONV>
 __global__ void __launch_bounds__(kNormBwdThreads)
 bwd_norm_pass1_kernel(const typename IO::elem* x, const typename IO::elem* __restrict__ z,
                       const typename IO::elem* __restrict__ dout, const float* __restrict__ sf,
@@ -68,7 +71,8 @@ bwd_norm_pass1_kernel(const typename IO::elem* x, const typename IO::elem* __res
                       const int32_t* __restrict__ rows, typename IO::elem* __restrict__ gout,
                       typename IO::elem* dz, float* __restrict__ gs, float* __restrict__ dDp,
                       float* __restrict__ dlnwp, float* __restrict__ dlnbp, int64_t T, int64_t h, int64_t w,
-                      int64_t K, int64_t P, int cols_axis, int E) {
+                      int64_t K, int64_t P, int cols_axis, int E, const float* __restrict__ cw,
+                      const float* __restrict__ cb) {
     constexpr int V = IO::V;
     constexpr int kTeams = kNormBwdThreads / TL;
     using raw = typename IO::raw;
@@ -77,6 +81,7 @@ bwd_norm_pass1_kernel(const typename IO::elem* x, const typename IO::elem* __res
     float* dsum = sm + E;
     float* slw = sm + 2 * E;
     float* slb = sm + 3 * E;
+    float* cwt = sm + 4 * E;  // CONV: [E][4] taps, then [E] bias
     float* red = sm;  // [kTeams][E], after the last token
     __shared__ int list[MASKED ? kNormBwdThreads : 1];
     __shared__ int wave_cnt[kMaxListWaves];
@@ -89,6 +94,8 @@ bwd_norm_pass1_kernel(const typename IO::elem* x, const typename IO::elem* __res
         slw[q] = lnw[q];
         slb[q] = lnb[q];
     }
+    if (CONV)
+        for (int q = tid; q < 5 * E; q += kNormBwdThreads) cwt[q] = q < 4 * E ? cw[q] : cb[q - 4 * E];
     __syncthreads();
     const float inv_e = 1.f / (float)E;
     float ag[NV][V], ad[NV][V], aw[NV][V], ab[NV][V];
@@ -179,10 +186,147 @@ bwd_norm_pass1_kernel(const typename IO::elem* x, const typename IO::elem* __res
         }
     };
 
+    // CONV: the same for a token whose x_conv the caller computed, given as
+    // xat(v, k) (channel (v TL + lane) V + k).  A copy of the arithmetic
+    // above: one shared body raised the plain kernels' register count past
+    // the three-waves-per-SIMD limit.
+    auto token_core = [&](auto xat, const raw (&zr)[NV], const raw (&dr)[NV], int64_t tok) {
+        float n[NV][V], dn[NV][V];
+        float sum = 0.f;
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+            const int c = (v * TL + lane) * V;
+#pragma unroll
+            for (int k = 0; k < V; ++k) {
+                n[v][k] = c < E ? fmaf(dsum[c + k], xat(v, k), srow[c + k]) : 0.f;
+                sum += n[v][k];
+            }
+        }
+        const float mean = team_sum<TL>(sum) * inv_e;
+        float sq = 0.f;
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+            if ((v * TL + lane) * V < E) {
+#pragma unroll
+                for (int k = 0; k < V; ++k) {
+                    const float d = n[v][k] - mean;
+                    sq = fmaf(d, d, sq);
+                }
+            }
+        }
+        const float r = __builtin_amdgcn_rsqf(team_sum<TL>(sq) * inv_e + eps);
+        float m1 = 0.f, m2 = 0.f;
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+            const int c = (v * TL + lane) * V;
+            if (c < E) {
+                float oz[V];
+#pragma unroll
+                for (int k = 0; k < V; ++k) {
+                    const float nv = (n[v][k] - mean) * r;
+                    const float zv = raw_at(zr[v], k), dv = raw_at(dr[v], k);
+                    const float sg = nb_sigmoid(zv);
+                    const float go = dv * zv * sg;
+                    const float lw = slw[c + k];
+                    oz[k] = dv * fmaf(nv, lw, slb[c + k]) * sg * fmaf(zv, 1.f - sg, 1.f);
+                    aw[v][k] = fmaf(go, nv, aw[v][k]);
+                    ab[v][k] += go;
+                    dn[v][k] = go * lw;
+                    m1 += dn[v][k];
+                    m2 = fmaf(dn[v][k], nv, m2);
+                    n[v][k] = nv;
+                }
+                store_vec<true>(dz + tok * E + c, oz);
+            }
+        }
+        m1 = team_sum<TL>(m1) * inv_e;
+        m2 = team_sum<TL>(m2) * inv_e;
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+            const int c = (v * TL + lane) * V;
+            if (c < E) {
+                float og[V];
+#pragma unroll
+                for (int k = 0; k < V; ++k) {
+                    const float g = r * (dn[v][k] - m1 - n[v][k] * m2);
+                    og[k] = g;
+                    ag[v][k] += g;
+                    ad[v][k] = fmaf(g, xat(v, k), ad[v][k]);
+                }
+                store_vec<true>(gout + tok * E + c, og);
+            }
+        }
+    };
+    auto load_zd = [&](int64_t tok, raw (&zr)[NV], raw (&dr)[NV]) {
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+            const int c = (v * TL + lane) * V;
+            if (c < E) {
+                zr[v] = load_raw<true>(z + tok * E + c);
+                dr[v] = load_raw<true>(dout + tok * E + c);
+            }
+        }
+    };
     if (MASKED) {
         for (int64_t k0 = 0; k0 < K; k0 += kNormBwdThreads) {
             const int n = row_token_list(rows + b * K, K, t, k0, list, wave_cnt);
             for (int i = team; i < n; i += kTeams) token(b * K + k0 + list[i]);
+        }
+    } else if (CONV) {
+        // the producer Conv1D on load: team `team` takes the run of cells
+        // [team Lr, team Lr + Lr) of the line in sequence order (the grid row
+        // t of a row-major sequence, the column t of a column-major one), each
+        // lane sliding the conv's window of three raw vectors over its vectors
+        // (a halo of three at the run's start, from the caches: x is read with
+        // allocating loads)
+        const int64_t base = b * h * w + (cols_axis ? t * w : t);
+        const int64_t step = cols_axis ? 1 : w;
+        const int Lr = (int)((P + kTeams - 1) / kTeams);
+        const int pa = team * Lr, pb = pa + Lr < (int)P ? pa + Lr : (int)P;
+        if (pa < pb) {
+            const typename IO::elem* ximg = x + b * h * w * E;
+            raw w3[NV], w2[NV], w1[NV];
+#pragma unroll
+            for (int v = 0; v < NV; ++v) {
+                const int c = (v * TL + lane) * V;
+                if (c < E) {
+                    if (cols_axis) load_halo<IO, true>(ximg, c, E, (int)t, pa, (int)h, (int)w, w3[v], w2[v], w1[v]);
+                    else load_halo<IO, false>(ximg, c, E, pa, (int)t, (int)h, (int)w, w3[v], w2[v], w1[v]);
+                }
+            }
+            for (int p = pa; p < pb; ++p) {
+                const int64_t tok = base + p * step;
+                raw xr[NV], zr[NV], dr[NV];
+#pragma unroll
+                for (int v = 0; v < NV; ++v) {
+                    const int c = (v * TL + lane) * V;
+                    if (c < E) xr[v] = load_raw<false>(x + tok * E + c);
+                }
+                load_zd(tok, zr, dr);
+                float xc[NV][V];
+#pragma unroll
+                for (int v = 0; v < NV; ++v) {
+                    const int c = (v * TL + lane) * V;
+                    if (c < E) {
+#pragma unroll
+                        for (int q = 0; q < V; ++q) {
+                            const f32x4 t4 = *reinterpret_cast<const f32x4*>(cwt + (c + q) * kTaps);
+                            float av = fmaf(t4.w, raw_at(xr[v], q), cwt[4 * E + c + q]);
+                            av = fmaf(t4.z, raw_at(w1[v], q), av);
+                            av = fmaf(t4.y, raw_at(w2[v], q), av);
+                            av = fmaf(t4.x, raw_at(w3[v], q), av);
+                            xc[v][q] = conv_silu_f(av);
+                        }
+                        w3[v] = w2[v];
+                        w2[v] = w1[v];
+                        w1[v] = xr[v];
+                    } else {
+#pragma unroll
+                        for (int q = 0; q < V; ++q) xc[v][q] = 0.f;
+                    }
+                }
+                token_core([&](int v, int k) { return xc[v][k]; }, zr, dr, tok);
+            }
         }
     } else {
         const int64_t base = b * h * w + (cols_axis ? t * w : t);
@@ -262,20 +406,23 @@ hipError_t pass1_launch(const Geom& g, const void* x, const void* z, const void*
                         const BwdWorkspace& ws, void* dx, void* dz, hipStream_t st) {
     using elem = typename IO::elem;
     constexpr int kTeams = kNormBwdThreads / TL;
-    const size_t lds = (size_t)((kTeams > 4 ? kTeams : 4) * g.E) * sizeof(float);
+    const bool conv = (p.flags & FASTVIM_FLAG_CONV) != 0;  // dense layers: x is the conv's input
+    const int rows_lds = conv ? (kTeams > 9 ? kTeams : 9) : (kTeams > 4 ? kTeams : 4);
+    const size_t lds = (size_t)(rows_lds * g.E) * sizeof(float);
     const dim3 grid((unsigned)(g.B * g.T)), block(kNormBwdThreads);
     const elem *xe = static_cast<const elem*>(x), *ze = static_cast<const elem*>(z),
                *de = static_cast<const elem*>(dout);
     elem *ge = static_cast<elem*>(dx), *dze = static_cast<elem*>(dz);
     const int cols = g.axis == FASTVIM_POOL_COLS;
-    if (g.masked)
-        hipLaunchKernelGGL((bwd_norm_pass1_kernel<IO, TL, NV, true>), grid, block, lds, st, xe, ze, de, ws.fwd.s_f,
-                           ws.fwd.s_b, p.fwd.D, p.bwd.D, p.ln_weight, p.ln_bias, p.ln_eps, ws.fwd.rows, ge, dze,
-                           ws.gs, ws.du, ws.du_f, ws.du_b, g.T, g.h, g.w, g.K, g.P, cols, (int)g.E);
-    else
-        hipLaunchKernelGGL((bwd_norm_pass1_kernel<IO, TL, NV, false>), grid, block, lds, st, xe, ze, de, ws.fwd.s_f,
-                           ws.fwd.s_b, p.fwd.D, p.bwd.D, p.ln_weight, p.ln_bias, p.ln_eps, ws.fwd.rows, ge, dze,
-                           ws.gs, ws.du, ws.du_f, ws.du_b, g.T, g.h, g.w, g.K, g.P, cols, (int)g.E);
+#define FASTVIM_P1(masked, cv)                                                                                     \
+    hipLaunchKernelGGL((bwd_norm_pass1_kernel<IO, TL, NV, masked, cv>), grid, block, lds, st, xe, ze, de,         \
+                       ws.fwd.s_f, ws.fwd.s_b, p.fwd.D, p.bwd.D, p.ln_weight, p.ln_bias, p.ln_eps, ws.fwd.rows, ge, \
+                       dze, ws.gs, ws.du, ws.du_f, ws.du_b, g.T, g.h, g.w, g.K, g.P, cols, (int)g.E, p.conv_w,      \
+                       p.conv_b)
+    if (g.masked) FASTVIM_P1(true, false);
+    else if (conv) FASTVIM_P1(false, true);
+    else FASTVIM_P1(false, false);
+#undef FASTVIM_P1
     return hipGetLastError();
 }
 
