@@ -95,9 +95,10 @@ fastvim_params effective_params(const fastvim_params& p) {
 // window where they read x get x_conv written out first (conv_seq.hip):
 // masked layers (the conv runs along the kept tokens), layers with the
 // post-SSM LayerNorm and unpooled layers.  Dense pooled layers without the
-// norm compute it in their pool and output stages (conv.hip), and the
-// forward pass's single launch computes it on load for dense COLS layers,
-// with or without the norm (fused.hip; run_fwd asks it first).
+// norm compute it in their pool and output stages (conv.hip); the forward
+// pass's single launch computes it on load for dense layers, with or without
+// the norm (fused.hip; run_fwd asks it first), and so does the backward pass
+// of dense layers with the norm (conv_written_bwd).
 bool conv_written(const Geom& g, uint32_t flags) {
     return (flags & FASTVIM_FLAG_CONV) && (g.masked || !g.pooled || (flags & FASTVIM_FLAG_POST_NORM));
 }
