@@ -514,8 +514,9 @@ class BwdCall:
     not twice).  pool_scale: as for the forward call.  groups: the call's
     image groups (0: the library's choice, 1: none; see fastvim_ssm_bwd in
     fastvim.h).  run() returns
-    {"dx": dx, "dz": dz, "fwd": {...}, "bwd": {...}} and, with ln,
-    "ln": {"weight": ..., "bias": ...}."""
+    {"dx": dx, "dz": dz, "fwd": {...}, "bwd": {...}}, with ln also
+    "ln": {"weight": ..., "bias": ...} and with conv "conv": {"weight": ...,
+    "bias": ...}."""
 
     def __init__(self, x: torch.Tensor, z: torch.Tensor, dout: torch.Tensor,
                  params: Dict[str, Dict[str, torch.Tensor]], pool_axis: int,

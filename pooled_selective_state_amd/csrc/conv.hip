@@ -242,11 +242,13 @@ namespace {
 // and the conv's adjoint, with a[q] the pre-activation and da = dxc silu'(a),
 //   dx[r]  = sum_k conv_w[k] da[r + 3 - k],  d conv_w[k] += da[r] x[r - 3 + k],
 //   d conv_b += da[r],  dD += g[r] x_conv[r].
-// A lane walks a run of the sequence positions of one scan position with a
-// front q = r + 3 three steps ahead of the position r it finishes: at the
-// front it loads x, z and dout and forms da[q]; at r it has x[r - 3 .. r + 3]
-// in a window and da[r .. r + 3] in a ring.  Positions before the sequence
-// have x = 0, positions after it da = 0.  Workgroups loop over the (image,
+// A lane walks a run of the sequence positions of one scan position, kBatchCb
+// positions' loads at a time.  At each position q it loads x, z and dout,
+// forms x_conv, dz and da[q] (x[q - 3 .. q] in a window) and adds its terms to
+// the sums, and it finishes dx[q - 3] from da[q - 3 .. q] (a ring of three).
+// Past the run it forms da for three more positions (the next run's first
+// cells) to finish its last dx.  Positions before the sequence have x = 0,
+// positions after it da = 0.  Workgroups loop over the (image,
 // scan position) items and keep per-lane sums; at the end each workgroup
 // writes one row of partials [dD | d conv_b | d conv_w] (6 E floats, its
 // channel slice), summed over the rows by a later kernel.
@@ -263,6 +265,7 @@ bwd_conv_epilogue_kernel(const typename IO::elem* __restrict__ x, const typename
                          float* __restrict__ parts, int B, int T, int P, int h, int w, int E, int VE, int VEs, int G,
                          float inv_p) {
     constexpr int V = IO::V;
+    constexpr int kBatchCb = V == 4 ? 4 : 1;  // positions whose loads are issued together (bf16: registers)
     using raw = typename IO::raw;
     extern __shared__ float red[];  // [G][6][VEs V]
     const int tid = threadIdx.x, c = tid % VEs, g = tid / VEs;
@@ -303,77 +306,103 @@ bwd_conv_epilogue_kernel(const typename IO::elem* __restrict__ x, const typename
                 sv[v + 2] = q1.z + q2.z;
                 sv[v + 3] = q1.w + q2.w;
             }
-            raw xw[7];  // x[q - 6 .. q]
-            raw zR[4], oR[4];  // z, dout of positions q - 3 .. q
-            float dR[4][V];    // da of positions q - 3 .. q
+            const float* ur = du + (b * T + t) * E + coff;
+            float uv[V];  // du / P at scan position t (the run's cells)
 #pragma unroll
-            for (int k = 0; k < 7; ++k) xw[k] = raw{};
+            for (int v = 0; v < V; ++v) uv[v] = ur[v] * inv_p;
+            auto pos = [&](int q) { return img + (int64_t)tok_of(q) * E + coff; };
+            raw x3{}, x2{}, x1{};  // x[q - 3 .. q - 1]
+            if (ra >= 3) x3 = load_raw<false>(x + pos(ra - 3));
+            if (ra >= 2) x2 = load_raw<false>(x + pos(ra - 2));
+            if (ra >= 1) x1 = load_raw<false>(x + pos(ra - 1));
+            float d3[V], d2[V], d1[V];  // da[q - 3 .. q - 1]
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                zR[k] = oR[k] = raw{};
+            for (int v = 0; v < V; ++v) d3[v] = d2[v] = d1[v] = 0.f;
+            // dx[q - 3] from da[q - 3 .. q] (q - 3 in the run), then the rings move on
+            auto finish = [&](const raw& xv, const float (&da)[V], int q) {
+                if (q - 3 >= ra) {
+                    float ox[V];
 #pragma unroll
-                for (int v = 0; v < V; ++v) dR[k][v] = 0.f;
-            }
-#pragma unroll 2
-            for (int q = ra - 3; q < rb + 3; ++q) {
-#pragma unroll
-                for (int k = 0; k < 6; ++k) xw[k] = xw[k + 1];
-#pragma unroll
-                for (int k = 0; k < 3; ++k) {
-                    zR[k] = zR[k + 1];
-                    oR[k] = oR[k + 1];
-#pragma unroll
-                    for (int v = 0; v < V; ++v) dR[k][v] = dR[k + 1][v];
+                    for (int v = 0; v < V; ++v)
+                        ox[v] = fmaf(W.w[v][0], da[v], fmaf(W.w[v][1], d1[v], fmaf(W.w[v][2], d2[v], W.w[v][3] * d3[v])));
+                    store_vec<true>(dx + pos(q - 3), ox);
                 }
-                const bool inseq = q >= 0 && q < n;
-                const int64_t off = img + (int64_t)tok_of(inseq ? q : 0) * E + coff;
-                xw[6] = inseq ? load_raw<false>(x + off) : raw{};
-                if (q >= ra) {  // front: da[q]
-                    if (inseq) {
-                        zR[3] = load_raw<false>(z + off);
-                        oR[3] = load_raw<false>(dout + off);
-                        const float* ur = du + (b * T + q / P) * E + coff;
+                x3 = x2;
+                x2 = x1;
+                x1 = xv;
 #pragma unroll
-                        for (int v = 0; v < V; ++v) {
-                            float a = fmaf(W.w[v][3], raw_at(xw[6], v), W.b[v]);
-                            a = fmaf(W.w[v][2], raw_at(xw[5], v), a);
-                            a = fmaf(W.w[v][1], raw_at(xw[4], v), a);
-                            a = fmaf(W.w[v][0], raw_at(xw[3], v), a);
-                            const float zv = raw_at(zR[3], v), sgz = __builtin_amdgcn_rcpf(1.f + __expf(-zv));
-                            const float gv = raw_at(oR[3], v) * zv * sgz;
-                            const float dxc = fmaf(gv, dsum[v], ur[v] * inv_p);
-                            const float sga = __builtin_amdgcn_rcpf(1.f + __expf(-a));
-                            dR[3][v] = dxc * sga * fmaf(a, 1.f - sga, 1.f);
-                        }
-                    } else {
-#pragma unroll
-                        for (int v = 0; v < V; ++v) dR[3][v] = 0.f;
-                    }
+                for (int v = 0; v < V; ++v) {
+                    d3[v] = d2[v];
+                    d2[v] = d1[v];
+                    d1[v] = da[v];
                 }
-                if (q >= ra + 3) {  // finish r = q - 3 (x[r - 3 .. r] = xw[0 .. 3])
-                    const int r = q - 3;
-                    float ox[V], oz[V];
+            };
+            // position q at the front: da[q]; for the run's own positions also
+            // dz[q] and the sums (those past the run only feed dx behind them)
+            auto step = [&](const raw& xv, const raw& zr, const raw& orw, const float (&uq)[V], int q, bool own) {
+                float da[V], oz[V];
 #pragma unroll
-                    for (int v = 0; v < V; ++v) {
-                        float a = fmaf(W.w[v][3], raw_at(xw[3], v), W.b[v]);
-                        a = fmaf(W.w[v][2], raw_at(xw[2], v), a);
-                        a = fmaf(W.w[v][1], raw_at(xw[1], v), a);
-                        a = fmaf(W.w[v][0], raw_at(xw[0], v), a);
-                        const float xc = conv_silu_f(a);
-                        const float zv = raw_at(zR[0], v), dv = raw_at(oR[0], v);
-                        const float sgz = __builtin_amdgcn_rcpf(1.f + __expf(-zv));
-                        const float gv = dv * zv * sgz;
+                for (int v = 0; v < V; ++v) {
+                    float a = fmaf(W.w[v][3], raw_at(xv, v), W.b[v]);
+                    a = fmaf(W.w[v][2], raw_at(x1, v), a);
+                    a = fmaf(W.w[v][1], raw_at(x2, v), a);
+                    a = fmaf(W.w[v][0], raw_at(x3, v), a);
+                    const float sga = __builtin_amdgcn_rcpf(1.f + __expf(-a));
+                    const float zv = raw_at(zr, v), dv = raw_at(orw, v);
+                    const float sgz = __builtin_amdgcn_rcpf(1.f + __expf(-zv));
+                    const float gv = dv * zv * sgz;
+                    const float dxc = fmaf(gv, dsum[v], uq[v]);
+                    da[v] = dxc * sga * fmaf(a, 1.f - sga, 1.f);
+                    if (own) {
+                        const float xc = a * sga;
                         oz[v] = dv * fmaf(dsum[v], xc, sv[v]) * sgz * fmaf(zv, 1.f - sgz, 1.f);
-                        ox[v] = fmaf(W.w[v][0], dR[3][v],
-                                     fmaf(W.w[v][1], dR[2][v], fmaf(W.w[v][2], dR[1][v], W.w[v][3] * dR[0][v])));
                         aD[v] = fmaf(gv, xc, aD[v]);
-                        aB[v] += dR[0][v];
-#pragma unroll
-                        for (int k = 0; k < kTaps; ++k) aW[v][k] = fmaf(dR[0][v], raw_at(xw[k], v), aW[v][k]);
+                        aB[v] += da[v];
+                        aW[v][0] = fmaf(da[v], raw_at(x3, v), aW[v][0]);
+                        aW[v][1] = fmaf(da[v], raw_at(x2, v), aW[v][1]);
+                        aW[v][2] = fmaf(da[v], raw_at(x1, v), aW[v][2]);
+                        aW[v][3] = fmaf(da[v], raw_at(xv, v), aW[v][3]);
                     }
-                    const int64_t ro = img + (int64_t)tok_of(r) * E + coff;
-                    store_vec<true>(dx + ro, ox);
-                    store_vec<true>(dz + ro, oz);
+                }
+                if (own) store_vec<true>(dz + pos(q), oz);
+                finish(xv, da, q);
+            };
+            // the run's positions, kBatchCb at a time with all their loads first
+            int q = ra;
+            for (; q + kBatchCb <= rb; q += kBatchCb) {
+                raw xf[kBatchCb], zf[kBatchCb], of[kBatchCb];
+#pragma unroll
+                for (int i = 0; i < kBatchCb; ++i) {
+                    const int64_t o = pos(q + i);
+                    xf[i] = load_raw<false>(x + o);
+                    zf[i] = load_raw<false>(z + o);
+                    of[i] = load_raw<false>(dout + o);
+                }
+#pragma unroll
+                for (int i = 0; i < kBatchCb; ++i) step(xf[i], zf[i], of[i], uv, q + i, true);
+            }
+            for (; q < rb; ++q) {
+                const int64_t o = pos(q);
+                const raw xv = load_raw<false>(x + o), zv = load_raw<false>(z + o), ov = load_raw<false>(dout + o);
+                step(xv, zv, ov, uv, q, true);
+            }
+            // three positions past the run (da = 0 past the sequence); the last
+            // run of a scan position reaches into the next one
+            for (; q < rb + 3; ++q) {
+                if (q < n) {
+                    const int64_t o = pos(q);
+                    const raw xv = load_raw<false>(x + o), zv = load_raw<false>(z + o),
+                              ov = load_raw<false>(dout + o);
+                    const float* uq = du + (b * T + q / P) * E + coff;
+                    float un[V];
+#pragma unroll
+                    for (int v = 0; v < V; ++v) un[v] = uq[v] * inv_p;
+                    step(xv, zv, ov, un, q, false);
+                } else {
+                    float da[V];
+#pragma unroll
+                    for (int v = 0; v < V; ++v) da[v] = 0.f;
+                    finish(raw{}, da, q);
                 }
             }
         }

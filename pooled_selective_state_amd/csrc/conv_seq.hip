@@ -315,19 +315,39 @@ conv_adjoint_kernel(const typename IO::elem* x, typename IO::elem* dx, const flo
             p1 = xv;
             emit(da, f);
         };
-        // whole batches: the batch's loads first (dxc at f0 .. f0 + 3 precedes
-        // every store of the batch, which reach at most position f0)
-        int f0 = 0;
-        for (; f0 + kBatch <= cnt; f0 += kBatch) {
-            raw xf[kBatch], gf[kBatch];
+        // whole batches, two in flight: the next batch's loads are issued
+        // before the current batch computes and stores (a load of dxc at
+        // position p always precedes the store of dx at p, and the stores of a
+        // batch reach at most its first position)
+        auto load_batch = [&](raw (&xo)[kBatch], raw (&go)[kBatch], int fb) {
 #pragma unroll
             for (int q = 0; q < kBatch; ++q) {
-                xf[q] = load_raw<false>(xp + (f0 + q) * ps);
-                gf[q] = load_raw<false>(gp + (f0 + q) * ps);
+                xo[q] = load_raw<false>(xp + (fb + q) * ps);
+                go[q] = load_raw<false>(gp + (fb + q) * ps);
             }
+        };
+        auto run_batch = [&](const raw (&xi)[kBatch], const raw (&gi)[kBatch], int fb) {
 #pragma unroll
-            for (int q = 0; q < kBatch; ++q) step(xf[q], gf[q], f0 + q);
+            for (int q = 0; q < kBatch; ++q) step(xi[q], gi[q], fb + q);
+        };
+        const int nb = cnt / kBatch;
+        raw xa[kBatch], ga[kBatch], xb2[kBatch], gb2[kBatch];
+        if (nb > 0) load_batch(xa, ga, 0);
+        int ib = 0;
+        for (; ib + 2 < nb; ib += 2) {  // batches ib + 1 and ib + 2 exist
+            load_batch(xb2, gb2, (ib + 1) * kBatch);
+            run_batch(xa, ga, ib * kBatch);
+            load_batch(xa, ga, (ib + 2) * kBatch);
+            run_batch(xb2, gb2, (ib + 1) * kBatch);
         }
+        if (ib + 2 == nb) {
+            load_batch(xb2, gb2, (ib + 1) * kBatch);
+            run_batch(xa, ga, ib * kBatch);
+            run_batch(xb2, gb2, (ib + 1) * kBatch);
+        } else if (ib + 1 == nb) {
+            run_batch(xa, ga, ib * kBatch);
+        }
+        const int f0 = nb * kBatch;
         for (int f = f0; f < cnt; ++f) {
             const raw xv = load_raw<false>(xp + f * ps), gv = load_raw<false>(gp + f * ps);
             step(xv, gv, f);
