@@ -167,21 +167,24 @@ conv_seq_kernel(const typename IO::elem* x, typename IO::elem* xc, const float* 
     for (int f = f0; f < cnt; ++f) step(load_raw<false>(xp + f * ps), f);
 }
 
-// da = dxc silu'(a) at the first three positions of every run but an
-// image's first, into halo[(b runs + sequence-order run) 3 + p][E] (fp32).
+// da = dxc silu'(a) at the first three positions of every run that starts an
+// adjoint slot's chunk (global run index U = c kAdjRunsPerSlot) but an
+// image's first, into halo[c 3 + p][E] (fp32).
 template <class IO, bool FROM_G>
 __global__ void __launch_bounds__(kSeqThreads)
 conv_adjoint_halo_kernel(const typename IO::elem* x, const typename IO::elem* dxc, const float* __restrict__ cw,
                          const float* __restrict__ cb, float* __restrict__ halo, SeqShape sq, int E, int VE,
-                         int64_t items, DxcFromG fg) {
+                         int64_t items, int64_t total_runs, DxcFromG fg) {
     constexpr int V = IO::V;
     using raw = typename IO::raw;
     const int64_t gi = (int64_t)blockIdx.x * kSeqThreads + threadIdx.x;
     if (gi >= items) return;
     const int c = (int)(gi % VE);
-    const int64_t br = gi / VE;  // (image, sequence-order run)
-    const int64_t b = br / sq.runs();
-    const int64_t sr = br - b * sq.runs();
+    const int64_t ci = gi / VE;  // chunk
+    const int64_t U = ci * kAdjRunsPerSlot;
+    if (U >= total_runs) return;
+    const int64_t b = U / sq.runs();
+    const int64_t sr = U - b * sq.runs();  // sequence-order run within the image
     if (sr == 0) return;
     const int line = (int)(sr / sq.nk), k = (int)(sr - (int64_t)line * sq.nk);
     const int r0 = line * sq.len + k * sq.L;  // >= 1
@@ -206,7 +209,7 @@ conv_adjoint_halo_kernel(const typename IO::elem* x, const typename IO::elem* dx
         const raw gr = load_raw<false>(gb + sq.off(r));
         float u[V];
         du_row<V, FROM_G>(fg, b, r / sq.len, E, coff, u);
-        float* dst = halo + ((br * 3 + p) * E + coff);
+        float* dst = halo + ((ci * 3 + p) * E + coff);
 #pragma unroll
         for (int v = 0; v < V; ++v) {
             float a = fmaf(W.w[v][3], raw_at(win[p + 3], v), W.b[v]);
@@ -220,14 +223,16 @@ conv_adjoint_halo_kernel(const typename IO::elem* x, const typename IO::elem* dx
 
 // The adjoint, in place.  Workgroup (group g, channel block cb) of k slots of
 // VB lanes (VB = min(VE, 256) vectors of a token, k = 256 / VB): lane l of
-// slot q takes vector cb VB + l and the launch's runs g k R + q + k i (R =
-// kAdjRunsPerSlot), so every lane has work whatever E is.  A lane walks its
-// run with a front f: at f it loads x and dxc and forms da[f] (past the run,
-// da comes from the halo buffer, past the sequence it is 0), adds the conv's
-// weight and bias gradient terms, and writes dx[f - 3] from da[f - 3 .. f].
-// dxc is read only at positions whose dx is written later by the same lane.
-// At the end the k slots' sums are added in LDS in a fixed order and the
-// workgroup writes its slice of partial row g: [d conv_b (E) | d conv_w (E, 4)].
+// slot q takes vector cb VB + l and the chunk of R = kAdjRunsPerSlot runs
+// g k R + q R + i, i < R, which are consecutive in sequence order, so every
+// lane has work whatever E is.  A lane walks its chunk with a front f: at f it
+// loads x and dxc and forms da[f], adds the conv's weight and bias gradient
+// terms, and writes dx[f - 3] from da[f - 3 .. f].  The walk goes on from one
+// run of the chunk into the next (the windows carry over); past the chunk's
+// last run da comes from the halo buffer (0 past the sequence).  dxc is read
+// only at positions whose dx is written later by the same lane.  At the end
+// the k slots' sums are added in LDS in a fixed order and the workgroup writes
+// its slice of partial row g: [d conv_b (E) | d conv_w (E, 4)].
 template <class IO, bool FROM_G>
 __global__ void __launch_bounds__(kSeqThreads)
 conv_adjoint_kernel(const typename IO::elem* x, typename IO::elem* dx, const float* __restrict__ cw,
@@ -235,6 +240,7 @@ conv_adjoint_kernel(const typename IO::elem* x, typename IO::elem* dx, const flo
                     SeqShape sq, int E, int VE, int VB, int64_t total_runs, DxcFromG fg) {
     constexpr int V = IO::V;
     using raw = typename IO::raw;
+    constexpr int kB = V == 4 ? kBatch : 1;  // positions per batch (bf16: registers)
     extern __shared__ float red[];  // [k][VB][5 V]
     const int k = (int)blockDim.x / VB;
     const int slot = (int)threadIdx.x / VB, lane = (int)threadIdx.x - slot * VB;
@@ -252,39 +258,46 @@ conv_adjoint_kernel(const typename IO::elem* x, typename IO::elem* dx, const flo
 #pragma unroll
         for (int t = 0; t < 4; ++t) sdw[t][v] = 0.f;
     }
-    const int64_t rpi = sq.runs();                      // runs per image
-    const int64_t rpg = (int64_t)k * kAdjRunsPerSlot;  // runs per workgroup
-    const int64_t run_end = min(((int64_t)blockIdx.x + 1) * rpg, total_runs);
+    const int64_t rpi = sq.runs();  // runs per image
     const int64_t ps = sq.pstride;
-    for (int64_t run = (int64_t)blockIdx.x * rpg + slot; run < run_end; run += k) {
-        const int64_t b = run / rpi;
-        int line, kk;
-        sq.run_of(run - b * rpi, &line, &kk);
+    const int64_t c0 = ((int64_t)blockIdx.x * k + slot) * kAdjRunsPerSlot;  // the slot's first run
+    raw p3{}, p2{}, p1{};
+    float d3[V], d2[V], d1[V];
+    int rc0 = 0;  // first position of the walk (in its image)
+    for (int i = 0; i < kAdjRunsPerSlot; ++i) {
+        const int64_t U = c0 + i;
+        if (U >= total_runs) break;
+        const int64_t b = U / rpi;
+        const int sr = (int)(U - b * rpi);  // sequence order within the image
+        const int line = sr / sq.nk, kk = sr - line * sq.nk;
         const int r0 = line * sq.len + kk * sq.L;
         const int cnt = min(sq.L, sq.len - kk * sq.L);
-        const int r1 = r0 + cnt;
-        const int64_t sr = b * rpi + (int64_t)line * sq.nk + kk;  // sequence-order run
+        const bool cont = i > 0 && sr > 0;  // the walk goes on from the previous run
+        const bool last = i + 1 == kAdjRunsPerSlot || U + 1 == total_runs || sr + 1 == rpi;
         const typename IO::elem* xb = x + b * (int64_t)sq.n * E + coff;
+        typename IO::elem* gbase = dx + b * (int64_t)sq.n * E + coff;
         const typename IO::elem* xp = xb + sq.off(r0);
-        typename IO::elem* gp = dx + b * (int64_t)sq.n * E + coff + sq.off(r0);
-        const float* hb = halo + ((sr + 1) * 3 * E + coff);  // the next run's first three positions
+        typename IO::elem* gp = gbase + sq.off(r0);
         float u[V];
         du_row<V, FROM_G>(fg, b, line, E, coff, u);  // one scan position per run
-        raw p3{}, p2{}, p1{};
-        if (r0 >= 3) p3 = load_raw<false>(xb + sq.off(r0 - 3));
-        if (r0 >= 2) p2 = load_raw<false>(xb + sq.off(r0 - 2));
-        if (r0 >= 1) p1 = load_raw<false>(xb + sq.off(r0 - 1));
-        float d3[V], d2[V], d1[V];
+        if (!cont) {
+            rc0 = r0;
+            p3 = p2 = p1 = raw{};
+            if (r0 >= 3) p3 = load_raw<false>(xb + sq.off(r0 - 3));
+            if (r0 >= 2) p2 = load_raw<false>(xb + sq.off(r0 - 2));
+            if (r0 >= 1) p1 = load_raw<false>(xb + sq.off(r0 - 1));
 #pragma unroll
-        for (int v = 0; v < V; ++v) d3[v] = d2[v] = d1[v] = 0.f;
-        // dx[f - 3] from da[f - 3 .. f] (f - 3 >= 0: the same for every lane of the run)
+            for (int v = 0; v < V; ++v) d3[v] = d2[v] = d1[v] = 0.f;
+        }
+        // dx[f - 3] from da[f - 3 .. f], for the positions of the walk: in this
+        // run, or (f < 3, a continued walk) at the end of the previous runs
         auto emit = [&](const float (&da)[V], int f) {
-            if (f >= 3 && valid) {
+            if (r0 + f - 3 >= rc0 && valid) {
                 float o[V];
 #pragma unroll
                 for (int v = 0; v < V; ++v)
                     o[v] = fmaf(W.w[v][0], da[v], fmaf(W.w[v][1], d1[v], fmaf(W.w[v][2], d2[v], W.w[v][3] * d3[v])));
-                store_vec<false>(gp + (f - 3) * ps, o);
+                store_vec<false>(f >= 3 ? gp + (f - 3) * ps : gbase + sq.off(r0 + f - 3), o);
             }
 #pragma unroll
             for (int v = 0; v < V; ++v) {
@@ -319,45 +332,48 @@ conv_adjoint_kernel(const typename IO::elem* x, typename IO::elem* dx, const flo
         // before the current batch computes and stores (a load of dxc at
         // position p always precedes the store of dx at p, and the stores of a
         // batch reach at most its first position)
-        auto load_batch = [&](raw (&xo)[kBatch], raw (&go)[kBatch], int fb) {
+        auto load_batch = [&](raw (&xo)[kB], raw (&go)[kB], int fb) {
 #pragma unroll
-            for (int q = 0; q < kBatch; ++q) {
+            for (int q = 0; q < kB; ++q) {
                 xo[q] = load_raw<false>(xp + (fb + q) * ps);
                 go[q] = load_raw<false>(gp + (fb + q) * ps);
             }
         };
-        auto run_batch = [&](const raw (&xi)[kBatch], const raw (&gi)[kBatch], int fb) {
+        auto run_batch = [&](const raw (&xi)[kB], const raw (&gi)[kB], int fb) {
 #pragma unroll
-            for (int q = 0; q < kBatch; ++q) step(xi[q], gi[q], fb + q);
+            for (int q = 0; q < kB; ++q) step(xi[q], gi[q], fb + q);
         };
-        const int nb = cnt / kBatch;
-        raw xa[kBatch], ga[kBatch], xb2[kBatch], gb2[kBatch];
+        const int nb = cnt / kB;
+        raw xa[kB], ga[kB], xb2[kB], gb2[kB];
         if (nb > 0) load_batch(xa, ga, 0);
         int ib = 0;
         for (; ib + 2 < nb; ib += 2) {  // batches ib + 1 and ib + 2 exist
-            load_batch(xb2, gb2, (ib + 1) * kBatch);
-            run_batch(xa, ga, ib * kBatch);
-            load_batch(xa, ga, (ib + 2) * kBatch);
-            run_batch(xb2, gb2, (ib + 1) * kBatch);
+            load_batch(xb2, gb2, (ib + 1) * kB);
+            run_batch(xa, ga, ib * kB);
+            load_batch(xa, ga, (ib + 2) * kB);
+            run_batch(xb2, gb2, (ib + 1) * kB);
         }
         if (ib + 2 == nb) {
-            load_batch(xb2, gb2, (ib + 1) * kBatch);
-            run_batch(xa, ga, ib * kBatch);
-            run_batch(xb2, gb2, (ib + 1) * kBatch);
+            load_batch(xb2, gb2, (ib + 1) * kB);
+            run_batch(xa, ga, ib * kB);
+            run_batch(xb2, gb2, (ib + 1) * kB);
         } else if (ib + 1 == nb) {
-            run_batch(xa, ga, ib * kBatch);
+            run_batch(xa, ga, ib * kB);
         }
-        const int f0 = nb * kBatch;
-        for (int f = f0; f < cnt; ++f) {
+        for (int f = nb * kB; f < cnt; ++f) {
             const raw xv = load_raw<false>(xp + f * ps), gv = load_raw<false>(gp + f * ps);
             step(xv, gv, f);
         }
-        // the three positions past the run: da from the halo (0 past the sequence)
-        for (int f = cnt; f < cnt + 3; ++f) {
-            float da[V];
+        if (last) {
+            // the three positions past the chunk: da from the halo of the next
+            // chunk's first run (0 past the sequence)
+            const float* hb = halo + ((U + 1) / kAdjRunsPerSlot * 3 * E + coff);
+            for (int f = cnt; f < cnt + 3; ++f) {
+                float da[V];
 #pragma unroll
-            for (int v = 0; v < V; ++v) da[v] = r0 + f < sq.n ? hb[(f - cnt) * E + v] : 0.f;
-            emit(da, f);
+                for (int v = 0; v < V; ++v) da[v] = r0 + f < sq.n ? hb[(f - cnt) * E + v] : 0.f;
+                emit(da, f);
+            }
         }
     }
     if (slot > 0) {
@@ -416,7 +432,8 @@ int adjoint_run(const Geom& g, int64_t floats, int64_t* groups) {
         const SeqShape s = seq_shape(g, L);
         const int64_t runs = g.B * s.runs();
         const int64_t gr = (runs + rpg - 1) / rpg;
-        const int64_t need = (s.runs() > 1 ? runs * 3 * g.E : 0) + gr * 5 * g.E +
+        const int64_t chunks = (runs + kAdjRunsPerSlot - 1) / kAdjRunsPerSlot;
+        const int64_t need = (s.runs() > 1 ? (chunks + 1) * 3 * g.E : 0) + gr * 5 * g.E +
                              ((gr + kColRowsPerBlock - 1) / kColRowsPerBlock) * 4 * g.E + 64;
         if (need <= floats || s.runs() == 1) {
             *groups = gr;
@@ -440,15 +457,17 @@ hipError_t conv_adjoint_t(const Geom& g, const void* x, void* dx, const fastvim_
     const int VE = (int)(g.E / IO::V);
     const int64_t total_runs = g.B * s.runs();
     float* halo = scratch;
-    float* parts = halo + (s.runs() > 1 ? total_runs * 3 * g.E : 0);
+    const int64_t chunks = (total_runs + kAdjRunsPerSlot - 1) / kAdjRunsPerSlot;
+    float* parts = halo + (s.runs() > 1 ? (chunks + 1) * 3 * g.E : 0);
     float* tmp = parts + groups * 5 * g.E;
     const elem* xe = static_cast<const elem*>(x);
     elem* de = static_cast<elem*>(dx);
     if (s.runs() > 1) {
-        const int64_t items = total_runs * VE;
+        const int64_t items = chunks * VE;
         hipLaunchKernelGGL((conv_adjoint_halo_kernel<IO, FROM_G>),
                            dim3((unsigned)((items + kSeqThreads - 1) / kSeqThreads)), dim3(kSeqThreads), 0, st, xe,
-                           static_cast<const elem*>(dx), p.conv_w, p.conv_b, halo, s, (int)g.E, VE, items, fg);
+                           static_cast<const elem*>(dx), p.conv_w, p.conv_b, halo, s, (int)g.E, VE, items,
+                           total_runs, fg);
     }
     const int VB = adjoint_vb(g), slots = adjoint_slots(g);
     const size_t lds = (size_t)((slots - 1) * VB * 5 * IO::V) * sizeof(float);

@@ -581,6 +581,26 @@ def test_bwd_conv_norm_block(io, axis, saved):
               ln=rand_ln(rng, E))
 
 
+# grids whose conv lines (grid rows for COLS, columns for ROWS) hold 1 to 3
+# cells: the conv's adjoint walks chunks of several lines, finishing dx of the
+# runs before the current one, and reads its halo past a chunk's end
+BLOCK_SHORT_LINES = [(3, 3, 2, 64, 4), (2, 1, 5, 72, 5), (2, 7, 1, 72, 5), (1, 2, 40, 136, 9), (2, 5, 3, 8, 3)]
+
+
+@pytest.mark.parametrize("shape", BLOCK_SHORT_LINES, ids=["x".join(map(str, s)) for s in BLOCK_SHORT_LINES])
+@pytest.mark.parametrize("axis", (P.POOL_COLS, P.POOL_ROWS))
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_bwd_conv_norm_block_short_lines(io, axis, shape):
+    B, h, w, E, R = shape
+    rng = np.random.default_rng(zlib.crc32(repr(("bwd-block-short", shape, axis, io)).encode()))
+    x, z, dout = (rng.standard_normal((B, h, w, E)).astype(np.float32) for _ in range(3))
+    x, z, dout = _io(io, x, z, dout)
+    prm = {"fwd": rand_dir(rng, E, 16, R, 0.1), "bwd": rand_dir(rng, E, 16, R, 0.1)}
+    tol, dt = _tol(io)
+    bwd_check(x, z, dout, prm, axis, tol, dt, "block %s axis %d %s" % (io, axis, shape), conv=rand_conv(rng, E),
+              ln=rand_ln(rng, E))
+
+
 @pytest.mark.parametrize("variant", ["pool_scale", "local"])
 def test_bwd_conv_norm_block_options(variant):
     B, h, w, E, R = 2, 12, 10, 64, 5
@@ -608,6 +628,26 @@ def test_bwd_conv_masked(io, axis, saved, norm):
     tol, dt = _tol(io)
     bwd_check(x, z, dout, prm, axis, tol, dt, "masked conv %s axis %d" % (io, axis), idx=idx, hw=(h, w),
               saved=saved, conv=rand_conv(rng, E), ln=rand_ln(rng, E) if norm else None)
+
+
+@pytest.mark.parametrize("K", [1, 2, 5])
+@pytest.mark.parametrize("io", ["f32"])
+def test_bwd_conv_masked_few_tokens(io, K):
+    """Masked layers keeping fewer tokens than the conv's window: runs shorter
+    than three positions, one per image.  (fp32 only: in bf16 the written-out
+    x_conv is rounded to bf16, and with a handful of tokens per image the
+    scan parameters' gradients do not average that rounding below the bf16
+    bar; test_bwd_conv_masked covers bf16 with 100 tokens.)"""
+    B, h, w, E, R = 5, 4, 3, 72, 6
+    rng = np.random.default_rng(zlib.crc32(repr(("bwd-conv-masked-few", io, K)).encode()))
+    x, z, dout = (rng.standard_normal((B, K, E)).astype(np.float32) for _ in range(3))
+    x, z, dout = _io(io, x, z, dout)
+    idx = random_mask(rng, B, h, w, K)
+    prm = {"fwd": rand_dir(rng, E, 16, R, 0.1), "bwd": rand_dir(rng, E, 16, R, 0.1)}
+    tol, dt = _tol(io)
+    for axis in (P.POOL_COLS, P.POOL_ROWS):
+        bwd_check(x, z, dout, prm, axis, tol, dt, "masked conv K=%d %s axis %d" % (K, io, axis), idx=idx,
+                  hw=(h, w), conv=rand_conv(rng, E), ln=rand_ln(rng, E) if K != 2 else None)
 
 
 @pytest.mark.parametrize("axis", (P.POOL_COLS, P.POOL_ROWS))
