@@ -26,10 +26,11 @@
 // next to each other in memory (the runs of a grid row, or the same run of
 // neighbouring columns).
 // The adjoint works in place: dxc arrives in the dx buffer and dx[r] replaces
-// it three positions behind the front that reads dxc.  Its reads past the
-// end of a run (the next run's first three positions) would race with the
-// next run's writes, so a pre-pass stores da at the first three positions of
-// every run into a halo buffer and the adjoint takes them from there.
+// it three positions behind the front that reads dxc.  A lane walks a chunk
+// of consecutive runs as one; its reads past the chunk's end (the next
+// chunk's first three positions) would race with that chunk's writes, so a
+// pre-pass stores da at the first three positions of every chunk into a halo
+// buffer and the adjoint takes them from there.
 #include "bwd_internal.h"
 #include "conv_common.h"
 
@@ -37,7 +38,7 @@ namespace fastvim {
 namespace {
 
 constexpr int kSeqThreads = 256;
-constexpr int kAdjRunsPerSlot = 4;  // runs per adjoint workgroup slot
+constexpr int kAdjRunsPerSlot = 4;  // runs per adjoint workgroup slot (one chunk)
 constexpr int kBatch = 4;           // positions whose loads are issued together
 
 // An image's sequence as lines of runs (element offsets within the image).
@@ -47,7 +48,7 @@ struct SeqShape {
     int lines;
     int L;           // positions per run
     int nk;          // runs per line
-    int colmajor;    // runs of neighbouring lines are neighbours in the launch
+    int colmajor;    // conv_seq_kernel: runs of neighbouring lines are neighbours in the launch
     int64_t pstride; // elements from one position of a line to the next
     int64_t lstride; // elements from one line's first position to the next line's
 
