@@ -1115,16 +1115,14 @@ bool fused_preferred(const Geom& g, bool norm, bool local, bool conv) {
     // pay off once an image's x is several MB: measured faster than the stage
     // kernels at 2048^2 (25 MB fp32, 12.6 MB bf16), slower at 1024^2 (6.3 MB)
     // and below.
-    // With the norm the single launch is faster in fp32 (2048^2, COLS: 1.90
-    // against 2.30 ms; ROWS, blocks of columns with their scan rows in LDS:
-    // 1.95 against 2.34 ms; with the conv on load 2.24 and 2.25 ms against
-    // 3.60 and 3.75 ms for the conv written out and the stage kernels).  In
-    // bf16 it is not: the COLS norm instances need 133 and 145 VGPRs (one
-    // workgroup per CU; 1.92 against 1.50 ms), ROWS measured the same as the
-    // stage kernels (1.50 ms), and with the conv both were slower (3.03 and
-    // 2.83 against 2.15 ms).
+    // With the norm the single launch is faster in fp32 (2048^2, COLS: 1.91
+    // against 2.31 ms; ROWS, blocks of columns with their scan rows in LDS:
+    // 1.95 against 2.34 ms; with the conv on load 2.18 and 2.17 ms against
+    // 3.61 and 3.63 ms for the conv written out and the stage kernels) and in
+    // bf16 (1.36 against 1.42 ms, ROWS 1.39 against 1.45 ms).  bf16 with the
+    // norm and the conv is not: 2.76 and 2.63 against 2.07 and 2.13 ms.
     const int64_t esz = g.io == FASTVIM_BF16 ? 2 : 4;
-    if (norm && g.io == FASTVIM_BF16) return false;
+    if (norm && conv && g.io == FASTVIM_BF16) return false;
     return g.h * g.w * g.E * esz >= (8ll << 20) && fused_supported(g, norm, local, conv);
 }
 
