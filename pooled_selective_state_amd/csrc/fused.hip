@@ -1120,7 +1120,9 @@ bool fused_preferred(const Geom& g, bool norm, bool local, bool conv) {
     // 1.95 against 2.34 ms; with the conv on load 2.18 and 2.17 ms against
     // 3.61 and 3.63 ms for the conv written out and the stage kernels) and in
     // bf16 (1.36 against 1.42 ms, ROWS 1.39 against 1.45 ms).  bf16 with the
-    // norm and the conv is not: 2.76 and 2.63 against 2.07 and 2.13 ms.
+    // norm and the conv on load is not (2.76 and 2.63 ms): such a layer writes
+    // x_conv out and runs the single launch with the norm on it (2.00 and
+    // 2.09 ms; the stage kernels 2.07 and 2.13 ms).
     const int64_t esz = g.io == FASTVIM_BF16 ? 2 : 4;
     if (norm && conv && g.io == FASTVIM_BF16) return false;
     return g.h * g.w * g.E * esz >= (8ll << 20) && fused_supported(g, norm, local, conv);
