@@ -748,10 +748,9 @@ bool conv_adjoint_fits_front(const Geom& g, uint32_t flags) {
     for (const int64_t b : {per, g.B - (n - 1) * per}) {
         Geom gp = g;
         gp.B = b;
-        // offsets only: the layout of a workspace placed at a dummy aligned address
-        BwdWorkspace w;
-        bwd_workspace_layout(gp, reinterpret_cast<void*>(uintptr_t(1) << 20), &w);
-        if (!conv_adjoint_fits(gp, w.du - w.front)) return false;
+        int64_t front = 0;
+        bwd_workspace_layout(gp, nullptr, nullptr, &front);
+        if (!conv_adjoint_fits(gp, front)) return false;
     }
     return true;
 }
@@ -937,7 +936,7 @@ size_t workspace_layout(const Geom& g, void* base, Workspace* ws) {
     return off;
 }
 
-size_t bwd_workspace_layout(const Geom& g, void* base, BwdWorkspace* ws) {
+size_t bwd_workspace_layout(const Geom& g, void* base, BwdWorkspace* ws, int64_t* front_floats) {
     size_t off = 0;
     auto take = [&](size_t bytes) {
         const size_t o = off;
@@ -976,6 +975,7 @@ size_t bwd_workspace_layout(const Geom& g, void* base, BwdWorkspace* ws) {
                       stage1(2 * MC, NX * E), stage1(bwd_conv_parts(g), 4 * E)})
         tmpf = v > tmpf ? v : tmpf;
     const size_t o_tmp = take((size_t)tmpf * sizeof(float));
+    if (front_floats) *front_floats = (int64_t)((o_du - o_u) / sizeof(float));
     if (base && ws) {
         char* c = static_cast<char*>(base);
         auto f = [&](size_t o) { return reinterpret_cast<float*>(c + o); };

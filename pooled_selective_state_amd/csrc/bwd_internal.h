@@ -64,7 +64,8 @@ int64_t bwd_tmax(int64_t R);
 // Second-pass workgroups (each a run of consecutive tokens of one grid row,
 // or of one image's kept tokens when masked): the rows of dDp.
 int64_t bwd_dd_parts(const Geom& g);
-size_t bwd_workspace_layout(const Geom& g, void* base, BwdWorkspace* ws);
+// front_floats (optional): floats of the regions before du (BwdWorkspace::front).
+size_t bwd_workspace_layout(const Geom& g, void* base, BwdWorkspace* ws, int64_t* front_floats = nullptr);
 
 hipError_t launch_bwd_pool(const Geom& g, const void* x, const void* z, const void* dout, const BwdWorkspace& ws,
                            hipStream_t st);
