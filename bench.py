@@ -31,8 +31,8 @@ Reported besides images/s:
 --profile-run times a few steps and the calibration copy only (for profiler
 runs); --profile-bwd adds three backward calls of the same workload, three
 more given the pooled tokens a forward call saved, and three each with the
-post-SSM LayerNorm, the local backward scan and the producer Conv1D (pooled
-tokens saved).
+post-SSM LayerNorm, the local backward scan, the producer Conv1D and both the
+Conv1D and the LayerNorm (pooled tokens saved).
 """
 from __future__ import annotations
 
@@ -314,7 +314,7 @@ def main():
         conv = {"weight": 0.5 * torch.randn(cfg.E, P.CONV_TAPS, device=dev, generator=g_ln),
                 "bias": 0.1 * torch.randn(cfg.E, device=dev, generator=g_ln)}
         for kept, lnk, cv, fl in ((None, None, None, 0), (su, None, None, 0), (su, ln, None, 0),
-                                  (su, None, None, P.FLAG_LOCAL_BWD), (su, None, conv, 0)):
+                                  (su, None, None, P.FLAG_LOCAL_BWD), (su, None, conv, 0), (su, ln, conv, 0)):
             bcall = P.BwdCall(x, z, dout, prm, P.POOL_COLS, saved_u=kept, ln=lnk, conv=cv, flags=fl)
             for _ in range(3):
                 bcall.run(stream)
