@@ -421,11 +421,15 @@ size_t fastvim_ssm_export_bytes(const fastvim_dims *dims, int pool_axis, int wha
  * of a masked layer), written to grads->conv_w and conv_b.  Dense layers
  * without the LayerNorm: the first pass pools x_conv (unless saved_u is
  * given) and the second computes x_conv and da where it reads x, so neither
- * is written.  Masked layers and the LayerNorm: x_conv is written into dz
- * first, the layer's backward pass runs on it (reading each cell's x_conv
- * before writing its dz) and leaves dL/dx_conv in dx, and the conv's adjoint
- * then runs in place on dx, its scratch the workspace (bf16 layers round
- * x_conv and dL/dx_conv to bf16 there).
+ * is written.  Dense layers with the LayerNorm: the pool and the norm's first
+ * pass compute x_conv where they read x, and the conv's adjoint takes the
+ * norm's second pass, forming dL/dx_conv from the norm's gradient as it
+ * reads it, in place on dx (its scratch the workspace).  Masked layers (and
+ * dense ones with the norm too small for that scratch): x_conv is written
+ * into dz first, the layer's backward pass runs on it (reading each cell's
+ * x_conv before writing its dz) and leaves dL/dx_conv in dx, and the conv's
+ * adjoint then runs in place on dx, its scratch the workspace (bf16 layers
+ * round x_conv and dL/dx_conv to bf16 there).
  *
  * Supported: pooled layers (COLS or ROWS, dense or masked) whose scan has at
  * most 720, 512, 384 or 288 steps at dt rank R <= 16, 32, 48 or 64 (the scan
@@ -478,9 +482,9 @@ size_t fastvim_ssm_bwd_workspace_bytes(const fastvim_dims *dims, int pool_axis);
  * Enqueues its kernels on stream and returns.
  *
  * Image groups.  A large call (by default: B >= 16 and h w E >= 2^20, or
- * K E >= 2^20 when masked: 4 groups, 2 with the LayerNorm, none with the
- * Conv1D computed on load; params.tuning's FASTVIM_TUNING_BWD_GROUPS sets the
- * count) runs in groups of ceil(B / groups) images: the first passes of all
+ * K E >= 2^20 when masked: 4 groups, 2 with the LayerNorm (with or without
+ * the Conv1D), none for dense layers with the Conv1D and without the norm;
+ * params.tuning's FASTVIM_TUNING_BWD_GROUPS sets the count) runs in groups of ceil(B / groups) images: the first passes of all
  * groups, then their second passes, in order on stream, while each group's
  * scan adjoint and parameter sums run on a second stream of the library's
  * own (one per device, default priority, created on the first such call and
