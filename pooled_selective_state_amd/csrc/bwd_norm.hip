@@ -77,25 +77,47 @@ bwd_norm_pass1_kernel(const typename IO::elem* x, const typename IO::elem* __res
     constexpr int kTeams = kNormBwdThreads / TL;
     using raw = typename IO::raw;
     extern __shared__ float sm[];
+    // The per-channel rows in LDS (Ep = NV TL V entries each) are stored in
+    // the lanes' order -- vector v, 16-byte quad j of the lane's vector, lane,
+    // element -- so that the 16-byte reads of consecutive lanes are
+    // consecutive and free of bank conflicts (for fp32 that is channel order;
+    // bf16 lanes hold two quads).  The conv's taps: one 16-byte vector per
+    // channel, in the order (vector v, element k, lane).
+    constexpr int kQ = V / 4;
+    const int Ep = NV * TL * V;
     float* srow = sm;
-    float* dsum = sm + E;
-    float* slw = sm + 2 * E;
-    float* slb = sm + 3 * E;
-    float* cwt = sm + 4 * E;  // CONV: [E][4] taps, then [E] bias
-    float* red = sm;  // [kTeams][E], after the last token
+    float* dsum = sm + Ep;
+    float* slw = sm + 2 * Ep;
+    float* slb = sm + 3 * Ep;
+    float* cwt = sm + 4 * Ep;  // CONV: Ep tap vectors, then Ep biases
+    float* red = sm;           // [kTeams][E], after the last token
     __shared__ int list[MASKED ? kNormBwdThreads : 1];
     __shared__ int wave_cnt[kMaxListWaves];
     const int64_t bt = blockIdx.x;
     const int64_t b = bt / T, t = bt - b * T;
     const int tid = threadIdx.x, team = tid / TL, lane = tid % TL;
+    // LDS position of channel q's row entry, and of the lane's element k of
+    // its vector v; tap-vector index of the lane's element k of vector v
+    auto lpos = [&](int q) {
+        const int v = q / (TL * V), r = q - v * TL * V, ln = r / V, k = r - ln * V;
+        return ((v * kQ + (k >> 2)) * TL + ln) * 4 + (k & 3);
+    };
+    auto lat = [&](int v, int k) { return ((v * kQ + (k >> 2)) * TL + lane) * 4 + (k & 3); };
+    auto tat = [&](int v, int k) { return (v * V + k) * TL + lane; };
     for (int q = tid; q < E; q += kNormBwdThreads) {
-        srow[q] = sf[bt * E + q] + sb[bt * E + q];
-        dsum[q] = Df[q] + Db[q];
-        slw[q] = lnw[q];
-        slb[q] = lnb[q];
+        const int o = lpos(q);
+        srow[o] = sf[bt * E + q] + sb[bt * E + q];
+        dsum[o] = Df[q] + Db[q];
+        slw[o] = lnw[q];
+        slb[o] = lnb[q];
     }
     if (CONV)
-        for (int q = tid; q < 5 * E; q += kNormBwdThreads) cwt[q] = q < 4 * E ? cw[q] : cb[q - 4 * E];
+        for (int q = tid; q < E; q += kNormBwdThreads) {
+            const int v = q / (TL * V), r = q - v * TL * V, ln = r / V, k = r - ln * V;
+            *reinterpret_cast<f32x4*>(cwt + ((v * V + k) * TL + ln) * kTaps) =
+                *reinterpret_cast<const f32x4*>(cw + q * kTaps);
+            cwt[4 * Ep + lpos(q)] = cb[q];
+        }
     __syncthreads();
     const float inv_e = 1.f / (float)E;
     float ag[NV][V], ad[NV][V], aw[NV][V], ab[NV][V];
@@ -126,7 +148,7 @@ bwd_norm_pass1_kernel(const typename IO::elem* x, const typename IO::elem* __res
             const int c = (v * TL + lane) * V;
 #pragma unroll
             for (int k = 0; k < V; ++k) {
-                n[v][k] = c < E ? fmaf(dsum[c + k], raw_at(xr[v], k), srow[c + k]) : 0.f;
+                n[v][k] = c < E ? fmaf(dsum[lat(v, k)], raw_at(xr[v], k), srow[lat(v, k)]) : 0.f;
                 sum += n[v][k];
             }
         }
@@ -155,8 +177,8 @@ bwd_norm_pass1_kernel(const typename IO::elem* x, const typename IO::elem* __res
                     const float zv = raw_at(zr[v], k), dv = raw_at(dr[v], k);
                     const float sg = nb_sigmoid(zv);
                     const float go = dv * zv * sg;
-                    const float lw = slw[c + k];
-                    oz[k] = dv * fmaf(nv, lw, slb[c + k]) * sg * fmaf(zv, 1.f - sg, 1.f);
+                    const float lw = slw[lat(v, k)];
+                    oz[k] = dv * fmaf(nv, lw, slb[lat(v, k)]) * sg * fmaf(zv, 1.f - sg, 1.f);
                     aw[v][k] = fmaf(go, nv, aw[v][k]);
                     ab[v][k] += go;
                     dn[v][k] = go * lw;
@@ -198,7 +220,7 @@ bwd_norm_pass1_kernel(const typename IO::elem* x, const typename IO::elem* __res
             const int c = (v * TL + lane) * V;
 #pragma unroll
             for (int k = 0; k < V; ++k) {
-                n[v][k] = c < E ? fmaf(dsum[c + k], xat(v, k), srow[c + k]) : 0.f;
+                n[v][k] = c < E ? fmaf(dsum[lat(v, k)], xat(v, k), srow[lat(v, k)]) : 0.f;
                 sum += n[v][k];
             }
         }
@@ -227,8 +249,8 @@ bwd_norm_pass1_kernel(const typename IO::elem* x, const typename IO::elem* __res
                     const float zv = raw_at(zr[v], k), dv = raw_at(dr[v], k);
                     const float sg = nb_sigmoid(zv);
                     const float go = dv * zv * sg;
-                    const float lw = slw[c + k];
-                    oz[k] = dv * fmaf(nv, lw, slb[c + k]) * sg * fmaf(zv, 1.f - sg, 1.f);
+                    const float lw = slw[lat(v, k)];
+                    oz[k] = dv * fmaf(nv, lw, slb[lat(v, k)]) * sg * fmaf(zv, 1.f - sg, 1.f);
                     aw[v][k] = fmaf(go, nv, aw[v][k]);
                     ab[v][k] += go;
                     dn[v][k] = go * lw;
@@ -310,8 +332,8 @@ bwd_norm_pass1_kernel(const typename IO::elem* x, const typename IO::elem* __res
                     if (c < E) {
 #pragma unroll
                         for (int q = 0; q < V; ++q) {
-                            const f32x4 t4 = *reinterpret_cast<const f32x4*>(cwt + (c + q) * kTaps);
-                            float av = fmaf(t4.w, raw_at(xr[v], q), cwt[4 * E + c + q]);
+                            const f32x4 t4 = *reinterpret_cast<const f32x4*>(cwt + tat(v, q) * kTaps);
+                            float av = fmaf(t4.w, raw_at(xr[v], q), cwt[4 * Ep + lat(v, q)]);
                             av = fmaf(t4.z, raw_at(w1[v], q), av);
                             av = fmaf(t4.y, raw_at(w2[v], q), av);
                             av = fmaf(t4.x, raw_at(w3[v], q), av);
@@ -407,8 +429,9 @@ hipError_t pass1_launch(const Geom& g, const void* x, const void* z, const void*
     using elem = typename IO::elem;
     constexpr int kTeams = kNormBwdThreads / TL;
     const bool conv = (p.flags & FASTVIM_FLAG_CONV) != 0;  // dense layers: x is the conv's input
-    const int rows_lds = conv ? (kTeams > 9 ? kTeams : 9) : (kTeams > 4 ? kTeams : 4);
-    const size_t lds = (size_t)(rows_lds * g.E) * sizeof(float);
+    const int64_t Ep = (int64_t)NV * TL * IO::V;  // padded row length (see the kernel)
+    const int64_t rows = (conv ? 9 : 4) * Ep, red = (int64_t)kTeams * g.E;
+    const size_t lds = (size_t)(rows > red ? rows : red) * sizeof(float);
     const dim3 grid((unsigned)(g.B * g.T)), block(kNormBwdThreads);
     const elem *xe = static_cast<const elem*>(x), *ze = static_cast<const elem*>(z),
                *de = static_cast<const elem*>(dout);
