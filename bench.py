@@ -204,26 +204,33 @@ def small_configs(P, C, torch, stream, nsets=4, calls=200):
         shape = (cfg.B, cfg.K, cfg.E) if cfg.masked else (cfg.B, cfg.h, cfg.w, cfg.E)
         prm = {d: {k: torch.from_numpy(v).cuda() for k, v in draw_dir_params(rng, cfg.E, cfg.N, cfg.R).items()}
                for d in ("fwd", "bwd")}
-        sets = []
+        sets, two = [], []
         for _ in range(nsets):
             x = torch.randn(shape, device="cuda", generator=g).to(dt)
             z = torch.randn(shape, device="cuda", generator=g).to(dt)
             idx = (torch.from_numpy(random_mask(rng, cfg.B, cfg.h, cfg.w, cfg.K)).cuda() if cfg.masked else None)
-            sets.append(P.SSMCall(x, z, prm, P.POOL_COLS, mask_idx=idx,
-                                  hw=(cfg.h, cfg.w) if cfg.masked else None))
-        for c in sets:
+            hw = (cfg.h, cfg.w) if cfg.masked else None
+            sets.append(P.SSMCall(x, z, prm, P.POOL_COLS, mask_idx=idx, hw=hw))
+            # the same layer with its scan and output stages as two launches
+            two.append(P.SSMCall(x, z, prm, P.POOL_COLS, mask_idx=idx, hw=hw, out=sets[-1].out,
+                                 workspace=sets[-1].workspace, tuning=P.tuning_scan_out(P.SCAN_OUT_TWO)))
+        for c in sets + two:
             c.run(stream)
         k = [0]
 
-        def step():
-            sets[k[0] % nsets].run(stream)
-            k[0] += 1
-        ms, per = time_steps(step, calls, stream)
+        def rotate(calls_):
+            def step():
+                calls_[k[0] % nsets].run(stream)
+                k[0] += 1
+            return step
+        ms, per = time_steps(rotate(sets), calls, stream)
+        ms_two, _ = time_steps(rotate(two), calls, stream)
         res[cfg.name] = {"ms": ms, "ms_median": float(np.median(per)), "images_per_s": cfg.B / (ms * 1e-3),
                          "tokens_per_s": cfg.B * cfg.tokens_per_image / (ms * 1e-3),
                          "hbm_frac": cfg.io_bytes() / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9), "dtype": cfg.io_dtype,
-                         "path": "stage kernels"}
-        del sets
+                         "path": "stage kernels, scan and output stages in one launch",
+                         "ms_scan_and_output_two_launches": ms_two}
+        del sets, two
         torch.cuda.empty_cache()
     return res
 
@@ -526,6 +533,16 @@ def main():
             b2.run(stream)
         chain()
         ch_ms, _ = time_steps(chain, n, stream)
+        # the same chain with each block's scan and output stages in one launch
+        one = P.tuning_scan_out(P.SCAN_OUT_ONE)
+        b1o = P.SSMCall(x2, z2, prm, P.POOL_COLS, workspace=b1.workspace, out=b1.out, tuning=one)
+        b2o = P.SSMCall(b1.out, z2b, prm, P.POOL_ROWS, workspace=b1.workspace, out=b2.out, tuning=one)
+
+        def chain_one():
+            b1o.run(stream)
+            b2o.run(stream)
+        chain_one()
+        ch_one_ms, _ = time_steps(chain_one, n, stream)
         s1 = P.SSMCall(x2, z2, prm, P.POOL_COLS, workspace=b1.workspace, out=b2.out, flags=P.FLAG_STAGED)
         s1.run(stream)
         p_scan, _ = time_steps(lambda: s1.stage(P.STAGE_SCAN, stream), n, stream)
@@ -535,10 +552,11 @@ def main():
         u2_scan, _ = time_steps(lambda: u2.stage(P.STAGE_SCAN, stream), 3, stream)
         extras["chain_1024"] = {"workload": c2.name, "two_block_ms": ch_ms, "images_per_s": c2.B / (ch_ms * 1e-3),
                                 "hbm_frac": 2 * 12 * n2 / (ch_ms * 1e-3) / (HBM_PEAK_GBS * 1e9),
+                                "two_block_ms_scan_and_output_one_launch": ch_one_ms,
                                 "pooled_scan_ms": p_scan, "unpooled_layer_ms": u2_ms, "unpooled_scan_ms": u2_scan,
                                 "scan_speedup_pooled": u2_scan / p_scan,
                                 "layer_speedup_pooled": u2_ms / (ch_ms / 2)}
-        del b1, b2, s1, u2
+        del b1, b2, b1o, b2o, s1, u2
         torch.cuda.empty_cache()
         extras["other_configs"] = small_configs(P, C, torch, stream)
         result["extras"] = extras

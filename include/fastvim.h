@@ -174,7 +174,8 @@ typedef struct fastvim_params {
  * exercise the give-up path (the kernel then finishes with invalid outputs,
  * NaN in every output block that follows a failed wait, and
  * fastvim_get_device_error reports FASTVIM_ERR_DEVICE_WAIT).  Other bits,
- * except FASTVIM_TUNING_BWD_GROUPS below: FASTVIM_ERR_ARG. */
+ * except FASTVIM_TUNING_BWD_GROUPS and FASTVIM_TUNING_SCAN_OUT below:
+ * FASTVIM_ERR_ARG. */
 #define FASTVIM_TUNING_LS(n) ((uint32_t)(n) & 0xffu)
 #define FASTVIM_TUNING_LE(n) (((uint32_t)(n) & 0xffu) << 8)
 #define FASTVIM_TUNING_POLL1 (1u << 16)
@@ -182,6 +183,13 @@ typedef struct fastvim_params {
  * at most 32; see fastvim_ssm_bwd).  The forward calls ignore them, the
  * backward call takes no other tuning bits. */
 #define FASTVIM_TUNING_BWD_GROUPS(n) (((uint32_t)(n) & 0x3fu) << 20)
+/* Bits 26-27: how the stage kernels of a pooled layer with a scan of at most
+ * 64 steps, without the post-SSM LayerNorm and without the Conv1D computed
+ * on load, run their scan and output stages: 0 = automatic (one launch for
+ * masked layers and for images of at most 1024 tokens, two launches
+ * otherwise), 1 = two launches, 2 = one launch; 3 is FASTVIM_ERR_ARG.  The
+ * results are the same either way, bit for bit. */
+#define FASTVIM_TUNING_SCAN_OUT(n) (((uint32_t)(n) & 0x3u) << 26)
 
 /* FASTVIM_FLAG_POST_NORM adds the post-SSM LayerNorm between the skip and the
  * gate (FastVim summary page, section 方法详解, bullet 5: LayerNorm after the

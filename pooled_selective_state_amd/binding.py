@@ -53,6 +53,15 @@ def tuning_lags(ls: int = 0, le: int = 0) -> int:
     return (int(ls) & 0xFF) | ((int(le) & 0xFF) << 8)
 
 
+# bits 26-27: the scan and output stages of short pooled stage-kernel layers
+# as one launch (0 = automatic, 1 = two launches, 2 = one launch)
+SCAN_OUT_AUTO, SCAN_OUT_TWO, SCAN_OUT_ONE = 0, 1, 2
+
+
+def tuning_scan_out(n: int) -> int:
+    return (int(n) & 0x3) << 26
+
+
 # workspace=NO_WORKSPACE: pass a NULL workspace, so the library takes its
 # scratch from the stream-ordered allocator on the call's stream
 NO_WORKSPACE = "stream-ordered"

@@ -122,8 +122,9 @@ int check_flags(const fastvim_params& p) {
                              FASTVIM_FLAG_POOL_SCALE | FASTVIM_FLAG_CHECK_IDX;
     if ((p.flags & ~(paths | options)) || (p.flags & paths) == paths) return FASTVIM_ERR_ARG;
     if (p.tuning & ~(FASTVIM_TUNING_LS(0xff) | FASTVIM_TUNING_LE(0xff) | FASTVIM_TUNING_POLL1 |
-                     FASTVIM_TUNING_BWD_GROUPS(0x3f)))
+                     FASTVIM_TUNING_BWD_GROUPS(0x3f) | FASTVIM_TUNING_SCAN_OUT(3)))
         return FASTVIM_ERR_ARG;
+    if (((p.tuning >> 26) & 3u) == 3u) return FASTVIM_ERR_ARG;
     return FASTVIM_OK;
 }
 
@@ -823,8 +824,18 @@ int check_stage_dst(const Geom& g, const StageDst& d, const void* x, const void*
     return FASTVIM_OK;
 }
 
+// The scan and output stages as one launch (scan_out.hip), for the short
+// pooled layers it supports: by the tuning word's bits 26-27, else for masked
+// layers and images of at most 1024 tokens.
+bool scan_out_chosen(const Geom& g, uint32_t flags) {
+    if (!scan_out_supported(g, flags)) return false;
+    const uint32_t set = (g.tuning >> 26) & 3u;
+    if (set) return set == 2u;
+    return g.masked || g.h * g.w <= 1024;
+}
+
 // The layer on a bound workspace: counters cleared, then the single launch or
-// the stage kernels.
+// the stage kernels (the scan and output stages of short layers as one).
 int run_fwd(const Geom& g, const void* x, const void* z, const fastvim_params& prm, const int32_t* idx, void* out,
             const Workspace& ws, hipStream_t s) {
     const bool norm = (prm.flags & FASTVIM_FLAG_POST_NORM) != 0;
@@ -846,7 +857,10 @@ int run_fwd(const Geom& g, const void* x, const void* z, const fastvim_params& p
     if (launch_zero_sync(ws, sync_words(g), s) != hipSuccess) return FASTVIM_ERR_HIP;
     const fastvim_params q = effective_params(prm);
     if (single) return launch_fused(g, x, z, q, ws, out, s) == hipSuccess ? FASTVIM_OK : FASTVIM_ERR_HIP;
+    const bool scan_out = scan_out_chosen(g, q.flags);
     for (int stage = FASTVIM_STAGE_ROWS; stage <= FASTVIM_STAGE_EPILOGUE; ++stage) {
+        if (scan_out && stage == FASTVIM_STAGE_SCAN)
+            return launch_scan_out(g, x, z, q, ws, out, s) == hipSuccess ? FASTVIM_OK : FASTVIM_ERR_HIP;
         const int st = run_stage(stage, g, x, z, q, idx, out, ws, s);
         if (st) return st;
     }

@@ -72,6 +72,11 @@ hipError_t launch_conv_pool(const Geom& g, const void* x, const fastvim_params& 
                             hipStream_t st);
 hipError_t launch_conv_epilogue(const Geom& g, const void* x, const void* z, const fastvim_params& p,
                                 const Workspace& ws, void* out, hipStream_t st);
+// Scan and output stage in one launch (scan_out.hip): pooled layers with
+// scans of at most 64 steps, without the LayerNorm or the Conv1D on load.
+bool scan_out_supported(const Geom& g, uint32_t flags);
+hipError_t launch_scan_out(const Geom& g, const void* x, const void* z, const fastvim_params& p,
+                           const Workspace& ws, void* out, hipStream_t st);
 hipError_t launch_epilogue_norm(const Geom& g, const void* x, const void* z, const fastvim_params& p,
                                 const Workspace& ws, void* out, hipStream_t st);
 // Single-launch dense pooled layer (fused.hip).

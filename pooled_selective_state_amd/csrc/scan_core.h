@@ -318,12 +318,19 @@ __device__ __forceinline__ void scan_step_preact_mfma(const ScanLane<RMAX>& L, c
 // otherwise it keeps the step sizes and recomputes them (where occupancy
 // matters more than the exponentials).  Neither needs a second step-size pass.
 // qs (MFMA phase 3 only): the wave's 256 floats of LDS.
-template <int RMAX, bool WRITE_THROUGH, bool LOCAL = false, bool KEEP_DECAYS = true, bool MFMA = false>
+// SLDS: every output is also stored to so, the workgroup's LDS copy
+// [direction][t][channel] (T x kScanCh floats per direction, t in scan
+// position order), for a consumer in the same workgroup; the workgroup then
+// covers kScanCh channels (the lanes' channel is (thread % 256) / kLps).
+template <int RMAX, bool WRITE_THROUGH, bool LOCAL = false, bool KEEP_DECAYS = true, bool MFMA = false,
+          bool SLDS = false>
 __device__ __forceinline__ void scan_chunk(const ScanArgs& a, ScanLane<RMAX>& L, const float* dr,
-                                           const float (&ucur)[kJ], int64_t base, float* qs = nullptr) {
+                                           const float (&ucur)[kJ], int64_t base, float* qs = nullptr,
+                                           float* so = nullptr) {
     constexpr int S = row_stride_lds<RMAX>();
     constexpr bool kKeep = LOCAL && KEEP_DECAYS;
     const int64_t T = a.T;
+    const int chl = (threadIdx.x & 255) / kLps;  // SLDS: the lane's channel in the workgroup
     float dl[kJ], du[kJ], du0[kJ], dl0[kJ];
     float aS[kKeep ? kChunk : 1][kNs];  // decays of the chunk's steps (LOCAL, KEEP_DECAYS)
     {
@@ -384,6 +391,10 @@ __device__ __forceinline__ void scan_chunk(const ScanArgs& a, ScanLane<RMAX>& L,
         if (L.valid && base + 4 * k + L.q < T) {
             if (WRITE_THROUGH) __hip_atomic_store(sp, keep, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             else *sp = keep;
+            if (SLDS) {
+                const int ti = (int)base + 4 * k + L.q;  // traversal step; backward: t = T - 1 - ti
+                so[((L.dir ? 2 * (int)T - 1 - ti : ti) * kScanCh) + chl] = keep;
+            }
         }
         sp += 4 * L.sstep;
     }
@@ -425,6 +436,7 @@ __device__ __forceinline__ void scan_chunk(const ScanArgs& a, ScanLane<RMAX>& L,
                 float* dst = L.sqb + (base + 4 * k) * a.E;
                 if (WRITE_THROUGH) __hip_atomic_store(dst, keep, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 else *dst = keep;
+                if (SLDS) so[(((int)T + (int)base + 4 * k + L.q) * kScanCh) + chl] = keep;
             }
         }
     }
@@ -440,10 +452,12 @@ __device__ __forceinline__ void scan_chunk(const ScanArgs& a, ScanLane<RMAX>& L,
 template <int RMAX>
 constexpr int chunk_lds_floats() { return 2 * kChunk * row_stride_lds<RMAX>(); }
 
-// KEEP_DECAYS as scan_chunk (LOCAL only).
-template <int RMAX, bool WRITE_THROUGH, class USrc, bool LOCAL = false, bool MFMA = false, bool KEEP_DECAYS = true>
+// KEEP_DECAYS and SLDS (with so) as scan_chunk (KEEP_DECAYS: LOCAL only).
+template <int RMAX, bool WRITE_THROUGH, class USrc, bool LOCAL = false, bool MFMA = false, bool KEEP_DECAYS = true,
+          bool SLDS = false>
 __device__ __forceinline__ void scan_tile(const ScanArgs& a, const USrc& usrc, int64_t b, int64_t e0,
-                                          float* xs /* chunk_lds_floats<RMAX>() */, float* qs = nullptr) {
+                                          float* xs /* chunk_lds_floats<RMAX>() */, float* qs = nullptr,
+                                          float* so = nullptr) {
     constexpr int S = row_stride_lds<RMAX>();
     constexpr int kPre = row_loads<RMAX>();
     ScanLane<RMAX> L;
@@ -491,7 +505,8 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, const USrc& usrc, i
         for (int j = 0; j < kJ; ++j) ucur[j] = pre_u[j];
         __syncthreads();
         if (c + 1 < nchunks) prefetch(base + kChunk);
-        scan_chunk<RMAX, WRITE_THROUGH, LOCAL, KEEP_DECAYS, MFMA>(a, L, xs + L.dir * kChunk * S, ucur, base, wqs);
+        scan_chunk<RMAX, WRITE_THROUGH, LOCAL, KEEP_DECAYS, MFMA, SLDS>(a, L, xs + L.dir * kChunk * S, ucur, base,
+                                                                      wqs, so);
     }
 }
 

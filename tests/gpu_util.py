@@ -71,17 +71,17 @@ def io_dtype(cfg_or_name):
 
 
 def gpu_call(x, z, params, axis, idx=None, hw=None, dtype=torch.float32, flags=0, ln=None, conv=None,
-             pool_scale=None):
+             pool_scale=None, tuning=0):
     """Prepared call on device copies of numpy inputs; returns the SSMCall.
     ln: None or {"weight", "bias", "eps"} (numpy) for the post-SSM LayerNorm;
     conv: None or {"weight", "bias"} (numpy) for the producer Conv1D;
-    pool_scale: None or the factor on the pooled tokens."""
+    pool_scale: None or the factor on the pooled tokens; tuning: the params.tuning word."""
     xd, zd = dev(x, dtype), dev(z, dtype)
     idd = None if idx is None else dev(idx, torch.int32)
     lnd = None if ln is None else {"weight": dev(ln["weight"]), "bias": dev(ln["bias"]), "eps": ln["eps"]}
     cvd = None if conv is None else {"weight": dev(conv["weight"]), "bias": dev(conv["bias"])}
     return P.SSMCall(xd, zd, dev_params(params), axis, mask_idx=idd, hw=hw, flags=flags, ln=lnd, conv=cvd,
-                     pool_scale=pool_scale)
+                     pool_scale=pool_scale, tuning=tuning)
 
 
 def status_ok(call):

@@ -465,10 +465,24 @@ def test_forward_accepts_the_backward_groups():
     c.params.tuning = P.tuning_bwd_groups(8) | P.tuning_lags(3, 7)
     c.x += 4
     expect(c, EALIGN)
-    for bad in (P.tuning_bwd_groups(8) | (1 << 26), 1 << 17):
+    for bad in (P.tuning_bwd_groups(8) | (1 << 28), 1 << 17, P.tuning_scan_out(3)):
         c = FakeCall()
         c.params.tuning = bad
         expect(c, EARG)
+
+
+def test_forward_scan_out_tuning():
+    """Bits 26-27 choose how short stage-kernel layers run their scan and
+    output stages: 0, 1 and 2 are accepted (the call goes on to its next
+    check, a misaligned x here), 3 is ARG."""
+    for n in (P.SCAN_OUT_AUTO, P.SCAN_OUT_TWO, P.SCAN_OUT_ONE):
+        c = FakeCall()
+        c.params.tuning = P.tuning_scan_out(n) | P.tuning_lags(3, 7)
+        c.x += 4
+        expect(c, EALIGN)
+    c = FakeCall()
+    c.params.tuning = P.tuning_scan_out(3)
+    expect(c, EARG)
 
 
 def test_bwd_workspace_covers_every_grouping():
