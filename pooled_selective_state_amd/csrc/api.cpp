@@ -858,7 +858,15 @@ int run_fwd(const Geom& g, const void* x, const void* z, const fastvim_params& p
     const fastvim_params q = effective_params(prm);
     if (single) return launch_fused(g, x, z, q, ws, out, s) == hipSuccess ? FASTVIM_OK : FASTVIM_ERR_HIP;
     const bool scan_out = scan_out_chosen(g, q.flags);
+    // masked layers: mask rows and pooling as one launch where the layer fits it
+    const bool mask_pool = !(q.flags & FASTVIM_FLAG_CONV) && mask_pool_supported(g);
     for (int stage = FASTVIM_STAGE_ROWS; stage <= FASTVIM_STAGE_EPILOGUE; ++stage) {
+        if (mask_pool && stage == FASTVIM_STAGE_ROWS) {
+            unsigned* status = (q.flags & FASTVIM_FLAG_CHECK_IDX) ? ws.sync + 1 : nullptr;
+            if (launch_mask_pool(g, idx, x, ws, status, s) != hipSuccess) return FASTVIM_ERR_HIP;
+            stage = FASTVIM_STAGE_POOL;  // done too
+            continue;
+        }
         if (scan_out && stage == FASTVIM_STAGE_SCAN)
             return launch_scan_out(g, x, z, q, ws, out, s) == hipSuccess ? FASTVIM_OK : FASTVIM_ERR_HIP;
         const int st = run_stage(stage, g, x, z, q, idx, out, ws, s);

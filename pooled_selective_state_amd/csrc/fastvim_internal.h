@@ -62,6 +62,11 @@ int fwd_on_scratch(const void* x, const void* z, const fastvim_params* params, c
 hipError_t launch_mask_rows(const Geom& g, const int32_t* idx, const Workspace& ws, unsigned* status,
                             hipStream_t st);
 hipError_t launch_pool(const Geom& g, const void* x, const Workspace& ws, hipStream_t st);
+// Masked layers: mask rows and pooling in one launch, one workgroup per image
+// (pool.hip), for at most 1024 kept tokens per image.
+bool mask_pool_supported(const Geom& g);
+hipError_t launch_mask_pool(const Geom& g, const int32_t* idx, const void* x, const Workspace& ws,
+                            unsigned* status, hipStream_t st);
 hipError_t launch_proj(const Geom& g, const void* x, const fastvim_params& p, const Workspace& ws,
                        hipStream_t st);
 hipError_t launch_scan(const Geom& g, const void* x, const fastvim_params& p, const Workspace& ws,

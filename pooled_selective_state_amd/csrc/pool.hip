@@ -145,6 +145,126 @@ pool_masked_kernel(const typename IO::elem* __restrict__ x, const int32_t* __res
     }
 }
 
+// Masked layers with at most kImgMaxK kept tokens per image: mask rows and
+// pooling in one launch, one 1024-thread workgroup per image.
+//   1. as mask_rows_kernel: LDS occurrence counts of the grid cells, the row
+//      of every kept token (-1 if out of range or repeated), the image's
+//      invalid count;
+//   2. per-row token lists in LDS, in increasing k: a token's place in its
+//      row's list is the number of valid tokens of that row before it;
+//   3. lane group g of G = blockDim / VE takes rows g, g + G, ...: lane c
+//      loads the 16-byte column c of the row's listed tokens kB at a time and
+//      adds them in list order, then writes u[b, row] = sum * pool_scale / P
+//      (an empty row pools to 0).
+// The row sums come out in token order, deterministically; one workgroup per
+// image replaces B*T small workgroups whose fixed costs (a list built with
+// barriers per row, an LDS reduction) outweighed their few loads.
+constexpr int kImgThreads = 1024;
+constexpr int64_t kImgMaxK = kImgThreads;
+
+template <class IO>
+__global__ void __launch_bounds__(kImgThreads)
+pool_masked_image_kernel(const typename IO::elem* __restrict__ x, const int32_t* __restrict__ idx,
+                         int32_t* __restrict__ rows, int32_t* __restrict__ bad, unsigned* __restrict__ status,
+                         float* __restrict__ u, int64_t T, int64_t K, int64_t hw, int64_t w, int axis, int VE,
+                         int64_t E, float inv_p) {
+    constexpr int V = IO::V;
+    constexpr int kB = 8;                    // listed tokens in flight per lane
+    extern __shared__ uint32_t sm[];         // cnt[hw], then rowk[K], list[K], rcnt[T], rstart[T]
+    uint32_t* cnt = sm;
+    int* rowk = reinterpret_cast<int*>(sm + hw);
+    int* list = rowk + K;
+    int* rcnt = list + K;
+    int* rstart = rcnt + T;
+    __shared__ uint32_t nbad;
+    const int64_t b = blockIdx.x;
+    const int tid = threadIdx.x;
+    if (tid == 0) nbad = 0;
+    for (int64_t q = tid; q < hw; q += blockDim.x) cnt[q] = 0;
+    for (int64_t q = tid; q < T; q += blockDim.x) rcnt[q] = 0;
+    __syncthreads();
+    // 1. validation and rows (K <= blockDim: one token per thread)
+    const bool has = tid < K;
+    const int64_t v = has ? idx[b * K + tid] : -1;
+    if (has && v >= 0 && v < hw) atomicAdd(&cnt[v], 1u);
+    __syncthreads();
+    int r = -1;
+    if (has) {
+        const bool ok = v >= 0 && v < hw && cnt[v] == 1u;
+        r = ok ? (int)(axis == FASTVIM_POOL_COLS ? v / w : v % w) : -1;
+        rows[b * K + tid] = r;
+        rowk[tid] = r;
+        if (!ok) atomicAdd(&nbad, 1u);
+        else atomicAdd(&rcnt[r], 1);
+    }
+    __syncthreads();
+    if (tid == 0) {
+        bad[b] = (int32_t)nbad;
+        if (status && nbad) atomicOr(status, kStatusBadIndex);
+        int acc = 0;
+        for (int64_t t = 0; t < T; ++t) {
+            rstart[t] = acc;
+            acc += rcnt[t];
+        }
+    }
+    __syncthreads();
+    // 2. per-row lists in token order
+    if (r >= 0) {
+        int rank = 0;
+        for (int k = 0; k < tid; ++k) rank += rowk[k] == r ? 1 : 0;
+        list[rstart[r] + rank] = tid;
+    }
+    __syncthreads();
+    // 3. row sums
+    const int G = (int)(blockDim.x / VE);
+    const int c = tid % VE, g = tid / VE;
+    if (g >= G) return;
+    const typename IO::elem* xs = x + b * K * E + (int64_t)c * V;
+    float* ub = u + b * T * E + (int64_t)c * V;
+    for (int64_t t = g; t < T; t += G) {
+        const int n = rcnt[t], s0 = rstart[t];
+        float acc[V];
+#pragma unroll
+        for (int q = 0; q < V; ++q) acc[q] = 0.f;
+        for (int i0 = 0; i0 < n; i0 += kB) {
+            float a[kB][V];
+#pragma unroll
+            for (int j = 0; j < kB; ++j)
+                if (i0 + j < n) load_vec<false>(xs + (int64_t)list[s0 + i0 + j] * E, a[j]);
+#pragma unroll
+            for (int j = 0; j < kB; ++j)
+                if (i0 + j < n) {
+#pragma unroll
+                    for (int q = 0; q < V; ++q) acc[q] += a[j][q];
+                }
+        }
+#pragma unroll
+        for (int q = 0; q < V; q += 4)
+            *reinterpret_cast<f32x4*>(ub + t * E + q) =
+                f32x4{acc[q] * inv_p, acc[q + 1] * inv_p, acc[q + 2] * inv_p, acc[q + 3] * inv_p};
+    }
+}
+
+// LDS bytes of pool_masked_image_kernel, or 0 when the layer does not fit it
+// (more kept tokens than threads, a row's lanes wider than the workgroup, or
+// more than 64 KB of LDS).
+template <class IO>
+size_t pool_masked_image_lds(const Geom& g) {
+    if (g.K > kImgMaxK || g.E / IO::V > kImgThreads) return 0;
+    const size_t bytes = (size_t)(g.h * g.w + 2 * g.K + 2 * g.T) * 4;
+    return bytes <= 64 * 1024 ? bytes : 0;
+}
+
+template <class IO>
+hipError_t pool_masked_image_t(const Geom& g, const int32_t* idx, const void* x, const Workspace& ws,
+                               unsigned* status, hipStream_t st) {
+    hipLaunchKernelGGL(pool_masked_image_kernel<IO>, dim3((unsigned)g.B), dim3(kImgThreads),
+                       pool_masked_image_lds<IO>(g), st, static_cast<const typename IO::elem*>(x), idx, ws.rows,
+                       ws.bad, status, ws.u, g.T, g.K, g.h * g.w, g.w, g.axis, (int)(g.E / IO::V), g.E,
+                       pool_norm(g));
+    return hipGetLastError();
+}
+
 // Threads per workgroup: G groups of VE lanes, G <= P, about 512 threads.
 void pick_groups(int64_t VE, int64_t P, int* G, int* threads) {
     int64_t g = 512 / VE;
@@ -191,6 +311,17 @@ hipError_t launch_mask_rows(const Geom& g, const int32_t* idx, const Workspace& 
     hipLaunchKernelGGL(mask_rows_kernel, dim3((unsigned)g.B), dim3(256), lds, st, idx, ws.rows, ws.bad, status,
                        g.K, g.h * g.w, g.w, g.axis);
     return hipGetLastError();
+}
+
+bool mask_pool_supported(const Geom& g) {
+    if (!g.masked || !g.pooled) return false;
+    return g.io == FASTVIM_BF16 ? pool_masked_image_lds<IoBf16>(g) != 0 : pool_masked_image_lds<IoF32>(g) != 0;
+}
+
+hipError_t launch_mask_pool(const Geom& g, const int32_t* idx, const void* x, const Workspace& ws,
+                            unsigned* status, hipStream_t st) {
+    return g.io == FASTVIM_BF16 ? pool_masked_image_t<IoBf16>(g, idx, x, ws, status, st)
+                                : pool_masked_image_t<IoF32>(g, idx, x, ws, status, st);
 }
 
 hipError_t launch_pool(const Geom& g, const void* x, const Workspace& ws, hipStream_t st) {
