@@ -11,6 +11,8 @@ Bar: 1e-4 fp32, 2e-2 bf16 (oracle on the bf16-rounded inputs).
 """
 from __future__ import annotations
 
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -27,7 +29,10 @@ KINDS = ("cols", "rows", "masked_cols", "masked_rows", "unpooled_row", "unpooled
 AXIS = {"cols": P.POOL_COLS, "rows": P.POOL_ROWS, "masked_cols": P.POOL_COLS, "masked_rows": P.POOL_ROWS,
         "unpooled_row": P.POOL_NONE_ROWMAJOR, "unpooled_col": P.POOL_NONE_COLMAJOR}
 FIELDS = ("x_proj_w", "dt_proj_w", "dt_proj_b", "A_log", "D")
-SEEDS = range(400)
+# 400 seeds by default; FASTVIM_RANDOM_SEEDS="a:b" runs seeds a .. b-1 instead
+# (for one-off wider sweeps)
+_seed_env = os.environ.get("FASTVIM_RANDOM_SEEDS", "")
+SEEDS = range(*map(int, _seed_env.split(":"))) if _seed_env else range(400)
 
 
 @pytest.fixture(scope="module", autouse=True)
