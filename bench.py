@@ -9,7 +9,7 @@ default path, one pipelined kernel launch (plus a one-block launch that resets
 its counters).  Prints one JSON line on stdout.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-extras] [--no-cpu-baseline]
-                    [--cpu-seconds S] [--profile-run] [--profile-bwd]
+                    [--cpu-seconds S] [--profile-run] [--profile-bwd] [--profile-small]
 
 Reported besides images/s:
   roofline      the single-launch kernel against the 8 TB/s HBM peak, with
@@ -32,7 +32,8 @@ Reported besides images/s:
 runs); --profile-bwd adds three backward calls of the same workload, three
 more given the pooled tokens a forward call saved, and three each with the
 post-SSM LayerNorm, the local backward scan, the producer Conv1D and both the
-Conv1D and the LayerNorm (pooled tokens saved).
+Conv1D and the LayerNorm (pooled tokens saved).  --profile-small runs only the
+small workloads (tiny, short-sequence, masked), a few calls of each form.
 """
 from __future__ import annotations
 
@@ -67,6 +68,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum CPU time of the oracle sample")
     ap.add_argument("--profile-run", action="store_true", help="layer steps and calibration copy only")
     ap.add_argument("--profile-bwd", action="store_true", help="with --profile-run: also three backward calls")
+    ap.add_argument("--profile-small", action="store_true",
+                    help="the small workloads only, a few calls each (for counter runs); prints their times")
     return ap.parse_args()
 
 
@@ -251,6 +254,12 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a ROCm GPU"
     P.lib()  # raises if the HIP library is not built
+    if args.profile_small:
+        # the tiny, short-sequence and masked workloads, each form of their
+        # scan and output stages, a few calls each (counter runs)
+        res = small_configs(P, C, torch, torch.cuda.current_stream(), nsets=2, calls=4)
+        print(json.dumps({"profile_small": res}), flush=True)
+        return
     cfg = C.HIRES_2048
     t0 = time.perf_counter()
     wl = draw_workload(cfg)

@@ -239,8 +239,12 @@ __device__ __forceinline__ void scan_lane_setup(const ScanArgs& a, int64_t b, in
 // Phase 3 for the kChunk steps of LDS rows dr: qv[j] is the step-size
 // pre-activation dt_proj_w[e] . delta_lowrank + dt_proj_b[e] of the lane's
 // own step q + 4j.
+// nv: steps of the chunk inside the sequence (kChunk unless it is the last,
+// partial chunk); the dot products of the steps past them are skipped (their
+// step sizes are never used).
 template <int RMAX>
-__device__ __forceinline__ void scan_step_preact(const ScanLane<RMAX>& L, const float* dr, float (&qv)[kJ]) {
+__device__ __forceinline__ void scan_step_preact(const ScanLane<RMAX>& L, const float* dr, float (&qv)[kJ],
+                                                 int nv = kChunk) {
     constexpr int S = row_stride_lds<RMAX>();
     const float* dq = dr + L.q * ScanLane<RMAX>::kWQ;
     // one group of 4 steps per iteration; qv rotates so its indices stay constant
@@ -249,6 +253,7 @@ __device__ __forceinline__ void scan_step_preact(const ScanLane<RMAX>& L, const 
         float own = 0.f;
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
+            if (4 * j + m >= nv) break;  // wave-uniform
             const float* row = dq + (4 * j + m) * S;
             float pq = 0.f;
 #pragma unroll
@@ -322,8 +327,12 @@ __device__ __forceinline__ void scan_step_preact_mfma(const ScanLane<RMAX>& L, c
 // [direction][t][channel] (T x kScanCh floats per direction, t in scan
 // position order), for a consumer in the same workgroup; the workgroup then
 // covers kScanCh channels (the lanes' channel is (thread % 256) / kLps).
+// TAIL: the chunk may run past the sequence end (the last chunk of a length
+// that is not a multiple of kChunk): the steps past it are skipped (they
+// would carry zero inputs and unit decays, so skipping them changes no
+// output); without TAIL every step runs.
 template <int RMAX, bool WRITE_THROUGH, bool LOCAL = false, bool KEEP_DECAYS = true, bool MFMA = false,
-          bool SLDS = false>
+          bool SLDS = false, bool TAIL = false>
 __device__ __forceinline__ void scan_chunk(const ScanArgs& a, ScanLane<RMAX>& L, const float* dr,
                                            const float (&ucur)[kJ], int64_t base, float* qs = nullptr,
                                            float* so = nullptr) {
@@ -331,12 +340,14 @@ __device__ __forceinline__ void scan_chunk(const ScanArgs& a, ScanLane<RMAX>& L,
     constexpr bool kKeep = LOCAL && KEEP_DECAYS;
     const int64_t T = a.T;
     const int chl = (threadIdx.x & 255) / kLps;  // SLDS: the lane's channel in the workgroup
+    // steps of the chunk inside the sequence (wave-uniform)
+    const int nv = TAIL ? (T - base < kChunk ? (int)(T - base) : kChunk) : kChunk;
     float dl[kJ], du[kJ], du0[kJ], dl0[kJ];
     float aS[kKeep ? kChunk : 1][kNs];  // decays of the chunk's steps (LOCAL, KEEP_DECAYS)
     {
         float qv[kJ];
         if (MFMA) scan_step_preact_mfma<RMAX>(L, dr, qs, qv);
-        else scan_step_preact<RMAX>(L, dr, qv);
+        else scan_step_preact<RMAX>(L, dr, qv, nv);
 #pragma unroll
         for (int j = 0; j < kJ; ++j) {
             const bool in = base + L.q + 4 * j < T;
@@ -357,6 +368,7 @@ __device__ __forceinline__ void scan_chunk(const ScanArgs& a, ScanLane<RMAX>& L,
     float* sp = L.sq + base * L.sstep;
 #pragma unroll
     for (int k = 0; k < kJ; ++k) {
+        if (TAIL && 4 * k >= nv) break;  // wave-uniform: the rest of the chunk is past the end
         float keep = 0.f;
         const float dk = dl[0], uk = du[0];
 #pragma unroll
@@ -367,6 +379,7 @@ __device__ __forceinline__ void scan_chunk(const ScanArgs& a, ScanLane<RMAX>& L,
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             const int s = 4 * k + m;
+            if (TAIL && s >= nv) break;  // wave-uniform
             const float dlt = m == 0 ? quad_bcast<0>(dk) : m == 1 ? quad_bcast<1>(dk)
                             : m == 2 ? quad_bcast<2>(dk) : quad_bcast<3>(dk);
             const float dus = m == 0 ? quad_bcast<0>(uk) : m == 1 ? quad_bcast<1>(uk)
@@ -414,6 +427,7 @@ __device__ __forceinline__ void scan_chunk(const ScanArgs& a, ScanLane<RMAX>& L,
 #pragma unroll
             for (int m = 3; m >= 0; --m) {
                 const int s = 4 * k + m;
+                if (TAIL && s >= nv) continue;  // wave-uniform: the state stays zero past the end
                 const float dus = m == 0 ? quad_bcast<0>(du0[k]) : m == 1 ? quad_bcast<1>(du0[k])
                                 : m == 2 ? quad_bcast<2>(du0[k]) : quad_bcast<3>(du0[k]);
                 const float dlt = kKeep ? 0.f
@@ -505,8 +519,12 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, const USrc& usrc, i
         for (int j = 0; j < kJ; ++j) ucur[j] = pre_u[j];
         __syncthreads();
         if (c + 1 < nchunks) prefetch(base + kChunk);
-        scan_chunk<RMAX, WRITE_THROUGH, LOCAL, KEEP_DECAYS, MFMA, SLDS>(a, L, xs + L.dir * kChunk * S, ucur, base,
-                                                                      wqs, so);
+        if (c + 1 == nchunks && iT % kChunk != 0)  // the last, partial chunk
+            scan_chunk<RMAX, WRITE_THROUGH, LOCAL, KEEP_DECAYS, MFMA, SLDS, true>(a, L, xs + L.dir * kChunk * S,
+                                                                                ucur, base, wqs, so);
+        else
+            scan_chunk<RMAX, WRITE_THROUGH, LOCAL, KEEP_DECAYS, MFMA, SLDS>(a, L, xs + L.dir * kChunk * S, ucur,
+                                                                          base, wqs, so);
     }
 }
 
