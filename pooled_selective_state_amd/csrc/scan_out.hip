@@ -25,10 +25,10 @@
 // A workgroup's output tokens are 64 channels wide: 256 bytes (fp32) or 128
 // bytes (bf16) per token, one 16-byte column per lane, 32 or 64 tokens per
 // pass of 512 lanes, kOutU tokens per lane in flight; for single-chunk scans
-// the first pass's x and z are loaded before the scan.  x and z are read for
-// the last time and out written once (non-temporal); x and out may be one
-// buffer (x_conv written out into out), each element being read by the lane
-// that then writes it.
+// each lane's first output token's x and z are loaded before the scan.  x and
+// z are read for the last time and out written once (non-temporal); x and
+// out may be one buffer (x_conv written out into out), each element being
+// read by the lane that then writes it.
 #include "scan_core.h"
 
 namespace fastvim {
