@@ -245,14 +245,16 @@ pool_masked_image_kernel(const typename IO::elem* __restrict__ x, const int32_t*
     }
 }
 
-// LDS bytes of pool_masked_image_kernel, or 0 when the layer does not fit it
-// (more kept tokens than threads, a row's lanes wider than the workgroup, or
-// more than 64 KB of LDS).
+// Dynamic LDS bytes of pool_masked_image_kernel, or 0 when the layer does not
+// fit it (more kept tokens than threads, a row's lanes wider than the
+// workgroup, or more than 60 KB of cell counts and lists: with the kernel's
+// static word the workgroup stays within the 64 KB it may hold).  Layers that
+// do not fit take the mask-rows and per-row pooling kernels.
 template <class IO>
 size_t pool_masked_image_lds(const Geom& g) {
     if (g.K > kImgMaxK || g.E / IO::V > kImgThreads) return 0;
     const size_t bytes = (size_t)(g.h * g.w + 2 * g.K + 2 * g.T) * 4;
-    return bytes <= 64 * 1024 ? bytes : 0;
+    return bytes <= 60 * 1024 ? bytes : 0;
 }
 
 template <class IO>

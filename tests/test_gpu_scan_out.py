@@ -125,10 +125,14 @@ def test_scan_out_options(option, axis):
 
 
 MASKED = [
-    # B, h, w, K, E, R: the masked Vim-B width, a ragged grid, every token kept
+    # B, h, w, K, E, R: the masked Vim-B width, a ragged grid, every token kept,
+    # the most kept tokens the one-launch mask validation and pooling takes
+    # (1024), and more (1100: the mask-rows and per-row pooling kernels)
     (3, 14, 14, 49, 1536, 48),
     (2, 9, 13, 30, 136, 7),
     (2, 6, 5, 30, 72, 16),
+    (1, 40, 33, 1024, 64, 8),
+    (1, 40, 40, 1100, 64, 8),
 ]
 
 
