@@ -16,6 +16,8 @@
 // A[l % 16][l / 16] and B[l / 16][l % 16], and MFMA i of the step covers
 // k = k0 + 4 (l / 16) + i for both operands.  Accumulator register r of lane
 // l holds output row 4 (l / 16) + r, column l % 16.
+#include <type_traits>
+
 #include "fastvim_internal.h"
 
 namespace fastvim {
@@ -122,6 +124,128 @@ proj_kernel(const Elem* __restrict__ src, int map_axis, int64_t M, int64_t T, in
     }
 }
 
+// Few tokens, long E (short, wide pooled layers: the masked Vim-B layer has
+// 3.6 k tokens of E = 1536): proj_kernel's 16-row workgroups each read the
+// whole weight slice from L2 for 16 tokens.  Here a workgroup takes RT
+// 16-row tiles, so every weight fragment it loads feeds RT tiles' MFMAs, and
+// kWidePW = 8 waves take interleaved 16-wide steps of E (two waves per SIMD,
+// as two proj_kernel workgroups per CU would have).  The waves' partial
+// tiles are added in a fixed order: waves w and w + 4 through LDS, then the
+// four sums as in proj_kernel (deterministic).  Operand layout as
+// proj_kernel; pooled tokens (fp32 u, row m is token m) only.
+constexpr int kWidePW = 8;
+
+template <int CT, int RT>
+__global__ void __launch_bounds__(64 * kWidePW)
+proj_wide_kernel(const float* __restrict__ u, int64_t M, int64_t E, const float* __restrict__ Wf,
+                 const float* __restrict__ Wb, int NX, int nout, float* __restrict__ xdbl) {
+    __shared__ float red[kWidePW / 2][RT][CT][256];  // partial tiles, [lane * 4 + r]
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int ri = lane & 15, kk = lane >> 4;
+    const int NO = 2 * NX;
+    const int64_t m0 = (int64_t)blockIdx.x * 16 * RT;
+    const int c0 = (int)blockIdx.y * CT * 16;
+    const float* rowp[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        const int64_t m = m0 + rt * 16 + ri < M ? m0 + rt * 16 + ri : M - 1;  // past M: a valid row, never stored
+        rowp[rt] = u + m * E + 4 * kk;
+    }
+    const float* wrow[CT];
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+        const int o = c0 + ct * 16 + ri;
+        wrow[ct] = (o < NX ? Wf + (int64_t)o * E : (o < NO ? Wb + (int64_t)(o - NX) * E : Wf)) + 4 * kk;
+    }
+    f32x4 acc[RT][CT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) acc[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto load_step = [&](int k0, float (&av)[RT][4], float (&bv)[CT][4]) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) load4(rowp[rt] + k0, av[rt]);
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) load4(wrow[ct] + k0, bv[ct]);
+    };
+    auto mfma_step = [&](const float (&av)[RT][4], const float (&bv)[CT][4]) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[rt][i], bv[ct][i], acc[rt][ct], 0, 0, 0);
+    };
+    // this wave's full 16-wide steps k0 = 16 wv + 16 kWidePW i, double-buffered
+    const int step = 16 * kWidePW;
+    const int Ef = (int)(E / 16) * 16;
+    float a0[RT][4], b0[CT][4], a1[RT][4], b1[CT][4];
+    int k0 = 16 * wv;
+    if (k0 < Ef) load_step(k0, a0, b0);
+    for (; k0 < Ef; k0 += 2 * step) {
+        const bool has1 = k0 + step < Ef;
+        if (has1) load_step(k0 + step, a1, b1);
+        mfma_step(a0, b0);
+        if (k0 + 2 * step < Ef) load_step(k0 + 2 * step, a0, b0);
+        if (has1) mfma_step(a1, b1);
+    }
+    if (Ef < E && wv == (Ef / 16) % kWidePW) {  // the tail of E (a multiple of 4), by the wave whose turn it is
+        const bool in = Ef + 4 * kk < E;
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            a0[rt][0] = a0[rt][1] = a0[rt][2] = a0[rt][3] = 0.f;
+            if (in) load4(rowp[rt] + Ef, a0[rt]);
+        }
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+            b0[ct][0] = b0[ct][1] = b0[ct][2] = b0[ct][3] = 0.f;
+            if (in) load4(wrow[ct] + Ef, b0[ct]);
+        }
+        mfma_step(a0, b0);
+    }
+    // waves 4..7 hand their partials to waves 0..3, which add them to their own
+    constexpr int kHalf = kWidePW / 2;
+    if (wv >= kHalf) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) red[wv - kHalf][rt][ct][lane * 4 + r] = acc[rt][ct][r];
+    }
+    __syncthreads();
+    if (wv < kHalf) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[rt][ct][r] += red[wv][rt][ct][lane * 4 + r];
+    }
+    __syncthreads();
+    if (wv < kHalf) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) red[wv][rt][ct][lane * 4 + r] = acc[rt][ct][r];
+    }
+    __syncthreads();
+    // row-major walk of each 16 x 16 tile, consecutive threads on consecutive columns
+    for (int e = threadIdx.x; e < RT * CT * 256; e += 64 * kWidePW) {
+        const int rt = e / (CT * 256), ct = (e >> 8) % CT, i = (e >> 4) & 15, j = e & 15;
+        const int src_idx = (16 * (i >> 2) + j) * 4 + (i & 3);
+        float v = red[0][rt][ct][src_idx];
+#pragma unroll
+        for (int q = 1; q < kHalf; ++q) v += red[q][rt][ct][src_idx];
+        const int64_t mm = m0 + rt * 16 + i;
+        const int o = c0 + ct * 16 + j;
+        if (mm < M && o < nout) xdbl[mm * NO + o] = v;
+    }
+}
+
 // Many tokens (unpooled layers): each wave owns RT 16-row tiles over all of
 // E, so every weight fragment it loads feeds RT tiles' MFMAs (the weights are
 // re-read from L2 once per 16 RT rows instead of once per 16) and no
@@ -215,6 +339,9 @@ constexpr int kRowsRT = 2;                       // row tiles per wave in proj_r
 constexpr int64_t kRowsMinTokens = 64 * 1024;    // token count from which it is used
 constexpr int kColSplit = 2;                     // column groups per row tile when row tiles are few ...
 constexpr int64_t kColSplitBelow = 512;          // ... fewer than this (two workgroups per CU)
+constexpr int kWideRT = 2;                       // row tiles per workgroup of proj_wide_kernel ...
+constexpr int64_t kWideMinE = 1024;              // ... for E of at least this ...
+constexpr int64_t kWideMinGroups = 192;          // ... when that still gives this many workgroups
 
 template <class Elem, int CT>
 hipError_t proj_launch(const Elem* src, int map_axis, const Geom& g, const fastvim_params& p, const Workspace& ws,
@@ -229,6 +356,15 @@ hipError_t proj_launch(const Elem* src, int map_axis, const Geom& g, const fastv
         if (rt < kColSplitBelow) {
             constexpr int CTS = (CT + kColSplit - 1) / kColSplit;
             const int ns = (CT + CTS - 1) / CTS;
+            const int64_t rt2 = (M + 16 * kWideRT - 1) / (16 * kWideRT);
+            if (std::is_same<Elem, float>::value && map_axis == FASTVIM_POOL_COLS && g.E >= kWideMinE &&
+                rt2 * ns >= kWideMinGroups) {
+                // pooled tokens of a short, wide layer
+                hipLaunchKernelGGL((proj_wide_kernel<CTS, kWideRT>), dim3((unsigned)rt2, (unsigned)ns),
+                                   dim3(64 * kWidePW), 0, st, reinterpret_cast<const float*>(src), M, g.E,
+                                   p.fwd.x_proj_w, p.bwd.x_proj_w, (int)g.NX, nout, ws.xdbl);
+                return hipGetLastError();
+            }
             hipLaunchKernelGGL((proj_kernel<Elem, CTS>), dim3((unsigned)rt, (unsigned)ns), dim3(64 * kPW), 0, st, src,
                                map_axis, M, g.T, g.h, g.w, g.E, p.fwd.x_proj_w, p.bwd.x_proj_w, (int)g.NX, nout,
                                ws.xdbl);

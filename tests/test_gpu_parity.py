@@ -94,6 +94,28 @@ def test_tiny_fastvim_t_layer(axis, io, path):
                  flags=PATHS[path])
 
 
+# Short, wide pooled layers (E >= 1024 and enough pooled tokens for 192
+# workgroups of 32 tokens) take the projection with 32-token workgroups and
+# 8 waves over E: every image against the oracle (out, D = 0 twin, u, both
+# x_proj directions, both scan outputs); the second case has a token count
+# off multiples of 32 and E off multiples of 16 (the tail step of E).
+SHORT_WIDE = [
+    # B, h, w, E, R
+    (48, 64, 2, 1024, 16),
+    (50, 62, 3, 1032, 20),
+]
+
+
+@pytest.mark.parametrize("shape", SHORT_WIDE, ids=["x".join(map(str, s)) for s in SHORT_WIDE])
+def test_projection_short_wide(shape):
+    B, h, w, E, R = shape
+    rng = np.random.default_rng(zlib.crc32(repr(shape).encode()))
+    x = rng.standard_normal((B, h, w, E)).astype(np.float32)
+    z = rng.standard_normal((B, h, w, E)).astype(np.float32)
+    prm = {"fwd": rand_dir(rng, E, 16, R, 0.1), "bwd": rand_dir(rng, E, 16, R, 0.1)}
+    _layer_check(x, z, prm, P.POOL_COLS, FP32_TOL, torch.float32, "short wide %s" % (shape,), chunk=16)
+
+
 RAGGED = [
     # B, h, w, E, R   (E not a multiple of 64, row counts not multiples of 32, odd grids)
     (3, 13, 7, 72, 5),
